@@ -1,0 +1,356 @@
+"""CPU oracle for the Sparse-BitLinear operator (Sparse-BitNet).
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow, obviously-correct
+definition of what the operator computes.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import it.  The product path (the HIP library and its Python binding) never
+calls it and shares no code with it.
+
+Sources (the pages this follows; cited by page and section):
+
+* [SUM]  "Sparse-BitNet：1.58-bit 大模型天然兼容半结构化稀疏 / Sparse-BitNet:
+  1.58-bit LLMs are Naturally Friendly to Semi-Structured Sparsity", the
+  structured summary of arXiv 2603.05168 at paper.rainbus.top.
+  Sections used: 前置知识 (prerequisites) > "1.58-bit BitNet 量化",
+  "半结构化 N:M 稀疏", "Straight-Through Estimator (STE)"; 核心方法 (core
+  method); 方法步骤详情 (method steps, the Algorithm 1 walk-through).
+* [GIST] the gist.science summary of arXiv 2603.05168, section
+  "2.2 Sparse-BitNet 框架" (Quant-then-Mask, mask from master weights, Dual STE).
+* [EXPL] "什麼是 Sparse-BitNet？核心概念一次搞懂" (openclaw-pages article),
+  sections "1.58 位元量化的技術原理" (threshold form of ternary rounding) and
+  "N:M 半結構化稀疏性的運作機制" (the worked 2:4 example).
+
+Arithmetic: every bf16 input is decoded exactly to float64.  The mask, the
+ternary codes, gamma, the int8 activations and the int32 accumulators are
+exact (integers or exactly-rounded values).  y, dX and dW are float64.
+
+Readings of points the pages leave open (each is repeated where it is used):
+
+* gamma is the correctly rounded (nearest-even) binary32 value of the exact
+  mean of |W| over the full, unmasked matrix.
+* RoundClip(W/gamma, -1, 1) ties go to 0: a weight is non-zero iff
+  |w| > gamma/2 (the threshold form on [EXPL]).
+* Top-N ties prefer the lower index; magnitude is compared on the bf16 value,
+  so +x and -x tie and +0/-0 are both 0.
+* Groups are M consecutive positions along d_in.
+* Activations: a_t = max_i |x[t,i]|; x_q = round-half-even(127 * x / a_t),
+  and a zero row quantizes to zeros.
+* Forward scale s = gamma * a_t / 127.
+* Backward (Dual STE, identity through quantizers and the mask):
+  dX = gamma * dY @ W_eff; dW = dY^T @ x~ with x~ = x_q * a_t / 127, dense over
+  every master weight, masked ones included.
+
+Parity pins live in ``tests/test_oracle_*.py``; none of them re-types these
+formulas.
+"""
+from __future__ import annotations
+
+import math
+from typing import Tuple
+
+import numpy as np
+
+FLT_MAX = float(np.finfo(np.float32).max)
+
+# ----------------------------------------------------------------------------
+# bf16 decoding
+# ----------------------------------------------------------------------------
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Decode bf16 bit patterns (uint16) to float64, exactly.  Asserts finiteness."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    exp = (bits >> 7) & 0xFF
+    assert not np.any(exp == 0xFF), "non-finite bf16 input"
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# gamma = mean |W|        [SUM] 前置知识 > 1.58-bit BitNet 量化:
+#                          gamma = ||W||_1 / (d_out * d_in)
+# ----------------------------------------------------------------------------
+
+BF16_QUANTUM_LOG2 = -133  # smallest bf16 subnormal is 2^-133
+
+
+def abs_sum_exact(W_bits: np.ndarray) -> int:
+    """Exact sum of |W| as a Python integer in units of 2^-133.
+
+    Every bf16 magnitude is an integer significand times a power of two:
+    normal (biased exponent e >= 1): (128 + fraction) * 2^(e - 134);
+    subnormal (e = 0): fraction * 2^-133.  Both equal sig * 2^(max(e,1) - 1)
+    in units of 2^-133.  Significands are summed per exponent (exactly: the
+    per-exponent sums stay far below 2^53) and then combined as big integers.
+    """
+    b = np.asarray(W_bits, dtype=np.uint16).astype(np.int64) & 0x7FFF
+    e = b >> 7
+    assert not np.any(e == 0xFF), "non-finite bf16 input"
+    frac = b & 0x7F
+    sig = np.where(e > 0, frac | 0x80, frac)
+    shift = np.maximum(e, 1) - 1
+    assert sig.size * 255 < 2 ** 53
+    per_exp = np.bincount(shift.ravel(), weights=sig.ravel().astype(np.float64), minlength=255)
+    total = 0
+    for s, v in enumerate(per_exp):
+        if v:
+            total += int(v) << s
+    return total
+
+
+def round_rational_to_f32(num: int, den: int) -> float:
+    """binary32 value nearest to num/den (ties to even), for num >= 0, den > 0.
+
+    Returned as a Python float holding an exactly representable binary32 value.
+    Handles the subnormal range (quantum 2^-149); overflow returns +inf.
+    """
+    assert num >= 0 and den > 0
+    if num == 0:
+        return 0.0
+    # exponent E with 2^E <= num/den < 2^(E+1)
+    E = num.bit_length() - den.bit_length()
+    if (num << max(0, -E)) < (den << max(0, E)):
+        E -= 1
+    q_exp = max(E, -126) - 23          # exponent of one unit in the last place
+    if q_exp >= 0:
+        n2, d2 = num, den << q_exp
+    else:
+        n2, d2 = num << (-q_exp), den
+    q, r = divmod(n2, d2)
+    if 2 * r > d2 or (2 * r == d2 and (q & 1)):
+        q += 1
+    val = math.ldexp(q, q_exp)
+    if val > FLT_MAX:
+        return math.inf
+    return val
+
+
+def gamma_f32(W_bits: np.ndarray) -> np.float32:
+    """gamma = RN_binary32( sum|W| / (d_out * d_in) ), over the full unmasked W.
+
+    [SUM] 前置知识 > 1.58-bit BitNet 量化 defines gamma as the mean absolute
+    value; [SUM] 核心方法 computes quantization and mask side by side on the
+    master weight, so gamma never sees the mask.  The pages do not fix the
+    arithmetic; the reading taken is the correctly rounded binary32 of the
+    exact mean, which does not depend on summation order.
+    """
+    W_bits = np.asarray(W_bits, dtype=np.uint16)
+    n = W_bits.size
+    assert n > 0
+    S = abs_sum_exact(W_bits)
+    return np.float32(round_rational_to_f32(S, n << 133))
+
+
+# ----------------------------------------------------------------------------
+# N:M top-N mask       [SUM] 前置知识 > 半结构化 N:M 稀疏 (||M_group||_0 = N
+#                      over every M consecutive positions); [SUM] 核心方法 (i)
+#                      M = Pi_{N:M}(|W|) on the continuous master weight;
+#                      [GIST] 2.2 (mask from master weights, not ternary ones)
+# ----------------------------------------------------------------------------
+
+
+def nm_mask(W_bits: np.ndarray, n_keep: int, m: int = 8) -> np.ndarray:
+    """Boolean keep-mask [d_out, d_in]: in every group of ``m`` consecutive
+    d_in positions keep the ``n_keep`` entries of largest |W|.
+
+    Ties: a stable sort by decreasing magnitude, so equal magnitudes keep the
+    lower index first.  Exactly ``n_keep`` slots are kept per group.
+    """
+    W = bf16_to_f64(W_bits)
+    d_out, d_in = W.shape
+    assert d_in % m == 0 and 1 <= n_keep <= m
+    mag = np.abs(W).reshape(d_out, d_in // m, m)
+    order = np.argsort(-mag, axis=-1, kind="stable")
+    keep = np.zeros_like(mag, dtype=bool)
+    np.put_along_axis(keep, order[..., :n_keep], True, axis=-1)
+    return keep.reshape(d_out, d_in)
+
+
+# ----------------------------------------------------------------------------
+# Ternary quantization  [SUM] 前置知识 > 1.58-bit BitNet 量化:
+#                       W_q = RoundClip(W / gamma, -1, +1);
+#                       [EXPL] 1.58 位元量化的技術原理: 0 when |w| <= gamma/2
+# ----------------------------------------------------------------------------
+
+
+def ternary(W_bits: np.ndarray, gamma: float) -> np.ndarray:
+    """W_q in {-1, 0, +1} (int8): sign(w) where |w| > gamma/2, else 0.
+
+    This is RoundClip(w/gamma, -1, 1) with the tie |w/gamma| = 1/2 going to 0,
+    evaluated as an exact float64 comparison (gamma/2 is exact).  gamma = 0
+    (an all-zero matrix) gives all zeros.
+    """
+    W = bf16_to_f64(W_bits)
+    half = float(gamma) / 2.0
+    return (np.sign(W) * (np.abs(W) > half)).astype(np.int8)
+
+
+def effective_weight(W_bits: np.ndarray, n_keep: int, m: int = 8
+                     ) -> Tuple[np.ndarray, np.ndarray, np.float32]:
+    """Quant-then-mask: W_eff = Q_t(W) * Pi_{N:M}(|W|).  Returns (W_eff int8, mask bool, gamma).
+
+    [SUM] 核心方法 (iii) and 方法步骤详情 steps (2), (4), (5); [GIST] 2.2.
+    """
+    g = gamma_f32(W_bits)
+    mask = nm_mask(W_bits, n_keep, m)
+    w_eff = ternary(W_bits, g) * mask.astype(np.int8)
+    return w_eff.astype(np.int8), mask, g
+
+
+# ----------------------------------------------------------------------------
+# Packed planes (the library's storage format, M = 8)
+# ----------------------------------------------------------------------------
+
+CODE_ZERO, CODE_PLUS, CODE_MINUS = 0b00, 0b01, 0b11
+
+
+def pack_codes(w_eff: np.ndarray) -> np.ndarray:
+    """Code plane uint16 [d_out, d_in/8]: slot j of group g at bits 2j..2j+1;
+    00 = 0, 01 = +1, 11 = -1 (10 never occurs)."""
+    d_out, d_in = w_eff.shape
+    assert d_in % 8 == 0
+    c = np.zeros(w_eff.shape, dtype=np.uint16)
+    c[w_eff == 1] = CODE_PLUS
+    c[w_eff == -1] = CODE_MINUS
+    c = c.reshape(d_out, d_in // 8, 8)
+    out = np.zeros((d_out, d_in // 8), dtype=np.uint16)
+    for j in range(8):
+        out |= (c[..., j] << (2 * j)).astype(np.uint16)
+    return out
+
+
+def pack_mask(mask: np.ndarray) -> np.ndarray:
+    """Mask plane uint8 [d_out, d_in/8]: bit j set iff slot j of the group is kept."""
+    d_out, d_in = mask.shape
+    assert d_in % 8 == 0
+    k = mask.reshape(d_out, d_in // 8, 8).astype(np.uint8)
+    out = np.zeros((d_out, d_in // 8), dtype=np.uint8)
+    for j in range(8):
+        out |= (k[..., j] << j).astype(np.uint8)
+    return out
+
+
+def unpack_codes(codes: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_codes``: int8 W_eff [d_out, 8 * groups]."""
+    codes = np.asarray(codes, dtype=np.uint16)
+    d_out, G = codes.shape
+    out = np.zeros((d_out, G, 8), dtype=np.int8)
+    for j in range(8):
+        f = (codes >> (2 * j)) & 3
+        assert not np.any(f == 0b10), "invalid code 10"
+        out[..., j] = np.where(f == CODE_PLUS, 1, np.where(f == CODE_MINUS, -1, 0))
+    return out.reshape(d_out, G * 8)
+
+
+def quant_mask_pack(W_bits: np.ndarray, n_keep: int):
+    """The packing step as the library exposes it: (codes, mask plane, gamma)."""
+    w_eff, mask, g = effective_weight(W_bits, n_keep, 8)
+    return pack_codes(w_eff), pack_mask(mask), g
+
+
+# ----------------------------------------------------------------------------
+# Activation quantization  [SUM] 前置知识 > 1.58-bit BitNet 量化 (absmax to
+#                          8-bit integers); [SUM] 方法步骤详情 step (3)
+# ----------------------------------------------------------------------------
+
+
+def act_quant(x_bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-token absmax int8 quantization: (x_q int8 [T, d_in], absmax float32 [T]).
+
+    a_t = max_i |x[t, i]|;  x_q = round-half-even(127 * x / a_t), a zero row
+    gives zeros.  The pages name absmax 8-bit quantization but not the
+    granularity, range or rounding; the reading is per token, scale 127
+    (so -128 never occurs) and ties to even.
+
+    Evaluated in float64: 127*x is exact, and the one rounding of the
+    quotient cannot move it across or onto a half-integer (for bf16 x and a_t
+    the exact quotient is either a half-integer or at least 2^-17 relative
+    away from one), so rint gives the exactly rounded value.  A test checks
+    this against exact rational arithmetic.
+    """
+    x = bf16_to_f64(x_bits)
+    assert x.ndim == 2
+    a = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0])
+    safe = np.where(a > 0, a, 1.0)
+    q = np.rint(127.0 * x / safe[:, None])
+    q[a == 0] = 0.0
+    assert np.all(np.abs(q) <= 127)
+    return q.astype(np.int8), a.astype(np.float32)
+
+
+def dequant_act(x_q: np.ndarray, absmax: np.ndarray) -> np.ndarray:
+    """x~ = x_q * a_t / 127 in float64 (the activation that enters the product)."""
+    return x_q.astype(np.float64) * (absmax.astype(np.float64)[:, None] / 127.0)
+
+
+# ----------------------------------------------------------------------------
+# Forward  [SUM] 前置知识 > 半结构化 N:M 稀疏 (y = (W (.) M) x);
+#          [SUM] 方法步骤详情 step (6): y ~= s * W_eff x~, s absorbs the scales
+# ----------------------------------------------------------------------------
+
+
+def forward_acc(w_eff: np.ndarray, x_q: np.ndarray) -> np.ndarray:
+    """Exact integer accumulators acc[t, o] = sum_i x_q[t, i] * W_eff[o, i] (int64).
+
+    The product is taken in float64: every term and every partial sum is an
+    integer of magnitude <= 127 * d_in < 2^53, so any summation order is exact.
+    """
+    d_in = x_q.shape[1]
+    assert 127 * d_in < 2 ** 53
+    acc = x_q.astype(np.float64) @ w_eff.astype(np.float64).T
+    out = acc.astype(np.int64)
+    assert np.all(np.abs(out) < 2 ** 31)
+    return out
+
+
+def forward_y(acc: np.ndarray, gamma: float, absmax: np.ndarray) -> np.ndarray:
+    """y[t, o] = acc[t, o] * gamma * a_t / 127, float64 (gamma, a_t widened exactly)."""
+    return acc.astype(np.float64) * (float(gamma) * absmax.astype(np.float64)[:, None] / 127.0)
+
+
+# ----------------------------------------------------------------------------
+# Backward (Dual STE)  [SUM] 前置知识 > Straight-Through Estimator (STE);
+#                      [SUM] 核心方法 (dense gradient to every master weight);
+#                      [SUM] 方法步骤详情 step (7); [GIST] 2.2
+# ----------------------------------------------------------------------------
+
+
+def backward(dY_bits: np.ndarray, w_eff: np.ndarray, gamma: float,
+             x_q: np.ndarray, absmax: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """(dX [T, d_in], dW [d_out, d_in]) in float64.
+
+    The straight-through estimator replaces both Q_t and Pi_{N:M} by the
+    identity, so the forward y = x~ (gamma W_eff)^T gives
+    dX = dY @ (gamma W_eff)   and   dW = dY^T @ x~   for every (o, i),
+    including masked positions.  The activation quantizer is also passed
+    straight through, so dX is the gradient w.r.t. the layer input.
+    """
+    dY = bf16_to_f64(dY_bits)
+    xt = dequant_act(x_q, absmax)
+    dX = float(gamma) * (dY @ w_eff.astype(np.float64))
+    dW = dY.T @ xt
+    return dX, dW
+
+
+def backward_stop_gradient(dY_bits, w_eff, gamma, x_q, absmax, mask):
+    """Ablation from [SUM] 前置知识 > STE ("mask without grad"): dW multiplied by the mask."""
+    dX, dW = backward(dY_bits, w_eff, gamma, x_q, absmax)
+    return dX, dW * mask
+
+
+# ----------------------------------------------------------------------------
+# Whole step
+# ----------------------------------------------------------------------------
+
+
+def sparse_bitlinear_step(W_bits, x_bits, dY_bits, n_keep: int):
+    """One forward + backward pass of a Sparse-BitLinear layer.  Returns a dict."""
+    w_eff, mask, g = effective_weight(W_bits, n_keep, 8)
+    x_q, a = act_quant(x_bits)
+    acc = forward_acc(w_eff, x_q)
+    y = forward_y(acc, g, a)
+    out = dict(gamma=g, mask=mask, w_eff=w_eff, codes=pack_codes(w_eff), mask_plane=pack_mask(mask),
+               x_q=x_q, absmax=a, acc=acc, y=y)
+    if dY_bits is not None:
+        dX, dW = backward(dY_bits, w_eff, g, x_q, a)
+        out.update(dX=dX, dW=dW)
+    return out

@@ -1,0 +1,134 @@
+"""The pins must catch plausible mistakes: plant each mistake in the oracle (on the
+CPU, via monkeypatch) and check that at least one pin test fails on it."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.sparse_bitlinear as sb
+
+import test_oracle_act as t_act
+import test_oracle_gamma as t_gamma
+import test_oracle_gemm as t_gemm
+import test_oracle_mask as t_mask
+import test_oracle_ternary as t_tern
+
+
+def _ties_to_higher_index(W_bits, n_keep, m=8):
+    W = sb.bf16_to_f64(W_bits)
+    d_out, d_in = W.shape
+    mag = np.abs(W).reshape(d_out, d_in // m, m)[..., ::-1]
+    order = np.argsort(-mag, axis=-1, kind="stable")
+    keep = np.zeros_like(mag, dtype=bool)
+    np.put_along_axis(keep, order[..., :n_keep], True, axis=-1)
+    return keep[..., ::-1].reshape(d_out, d_in)
+
+
+def _ternary_ge(W_bits, gamma):
+    W = sb.bf16_to_f64(W_bits)
+    return (np.sign(W) * (np.abs(W) >= float(gamma) / 2.0)).astype(np.int8)
+
+
+def _gamma_after_mask(W_bits, n_keep, m=8):
+    mask = sb.nm_mask(W_bits, n_keep, m)
+    Wm = np.where(mask, W_bits, np.uint16(0)).astype(np.uint16)
+    g = sb.gamma_f32(Wm)
+    return (sb.ternary(W_bits, g) * mask).astype(np.int8), mask, g
+
+
+def _act_quant_128(x_bits):
+    x = sb.bf16_to_f64(x_bits)
+    a = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0])
+    safe = np.where(a > 0, a, 1.0)
+    q = np.clip(np.rint(128.0 * x / safe[:, None]), -128, 127)
+    q[a == 0] = 0
+    return q.astype(np.int8), a.astype(np.float32)
+
+
+def _act_quant_half_away(x_bits):
+    x = sb.bf16_to_f64(x_bits)
+    a = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0])
+    safe = np.where(a > 0, a, 1.0)
+    z = 127.0 * x / safe[:, None]
+    q = np.sign(z) * np.floor(np.abs(z) + 0.5)
+    q[a == 0] = 0
+    return q.astype(np.int8), a.astype(np.float32)
+
+
+def _backward_no_gamma(dY_bits, w_eff, gamma, x_q, absmax):
+    dY = sb.bf16_to_f64(dY_bits)
+    return dY @ w_eff.astype(np.float64), dY.T @ sb.dequant_act(x_q, absmax)
+
+
+def _backward_raw_x(dY_bits, w_eff, gamma, x_q, absmax):
+    dY = sb.bf16_to_f64(dY_bits)
+    return float(gamma) * (dY @ w_eff.astype(np.float64)), dY.T @ x_q.astype(np.float64)
+
+
+def _backward_weff_transposed_dw(dY_bits, w_eff, gamma, x_q, absmax):
+    dY = sb.bf16_to_f64(dY_bits)
+    dW = dY.T @ sb.dequant_act(x_q, absmax)
+    return float(gamma) * (dY @ w_eff.astype(np.float64)), dW * (w_eff != 0)
+
+
+def _forward_y_no_127(acc, gamma, absmax):
+    return acc.astype(np.float64) * (float(gamma) * absmax.astype(np.float64)[:, None])
+
+
+_ORIG_PACK = sb.pack_codes
+
+
+def _pack_minus_as_10(w_eff):
+    out = _ORIG_PACK(np.where(w_eff == -1, 0, w_eff).astype(np.int8))
+    d_out, d_in = w_eff.shape
+    neg = (w_eff == -1).reshape(d_out, d_in // 8, 8)
+    for j in range(8):
+        out |= (neg[..., j].astype(np.uint16) << (2 * j + 1)).astype(np.uint16)
+    return out
+
+
+def _round_ties_up(num, den):
+    E = num.bit_length() - den.bit_length()
+    if (num << max(0, -E)) < (den << max(0, E)):
+        E -= 1
+    q_exp = max(E, -126) - 23
+    n2, d2 = (num, den << q_exp) if q_exp >= 0 else (num << -q_exp, den)
+    q, r = divmod(n2, d2)
+    if 2 * r >= d2:
+        q += 1
+    return math.ldexp(q, q_exp)
+
+
+MUTANTS = [
+    ("mask ties to higher index", "nm_mask", _ties_to_higher_index, [t_mask.test_mask_signed_zero_and_sign_ties]),
+    ("ternary tie goes to +-1", "ternary", _ternary_ge, [t_tern.test_ternary_boundary_rows]),
+    ("gamma from masked weights", "effective_weight", _gamma_after_mask, [t_tern.test_quant_then_mask_uses_full_matrix_gamma]),
+    ("activation scale 128", "act_quant", _act_quant_128, [t_act.test_act_quant_properties]),
+    ("activation rounding half away from zero", "act_quant", _act_quant_half_away,
+     [lambda: t_act.test_act_quant_exact_rational(1.984375)]),
+    ("dX without gamma", "backward", _backward_no_gamma,
+     [lambda: t_gemm.test_forward_and_backward_match_torch_ste(6)]),
+    ("dW from raw x_q", "backward", _backward_raw_x,
+     [lambda: t_gemm.test_forward_and_backward_match_torch_ste(6)]),
+    ("dW stop-gradient through the mask", "backward", _backward_weff_transposed_dw,
+     [t_gemm.test_dual_ste_masked_weights_get_dense_gradient]),
+    ("y without the /127", "forward_y", _forward_y_no_127,
+     [lambda: t_gemm.test_forward_and_backward_match_torch_ste(4)]),
+    ("-1 packed as 10", "pack_codes", _pack_minus_as_10, [t_tern.test_pack_codes_bit_layout]),
+    ("rational rounding ties up", "round_rational_to_f32", _round_ties_up,
+     [t_gamma.test_round_rational_matches_numpy_on_exact_doubles]),
+]
+
+
+@pytest.mark.parametrize("name,attr,fn,tests", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(monkeypatch, name, attr, fn, tests):
+    monkeypatch.setattr(sb, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn, raising=False)
+    caught = False
+    for t in tests:
+        try:
+            t()
+        except AssertionError:
+            caught = True
+    assert caught, f"no pin caught the planted mistake: {name}"
