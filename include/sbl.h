@@ -1,0 +1,217 @@
+/*
+ * sbl.h -- C ABI of the Sparse-BitLinear library for AMD MI355X (gfx950).
+ *
+ * Sparse-BitLinear is the layer of Sparse-BitNet that replaces every linear
+ * layer: a BF16 master weight W [d_out, d_in] is quantized to ternary codes
+ * {-1, 0, +1} with the absmean scale gamma, masked to N kept slots in every
+ * group of 8 consecutive d_in positions (top-N by |W| of the master weight),
+ * and multiplied with per-token absmax int8 activations.  The backward pass is
+ * the Dual straight-through estimator: dW flows densely to every master
+ * weight, masked ones included, and dX goes through the effective weight.
+ *
+ * Sources, cited by page and section:
+ *   [SUM]  "Sparse-BitNet: 1.58-bit LLMs are Naturally Friendly to
+ *          Semi-Structured Sparsity" -- structured summary of arXiv
+ *          2603.05168 (paper.rainbus.top).  Sections: 前置知识 (prerequisites)
+ *          > "1.58-bit BitNet 量化", "半结构化 N:M 稀疏",
+ *          "Straight-Through Estimator (STE)"; 核心方法 (core method);
+ *          方法步骤详情 (method steps).
+ *   [GIST] gist.science summary of arXiv 2603.05168, section
+ *          "2.2 Sparse-BitNet 框架".
+ *   [EXPL] "什麼是 Sparse-BitNet？核心概念一次搞懂" (openclaw-pages), section
+ *          "1.58 位元量化的技術原理" (ternary threshold form).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers (memory on the current HIP
+ *     device) unless stated otherwise; all tensors are dense row-major.
+ *     bfloat16 values are passed as their uint16 bit patterns.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     device memory; scratch space is a caller-provided workspace.
+ *   - `hip_stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Every call only enqueues work on that stream and returns
+ *     without synchronizing.  gamma and absmax stay in device memory and are
+ *     read by later calls in stream order.
+ *   - Every function returns an sbl_status.  Arguments are validated on the
+ *     host before anything is enqueued, so an error return means no work was
+ *     enqueued.  A HIP launch failure returns SBL_ERR_HIP with detail text in
+ *     sbl_last_error().  Faults inside kernels surface at the caller's next
+ *     synchronization, as with any HIP work.
+ *   - Inputs must be finite; non-finite inputs give unspecified results.
+ *   - All outputs are bitwise deterministic: no floating-point atomics, and
+ *     every reduction runs in a fixed order.
+ *   - Device pointers must be 16-byte aligned, except absmax/gamma (4-byte).
+ *   - Calls on different streams that write the same buffers race; ordering
+ *     across streams is the caller's job.
+ */
+#ifndef SBL_H_
+#define SBL_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SBL_API __attribute__((visibility("default")))
+#else
+#define SBL_API
+#endif
+
+typedef enum {
+  SBL_OK = 0,
+  SBL_ERR_INVALID_ARG = -1, /* NULL or misaligned pointer, unknown dtype/flag */
+  SBL_ERR_SHAPE = -2,       /* a size outside the supported range           */
+  SBL_ERR_UNSUPPORTED = -3, /* a valid but unimplemented option (e.g. n_keep) */
+  SBL_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than required      */
+  SBL_ERR_HIP = -5          /* a HIP runtime call failed                    */
+} sbl_status;
+
+typedef enum {
+  SBL_F32 = 0,  /* float32                                    */
+  SBL_BF16 = 1, /* bfloat16 (round to nearest even)           */
+  SBL_I32 = 2   /* raw int32 accumulators (sbl_forward only)  */
+} sbl_dtype;
+
+/* sbl_backward flags: which gradients to compute. */
+enum { SBL_BWD_DX = 1, SBL_BWD_DW = 2 };
+
+/* Size limits checked by every entry point. */
+#define SBL_MAX_DIM ((int64_t)1 << 24)      /* d_in, d_out, T each <= 16,777,216 */
+#define SBL_MAX_WEIGHTS ((int64_t)1 << 36)  /* d_out * d_in                       */
+
+/* ------------------------------------------------------------------------ */
+/* Weight side: gamma, N:8 mask, ternary codes                               */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace sbl_quant_mask_pack needs for a [d_out, d_in] weight.
+ * Returns 0 for shapes sbl_quant_mask_pack would reject. */
+SBL_API size_t sbl_quant_mask_pack_workspace_size(int64_t d_out, int64_t d_in);
+
+/* Quant-then-mask of a BF16 master weight ([SUM] 核心方法 (i)-(iii);
+ * 方法步骤详情 steps (2), (4), (5); [GIST] 2.2):
+ *
+ *   gamma  = mean |W| over the full, unmasked matrix ([SUM] 前置知识 >
+ *            1.58-bit BitNet 量化), as the correctly rounded (nearest-even)
+ *            float32 of the exact mean, so it is independent of summation
+ *            order;
+ *   mask   = in every group of 8 consecutive d_in positions, keep the n_keep
+ *            slots of largest |W| (bf16 magnitude; ties to the lower index)
+ *            ([SUM] 前置知识 > 半结构化 N:M 稀疏; 核心方法 (i));
+ *   W_q    = RoundClip(W/gamma, -1, 1) = sign(W) if |W| > gamma/2 else 0
+ *            (tie goes to 0; [EXPL] threshold form);
+ *   W_eff  = W_q * mask.
+ *
+ * W_bf16 : [d_out, d_in] bf16 bits.           d_in % 8 == 0, d_in >= 8.
+ * n_keep : N of N:8, one of 2, 4, 6, 8.       d_out >= 1.
+ * codes  : [d_out, d_in/8] uint16 code plane.  Slot j (d_in position 8g+j)
+ *          of group g sits at bits 2j..2j+1: 00 = 0, 01 = +1, 11 = -1 (10 is
+ *          never written).  Masked slots hold 00.
+ * mask   : [d_out, d_in/8] uint8 mask plane, bit j = slot j kept.  May be
+ *          NULL when the caller does not need it.
+ * gamma  : one float32 in device memory.
+ * workspace: at least sbl_quant_mask_pack_workspace_size(d_out, d_in) bytes,
+ *          device memory; contents need no initialization and are clobbered.
+ */
+SBL_API int sbl_quant_mask_pack(const uint16_t* W_bf16, int64_t d_out, int64_t d_in, int n_keep,
+                                uint16_t* codes, uint8_t* mask, float* gamma, void* workspace,
+                                size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* Activation side                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* Per-token absmax 8-bit quantization ([SUM] 前置知识 > 1.58-bit BitNet 量化,
+ * last sentence; 方法步骤详情 step (3)):
+ *
+ *   absmax[t] = max_i |x[t, i]|;
+ *   x_q[t, i] = round-half-even(127 * x[t, i] / absmax[t])  (|x_q| <= 127),
+ *   a zero row gives x_q = 0 and absmax = 0.
+ *
+ * x_bf16 : [T, d_in] bf16 bits.  T >= 0 (T = 0 is a no-op), d_in % 8 == 0.
+ * x_q    : [T, d_in] int8.
+ * absmax : [T] float32 (the exact bf16 value of the row maximum).
+ */
+SBL_API int sbl_act_quant(const uint16_t* x_bf16, int64_t T, int64_t d_in, int8_t* x_q, float* absmax,
+                          void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* Forward                                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* Forward product ([SUM] 前置知识 > 半结构化 N:M 稀疏: y = (W (.) M) x;
+ * 方法步骤详情 step (6): y ~= s * W_eff x~, s absorbing the scales):
+ *
+ *   acc[t, o] = sum_i x_q[t, i] * W_eff[o, i]        (exact int32)
+ *   y[t, o]   = acc[t, o] * gamma * absmax[t] / 127
+ *
+ * codes, gamma : from sbl_quant_mask_pack for W [d_out, d_in].
+ * x_q, absmax  : from sbl_act_quant, [T, d_in] and [T].
+ * y            : [T, d_out] of y_dtype: SBL_F32, SBL_BF16, or SBL_I32 (acc).
+ * T = 0 is a no-op.  Small T (decode, T <= 16) uses a streaming kernel;
+ * larger T uses the int8 matrix-core kernel; both give identical results.
+ */
+SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t* x_q, const float* absmax,
+                        int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* Backward (Dual STE)                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace sbl_backward needs (split-K partial sums of dW for
+ * shapes with few output tiles).  May be 0. */
+SBL_API size_t sbl_backward_workspace_size(int64_t T, int64_t d_in, int64_t d_out, int flags);
+
+/* Dual-STE backward ([SUM] 前置知识 > Straight-Through Estimator (STE);
+ * 核心方法 (dense gradient flow); 方法步骤详情 step (7); [GIST] 2.2).  The
+ * straight-through estimator replaces the ternary quantizer, the N:M
+ * selector and the activation quantizer by the identity, so for the forward
+ * y = x~ (gamma W_eff)^T with x~ = x_q * absmax / 127:
+ *
+ *   dX[t, i] = gamma * sum_o dY[t, o] * W_eff[o, i]      (flags & SBL_BWD_DX)
+ *   dW[o, i] = sum_t dY[t, o] * x~[t, i]                 (flags & SBL_BWD_DW)
+ *
+ * dW is dense: every (o, i), masked positions included, gets its gradient.
+ * Both products run on bf16 matrix cores with float32 accumulation (x~ is
+ * rounded to bf16 once, W_eff in {-1,0,1} is exact in bf16).
+ *
+ * dY_bf16 : [T, d_out] bf16 bits.
+ * dX      : [T, d_in] of dx_dtype (SBL_BF16 or SBL_F32); may be NULL without
+ *           SBL_BWD_DX.
+ * dW      : [d_out, d_in] float32; may be NULL without SBL_BWD_DW.  With
+ *           T = 0, dW is set to zero.
+ * workspace: at least sbl_backward_workspace_size(...) bytes (may be NULL
+ *           when that size is 0).
+ */
+SBL_API int sbl_backward(const uint16_t* codes, const float* gamma, const int8_t* x_q, const float* absmax,
+                         const uint16_t* dY_bf16, int64_t T, int64_t d_in, int64_t d_out, void* dX,
+                         int dx_dtype, float* dW, int flags, void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
+
+/* ------------------------------------------------------------------------ */
+/* Status and test hooks                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Static English text for a status code. */
+SBL_API const char* sbl_status_string(int status);
+
+/* Detail of the last error on the calling thread (thread-local, static
+ * storage valid until the next failing call on that thread). */
+SBL_API const char* sbl_last_error(void);
+
+/* Library version string. */
+SBL_API const char* sbl_version(void);
+
+/* HOST-side test hook for the exact gamma rounding that the device code uses
+ * (the same function, compiled for the host).  S is an unsigned integer of
+ * n_words little-endian 32-bit words holding sum|W| in units of 2^-133;
+ * count = d_out * d_in.  Writes RN_float32(S * 2^-133 / count) to *out (host
+ * pointer).  n_words <= 10. */
+SBL_API int sbl_test_round_mean(const uint32_t* S_words, int n_words, int64_t count, float* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SBL_H_ */

@@ -1,0 +1,224 @@
+"""Sparse-BitLinear for AMD MI355X (gfx950): Python binding of ``libsbl.so``.
+
+Thin argument marshalling over the C ABI declared in ``include/sbl.h``; every
+step of the operator runs in the library's HIP kernels.  PyTorch supplies
+device memory and the current HIP stream only.  There is no fallback: if the
+library is missing or no GPU is present, calls raise.
+
+Functions mirror the C entry points:
+
+* ``quant_mask_pack(W, n_keep)`` -> ``(codes, mask, gamma)``
+* ``act_quant(x)`` -> ``(x_q, absmax)``
+* ``forward(codes, gamma, x_q, absmax, d_out, out_dtype)`` -> ``y``
+* ``backward(codes, gamma, x_q, absmax, dY, ...)`` -> ``(dX, dW)``
+
+``SparseBitLinearFunction`` wraps them as a ``torch.autograd.Function``
+(quantize/mask/pack every call, Dual-STE backward).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "lib", "SblError", "quant_mask_pack", "act_quant", "forward", "backward",
+    "quant_workspace_size", "backward_workspace_size", "SparseBitLinearFunction", "sparse_bitlinear",
+    "F32", "BF16", "I32", "BWD_DX", "BWD_DW",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsbl.so")
+
+F32, BF16, I32 = 0, 1, 2
+BWD_DX, BWD_DW = 1, 2
+
+_c_i64 = ctypes.c_int64
+_c_ptr = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_size = ctypes.c_size_t
+
+_SIGNATURES = {
+    "sbl_quant_mask_pack_workspace_size": (_c_size, [_c_i64, _c_i64]),
+    "sbl_quant_mask_pack": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+    "sbl_act_quant": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "sbl_forward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
+    "sbl_backward_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int]),
+    "sbl_backward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int,
+                              _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr]),
+    "sbl_status_string": (ctypes.c_char_p, [_c_int]),
+    "sbl_last_error": (ctypes.c_char_p, []),
+    "sbl_version": (ctypes.c_char_p, []),
+    "sbl_test_round_mean": (_c_int, [ctypes.POINTER(ctypes.c_uint32), _c_int, _c_i64, ctypes.POINTER(ctypes.c_float)]),
+}
+
+
+class SblError(RuntimeError):
+    """A libsbl call returned a non-zero status."""
+
+    def __init__(self, status: int, func: str):
+        self.status = status
+        msg = lib.sbl_status_string(status).decode()
+        detail = lib.sbl_last_error().decode()
+        super().__init__(f"{func} failed: {msg} ({status}): {detail}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m sparsity_sparse_bitlinear_amd.build` "
+            "(hipcc for gfx950).  There is no fallback implementation.")
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+def _check(status: int, func: str) -> None:
+    if status != 0:
+        raise SblError(status, func)
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _as_bits16(t: torch.Tensor, name: str) -> torch.Tensor:
+    _dev(t, name)
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bfloat16 values (bfloat16, or int16/uint16 bit patterns)")
+    return t
+
+
+def quant_workspace_size(d_out: int, d_in: int) -> int:
+    return int(lib.sbl_quant_mask_pack_workspace_size(d_out, d_in))
+
+
+def backward_workspace_size(T: int, d_in: int, d_out: int, flags: int = BWD_DX | BWD_DW) -> int:
+    return int(lib.sbl_backward_workspace_size(T, d_in, d_out, flags))
+
+
+def quant_mask_pack(W: torch.Tensor, n_keep: int = 6, *, codes: Optional[torch.Tensor] = None,
+                    mask: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, want_mask: bool = True, stream=None):
+    """gamma, N:8 mask and 2-bit ternary code plane of the bf16 master weight ``W`` [d_out, d_in].
+
+    Returns ``(codes int16 [d_out, d_in/8] (uint16 bit patterns), mask uint8 [d_out, d_in/8] or None,
+    gamma float32 [1])``; all on W's device.
+    """
+    _as_bits16(W, "W")
+    d_out, d_in = W.shape
+    dev = W.device
+    if codes is None:
+        codes = torch.empty((d_out, d_in // 8), dtype=torch.int16, device=dev)
+    if mask is None and want_mask:
+        mask = torch.empty((d_out, d_in // 8), dtype=torch.uint8, device=dev)
+    if gamma is None:
+        gamma = torch.empty((1,), dtype=torch.float32, device=dev)
+    need = quant_workspace_size(d_out, d_in)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _check(lib.sbl_quant_mask_pack(_ptr(W), d_out, d_in, int(n_keep), _ptr(codes), _ptr(mask), _ptr(gamma),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)), "sbl_quant_mask_pack")
+    return codes, mask, gamma
+
+
+def act_quant(x: torch.Tensor, *, x_q: Optional[torch.Tensor] = None, absmax: Optional[torch.Tensor] = None,
+              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-token absmax int8 quantization of bf16 ``x`` [T, d_in] -> (x_q int8, absmax float32 [T])."""
+    _as_bits16(x, "x")
+    T, d_in = x.shape
+    if x_q is None:
+        x_q = torch.empty((T, d_in), dtype=torch.int8, device=x.device)
+    if absmax is None:
+        absmax = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _check(lib.sbl_act_quant(_ptr(x), T, d_in, _ptr(x_q), _ptr(absmax), _stream(stream)), "sbl_act_quant")
+    return x_q, absmax
+
+
+_OUT_TORCH = {F32: torch.float32, BF16: torch.bfloat16, I32: torch.int32}
+
+
+def forward(codes: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax: torch.Tensor, *,
+            out_dtype: int = F32, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y[t, o] = (sum_i x_q[t, i] W_eff[o, i]) * gamma * absmax[t] / 127  (or the raw int32 sums)."""
+    for t, n in ((codes, "codes"), (gamma, "gamma"), (x_q, "x_q"), (absmax, "absmax")):
+        _dev(t, n)
+    d_out, G = codes.shape
+    T, d_in = x_q.shape
+    if G * 8 != d_in:
+        raise ValueError(f"codes [{d_out}, {G}] do not match x_q [{T}, {d_in}]")
+    if y is None:
+        y = torch.empty((T, d_out), dtype=_OUT_TORCH[out_dtype], device=x_q.device)
+    _check(lib.sbl_forward(_ptr(codes), _ptr(gamma), _ptr(x_q), _ptr(absmax), T, d_in, d_out, _ptr(y),
+                           int(out_dtype), _stream(stream)), "sbl_forward")
+    return y
+
+
+def backward(codes: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax: torch.Tensor,
+             dY: torch.Tensor, *, need_dx: bool = True, need_dw: bool = True, dx_dtype: int = BF16,
+             dX: Optional[torch.Tensor] = None, dW: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, stream=None):
+    """Dual-STE gradients: dX = gamma dY W_eff [T, d_in], dW = dY^T x~ [d_out, d_in] (float32)."""
+    _as_bits16(dY, "dY")
+    d_out, G = codes.shape
+    T, d_in = x_q.shape
+    flags = (BWD_DX if need_dx else 0) | (BWD_DW if need_dw else 0)
+    if need_dx and dX is None:
+        dX = torch.empty((T, d_in), dtype=_OUT_TORCH[dx_dtype], device=dY.device)
+    if need_dw and dW is None:
+        dW = torch.empty((d_out, d_in), dtype=torch.float32, device=dY.device)
+    need = backward_workspace_size(T, d_in, d_out, flags)
+    if need and workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=dY.device)
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib.sbl_backward(_ptr(codes), _ptr(gamma), _ptr(x_q), _ptr(absmax), _ptr(dY), T, d_in, d_out,
+                            _ptr(dX if need_dx else None), int(dx_dtype), _ptr(dW if need_dw else None), flags,
+                            _ptr(workspace), ws_bytes, _stream(stream)), "sbl_backward")
+    return (dX if need_dx else None), (dW if need_dw else None)
+
+
+class SparseBitLinearFunction(torch.autograd.Function):
+    """y = Sparse-BitLinear(x; W) with the mask and codes recomputed from W on every call.
+
+    x: bf16 [T, d_in]; W: bf16 master weight [d_out, d_in].  Returns y float32 [T, d_out].
+    Backward (Dual STE): grad_x bf16 [T, d_in], grad_W float32 [d_out, d_in] (dense).
+    """
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, W: torch.Tensor, n_keep: int = 6):
+        codes, _, gamma = quant_mask_pack(W.contiguous(), n_keep, want_mask=False)
+        x_q, absmax = act_quant(x.contiguous())
+        y = forward(codes, gamma, x_q, absmax, out_dtype=F32)
+        ctx.save_for_backward(codes, gamma, x_q, absmax)
+        return y
+
+    @staticmethod
+    def backward(ctx, grad_y: torch.Tensor):
+        codes, gamma, x_q, absmax = ctx.saved_tensors
+        dY = grad_y.to(torch.bfloat16).contiguous()
+        dX, dW = backward(codes, gamma, x_q, absmax, dY, need_dx=ctx.needs_input_grad[0],
+                          need_dw=ctx.needs_input_grad[1], dx_dtype=BF16)
+        return dX, dW, None
+
+
+def sparse_bitlinear(x: torch.Tensor, W: torch.Tensor, n_keep: int = 6) -> torch.Tensor:
+    return SparseBitLinearFunction.apply(x, W, n_keep)

@@ -1,0 +1,110 @@
+// Per-token absmax int8 activation quantization on gfx950.
+//
+// [SUM] 前置知识 > 1.58-bit BitNet 量化 (activations absmax-quantized to
+// 8-bit integers) and 方法步骤详情 step (3):
+//   a_t = max_i |x[t,i]|,  x_q[t,i] = round-half-even(127 x[t,i] / a_t).
+//
+// One wavefront per token row: the row is held in registers (up to NC 16-byte
+// chunks per lane), the maximum is a wave reduction on the 15-bit magnitude
+// bits (integer order equals magnitude order for finite bf16), then every
+// element is quantized from registers.  Rows longer than 64*NC chunks re-read
+// the remainder.
+//
+// Binary32 evaluation: x and a are first scaled by the same exact power of two
+// so that a lands in [1, 2) (this keeps 127*x finite and a normal), then
+// q = rint(fl(fl(127 x') / a')).  For bf16 inputs the exact quotient is either a
+// half-integer or at least 2^-17 (relative) away from one, so the single
+// binary32 rounding of the division cannot change the rounded integer: the
+// result equals the exact round-half-even of 127 x / a.
+#include "sbl_internal.h"
+
+namespace sbl {
+
+__device__ __forceinline__ uint32_t max_mag2(uint32_t w) {
+  return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
+}
+
+__device__ __forceinline__ int quant_one(uint32_t h16, int k, float as) {
+  const float x = __uint_as_float(h16 << 16);
+  const float xs = ldexpf(x, k);
+  return (int)rintf((127.0f * xs) / as);
+}
+
+__device__ __forceinline__ uint32_t quant_word_pair(uint32_t w0, uint32_t w1, int k, float as) {
+  const int q0 = quant_one(w0 & 0xFFFFu, k, as);
+  const int q1 = quant_one(w0 >> 16, k, as);
+  const int q2 = quant_one(w1 & 0xFFFFu, k, as);
+  const int q3 = quant_one(w1 >> 16, k, as);
+  return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+         ((uint32_t)(q3 & 0xFF) << 24);
+}
+
+__device__ __forceinline__ uint2 quant_chunk(uint4 v, int k, float as) {
+  return make_uint2(quant_word_pair(v.x, v.y, k, as), quant_word_pair(v.z, v.w, k, as));
+}
+
+template <int NC>
+__global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ x, int64_t T, int d_in,
+                                                   int8_t* __restrict__ xq, float* __restrict__ absmax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int nch = d_in >> 3;  // 16-byte chunks per row
+  const uint4* row = (const uint4*)(x + t * (int64_t)d_in);
+  uint2* out = (uint2*)(xq + t * (int64_t)d_in);
+
+  uint4 v[NC];
+  uint32_t m = 0;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int idx = lane + 64 * c;
+    if (idx < nch) {
+      v[c] = row[idx];
+      m = max(m, max(max_mag2(v[c].x), max_mag2(v[c].y)));
+      m = max(m, max(max_mag2(v[c].z), max_mag2(v[c].w)));
+    } else {
+      v[c] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  for (int idx = lane + 64 * NC; idx < nch; idx += 64) {  // rows longer than the register window
+    const uint4 w = row[idx];
+    m = max(m, max(max_mag2(w.x), max_mag2(w.y)));
+    m = max(m, max(max_mag2(w.z), max_mag2(w.w)));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+
+  const float a = __uint_as_float(m << 16);
+  if (lane == 0) absmax[t] = a;
+  if (m == 0) {
+    for (int idx = lane; idx < nch; idx += 64) out[idx] = make_uint2(0, 0);
+    return;
+  }
+  int e;
+  (void)frexpf(a, &e);  // a = f * 2^e, f in [0.5, 1)
+  const int k = 1 - e;  // a * 2^k in [1, 2)
+  const float as = ldexpf(a, k);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int idx = lane + 64 * c;
+    if (idx < nch) out[idx] = quant_chunk(v[c], k, as);
+  }
+  for (int idx = lane + 64 * NC; idx < nch; idx += 64) out[idx] = quant_chunk(row[idx], k, as);
+}
+
+hipError_t launch_act_quant(const uint16_t* x, int64_t T, int64_t d_in, int8_t* xq, float* absmax, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int nch = (int)(d_in / 8);
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (nch <= 64 * 4)
+    hipLaunchKernelGGL(k_act_quant<4>, grid, block, 0, s, x, T, (int)d_in, xq, absmax);
+  else if (nch <= 64 * 8)
+    hipLaunchKernelGGL(k_act_quant<8>, grid, block, 0, s, x, T, (int)d_in, xq, absmax);
+  else if (nch <= 64 * 16)
+    hipLaunchKernelGGL(k_act_quant<16>, grid, block, 0, s, x, T, (int)d_in, xq, absmax);
+  else
+    hipLaunchKernelGGL(k_act_quant<24>, grid, block, 0, s, x, T, (int)d_in, xq, absmax);
+  return hipGetLastError();
+}
+
+}  // namespace sbl

@@ -1,0 +1,186 @@
+// C ABI of libsbl: argument validation, workspace sizing and kernel launches
+// on the caller's stream.  Every check runs on the host before any launch, so
+// an error return means nothing was enqueued.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+
+#include "sbl_internal.h"
+
+namespace sbl {
+
+static thread_local char g_last_error[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  set_error("%s: %s (%s)", what, hipGetErrorString(e), hipGetErrorName(e));
+  return SBL_ERR_HIP;
+}
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+#define SBL_REQUIRE(cond, code, ...)   \
+  do {                                 \
+    if (!(cond)) {                     \
+      set_error(__VA_ARGS__);          \
+      return (code);                   \
+    }                                  \
+  } while (0)
+
+static int check_dims(int64_t d_out, int64_t d_in) {
+  SBL_REQUIRE(d_in >= 8 && d_in % 8 == 0, SBL_ERR_SHAPE, "d_in=%lld must be a positive multiple of 8",
+              (long long)d_in);
+  SBL_REQUIRE(d_out >= 1, SBL_ERR_SHAPE, "d_out=%lld must be >= 1", (long long)d_out);
+  SBL_REQUIRE(d_in <= SBL_MAX_DIM && d_out <= SBL_MAX_DIM, SBL_ERR_SHAPE, "d_in/d_out above %lld",
+              (long long)SBL_MAX_DIM);
+  SBL_REQUIRE(d_in * d_out <= SBL_MAX_WEIGHTS, SBL_ERR_SHAPE, "d_out*d_in above %lld", (long long)SBL_MAX_WEIGHTS);
+  return SBL_OK;
+}
+
+static int check_tokens(int64_t T) {
+  SBL_REQUIRE(T >= 0 && T <= SBL_MAX_DIM, SBL_ERR_SHAPE, "T=%lld outside [0, %lld]", (long long)T,
+              (long long)SBL_MAX_DIM);
+  return SBL_OK;
+}
+
+}  // namespace sbl
+
+using namespace sbl;
+
+extern "C" {
+
+SBL_API const char* sbl_version(void) { return "sbl 0.1.0 (gfx950)"; }
+
+SBL_API const char* sbl_status_string(int status) {
+  switch (status) {
+    case SBL_OK: return "ok";
+    case SBL_ERR_INVALID_ARG: return "invalid argument";
+    case SBL_ERR_SHAPE: return "unsupported shape";
+    case SBL_ERR_UNSUPPORTED: return "unsupported option";
+    case SBL_ERR_WORKSPACE: return "workspace missing or too small";
+    case SBL_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+SBL_API const char* sbl_last_error(void) { return g_last_error; }
+
+SBL_API size_t sbl_quant_mask_pack_workspace_size(int64_t d_out, int64_t d_in) {
+  if (check_dims(d_out, d_in) != SBL_OK) return 0;
+  return quant_workspace_bytes(d_out, d_in);
+}
+
+SBL_API int sbl_quant_mask_pack(const uint16_t* W_bf16, int64_t d_out, int64_t d_in, int n_keep, uint16_t* codes,
+                                uint8_t* mask, float* gamma, void* workspace, size_t workspace_bytes,
+                                void* hip_stream) {
+  int rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(n_keep == 2 || n_keep == 4 || n_keep == 6 || n_keep == 8, SBL_ERR_UNSUPPORTED,
+              "n_keep=%d: supported N:8 patterns are 2, 4, 6, 8", n_keep);
+  SBL_REQUIRE(W_bf16 && codes && gamma, SBL_ERR_INVALID_ARG, "W, codes and gamma must be non-NULL");
+  SBL_REQUIRE(aligned(W_bf16, 16) && aligned(codes, 16) && aligned(gamma, 4), SBL_ERR_INVALID_ARG,
+              "W and codes must be 16-byte aligned, gamma 4-byte aligned");
+  const size_t need = quant_workspace_bytes(d_out, d_in);
+  SBL_REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 16), SBL_ERR_WORKSPACE,
+              "workspace of %zu bytes (16-byte aligned) required, got %zu", need,
+              workspace ? workspace_bytes : (size_t)0);
+  hipError_t e = launch_quant_mask_pack(W_bf16, d_out, d_in, n_keep, codes, mask, gamma, workspace,
+                                        (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_quant_mask_pack launch");
+  return SBL_OK;
+}
+
+SBL_API int sbl_act_quant(const uint16_t* x_bf16, int64_t T, int64_t d_in, int8_t* x_q, float* absmax,
+                          void* hip_stream) {
+  int rc = check_tokens(T);
+  if (rc != SBL_OK) return rc;
+  rc = check_dims(1, d_in);
+  if (rc != SBL_OK) return rc;
+  if (T == 0) return SBL_OK;
+  SBL_REQUIRE(x_bf16 && x_q && absmax, SBL_ERR_INVALID_ARG, "x, x_q and absmax must be non-NULL");
+  SBL_REQUIRE(aligned(x_bf16, 16) && aligned(x_q, 16) && aligned(absmax, 4), SBL_ERR_INVALID_ARG,
+              "x and x_q must be 16-byte aligned, absmax 4-byte aligned");
+  SBL_REQUIRE(T * d_in <= SBL_MAX_WEIGHTS * 16, SBL_ERR_SHAPE, "T*d_in too large");
+  hipError_t e = launch_act_quant(x_bf16, T, d_in, x_q, absmax, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_act_quant launch");
+  return SBL_OK;
+}
+
+SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t* x_q, const float* absmax, int64_t T,
+                        int64_t d_in, int64_t d_out, void* y, int y_dtype, void* hip_stream) {
+  int rc = check_tokens(T);
+  if (rc != SBL_OK) return rc;
+  rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(y_dtype == SBL_F32 || y_dtype == SBL_BF16 || y_dtype == SBL_I32, SBL_ERR_INVALID_ARG,
+              "y_dtype=%d is not SBL_F32, SBL_BF16 or SBL_I32", y_dtype);
+  if (T == 0) return SBL_OK;
+  SBL_REQUIRE(codes && gamma && x_q && absmax && y, SBL_ERR_INVALID_ARG, "NULL pointer argument");
+  SBL_REQUIRE(aligned(codes, 16) && aligned(x_q, 16) && aligned(y, 16) && aligned(gamma, 4) && aligned(absmax, 4),
+              SBL_ERR_INVALID_ARG, "codes, x_q, y must be 16-byte aligned; gamma, absmax 4-byte aligned");
+  hipError_t e = launch_forward(codes, gamma, x_q, absmax, T, d_in, d_out, y, y_dtype, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_forward launch");
+  return SBL_OK;
+}
+
+SBL_API size_t sbl_backward_workspace_size(int64_t T, int64_t d_in, int64_t d_out, int flags) {
+  if (check_tokens(T) != SBL_OK || check_dims(d_out, d_in) != SBL_OK) return 0;
+  return backward_workspace_bytes(T, d_in, d_out, flags);
+}
+
+SBL_API int sbl_backward(const uint16_t* codes, const float* gamma, const int8_t* x_q, const float* absmax,
+                         const uint16_t* dY_bf16, int64_t T, int64_t d_in, int64_t d_out, void* dX, int dx_dtype,
+                         float* dW, int flags, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int rc = check_tokens(T);
+  if (rc != SBL_OK) return rc;
+  rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(flags >= 1 && flags <= (SBL_BWD_DX | SBL_BWD_DW), SBL_ERR_INVALID_ARG,
+              "flags=%d must be a non-empty combination of SBL_BWD_DX and SBL_BWD_DW", flags);
+  if (flags & SBL_BWD_DX) {
+    SBL_REQUIRE(dx_dtype == SBL_F32 || dx_dtype == SBL_BF16, SBL_ERR_INVALID_ARG,
+                "dx_dtype=%d is not SBL_F32 or SBL_BF16", dx_dtype);
+    if (T > 0) {
+      SBL_REQUIRE(dX && codes && gamma && dY_bf16, SBL_ERR_INVALID_ARG, "dX, codes, gamma, dY must be non-NULL");
+      SBL_REQUIRE(aligned(dX, 16) && aligned(codes, 16) && aligned(dY_bf16, 16) && aligned(gamma, 4),
+                  SBL_ERR_INVALID_ARG, "dX, codes, dY must be 16-byte aligned; gamma 4-byte aligned");
+    }
+  }
+  if (flags & SBL_BWD_DW) {
+    SBL_REQUIRE(dW && aligned(dW, 16), SBL_ERR_INVALID_ARG, "dW must be non-NULL and 16-byte aligned");
+    if (T > 0) {
+      SBL_REQUIRE(x_q && absmax && dY_bf16, SBL_ERR_INVALID_ARG, "x_q, absmax, dY must be non-NULL");
+      SBL_REQUIRE(aligned(x_q, 16) && aligned(absmax, 4) && aligned(dY_bf16, 16), SBL_ERR_INVALID_ARG,
+                  "x_q, dY must be 16-byte aligned; absmax 4-byte aligned");
+    }
+  }
+  const size_t need = backward_workspace_bytes(T, d_in, d_out, flags);
+  if (need > 0) {
+    SBL_REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 16), SBL_ERR_WORKSPACE,
+                "workspace of %zu bytes (16-byte aligned) required, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  }
+  if (T == 0 && !(flags & SBL_BWD_DW)) return SBL_OK;
+  hipError_t e = launch_backward(codes, gamma, x_q, absmax, dY_bf16, T, d_in, d_out, dX, dx_dtype, dW, flags,
+                                 workspace, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_backward launch");
+  return SBL_OK;
+}
+
+SBL_API int sbl_test_round_mean(const uint32_t* S_words, int n_words, int64_t count, float* out) {
+  SBL_REQUIRE(S_words && out && n_words >= 1 && n_words <= 10, SBL_ERR_INVALID_ARG, "bad arguments");
+  SBL_REQUIRE(count >= 1 && count <= SBL_MAX_WEIGHTS, SBL_ERR_SHAPE, "count outside [1, 2^36]");
+  uint32_t w[10] = {0};
+  for (int i = 0; i < n_words; ++i) w[i] = S_words[i];
+  *out = round_mean_words(w, 10, (unsigned long long)count);
+  return SBL_OK;
+}
+
+}  // extern "C"

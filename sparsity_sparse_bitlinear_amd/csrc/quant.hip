@@ -1,0 +1,326 @@
+// Weight side of Sparse-BitLinear on gfx950: gamma = mean|W| (exact), the N:8
+// top-N mask on |W|, ternary codes and the packed planes.
+//
+// [SUM] 前置知识 > 1.58-bit BitNet 量化 defines gamma = ||W||_1 / (d_out d_in)
+// and W_q = RoundClip(W/gamma, -1, 1); 前置知识 > 半结构化 N:M 稀疏 defines the
+// N-of-M group mask; 核心方法 (i)-(iii) computes the mask from |W| of the
+// master weight and applies it after quantization ([GIST] 2.2 likewise).
+//
+// Three launches, all on the caller's stream:
+//   k_absum          pass 1 over W: exact integer partial sums of |W| per block
+//   k_gamma_finalize one block: exact total, one correctly rounded division
+//   k_mask_quant_pack pass 2 over W: per 8-group sorting network -> keep bits,
+//                     threshold |w| > gamma/2 -> 2-bit codes, write both planes
+#include "sbl_internal.h"
+
+namespace sbl {
+
+// ---------------------------------------------------------------------------
+// Exact rounding of the mean (host and device).
+// ---------------------------------------------------------------------------
+
+// S = sum of nwords little-endian 32-bit words, in units of 2^-133.
+// Returns the binary32 value nearest to S * 2^-133 / count (ties to even).
+// Requires 1 <= count < 2^37 so that the 64-bit quotient below keeps at least
+// 27 significant bits.
+__host__ __device__ float round_mean_words(const uint32_t* w, int nwords, unsigned long long count) {
+  int top = -1;
+  for (int i = nwords - 1; i >= 0; --i) {
+    if (w[i]) { top = i; break; }
+  }
+  if (top < 0) return 0.0f;
+  const int p = top * 32 + 31 - __builtin_clz(w[top]);  // position of the leading one
+  // M = bits [p-63, p] of S (left-aligned 64-bit window), sticky = any lower bit.
+  unsigned long long M = 0;
+  bool sticky = false;
+  for (int b = 0; b < 64; ++b) {
+    const int pos = p - 63 + b;
+    unsigned long long bit = 0;
+    if (pos >= 0) bit = (w[pos >> 5] >> (pos & 31)) & 1u;
+    M |= bit << b;
+  }
+  for (int pos = 0; pos < p - 63; ++pos) {
+    if ((w[pos >> 5] >> (pos & 31)) & 1u) { sticky = true; break; }
+  }
+  // value = (M + f) * 2^(p - 63 - 133) / count, f in [0, 1) (f > 0 iff sticky)
+  const unsigned long long Q = M / count;
+  const unsigned long long R = M % count;
+  sticky = sticky || (R != 0);
+  const int base_exp = p - 63 - 133;  // value = (Q + frac) * 2^base_exp, frac in [0,1)
+  const int qb = 64 - __builtin_clzll(Q);
+  const int e_top = qb - 1 + base_exp;
+  int shift = (e_top >= -126) ? (qb - 24) : (-149 - base_exp);
+  if (shift > 64) return 0.0f;  // below half of the smallest subnormal
+  unsigned long long kept, rem, half;
+  if (shift == 64) {
+    kept = 0; rem = Q; half = 1ull << 63;
+  } else {
+    kept = Q >> shift;
+    rem = Q & ((1ull << shift) - 1);
+    half = 1ull << (shift - 1);
+  }
+  if (rem > half || (rem == half && (sticky || (kept & 1)))) kept += 1;
+  return ldexpf((float)kept, shift + base_exp);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: exact partial sums of |W|.
+// ---------------------------------------------------------------------------
+
+struct U128 {
+  unsigned long long lo, hi;
+};
+
+__device__ __forceinline__ void add128(U128& a, const U128& b) {
+  const unsigned long long lo = a.lo + b.lo;
+  a.hi += b.hi + (lo < a.lo ? 1ull : 0ull);
+  a.lo = lo;
+}
+
+__device__ __forceinline__ void absum_half(uint32_t h, U128& acc, unsigned long long* hist, bool& any_hist) {
+  const uint32_t mag = h & 0x7FFFu;
+  const uint32_t e = mag >> 7;
+  const uint32_t sig = (mag & 0x7Fu) | (e ? 0x80u : 0u);
+  const uint32_t ee = e ? e : 1u;
+  const uint32_t off = ee - (uint32_t)kWinLo;  // wraps for ee < kWinLo
+  const bool in = off <= (uint32_t)(kWinHi - kWinLo);
+  const unsigned long long v = (unsigned long long)(in ? sig : 0u) << (in ? off : 0u);
+  const unsigned long long lo = acc.lo + v;
+  acc.hi += (lo < acc.lo) ? 1ull : 0ull;
+  acc.lo = lo;
+  if (__builtin_expect(!in && sig != 0u, 0)) {
+    atomicAdd(&hist[ee], (unsigned long long)sig);
+    any_hist = true;
+  }
+}
+
+__global__ __launch_bounds__(kAbsumThreads) void k_absum(const uint4* __restrict__ W, int64_t n_vec8,
+                                                         AbsumPartial* __restrict__ part,
+                                                         unsigned long long* __restrict__ hist_out) {
+  __shared__ unsigned long long hist[256];
+  __shared__ U128 red[kAbsumThreads];
+  __shared__ int block_any;
+  const int tid = threadIdx.x;
+  hist[tid] = 0;
+  if (tid == 0) block_any = 0;
+  __syncthreads();
+
+  U128 acc = {0, 0};
+  bool any_hist = false;
+  const int64_t stride = (int64_t)gridDim.x * kAbsumThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kAbsumThreads + tid; i < n_vec8; i += stride) {
+    const uint4 v = W[i];
+    absum_half(v.x & 0xFFFFu, acc, hist, any_hist);
+    absum_half(v.x >> 16, acc, hist, any_hist);
+    absum_half(v.y & 0xFFFFu, acc, hist, any_hist);
+    absum_half(v.y >> 16, acc, hist, any_hist);
+    absum_half(v.z & 0xFFFFu, acc, hist, any_hist);
+    absum_half(v.z >> 16, acc, hist, any_hist);
+    absum_half(v.w & 0xFFFFu, acc, hist, any_hist);
+    absum_half(v.w >> 16, acc, hist, any_hist);
+  }
+  if (any_hist) block_any = 1;  // benign race: every writer stores 1
+  red[tid] = acc;
+  __syncthreads();
+  for (int s = kAbsumThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) {
+      U128 a = red[tid];
+      add128(a, red[tid + s]);
+      red[tid] = a;
+    }
+    __syncthreads();
+  }
+  const int any = block_any;
+  if (tid == 0) {
+    AbsumPartial p;
+    p.lo = red[0].lo;
+    p.hi = red[0].hi;
+    p.flag = (unsigned long long)any;
+    p.pad = 0;
+    part[blockIdx.x] = p;
+  }
+  if (any) hist_out[(size_t)blockIdx.x * 256 + tid] = hist[tid];
+}
+
+// Adds v * 2^shift into the little-endian word array w[0..nw).
+__device__ void add_shifted(uint32_t* w, int nw, unsigned long long v, int shift) {
+  if (!v) return;
+  int q = shift >> 5;
+  const int r = shift & 31;
+  uint32_t parts[3];
+  parts[0] = (uint32_t)(v << r);
+  parts[1] = (uint32_t)(r ? (v >> (32 - r)) : (v >> 32));
+  parts[2] = (uint32_t)(r ? (v >> (64 - r)) : 0ull);
+  unsigned long long carry = 0;
+  for (int k = 0; q + k < nw; ++k) {
+    const unsigned long long s = (unsigned long long)w[q + k] + (k < 3 ? parts[k] : 0u) + carry;
+    w[q + k] = (uint32_t)s;
+    carry = s >> 32;
+    if (k >= 2 && carry == 0) break;
+  }
+}
+
+constexpr int kSumWords = 10;  // 320 bits: enough for any finite bf16 matrix below 2^40 weights
+
+__global__ __launch_bounds__(256) void k_gamma_finalize(const AbsumPartial* __restrict__ part,
+                                                        const unsigned long long* __restrict__ hist_in,
+                                                        int nblocks, unsigned long long count,
+                                                        float* __restrict__ gamma) {
+  __shared__ U128 red[256];
+  __shared__ unsigned long long bins[256];
+  __shared__ int any_flag;
+  const int tid = threadIdx.x;
+  if (tid == 0) any_flag = 0;
+  __syncthreads();
+  U128 acc = {0, 0};
+  int any = 0;
+  for (int b = tid; b < nblocks; b += 256) {
+    const AbsumPartial p = part[b];
+    U128 v = {p.lo, p.hi};
+    add128(acc, v);
+    any |= (p.flag != 0);
+  }
+  if (any) any_flag = 1;
+  red[tid] = acc;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) {
+      U128 a = red[tid];
+      add128(a, red[tid + s]);
+      red[tid] = a;
+    }
+    __syncthreads();
+  }
+  unsigned long long bin = 0;
+  if (any_flag) {
+    for (int b = 0; b < nblocks; ++b) {
+      if (part[b].flag) bin += hist_in[(size_t)b * 256 + tid];
+    }
+  }
+  bins[tid] = bin;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t w[kSumWords];
+    for (int i = 0; i < kSumWords; ++i) w[i] = 0;
+    // fast window: units of 2^(kWinLo - 134) = 2^(kWinLo - 1) * 2^-133
+    add_shifted(w, kSumWords, red[0].lo, kWinLo - 1);
+    add_shifted(w, kSumWords, red[0].hi, kWinLo - 1 + 64);
+    // histogram bin e (biased exponent, >= 1): units of 2^(e - 134) = 2^(e - 1) * 2^-133
+    for (int e = 1; e < 255; ++e) add_shifted(w, kSumWords, bins[e], e - 1);
+    *gamma = round_mean_words(w, kSumWords, count);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: mask, ternary codes, packing.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void cswap_desc(uint32_t& a, uint32_t& b) {
+  const uint32_t hi = max(a, b), lo = min(a, b);
+  a = hi;
+  b = lo;
+}
+
+// One group of 8 bf16 values (4 words).  Rank keys u_j = (|w_j| bits << 3) | (7 - j)
+// are distinct and order slots by magnitude, lower index first on ties; an
+// optimal 19-comparator network sorts them and the N-th largest is the
+// keep threshold.
+// |w| > gamma/2  <=>  2|w| > gamma.  Both sides are non-negative binary32
+// values, compared through their bit patterns (monotone for non-negative
+// floats), so no floating-point mode (denormal flushing) can change the
+// decision.  Doubling a magnitude in bit form: add one to the exponent of a
+// normal value (values near the top become inf/NaN patterns, which still
+// compare above every finite gamma), shift a subnormal left by one.
+__device__ __forceinline__ bool above_half_gamma(uint32_t mag16, uint32_t gamma_bits) {
+  const uint32_t b = mag16 << 16;
+  const uint32_t twice = (b & 0x7F800000u) ? (b + 0x00800000u) : (b << 1);
+  return twice > gamma_bits;
+}
+
+template <int N>
+__device__ __forceinline__ void pack_group(const uint4 v, uint32_t gamma_bits, uint16_t& code_out,
+                                           uint8_t& mask_out) {
+  uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                   v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+  uint32_t u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) u[j] = ((h[j] & 0x7FFFu) << 3) | (uint32_t)(7 - j);
+  uint32_t thr = 0;
+  if constexpr (N < 8) {
+    uint32_t s[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] = u[j];
+    cswap_desc(s[0], s[2]); cswap_desc(s[1], s[3]); cswap_desc(s[4], s[6]); cswap_desc(s[5], s[7]);
+    cswap_desc(s[0], s[4]); cswap_desc(s[1], s[5]); cswap_desc(s[2], s[6]); cswap_desc(s[3], s[7]);
+    cswap_desc(s[0], s[1]); cswap_desc(s[2], s[3]); cswap_desc(s[4], s[5]); cswap_desc(s[6], s[7]);
+    cswap_desc(s[2], s[4]); cswap_desc(s[3], s[5]);
+    cswap_desc(s[1], s[4]); cswap_desc(s[3], s[6]);
+    cswap_desc(s[1], s[2]); cswap_desc(s[3], s[4]); cswap_desc(s[5], s[6]);
+    thr = s[N - 1];
+  }
+  uint32_t code = 0, mask = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bool keep = (N == 8) || (u[j] >= thr);
+    const bool nz = above_half_gamma(h[j] & 0x7FFFu, gamma_bits);
+    const uint32_t c = (keep && nz) ? ((h[j] & 0x8000u) ? 3u : 1u) : 0u;
+    code |= c << (2 * j);
+    mask |= (keep ? 1u : 0u) << j;
+  }
+  code_out = (uint16_t)code;
+  mask_out = (uint8_t)mask;
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void k_mask_quant_pack(const uint4* __restrict__ W, int64_t n_groups,
+                                                         const float* __restrict__ gamma_p,
+                                                         uint16_t* __restrict__ codes, uint8_t* __restrict__ mask) {
+  const uint32_t gamma_bits = __float_as_uint(*gamma_p);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n_groups; g += stride) {
+    uint16_t c;
+    uint8_t m;
+    pack_group<N>(W[g], gamma_bits, c, m);
+    codes[g] = c;
+    if (mask) mask[g] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+int absum_blocks(int64_t n_vec8) {
+  int64_t b = (n_vec8 + kAbsumThreads - 1) / kAbsumThreads;
+  if (b < 1) b = 1;
+  if (b > kAbsumMaxBlocks) b = kAbsumMaxBlocks;
+  return (int)b;
+}
+
+size_t quant_workspace_bytes(int64_t d_out, int64_t d_in) {
+  const int nb = absum_blocks(d_out * d_in / 8);
+  return (size_t)nb * sizeof(AbsumPartial) + (size_t)nb * 256 * sizeof(unsigned long long);
+}
+
+hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int n_keep, uint16_t* codes,
+                                  uint8_t* mask, float* gamma, void* ws, hipStream_t s) {
+  const int64_t n_groups = d_out * d_in / 8;
+  const int nb = absum_blocks(n_groups);
+  AbsumPartial* part = (AbsumPartial*)ws;
+  unsigned long long* hist = (unsigned long long*)((char*)ws + (size_t)nb * sizeof(AbsumPartial));
+  hipLaunchKernelGGL(k_absum, dim3(nb), dim3(kAbsumThreads), 0, s, (const uint4*)W, n_groups, part, hist);
+  hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(256), 0, s, (const AbsumPartial*)part,
+                     (const unsigned long long*)hist, nb, (unsigned long long)(d_out * d_in), gamma);
+  int64_t pb = (n_groups + 255) / 256;
+  if (pb > 65536) pb = 65536;
+  const dim3 grid((unsigned)pb), block(256);
+  switch (n_keep) {
+    case 2: hipLaunchKernelGGL(k_mask_quant_pack<2>, grid, block, 0, s, (const uint4*)W, n_groups, gamma, codes, mask); break;
+    case 4: hipLaunchKernelGGL(k_mask_quant_pack<4>, grid, block, 0, s, (const uint4*)W, n_groups, gamma, codes, mask); break;
+    case 6: hipLaunchKernelGGL(k_mask_quant_pack<6>, grid, block, 0, s, (const uint4*)W, n_groups, gamma, codes, mask); break;
+    default: hipLaunchKernelGGL(k_mask_quant_pack<8>, grid, block, 0, s, (const uint4*)W, n_groups, gamma, codes, mask); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sbl

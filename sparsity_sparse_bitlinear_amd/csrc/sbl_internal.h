@@ -1,0 +1,73 @@
+// Internal declarations shared by the HIP translation units of libsbl.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sbl.h"
+
+namespace sbl {
+
+// ---------------------------------------------------------------------------
+// Vector types used for MFMA operands and 16-byte memory traffic.
+// ---------------------------------------------------------------------------
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+#define SBL_LDS __attribute__((address_space(3)))
+
+// Error reporting (thread-local detail text), implemented in api.hip.
+void set_error(const char* fmt, ...);
+int hip_fail(hipError_t e, const char* what);
+
+// ---------------------------------------------------------------------------
+// gamma: exact sum of |W| and its correctly rounded mean.
+// ---------------------------------------------------------------------------
+
+// Per-thread fast accumulation window: bf16 magnitudes with biased exponent
+// E in [kWinLo, kWinLo + 56] are accumulated as (significand << (E - kWinLo))
+// in units of 2^(kWinLo - 134); everything else that is non-zero goes to an
+// exact per-exponent histogram.
+constexpr int kWinLo = 80;
+constexpr int kWinHi = kWinLo + 56;
+
+// Partial results of one absum block (written to the workspace).
+struct AbsumPartial {
+  unsigned long long lo;    // 128-bit fast-window sum, low word
+  unsigned long long hi;    // high word
+  unsigned long long flag;  // non-zero iff the block has a histogram
+  unsigned long long pad;
+};
+
+constexpr int kAbsumThreads = 256;
+constexpr int kAbsumMaxBlocks = 1024;
+
+size_t quant_workspace_bytes(int64_t d_out, int64_t d_in);
+int absum_blocks(int64_t n_vec8);
+
+hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int n_keep, uint16_t* codes,
+                                  uint8_t* mask, float* gamma, void* ws, hipStream_t s);
+
+// Host/device: RN_float32(S * 2^-133 / count) for S given as 32-bit words.
+__host__ __device__ float round_mean_words(const uint32_t* w, int nwords, unsigned long long count);
+
+// ---------------------------------------------------------------------------
+// activations, forward, backward launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_act_quant(const uint16_t* x, int64_t T, int64_t d_in, int8_t* xq, float* absmax, hipStream_t s);
+
+hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
+                          int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s);
+
+size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flags);
+hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
+                           const uint16_t* dY, int64_t T, int64_t d_in, int64_t d_out, void* dX, int dx_dtype,
+                           float* dW, int flags, void* ws, hipStream_t s);
+
+}  // namespace sbl

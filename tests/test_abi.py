@@ -1,0 +1,131 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the
+header declares, rejects bad arguments before touching the GPU, and its exact
+gamma rounding (the device routine, compiled for the host) matches the oracle."""
+import ctypes
+import os
+import re
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sbl.h")
+
+sbl = pytest.importorskip("sparsity_sparse_bitlinear_amd", reason="libsbl.so not built")
+lib = sbl.lib
+
+OK, INVALID, SHAPE, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3, -4
+P = ctypes.c_void_p(0x10000)        # a fake, aligned, non-NULL address (never dereferenced)
+P_MIS = ctypes.c_void_p(0x10002)    # misaligned
+NULL = ctypes.c_void_p(0)
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SBL_API\s+[\w\s\*]+?\b(sbl_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_symbols()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    for n in ("sbl_quant_mask_pack", "sbl_act_quant", "sbl_forward", "sbl_backward"):
+        assert n in names
+
+
+def test_status_strings():
+    assert lib.sbl_status_string(0) == b"ok"
+    for code in (INVALID, SHAPE, UNSUPPORTED, WORKSPACE, -5):
+        assert lib.sbl_status_string(code) not in (b"ok", b"unknown status")
+    assert lib.sbl_version().startswith(b"sbl")
+
+
+def test_quant_mask_pack_validation():
+    ws = lib.sbl_quant_mask_pack_workspace_size(256, 256)
+    assert ws > 0
+    assert lib.sbl_quant_mask_pack_workspace_size(256, 12) == 0
+    f = lib.sbl_quant_mask_pack
+    assert f(P, 256, 12, 6, P, P, P, P, ws, NULL) == SHAPE          # d_in not a multiple of 8
+    assert f(P, 256, 0, 6, P, P, P, P, ws, NULL) == SHAPE
+    assert f(P, 0, 256, 6, P, P, P, P, ws, NULL) == SHAPE
+    assert f(P, 256, 256, 5, P, P, P, P, ws, NULL) == UNSUPPORTED   # 5:8 not built
+    assert f(NULL, 256, 256, 6, P, P, P, P, ws, NULL) == INVALID
+    assert f(P, 256, 256, 6, NULL, P, P, P, ws, NULL) == INVALID
+    assert f(P, 256, 256, 6, P, P, NULL, P, ws, NULL) == INVALID
+    assert f(P_MIS, 256, 256, 6, P, P, P, P, ws, NULL) == INVALID
+    assert f(P, 256, 256, 6, P, P, P, P, ws - 1, NULL) == WORKSPACE
+    assert f(P, 256, 256, 6, P, P, P, NULL, ws, NULL) == WORKSPACE
+    assert b"workspace" in lib.sbl_last_error()
+    assert f(P, 1 << 20, 1 << 20, 6, P, P, P, P, ws, NULL) == SHAPE  # above the weight limit
+
+
+def test_act_quant_validation():
+    f = lib.sbl_act_quant
+    assert f(NULL, 0, 256, NULL, NULL, NULL) == OK                   # T = 0 is a no-op
+    assert f(P, -1, 256, P, P, NULL) == SHAPE
+    assert f(P, 4, 100, P, P, NULL) == SHAPE
+    assert f(NULL, 4, 256, P, P, NULL) == INVALID
+    assert f(P, 4, 256, P_MIS, P, NULL) == INVALID
+
+
+def test_forward_validation():
+    f = lib.sbl_forward
+    assert f(NULL, NULL, NULL, NULL, 0, 256, 256, NULL, 0, NULL) == OK
+    assert f(P, P, P, P, 4, 256, 256, P, 7, NULL) == INVALID          # bad dtype
+    assert f(P, P, P, P, 4, 250, 256, P, 0, NULL) == SHAPE
+    assert f(P, P, NULL, P, 4, 256, 256, P, 0, NULL) == INVALID
+    assert f(P, P, P, P, 4, 256, 256, P_MIS, 0, NULL) == INVALID
+
+
+def test_backward_validation():
+    f = lib.sbl_backward
+    assert lib.sbl_backward_workspace_size(64, 256, 256, 1) == 0     # dX needs no workspace
+    assert f(P, P, P, P, P, 4, 256, 256, P, 1, P, 0, NULL, 0, NULL) == INVALID   # no flags
+    assert f(P, P, P, P, P, 4, 256, 256, P, 2, P, 4, NULL, 0, NULL) == INVALID   # unknown flag
+    assert f(P, P, P, P, P, 4, 256, 256, P, 2, P, 1, NULL, 0, NULL) == INVALID   # I32 dX
+    assert f(P, P, P, P, P, 4, 256, 256, NULL, 1, P, 1, NULL, 0, NULL) == INVALID
+    assert f(P, P, P, P, P, 4, 256, 256, P, 1, NULL, 2, NULL, 0, NULL) == INVALID
+    # a shape that needs split-K workspace
+    need = lib.sbl_backward_workspace_size(32768, 2048, 256, 2)
+    assert need > 0
+    assert f(P, P, P, P, P, 32768, 2048, 256, P, 1, P, 2, NULL, 0, NULL) == WORKSPACE
+    assert f(P, P, P, P, P, 32768, 2048, 256, P, 1, P, 2, P, need - 16, NULL) == WORKSPACE
+    assert f(NULL, NULL, NULL, NULL, NULL, 0, 256, 256, NULL, 1, NULL, 1, NULL, 0, NULL) == OK
+
+
+def _round_mean_lib(S: int, count: int) -> float:
+    words = (ctypes.c_uint32 * 10)(*[(S >> (32 * i)) & 0xFFFFFFFF for i in range(10)])
+    out = ctypes.c_float()
+    assert lib.sbl_test_round_mean(words, 10, count, ctypes.byref(out)) == OK
+    return out.value
+
+
+def test_gamma_rounding_routine_matches_oracle():
+    g = np.random.default_rng(21)
+    cases = []
+    for _ in range(3000):
+        count = int(g.integers(1, 1 << 36))
+        bits = int(g.integers(1, 300))
+        S = int(g.integers(0, 1 << 62)) << max(0, bits - 62) | int(g.integers(0, 1 << 20))
+        S &= (1 << 300) - 1
+        cases.append((S, count))
+    # subnormal results, ties, exact values
+    for count in (1, 3, 8, 65536, 12345, (1 << 36) - 1):
+        for S in (1, 2, 3, 7, 1 << 23, (1 << 24) + 1, 3 << 130, (1 << 40) - 1, 123456789 << 200):
+            cases.append((S, count))
+    for S, count in cases:
+        want = oracle.round_rational_to_f32(S, count << 133)
+        got = _round_mean_lib(S, count)
+        assert np.float32(got) == np.float32(want), (S, count, got, want)
+
+
+def test_gamma_rounding_routine_on_real_sums():
+    from sbl_inputs import weight
+    for i, (d_out, d_in) in enumerate(((256, 256), (17, 24), (1536, 1536))):
+        W = weight(5, i, d_out, d_in)
+        S = oracle.abs_sum_exact(W)
+        assert np.float32(_round_mean_lib(S, W.size)) == oracle.gamma_f32(W)

@@ -1,0 +1,264 @@
+"""GPU parity of every step against the CPU oracle, on seeded inputs.
+
+Bit-exact: gamma bits, code plane, mask plane, x_q, absmax bits, int32
+accumulators.  Float: y within 1e-5 relative; dX and dW within 2e-2 of the
+float64 oracle (per-row L2 and elementwise against max|ref|).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sbl_inputs import (activation, boundary_row_weight, f32_to_bf16_bits, grad_out, sample_rows,
+                        tie_heavy_weight, weight)
+
+from gpu_util import assert_grad_close, assert_y_close, bf16_to_f64, bits16, f32_bits, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+sbl = pytest.importorskip("sparsity_sparse_bitlinear_amd")
+
+
+def gpu_pack(W_bits, n):
+    codes, mask, gamma = sbl.quant_mask_pack(to_dev_bf16(W_bits), n)
+    torch.cuda.synchronize()
+    return bits16(codes), mask.cpu().numpy(), gamma.cpu().numpy()[0]
+
+
+def check_pack(W_bits, n):
+    codes, mask, g = gpu_pack(W_bits, n)
+    rc, rm, rg = oracle.quant_mask_pack(W_bits, n)
+    assert f32_bits(g) == f32_bits(rg), (float(g), float(rg))
+    np.testing.assert_array_equal(mask, rm)
+    np.testing.assert_array_equal(codes, rc)
+
+
+# ---------------------------------------------------------------------------
+# quant / mask / pack
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [2, 4, 6, 8])
+@pytest.mark.parametrize("shape", [(256, 256), (1, 8), (3, 24), (40, 64), (333, 72), (517, 1032)])
+def test_pack_parity_gaussian(shape, n):
+    check_pack(weight(11, shape[0] * 7 + shape[1], *shape), n)
+
+
+@pytest.mark.parametrize("n", [2, 4, 6, 8])
+def test_pack_parity_tie_heavy(n):
+    check_pack(tie_heavy_weight(1, 96, 256), n)
+    check_pack(tie_heavy_weight(2, 64, 64, alphabet=(-1, 1), scale=0.5), n)
+
+
+def test_pack_boundary_rows():
+    W = boundary_row_weight(24, 64)     # gamma = 1 exactly; |w| = 0.5 sits on the threshold
+    check_pack(W, 8)
+    check_pack(W, 6)
+
+
+def test_pack_all_zero_and_signed_zero():
+    W = np.zeros((16, 64), np.uint16)
+    W[::2, 1::3] = 0x8000
+    check_pack(W, 6)
+    check_pack(W, 8)
+
+
+def test_pack_extreme_magnitudes():
+    # huge (>= 1024) and tiny (< 2^-47) values and bf16 subnormals take the exact
+    # per-exponent path of the gamma reduction
+    g = np.random.default_rng(5)
+    base = g.standard_normal((64, 256)).astype(np.float32) * 0.02
+    base[g.random(base.shape) < 0.01] *= 1e30
+    base[g.random(base.shape) < 0.01] *= 1e-30
+    W = f32_to_bf16_bits(base)
+    sub = g.random(W.shape) < 0.01
+    W[sub] = g.integers(1, 0x80, size=int(sub.sum())).astype(np.uint16)  # bf16 subnormals
+    for n in (2, 6, 8):
+        check_pack(W, n)
+    tiny = f32_to_bf16_bits(np.full((8, 64), 3e-38, np.float32))      # gamma in the subnormal-adjacent range
+    check_pack(tiny, 6)
+    maxv = np.full((4, 64), 0x7F7F, np.uint16)                          # largest finite bf16
+    check_pack(maxv, 6)
+
+
+def test_pack_large_matrix():
+    check_pack(weight(3, 4, 11008, 2048), 6)
+
+
+# ---------------------------------------------------------------------------
+# activation quantization
+# ---------------------------------------------------------------------------
+
+def check_act(x_bits):
+    xq, a = sbl.act_quant(to_dev_bf16(x_bits))
+    torch.cuda.synchronize()
+    rq, ra = oracle.act_quant(x_bits)
+    np.testing.assert_array_equal(f32_bits(a.cpu().numpy()), f32_bits(ra))
+    np.testing.assert_array_equal(xq.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("shape,dist,outl", [((64, 256), "normal", 0.0), ((513, 896), "normal", 0.001),
+                                             ((7, 8), "normal", 0.0), ((3, 11008), "student_t4", 0.0),
+                                             ((300, 2048), "student_t4", 0.0), ((5, 16392), "normal", 0.0),
+                                             ((2, 40008), "normal", 0.0)])
+def test_act_parity(shape, dist, outl):
+    check_act(activation(21, shape[1], *shape, dist=dist, outlier_frac=outl))
+
+
+def test_act_edge_rows():
+    g = np.random.default_rng(9)
+    x = f32_to_bf16_bits(g.standard_normal((8, 136)).astype(np.float32))
+    x[0] = 0                                   # zero row
+    x[1] = 0x8000                              # -0.0 row
+    x[2] = 0
+    x[2, 17] = 0xBF80                          # single -1.0
+    x[3] = g.integers(0, 0x80, size=136).astype(np.uint16)                 # subnormal row
+    x[4] = f32_to_bf16_bits((g.standard_normal(136) * 1e38).astype(np.float32))   # near FLT_MAX
+    x[5] = f32_to_bf16_bits(np.array([1.984375] + [(2 * k + 1) / 128.0 for k in range(135)], np.float32))  # exact ties
+    check_act(x)
+    check_act(x[:0])
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+def gpu_forward(W_bits, x_bits, n, out_dtype):
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W_bits), n)
+    xq, a = sbl.act_quant(to_dev_bf16(x_bits))
+    y = sbl.forward(codes, gamma, xq, a, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return y
+
+
+def ref_forward(W_bits, x_bits, n, rows=None):
+    w_eff, _, g = oracle.effective_weight(W_bits, n)
+    xs = x_bits if rows is None else x_bits[rows]
+    xq, a = oracle.act_quant(xs)
+    acc = oracle.forward_acc(w_eff, xq)
+    return acc, oracle.forward_y(acc, g, a)
+
+
+FWD_SHAPES = [(64, 256, 256), (77, 200, 328), (1, 8, 8), (130, 136, 136), (513, 4864, 896), (33, 40, 1032)]
+
+
+@pytest.mark.parametrize("n", [6, 2, 8, 4])
+@pytest.mark.parametrize("T,d_out,d_in", FWD_SHAPES)
+def test_forward_parity(T, d_out, d_in, n):
+    W = weight(31, d_out + d_in, d_out, d_in)
+    x = activation(31, d_out + d_in + T, T, d_in, dist="student_t4")
+    acc_ref, y_ref = ref_forward(W, x, n)
+    acc = gpu_forward(W, x, n, sbl.I32).cpu().numpy()
+    np.testing.assert_array_equal(acc, acc_ref)
+    y = gpu_forward(W, x, n, sbl.F32).cpu().numpy()
+    assert_y_close(y, y_ref, acc_ref)
+    yb = gpu_forward(W, x, n, sbl.BF16).float().cpu().numpy()
+    assert np.all(np.abs(yb - y_ref) <= 2.0 ** -8 * np.abs(y_ref) + 1e-30)
+
+
+def test_forward_large_tiles_sampled():
+    # big enough for the 256 x 256 tile path; compare 96 sampled tokens exactly
+    T, d_out, d_in = 4096, 8192, 520          # d_in % 16 == 8 and d_in/8 % 8 != 0: unaligned loaders
+    W = weight(41, 0, d_out, d_in)
+    x = activation(41, 1, T, d_in)
+    rows = sample_rows(41, 2, T, 96)
+    acc = gpu_forward(W, x, 6, sbl.I32)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    acc_ref, y_ref = ref_forward(W, x, 6, rows)
+    np.testing.assert_array_equal(acc, acc_ref)
+    y = gpu_forward(W, x, 6, sbl.F32)[torch.from_numpy(rows).cuda()].cpu().numpy()
+    assert_y_close(y, y_ref, acc_ref)
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def gpu_backward(W_bits, x_bits, dY_bits, n, dx_dtype=1):
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W_bits), n)
+    xq, a = sbl.act_quant(to_dev_bf16(x_bits))
+    dX, dW = sbl.backward(codes, gamma, xq, a, to_dev_bf16(dY_bits), dx_dtype=dx_dtype)
+    torch.cuda.synchronize()
+    return dX, dW
+
+
+BWD_SHAPES = [(64, 256, 256), (77, 200, 328), (513, 136, 72), (1, 8, 8), (300, 40, 1032), (4096, 256, 2048)]
+
+
+@pytest.mark.parametrize("T,d_out,d_in", BWD_SHAPES)
+def test_backward_parity(T, d_out, d_in):
+    W = weight(51, d_out + d_in, d_out, d_in)
+    x = activation(51, d_out + d_in + T, T, d_in, dist="student_t4")
+    dY = grad_out(51, d_out + d_in + T, T, d_out)
+    r = oracle.sparse_bitlinear_step(W, x, dY, 6)
+    dX, dW = gpu_backward(W, x, dY, 6)
+    assert_grad_close(bf16_to_f64(dX), r["dX"])
+    assert_grad_close(dW.cpu().numpy(), r["dW"])
+    dX32, _ = gpu_backward(W, x, dY, 6, dx_dtype=0)
+    assert_grad_close(dX32.cpu().numpy().astype(np.float64), r["dX"], tol=2e-3)
+    # Dual STE: masked positions receive their (non-zero) dense gradient
+    masked = ~r["mask"]
+    if masked.any():
+        assert np.count_nonzero(dW.cpu().numpy()[masked]) > 0.99 * masked.sum()
+
+
+def test_backward_dx_large_tiles_sampled():
+    T, d_out, d_in = 4096, 264, 8192
+    W = weight(61, 0, d_out, d_in)
+    x = activation(61, 1, T, d_in)
+    dY = grad_out(61, 2, T, d_out)
+    rows = sample_rows(61, 3, T, 64)
+    dX, dW = gpu_backward(W, x, dY, 6)
+    w_eff, _, g = oracle.effective_weight(W, 6)
+    xq, a = oracle.act_quant(x)
+    dX_ref, _ = oracle.backward(dY[rows], w_eff, g, xq[rows], a[rows])
+    assert_grad_close(bf16_to_f64(dX)[rows], dX_ref)
+    cols = sample_rows(61, 4, d_out, 32)       # sampled rows o of dW over all T
+    dW_ref = oracle.bf16_to_f64(dY[:, cols]).T @ oracle.dequant_act(xq, a)
+    assert_grad_close(dW.cpu().numpy()[cols], dW_ref)
+
+
+def test_backward_zero_tokens():
+    W = weight(71, 0, 64, 64)
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+    xq = torch.empty((0, 64), dtype=torch.int8, device="cuda")
+    a = torch.empty((0,), dtype=torch.float32, device="cuda")
+    dY = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    dW = torch.full((64, 64), 7.0, device="cuda")
+    dX, dW = sbl.backward(codes, gamma, xq, a, dY, dW=dW)
+    torch.cuda.synchronize()
+    assert dX.shape == (0, 64) and torch.all(dW == 0)
+    y = sbl.forward(codes, gamma, xq, a)
+    assert y.shape == (0, 64)
+
+
+# ---------------------------------------------------------------------------
+# whole step, determinism, autograd wrapper
+# ---------------------------------------------------------------------------
+
+def test_step_bitwise_deterministic():
+    W = weight(81, 0, 512, 1024)
+    x = activation(81, 1, 1000, 1024, dist="student_t4")
+    dY = grad_out(81, 2, 1000, 512)
+    outs = []
+    for _ in range(2):
+        codes, mask, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+        xq, a = sbl.act_quant(to_dev_bf16(x))
+        y = sbl.forward(codes, gamma, xq, a)
+        dX, dW = sbl.backward(codes, gamma, xq, a, to_dev_bf16(dY))
+        torch.cuda.synchronize()
+        outs.append([t.cpu() for t in (codes, mask, gamma, xq, a, y, dX.view(torch.int16), dW)])
+    for u, v in zip(*outs):
+        assert torch.equal(u, v)
+
+
+def test_autograd_function_matches_oracle():
+    W = weight(91, 0, 96, 128)
+    x = activation(91, 1, 40, 128)
+    dY = grad_out(91, 2, 40, 96)
+    xt = to_dev_bf16(x).requires_grad_(True)
+    Wt = to_dev_bf16(W).requires_grad_(True)
+    y = sbl.sparse_bitlinear(xt, Wt, 6)
+    y.backward(to_dev_bf16(dY).float())
+    r = oracle.sparse_bitlinear_step(W, x, dY, 6)
+    assert_y_close(y.detach().cpu().numpy(), r["y"], r["acc"])
+    assert_grad_close(bf16_to_f64(xt.grad), r["dX"])
+    assert_grad_close(Wt.grad.float().cpu().numpy().astype(np.float64), r["dW"], tol=2e-2)
