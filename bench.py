@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Sparse-BitLinear 6:8 forward + Dual-STE backward throughput on one MI355X.
+
+Workload (default): the 3B-like decoder-layer linears q/o 2048->2048, k/v
+2048->256, gate/up 2048->11008, down 11008->2048, 16 x 2048 = 32768 tokens,
+bf16 master weights ~ N(0, 0.02), Student-t(4) activations, dY ~ N(0, 1),
+all seeded synthetic data already resident in HBM.
+
+One step = for each of the 7 linears, in order:
+  sbl_quant_mask_pack (gamma, 6:8 mask, codes; recomputed every step)
+  sbl_act_quant       (per-token absmax int8)
+  sbl_forward         (int8 MFMA, y float32)
+  sbl_backward(dX)    (bf16 MFMA, dX bf16)
+  sbl_backward(dW)    (bf16 MFMA, dW float32, dense)
+Metric: tokens per second of whole steps.  Prints one JSON line.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="index into sbl_inputs.WORKLOADS (2 or 3)")
+    ap.add_argument("--n-keep", type=int, default=6)
+    ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="print the per-linear breakdown to stderr")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparsity_sparse_bitlinear_amd as sbl
+    from sbl_inputs import WORKLOADS, activation, grad_out, weight
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.workload]
+    if not wl.backward or len(wl.T) != 1:
+        print(f"workload {args.workload} is not a single-T fwd+bwd training workload", file=sys.stderr)
+        sys.exit(2)
+    T = wl.T[0]
+    n_keep = args.n_keep
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    t_gen = time.time()
+    layers = []
+    for mi, L in enumerate(wl.linears):
+        d_out, d_in = L.d_out, L.d_in
+        W = up(weight(wl.cfg, mi, d_out, d_in))
+        x = up(activation(wl.cfg, mi, T, d_in, dist=wl.act_dist, outlier_frac=wl.outlier_frac))
+        dY = up(grad_out(wl.cfg, mi, T, d_out))
+        layers.append(dict(
+            name=L.name, d_out=d_out, d_in=d_in, W=W, x=x, dY=dY,
+            codes=torch.empty((d_out, d_in // 8), dtype=torch.int16, device=dev),
+            mask=torch.empty((d_out, d_in // 8), dtype=torch.uint8, device=dev),
+            gamma=torch.empty((1,), dtype=torch.float32, device=dev),
+            qws=torch.empty((max(16, sbl.quant_workspace_size(d_out, d_in)),), dtype=torch.uint8, device=dev),
+            x_q=torch.empty((T, d_in), dtype=torch.int8, device=dev),
+            absmax=torch.empty((T,), dtype=torch.float32, device=dev),
+            y=torch.empty((T, d_out), dtype=torch.float32, device=dev),
+            dX=torch.empty((T, d_in), dtype=torch.bfloat16, device=dev),
+            dW=torch.empty((d_out, d_in), dtype=torch.float32, device=dev),
+            bws=torch.empty((max(16, sbl.backward_workspace_size(T, d_in, d_out, sbl.BWD_DW)),),
+                            dtype=torch.uint8, device=dev),
+        ))
+    torch.cuda.synchronize()
+    t_gen = time.time() - t_gen
+
+    parts = ("quant", "act", "fwd", "dx", "dw")
+
+    def step(events=None):
+        for li, Lr in enumerate(layers):
+            def mark(k):
+                if events is not None:
+                    events[li][k].record()
+            mark(0)
+            sbl.quant_mask_pack(Lr["W"], n_keep, codes=Lr["codes"], mask=Lr["mask"], gamma=Lr["gamma"],
+                                workspace=Lr["qws"])
+            mark(1)
+            sbl.act_quant(Lr["x"], x_q=Lr["x_q"], absmax=Lr["absmax"])
+            mark(2)
+            sbl.forward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], out_dtype=sbl.F32, y=Lr["y"])
+            mark(3)
+            sbl.backward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], Lr["dY"], need_dx=True, need_dw=False,
+                         dx_dtype=sbl.BF16, dX=Lr["dX"])
+            mark(4)
+            sbl.backward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], Lr["dY"], need_dx=False, need_dw=True,
+                         dW=Lr["dW"], workspace=Lr["bws"])
+            mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region 1: plain steps, bracketed by synchronize (one process: no barrier needed).
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = T * args.steps / elapsed
+
+    # Timed region 2: the same steps with HIP events between the calls (same stream), for the
+    # per-kernel durations behind the roofline figures.
+    sums = np.zeros((len(layers), len(parts)))
+    for _ in range(args.steps):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in layers]
+        step(ev)
+        torch.cuda.synchronize()
+        for li in range(len(layers)):
+            for k in range(5):
+                sums[li, k] += ev[li][k].elapsed_time(ev[li][k + 1])
+    per_launch_ms = sums / args.steps          # [layer, part]
+
+    # Algorithmic work per launch (units x per-unit figure).
+    work = []
+    for Lr in layers:
+        d_out, d_in = Lr["d_out"], Lr["d_in"]
+        nw = d_out * d_in
+        work.append(dict(
+            quant=2.375 * nw,                                   # bytes: read W (2) + codes (0.25) + mask (0.125)
+            act=3.0 * T * d_in + 4.0 * T,                       # bytes: read x (2), write x_q (1), absmax (4/token)
+            fwd=2.0 * T * d_out * d_in * n_keep / 8.0,          # int8 ops on kept weights
+            dx=2.0 * T * d_out * d_in * n_keep / 8.0,           # bf16 flops on kept weights
+            dw=2.0 * T * d_out * d_in,                          # bf16 flops, dense (Dual STE)
+            fwd_issued=2.0 * T * d_out * d_in,
+            dx_issued=2.0 * T * d_out * d_in,
+        ))
+    tot_ms = per_launch_ms.sum(axis=0)
+    def rate(part):
+        return sum(w[part] for w in work) / (tot_ms[parts.index(part)] * 1e-3)
+    kernels = {
+        "quant_mask_pack": dict(ms=tot_ms[0], GBps=rate("quant") / 1e9, frac_hbm=rate("quant") / 1e9 / HBM_PEAK_GBS),
+        "act_quant": dict(ms=tot_ms[1], GBps=rate("act") / 1e9, frac_hbm=rate("act") / 1e9 / HBM_PEAK_GBS),
+        "forward_int8": dict(ms=tot_ms[2], TOPs=rate("fwd") / 1e12, frac_int8=rate("fwd") / 1e12 / INT8_PEAK_TOPS,
+                             frac_int8_issued=sum(w["fwd_issued"] for w in work) / (tot_ms[2] * 1e-3) / 1e12 / INT8_PEAK_TOPS),
+        "backward_dx_bf16": dict(ms=tot_ms[3], TFLOPs=rate("dx") / 1e12, frac_bf16=rate("dx") / 1e12 / BF16_PEAK_TFLOPS,
+                                 frac_bf16_issued=sum(w["dx_issued"] for w in work) / (tot_ms[3] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS),
+        "backward_dw_bf16": dict(ms=tot_ms[4], TFLOPs=rate("dw") / 1e12, frac_bf16=rate("dw") / 1e12 / BF16_PEAK_TFLOPS),
+    }
+    gemm_parts = {"fwd": ("forward_int8", "TOP/s", INT8_PEAK_TOPS), "dx": ("backward_dx_bf16", "TFLOP/s", BF16_PEAK_TFLOPS),
+                  "dw": ("backward_dw_bf16", "TFLOP/s", BF16_PEAK_TFLOPS)}
+    dom = max(gemm_parts, key=lambda p: tot_ms[parts.index(p)])
+    dname, dunit, dpeak = gemm_parts[dom]
+    n_launch = len(layers)
+    achieved = sum(w[dom] for w in work) / n_launch / (tot_ms[parts.index(dom)] / n_launch * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 1), "peak": dpeak,
+                "unit": dunit, "frac": round(achieved / dpeak, 4), "traffic": None,
+                "launches_per_step": n_launch,
+                "avg_launch_ms": round(tot_ms[parts.index(dom)] / n_launch, 4)}
+
+    # CPU baseline: the oracle on a bounded sample, on this host's cores.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, T, n_keep, args.cpu_tokens)
+
+    line = {
+        "metric": "Sparse-BitLinear 6:8 fwd+bwd tokens/s at 3B shapes; % int8 MFMA / HBM peak",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 fwd / bf16 bwd (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "n_keep": n_keep, "m": 8,
+                   "linears": [f"{Lr['name']} {Lr['d_in']}->{Lr['d_out']}" for Lr in layers],
+                   "y_dtype": "f32", "dx_dtype": "bf16", "dw_dtype": "f32"},
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kernels.items()},
+        "cpu_baseline": cpu,
+        "input_gen_s": round(t_gen, 1),
+    }
+    if args.breakdown:
+        for li, Lr in enumerate(layers):
+            print(Lr["name"], " ".join(f"{p}={per_launch_ms[li, k]:.4f}ms" for k, p in enumerate(parts)),
+                  file=sys.stderr)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, T, n_keep, T_s):
+    """Oracle time for one step, estimated from a bounded sample: quant/mask/pack of all
+    matrices at full size (a per-step cost independent of T) plus act quant, forward and
+    backward of every linear on T_s tokens, scaled by T / T_s."""
+    import numpy as np
+
+    import oracle
+    from sbl_inputs import activation, grad_out, sample_rows, weight
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t_fixed = 0.0
+    t_tok = 0.0
+    for mi, L in enumerate(wl.linears):
+        W = weight(wl.cfg, mi, L.d_out, L.d_in)
+        rows = sample_rows(wl.cfg, 100 + mi, T, T_s)
+        x = activation(wl.cfg, mi, T, L.d_in, dist=wl.act_dist, outlier_frac=wl.outlier_frac, rows=rows)
+        dY = grad_out(wl.cfg, mi, T, L.d_out, rows=rows)
+        t0 = time.perf_counter()
+        w_eff, mask, g = oracle.effective_weight(W, n_keep)
+        oracle.pack_codes(w_eff)
+        oracle.pack_mask(mask)
+        t1 = time.perf_counter()
+        xq, a = oracle.act_quant(x)
+        acc = oracle.forward_acc(w_eff, xq)
+        oracle.forward_y(acc, g, a)
+        oracle.backward(dY, w_eff, g, xq, a)
+        t2 = time.perf_counter()
+        t_fixed += t1 - t0
+        t_tok += t2 - t1
+    est = t_fixed + t_tok * (T / T_s)
+    return {"value": round(T / est, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"all {len(wl.linears)} linears: quant/mask/pack at full size ({t_fixed:.1f} s) + "
+                      f"act quant, forward, backward on {T_s} of {T} sampled tokens ({t_tok:.1f} s), "
+                      f"token part scaled by {T // T_s}; estimated {est:.1f} s per step"}
+
+
+if __name__ == "__main__":
+    main()

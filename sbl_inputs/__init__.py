@@ -5,8 +5,10 @@ benchmark.  It holds NO arithmetic of the method itself: it only draws random
 numbers, rounds them to bfloat16 bit patterns, and builds hand-shaped edge-case
 tensors.  Both sides of every parity comparison receive the same bit patterns.
 
-Stream layout: ``numpy.random.Generator(PCG64(SeedSequence([cfg, mat, kind])))``
-with ``kind`` 0 = W, 1 = x, 2 = dY, 3 = outlier-channel choice.
+Stream layout: ``numpy.random.Generator(PCG64(SeedSequence([cfg, mat, kind, ...])))``
+with ``kind`` 0 = W, 1 = x, 2 = dY, 3 = outlier-channel choice; x and dY are
+drawn in blocks of ROW_BLOCK token rows, block b from the stream
+``[cfg, mat, kind, b]``.
 
 Workloads (all tensors are bfloat16 bit patterns stored as ``uint16``):
 
@@ -19,6 +21,8 @@ Workloads (all tensors are bfloat16 bit patterns stored as ``uint16``):
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -61,36 +65,82 @@ def weight(cfg: int, mat: int, d_out: int, d_in: int, std: float = 0.02) -> np.n
     return f32_to_bf16_bits(_normal_f32(rng(cfg, mat, KIND_W), (d_out, d_in), std))
 
 
+ROW_BLOCK = 2048  # token rows per independently seeded block
+
+
+def _row_blocks(T: int, rows: Optional[np.ndarray]):
+    if rows is None:
+        return list(range((T + ROW_BLOCK - 1) // ROW_BLOCK))
+    return sorted(set(int(r) // ROW_BLOCK for r in np.asarray(rows)))
+
+
+def _blocked(T: int, ncols: int, fill, rows: Optional[np.ndarray], threads: Optional[int]) -> np.ndarray:
+    """Assemble a [T, ncols] bf16 tensor from row blocks of ROW_BLOCK tokens; block b is drawn by
+    ``fill(b, nrows)`` from its own seeded stream, so any subset of rows can be regenerated alone
+    and blocks can be drawn in parallel threads (numpy releases the GIL while filling)."""
+    blocks = _row_blocks(T, rows)
+    out = {}
+
+    def work(b):
+        n = min(ROW_BLOCK, T - b * ROW_BLOCK)
+        out[b] = f32_to_bf16_bits(fill(b, n))
+
+    nthreads = threads if threads is not None else min(16, os.cpu_count() or 1)
+    if nthreads > 1 and len(blocks) > 1:
+        with ThreadPoolExecutor(max_workers=nthreads) as ex:
+            list(ex.map(work, blocks))
+    else:
+        for b in blocks:
+            work(b)
+    if rows is None:
+        if not blocks:
+            return np.zeros((0, ncols), np.uint16)
+        return np.concatenate([out[b] for b in blocks], axis=0)
+    rows = np.asarray(rows)
+    res = np.empty((len(rows), ncols), np.uint16)
+    for k, r in enumerate(rows):
+        res[k] = out[int(r) // ROW_BLOCK][int(r) % ROW_BLOCK]
+    return res
+
+
 def activation(cfg: int, mat: int, T: int, d_in: int, dist: str = "normal",
                outlier_frac: float = 0.0, outlier_scale: float = 20.0,
-               rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Activations x [T, d_in] (bf16 bits).
+               rows: Optional[np.ndarray] = None, threads: Optional[int] = None) -> np.ndarray:
+    """Activations x [T, d_in] (bf16 bits), drawn in row blocks of ROW_BLOCK tokens.
 
     ``dist`` is ``"normal"`` (N(0,1)) or ``"student_t4"`` (Student-t, nu = 4).
     ``outlier_frac`` > 0 picks ``max(1, round(frac * d_in))`` seeded columns and
     scales them by ``outlier_scale`` before rounding to bf16.
-    ``rows``: optional token indices; only those rows of the full tensor are
-    returned (the full tensor is still drawn, so the values are identical).
+    ``rows``: optional token indices; only those rows are returned (identical to
+    the same rows of the full tensor).
     """
-    g = rng(cfg, mat, KIND_X)
-    if dist == "normal":
-        full = g.standard_normal(size=(T, d_in), dtype=np.float32)
-    elif dist == "student_t4":
-        full = g.standard_t(4.0, size=(T, d_in)).astype(np.float32)
-    else:
+    if dist not in ("normal", "student_t4"):
         raise ValueError(f"unknown activation distribution {dist!r}")
+    cols = None
     if outlier_frac > 0.0:
         k = max(1, int(round(outlier_frac * d_in)))
         cols = rng(cfg, mat, KIND_OUTLIER).choice(d_in, size=k, replace=False)
-        full[:, cols] *= np.float32(outlier_scale)
-    if rows is not None:
-        full = full[np.asarray(rows)]
-    return f32_to_bf16_bits(full)
+
+    def fill(b, n):
+        g = rng(cfg, mat, KIND_X, (b,))
+        if dist == "normal":
+            blk = g.standard_normal(size=(n, d_in), dtype=np.float32)
+        else:
+            blk = g.standard_t(4.0, size=(n, d_in)).astype(np.float32)
+        if cols is not None:
+            blk[:, cols] *= np.float32(outlier_scale)
+        return blk
+
+    return _blocked(T, d_in, fill, rows, threads)
 
 
-def grad_out(cfg: int, mat: int, T: int, d_out: int) -> np.ndarray:
-    """Upstream gradient dY [T, d_out] ~ N(0, 1), bf16 bits."""
-    return f32_to_bf16_bits(rng(cfg, mat, KIND_DY).standard_normal(size=(T, d_out), dtype=np.float32))
+def grad_out(cfg: int, mat: int, T: int, d_out: int, rows: Optional[np.ndarray] = None,
+             threads: Optional[int] = None) -> np.ndarray:
+    """Upstream gradient dY [T, d_out] ~ N(0, 1), bf16 bits, drawn in row blocks."""
+    def fill(b, n):
+        return rng(cfg, mat, KIND_DY, (b,)).standard_normal(size=(n, d_out), dtype=np.float32)
+
+    return _blocked(T, d_out, fill, rows, threads)
 
 
 # ----------------------------------------------------------------------------
