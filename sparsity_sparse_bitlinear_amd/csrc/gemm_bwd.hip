@@ -8,352 +8,367 @@
 //   dW[o,i] = sum_t dY[t,o] x~[t,i]                (k_bwd_dw, dense over (o,i))
 //
 // Both use v_mfma_f32_32x32x16_bf16 (lane l holds A[m = l%32][k = 8(l/32)+0..7]
-// and B[k = 8(l/32)+0..7][n = l%32]).  Operands whose reduction index is not
-// contiguous in memory are staged into LDS in their natural layout and read
-// with ds_read_b64_tr_b16, which hands each lane 4 consecutive-k values of one
-// column: in each 16-lane group, lane q addresses row kb + q/4, columns
-// n0 + 4(q%4) .. +3, and lane i receives rows kb..kb+3 of column n0 + i.
-//
-//   dX: A = dY [T, d_out] (k = o contiguous, plain 16-byte fragment reads);
-//       B = W_eff rows o, expanded from the code plane to bf16 {-1,0,+1}
-//       (exact) in natural [o][i] layout, transposed by the tr16 read.
-//   dW: A = dY^T, staged as [t][o]; B = x~ = x_q * a_t / 127 converted to bf16
-//       while staging as [t][i]; both read with tr16.  Few output tiles: the
-//       token range is split and the partial sums are added in a fixed order
-//       by k_splitk_reduce (deterministic).
+// and B[k = 8(l/32)+0..7][n = l%32]) with fp32 accumulation.  All operands
+// sit in LDS as K-contiguous rows (see gemm_common.h).  Operands whose
+// reduction index is not contiguous in memory are transposed in registers
+// while they are staged, in 4 x 4 or 4 x 8 blocks, and written with 8-byte
+// LDS stores:
+//   dX: A = dY [T, d_out] (k = o contiguous, a plain copy); B = W_eff^T: four
+//       code words of consecutive rows o give, for each column i, four
+//       consecutive-k bf16 values {-1,0,+1} (exact).
+//   dW: A = dY^T: four rows t of dY give, for each o, four consecutive-k
+//       values (byte permutes); B = x~^T: four rows t of x_q are widened,
+//       scaled by a_t / 127 and rounded to bf16 pairwise along t.
+// Global loads are buffer loads through per-K-step resources, so rows past a
+// matrix edge read as zero.  dW with few output tiles splits the token range; the partial sums are added
+// in a fixed order by k_splitk_reduce (deterministic).
 #include <algorithm>
 
-#include "sbl_internal.h"
+#include "gemm_common.h"
 
 namespace sbl {
 
 namespace {
 
-constexpr int kBKb = 32;  // k elements per tile (bf16)
+using namespace gemm;
 
-__device__ __forceinline__ int swz(int row, int c) { return row * 64 + 16 * (c ^ ((row >> 2) & 3)); }
+constexpr int kBK = 32;  // k elements (bf16) per LDS row
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16_rne(lo) | ((uint32_t)f32_to_bf16_rne(hi) << 16);
-}
-
-// Two 2-bit codes (a 4-bit nibble) -> two bf16 values {0, +1 = 0x3F80, -1 = 0xBF80}.
-__device__ __forceinline__ uint32_t code2_to_bf16x2(uint32_t nib) {
-  const uint32_t s = (nib & 3u) | ((nib & 0xCu) << 14);
+// Two 2-bit codes in bits 0-1 and 16-17 -> two bf16 values {0, +1 = 0x3F80, -1 = 0xBF80}.
+__device__ __forceinline__ uint32_t code_pair_to_bf16x2(uint32_t s) {
   return (s * 0x3F80u) | ((s & 0x20002u) << 7);
 }
 
-__device__ __forceinline__ uint4 code8_to_bf16x8(uint32_t c) {
-  return make_uint4(code2_to_bf16x2(c), code2_to_bf16x2(c >> 4), code2_to_bf16x2(c >> 8),
-                    code2_to_bf16x2(c >> 12));
-}
-
-__device__ __forceinline__ v4s tr16(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBL_LDS v4s*)(SBL_LDS char*)p);
-}
-
-// 32x32x16 operand fragment (8 bf16 over k) from an LDS tile stored [k][mn] with
-// pitch `pitch` bytes; k rows k0..k0+15, mn columns c0..c0+31.
-__device__ __forceinline__ v8bf frag_tr(const char* base, int pitch, int k0, int c0, int lane) {
-  const int g = lane >> 4, q = lane & 15;
-  const int row = k0 + 8 * (g >> 1) + (q >> 2);
-  const int col = c0 + 16 * (g & 1) + 4 * (q & 3);
-  const char* p = base + row * pitch + col * 2;
-  const v4s lo = tr16(p);
-  const v4s hi = tr16(p + 4 * pitch);
-  v8s r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(v8bf, r);
-}
-
 // ---------------------------------------------------------------------------
-// dX = gamma * dY @ W_eff
+// dX = gamma * dY @ W_eff      (M = tokens, N = d_in, K = d_out)
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int OUT>
-__global__ __launch_bounds__(256) void k_bwd_dx(const uint16_t* __restrict__ dY, const uint16_t* __restrict__ codes,
-                                                const float* __restrict__ gamma_p, int T, int d_in, int d_out,
-                                                void* __restrict__ dX) {
-  static_assert((BM / WM) * (BN / WN) == 4, "4 waves per block");
-  constexpr int MI = WM / 32, NJ = WN / 32;
-  constexpr int CA = BM * 4 / 256;           // 16-byte chunks of A per thread
-  constexpr int GB = BN / 8;                 // code groups per B row
-  constexpr int RB = 256 / GB;               // B rows covered per pass
-  constexpr int CB = kBKb / RB;              // passes
-  constexpr int PB = (BN + 32) * 2;          // B pitch in bytes (== 64 mod 256)
-  __shared__ __attribute__((aligned(16))) char lds[2 * BM * 64 + 2 * kBKb * PB];
+template <int OUT, bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_dx(const uint16_t* __restrict__ dY,
+                                                        const uint16_t* __restrict__ codes,
+                                                        const float* __restrict__ gamma_p, int T, int d_in,
+                                                        int d_out, void* __restrict__ dX) {
+  constexpr int CA = kBM * 4 / kThreads;
+  __shared__ __attribute__((aligned(16))) char lds[2 * (kBM + kBN) * kRow];
   char* As = lds;
-  char* Bs = lds + 2 * BM * 64;
+  char* Bs = lds + 2 * kBM * kRow;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm0 = (wave / (BN / WN)) * WM;
-  const int wn0 = (wave % (BN / WN)) * WN;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  const int wm0 = (wave >> 1) * kWM;
+  const int wn0 = (wave & 1) * kWN;
+  int mt, nt;
+  xcd_tile(blockIdx.x, (T + kBM - 1) / kBM, (d_in + kBN - 1) / kBN, mt, nt);
+  const int m0 = mt * kBM;
+  const int n0 = nt * kBN;
   const int G = d_in >> 3;
-  const int nk = (d_out + kBKb - 1) / kBKb;
-  const bool a_vec = (d_out & 7) == 0;
+  const int nk = (d_out + kBK - 1) / kBK;
 
-  uint4 ra[CA];
-  uint32_t rb[CB];
+  const int rows_a = min(kBM, T - m0);
+  const uint16_t* a_base = dY + (int64_t)m0 * d_out;
+  uint32_t a_off[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int q = tid + kThreads * i;
+    a_off[i] = (uint32_t)((q >> 2) * d_out * 2 + 16 * (q & 3));
+  }
+  // B: thread -> 4 consecutive code rows o (4 * og .. +3) x half a group (4 columns i);
+  // the 32 lanes of a half-wave cover all 8 k-slots of 4 LDS rows (conflict-free stores)
+  const int og = tid & 7;              // 0..7
+  const int gh = tid >> 3;             // 16 groups x 2 halves
+  const int bg = (n0 >> 3) + (gh >> 1);
+  const int bh = gh & 1;
+  // code word (row 4 * og + r, group bg) relative to the K-step base; groups past
+  // the row end read as zero
+  uint32_t b_off[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) b_off[r] = bg < G ? (uint32_t)(((4 * og + r) * G + (gh >> 1)) * 2) : kOOB;
+  const uint16_t* b_base = codes + (n0 >> 3);
 
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * kBKb;
+  uint4 ra[2][CA];
+  uint32_t rb[2][4];
+
+  // Buffer loads through per-K-step resources: token rows past T and code rows
+  // past d_out read as zero.
+  auto load_tile = [&](int kt, int st) {
+    const int k0 = kt * kBK;
+    const auto ar = make_rsrc(a_base + k0, clamp_bytes(((int64_t)rows_a * d_out - k0) * 2));
+    const auto br = make_rsrc(b_base + (int64_t)k0 * G, clamp_bytes(((int64_t)(d_out - k0) * G - (n0 >> 3)) * 2));
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
-      const int q = tid + 256 * i;
-      const int row = q >> 2, c = q & 3;
-      const int m = m0 + row, k = k0 + 8 * c;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < T) {
-        const uint16_t* p = dY + (int64_t)m * d_out + k;
-        if (a_vec) {
-          if (k < d_out) v = *(const uint4*)p;
-        } else {
-          uint32_t w[4] = {0, 0, 0, 0};
+      const int k = k0 + 8 * ((tid + kThreads * i) & 3);
+      if constexpr (VEC) {
+        ra[st][i] = bload16(ar, k < d_out ? a_off[i] : kOOB);
+      } else {
+        uint32_t w[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (k + j < d_out) w[j >> 1] |= (uint32_t)p[j] << (16 * (j & 1));
-          v = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+        for (int j = 0; j < 8; ++j) w[j] = bload2(ar, k + j < d_out ? a_off[i] + 2 * j : kOOB);
+        ra[st][i] = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
       }
-      ra[i] = v;
     }
 #pragma unroll
-    for (int s = 0; s < CB; ++s) {
-      const int r = tid / GB + RB * s, gi = tid % GB;
-      const int o = k0 + r, g = (n0 >> 3) + gi;
-      rb[s] = (o < d_out && g < G) ? (uint32_t)codes[(int64_t)o * G + g] : 0u;
-    }
+    for (int r = 0; r < 4; ++r) rb[st][r] = bload2(br, b_off[r]);
   };
-  auto store_tile = [&](int buf) {
-    char* a = As + buf * BM * 64;
+  auto store_tile = [&](int buf, int st) {
+    char* a = As + buf * kBM * kRow;
 #pragma unroll
     for (int i = 0; i < CA; ++i) {
-      const int q = tid + 256 * i;
-      *(uint4*)(a + swz(q >> 2, q & 3)) = ra[i];
+      const int q = tid + kThreads * i;
+      *(uint4*)(a + swz(q >> 2, q & 3)) = ra[st][i];
     }
-    char* b = Bs + buf * kBKb * PB;
+    char* b = Bs + buf * kBN * kRow;
+    const uint32_t w01 = rb[st][0] | (rb[st][1] << 16);
+    const uint32_t w23 = rb[st][2] | (rb[st][3] << 16);
 #pragma unroll
-    for (int s = 0; s < CB; ++s) {
-      const int r = tid / GB + RB * s, gi = tid % GB;
-      *(uint4*)(b + r * PB + gi * 16) = code8_to_bf16x8(rb[s]);
+    for (int j = 0; j < 4; ++j) {
+      const int slot = 4 * bh + j;           // position i within the group
+      const int row = 8 * (gh >> 1) + slot;  // LDS row = column i within the block tile
+      uint2 v;
+      v.x = code_pair_to_bf16x2((w01 >> (2 * slot)) & 0x00030003u);
+      v.y = code_pair_to_bf16x2((w23 >> (2 * slot)) & 0x00030003u);
+      *(uint2*)(b + swz(row, og >> 1) + 8 * (og & 1)) = v;
     }
   };
 
-  v16f acc[MI][NJ];
+  v16f acc[kMI][kNJ];
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < kMI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < kNJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
-    const char* a = As + buf * BM * 64;
-    const char* b = Bs + buf * kBKb * PB;
+  auto compute = [&](int buf) {
+    const char* a = As + buf * kBM * kRow;
+    const char* b = Bs + buf * kBN * kRow;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int lc = 2 * ks + (lane >> 5);
-      v8bf fa[MI], fb[NJ];
+      v8bf fa[kMI], fb[kNJ];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) fa[i] = *(const v8bf*)(a + swz(wm0 + 32 * i + (lane & 31), lc));
+      for (int i = 0; i < kMI; ++i) fa[i] = __builtin_bit_cast(v8bf, frag(a, wm0 + 32 * i, ks, lane));
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) fb[j] = frag_tr(b, PB, 16 * ks, wn0 + 32 * j, lane);
+      for (int j = 0; j < kNJ; ++j) fb[j] = __builtin_bit_cast(v8bf, frag(b, wn0 + 32 * j, ks, lane));
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < kMI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < kNJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
+  };
+
+  // Software pipeline over K steps: tile k sits in register stage k % 2 and LDS
+  // buffer k % 2.  Each step issues the loads of tile k + 2, multiplies tile k
+  // and writes tile k + 1 to LDS.  Tile indices past the end are clamped (the
+  // extra loads and stores are never multiplied), keeping the loop body free
+  // of conditionals.
+  const int last = nk - 1;
+  load_tile(0, 0);
+  load_tile(min(1, last), 1);
+  store_tile(0, 0);
+  __syncthreads();
+  int k = 0;
+  for (; k + 2 <= nk; k += 2) {
+    load_tile(min(k + 2, last), 0);
+    compute(0);
+    store_tile(1, 1);
+    __syncthreads();
+    load_tile(min(k + 3, last), 1);
+    compute(1);
+    store_tile(0, 0);
     __syncthreads();
   }
+  if (k < nk) compute(0);
 
   const float gamma = *gamma_p;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  for (int i = 0; i < kMI; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int m = m0 + wm0 + 32 * i + acc_row(r, lane);
       if (m >= T) continue;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+      for (int j = 0; j < kNJ; ++j) {
         const int n = n0 + wn0 + 32 * j + (lane & 31);
         if (n >= d_in) continue;
         const float v = acc[i][j][r] * gamma;
         const int64_t off = (int64_t)m * d_in + n;
         if constexpr (OUT == SBL_F32) ((float*)dX)[off] = v;
-        else ((uint16_t*)dX)[off] = f32_to_bf16_rne(v);
+        else ((__bf16*)dX)[off] = (__bf16)v;
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// dW = dY^T @ x~  (M = d_out, N = d_in, K = tokens)
+// dW = dY^T @ x~      (M = d_out, N = d_in, K = tokens)
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void k_bwd_dw(const uint16_t* __restrict__ dY, const int8_t* __restrict__ xq,
-                                                const float* __restrict__ absmax, int T, int d_in, int d_out,
-                                                int k_per_split, float* __restrict__ out) {
-  static_assert((BM / WM) * (BN / WN) == 4, "4 waves per block");
-  constexpr int MI = WM / 32, NJ = WN / 32;
-  constexpr int PA = (BM + 32) * 2;
-  constexpr int PB = (BN + 32) * 2;
-  constexpr int CPA = BM / 8;                 // 16-byte chunks per A row (8 bf16)
-  constexpr int CA = kBKb * CPA / 256;
-  constexpr int CPB = BN / 16;                // 16-byte chunks per x_q row (16 int8)
-  constexpr int CB = kBKb * CPB / 256;
-  static_assert(CA >= 1 && CB >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) char lds[2 * kBKb * (PA + PB)];
+
+// bf16 halves: low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi)
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
+}
+
+__device__ __forceinline__ float sbyte(uint32_t w, int b) { return (float)(int)(int8_t)((w >> (8 * b)) & 0xFFu); }
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads, 2) void k_bwd_dw(const uint16_t* __restrict__ dY,
+                                                        const int8_t* __restrict__ xq,
+                                                        const float* __restrict__ absmax, int T, int d_in,
+                                                        int d_out, int k_per_split, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * (kBM + kBN) * kRow];
   char* As = lds;
-  char* Bs = lds + 2 * kBKb * PA;
+  char* Bs = lds + 2 * kBM * kRow;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm0 = (wave / (BN / WN)) * WM;
-  const int wn0 = (wave % (BN / WN)) * WN;
-  const int m0 = blockIdx.y * BM;   // output rows (o)
-  const int n0 = blockIdx.x * BN;   // output cols (i)
-  const int kbeg = blockIdx.z * k_per_split;
+  const int wm0 = (wave >> 1) * kWM;
+  const int wn0 = (wave & 1) * kWN;
+  const int gm = (d_out + kBM - 1) / kBM, gn = (d_in + kBN - 1) / kBN;
+  const int split = blockIdx.x / (gm * gn);
+  int mt, nt;
+  xcd_tile(blockIdx.x - split * gm * gn, gm, gn, mt, nt);
+  const int m0 = mt * kBM;  // output rows (o)
+  const int n0 = nt * kBN;  // output cols (i)
+  const int kbeg = split * k_per_split;
   const int kend = min(T, kbeg + k_per_split);
-  const int nk = kend > kbeg ? (kend - kbeg + kBKb - 1) / kBKb : 0;
-  const bool a_vec = (d_out & 7) == 0;
-  const bool b_vec = (d_in & 15) == 0;
+  const int nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
 
-  uint4 ra[CA];
-  uint4 rb[CB];
-  float rs[CB];
+  // A: thread -> 4 consecutive tokens (4 * tg .. +3) x 8 consecutive o (8 * oc .. +7);
+  // the 32 lanes of a half-wave cover all 8 k-slots of 4 LDS rows (conflict-free stores)
+  const int tg = tid & 7;    // 0..7
+  const int oc = tid >> 3;   // 0..31
+  const int a_o = m0 + 8 * oc;
+  // B: thread -> the same 4 tokens x 4 consecutive i (4 * oc .. +3)
+  const int b_i = n0 + 4 * oc;
+  // Lane offsets relative to the K-step base (token t0 = kbeg + 32 kt); columns
+  // past the matrix edge read as zero.
+  uint32_t a_off[4], b_off[4], s_off[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 4 * tg + r;
+    a_off[r] = a_o < d_out ? (uint32_t)((t * d_out + 8 * oc) * 2) : kOOB;
+    b_off[r] = b_i < d_in ? (uint32_t)(t * d_in + 4 * oc) : kOOB;
+    s_off[r] = (uint32_t)(t * 4);
+  }
 
-  auto load_tile = [&](int kt) {
-    const int t0 = kbeg + kt * kBKb;
+  uint4 ra[2][4];
+  uint32_t rb[2][4];
+  float rs[2][4];
+
+  // Buffer loads through per-K-step resources: tokens past the split end read
+  // as zero (x_q = 0 and a_t = 0).
+  auto load_tile = [&](int kt, int st) {
+    const int t0 = kbeg + kt * kBK;
+    const int64_t nt_ = kend - t0;
+    const auto ar = make_rsrc(dY + (int64_t)t0 * d_out + m0, clamp_bytes((nt_ * d_out - m0) * 2));
+    const auto br = make_rsrc(xq + (int64_t)t0 * d_in + n0, clamp_bytes(nt_ * d_in - n0));
+    const auto sr = make_rsrc(absmax + t0, clamp_bytes(nt_ * 4));
 #pragma unroll
-    for (int s = 0; s < CA; ++s) {
-      const int q = tid + 256 * s;
-      const int r = q / CPA, c = q % CPA;
-      const int t = t0 + r, o = m0 + 8 * c;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (t < kend) {
-        const uint16_t* p = dY + (int64_t)t * d_out + o;
-        if (a_vec) {
-          if (o < d_out) v = *(const uint4*)p;
-        } else {
-          uint32_t w[4] = {0, 0, 0, 0};
+    for (int r = 0; r < 4; ++r) {
+      if constexpr (VEC) {
+        ra[st][r] = bload16(ar, a_off[r]);
+      } else {
+        uint32_t w[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (o + j < d_out) w[j >> 1] |= (uint32_t)p[j] << (16 * (j & 1));
-          v = make_uint4(w[0], w[1], w[2], w[3]);
-        }
+        for (int j = 0; j < 8; ++j) w[j] = bload2(ar, a_o + j < d_out ? a_off[r] + 2 * j : kOOB);
+        ra[st][r] = make_uint4(w[0] | (w[1] << 16), w[2] | (w[3] << 16), w[4] | (w[5] << 16), w[6] | (w[7] << 16));
       }
-      ra[s] = v;
-    }
-#pragma unroll
-    for (int s = 0; s < CB; ++s) {
-      const int q = tid + 256 * s;
-      const int r = q / CPB, c = q % CPB;
-      const int t = t0 + r, i = n0 + 16 * c;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      float sc = 0.0f;
-      if (t < kend) {
-        sc = absmax[t] / 127.0f;
-        const int8_t* p = xq + (int64_t)t * d_in + i;
-        if (b_vec) {
-          if (i < d_in) v = *(const uint4*)p;
-        } else {
-          if (i < d_in) { const uint2 h = *(const uint2*)p; v.x = h.x; v.y = h.y; }
-          if (i + 8 < d_in) { const uint2 h = *(const uint2*)(p + 8); v.z = h.x; v.w = h.y; }
-        }
-      }
-      rb[s] = v;
-      rs[s] = sc;
+      rb[st][r] = bload4(br, b_off[r]);
+      rs[st][r] = __uint_as_float(bload4(sr, s_off[r]));
     }
   };
-  auto cvt4 = [](uint32_t w, float sc, uint32_t& lo, uint32_t& hi) {
-    const float f0 = (float)(int)(int8_t)(w & 0xFFu) * sc;
-    const float f1 = (float)(int)(int8_t)((w >> 8) & 0xFFu) * sc;
-    const float f2 = (float)(int)(int8_t)((w >> 16) & 0xFFu) * sc;
-    const float f3 = (float)(int)(int8_t)(w >> 24) * sc;
-    lo = pack_bf16x2(f0, f1);
-    hi = pack_bf16x2(f2, f3);
-  };
-  auto store_tile = [&](int buf) {
-    char* a = As + buf * kBKb * PA;
+  auto store_tile = [&](int buf, int st) {
+    // A rows o (8 * oc + 2p, +1), k = 4 * tg .. +3
+    char* a = As + buf * kBM * kRow;
+    const uint32_t w0[4] = {ra[st][0].x, ra[st][0].y, ra[st][0].z, ra[st][0].w};
+    const uint32_t w1[4] = {ra[st][1].x, ra[st][1].y, ra[st][1].z, ra[st][1].w};
+    const uint32_t w2[4] = {ra[st][2].x, ra[st][2].y, ra[st][2].z, ra[st][2].w};
+    const uint32_t w3[4] = {ra[st][3].x, ra[st][3].y, ra[st][3].z, ra[st][3].w};
 #pragma unroll
-    for (int s = 0; s < CA; ++s) {
-      const int q = tid + 256 * s;
-      *(uint4*)(a + (q / CPA) * PA + (q % CPA) * 16) = ra[s];
+    for (int p = 0; p < 4; ++p) {
+      uint2 lo, hi;
+      lo.x = pack_lo(w0[p], w1[p]);
+      lo.y = pack_lo(w2[p], w3[p]);
+      hi.x = pack_hi(w0[p], w1[p]);
+      hi.y = pack_hi(w2[p], w3[p]);
+      const int row = 8 * oc + 2 * p;
+      *(uint2*)(a + swz(row, tg >> 1) + 8 * (tg & 1)) = lo;
+      *(uint2*)(a + swz(row + 1, tg >> 1) + 8 * (tg & 1)) = hi;
     }
-    char* b = Bs + buf * kBKb * PB;
+    // B rows i (4 * oc + j), k = 4 * tg .. +3: x_q * a_t / 127 rounded to bf16
+    char* b = Bs + buf * kBN * kRow;
+    const float s0 = rs[st][0] * (1.0f / 127.0f), s1 = rs[st][1] * (1.0f / 127.0f);
+    const float s2 = rs[st][2] * (1.0f / 127.0f), s3 = rs[st][3] * (1.0f / 127.0f);
 #pragma unroll
-    for (int s = 0; s < CB; ++s) {
-      const int q = tid + 256 * s;
-      char* p = b + (q / CPB) * PB + (q % CPB) * 32;
-      uint4 u0, u1;
-      cvt4(rb[s].x, rs[s], u0.x, u0.y);
-      cvt4(rb[s].y, rs[s], u0.z, u0.w);
-      cvt4(rb[s].z, rs[s], u1.x, u1.y);
-      cvt4(rb[s].w, rs[s], u1.z, u1.w);
-      *(uint4*)p = u0;
-      *(uint4*)(p + 16) = u1;
+    for (int j = 0; j < 4; ++j) {
+      uint2 v;
+      v.x = cvt_pk_bf16(sbyte(rb[st][0], j) * s0, sbyte(rb[st][1], j) * s1);
+      v.y = cvt_pk_bf16(sbyte(rb[st][2], j) * s2, sbyte(rb[st][3], j) * s3);
+      *(uint2*)(b + swz(4 * oc + j, tg >> 1) + 8 * (tg & 1)) = v;
     }
   };
 
-  v16f acc[MI][NJ];
+  v16f acc[kMI][kNJ];
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int i = 0; i < kMI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int j = 0; j < kNJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  if (nk > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load_tile(kt + 1);
-    const char* a = As + buf * kBKb * PA;
-    const char* b = Bs + buf * kBKb * PB;
+  auto compute = [&](int buf) {
+    const char* a = As + buf * kBM * kRow;
+    const char* b = Bs + buf * kBN * kRow;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      v8bf fa[MI], fb[NJ];
+      v8bf fa[kMI], fb[kNJ];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) fa[i] = frag_tr(a, PA, 16 * ks, wm0 + 32 * i, lane);
+      for (int i = 0; i < kMI; ++i) fa[i] = __builtin_bit_cast(v8bf, frag(a, wm0 + 32 * i, ks, lane));
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) fb[j] = frag_tr(b, PB, 16 * ks, wn0 + 32 * j, lane);
+      for (int j = 0; j < kNJ; ++j) fb[j] = __builtin_bit_cast(v8bf, frag(b, wn0 + 32 * j, ks, lane));
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int i = 0; i < kMI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
+        for (int j = 0; j < kNJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tile(buf ^ 1);
+  };
+
+  if (nk > 0) {
+    const int last = nk - 1;
+    load_tile(0, 0);
+    load_tile(min(1, last), 1);
+    store_tile(0, 0);
     __syncthreads();
+    int k = 0;
+    for (; k + 2 <= nk; k += 2) {
+      load_tile(min(k + 2, last), 0);
+      compute(0);
+      store_tile(1, 1);
+      __syncthreads();
+      load_tile(min(k + 3, last), 1);
+      compute(1);
+      store_tile(0, 0);
+      __syncthreads();
+    }
+    if (k < nk) compute(0);
   }
 
-  float* dst = out + (size_t)blockIdx.z * (size_t)d_out * (size_t)d_in;
+  float* dst = out + (size_t)split * (size_t)d_out * (size_t)d_in;
 #pragma unroll
-  for (int i = 0; i < MI; ++i) {
+  for (int i = 0; i < kMI; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int m = m0 + wm0 + 32 * i + acc_row(r, lane);
       if (m >= d_out) continue;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
+      for (int j = 0; j < kNJ; ++j) {
         const int n = n0 + wn0 + 32 * j + (lane & 31);
         if (n < d_in) dst[(int64_t)m * d_in + n] = acc[i][j][r];
       }
@@ -380,20 +395,21 @@ __global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int64_t
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
 }
 
-// Tile configuration of the dW product.
-constexpr int kDwBM = 256, kDwBN = 256;
-
+// Token-range splits for dW: enough blocks to fill two slots on every CU, where a
+// split earns its keep (each extra split adds a partial write and read of dW).
 int dw_splits(int64_t T, int64_t d_in, int64_t d_out) {
-  const int64_t tiles = ((d_out + kDwBM - 1) / kDwBM) * ((d_in + kDwBN - 1) / kDwBN);
+  const int64_t tiles = ((d_out + kBM - 1) / kBM) * ((d_in + kBN - 1) / kBN);
   if (T <= 0) return 1;
+  const int64_t slots = 512;  // 256 CUs x 2 resident blocks
   int best = 1;
-  double best_eff = 0.0;
-  const int64_t max_s = std::max<int64_t>(1, std::min<int64_t>(32, T / 512));
+  double best_cost = 1e300;
+  const int64_t max_s = std::max<int64_t>(1, std::min<int64_t>(16, T / 1024));
   for (int s = 1; s <= max_s; ++s) {
     const int64_t w = tiles * s;
-    const double eff = (double)w / (double)(256 * ((w + 255) / 256));
-    // each extra split costs one more partial write + read; require a real gain
-    if (eff > best_eff * 1.08) { best = s; best_eff = eff; }
+    const double rounds = (double)((w + slots - 1) / slots);
+    // time ~ rounds * (work per block) + reduction traffic, in units of one full-K tile
+    const double cost = rounds / s + (s > 1 ? 0.02 * s * (double)tiles / slots : 0.0);
+    if (cost < best_cost * 0.97) { best = s; best_cost = cost; }
   }
   return best;
 }
@@ -411,19 +427,14 @@ hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8
                            const uint16_t* dY, int64_t T, int64_t d_in, int64_t d_out, void* dX, int dx_dtype,
                            float* dW, int flags, void* ws, hipStream_t s) {
   if ((flags & SBL_BWD_DX) && T > 0) {
-    const int64_t tiles256 = ((T + 255) / 256) * ((d_in + 255) / 256);
-    if (tiles256 >= 512) {
-      const dim3 grid((unsigned)((d_in + 255) / 256), (unsigned)((T + 255) / 256));
-      if (dx_dtype == SBL_F32)
-        hipLaunchKernelGGL((k_bwd_dx<256, 256, 128, 128, SBL_F32>), grid, dim3(256), 0, s, dY, codes, gamma, (int)T, (int)d_in, (int)d_out, dX);
-      else
-        hipLaunchKernelGGL((k_bwd_dx<256, 256, 128, 128, SBL_BF16>), grid, dim3(256), 0, s, dY, codes, gamma, (int)T, (int)d_in, (int)d_out, dX);
+    const dim3 grid((unsigned)(((d_in + kBN - 1) / kBN) * ((T + kBM - 1) / kBM)));
+    const bool vec = d_out % 8 == 0;
+    if (dx_dtype == SBL_F32) {
+      if (vec) hipLaunchKernelGGL((k_bwd_dx<SBL_F32, true>), grid, dim3(kThreads), 0, s, dY, codes, gamma, (int)T, (int)d_in, (int)d_out, dX);
+      else hipLaunchKernelGGL((k_bwd_dx<SBL_F32, false>), grid, dim3(kThreads), 0, s, dY, codes, gamma, (int)T, (int)d_in, (int)d_out, dX);
     } else {
-      const dim3 grid((unsigned)((d_in + 127) / 128), (unsigned)((T + 127) / 128));
-      if (dx_dtype == SBL_F32)
-        hipLaunchKernelGGL((k_bwd_dx<128, 128, 64, 64, SBL_F32>), grid, dim3(256), 0, s, dY, codes, gamma, (int)T, (int)d_in, (int)d_out, dX);
-      else
-        hipLaunchKernelGGL((k_bwd_dx<128, 128, 64, 64, SBL_BF16>), grid, dim3(256), 0, s, dY, codes, gamma, (int)T, (int)d_in, (int)d_out, dX);
+      if (vec) hipLaunchKernelGGL((k_bwd_dx<SBL_BF16, true>), grid, dim3(kThreads), 0, s, dY, codes, gamma, (int)T, (int)d_in, (int)d_out, dX);
+      else hipLaunchKernelGGL((k_bwd_dx<SBL_BF16, false>), grid, dim3(kThreads), 0, s, dY, codes, gamma, (int)T, (int)d_in, (int)d_out, dX);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -435,11 +446,17 @@ hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8
       return hipGetLastError();
     }
     const int S = dw_splits(T, d_in, d_out);
-    const int64_t kps = ((T + S - 1) / S + kBKb - 1) / kBKb * kBKb;
-    const dim3 grid((unsigned)((d_in + kDwBN - 1) / kDwBN), (unsigned)((d_out + kDwBM - 1) / kDwBM), (unsigned)S);
+    const int64_t kps = ((T + S - 1) / S + kBK - 1) / kBK * kBK;
+    const int64_t tiles = ((d_in + kBN - 1) / kBN) * ((d_out + kBM - 1) / kBM);
+    const dim3 grid((unsigned)(tiles * S));
     float* target = S > 1 ? (float*)ws : dW;
-    hipLaunchKernelGGL((k_bwd_dw<kDwBM, kDwBN, 128, 128>), grid, dim3(256), 0, s, dY, xq, absmax, (int)T, (int)d_in,
-                       (int)d_out, (int)kps, target);
+    // vector path: 16-byte dY rows (d_out % 8); x_q words are 4-byte aligned since d_in % 8 == 0
+    if (d_out % 8 == 0)
+      hipLaunchKernelGGL((k_bwd_dw<true>), grid, dim3(kThreads), 0, s, dY, xq, absmax, (int)T, (int)d_in, (int)d_out,
+                         (int)kps, target);
+    else
+      hipLaunchKernelGGL((k_bwd_dw<false>), grid, dim3(kThreads), 0, s, dY, xq, absmax, (int)T, (int)d_in, (int)d_out,
+                         (int)kps, target);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (S > 1) {

@@ -1,0 +1,91 @@
+// Shared pieces of the matrix-core kernels (forward int8, backward bf16).
+//
+// Every kernel computes one BM x BN output tile per block of 256 threads
+// (4 waves in a 2 x 2 grid, 128 x 64 per wave, 32 x 32 MFMA tiles).  Both
+// operands live in LDS as K-contiguous rows of 64 bytes (32 bf16 or 64 int8
+// values per K step), 4 chunks of 16 bytes per row, swizzled (see swz) so
+// that fragment reads and staging stores are free of bank conflicts.  A fragment is
+// one ds_read_b128: lane l reads row (base + l % 32), chunk (2 ks + l / 32),
+// which is the MFMA operand layout (row = l % 32, k = 8 or 16 per l / 32).
+// 128 accumulator registers per wave keep two blocks resident per CU, so one
+// block's loads, barriers and epilogue overlap the other's matrix work.
+#pragma once
+
+#include "sbl_internal.h"
+
+namespace sbl {
+namespace gemm {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 256;      // block rows (M)
+constexpr int kBN = 128;      // block cols (N)
+constexpr int kWM = 128;      // wave rows
+constexpr int kWN = 64;       // wave cols
+constexpr int kMI = kWM / 32; // MFMA tiles per wave along M
+constexpr int kNJ = kWN / 32; // MFMA tiles per wave along N
+constexpr int kRow = 64;      // bytes per LDS row (one K step)
+
+
+// LDS address of chunk c (16 bytes) of K-row `row`.  LDS reads are served in
+// groups of 16 lanes over 64 banks of 4 bytes (256 bytes per cycle); a 64-byte
+// row fills a quarter of the banks, so 16 consecutive rows reading the same
+// chunk cover all 64 banks once when chunk c of row r is stored at position
+// c ^ ((r >> 2) & 3).  The staging stores (16-byte rows copies, and 8-byte
+// transposed stores whose 32 lanes cover all 8 k-slots of 4 rows) are also
+// conflict-free under this layout.
+__device__ __forceinline__ int swz(int row, int c) { return row * kRow + 16 * (c ^ ((row >> 2) & 3)); }
+
+__device__ __forceinline__ v4i frag(const char* base, int row0, int ks, int lane) {
+  return *(const v4i*)(base + swz(row0 + (lane & 31), 2 * ks + (lane >> 5)));
+}
+
+// Block index -> (m tile, n tile).  Blocks are dispatched round-robin over
+// the 8 XCDs (b % 8); XCD x gets a contiguous range of tiles in row-major
+// order (n fastest), so the tiles resident on one XCD share A rows in its L2.
+__device__ __forceinline__ void xcd_tile(int b, int gm, int gn, int& mt, int& nt) {
+  const int nb = gm * gn;
+  int tile = b;
+  if (nb >= 8) {
+    const int x = b & 7, local = b >> 3;
+    const int q = nb >> 3, r = nb & 7;
+    tile = x * q + min(x, r) + local;
+  }
+  mt = tile / gn;
+  nt = tile - mt * gn;
+}
+
+// Buffer resource for raw (unformatted) loads of `bytes` bytes at `base`.
+// Accesses at offsets at or beyond `bytes` return zero, which is how tile rows
+// past the end of a matrix are zero-filled without per-lane selects.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Lane offset that is always out of range (reads return zero): resources are
+// never larger than kMaxRsrcBytes, and valid lane offsets stay below it.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int64_t kMaxRsrcBytes = 0x7FFFFFF0LL;
+
+// Clamp a byte count to [0, kMaxRsrcBytes].
+__device__ __forceinline__ uint32_t clamp_bytes(int64_t b) {
+  return b <= 0 ? 0u : (b >= kMaxRsrcBytes ? (uint32_t)kMaxRsrcBytes : (uint32_t)b);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+// Row index (within the wave tile) of accumulator register r of lane l.
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+}  // namespace gemm
+}  // namespace sbl
