@@ -78,7 +78,7 @@ typedef enum {
 enum { SBL_BWD_DX = 1, SBL_BWD_DW = 2 };
 
 /* Size limits checked by every entry point. */
-#define SBL_MAX_DIM ((int64_t)1 << 22)      /* d_in, d_out, T each <= 4,194,304 */
+#define SBL_MAX_DIM ((int64_t)1 << 21)      /* d_in, d_out, T each <= 2,097,152 */
 #define SBL_MAX_WEIGHTS ((int64_t)1 << 36)  /* d_out * d_in                       */
 
 /* ------------------------------------------------------------------------ */

@@ -101,6 +101,18 @@ def _dev(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out(t: torch.Tensor, shape, dtypes, device, name: str) -> torch.Tensor:
+    """Check a caller-provided output buffer: the kernels write exactly ``shape`` elements of one of ``dtypes``."""
+    _dev(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
 def _as_bits16(t: torch.Tensor, name: str) -> torch.Tensor:
     _dev(t, name)
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
@@ -129,13 +141,18 @@ def quant_mask_pack(W: torch.Tensor, n_keep: int = 6, *, codes: Optional[torch.T
     dev = W.device
     if codes is None:
         codes = torch.empty((d_out, d_in // 8), dtype=torch.int16, device=dev)
+    _out(codes, (d_out, d_in // 8), (torch.int16, torch.uint16), dev, "codes")
     if mask is None and want_mask:
         mask = torch.empty((d_out, d_in // 8), dtype=torch.uint8, device=dev)
+    if mask is not None:
+        _out(mask, (d_out, d_in // 8), (torch.uint8,), dev, "mask")
     if gamma is None:
         gamma = torch.empty((1,), dtype=torch.float32, device=dev)
+    _out(gamma, (1,), (torch.float32,), dev, "gamma")
     need = quant_workspace_size(d_out, d_in)
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _out(workspace, (workspace.numel(),), (torch.uint8,), dev, "workspace")
     _check(lib.sbl_quant_mask_pack(_ptr(W), d_out, d_in, int(n_keep), _ptr(codes), _ptr(mask), _ptr(gamma),
                                    _ptr(workspace), workspace.numel(), _stream(stream)), "sbl_quant_mask_pack")
     return codes, mask, gamma
@@ -150,6 +167,8 @@ def act_quant(x: torch.Tensor, *, x_q: Optional[torch.Tensor] = None, absmax: Op
         x_q = torch.empty((T, d_in), dtype=torch.int8, device=x.device)
     if absmax is None:
         absmax = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _out(x_q, (T, d_in), (torch.int8,), x.device, "x_q")
+    _out(absmax, (T,), (torch.float32,), x.device, "absmax")
     _check(lib.sbl_act_quant(_ptr(x), T, d_in, _ptr(x_q), _ptr(absmax), _stream(stream)), "sbl_act_quant")
     return x_q, absmax
 
@@ -166,8 +185,11 @@ def forward(codes: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax:
     T, d_in = x_q.shape
     if G * 8 != d_in:
         raise ValueError(f"codes [{d_out}, {G}] do not match x_q [{T}, {d_in}]")
+    if out_dtype not in _OUT_TORCH:
+        raise ValueError(f"unknown out_dtype {out_dtype}")
     if y is None:
         y = torch.empty((T, d_out), dtype=_OUT_TORCH[out_dtype], device=x_q.device)
+    _out(y, (T, d_out), (_OUT_TORCH[out_dtype],), x_q.device, "y")
     _check(lib.sbl_forward(_ptr(codes), _ptr(gamma), _ptr(x_q), _ptr(absmax), T, d_in, d_out, _ptr(y),
                            int(out_dtype), _stream(stream)), "sbl_forward")
     return y
@@ -182,13 +204,23 @@ def backward(codes: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax
     d_out, G = codes.shape
     T, d_in = x_q.shape
     flags = (BWD_DX if need_dx else 0) | (BWD_DW if need_dw else 0)
-    if need_dx and dX is None:
-        dX = torch.empty((T, d_in), dtype=_OUT_TORCH[dx_dtype], device=dY.device)
-    if need_dw and dW is None:
-        dW = torch.empty((d_out, d_in), dtype=torch.float32, device=dY.device)
+    if tuple(dY.shape) != (T, d_out):
+        raise ValueError(f"dY has shape {tuple(dY.shape)}, expected {(T, d_out)}")
+    if dx_dtype not in (F32, BF16):
+        raise ValueError(f"dx_dtype must be F32 or BF16, got {dx_dtype}")
+    if need_dx:
+        if dX is None:
+            dX = torch.empty((T, d_in), dtype=_OUT_TORCH[dx_dtype], device=dY.device)
+        _out(dX, (T, d_in), (_OUT_TORCH[dx_dtype],), dY.device, "dX")
+    if need_dw:
+        if dW is None:
+            dW = torch.empty((d_out, d_in), dtype=torch.float32, device=dY.device)
+        _out(dW, (d_out, d_in), (torch.float32,), dY.device, "dW")
     need = backward_workspace_size(T, d_in, d_out, flags)
     if need and workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=dY.device)
+    if workspace is not None:
+        _out(workspace, (workspace.numel(),), (torch.uint8,), dY.device, "workspace")
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(lib.sbl_backward(_ptr(codes), _ptr(gamma), _ptr(x_q), _ptr(absmax), _ptr(dY), T, d_in, d_out,
                             _ptr(dX if need_dx else None), int(dx_dtype), _ptr(dW if need_dw else None), flags,

@@ -23,6 +23,7 @@
 // matrix edge read as zero.  dW with few output tiles splits the token range; the partial sums are added
 // in a fixed order by k_splitk_reduce (deterministic).
 #include <algorithm>
+#include <cmath>
 
 #include "gemm_common.h"
 
@@ -33,6 +34,12 @@ namespace {
 using namespace gemm;
 
 constexpr int kBK = 32;  // k elements (bf16) per LDS row
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
+}
 
 // Two 2-bit codes in bits 0-1 and 16-17 -> two bf16 values {0, +1 = 0x3F80, -1 = 0xBF80}.
 __device__ __forceinline__ uint32_t code_pair_to_bf16x2(uint32_t s) {
@@ -200,18 +207,148 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dx(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// W_eff^T as bf16 for the direct-load dX path:  WT[i, o] = W_eff[o, i] in
+// {-1, 0, +1} (exact), WT [d_in, d_out] row-major, d_out % 8 == 0.  A block
+// transposes 64 code rows o x 32 groups (256 columns i) through LDS and writes
+// 16-byte runs of 8 consecutive o.
+// ---------------------------------------------------------------------------
+constexpr int kTrO = 64, kTrG = 32;
+
+__global__ __launch_bounds__(256) void k_weff_t_bf16(const uint16_t* __restrict__ codes, int d_out, int d_in,
+                                                     uint16_t* __restrict__ WT) {
+  __shared__ uint16_t tile[kTrO][kTrG + 1];
+  const int G = d_in >> 3;
+  const int o0 = blockIdx.x * kTrO, g0 = blockIdx.y * kTrG;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kTrO * kTrG; e += 256) {
+    const int r = e / kTrG, g = e % kTrG;
+    tile[r][g] = (o0 + r < d_out && g0 + g < G) ? codes[(int64_t)(o0 + r) * G + g0 + g] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int c = tid; c < kTrG * 8 * (kTrO / 8); c += 256) {
+    const int il = c / (kTrO / 8), oc = c % (kTrO / 8);
+    const int i = g0 * 8 + il, o = o0 + 8 * oc;
+    if (i >= d_in || o >= d_out) continue;
+    const int gl = il >> 3, slot = il & 7;
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t pair = (uint32_t)tile[8 * oc + 2 * u][gl] | ((uint32_t)tile[8 * oc + 2 * u + 1][gl] << 16);
+      v[u] = code_pair_to_bf16x2((pair >> (2 * slot)) & 0x00030003u);
+    }
+    *(uint4*)(WT + (int64_t)i * d_out + o) = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Token-contiguous operands for dW = dY^T x~ on the plain GEMM engine:
+//   dYT[o, t] = dY[t, o]                          (bf16 copy)
+//   xT [i, t] = bf16(x_q[t, i] * (a_t / 127))     (x~, rounded once to bf16)
+// Both [C, T8] with T8 = T rounded up to 8; columns t >= T are zero.  A block
+// moves a 64 x 64 tile through LDS: rows of the source are read in 16-byte
+// (bf16) or 8-byte (int8) pieces, rows of the result are written as 16-byte
+// runs of 8 consecutive t.
+// ---------------------------------------------------------------------------
+constexpr int kTT = 64;
+
+template <bool DEQ, bool VEC>
+__global__ __launch_bounds__(256) void k_token_major(const void* __restrict__ src, const float* __restrict__ absmax,
+                                                     int T, int C, int T8, uint16_t* __restrict__ dst) {
+  __shared__ uint32_t tile[kTT][kTT / 2 + 1];  // [t][c pair], bf16 pairs; odd pitch spreads the banks
+  const int t0 = blockIdx.x * kTT, c0 = blockIdx.y * kTT;
+  const int tid = threadIdx.x;
+  // phase 1: 64 rows t x 8 pieces of 8 columns
+  for (int e = tid; e < kTT * (kTT / 8); e += 256) {
+    const int r = e >> 3, pc = e & 7;
+    const int t = t0 + r, c = c0 + 8 * pc;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (t < T) {
+      if constexpr (DEQ) {
+        const int8_t* row = (const int8_t*)src + (int64_t)t * C;
+        const float sc = absmax[t] * (1.0f / 127.0f);
+        int8_t q[8];
+        if (VEC && c + 8 <= C) {
+          const uint2 v = *(const uint2*)(row + c);
+          __builtin_memcpy(q, &v, 8);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) q[u] = c + u < C ? row[c + u] : (int8_t)0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = cvt_pk_bf16((float)q[2 * u] * sc, (float)q[2 * u + 1] * sc);
+      } else {
+        const uint16_t* row = (const uint16_t*)src + (int64_t)t * C;
+        if (VEC && c + 8 <= C) {
+          const uint4 v = *(const uint4*)(row + c);
+          w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t lo = c + 2 * u < C ? row[c + 2 * u] : 0u;
+            const uint32_t hi = c + 2 * u + 1 < C ? row[c + 2 * u + 1] : 0u;
+            w[u] = lo | (hi << 16);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) tile[r][4 * pc + u] = w[u];
+  }
+  __syncthreads();
+  // phase 2: 64 rows c x 8 runs of 8 t
+  for (int e = tid; e < kTT * (kTT / 8); e += 256) {
+    const int cl = e >> 3, rt = e & 7;
+    const int c = c0 + cl, t = t0 + 8 * rt;
+    if (c >= C || t >= T8) continue;
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t a = tile[8 * rt + 2 * u][cl >> 1], b = tile[8 * rt + 2 * u + 1][cl >> 1];
+      v[u] = (cl & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+    }
+    *(uint4*)(dst + (int64_t)c * T8 + t) = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+bool dx_direct(int64_t T, int64_t d_in, int64_t d_out) {
+  return T > 0 && d_out % 8 == 0 && gemm_nt_bf16_supported(T, d_in, d_out);
+}
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+int64_t round8(int64_t t) { return (t + 7) & ~(int64_t)7; }
+
+bool dw_direct(int64_t T, int64_t d_in, int64_t d_out) {
+  return T > 0 && gemm_nt_bf16_supported(d_out, d_in, round8(T));
+}
+
+// K splits for the plain GEMM engine (one 256 x 256 block per CU): pick S to
+// minimise rounds(tiles * S) / S of full-K block time plus the partial-sum
+// traffic, with K pieces that are whole 32-token steps.
+void nt_splits(int64_t M, int64_t N, int64_t K, int& S, int64_t& kps) {
+  const int64_t tiles = gemm_nt_bf16_tiles(M, N);
+  const double slots = 256.0;
+  const double t_block = 2.0 * 256.0 * 256.0 * (double)K / 5.0e12;  // seconds per full-K block, ~half of peak
+  const double t_byte = 1.0 / 5.0e12;                                 // seconds per byte of partial-sum traffic
+  S = 1;
+  double best = 1e300;
+  const int max_s = (int)std::max<int64_t>(1, std::min<int64_t>(32, K / 512));
+  for (int s = 1; s <= max_s; ++s) {
+    const double rounds = std::ceil((double)tiles * s / slots);
+    const double cost = rounds * t_block / s + (s > 1 ? (double)(s + 1) * 4.0 * (double)M * (double)N * t_byte : 0.0);
+    if (cost < best * 0.97) { best = cost; S = s; }
+  }
+  kps = ((K + S - 1) / S + 31) / 32 * 32;
+  S = (int)((K + kps - 1) / kps);
+}
+
+// ---------------------------------------------------------------------------
 // dW = dY^T @ x~      (M = d_out, N = d_in, K = tokens)
 // ---------------------------------------------------------------------------
 
 // bf16 halves: low halves of a and b -> (a.lo, b.lo); high halves -> (a.hi, b.hi)
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
-
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  typedef float v2f __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
-}
 
 __device__ __forceinline__ float sbyte(uint32_t w, int b) { return (float)(int)(int8_t)((w >> (8 * b)) & 0xFFu); }
 
@@ -416,17 +553,53 @@ int dw_splits(int64_t T, int64_t d_in, int64_t d_out) {
 
 }  // namespace
 
+// Workspace of the dW path: dY^T and x~^T ([d_out, T8] and [d_in, T8] bf16),
+// then the split-K partial sums.
+struct DwLayout {
+  size_t dyt, xt, part, total;
+  int S;
+  int64_t kps;
+};
+
+DwLayout dw_layout(int64_t T, int64_t d_in, int64_t d_out) {
+  DwLayout L{};
+  const int64_t T8 = round8(T);
+  nt_splits(d_out, d_in, T8, L.S, L.kps);
+  L.dyt = 0;
+  L.xt = align256((size_t)d_out * (size_t)T8 * 2);
+  L.part = L.xt + align256((size_t)d_in * (size_t)T8 * 2);
+  L.total = L.part + (L.S > 1 ? (size_t)L.S * (size_t)d_out * (size_t)d_in * sizeof(float) : 0);
+  return L;
+}
+
+// The dX transpose plane and the dW buffers are used one after the other on
+// the same stream, so they share the workspace.
 size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flags) {
-  if (!(flags & SBL_BWD_DW) || T == 0) return 0;
-  const int S = dw_splits(T, d_in, d_out);
-  if (S <= 1) return 0;
-  return (size_t)S * (size_t)d_out * (size_t)d_in * sizeof(float);
+  size_t dx = 0, dw = 0;
+  if ((flags & SBL_BWD_DX) && dx_direct(T, d_in, d_out)) dx = align256((size_t)d_out * (size_t)d_in * 2);
+  if ((flags & SBL_BWD_DW) && T > 0) {
+    if (dw_direct(T, d_in, d_out)) {
+      dw = dw_layout(T, d_in, d_out).total;
+    } else {
+      const int S = dw_splits(T, d_in, d_out);
+      if (S > 1) dw = (size_t)S * (size_t)d_out * (size_t)d_in * sizeof(float);
+    }
+  }
+  return std::max(dx, dw);
 }
 
 hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                            const uint16_t* dY, int64_t T, int64_t d_in, int64_t d_out, void* dX, int dx_dtype,
                            float* dW, int flags, void* ws, hipStream_t s) {
-  if ((flags & SBL_BWD_DX) && T > 0) {
+  if ((flags & SBL_BWD_DX) && dx_direct(T, d_in, d_out)) {
+    uint16_t* WT = (uint16_t*)ws;
+    const dim3 tgrid((unsigned)((d_out + kTrO - 1) / kTrO), (unsigned)((d_in / 8 + kTrG - 1) / kTrG));
+    hipLaunchKernelGGL(k_weff_t_bf16, tgrid, dim3(256), 0, s, codes, (int)d_out, (int)d_in, WT);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_gemm_nt_bf16(dY, WT, T, d_in, d_out, gamma, dX, dx_dtype, s);
+    if (e != hipSuccess) return e;
+  } else if ((flags & SBL_BWD_DX) && T > 0) {
     const dim3 grid((unsigned)(((d_in + kBN - 1) / kBN) * ((T + kBM - 1) / kBM)));
     const bool vec = d_out % 8 == 0;
     if (dx_dtype == SBL_F32) {
@@ -444,6 +617,32 @@ hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8
     if (T == 0) {
       hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 65536)), dim3(256), 0, s, dW, n);
       return hipGetLastError();
+    }
+    if (dw_direct(T, d_in, d_out)) {
+      const DwLayout L = dw_layout(T, d_in, d_out);
+      const int64_t T8 = round8(T);
+      uint16_t* dyt = (uint16_t*)((char*)ws + L.dyt);
+      uint16_t* xt = (uint16_t*)((char*)ws + L.xt);
+      const dim3 g1((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_out + kTT - 1) / kTT));
+      if (d_out % 8 == 0)
+        hipLaunchKernelGGL((k_token_major<false, true>), g1, dim3(256), 0, s, dY, nullptr, (int)T, (int)d_out, (int)T8, dyt);
+      else
+        hipLaunchKernelGGL((k_token_major<false, false>), g1, dim3(256), 0, s, dY, nullptr, (int)T, (int)d_out, (int)T8, dyt);
+      const dim3 g2((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_in + kTT - 1) / kTT));
+      hipLaunchKernelGGL((k_token_major<true, true>), g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      float* target = L.S > 1 ? (float*)((char*)ws + L.part) : dW;
+      e = launch_gemm_nt_bf16(dyt, xt, d_out, d_in, T8, nullptr, target, SBL_F32, s, L.S, L.kps);
+      if (e != hipSuccess) return e;
+      if (L.S > 1) {
+        const int64_t n4 = n / 4;
+        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 65536)), dim3(256), 0,
+                           s, (const float4*)target, n4, L.S, (float4*)dW);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
     }
     const int S = dw_splits(T, d_in, d_out);
     const int64_t kps = ((T + S - 1) / S + kBK - 1) / kBK * kBK;

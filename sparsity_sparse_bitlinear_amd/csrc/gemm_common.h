@@ -84,6 +84,47 @@ __device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t of
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Direct-to-LDS loads.  One buffer_load_dwordx4 ... lds per wave moves 64
+// lanes x 16 bytes from arbitrary per-lane global offsets into 1 KB of LDS
+// starting at a wave-uniform address (lane l lands at +16 l), without passing
+// through registers.  Out-of-range offsets write zeros.  Completion is tracked
+// by vmcnt, so a consumer waits on vmcnt and then meets the other waves at a
+// barrier; nothing else orders these writes.
+// ---------------------------------------------------------------------------
+// soff (wave-uniform) is added to every lane's offset.  Callers size the
+// resource so that in-range accesses stay below num_records with or without
+// soff, and send out-of-range lanes to kOOB.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_wave_base, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SBL_LDS void*)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt
+// left at their maxima so they are not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Same, and also wait for all LDS reads of this wave (lgkmcnt = 0).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which would
+// wait for every outstanding load, including the prefetches still in flight).
+// The empty asm keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void barrier_only() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Row index (within the wave tile) of accumulator register r of lane l.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 

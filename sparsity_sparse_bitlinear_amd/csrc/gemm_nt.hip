@@ -1,0 +1,228 @@
+// C = alpha * A B^T on gfx950 bf16 matrix cores, both operands K-contiguous.
+//
+//   C[m, n] = alpha * sum_k A[m, k] * B[n, k]     A [M, K], B [N, K] bf16 row-major,
+//                                                  C [M, N] float32 or bf16
+//
+// This is the plain-GEMM engine behind both products of the Dual-STE backward
+// ([SUM] 方法步骤详情 step (7)):
+//   dX = gamma * dY W_eff      A = dY [T, d_out], B = W_eff^T [d_in, d_out]
+//                              (expanded once per call into bf16 {-1, 0, +1}, exact)
+//   dW = dY^T x~               A = dY^T [d_out, T], B = x~^T [d_in, T]
+//                              (both transposed once per call, token-contiguous)
+//
+// Operand tiles move from global memory to LDS with direct-to-LDS buffer loads
+// (no register staging and no LDS store instructions), through a ring of three
+// LDS stages: while the waves multiply stage k, the loads of stage k + 1 are in
+// flight and those of stage k + 2 are issued.  One barrier per K step.  The LDS
+// layout is the one of gemm_common.h (64-byte K rows, XOR-swizzled 16-byte
+// chunks): each lane of a direct load picks the global chunk that belongs at
+// its LDS position, which is how the swizzle is applied without a store.
+#include "gemm_common.h"
+
+namespace sbl {
+
+namespace {
+
+using namespace gemm;
+
+// Block tile 256 x 256 computed by 8 waves (2 along M x 4 along N, 128 x 64
+// each): one block per CU.  Loading 32 KB per K step for 2M multiply-adds
+// halves the bytes each CU pulls through its L1 per matrix instruction
+// compared with a 256 x 128 tile, which is what the L2-to-CU path can feed.
+constexpr int kNT = 512;                  // threads per block
+constexpr int kBNn = 256;                 // block cols (N)
+constexpr int kStages = 4;
+constexpr int kStageA = kBM * kRow;       // 16 KB: 256 rows x 32 bf16
+constexpr int kStageB = kBNn * kRow;      // 16 KB
+constexpr int kStage = kStageA + kStageB; // 32 KB
+constexpr int kDmaA = kBM * 4 / kNT;      // direct loads per thread per K step (A)
+constexpr int kDmaB = kBNn * 4 / kNT;     // (B)
+constexpr int kDmaStep = kDmaA + kDmaB;
+constexpr int kKStep = kRow / 2;          // 32 bf16 per K step
+
+// Requires K % 8 == 0 (16-byte rows, K chunks never straddle a row end).
+// blockIdx.y selects a K range [kps * y, kps * (y + 1)) (split-K); block y writes
+// its partial product to C + y * M * N.  alpha_p == nullptr means alpha = 1.
+template <int OUT>
+__global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restrict__ A,
+                                                              const uint16_t* __restrict__ B, int M, int N, int K,
+                                                              int kps, const float* __restrict__ alpha_p,
+                                                              void* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS targets live in SGPRs
+  const int wm0 = (wave >> 2) * kWM;
+  const int wn0 = (wave & 3) * kWN;
+  int mt, nt;
+  xcd_tile(blockIdx.x, (M + kBM - 1) / kBM, (N + kBNn - 1) / kBNn, mt, nt);
+  const int m0 = mt * kBM;
+  const int n0 = nt * kBNn;
+  const int kbeg = blockIdx.y * kps;
+  const int kend = min(K, kbeg + kps);
+  const int nk = (kend - kbeg + kKStep - 1) / kKStep;  // >= 1: the host never makes an empty split
+  const int rows_a = min(kBM, M - m0);
+  const int rows_b = min(kBNn, N - n0);
+  const uint16_t* a_base = A + (int64_t)m0 * K;
+  const uint16_t* b_base = B + (int64_t)n0 * K;
+
+  // Direct-load lanes: LDS chunk position p (16 bytes) of a stage holds row
+  // p / 4, logical chunk (p % 4) ^ ((row / 4) % 4), i.e. swz(row, c) = 16 p.
+  // Wave w fills positions [64 (kDma w + i), +64) with its i-th load.
+  uint32_t a_off[kDmaA], b_off[kDmaB];
+  int a_k[kDmaA], b_k[kDmaB];
+#pragma unroll
+  for (int i = 0; i < kDmaA; ++i) {
+    const int p = 64 * (kDmaA * wave + i) + lane;
+    const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
+    a_off[i] = (uint32_t)(r * K * 2 + 16 * c);
+    a_k[i] = 8 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < kDmaB; ++i) {
+    const int p = 64 * (kDmaB * wave + i) + lane;
+    const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
+    b_off[i] = (uint32_t)(r * K * 2 + 16 * c);
+    b_k[i] = 8 * c;
+  }
+
+  // Loads of K step kt into stage st.  The resources span the valid rows of the
+  // block (rows past M or N read as zero) and the K offset rides in soffset;
+  // chunks past K (last step only) are sent out of range explicitly.
+  const auto ar = make_rsrc(a_base, clamp_bytes((int64_t)rows_a * K * 2));
+  const auto br = make_rsrc(b_base, clamp_bytes((int64_t)rows_b * K * 2));
+  const bool ktail = ((kend - kbeg) % kKStep) != 0;
+  auto issue = [&](int kt, int st) {
+    const int k0 = kbeg + kt * kKStep;
+    const uint32_t soff = (uint32_t)k0 * 2;
+    char* sa = lds + st * kStage;
+    char* sb = sa + kStageA;
+#pragma unroll
+    for (int i = 0; i < kDmaA; ++i)
+      dma16(ar, sa + 1024 * (kDmaA * wave + i), ktail && k0 + a_k[i] >= kend ? kOOB : a_off[i], soff);
+#pragma unroll
+    for (int i = 0; i < kDmaB; ++i)
+      dma16(br, sb + 1024 * (kDmaB * wave + i), ktail && k0 + b_k[i] >= kend ? kOOB : b_off[i], soff);
+  };
+
+  v16f acc[kMI][kNJ];
+#pragma unroll
+  for (int i = 0; i < kMI; ++i)
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Fragments of one 16-wide K slice (ks = 0, 1 of a K step) of a stage.
+  auto rd = [&](int st, int ks, v8bf (&fa)[kMI], v8bf (&fb)[kNJ]) {
+    const char* a = lds + st * kStage;
+    const char* b = a + kStageA;
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) fa[i] = __builtin_bit_cast(v8bf, frag(a, wm0 + 32 * i, ks, lane));
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) fb[j] = __builtin_bit_cast(v8bf, frag(b, wn0 + 32 * j, ks, lane));
+  };
+  auto mm = [&](const v8bf (&fa)[kMI], const v8bf (&fb)[kNJ]) {
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  // Step k (stage k % S has landed; its first K slice is already in fa0/fb0):
+  //   read slice 1 of stage k             | multiply slice 0 of step k
+  //   wait: own reads done, own loads of step k + 1 landed; barrier (every
+  //   wave's loads of k + 1 landed, every wave done reading stage k)
+  //   refill stage k % S with step k + S
+  //   read slice 0 of stage k + 1         | multiply slice 1 of step k
+  // so every group of LDS reads has 8 matrix instructions to hide behind.
+  // Past the last step the load index is clamped: the redundant loads go to a
+  // stage nobody reads again.
+  v8bf fa0[kMI], fb0[kNJ], fa1[kMI], fb1[kNJ];
+  const int last = nk - 1;
+#pragma unroll
+  for (int s0 = 0; s0 < kStages; ++s0) issue(min(s0, last), s0);
+  wait_vmcnt<(kStages - 1) * kDmaStep>();
+  barrier_only();
+  rd(0, 0, fa0, fb0);
+  int sc = 0;
+  for (int k = 0; k < nk; ++k) {
+    const int sn = sc == kStages - 1 ? 0 : sc + 1;
+    rd(sc, 1, fa1, fb1);
+    mm(fa0, fb0);
+    // issue order: one matrix instruction (its operands were read a step
+    // earlier), the 6 LDS reads, the other 7 matrix instructions
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kMI * kNJ - 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_lgkm0<(kStages - 2) * kDmaStep>();
+    barrier_only();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(min(k + kStages, last), sc);
+    rd(sn, 0, fa0, fb0);
+    mm(fa1, fb1);
+    // LDS reads first, then matrix instructions with the direct loads between them
+    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 1);
+#pragma unroll
+    for (int i = 0; i < kDmaStep; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMI * kNJ - kDmaStep, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    sc = sn;
+  }
+  // No direct loads may still target LDS when the block retires.
+  wait_vmcnt<0>();
+
+  const float alpha = alpha_p ? *alpha_p : 1.0f;
+  C = (char*)C + (size_t)blockIdx.y * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
+#pragma unroll
+  for (int i = 0; i < kMI; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + wm0 + 32 * i + acc_row(r, lane);
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j) {
+        const int n = n0 + wn0 + 32 * j + (lane & 31);
+        if (n >= N) continue;
+        const float v = acc[i][j][r] * alpha;
+        const int64_t off = (int64_t)m * N + n;
+        if constexpr (OUT == SBL_F32) ((float*)C)[off] = v;
+        else ((__bf16*)C)[off] = (__bf16)v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool gemm_nt_bf16_supported(int64_t M, int64_t N, int64_t K) {
+  // K % 8: whole 16-byte chunks per row; the per-block resources must stay
+  // below the 2 GiB range of a buffer offset.
+  return M > 0 && N > 0 && K > 0 && K % 8 == 0 && (int64_t)kBM * K * 2 <= kMaxRsrcBytes &&
+         (int64_t)kBNn * K * 2 <= kMaxRsrcBytes;
+}
+
+int64_t gemm_nt_bf16_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + kBNn - 1) / kBNn); }
+
+hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
+                               const float* alpha, void* C, int out_dtype, hipStream_t s, int splits,
+                               int64_t k_per_split) {
+  if (splits < 1) splits = 1;
+  if (splits == 1) k_per_split = K;
+  const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
+  if (out_dtype == SBL_F32)
+    hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K, (int)k_per_split,
+                       alpha, C);
+  else
+    hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_BF16>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
+                       (int)k_per_split, alpha, C);
+  return hipGetLastError();
+}
+
+}  // namespace sbl

@@ -65,6 +65,17 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t T, int64_t d_in, int8_t* 
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s);
 
+// C[M, N] = alpha * A[M, K] B[N, K]^T, bf16 operands, float32 or bf16 output
+// (gemm_nt.hip).  Only for shapes where gemm_nt_bf16_supported() holds.
+// alpha == nullptr means 1.  With splits > 1 the K range is cut into pieces of
+// k_per_split (a multiple of 32, none empty) and piece z writes its partial
+// product to C + z * M * N.
+bool gemm_nt_bf16_supported(int64_t M, int64_t N, int64_t K);
+int64_t gemm_nt_bf16_tiles(int64_t M, int64_t N);
+hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
+                               const float* alpha, void* C, int out_dtype, hipStream_t s, int splits = 1,
+                               int64_t k_per_split = 0);
+
 size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flags);
 hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                            const uint16_t* dY, int64_t T, int64_t d_in, int64_t d_out, void* dX, int dx_dtype,

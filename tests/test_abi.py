@@ -83,7 +83,11 @@ def test_forward_validation():
 
 def test_backward_validation():
     f = lib.sbl_backward
-    assert lib.sbl_backward_workspace_size(64, 256, 256, 1) == 0     # dX needs no workspace
+    # dX: the bf16 transpose of W_eff (d_out % 8 == 0), else no workspace
+    assert lib.sbl_backward_workspace_size(64, 256, 256, 1) == 2 * 256 * 256
+    assert lib.sbl_backward_workspace_size(64, 256, 252, 1) == 0
+    assert lib.sbl_backward_workspace_size(0, 256, 256, 1) == 0
+    assert f(P, P, P, P, P, 4, 256, 256, P, 1, P, 1, NULL, 0, NULL) == WORKSPACE
     assert f(P, P, P, P, P, 4, 256, 256, P, 1, P, 0, NULL, 0, NULL) == INVALID   # no flags
     assert f(P, P, P, P, P, 4, 256, 256, P, 2, P, 4, NULL, 0, NULL) == INVALID   # unknown flag
     assert f(P, P, P, P, P, 4, 256, 256, P, 2, P, 1, NULL, 0, NULL) == INVALID   # I32 dX

@@ -180,7 +180,8 @@ def gpu_backward(W_bits, x_bits, dY_bits, n, dx_dtype=1):
     return dX, dW
 
 
-BWD_SHAPES = [(64, 256, 256), (77, 200, 328), (513, 136, 72), (1, 8, 8), (300, 40, 1032), (4096, 256, 2048)]
+BWD_SHAPES = [(64, 256, 256), (77, 200, 328), (513, 136, 72), (1, 8, 8), (300, 40, 1032), (4096, 256, 2048),
+              (45, 100, 64), (130, 12, 264), (1000, 520, 776)]
 
 
 @pytest.mark.parametrize("T,d_out,d_in", BWD_SHAPES)
