@@ -159,8 +159,12 @@ SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t*
 /* Backward (Dual STE)                                                        */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of workspace sbl_backward needs (split-K partial sums of dW for
- * shapes with few output tiles).  May be 0. */
+/* Bytes of workspace sbl_backward needs for these flags.  It holds the
+ * per-call operand copies of the matrix-core path -- W_eff^T as bf16
+ * ([d_in, d_out], for dX), dY^T and x~^T as bf16 ([d_out, T8] and
+ * [d_in, T8] with T8 = T rounded up to 8, for dW) -- and split-K partial sums
+ * of dW.  The dX and dW parts are used one after the other and share the
+ * space.  0 when nothing is needed (e.g. T = 0). */
 SBL_API size_t sbl_backward_workspace_size(int64_t T, int64_t d_in, int64_t d_out, int flags);
 
 /* Dual-STE backward ([SUM] 前置知识 > Straight-Through Estimator (STE);

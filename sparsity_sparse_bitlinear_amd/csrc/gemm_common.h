@@ -54,6 +54,25 @@ __device__ __forceinline__ void xcd_tile(int b, int gm, int gn, int& mt, int& nt
   nt = tile - mt * gn;
 }
 
+// Same split over the XCDs, but each XCD walks its range in groups of GM tile
+// rows, column by column inside a group: the blocks resident on an XCD at one
+// time then cover about a GM x (resident / GM) patch of the output, so both
+// operands are shared in its L2 instead of one of them streaming through.
+__device__ __forceinline__ void xcd_tile_grouped(int b, int gm, int gn, int GM, int& mt, int& nt) {
+  const int nb = gm * gn;
+  int tile = b;
+  if (nb >= 8) {
+    const int x = b & 7, local = b >> 3;
+    const int q = nb >> 3, r = nb & 7;
+    tile = x * q + min(x, r) + local;
+  }
+  const int g = tile / (GM * gn);
+  const int rem = tile - g * GM * gn;
+  const int rows = min(GM, gm - g * GM);
+  mt = g * GM + rem % rows;
+  nt = rem / rows;
+}
+
 // Buffer resource for raw (unformatted) loads of `bytes` bytes at `base`.
 // Accesses at offsets at or beyond `bytes` return zero, which is how tile rows
 // past the end of a matrix are zero-filled without per-lane selects.
@@ -98,6 +117,11 @@ __device__ __forceinline__ uint32_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t of
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_wave_base, uint32_t voff,
                                       uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SBL_LDS void*)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
+// 4-byte variant: lane l lands at +4 l (256 bytes per wave).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char* lds_wave_base, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SBL_LDS void*)lds_wave_base, 4, voff, soff, 0, 0);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding

@@ -22,6 +22,12 @@ namespace {
 
 using namespace gemm;
 
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
+}
+
 // 4 two-bit codes (one byte) -> 4 int8 values.
 __device__ __forceinline__ uint32_t expand4(uint32_t byte4codes) {
   uint32_t x = byte4codes & 0xFFu;
@@ -188,6 +194,195 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_i8(const int8_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct-load forward (d_in % 64 == 0): block tile 256 tokens x 256 outputs,
+// 8 waves (2 along M x 4 along N, 128 x 64 each), one block per CU.  Per K
+// step of 64: the x_q tile (256 rows x 64 bytes, swizzled as in
+// gemm_common.h) and the code tile (256 rows x 8 code words = 16 bytes) move
+// to LDS with direct-to-LDS loads through a ring of kFS stages; each wave
+// expands the code words of its own B fragments in registers (one 32-bit word
+// = 16 codes = one MFMA operand of 16 int8).
+// ---------------------------------------------------------------------------
+constexpr int kFT = 512;                   // threads
+constexpr int kFBN = 256;                  // block cols (outputs)
+constexpr int kFS = 4;                     // LDS stages
+constexpr int kFStageA = kBM * kRow;       // 16 KB
+constexpr int kFStageB = kFBN * 16;        // 4 KB of code words
+constexpr int kFStage = kFStageA + kFStageB;
+constexpr int kFDmaA = kBM * 4 / kFT;      // 2 direct loads per thread per K step
+
+template <int OUT>
+__global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restrict__ xq,
+                                                         const uint16_t* __restrict__ codes,
+                                                         const float* __restrict__ gamma_p,
+                                                         const float* __restrict__ absmax, int T, int d_in,
+                                                         int d_out, void* __restrict__ y) {
+  __shared__ __attribute__((aligned(1024))) char lds[kFS * kFStage];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave >> 2) * kWM;
+  const int wn0 = (wave & 3) * kWN;
+  int mt, nt;
+  xcd_tile_grouped(blockIdx.x, (T + kBM - 1) / kBM, (d_out + kFBN - 1) / kFBN, 4, mt, nt);
+  const int m0 = mt * kBM;
+  const int n0 = nt * kFBN;
+  const int G = d_in >> 3;
+  const int nk = d_in >> 6;
+  const int rows_a = min(kBM, T - m0);
+  const int rows_b = min(kFBN, d_out - n0);
+  const auto ar = make_rsrc(xq + (int64_t)m0 * d_in, clamp_bytes((int64_t)rows_a * d_in));
+  const auto br = make_rsrc(codes + (int64_t)n0 * G, clamp_bytes((int64_t)rows_b * G * 2));
+
+  uint32_t a_off[kFDmaA];
+#pragma unroll
+  for (int i = 0; i < kFDmaA; ++i) {
+    const int p = 64 * (kFDmaA * wave + i) + lane;
+    const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
+    a_off[i] = (uint32_t)(r * d_in + 16 * c);
+  }
+  // code tile: 256 rows x 4 words of 32 bits (8 groups); every wave moves
+  // 2 x 64 words with 4-byte direct loads, word p = row p / 4, word p % 4
+  uint32_t b_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = 64 * (2 * wave + i) + lane;
+    b_off[i] = (uint32_t)((p >> 2) * G * 2 + 4 * (p & 3));
+  }
+
+  auto issue = [&](int kt, int st) {
+    char* sa = lds + st * kFStage;
+#pragma unroll
+    for (int i = 0; i < kFDmaA; ++i) dma16(ar, sa + 1024 * (kFDmaA * wave + i), a_off[i], (uint32_t)kt * 64);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma4(br, sa + kFStageA + 256 * (2 * wave + i), b_off[i], (uint32_t)kt * 16);
+  };
+
+  v16i acc[kMI][kNJ];
+#pragma unroll
+  for (int i = 0; i < kMI; ++i)
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+
+  // K slice ks (32 of the 64 k of a step): A fragments, and the code word
+  // (groups 4 ks + 2 (l / 32), +1) of output row wn0 + 32 j + l % 32.
+  auto rd = [&](int st, int ks, v4i (&fa)[kMI], uint32_t (&wb)[kNJ]) {
+    const char* a = lds + st * kFStage;
+    const char* b = a + kFStageA;
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) fa[i] = frag(a, wm0 + 32 * i, ks, lane);
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j)
+      wb[j] = *(const uint32_t*)(b + 16 * (wn0 + 32 * j + (lane & 31)) + 4 * (2 * ks + (lane >> 5)));
+  };
+  // The code fragment is the MFMA's first operand, so accumulator register r
+  // of lane l holds C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]: four
+  // consecutive outputs of one token per group of four registers.
+  auto mm = [&](const v4i (&fa)[kMI], const v4i (&fb)[kNJ]) {
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+  auto expand = [&](const uint32_t (&wb)[kNJ], v4i (&fb)[kNJ]) {
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) fb[j] = __builtin_bit_cast(v4i, expand16(wb[j]));
+  };
+
+  // Same schedule as the bf16 engine (read slice 1 while multiplying slice 0,
+  // wait + barrier in the middle of the step, refill the stage just read,
+  // read slice 0 of the next stage while multiplying slice 1), and the code
+  // words of the slice read in one half are expanded between the matrix
+  // instructions of that half, ready for the next.
+  v4i fa0[kMI], fa1[kMI], fb0[kNJ], fb1[kNJ];
+  uint32_t wb0[kNJ], wb1[kNJ];
+  const int last = nk - 1;
+#pragma unroll
+  for (int s0 = 0; s0 < kFS; ++s0) issue(min(s0, last), s0);
+  wait_vmcnt<(kFS - 1) * (kFDmaA + 2)>();
+  barrier_only();
+  rd(0, 0, fa0, wb0);
+  expand(wb0, fb0);
+  int sc = 0;
+  for (int k = 0; k < nk; ++k) {
+    const int sn = sc == kFS - 1 ? 0 : sc + 1;
+    rd(sc, 1, fa1, wb1);
+    mm(fa0, fb0);
+    expand(wb1, fb1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_lgkm0<(kFS - 2) * (kFDmaA + 2)>();
+    barrier_only();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(min(k + kFS, last), sc);
+    rd(sn, 0, fa0, wb0);
+    mm(fa1, fb1);
+    expand(wb0, fb0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    sc = sn;
+  }
+  wait_vmcnt<0>();
+
+  // Epilogue: each lane stores runs of 4 consecutive outputs of its token
+  // (8 or 16 bytes); element stores only where a run leaves the matrix or
+  // rows are not 4-aligned.
+  const float g127 = *gamma_p * (1.0f / 127.0f);
+  const bool vec_out = (d_out & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < kMI; ++i) {
+    const int m = m0 + wm0 + 32 * i + (lane & 31);
+    if (m >= T) continue;
+    const float s = g127 * absmax[m];
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
+        if (n >= d_out) continue;
+        const int64_t off = (int64_t)m * d_out + n;
+        const int a0 = acc[i][j][4 * q], a1 = acc[i][j][4 * q + 1], a2 = acc[i][j][4 * q + 2],
+                  a3 = acc[i][j][4 * q + 3];
+        if (vec_out && n + 4 <= d_out) {
+          if constexpr (OUT == SBL_I32) {
+            *(int4*)((int*)y + off) = make_int4(a0, a1, a2, a3);
+          } else if constexpr (OUT == SBL_F32) {
+            *(float4*)((float*)y + off) = make_float4((float)a0 * s, (float)a1 * s, (float)a2 * s, (float)a3 * s);
+          } else {
+            *(uint2*)((__bf16*)y + off) =
+                make_uint2(cvt_pk_bf16((float)a0 * s, (float)a1 * s), cvt_pk_bf16((float)a2 * s, (float)a3 * s));
+          }
+        } else {
+          const int av[4] = {a0, a1, a2, a3};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (n + u >= d_out) break;
+            if constexpr (OUT == SBL_I32) ((int*)y)[off + u] = av[u];
+            else if constexpr (OUT == SBL_F32) ((float*)y)[off + u] = (float)av[u] * s;
+            else ((__bf16*)y)[off + u] = (__bf16)((float)av[u] * s);
+          }
+        }
+      }
+    }
+  }
+}
+
 template <bool VEC>
 hipError_t launch_fwd_v(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax, int64_t T,
                         int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
@@ -215,6 +410,25 @@ hipError_t launch_fwd_v(const uint16_t* codes, const float* gamma, const int8_t*
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (d_in % 64 == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes) {
+    const int64_t nb = ((d_out + kFBN - 1) / kFBN) * ((T + kBM - 1) / kBM);
+    const dim3 grid((unsigned)nb), block(kFT);
+    switch (y_dtype) {
+      case SBL_F32:
+        hipLaunchKernelGGL((k_fwd_i8_direct<SBL_F32>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T, (int)d_in,
+                           (int)d_out, y);
+        break;
+      case SBL_BF16:
+        hipLaunchKernelGGL((k_fwd_i8_direct<SBL_BF16>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+                           (int)d_in, (int)d_out, y);
+        break;
+      default:
+        hipLaunchKernelGGL((k_fwd_i8_direct<SBL_I32>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T, (int)d_in,
+                           (int)d_out, y);
+        break;
+    }
+    return hipGetLastError();
+  }
   if (d_in % 64 == 0) return launch_fwd_v<true>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
   return launch_fwd_v<false>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
 }

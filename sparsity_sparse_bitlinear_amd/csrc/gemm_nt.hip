@@ -29,6 +29,12 @@ using namespace gemm;
 // each): one block per CU.  Loading 32 KB per K step for 2M multiply-adds
 // halves the bytes each CU pulls through its L1 per matrix instruction
 // compared with a 256 x 128 tile, which is what the L2-to-CU path can feed.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
+}
+
 constexpr int kNT = 512;                  // threads per block
 constexpr int kBNn = 256;                 // block cols (N)
 constexpr int kStages = 4;
@@ -56,7 +62,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   const int wm0 = (wave >> 2) * kWM;
   const int wn0 = (wave & 3) * kWN;
   int mt, nt;
-  xcd_tile(blockIdx.x, (M + kBM - 1) / kBM, (N + kBNn - 1) / kBNn, mt, nt);
+  xcd_tile_grouped(blockIdx.x, (M + kBM - 1) / kBM, (N + kBNn - 1) / kBNn, 4, mt, nt);
   const int m0 = mt * kBM;
   const int n0 = nt * kBNn;
   const int kbeg = blockIdx.y * kps;
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     for (int i = 0; i < kMI; ++i)
 #pragma unroll
       for (int j = 0; j < kNJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
 
   // Step k (stage k % S has landed; its first K slice is already in fa0/fb0):
@@ -178,22 +184,37 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // No direct loads may still target LDS when the block retires.
   wait_vmcnt<0>();
 
+  // B is the MFMA's first operand, so accumulator register r of lane l holds
+  // C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]: each lane stores runs
+  // of 4 consecutive outputs of one row (16 bytes in float32, 8 in bf16).
   const float alpha = alpha_p ? *alpha_p : 1.0f;
   C = (char*)C + (size_t)blockIdx.y * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
+  const bool vec_out = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < kMI; ++i) {
+    const int m = m0 + wm0 + 32 * i + (lane & 31);
+    if (m >= M) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = m0 + wm0 + 32 * i + acc_row(r, lane);
-      if (m >= M) continue;
+    for (int j = 0; j < kNJ; ++j) {
 #pragma unroll
-      for (int j = 0; j < kNJ; ++j) {
-        const int n = n0 + wn0 + 32 * j + (lane & 31);
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
         if (n >= N) continue;
-        const float v = acc[i][j][r] * alpha;
         const int64_t off = (int64_t)m * N + n;
-        if constexpr (OUT == SBL_F32) ((float*)C)[off] = v;
-        else ((__bf16*)C)[off] = (__bf16)v;
+        const float v0 = acc[i][j][4 * q] * alpha, v1 = acc[i][j][4 * q + 1] * alpha;
+        const float v2 = acc[i][j][4 * q + 2] * alpha, v3 = acc[i][j][4 * q + 3] * alpha;
+        if (vec_out && n + 4 <= N) {
+          if constexpr (OUT == SBL_F32) *(float4*)((float*)C + off) = make_float4(v0, v1, v2, v3);
+          else *(uint2*)((__bf16*)C + off) = make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
+        } else {
+          const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (n + u >= N) break;
+            if constexpr (OUT == SBL_F32) ((float*)C)[off + u] = vv[u];
+            else ((__bf16*)C)[off + u] = (__bf16)vv[u];
+          }
+        }
       }
     }
   }
