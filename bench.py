@@ -9,7 +9,7 @@ all seeded synthetic data already resident in HBM.
 One step = for each of the 7 linears, in order:
   sbl_quant_mask_pack (gamma, 6:8 mask, codes; recomputed every step)
   sbl_act_quant       (per-token absmax int8)
-  sbl_forward         (int8 MFMA, y float32)
+  sbl_forward         (int8 MFMA, y bf16)
   sbl_backward(dX)    (bf16 MFMA, dX bf16)
   sbl_backward(dW)    (bf16 MFMA, dW float32, dense)
 Metric: tokens per second of whole steps.  Prints one JSON line.
@@ -89,10 +89,10 @@ def main():
             qws=torch.empty((max(16, sbl.quant_workspace_size(d_out, d_in)),), dtype=torch.uint8, device=dev),
             x_q=torch.empty((T, d_in), dtype=torch.int8, device=dev),
             absmax=torch.empty((T,), dtype=torch.float32, device=dev),
-            y=torch.empty((T, d_out), dtype=torch.float32, device=dev),
+            y=torch.empty((T, d_out), dtype=torch.bfloat16, device=dev),
             dX=torch.empty((T, d_in), dtype=torch.bfloat16, device=dev),
             dW=torch.empty((d_out, d_in), dtype=torch.float32, device=dev),
-            bws=torch.empty((max(16, sbl.backward_workspace_size(T, d_in, d_out, sbl.BWD_DW)),),
+            bws=torch.empty((max(16, sbl.backward_workspace_size(T, d_in, d_out, sbl.BWD_DX | sbl.BWD_DW)),),
                             dtype=torch.uint8, device=dev),
         ))
     torch.cuda.synchronize()
@@ -111,10 +111,10 @@ def main():
             mark(1)
             sbl.act_quant(Lr["x"], x_q=Lr["x_q"], absmax=Lr["absmax"])
             mark(2)
-            sbl.forward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], out_dtype=sbl.F32, y=Lr["y"])
+            sbl.forward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], out_dtype=sbl.BF16, y=Lr["y"])
             mark(3)
             sbl.backward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], Lr["dY"], need_dx=True, need_dw=False,
-                         dx_dtype=sbl.BF16, dX=Lr["dX"])
+                         dx_dtype=sbl.BF16, dX=Lr["dX"], workspace=Lr["bws"])
             mark(4)
             sbl.backward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], Lr["dY"], need_dx=False, need_dw=True,
                          dW=Lr["dW"], workspace=Lr["bws"])
@@ -172,15 +172,20 @@ def main():
                                  frac_bf16_issued=sum(w["dx_issued"] for w in work) / (tot_ms[3] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS),
         "backward_dw_bf16": dict(ms=tot_ms[4], TFLOPs=rate("dw") / 1e12, frac_bf16=rate("dw") / 1e12 / BF16_PEAK_TFLOPS),
     }
-    gemm_parts = {"fwd": ("forward_int8", "TOP/s", INT8_PEAK_TOPS), "dx": ("backward_dx_bf16", "TFLOP/s", BF16_PEAK_TFLOPS),
-                  "dw": ("backward_dw_bf16", "TFLOP/s", BF16_PEAK_TFLOPS)}
+    # HIP kernels behind each timed call (the events bracket the whole call)
+    gemm_parts = {
+        "fwd": ("forward_int8", "TOP/s", INT8_PEAK_TOPS, ["k_fwd_i8_direct<bf16>"]),
+        "dx": ("backward_dx_bf16", "TFLOP/s", BF16_PEAK_TFLOPS, ["k_weff_t_bf16", "k_gemm_nt_bf16<bf16>"]),
+        "dw": ("backward_dw_bf16", "TFLOP/s", BF16_PEAK_TFLOPS,
+               ["k_token_major<dY>", "k_token_major<x~>", "k_gemm_nt_bf16<f32>", "k_splitk_reduce (split-K shapes)"]),
+    }
     dom = max(gemm_parts, key=lambda p: tot_ms[parts.index(p)])
-    dname, dunit, dpeak = gemm_parts[dom]
+    dname, dunit, dpeak, dkernels = gemm_parts[dom]
     n_launch = len(layers)
     achieved = sum(w[dom] for w in work) / n_launch / (tot_ms[parts.index(dom)] / n_launch * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 1), "peak": dpeak,
                 "unit": dunit, "frac": round(achieved / dpeak, 4), "traffic": None,
-                "launches_per_step": n_launch,
+                "launches_per_step": n_launch, "hip_kernels": dkernels,
                 "avg_launch_ms": round(tot_ms[parts.index(dom)] / n_launch, 4)}
 
     # CPU baseline: the oracle on a bounded sample, on this host's cores.
@@ -203,7 +208,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "n_keep": n_keep, "m": 8,
                    "linears": [f"{Lr['name']} {Lr['d_in']}->{Lr['d_out']}" for Lr in layers],
-                   "y_dtype": "f32", "dx_dtype": "bf16", "dw_dtype": "f32"},
+                   "y_dtype": "bf16", "dx_dtype": "bf16", "dw_dtype": "f32"},
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},

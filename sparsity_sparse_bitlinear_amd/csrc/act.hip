@@ -24,23 +24,30 @@ __device__ __forceinline__ uint32_t max_mag2(uint32_t w) {
   return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
 }
 
-__device__ __forceinline__ int quant_one(uint32_t h16, int k, float as) {
-  const float x = __uint_as_float(h16 << 16);
-  const float xs = ldexpf(x, k);
-  return (int)rintf((127.0f * xs) / as);
+// Fast path: qf = fl(x' * fl(127 / a')) differs from the exact quotient
+// q = 127 x' / a' by less than |q| 2^-23 <= 2^-16 (|q| <= 127).  When qf is
+// more than 2^-14 away from a half-integer, rint(qf) is therefore the integer
+// nearest to q; otherwise (ties included) the element takes the division path,
+// which is exact as stated above.
+__device__ __forceinline__ int quant_one(uint32_t h16, int k, float as, float c) {
+  const float xs = ldexpf(__uint_as_float(h16 << 16), k);
+  const float qf = xs * c;
+  float r = rintf(qf);
+  if (__builtin_expect(fabsf(qf - r) > 0.5f - 0x1p-14f, 0)) r = rintf((127.0f * xs) / as);
+  return (int)r;
 }
 
-__device__ __forceinline__ uint32_t quant_word_pair(uint32_t w0, uint32_t w1, int k, float as) {
-  const int q0 = quant_one(w0 & 0xFFFFu, k, as);
-  const int q1 = quant_one(w0 >> 16, k, as);
-  const int q2 = quant_one(w1 & 0xFFFFu, k, as);
-  const int q3 = quant_one(w1 >> 16, k, as);
+__device__ __forceinline__ uint32_t quant_word_pair(uint32_t w0, uint32_t w1, int k, float as, float c) {
+  const int q0 = quant_one(w0 & 0xFFFFu, k, as, c);
+  const int q1 = quant_one(w0 >> 16, k, as, c);
+  const int q2 = quant_one(w1 & 0xFFFFu, k, as, c);
+  const int q3 = quant_one(w1 >> 16, k, as, c);
   return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
          ((uint32_t)(q3 & 0xFF) << 24);
 }
 
-__device__ __forceinline__ uint2 quant_chunk(uint4 v, int k, float as) {
-  return make_uint2(quant_word_pair(v.x, v.y, k, as), quant_word_pair(v.z, v.w, k, as));
+__device__ __forceinline__ uint2 quant_chunk(uint4 v, int k, float as, float c) {
+  return make_uint2(quant_word_pair(v.x, v.y, k, as, c), quant_word_pair(v.z, v.w, k, as, c));
 }
 
 template <int NC>
@@ -84,12 +91,13 @@ __global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ 
   (void)frexpf(a, &e);  // a = f * 2^e, f in [0.5, 1)
   const int k = 1 - e;  // a * 2^k in [1, 2)
   const float as = ldexpf(a, k);
+  const float c127 = 127.0f / as;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int idx = lane + 64 * c;
-    if (idx < nch) out[idx] = quant_chunk(v[c], k, as);
+    if (idx < nch) out[idx] = quant_chunk(v[c], k, as, c127);
   }
-  for (int idx = lane + 64 * NC; idx < nch; idx += 64) out[idx] = quant_chunk(row[idx], k, as);
+  for (int idx = lane + 64 * NC; idx < nch; idx += 64) out[idx] = quant_chunk(row[idx], k, as, c127);
 }
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t T, int64_t d_in, int8_t* xq, float* absmax, hipStream_t s) {

@@ -245,11 +245,11 @@ __global__ __launch_bounds__(256) void k_weff_t_bf16(const uint16_t* __restrict_
 //   dYT[o, t] = dY[t, o]                          (bf16 copy)
 //   xT [i, t] = bf16(x_q[t, i] * (a_t / 127))     (x~, rounded once to bf16)
 // Both [C, T8] with T8 = T rounded up to 8; columns t >= T are zero.  A block
-// moves a 64 x 64 tile through LDS: rows of the source are read in 16-byte
+// moves a 128 x 128 tile through LDS: rows of the source are read in 16-byte
 // (bf16) or 8-byte (int8) pieces, rows of the result are written as 16-byte
 // runs of 8 consecutive t.
 // ---------------------------------------------------------------------------
-constexpr int kTT = 64;
+constexpr int kTT = 128;
 
 template <bool DEQ, bool VEC>
 __global__ __launch_bounds__(256) void k_token_major(const void* __restrict__ src, const float* __restrict__ absmax,
@@ -257,9 +257,10 @@ __global__ __launch_bounds__(256) void k_token_major(const void* __restrict__ sr
   __shared__ uint32_t tile[kTT][kTT / 2 + 1];  // [t][c pair], bf16 pairs; odd pitch spreads the banks
   const int t0 = blockIdx.x * kTT, c0 = blockIdx.y * kTT;
   const int tid = threadIdx.x;
-  // phase 1: 64 rows t x 8 pieces of 8 columns
+  // phase 1: 128 rows t x 16 pieces of 8 columns (256-byte bf16 / 128-byte int8 row segments)
+#pragma unroll 4
   for (int e = tid; e < kTT * (kTT / 8); e += 256) {
-    const int r = e >> 3, pc = e & 7;
+    const int r = e >> 4, pc = e & 15;
     const int t = t0 + r, c = c0 + 8 * pc;
     uint32_t w[4] = {0u, 0u, 0u, 0u};
     if (t < T) {
@@ -295,9 +296,10 @@ __global__ __launch_bounds__(256) void k_token_major(const void* __restrict__ sr
     for (int u = 0; u < 4; ++u) tile[r][4 * pc + u] = w[u];
   }
   __syncthreads();
-  // phase 2: 64 rows c x 8 runs of 8 t
+  // phase 2: 128 rows c x 16 runs of 8 t (256-byte row segments)
+#pragma unroll 4
   for (int e = tid; e < kTT * (kTT / 8); e += 256) {
-    const int cl = e >> 3, rt = e & 7;
+    const int cl = e >> 4, rt = e & 15;
     const int c = c0 + cl, t = t0 + 8 * rt;
     if (c >= C || t >= T8) continue;
     uint32_t v[4];
@@ -324,7 +326,7 @@ bool dw_direct(int64_t T, int64_t d_in, int64_t d_out) {
 
 // K splits for the plain GEMM engine (one 256 x 256 block per CU): pick S to
 // minimise rounds(tiles * S) / S of full-K block time plus the partial-sum
-// traffic, with K pieces that are whole 32-token steps.
+// traffic, with K pieces that are whole 64-token steps.
 void nt_splits(int64_t M, int64_t N, int64_t K, int& S, int64_t& kps) {
   const int64_t tiles = gemm_nt_bf16_tiles(M, N);
   const double slots = 256.0;
@@ -338,7 +340,7 @@ void nt_splits(int64_t M, int64_t N, int64_t K, int& S, int64_t& kps) {
     const double cost = rounds * t_block / s + (s > 1 ? (double)(s + 1) * 4.0 * (double)M * (double)N * t_byte : 0.0);
     if (cost < best * 0.97) { best = cost; S = s; }
   }
-  kps = ((K + S - 1) / S + 31) / 32 * 32;
+  kps = ((K + S - 1) / S + 63) / 64 * 64;  // whole 64-token K steps
   S = (int)((K + kps - 1) / kps);
 }
 

@@ -11,12 +11,12 @@
 //                              (both transposed once per call, token-contiguous)
 //
 // Operand tiles move from global memory to LDS with direct-to-LDS buffer loads
-// (no register staging and no LDS store instructions), through a ring of three
-// LDS stages: while the waves multiply stage k, the loads of stage k + 1 are in
-// flight and those of stage k + 2 are issued.  One barrier per K step.  The LDS
-// layout is the one of gemm_common.h (64-byte K rows, XOR-swizzled 16-byte
-// chunks): each lane of a direct load picks the global chunk that belongs at
-// its LDS position, which is how the swizzle is applied without a store.
+// (no register staging and no LDS store instructions) through two LDS stages
+// of one K step (64 bf16) each: a step's loads are issued one step ahead, in
+// the middle of the previous step.  Each lane of a direct load picks the
+// global chunk that belongs at its LDS position, which is how the swizzle
+// (see swz8) is applied without a store.  128-byte row pieces per K step let
+// every load cover whole cache lines.
 #include "gemm_common.h"
 
 namespace sbl {
@@ -26,7 +26,7 @@ namespace {
 using namespace gemm;
 
 // Block tile 256 x 256 computed by 8 waves (2 along M x 4 along N, 128 x 64
-// each): one block per CU.  Loading 32 KB per K step for 2M multiply-adds
+// each): one block per CU.  Loading 64 KB per K step for 4M multiply-adds
 // halves the bytes each CU pulls through its L1 per matrix instruction
 // compared with a 256 x 128 tile, which is what the L2-to-CU path can feed.
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
@@ -37,14 +37,22 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 
 constexpr int kNT = 512;                  // threads per block
 constexpr int kBNn = 256;                 // block cols (N)
-constexpr int kStages = 4;
-constexpr int kStageA = kBM * kRow;       // 16 KB: 256 rows x 32 bf16
-constexpr int kStageB = kBNn * kRow;      // 16 KB
-constexpr int kStage = kStageA + kStageB; // 32 KB
-constexpr int kDmaA = kBM * 4 / kNT;      // direct loads per thread per K step (A)
-constexpr int kDmaB = kBNn * 4 / kNT;     // (B)
+constexpr int kRowK = 128;                // bytes per LDS row: 64 bf16 per K step
+constexpr int kStages = 2;
+constexpr int kStageA = kBM * kRowK;      // 32 KB
+constexpr int kStageB = kBNn * kRowK;     // 32 KB
+constexpr int kStage = kStageA + kStageB; // 64 KB
+constexpr int kDmaA = kBM * 8 / kNT;      // 4
+constexpr int kDmaB = kBNn * 8 / kNT;     // 4
 constexpr int kDmaStep = kDmaA + kDmaB;
-constexpr int kKStep = kRow / 2;          // 32 bf16 per K step
+constexpr int kKStep = kRowK / 2;         // 64 bf16 per K step
+
+// LDS address of 16-byte chunk c (0..7) of K-row `row`.  A fragment read is 16
+// lanes on 16 consecutive rows, same chunk: the 8 even rows then sit in banks
+// 0-31 and the 8 odd rows in banks 32-63, and c ^ ((row / 2) % 8) gives each
+// of the 8 a different 16-byte bank group, so the read is conflict-free.  The
+// direct loads fill whole 1 KB runs (8 rows).
+__device__ __forceinline__ int swz8(int row, int c) { return row * kRowK + 16 * (c ^ ((row >> 1) & 7)); }
 
 // Requires K % 8 == 0 (16-byte rows, K chunks never straddle a row end).
 // blockIdx.y selects a K range [kps * y, kps * (y + 1)) (split-K); block y writes
@@ -74,21 +82,21 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   const uint16_t* b_base = B + (int64_t)n0 * K;
 
   // Direct-load lanes: LDS chunk position p (16 bytes) of a stage holds row
-  // p / 4, logical chunk (p % 4) ^ ((row / 4) % 4), i.e. swz(row, c) = 16 p.
+  // p / 8, logical chunk (p % 8) ^ ((row / 2) % 8), i.e. swz8(row, c) = 16 p.
   // Wave w fills positions [64 (kDma w + i), +64) with its i-th load.
   uint32_t a_off[kDmaA], b_off[kDmaB];
   int a_k[kDmaA], b_k[kDmaB];
 #pragma unroll
   for (int i = 0; i < kDmaA; ++i) {
     const int p = 64 * (kDmaA * wave + i) + lane;
-    const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
+    const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
     a_off[i] = (uint32_t)(r * K * 2 + 16 * c);
     a_k[i] = 8 * c;
   }
 #pragma unroll
   for (int i = 0; i < kDmaB; ++i) {
     const int p = 64 * (kDmaB * wave + i) + lane;
-    const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
+    const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
     b_off[i] = (uint32_t)(r * K * 2 + 16 * c);
     b_k[i] = 8 * c;
   }
@@ -120,14 +128,16 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Fragments of one 16-wide K slice (ks = 0, 1 of a K step) of a stage.
+  // Fragments of K slice ks (16 of the 64 k of a step) of a stage.
   auto rd = [&](int st, int ks, v8bf (&fa)[kMI], v8bf (&fb)[kNJ]) {
     const char* a = lds + st * kStage;
     const char* b = a + kStageA;
 #pragma unroll
-    for (int i = 0; i < kMI; ++i) fa[i] = __builtin_bit_cast(v8bf, frag(a, wm0 + 32 * i, ks, lane));
+    for (int i = 0; i < kMI; ++i)
+      fa[i] = __builtin_bit_cast(v8bf, *(const v4i*)(a + swz8(wm0 + 32 * i + (lane & 31), 2 * ks + (lane >> 5))));
 #pragma unroll
-    for (int j = 0; j < kNJ; ++j) fb[j] = __builtin_bit_cast(v8bf, frag(b, wn0 + 32 * j, ks, lane));
+    for (int j = 0; j < kNJ; ++j)
+      fb[j] = __builtin_bit_cast(v8bf, *(const v4i*)(b + swz8(wn0 + 32 * j + (lane & 31), 2 * ks + (lane >> 5))));
   };
   auto mm = [&](const v8bf (&fa)[kMI], const v8bf (&fb)[kNJ]) {
 #pragma unroll
@@ -136,50 +146,53 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       for (int j = 0; j < kNJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
+#define ORDER_SLICE(id)                                            \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, id);              \
+  __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, id);      \
+  __builtin_amdgcn_sched_group_barrier(0x008, kMI * kNJ - 1, id);
 
-  // Step k (stage k % S has landed; its first K slice is already in fa0/fb0):
-  //   read slice 1 of stage k             | multiply slice 0 of step k
-  //   wait: own reads done, own loads of step k + 1 landed; barrier (every
-  //   wave's loads of k + 1 landed, every wave done reading stage k)
-  //   refill stage k % S with step k + S
-  //   read slice 0 of stage k + 1         | multiply slice 1 of step k
-  // so every group of LDS reads has 8 matrix instructions to hide behind.
-  // Past the last step the load index is clamped: the redundant loads go to a
-  // stage nobody reads again.
+  // Step k (stage k % 2 has landed; slice 0 is already in fa0/fb0): each of
+  // the 4 slices is read while the previous one is multiplied.  Before the
+  // last slice: wait for this wave's loads of step k + 1 and for its reads of
+  // stage k, barrier (every wave's loads landed, every wave done reading stage
+  // k), refill stage k % 2 with step k + 2, then read slice 0 of step k + 1
+  // while multiplying slice 3.  Past the last step the load index is clamped:
+  // the redundant loads go to a stage nobody reads again.
   v8bf fa0[kMI], fb0[kNJ], fa1[kMI], fb1[kNJ];
   const int last = nk - 1;
-#pragma unroll
-  for (int s0 = 0; s0 < kStages; ++s0) issue(min(s0, last), s0);
-  wait_vmcnt<(kStages - 1) * kDmaStep>();
+  issue(0, 0);
+  issue(min(1, last), 1);
+  wait_vmcnt<kDmaStep>();
   barrier_only();
   rd(0, 0, fa0, fb0);
   int sc = 0;
   for (int k = 0; k < nk; ++k) {
-    const int sn = sc == kStages - 1 ? 0 : sc + 1;
     rd(sc, 1, fa1, fb1);
     mm(fa0, fb0);
-    // issue order: one matrix instruction (its operands were read a step
-    // earlier), the 6 LDS reads, the other 7 matrix instructions
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, kMI * kNJ - 1, 0);
+    ORDER_SLICE(0)
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_lgkm0<(kStages - 2) * kDmaStep>();
+    rd(sc, 2, fa0, fb0);
+    mm(fa1, fb1);
+    ORDER_SLICE(1)
+    __builtin_amdgcn_sched_barrier(0);
+    rd(sc, 3, fa1, fb1);
+    mm(fa0, fb0);
+    ORDER_SLICE(2)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_lgkm0<0>();
     barrier_only();
     __builtin_amdgcn_sched_barrier(0);
-    issue(min(k + kStages, last), sc);
-    rd(sn, 0, fa0, fb0);
+    issue(min(k + 2, last), sc);
+    rd(sc ^ 1, 0, fa0, fb0);
     mm(fa1, fb1);
-    // LDS reads first, then matrix instructions with the direct loads between them
-    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 3);
 #pragma unroll
-    for (int i = 0; i < kDmaStep; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);
+    for (int i = 0; i < kMI * kNJ; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 3);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, kMI * kNJ - kDmaStep, 1);
     __builtin_amdgcn_sched_barrier(0);
-    sc = sn;
+    sc ^= 1;
   }
   // No direct loads may still target LDS when the block retires.
   wait_vmcnt<0>();

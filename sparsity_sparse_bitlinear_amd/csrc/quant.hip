@@ -7,7 +7,8 @@
 // master weight and applies it after quantization ([GIST] 2.2 likewise).
 //
 // Three launches, all on the caller's stream:
-//   k_absum          pass 1 over W: exact integer partial sums of |W| per block
+//   k_absum          pass 1 over W: exact partial sums of |W| per block (float64
+//                    window sums flushed to 128-bit integers, integer fallback)
 //   k_gamma_finalize one block: exact total, one correctly rounded division
 //   k_mask_quant_pack pass 2 over W: per 8-group sorting network -> keep bits,
 //                     threshold |w| > gamma/2 -> 2-bit codes, write both planes
@@ -18,6 +19,31 @@ namespace sbl {
 // ---------------------------------------------------------------------------
 // Exact rounding of the mean (host and device).
 // ---------------------------------------------------------------------------
+
+// Word idx of the little-endian word array (zero outside it).
+__host__ __device__ static inline uint32_t word_at(const uint32_t* w, int nwords, int idx) {
+  return (idx >= 0 && idx < nwords) ? w[idx] : 0u;
+}
+
+// 64 bits of S starting at bit position lo (lo may be negative; bits below 0
+// read as zero).
+__host__ __device__ static inline unsigned long long bits64(const uint32_t* w, int nwords, int lo) {
+  const int q = lo >= 0 ? lo >> 5 : -((31 - lo) >> 5);  // floor(lo / 32)
+  const int r = lo - 32 * q;                           // 0..31
+  const unsigned long long w0 = word_at(w, nwords, q), w1 = word_at(w, nwords, q + 1);
+  const unsigned long long w2 = word_at(w, nwords, q + 2);
+  const unsigned long long low = w0 | (w1 << 32);
+  return r ? ((low >> r) | (w2 << (64 - r))) : low;
+}
+
+// True iff any bit of S below position lo (exclusive) is set.
+__host__ __device__ static inline bool any_below(const uint32_t* w, int nwords, int lo) {
+  if (lo <= 0) return false;
+  const int q = lo >> 5, r = lo & 31;
+  for (int i = 0; i < q && i < nwords; ++i)
+    if (w[i]) return true;
+  return r && q < nwords && (w[q] & ((1u << r) - 1u));
+}
 
 // S = sum of nwords little-endian 32-bit words, in units of 2^-133.
 // Returns the binary32 value nearest to S * 2^-133 / count (ties to even).
@@ -31,17 +57,8 @@ __host__ __device__ float round_mean_words(const uint32_t* w, int nwords, unsign
   if (top < 0) return 0.0f;
   const int p = top * 32 + 31 - __builtin_clz(w[top]);  // position of the leading one
   // M = bits [p-63, p] of S (left-aligned 64-bit window), sticky = any lower bit.
-  unsigned long long M = 0;
-  bool sticky = false;
-  for (int b = 0; b < 64; ++b) {
-    const int pos = p - 63 + b;
-    unsigned long long bit = 0;
-    if (pos >= 0) bit = (w[pos >> 5] >> (pos & 31)) & 1u;
-    M |= bit << b;
-  }
-  for (int pos = 0; pos < p - 63; ++pos) {
-    if ((w[pos >> 5] >> (pos & 31)) & 1u) { sticky = true; break; }
-  }
+  const unsigned long long M = bits64(w, nwords, p - 63);
+  bool sticky = any_below(w, nwords, p - 63);
   // value = (M + f) * 2^(p - 63 - 133) / count, f in [0, 1) (f > 0 iff sticky)
   const unsigned long long Q = M / count;
   const unsigned long long R = M % count;
@@ -94,6 +111,22 @@ __device__ __forceinline__ void absum_half(uint32_t h, U128& acc, unsigned long 
   }
 }
 
+// True iff every non-zero magnitude of the 8 values has its exponent in the
+// float64 window [kWinLo, kFastHi].
+__device__ __forceinline__ bool in_fast_window(const uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  bool ok = true;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t mag = (w[i] >> (16 * h)) & 0x7FFFu;
+      ok = ok && (mag == 0u || ((mag >> 7) - (uint32_t)kWinLo) <= (uint32_t)(kFastHi - kWinLo));
+    }
+  }
+  return ok;
+}
+
 __global__ __launch_bounds__(kAbsumThreads) void k_absum(const uint4* __restrict__ W, int64_t n_vec8,
                                                          AbsumPartial* __restrict__ part,
                                                          unsigned long long* __restrict__ hist_out) {
@@ -106,18 +139,37 @@ __global__ __launch_bounds__(kAbsumThreads) void k_absum(const uint4* __restrict
   __syncthreads();
 
   U128 acc = {0, 0};
+  double fsum = 0.0;  // exact: at most 256 window values since the last flush
+  int fcount = 0;
   bool any_hist = false;
   const int64_t stride = (int64_t)gridDim.x * kAbsumThreads;
   for (int64_t i = (int64_t)blockIdx.x * kAbsumThreads + tid; i < n_vec8; i += stride) {
     const uint4 v = W[i];
-    absum_half(v.x & 0xFFFFu, acc, hist, any_hist);
-    absum_half(v.x >> 16, acc, hist, any_hist);
-    absum_half(v.y & 0xFFFFu, acc, hist, any_hist);
-    absum_half(v.y >> 16, acc, hist, any_hist);
-    absum_half(v.z & 0xFFFFu, acc, hist, any_hist);
-    absum_half(v.z >> 16, acc, hist, any_hist);
-    absum_half(v.w & 0xFFFFu, acc, hist, any_hist);
-    absum_half(v.w >> 16, acc, hist, any_hist);
+    if (__builtin_expect(in_fast_window(v), 1)) {
+      fsum += (double)__uint_as_float((v.x & 0x7FFFu) << 16) + (double)__uint_as_float(v.x & 0x7FFF0000u);
+      fsum += (double)__uint_as_float((v.y & 0x7FFFu) << 16) + (double)__uint_as_float(v.y & 0x7FFF0000u);
+      fsum += (double)__uint_as_float((v.z & 0x7FFFu) << 16) + (double)__uint_as_float(v.z & 0x7FFF0000u);
+      fsum += (double)__uint_as_float((v.w & 0x7FFFu) << 16) + (double)__uint_as_float(v.w & 0x7FFF0000u);
+      if (++fcount == 32) {  // 256 values: move the exact integer fsum * 2^(134 - kWinLo) < 2^53 out
+        const U128 f = {(unsigned long long)ldexp(fsum, 134 - kWinLo), 0ull};
+        add128(acc, f);
+        fsum = 0.0;
+        fcount = 0;
+      }
+    } else {
+      absum_half(v.x & 0xFFFFu, acc, hist, any_hist);
+      absum_half(v.x >> 16, acc, hist, any_hist);
+      absum_half(v.y & 0xFFFFu, acc, hist, any_hist);
+      absum_half(v.y >> 16, acc, hist, any_hist);
+      absum_half(v.z & 0xFFFFu, acc, hist, any_hist);
+      absum_half(v.z >> 16, acc, hist, any_hist);
+      absum_half(v.w & 0xFFFFu, acc, hist, any_hist);
+      absum_half(v.w >> 16, acc, hist, any_hist);
+    }
+  }
+  {
+    const U128 f = {(unsigned long long)ldexp(fsum, 134 - kWinLo), 0ull};
+    add128(acc, f);
   }
   if (any_hist) block_any = 1;  // benign race: every writer stores 1
   red[tid] = acc;

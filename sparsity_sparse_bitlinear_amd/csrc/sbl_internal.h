@@ -30,12 +30,17 @@ int hip_fail(hipError_t e, const char* what);
 // gamma: exact sum of |W| and its correctly rounded mean.
 // ---------------------------------------------------------------------------
 
-// Per-thread fast accumulation window: bf16 magnitudes with biased exponent
-// E in [kWinLo, kWinLo + 56] are accumulated as (significand << (E - kWinLo))
-// in units of 2^(kWinLo - 134); everything else that is non-zero goes to an
-// exact per-exponent histogram.
-constexpr int kWinLo = 80;
+// Accumulation windows of the exact sum, by biased bf16 exponent E:
+//   E in [kWinLo, kWinLo + 37]: summed in float64 per thread (every partial
+//     sum of up to 256 such values is a multiple of 2^(kWinLo - 134) below
+//     2^(kWinLo - 134 + 53), hence exact), flushed to a 128-bit integer in
+//     units of 2^(kWinLo - 134) every 256 values;
+//   E in [kWinLo, kWinLo + 56] (a group of 8 with any value outside the
+//     float64 window): significand << (E - kWinLo) into the same integer;
+//   anything else non-zero: an exact per-exponent histogram.
+constexpr int kWinLo = 96;
 constexpr int kWinHi = kWinLo + 56;
+constexpr int kFastHi = kWinLo + 37;
 
 // Partial results of one absum block (written to the workspace).
 struct AbsumPartial {
@@ -68,7 +73,7 @@ hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_
 // C[M, N] = alpha * A[M, K] B[N, K]^T, bf16 operands, float32 or bf16 output
 // (gemm_nt.hip).  Only for shapes where gemm_nt_bf16_supported() holds.
 // alpha == nullptr means 1.  With splits > 1 the K range is cut into pieces of
-// k_per_split (a multiple of 32, none empty) and piece z writes its partial
+// k_per_split (a multiple of 64, none empty) and piece z writes its partial
 // product to C + z * M * N.
 bool gemm_nt_bf16_supported(int64_t M, int64_t N, int64_t K);
 int64_t gemm_nt_bf16_tiles(int64_t M, int64_t N);

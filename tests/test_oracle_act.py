@@ -64,6 +64,27 @@ def test_act_quant_binary32_sequence_agrees(a):
     assert np.array_equal(q, q32)
 
 
+@pytest.mark.parametrize("a", ABSMAX_CASES)
+def test_act_quant_reciprocal_fast_path_agrees(a):
+    # A GPU kernel may replace the division by a multiplication with fl32(127 / a'):
+    # qf = fl32(x' * fl32(127 / a')) is within |q| 2^-23 <= 2^-16 of the exact quotient, so
+    # rint(qf) is exact whenever qf is more than 2^-14 away from a half-integer; the other
+    # elements (ties among them) fall back to the division.  Exhaustive over every bf16 x.
+    rows, av = _rows_for(a)
+    q, _ = oracle.act_quant(rows)
+    x32 = bf16_bits_to_f32(rows)
+    a32 = np.max(np.abs(x32), axis=1, keepdims=True)
+    k = (1 - np.frexp(a32)[1]).astype(np.int32)
+    xs, as_ = np.ldexp(x32, k).astype(np.float32), np.ldexp(a32, k).astype(np.float32)
+    c = (np.float32(127.0) / as_).astype(np.float32)
+    qf = (xs * c).astype(np.float32)
+    r = np.rint(qf)
+    slow = np.abs(qf - r) > np.float32(0.5 - 2.0 ** -14)
+    r[slow] = np.rint((np.float32(127.0) * xs[slow]) / np.broadcast_to(as_, xs.shape)[slow])
+    assert np.array_equal(q, r.astype(np.int8))
+    assert slow.mean() < 0.01
+
+
 def test_act_quant_properties():
     x = activation(0, 0, 64, 256, dist="student_t4")
     q, a = oracle.act_quant(x)
