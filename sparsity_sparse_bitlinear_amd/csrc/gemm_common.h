@@ -39,6 +39,14 @@ __device__ __forceinline__ v4i frag(const char* base, int row0, int ks, int lane
   return *(const v4i*)(base + swz(row0 + (lane & 31), 2 * ks + (lane >> 5)));
 }
 
+// Wide K steps (direct-load kernels): LDS rows of kRowK = 128 bytes, 8 chunks.
+// A fragment read is 16 lanes on 16 consecutive rows, same chunk: the 8 even
+// rows then sit in banks 0-31 and the 8 odd rows in banks 32-63, and
+// c ^ ((row / 2) % 8) gives each of the 8 a different 16-byte bank group, so
+// the read is conflict-free.  Direct loads fill whole 1 KB runs (8 rows).
+constexpr int kRowK = 128;
+__device__ __forceinline__ int swz8(int row, int c) { return row * kRowK + 16 * (c ^ ((row >> 1) & 7)); }
+
 // Block index -> (m tile, n tile).  Blocks are dispatched round-robin over
 // the 8 XCDs (b % 8); XCD x gets a contiguous range of tiles in row-major
 // order (n fastest), so the tiles resident on one XCD share A rows in its L2.

@@ -195,21 +195,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_i8(const int8_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Direct-load forward (d_in % 64 == 0): block tile 256 tokens x 256 outputs,
+// Direct-load forward (d_in % 128 == 0): block tile 256 tokens x 256 outputs,
 // 8 waves (2 along M x 4 along N, 128 x 64 each), one block per CU.  Per K
-// step of 64: the x_q tile (256 rows x 64 bytes, swizzled as in
-// gemm_common.h) and the code tile (256 rows x 8 code words = 16 bytes) move
-// to LDS with direct-to-LDS loads through a ring of kFS stages; each wave
-// expands the code words of its own B fragments in registers (one 32-bit word
-// = 16 codes = one MFMA operand of 16 int8).
+// step of 128: the x_q tile (256 rows x 128 bytes, swizzled as swz8) and the
+// code tile (256 rows x 16 code words = 32 bytes) move to LDS with direct-to-
+// LDS loads through two stages; each wave expands the code words of its own B
+// fragments in registers (one 32-bit word = 16 codes = one MFMA operand of 16
+// int8), one slice ahead of the matrix instructions that use them.
 // ---------------------------------------------------------------------------
 constexpr int kFT = 512;                   // threads
 constexpr int kFBN = 256;                  // block cols (outputs)
-constexpr int kFS = 4;                     // LDS stages
-constexpr int kFStageA = kBM * kRow;       // 16 KB
-constexpr int kFStageB = kFBN * 16;        // 4 KB of code words
+constexpr int kFS = 2;                     // LDS stages
+constexpr int kFK = 128;                   // k per step
+constexpr int kFStageA = kBM * kRowK;      // 32 KB
+constexpr int kFStageB = kFBN * 32;        // 8 KB of code words
 constexpr int kFStage = kFStageA + kFStageB;
-constexpr int kFDmaA = kBM * 4 / kFT;      // 2 direct loads per thread per K step
+constexpr int kFDmaA = kBM * 8 / kFT;      // 4 direct loads per thread per K step
+constexpr int kFDmaStep = kFDmaA + 1;
+
+// Byte offset of code word w (0..7, groups 2w and 2w + 1 of the step) of tile
+// row n: the two 16-byte halves of a row swap places on rows with bit 3 set,
+// which halves the bank conflicts of the 32 rows a fragment read touches.
+__device__ __forceinline__ int code_word_at(int n, int w) { return 32 * n + 16 * ((w >> 2) ^ ((n >> 3) & 1)) + 4 * (w & 3); }
 
 template <int OUT>
 __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restrict__ xq,
@@ -228,34 +235,33 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
   const int m0 = mt * kBM;
   const int n0 = nt * kFBN;
   const int G = d_in >> 3;
-  const int nk = d_in >> 6;
+  const int nk = d_in / kFK;
   const int rows_a = min(kBM, T - m0);
   const int rows_b = min(kFBN, d_out - n0);
   const auto ar = make_rsrc(xq + (int64_t)m0 * d_in, clamp_bytes((int64_t)rows_a * d_in));
   const auto br = make_rsrc(codes + (int64_t)n0 * G, clamp_bytes((int64_t)rows_b * G * 2));
 
+  // x_q tile: LDS chunk position p holds row p / 8, logical chunk (p % 8) ^ ((row / 2) % 8)
   uint32_t a_off[kFDmaA];
 #pragma unroll
   for (int i = 0; i < kFDmaA; ++i) {
     const int p = 64 * (kFDmaA * wave + i) + lane;
-    const int r = p >> 2, c = (p & 3) ^ ((r >> 2) & 3);
+    const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
     a_off[i] = (uint32_t)(r * d_in + 16 * c);
   }
-  // code tile: 256 rows x 4 words of 32 bits (8 groups); every wave moves
-  // 2 x 64 words with 4-byte direct loads, word p = row p / 4, word p % 4
-  uint32_t b_off[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = 64 * (2 * wave + i) + lane;
-    b_off[i] = (uint32_t)((p >> 2) * G * 2 + 4 * (p & 3));
+  // code tile: chunk position p holds row p / 2, half (p % 2) ^ ((row / 8) % 2)
+  uint32_t b_off;
+  {
+    const int p = 64 * wave + lane;
+    const int r = p >> 1, h = (p & 1) ^ ((r >> 3) & 1);
+    b_off = (uint32_t)(r * G * 2 + 16 * h);
   }
 
   auto issue = [&](int kt, int st) {
     char* sa = lds + st * kFStage;
 #pragma unroll
-    for (int i = 0; i < kFDmaA; ++i) dma16(ar, sa + 1024 * (kFDmaA * wave + i), a_off[i], (uint32_t)kt * 64);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) dma4(br, sa + kFStageA + 256 * (2 * wave + i), b_off[i], (uint32_t)kt * 16);
+    for (int i = 0; i < kFDmaA; ++i) dma16(ar, sa + 1024 * (kFDmaA * wave + i), a_off[i], (uint32_t)kt * kFK);
+    dma16(br, sa + kFStageA + 1024 * wave, b_off, (uint32_t)kt * (kFK / 4));
   };
 
   v16i acc[kMI][kNJ];
@@ -266,16 +272,16 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-  // K slice ks (32 of the 64 k of a step): A fragments, and the code word
+  // K slice ks (32 of the 128 k of a step): A fragments, and the code word
   // (groups 4 ks + 2 (l / 32), +1) of output row wn0 + 32 j + l % 32.
   auto rd = [&](int st, int ks, v4i (&fa)[kMI], uint32_t (&wb)[kNJ]) {
     const char* a = lds + st * kFStage;
     const char* b = a + kFStageA;
 #pragma unroll
-    for (int i = 0; i < kMI; ++i) fa[i] = frag(a, wm0 + 32 * i, ks, lane);
+    for (int i = 0; i < kMI; ++i) fa[i] = *(const v4i*)(a + swz8(wm0 + 32 * i + (lane & 31), 2 * ks + (lane >> 5)));
 #pragma unroll
     for (int j = 0; j < kNJ; ++j)
-      wb[j] = *(const uint32_t*)(b + 16 * (wn0 + 32 * j + (lane & 31)) + 4 * (2 * ks + (lane >> 5)));
+      wb[j] = *(const uint32_t*)(b + code_word_at(wn0 + 32 * j + (lane & 31), 2 * ks + (lane >> 5)));
   };
   // The code fragment is the MFMA's first operand, so accumulator register r
   // of lane l holds C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]: four
@@ -291,53 +297,60 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) fb[j] = __builtin_bit_cast(v4i, expand16(wb[j]));
   };
+#define SBL_FWD_SLICE_ORDER(id)                                 \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, id);           \
+  __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, id);   \
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, id);           \
+  __builtin_amdgcn_sched_group_barrier(0x002, 12, id);          \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, id);           \
+  __builtin_amdgcn_sched_group_barrier(0x002, 12, id);          \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, id);           \
+  __builtin_amdgcn_sched_group_barrier(0x002, 12, id);          \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, id);           \
+  __builtin_amdgcn_sched_group_barrier(0x002, 12, id);          \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, id);           \
+  __builtin_amdgcn_sched_barrier(0);
 
-  // Same schedule as the bf16 engine (read slice 1 while multiplying slice 0,
-  // wait + barrier in the middle of the step, refill the stage just read,
-  // read slice 0 of the next stage while multiplying slice 1), and the code
-  // words of the slice read in one half are expanded between the matrix
-  // instructions of that half, ready for the next.
+  // Step k (stage k % 2 has landed; slice 0 is read and expanded): each of the
+  // 4 slices is read and its code words expanded while the previous slice is
+  // multiplied.  Before the last slice: wait for this wave's loads of step
+  // k + 1 and its reads of stage k, barrier, refill stage k % 2 with step
+  // k + 2, then read slice 0 of step k + 1 while multiplying slice 3.  Past the
+  // last step the load index is clamped (redundant loads, never read).
   v4i fa0[kMI], fa1[kMI], fb0[kNJ], fb1[kNJ];
   uint32_t wb0[kNJ], wb1[kNJ];
   const int last = nk - 1;
-#pragma unroll
-  for (int s0 = 0; s0 < kFS; ++s0) issue(min(s0, last), s0);
-  wait_vmcnt<(kFS - 1) * (kFDmaA + 2)>();
+  issue(0, 0);
+  issue(min(1, last), 1);
+  wait_vmcnt<kFDmaStep>();
   barrier_only();
   rd(0, 0, fa0, wb0);
   expand(wb0, fb0);
   int sc = 0;
   for (int k = 0; k < nk; ++k) {
-    const int sn = sc == kFS - 1 ? 0 : sc + 1;
     rd(sc, 1, fa1, wb1);
     mm(fa0, fb0);
     expand(wb1, fb1);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_lgkm0<(kFS - 2) * (kFDmaA + 2)>();
-    barrier_only();
-    __builtin_amdgcn_sched_barrier(0);
-    issue(min(k + kFS, last), sc);
-    rd(sn, 0, fa0, wb0);
+    SBL_FWD_SLICE_ORDER(0)
+    rd(sc, 2, fa0, wb0);
     mm(fa1, fb1);
     expand(wb0, fb0);
-    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 1);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-    }
+    SBL_FWD_SLICE_ORDER(1)
+    rd(sc, 3, fa1, wb1);
+    mm(fa0, fb0);
+    expand(wb1, fb1);
+    SBL_FWD_SLICE_ORDER(2)
+    wait_vmcnt_lgkm0<0>();
+    barrier_only();
     __builtin_amdgcn_sched_barrier(0);
-    sc = sn;
+    issue(min(k + 2, last), sc);
+    rd(sc ^ 1, 0, fa0, wb0);
+    mm(fa1, fb1);
+    expand(wb0, fb0);
+    SBL_FWD_SLICE_ORDER(3)
+    sc ^= 1;
   }
+#undef SBL_FWD_SLICE_ORDER
   wait_vmcnt<0>();
 
   // Epilogue: each lane stores runs of 4 consecutive outputs of its token
@@ -410,7 +423,7 @@ hipError_t launch_fwd_v(const uint16_t* codes, const float* gamma, const int8_t*
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (d_in % 64 == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes) {
+  if (d_in % kFK == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes) {
     const int64_t nb = ((d_out + kFBN - 1) / kFBN) * ((T + kBM - 1) / kBM);
     const dim3 grid((unsigned)nb), block(kFT);
     switch (y_dtype) {

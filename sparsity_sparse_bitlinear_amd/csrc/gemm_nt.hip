@@ -37,7 +37,6 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 
 constexpr int kNT = 512;                  // threads per block
 constexpr int kBNn = 256;                 // block cols (N)
-constexpr int kRowK = 128;                // bytes per LDS row: 64 bf16 per K step
 constexpr int kStages = 2;
 constexpr int kStageA = kBM * kRowK;      // 32 KB
 constexpr int kStageB = kBNn * kRowK;     // 32 KB
@@ -46,13 +45,6 @@ constexpr int kDmaA = kBM * 8 / kNT;      // 4
 constexpr int kDmaB = kBNn * 8 / kNT;     // 4
 constexpr int kDmaStep = kDmaA + kDmaB;
 constexpr int kKStep = kRowK / 2;         // 64 bf16 per K step
-
-// LDS address of 16-byte chunk c (0..7) of K-row `row`.  A fragment read is 16
-// lanes on 16 consecutive rows, same chunk: the 8 even rows then sit in banks
-// 0-31 and the 8 odd rows in banks 32-63, and c ^ ((row / 2) % 8) gives each
-// of the 8 a different 16-byte bank group, so the read is conflict-free.  The
-// direct loads fill whole 1 KB runs (8 rows).
-__device__ __forceinline__ int swz8(int row, int c) { return row * kRowK + 16 * (c ^ ((row >> 1) & 7)); }
 
 // Requires K % 8 == 0 (16-byte rows, K chunks never straddle a row end).
 // blockIdx.y selects a K range [kps * y, kps * (y + 1)) (split-K); block y writes

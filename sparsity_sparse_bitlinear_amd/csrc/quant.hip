@@ -220,6 +220,7 @@ __global__ __launch_bounds__(256) void k_gamma_finalize(const AbsumPartial* __re
                                                         float* __restrict__ gamma) {
   __shared__ U128 red[256];
   __shared__ unsigned long long bins[256];
+  __shared__ int flags[256];
   __shared__ int any_flag;
   const int tid = threadIdx.x;
   if (tid == 0) any_flag = 0;
@@ -243,10 +244,17 @@ __global__ __launch_bounds__(256) void k_gamma_finalize(const AbsumPartial* __re
     }
     __syncthreads();
   }
+  // Histogram bins of the blocks that have one: the flags are staged in LDS so
+  // that the serial walk over blocks reads global memory only for flagged ones.
   unsigned long long bin = 0;
   if (any_flag) {
-    for (int b = 0; b < nblocks; ++b) {
-      if (part[b].flag) bin += hist_in[(size_t)b * 256 + tid];
+    for (int b0 = 0; b0 < nblocks; b0 += 256) {
+      __syncthreads();
+      flags[tid] = (b0 + tid < nblocks) ? (part[b0 + tid].flag != 0) : 0;
+      __syncthreads();
+      const int nb = min(256, nblocks - b0);
+      for (int b = 0; b < nb; ++b)
+        if (flags[b]) bin += hist_in[(size_t)(b0 + b) * 256 + tid];
     }
   }
   bins[tid] = bin;
@@ -258,7 +266,8 @@ __global__ __launch_bounds__(256) void k_gamma_finalize(const AbsumPartial* __re
     add_shifted(w, kSumWords, red[0].lo, kWinLo - 1);
     add_shifted(w, kSumWords, red[0].hi, kWinLo - 1 + 64);
     // histogram bin e (biased exponent, >= 1): units of 2^(e - 134) = 2^(e - 1) * 2^-133
-    for (int e = 1; e < 255; ++e) add_shifted(w, kSumWords, bins[e], e - 1);
+    if (any_flag)
+      for (int e = 1; e < 255; ++e) add_shifted(w, kSumWords, bins[e], e - 1);
     *gamma = round_mean_words(w, kSumWords, count);
   }
 }

@@ -138,7 +138,8 @@ def ref_forward(W_bits, x_bits, n, rows=None):
     return acc, oracle.forward_y(acc, g, a)
 
 
-FWD_SHAPES = [(64, 256, 256), (77, 200, 328), (1, 8, 8), (130, 136, 136), (513, 4864, 896), (33, 40, 1032)]
+FWD_SHAPES = [(64, 256, 256), (77, 200, 328), (1, 8, 8), (130, 136, 136), (513, 4864, 896), (33, 40, 1032),
+              (100, 300, 192), (700, 1000, 1152)]
 
 
 @pytest.mark.parametrize("n", [6, 2, 8, 4])
