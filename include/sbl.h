@@ -149,8 +149,10 @@ SBL_API int sbl_act_quant(const uint16_t* x_bf16, int64_t T, int64_t d_in, int8_
  * codes, gamma : from sbl_quant_mask_pack for W [d_out, d_in].
  * x_q, absmax  : from sbl_act_quant, [T, d_in] and [T].
  * y            : [T, d_out] of y_dtype: SBL_F32, SBL_BF16, or SBL_I32 (acc).
- * T = 0 is a no-op.  Small T (decode, T <= 16) uses a streaming kernel;
- * larger T uses the int8 matrix-core kernel; both give identical results.
+ * T = 0 is a no-op.  Decode-sized T (T <= 64, d_in % 64 == 0) uses a kernel
+ * that streams the code plane once with a split K range per block; larger T
+ * uses tiled int8 matrix-core kernels.  All paths compute the same exact
+ * int32 sums, so the results are identical.
  */
 SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t* x_q, const float* absmax,
                         int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, void* hip_stream);

@@ -396,6 +396,134 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode forward (T <= 64, d_in % 64 == 0): the code plane is streamed once and
+// every weight meets at most 64 tokens, so the kernel is bound by the code
+// bytes, not by the matrix cores.  A block owns 16 output rows; its 4 waves
+// split the K range and each runs v_mfma_i32_16x16x64_i8 with the expanded
+// code words as the first operand (lane l: row l % 16, k 16 (l / 16) + 0..15,
+// one 32-bit word of 16 codes) and up to 4 tiles of 16 tokens as the second
+// (x_q rows past T read as zero).  Accumulator register r of lane l then holds
+// C[t = l % 16][o = 4 (l / 16) + r].  The 4 partial sums are added in LDS in a
+// fixed order (integers: exact) and scaled as in the large-T kernels.
+// ---------------------------------------------------------------------------
+constexpr int kDecRows = 16;
+constexpr int kDecWaves = 4;
+constexpr int kDecUnroll = 4;
+
+template <int NTT, int OUT>
+__global__ __launch_bounds__(64 * kDecWaves) void k_fwd_decode(const int8_t* __restrict__ xq,
+                                                              const uint16_t* __restrict__ codes,
+                                                              const float* __restrict__ gamma_p,
+                                                              const float* __restrict__ absmax, int T, int d_in,
+                                                              int d_out, void* __restrict__ y) {
+  __shared__ int red[kDecWaves - 1][NTT][4][64];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int o0 = blockIdx.x * kDecRows;
+  const int G = d_in >> 3;
+  const int nks = d_in >> 6;
+  const int per = (nks + kDecWaves - 1) / kDecWaves;
+  const int s_begin = wave * per, s_end = min(nks, s_begin + per);
+  const int rows = min(kDecRows, d_out - o0);
+  const auto br = make_rsrc(codes + (int64_t)o0 * G, clamp_bytes((int64_t)rows * G * 2));
+  const auto xr = make_rsrc(xq, clamp_bytes((int64_t)T * d_in));
+  const int q = lane >> 4, r16 = lane & 15;
+  const uint32_t b_off = (uint32_t)(r16 * G * 2 + 4 * q);
+  uint32_t x_off[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) x_off[tt] = (uint32_t)((16 * tt + r16) * d_in + 16 * q);
+
+  v4i acc[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) acc[tt] = (v4i){0, 0, 0, 0};
+  for (int s0 = s_begin; s0 < s_end; s0 += kDecUnroll) {
+    uint32_t wb[kDecUnroll];
+    v4i fx[kDecUnroll][NTT];
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const bool ok = s0 + u < s_end;
+      wb[u] = bload4(br, ok ? b_off + (uint32_t)(s0 + u) * 16 : kOOB);
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt)
+        fx[u][tt] = __builtin_bit_cast(v4i, bload16(xr, ok ? x_off[tt] + (uint32_t)(s0 + u) * 64 : kOOB));
+    }
+#pragma unroll
+    for (int u = 0; u < kDecUnroll; ++u) {
+      const v4i fb = __builtin_bit_cast(v4i, expand16(wb[u]));
+#pragma unroll
+      for (int tt = 0; tt < NTT; ++tt) acc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb, fx[u][tt], acc[tt], 0, 0, 0);
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave - 1][tt][r][lane] = acc[tt][r];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < kDecWaves - 1; ++w)
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[tt][r] += red[w][tt][r][lane];
+
+  const float g127 = *gamma_p * (1.0f / 127.0f);
+  const bool vec_out = (d_out & 3) == 0;
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int t = 16 * tt + r16;
+    const int o = o0 + 4 * q;
+    if (t >= T || o >= d_out) continue;
+    const float sc = g127 * absmax[t];
+    const int64_t off = (int64_t)t * d_out + o;
+    const int a0 = acc[tt][0], a1 = acc[tt][1], a2 = acc[tt][2], a3 = acc[tt][3];
+    if (vec_out && o + 4 <= d_out) {
+      if constexpr (OUT == SBL_I32) {
+        *(int4*)((int*)y + off) = make_int4(a0, a1, a2, a3);
+      } else if constexpr (OUT == SBL_F32) {
+        *(float4*)((float*)y + off) = make_float4((float)a0 * sc, (float)a1 * sc, (float)a2 * sc, (float)a3 * sc);
+      } else {
+        *(uint2*)((__bf16*)y + off) =
+            make_uint2(cvt_pk_bf16((float)a0 * sc, (float)a1 * sc), cvt_pk_bf16((float)a2 * sc, (float)a3 * sc));
+      }
+    } else {
+      const int av[4] = {a0, a1, a2, a3};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (o + u >= d_out) break;
+        if constexpr (OUT == SBL_I32) ((int*)y)[off + u] = av[u];
+        else if constexpr (OUT == SBL_F32) ((float*)y)[off + u] = (float)av[u] * sc;
+        else ((__bf16*)y)[off + u] = (__bf16)((float)av[u] * sc);
+      }
+    }
+  }
+}
+
+template <int NTT>
+hipError_t launch_decode(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax, int64_t T,
+                         int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
+  const dim3 grid((unsigned)((d_out + kDecRows - 1) / kDecRows)), block(64 * kDecWaves);
+  switch (y_dtype) {
+    case SBL_F32:
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_F32>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T, (int)d_in,
+                         (int)d_out, y);
+      break;
+    case SBL_BF16:
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_BF16>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+                         (int)d_in, (int)d_out, y);
+      break;
+    default:
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_I32>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T, (int)d_in,
+                         (int)d_out, y);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <bool VEC>
 hipError_t launch_fwd_v(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax, int64_t T,
                         int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
@@ -423,6 +551,10 @@ hipError_t launch_fwd_v(const uint16_t* codes, const float* gamma, const int8_t*
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
+  if (T <= 64 && d_in % 64 == 0) {
+    if (T <= 16) return launch_decode<1>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
+    return launch_decode<4>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
+  }
   if (d_in % kFK == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes) {
     const int64_t nb = ((d_out + kFBN - 1) / kFBN) * ((T + kBM - 1) / kBM);
     const dim3 grid((unsigned)nb), block(kFT);

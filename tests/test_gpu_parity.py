@@ -169,6 +169,51 @@ def test_forward_large_tiles_sampled():
     assert_y_close(y, y_ref, acc_ref)
 
 
+# Decode (T <= 64): the streaming kernel, every mask, ragged row counts.
+DECODE_T = [1, 5, 8, 16, 17, 33, 64]
+
+
+@pytest.mark.parametrize("n", [6, 4, 2])
+@pytest.mark.parametrize("d_out,d_in", [(256, 2048), (130, 448), (2050, 640), (7, 64)])
+@pytest.mark.parametrize("T", DECODE_T)
+def test_decode_parity(T, d_out, d_in, n):
+    W = weight(61, d_out + d_in, d_out, d_in)
+    x = activation(61, d_out + d_in + T, T, d_in, dist="student_t4")
+    acc_ref, y_ref = ref_forward(W, x, n)
+    acc = gpu_forward(W, x, n, sbl.I32).cpu().numpy()
+    np.testing.assert_array_equal(acc, acc_ref)
+    y = gpu_forward(W, x, n, sbl.F32).cpu().numpy()
+    assert_y_close(y, y_ref, acc_ref)
+    yb = gpu_forward(W, x, n, sbl.BF16).float().cpu().numpy()
+    assert np.all(np.abs(yb - y_ref) <= 2.0 ** -8 * np.abs(y_ref) + 1e-30)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+@pytest.mark.parametrize("name,d_out,d_in", [("gate", 11008, 2048), ("down", 2048, 11008)])
+def test_decode_full_size(T, name, d_out, d_in):
+    # decode workload: 3B-like matrices, Student-t(4) activations, T = 1 / 8 / 64, exact int32
+    W = weight(71, d_in, d_out, d_in)
+    x = activation(71, d_out + T, T, d_in, dist="student_t4")
+    acc_ref, _ = ref_forward(W, x, 6)
+    acc = gpu_forward(W, x, 6, sbl.I32).cpu().numpy()
+    np.testing.assert_array_equal(acc, acc_ref)
+
+
+@pytest.mark.parametrize("name,d_out,d_in", [("gate", 11008, 2048), ("down", 2048, 11008)])
+def test_forward_full_size_sampled(name, d_out, d_in):
+    # the 3B-like training shapes at 32768 tokens, as timed: 64 sampled tokens, all outputs, exact int32
+    T = 32768
+    W = weight(81, d_in, d_out, d_in)
+    x = activation(81, d_out, T, d_in, dist="student_t4")
+    rows = sample_rows(81, 2, T, 64)
+    idx = torch.from_numpy(rows).cuda()
+    acc = gpu_forward(W, x, 6, sbl.I32)[idx].cpu().numpy()
+    acc_ref, y_ref = ref_forward(W, x, 6, rows)
+    np.testing.assert_array_equal(acc, acc_ref)
+    yb = gpu_forward(W, x, 6, sbl.BF16)[idx].float().cpu().numpy()
+    assert np.all(np.abs(yb - y_ref) <= 2.0 ** -8 * np.abs(y_ref) + 1e-30)
+
+
 # ---------------------------------------------------------------------------
 # backward
 # ---------------------------------------------------------------------------
@@ -214,6 +259,25 @@ def test_backward_dx_large_tiles_sampled():
     dX_ref, _ = oracle.backward(dY[rows], w_eff, g, xq[rows], a[rows])
     assert_grad_close(bf16_to_f64(dX)[rows], dX_ref)
     cols = sample_rows(61, 4, d_out, 32)       # sampled rows o of dW over all T
+    dW_ref = oracle.bf16_to_f64(dY[:, cols]).T @ oracle.dequant_act(xq, a)
+    assert_grad_close(dW.cpu().numpy()[cols], dW_ref)
+
+
+@pytest.mark.parametrize("name,d_out,d_in", [("gate", 11008, 2048), ("down", 2048, 11008)])
+def test_backward_full_size_sampled(name, d_out, d_in):
+    # the 3B-like training shapes at 32768 tokens, as timed: dX on 64 sampled tokens,
+    # dW on 32 sampled output rows over all tokens (split-K and transposes included)
+    T = 32768
+    W = weight(91, d_in, d_out, d_in)
+    x = activation(91, d_out, T, d_in, dist="student_t4")
+    dY = grad_out(91, d_out + 1, T, d_out)
+    dX, dW = gpu_backward(W, x, dY, 6)
+    w_eff, _, g = oracle.effective_weight(W, 6)
+    xq, a = oracle.act_quant(x)
+    rows = sample_rows(91, 3, T, 64)
+    dX_ref, _ = oracle.backward(dY[rows], w_eff, g, xq[rows], a[rows])
+    assert_grad_close(bf16_to_f64(dX)[rows], dX_ref)
+    cols = sample_rows(91, 4, d_out, 32)
     dW_ref = oracle.bf16_to_f64(dY[:, cols]).T @ oracle.dequant_act(xq, a)
     assert_grad_close(dW.cpu().numpy()[cols], dW_ref)
 
