@@ -15,6 +15,7 @@ One step = for each of the 7 linears, in order:
 Metric: tokens per second of whole steps.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+       python bench.py --workload 4     (decode: per-layer latency at 1/8/64 tokens, 6/4/2:8)
 """
 from __future__ import annotations
 
@@ -38,7 +39,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, help="index into sbl_inputs.WORKLOADS (2 or 3)")
+    ap.add_argument("--workload", type=int, default=3, help="index into sbl_inputs.WORKLOADS (2, 3, or 4 = decode)")
     ap.add_argument("--n-keep", type=int, default=6)
     ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -64,6 +65,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     wl = WORKLOADS[args.workload]
+    if not wl.backward and len(wl.T) > 1:
+        run_decode(args, wl)
+        return
     if not wl.backward or len(wl.T) != 1:
         print(f"workload {args.workload} is not a single-T fwd+bwd training workload", file=sys.stderr)
         sys.exit(2)
@@ -219,6 +223,81 @@ def main():
         for li, Lr in enumerate(layers):
             print(Lr["name"], " ".join(f"{p}={per_launch_ms[li, k]:.4f}ms" for k, p in enumerate(parts)),
                   file=sys.stderr)
+    print(json.dumps(line), flush=True)
+
+
+def run_decode(args, wl, copies: int = 16):
+    """Decode workload: act quant + forward of every linear of a layer on pre-packed codes, for
+    each token count and mask.  `copies` distinct packed copies of the layer (more bytes than
+    the 256 MB last-level cache) are walked in turn inside one captured HIP graph, so the code
+    planes stream from HBM; the figure is graph time / copies per layer."""
+    import numpy as np
+    import torch
+
+    import sparsity_sparse_bitlinear_amd as sbl
+    from sbl_inputs import activation, weight
+
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    Ws = [up(weight(wl.cfg, mi, L.d_out, L.d_in)) for mi, L in enumerate(wl.linears)]
+    results = []
+    for n_keep in wl.n_keep:
+        packed = [sbl.quant_mask_pack(W, n_keep, want_mask=False) for W in Ws]
+        # distinct buffers holding the same packed layer: the graph walks all of them
+        layers = [[(L, codes.clone(), gamma.clone()) for L, (codes, _, gamma) in zip(wl.linears, packed)]
+                  for _ in range(copies)]
+        torch.cuda.synchronize()
+        code_bytes = sum(L.d_out * L.d_in // 4 for L in wl.linears)
+        for T in wl.T:
+            bufs = []
+            for mi, L in enumerate(wl.linears):
+                x = up(activation(wl.cfg, mi, T, L.d_in, dist=wl.act_dist))
+                bufs.append(dict(x=x, x_q=torch.empty((T, L.d_in), dtype=torch.int8, device=dev),
+                                 a=torch.empty((T,), dtype=torch.float32, device=dev),
+                                 y=torch.empty((T, L.d_out), dtype=torch.bfloat16, device=dev)))
+
+            def layer(mats):
+                for (L, codes, gamma), b in zip(mats, bufs):
+                    sbl.act_quant(b["x"], x_q=b["x_q"], absmax=b["a"])
+                    sbl.forward(codes, gamma, b["x_q"], b["a"], out_dtype=sbl.BF16, y=b["y"])
+
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for mats in layers:         # warm up outside the capture
+                    layer(mats)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for mats in layers:
+                    layer(mats)
+            for _ in range(args.warmup):
+                g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / args.steps / copies
+            io_bytes = sum(2 * T * L.d_in + 2 * T * L.d_out for L in wl.linears)
+            results.append({"T": T, "n_keep": n_keep, "us_per_layer": round(us, 3),
+                            "tokens_per_s": round(T / (us * 1e-6), 1),
+                            "GBps": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9, 1),
+                            "frac_hbm": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+            del g
+    line = {"metric": "Sparse-BitLinear decode: act quant + forward of a 3B-like layer (7 linears) on packed codes",
+            "value": results[0]["us_per_layer"], "unit": "us per layer (T=%d, %d:8)" % (results[0]["T"], results[0]["n_keep"]),
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+            "vs_baseline": None, "dtype": "int8 x ternary (int32 accumulate), y bf16", "data": "synthetic",
+            "config": {"workload": wl.name, "layer_copies_per_graph": copies,
+                       "code_bytes_per_layer": code_bytes}, "results": results}
     print(json.dumps(line), flush=True)
 
 

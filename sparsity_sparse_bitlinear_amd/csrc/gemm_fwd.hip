@@ -409,7 +409,6 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
 // ---------------------------------------------------------------------------
 constexpr int kDecRows = 16;
 constexpr int kDecWaves = 4;
-constexpr int kDecUnroll = 4;
 
 template <int NTT, int OUT>
 __global__ __launch_bounds__(64 * kDecWaves) void k_fwd_decode(const int8_t* __restrict__ xq,
@@ -417,6 +416,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_fwd_decode(const int8_t* __r
                                                               const float* __restrict__ gamma_p,
                                                               const float* __restrict__ absmax, int T, int d_in,
                                                               int d_out, void* __restrict__ y) {
+  constexpr int kDecUnroll = 4;  // k steps in flight per wave
   __shared__ int red[kDecWaves - 1][NTT][4][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_fwd_decode(const int8_t* __r
   }
   __syncthreads();
   if (wave != 0) return;
-#pragma unroll
+#pragma unroll 1
   for (int w = 0; w < kDecWaves - 1; ++w)
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)

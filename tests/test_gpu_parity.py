@@ -199,6 +199,43 @@ def test_decode_full_size(T, name, d_out, d_in):
     np.testing.assert_array_equal(acc, acc_ref)
 
 
+def test_decode_graph_replay_matches_eager():
+    # act quant + forward captured in a HIP graph (as the decode measurement runs them):
+    # every replay, with eager work between replays, equals the eager result
+    W = weight(75, 0, 512, 1024)
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6, want_mask=False)
+    x = to_dev_bf16(activation(75, 1, 8, 1024, dist="student_t4"))
+    xq = torch.empty((8, 1024), dtype=torch.int8, device="cuda")
+    a = torch.empty((8,), dtype=torch.float32, device="cuda")
+    y = torch.empty((8, 512), dtype=torch.bfloat16, device="cuda")
+
+    def run():
+        sbl.act_quant(x, x_q=xq, absmax=a)
+        sbl.forward(codes, gamma, xq, a, out_dtype=sbl.BF16, y=y)
+
+    run()
+    torch.cuda.synchronize()
+    want = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(4):
+        y.zero_()
+        xq.zero_()
+        other = sbl.forward(codes, gamma, xq, a)        # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"replay {i}"
+        assert other.shape == (8, 512)
+
+
 @pytest.mark.parametrize("name,d_out,d_in", [("gate", 11008, 2048), ("down", 2048, 11008)])
 def test_forward_full_size_sampled(name, d_out, d_in):
     # the 3B-like training shapes at 32768 tokens, as timed: 64 sampled tokens, all outputs, exact int32
