@@ -30,6 +30,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per sbl_backward(dW) call on the default workload (FETCH_SIZE x 2.000 + WRITE_SIZE,
+# scale factors from a plain 1 GiB copy), averaged over the 7 linears; measured with rocprofv3
+# --pmc for the dW kernel sources whose hash is given (profiles/traffic_dw_3b_32768tok.md).
+DW_TRAFFIC_BYTES = 2.99e9
+DW_TRAFFIC_SRC_SHA = "a8499784ba65b525"
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -187,8 +193,12 @@ def main():
     dname, dunit, dpeak, dkernels = gemm_parts[dom]
     n_launch = len(layers)
     achieved = sum(w[dom] for w in work) / n_launch / (tot_ms[parts.index(dom)] / n_launch * 1e-3) / 1e12
+    traffic = None
+    if dom == "dw" and args.workload == 3 and n_keep == 6 and _dw_sources_sha() == DW_TRAFFIC_SRC_SHA:
+        traffic = DW_TRAFFIC_BYTES
     roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 1), "peak": dpeak,
-                "unit": dunit, "frac": round(achieved / dpeak, 4), "traffic": None,
+                "unit": dunit, "frac": round(achieved / dpeak, 4), "traffic": traffic,
+                "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                 "launches_per_step": n_launch, "hip_kernels": dkernels,
                 "avg_launch_ms": round(tot_ms[parts.index(dom)] / n_launch, 4)}
 
@@ -224,6 +234,15 @@ def main():
             print(Lr["name"], " ".join(f"{p}={per_launch_ms[li, k]:.4f}ms" for k, p in enumerate(parts)),
                   file=sys.stderr)
     print(json.dumps(line), flush=True)
+
+
+def _dw_sources_sha() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm_common.h", "gemm_nt.hip", "gemm_bwd.hip"):
+        with open(os.path.join(ROOT, "sparsity_sparse_bitlinear_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def run_decode(args, wl, copies: int = 16):
