@@ -10,8 +10,8 @@ One step = for each of the 7 linears, in order:
   sbl_quant_mask_pack (gamma, 6:8 mask, codes; recomputed every step)
   sbl_act_quant       (per-token absmax int8)
   sbl_forward         (int8 MFMA, y bf16)
-  sbl_backward(dX)    (bf16 MFMA, dX bf16)
-  sbl_backward(dW)    (bf16 MFMA, dW float32, dense)
+  sbl_backward        (dX and dW in one call: bf16 MFMA, dX bf16, dW float32 dense;
+                       the dX product leaves dY^T behind for dW)
 Metric: tokens per second of whole steps.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
@@ -31,11 +31,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per sbl_backward(dW) call on the default workload (FETCH_SIZE x 2.000 + WRITE_SIZE,
-# scale factors from a plain 1 GiB copy), averaged over the 7 linears; measured with rocprofv3
-# --pmc for the dW kernel sources whose hash is given (profiles/traffic_dw_3b_32768tok.md).
-DW_TRAFFIC_BYTES = 2.99e9
-DW_TRAFFIC_SRC_SHA = "a8499784ba65b525"
+# HBM bytes per sbl_backward(dX + dW) call on the default workload (FETCH_SIZE x 2.000 +
+# WRITE_SIZE, scale factors from a plain 1 GiB copy), averaged over the 7 linears; measured with
+# rocprofv3 --pmc for the backward kernel sources whose hash is given
+# (profiles/traffic_backward_3b_32768tok.md).  None until measured for these sources.
+BWD_TRAFFIC_BYTES = None
+BWD_TRAFFIC_SRC_SHA = ""
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -108,7 +109,7 @@ def main():
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
-    parts = ("quant", "act", "fwd", "dx", "dw")
+    parts = ("quant", "act", "fwd", "bwd")
 
     def step(events=None):
         for li, Lr in enumerate(layers):
@@ -123,12 +124,9 @@ def main():
             mark(2)
             sbl.forward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], out_dtype=sbl.BF16, y=Lr["y"])
             mark(3)
-            sbl.backward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], Lr["dY"], need_dx=True, need_dw=False,
-                         dx_dtype=sbl.BF16, dX=Lr["dX"], workspace=Lr["bws"])
+            sbl.backward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], Lr["dY"], dx_dtype=sbl.BF16,
+                         dX=Lr["dX"], dW=Lr["dW"], workspace=Lr["bws"])
             mark(4)
-            sbl.backward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], Lr["dY"], need_dx=False, need_dw=True,
-                         dW=Lr["dW"], workspace=Lr["bws"])
-            mark(5)
 
     for _ in range(args.warmup):
         step()
@@ -148,11 +146,11 @@ def main():
     # per-kernel durations behind the roofline figures.
     sums = np.zeros((len(layers), len(parts)))
     for _ in range(args.steps):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in layers]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in layers]
         step(ev)
         torch.cuda.synchronize()
         for li in range(len(layers)):
-            for k in range(5):
+            for k in range(len(parts)):
                 sums[li, k] += ev[li][k].elapsed_time(ev[li][k + 1])
     per_launch_ms = sums / args.steps          # [layer, part]
 
@@ -165,10 +163,9 @@ def main():
             quant=2.375 * nw,                                   # bytes: read W (2) + codes (0.25) + mask (0.125)
             act=3.0 * T * d_in + 4.0 * T,                       # bytes: read x (2), write x_q (1), absmax (4/token)
             fwd=2.0 * T * d_out * d_in * n_keep / 8.0,          # int8 ops on kept weights
-            dx=2.0 * T * d_out * d_in * n_keep / 8.0,           # bf16 flops on kept weights
-            dw=2.0 * T * d_out * d_in,                          # bf16 flops, dense (Dual STE)
+            bwd=2.0 * T * d_out * d_in * n_keep / 8.0 + 2.0 * T * d_out * d_in,  # dX on kept weights + dense dW
             fwd_issued=2.0 * T * d_out * d_in,
-            dx_issued=2.0 * T * d_out * d_in,
+            bwd_issued=4.0 * T * d_out * d_in,
         ))
     tot_ms = per_launch_ms.sum(axis=0)
     def rate(part):
@@ -178,24 +175,24 @@ def main():
         "act_quant": dict(ms=tot_ms[1], GBps=rate("act") / 1e9, frac_hbm=rate("act") / 1e9 / HBM_PEAK_GBS),
         "forward_int8": dict(ms=tot_ms[2], TOPs=rate("fwd") / 1e12, frac_int8=rate("fwd") / 1e12 / INT8_PEAK_TOPS,
                              frac_int8_issued=sum(w["fwd_issued"] for w in work) / (tot_ms[2] * 1e-3) / 1e12 / INT8_PEAK_TOPS),
-        "backward_dx_bf16": dict(ms=tot_ms[3], TFLOPs=rate("dx") / 1e12, frac_bf16=rate("dx") / 1e12 / BF16_PEAK_TFLOPS,
-                                 frac_bf16_issued=sum(w["dx_issued"] for w in work) / (tot_ms[3] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS),
-        "backward_dw_bf16": dict(ms=tot_ms[4], TFLOPs=rate("dw") / 1e12, frac_bf16=rate("dw") / 1e12 / BF16_PEAK_TFLOPS),
+        "backward_bf16": dict(ms=tot_ms[3], TFLOPs=rate("bwd") / 1e12, frac_bf16=rate("bwd") / 1e12 / BF16_PEAK_TFLOPS,
+                              frac_bf16_issued=sum(w["bwd_issued"] for w in work) / (tot_ms[3] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS),
     }
     # HIP kernels behind each timed call (the events bracket the whole call)
     gemm_parts = {
         "fwd": ("forward_int8", "TOP/s", INT8_PEAK_TOPS, ["k_fwd_i8_direct<bf16>"]),
-        "dx": ("backward_dx_bf16", "TFLOP/s", BF16_PEAK_TFLOPS, ["k_weff_t_bf16", "k_gemm_nt_bf16<bf16>"]),
-        "dw": ("backward_dw_bf16", "TFLOP/s", BF16_PEAK_TFLOPS,
-               ["k_token_major<dY>", "k_token_major<x~>", "k_gemm_nt_bf16<f32>", "k_splitk_reduce (split-K shapes)"]),
+        "bwd": ("backward_bf16 (dX + dW)", "TFLOP/s", BF16_PEAK_TFLOPS,
+                ["k_weff_t_bf16", "k_gemm_nt_bf16<bf16, writes dY^T>", "k_token_major<x~>", "k_gemm_nt_bf16<f32>",
+                 "k_splitk_reduce (split-K shapes)"]),
     }
     dom = max(gemm_parts, key=lambda p: tot_ms[parts.index(p)])
     dname, dunit, dpeak, dkernels = gemm_parts[dom]
     n_launch = len(layers)
     achieved = sum(w[dom] for w in work) / n_launch / (tot_ms[parts.index(dom)] / n_launch * 1e-3) / 1e12
     traffic = None
-    if dom == "dw" and args.workload == 3 and n_keep == 6 and _dw_sources_sha() == DW_TRAFFIC_SRC_SHA:
-        traffic = DW_TRAFFIC_BYTES
+    if (dom == "bwd" and args.workload == 3 and n_keep == 6 and BWD_TRAFFIC_BYTES is not None
+            and _bwd_sources_sha() == BWD_TRAFFIC_SRC_SHA):
+        traffic = BWD_TRAFFIC_BYTES
     roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 1), "peak": dpeak,
                 "unit": dunit, "frac": round(achieved / dpeak, 4), "traffic": traffic,
                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
@@ -236,7 +233,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def _dw_sources_sha() -> str:
+def _bwd_sources_sha() -> str:
     import hashlib
     h = hashlib.sha256()
     for f in ("gemm_common.h", "gemm_nt.hip", "gemm_bwd.hip"):

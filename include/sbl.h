@@ -165,8 +165,12 @@ SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t*
  * per-call operand copies of the matrix-core path -- W_eff^T as bf16
  * ([d_in, d_out], for dX), dY^T and x~^T as bf16 ([d_out, T8] and
  * [d_in, T8] with T8 = T rounded up to 8, for dW) -- and split-K partial sums
- * of dW.  The dX and dW parts are used one after the other and share the
- * space.  0 when nothing is needed (e.g. T = 0). */
+ * of dW.  With SBL_BWD_DX | SBL_BWD_DW on shapes that take the matrix-core
+ * path for both, the dX product also writes dY^T into the workspace, which
+ * the dW product then reads, so that region is kept from one to the other and
+ * W_eff^T shares space with x~^T only; otherwise the dX and dW parts are used
+ * one after the other and share the space.  0 when nothing is needed (e.g.
+ * T = 0). */
 SBL_API size_t sbl_backward_workspace_size(int64_t T, int64_t d_in, int64_t d_out, int flags);
 
 /* Dual-STE backward ([SUM] 前置知识 > Straight-Through Estimator (STE);
@@ -187,8 +191,10 @@ SBL_API size_t sbl_backward_workspace_size(int64_t T, int64_t d_in, int64_t d_ou
  *           SBL_BWD_DX.
  * dW      : [d_out, d_in] float32; may be NULL without SBL_BWD_DW.  With
  *           T = 0, dW is set to zero.
- * workspace: at least sbl_backward_workspace_size(...) bytes (may be NULL
- *           when that size is 0).
+ * workspace: at least sbl_backward_workspace_size(...) bytes for the same
+ *           flags (may be NULL when that size is 0).  Asking for both
+ *           gradients in one call costs less than two calls: dY is
+ *           transposed once, by the dX product, for both.
  */
 SBL_API int sbl_backward(const uint16_t* codes, const float* gamma, const int8_t* x_q, const float* absmax,
                          const uint16_t* dY_bf16, int64_t T, int64_t d_in, int64_t d_out, void* dX,

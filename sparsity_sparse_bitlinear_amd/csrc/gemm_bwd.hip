@@ -556,14 +556,16 @@ int dw_splits(int64_t T, int64_t d_in, int64_t d_out) {
 }  // namespace
 
 // Workspace of the dW path: dY^T and x~^T ([d_out, T8] and [d_in, T8] bf16),
-// then the split-K partial sums.
+// then the split-K partial sums.  When dX and dW are computed in one call, the
+// dX product writes dY^T itself, and W_eff^T (needed only by the dX product)
+// sits where x~^T is written afterwards.
 struct DwLayout {
-  size_t dyt, xt, part, total;
+  size_t dyt, xt, part, wt, total;
   int S;
   int64_t kps;
 };
 
-DwLayout dw_layout(int64_t T, int64_t d_in, int64_t d_out) {
+DwLayout dw_layout(int64_t T, int64_t d_in, int64_t d_out, bool fused) {
   DwLayout L{};
   const int64_t T8 = round8(T);
   nt_splits(d_out, d_in, T8, L.S, L.kps);
@@ -571,17 +573,55 @@ DwLayout dw_layout(int64_t T, int64_t d_in, int64_t d_out) {
   L.xt = align256((size_t)d_out * (size_t)T8 * 2);
   L.part = L.xt + align256((size_t)d_in * (size_t)T8 * 2);
   L.total = L.part + (L.S > 1 ? (size_t)L.S * (size_t)d_out * (size_t)d_in * sizeof(float) : 0);
+  L.wt = L.xt;
+  if (fused) L.total = std::max(L.total, L.wt + align256((size_t)d_out * (size_t)d_in * 2));
   return L;
+}
+
+bool fused_backward(int64_t T, int64_t d_in, int64_t d_out, int flags) {
+  return (flags & SBL_BWD_DX) && (flags & SBL_BWD_DW) && dx_direct(T, d_in, d_out) && dw_direct(T, d_in, d_out);
+}
+
+// dW on the plain GEMM engine from the layout L: dY^T (unless the dX product
+// already wrote it), x~^T, the product, and the split-K sum.
+hipError_t run_dw_direct(const int8_t* xq, const float* absmax, const uint16_t* dY, int64_t T, int64_t d_in,
+                         int64_t d_out, float* dW, void* ws, const DwLayout& L, bool dyt_ready, hipStream_t s) {
+  const int64_t T8 = round8(T);
+  const int64_t n = d_out * d_in;
+  uint16_t* dyt = (uint16_t*)((char*)ws + L.dyt);
+  uint16_t* xt = (uint16_t*)((char*)ws + L.xt);
+  if (!dyt_ready) {
+    const dim3 g1((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_out + kTT - 1) / kTT));
+    if (d_out % 8 == 0)
+      hipLaunchKernelGGL((k_token_major<false, true>), g1, dim3(256), 0, s, dY, nullptr, (int)T, (int)d_out, (int)T8, dyt);
+    else
+      hipLaunchKernelGGL((k_token_major<false, false>), g1, dim3(256), 0, s, dY, nullptr, (int)T, (int)d_out, (int)T8, dyt);
+  }
+  const dim3 g2((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_in + kTT - 1) / kTT));
+  hipLaunchKernelGGL((k_token_major<true, true>), g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  float* target = L.S > 1 ? (float*)((char*)ws + L.part) : dW;
+  e = launch_gemm_nt_bf16(dyt, xt, d_out, d_in, T8, nullptr, target, SBL_F32, s, L.S, L.kps);
+  if (e != hipSuccess) return e;
+  if (L.S > 1) {
+    const int64_t n4 = n / 4;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 65536)), dim3(256), 0, s,
+                       (const float4*)target, n4, L.S, (float4*)dW);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 // The dX transpose plane and the dW buffers are used one after the other on
 // the same stream, so they share the workspace.
 size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flags) {
+  if (fused_backward(T, d_in, d_out, flags)) return dw_layout(T, d_in, d_out, true).total;
   size_t dx = 0, dw = 0;
   if ((flags & SBL_BWD_DX) && dx_direct(T, d_in, d_out)) dx = align256((size_t)d_out * (size_t)d_in * 2);
   if ((flags & SBL_BWD_DW) && T > 0) {
     if (dw_direct(T, d_in, d_out)) {
-      dw = dw_layout(T, d_in, d_out).total;
+      dw = dw_layout(T, d_in, d_out, false).total;
     } else {
       const int S = dw_splits(T, d_in, d_out);
       if (S > 1) dw = (size_t)S * (size_t)d_out * (size_t)d_in * sizeof(float);
@@ -593,6 +633,19 @@ size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flag
 hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                            const uint16_t* dY, int64_t T, int64_t d_in, int64_t d_out, void* dX, int dx_dtype,
                            float* dW, int flags, void* ws, hipStream_t s) {
+  if (fused_backward(T, d_in, d_out, flags)) {
+    // dX, leaving dY^T behind in the workspace, then dW from it
+    const DwLayout L = dw_layout(T, d_in, d_out, true);
+    uint16_t* WT = (uint16_t*)((char*)ws + L.wt);
+    const dim3 tgrid((unsigned)((d_out + kTrO - 1) / kTrO), (unsigned)((d_in / 8 + kTrG - 1) / kTrG));
+    hipLaunchKernelGGL(k_weff_t_bf16, tgrid, dim3(256), 0, s, codes, (int)d_out, (int)d_in, WT);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_gemm_nt_bf16(dY, WT, T, d_in, d_out, gamma, dX, dx_dtype, s, 1, 0, (uint16_t*)((char*)ws + L.dyt),
+                            round8(T));
+    if (e != hipSuccess) return e;
+    return run_dw_direct(xq, absmax, dY, T, d_in, d_out, dW, ws, L, true, s);
+  }
   if ((flags & SBL_BWD_DX) && dx_direct(T, d_in, d_out)) {
     uint16_t* WT = (uint16_t*)ws;
     const dim3 tgrid((unsigned)((d_out + kTrO - 1) / kTrO), (unsigned)((d_in / 8 + kTrG - 1) / kTrG));
@@ -620,32 +673,8 @@ hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8
       hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)std::min<int64_t>((n + 255) / 256, 65536)), dim3(256), 0, s, dW, n);
       return hipGetLastError();
     }
-    if (dw_direct(T, d_in, d_out)) {
-      const DwLayout L = dw_layout(T, d_in, d_out);
-      const int64_t T8 = round8(T);
-      uint16_t* dyt = (uint16_t*)((char*)ws + L.dyt);
-      uint16_t* xt = (uint16_t*)((char*)ws + L.xt);
-      const dim3 g1((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_out + kTT - 1) / kTT));
-      if (d_out % 8 == 0)
-        hipLaunchKernelGGL((k_token_major<false, true>), g1, dim3(256), 0, s, dY, nullptr, (int)T, (int)d_out, (int)T8, dyt);
-      else
-        hipLaunchKernelGGL((k_token_major<false, false>), g1, dim3(256), 0, s, dY, nullptr, (int)T, (int)d_out, (int)T8, dyt);
-      const dim3 g2((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_in + kTT - 1) / kTT));
-      hipLaunchKernelGGL((k_token_major<true, true>), g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      float* target = L.S > 1 ? (float*)((char*)ws + L.part) : dW;
-      e = launch_gemm_nt_bf16(dyt, xt, d_out, d_in, T8, nullptr, target, SBL_F32, s, L.S, L.kps);
-      if (e != hipSuccess) return e;
-      if (L.S > 1) {
-        const int64_t n4 = n / 4;
-        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 65536)), dim3(256), 0,
-                           s, (const float4*)target, n4, L.S, (float4*)dW);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-      }
-      return hipSuccess;
-    }
+    if (dw_direct(T, d_in, d_out))
+      return run_dw_direct(xq, absmax, dY, T, d_in, d_out, dW, ws, dw_layout(T, d_in, d_out, false), false, s);
     const int S = dw_splits(T, d_in, d_out);
     const int64_t kps = ((T + S - 1) / S + kBK - 1) / kBK * kBK;
     const int64_t tiles = ((d_in + kBN - 1) / kBN) * ((d_out + kBM - 1) / kBM);

@@ -49,11 +49,19 @@ constexpr int kKStep = kRowK / 2;         // 64 bf16 per K step
 // Requires K % 8 == 0 (16-byte rows, K chunks never straddle a row end).
 // blockIdx.y selects a K range [kps * y, kps * (y + 1)) (split-K); block y writes
 // its partial product to C + y * M * N.  alpha_p == nullptr means alpha = 1.
-template <int OUT>
+//
+// WTA (no split-K): the A tiles staged in LDS are also written out transposed,
+// AT[k, m] = A[m, k] with row length at_ld (>= M, a multiple of 8; columns M
+// to at_ld read as zero from the tile and are written as zeros).  This is how
+// the dX product leaves dY^T behind for dW: every (m tile, K step) is written
+// once, by the block whose column tile index equals the step modulo the number
+// of column tiles, from the stage as soon as it has landed.
+template <int OUT, bool WTA>
 __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B, int M, int N, int K,
                                                               int kps, const float* __restrict__ alpha_p,
-                                                              void* __restrict__ C) {
+                                                              void* __restrict__ C, uint16_t* __restrict__ AT,
+                                                              int at_ld) {
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
 
   const int tid = threadIdx.x;
@@ -131,6 +139,36 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     for (int j = 0; j < kNJ; ++j)
       fb[j] = __builtin_bit_cast(v8bf, *(const v4i*)(b + swz8(wn0 + 32 * j + (lane & 31), 2 * ks + (lane >> 5))));
   };
+  // Transposed copy of the A tile of stage st (K step k0): wave w takes 16
+  // K-columns (16 (w % 4) ..) and 128 rows (128 (w / 4) ..) in 4 rounds of 32;
+  // in each round its 16-lane group g reads rows 8 g .. 8 g + 7 with two
+  // ds_read_b64_tr_b16 (lane i: 4 rows of column i each) and stores them as
+  // one 16-byte run of AT row k0 + column.
+  const int gn = (N + kBNn - 1) / kBNn;
+  auto write_at = [&](int st, int k0) {
+    const char* a = lds + st * kStage;
+    const int kb = 16 * (wave & 3), tb0 = 128 * (wave >> 2);
+    const int g = lane >> 4, q = lane & 15;
+    const auto atr = make_rsrc(AT + (int64_t)k0 * at_ld + m0, clamp_bytes((int64_t)(K - k0) * at_ld * 2 - m0 * 2));
+    const int kc = kb + 4 * (q & 3);                    // first of the 4 columns lane q addresses
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t0 = tb0 + 32 * r + 8 * g;              // first of this group's 8 rows
+      v4s part[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = t0 + 4 * h + (q >> 2);
+        const SBL_LDS char* p = (const SBL_LDS char*)(a + swz8(row, kc >> 3) + 2 * (kc & 7));
+        part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBL_LDS v4s*)p);
+      }
+      const int col = kb + q;                           // this lane's K column
+      const bool ok = k0 + col < K && m0 + t0 < at_ld;
+      const v4i v = __builtin_bit_cast(v4i, (v8s){part[0][0], part[0][1], part[0][2], part[0][3],
+                                                   part[1][0], part[1][1], part[1][2], part[1][3]});
+      __builtin_amdgcn_raw_buffer_store_b128(v, atr, ok ? (uint32_t)((col * at_ld + t0) * 2) : kOOB, 0, 0);
+    }
+  };
+
   auto mm = [&](const v8bf (&fa)[kMI], const v8bf (&fb)[kNJ]) {
 #pragma unroll
     for (int i = 0; i < kMI; ++i)
@@ -156,6 +194,9 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   issue(min(1, last), 1);
   wait_vmcnt<kDmaStep>();
   barrier_only();
+  if constexpr (WTA) {
+    if (nt == 0) write_at(0, kbeg);
+  }
   rd(0, 0, fa0, fb0);
   int sc = 0;
   for (int k = 0; k < nk; ++k) {
@@ -174,6 +215,13 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     wait_vmcnt_lgkm0<0>();
     barrier_only();
     __builtin_amdgcn_sched_barrier(0);
+    // Transposed copy of step k + 1's A tile: it has just landed and is not
+    // refilled before the next barrier; no loads are in flight yet, so the
+    // reads wait for nothing.
+    if constexpr (WTA) {
+      if (k + 1 < nk && (k + 1) % gn == nt) write_at(sc ^ 1, kbeg + (k + 1) * kKStep);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     issue(min(k + 2, last), sc);
     rd(sc ^ 1, 0, fa0, fb0);
     mm(fa1, fb1);
@@ -238,16 +286,26 @@ int64_t gemm_nt_bf16_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) 
 
 hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
                                const float* alpha, void* C, int out_dtype, hipStream_t s, int splits,
-                               int64_t k_per_split) {
+                               int64_t k_per_split, uint16_t* AT, int64_t at_ld) {
   if (splits < 1) splits = 1;
   if (splits == 1) k_per_split = K;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
-  if (out_dtype == SBL_F32)
-    hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K, (int)k_per_split,
-                       alpha, C);
-  else
-    hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_BF16>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
-                       (int)k_per_split, alpha, C);
+  if (AT) {
+    if (splits != 1) return hipErrorInvalidValue;
+    if (out_dtype == SBL_F32)
+      hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32, true>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
+                         (int)k_per_split, alpha, C, AT, (int)at_ld);
+    else
+      hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_BF16, true>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
+                         (int)k_per_split, alpha, C, AT, (int)at_ld);
+  } else {
+    if (out_dtype == SBL_F32)
+      hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32, false>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
+                         (int)k_per_split, alpha, C, nullptr, 0);
+    else
+      hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_BF16, false>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
+                         (int)k_per_split, alpha, C, nullptr, 0);
+  }
   return hipGetLastError();
 }
 

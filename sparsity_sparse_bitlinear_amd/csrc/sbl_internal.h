@@ -77,9 +77,11 @@ hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_
 // product to C + z * M * N.
 bool gemm_nt_bf16_supported(int64_t M, int64_t N, int64_t K);
 int64_t gemm_nt_bf16_tiles(int64_t M, int64_t N);
+// AT != nullptr (splits == 1): also write A^T [K, at_ld] (at_ld >= M, a multiple
+// of 8; columns from M to at_ld become zero).
 hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
                                const float* alpha, void* C, int out_dtype, hipStream_t s, int splits = 1,
-                               int64_t k_per_split = 0);
+                               int64_t k_per_split = 0, uint16_t* AT = nullptr, int64_t at_ld = 0);
 
 size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flags);
 hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,

@@ -319,6 +319,22 @@ def test_backward_full_size_sampled(name, d_out, d_in):
     assert_grad_close(dW.cpu().numpy()[cols], dW_ref)
 
 
+@pytest.mark.parametrize("T,d_out,d_in", [(1000, 520, 776), (77, 200, 328), (4096, 256, 2048), (300, 2048, 512)])
+def test_backward_fused_matches_separate(T, d_out, d_in):
+    # dX and dW in one call (the dX product writes dY^T for dW) equal the two separate calls bit for bit
+    W = weight(95, d_out + d_in, d_out, d_in)
+    x = activation(95, d_out + d_in + T, T, d_in, dist="student_t4")
+    dY = to_dev_bf16(grad_out(95, d_out + d_in + T + 1, T, d_out))
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+    xq, a = sbl.act_quant(to_dev_bf16(x))
+    dX, dW = sbl.backward(codes, gamma, xq, a, dY)
+    dX1, _ = sbl.backward(codes, gamma, xq, a, dY, need_dw=False)
+    _, dW1 = sbl.backward(codes, gamma, xq, a, dY, need_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dX.view(torch.int16), dX1.view(torch.int16))
+    assert torch.equal(dW, dW1)
+
+
 def test_backward_zero_tokens():
     W = weight(71, 0, 64, 64)
     codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
