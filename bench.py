@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print the per-linear breakdown to stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -59,7 +61,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "this build has no multi-GPU path.", file=sys.stderr)
+              "the operator has no multi-GPU path here.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -71,6 +73,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        # 1 GiB read + 1 GiB written per copy, float32
+        a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print("copy calibration done", flush=True)
+        return
     wl = WORKLOADS[args.workload]
     if not wl.backward and len(wl.T) > 1:
         run_decode(args, wl)

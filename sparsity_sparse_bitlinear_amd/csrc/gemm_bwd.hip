@@ -207,37 +207,62 @@ __global__ __launch_bounds__(kThreads, 2) void k_bwd_dx(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// W_eff^T as bf16 for the direct-load dX path:  WT[i, o] = W_eff[o, i] in
-// {-1, 0, +1} (exact), WT [d_in, d_out] row-major, d_out % 8 == 0.  A block
-// transposes 64 code rows o x 32 groups (256 columns i) through LDS and writes
-// 16-byte runs of 8 consecutive o.
+// W_eff^T for the direct-load dX product, still as 2-bit codes: the code plane
+// [d_out, d_in / 8] transposed to one row per column i, in the word layout the
+// product widens in registers (gemm_nt.hip, BC): per 64 rows o from o = 64 s,
+// 4 words; word 2 h + w holds groups g = 4 w + 2 ss + h (ss = 0, 1) of 8
+// consecutive o, the codes of o = 64 s + 8 g + 2 q and + 1 at bits 14 - 2p and
+// 30 - 2p, p = 4 ss + q.  Rows are k64 / 4 bytes, k64 = d_out rounded up to
+// 64; codes past d_out are 00 (zero).  A block takes 256 columns x 256 rows o
+// through LDS (group-major, so a column's codes of 8 consecutive o are one
+// 16-byte read) and writes 64 contiguous bytes per column.
 // ---------------------------------------------------------------------------
-constexpr int kTrO = 64, kTrG = 32;
+constexpr int kCtI = 256, kCtO = 256;
 
-__global__ __launch_bounds__(256) void k_weff_t_bf16(const uint16_t* __restrict__ codes, int d_out, int d_in,
-                                                     uint16_t* __restrict__ WT) {
-  __shared__ uint16_t tile[kTrO][kTrG + 1];
+__global__ __launch_bounds__(256) void k_codes_t(const uint16_t* __restrict__ codes, int d_out, int d_in, int k64,
+                                                 uint32_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kCtI / 8][kCtO + 8];  // [group][o]
   const int G = d_in >> 3;
-  const int o0 = blockIdx.x * kTrO, g0 = blockIdx.y * kTrG;
+  const int i0 = blockIdx.x * kCtI, o0 = blockIdx.y * kCtO;
+  const int g0 = i0 >> 3;
   const int tid = threadIdx.x;
-  for (int e = tid; e < kTrO * kTrG; e += 256) {
-    const int r = e / kTrG, g = e % kTrG;
-    tile[r][g] = (o0 + r < d_out && g0 + g < G) ? codes[(int64_t)(o0 + r) * G + g0 + g] : (uint16_t)0;
+  for (int e = tid; e < kCtO * (kCtI / 8); e += 256) {
+    const int r = e / (kCtI / 8), g = e % (kCtI / 8);
+    tile[g][r] = (o0 + r < d_out && g0 + g < G) ? codes[(int64_t)(o0 + r) * G + g0 + g] : (uint16_t)0;
   }
   __syncthreads();
-  for (int c = tid; c < kTrG * 8 * (kTrO / 8); c += 256) {
-    const int il = c / (kTrO / 8), oc = c % (kTrO / 8);
-    const int i = g0 * 8 + il, o = o0 + 8 * oc;
-    if (i >= d_in || o >= d_out) continue;
-    const int gl = il >> 3, slot = il & 7;
-    uint32_t v[4];
+  const int i = i0 + tid;
+  if (i >= d_in) return;
+  const int gl = tid >> 3, sh = 2 * (tid & 7);
+  const int64_t row_words = k64 / 16;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t pair = (uint32_t)tile[8 * oc + 2 * u][gl] | ((uint32_t)tile[8 * oc + 2 * u + 1][gl] << 16);
-      v[u] = code_pair_to_bf16x2((pair >> (2 * slot)) & 0x00030003u);
+  for (int st = 0; st < kCtO / 64; ++st) {
+    const int ob = o0 + 64 * st;
+    if (ob >= k64) break;
+    uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      const uint4 v = *(const uint4*)&tile[gl][64 * st + 8 * g];
+      const uint32_t e2[4] = {v.x, v.y, v.z, v.w};  // o = 8 g + 2 q (low half) and + 1 (high half)
+      const int ks = g >> 1, h = g & 1;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int p = 4 * (ks & 1) + q;
+        const uint32_t c0 = (e2[q] >> sh) & 3u, c1 = (e2[q] >> (16 + sh)) & 3u;
+        wv[2 * h + (ks >> 1)] |= (c0 << (14 - 2 * p)) | (c1 << (30 - 2 * p));
+      }
     }
-    *(uint4*)(WT + (int64_t)i * d_out + o) = make_uint4(v[0], v[1], v[2], v[3]);
+    *(uint4*)(out + (int64_t)i * row_words + ob / 16) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
   }
+}
+
+size_t codes_t_bytes(int64_t d_in, int64_t d_out) { return (size_t)d_in * (size_t)(((d_out + 63) & ~63) / 4); }
+
+hipError_t launch_codes_t(const uint16_t* codes, int64_t d_out, int64_t d_in, uint32_t* out, hipStream_t s) {
+  const int64_t k64 = (d_out + 63) & ~(int64_t)63;
+  const dim3 grid((unsigned)((d_in + kCtI - 1) / kCtI), (unsigned)((k64 + kCtO - 1) / kCtO));
+  hipLaunchKernelGGL(k_codes_t, grid, dim3(256), 0, s, codes, (int)d_out, (int)d_in, (int)k64, out);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -574,7 +599,7 @@ DwLayout dw_layout(int64_t T, int64_t d_in, int64_t d_out, bool fused) {
   L.part = L.xt + align256((size_t)d_in * (size_t)T8 * 2);
   L.total = L.part + (L.S > 1 ? (size_t)L.S * (size_t)d_out * (size_t)d_in * sizeof(float) : 0);
   L.wt = L.xt;
-  if (fused) L.total = std::max(L.total, L.wt + align256((size_t)d_out * (size_t)d_in * 2));
+  if (fused) L.total = std::max(L.total, L.wt + align256(codes_t_bytes(d_in, d_out)));
   return L;
 }
 
@@ -618,7 +643,7 @@ hipError_t run_dw_direct(const int8_t* xq, const float* absmax, const uint16_t* 
 size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flags) {
   if (fused_backward(T, d_in, d_out, flags)) return dw_layout(T, d_in, d_out, true).total;
   size_t dx = 0, dw = 0;
-  if ((flags & SBL_BWD_DX) && dx_direct(T, d_in, d_out)) dx = align256((size_t)d_out * (size_t)d_in * 2);
+  if ((flags & SBL_BWD_DX) && dx_direct(T, d_in, d_out)) dx = align256(codes_t_bytes(d_in, d_out));
   if ((flags & SBL_BWD_DW) && T > 0) {
     if (dw_direct(T, d_in, d_out)) {
       dw = dw_layout(T, d_in, d_out, false).total;
@@ -636,23 +661,19 @@ hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8
   if (fused_backward(T, d_in, d_out, flags)) {
     // dX, leaving dY^T behind in the workspace, then dW from it
     const DwLayout L = dw_layout(T, d_in, d_out, true);
-    uint16_t* WT = (uint16_t*)((char*)ws + L.wt);
-    const dim3 tgrid((unsigned)((d_out + kTrO - 1) / kTrO), (unsigned)((d_in / 8 + kTrG - 1) / kTrG));
-    hipLaunchKernelGGL(k_weff_t_bf16, tgrid, dim3(256), 0, s, codes, (int)d_out, (int)d_in, WT);
-    hipError_t e = hipGetLastError();
+    uint32_t* WT = (uint32_t*)((char*)ws + L.wt);
+    hipError_t e = launch_codes_t(codes, d_out, d_in, WT, s);
     if (e != hipSuccess) return e;
-    e = launch_gemm_nt_bf16(dY, WT, T, d_in, d_out, gamma, dX, dx_dtype, s, 1, 0, (uint16_t*)((char*)ws + L.dyt),
-                            round8(T));
+    e = launch_gemm_nt_codes(dY, WT, T, d_in, d_out, gamma, dX, dx_dtype, s, (uint16_t*)((char*)ws + L.dyt),
+                             round8(T));
     if (e != hipSuccess) return e;
     return run_dw_direct(xq, absmax, dY, T, d_in, d_out, dW, ws, L, true, s);
   }
   if ((flags & SBL_BWD_DX) && dx_direct(T, d_in, d_out)) {
-    uint16_t* WT = (uint16_t*)ws;
-    const dim3 tgrid((unsigned)((d_out + kTrO - 1) / kTrO), (unsigned)((d_in / 8 + kTrG - 1) / kTrG));
-    hipLaunchKernelGGL(k_weff_t_bf16, tgrid, dim3(256), 0, s, codes, (int)d_out, (int)d_in, WT);
-    hipError_t e = hipGetLastError();
+    uint32_t* WT = (uint32_t*)ws;
+    hipError_t e = launch_codes_t(codes, d_out, d_in, WT, s);
     if (e != hipSuccess) return e;
-    e = launch_gemm_nt_bf16(dY, WT, T, d_in, d_out, gamma, dX, dx_dtype, s);
+    e = launch_gemm_nt_codes(dY, WT, T, d_in, d_out, gamma, dX, dx_dtype, s);
     if (e != hipSuccess) return e;
   } else if ((flags & SBL_BWD_DX) && T > 0) {
     const dim3 grid((unsigned)(((d_in + kBN - 1) / kBN) * ((T + kBM - 1) / kBM)));

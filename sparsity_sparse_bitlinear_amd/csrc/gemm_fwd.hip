@@ -264,6 +264,16 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
     dma16(br, sa + kFStageA + 1024 * wave, b_off, (uint32_t)kt * (kFK / 4));
   };
 
+  // Output scales of this lane's rows, fetched before the K loop so the
+  // epilogue does not wait on them.
+  float am[kMI];
+#pragma unroll
+  for (int i = 0; i < kMI; ++i) {
+    const int m = m0 + wm0 + 32 * i + (lane & 31);
+    am[i] = m < T ? absmax[m] : 0.0f;
+  }
+  const float g127 = *gamma_p * (1.0f / 127.0f);
+
   v16i acc[kMI][kNJ];
 #pragma unroll
   for (int i = 0; i < kMI; ++i)
@@ -353,16 +363,54 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
 #undef SBL_FWD_SLICE_ORDER
   wait_vmcnt<0>();
 
+  // bf16 output with 16-byte aligned rows: the wave's 128 x 64 result goes
+  // through LDS in two rounds of 64 rows (8 KB per wave, rows of 128 bytes,
+  // 16-byte chunks swizzled by row) so that each store instruction writes 8
+  // whole 128-byte row segments.
+  if constexpr (OUT == SBL_BF16) {
+    if ((d_out & 7) == 0) {
+      __syncthreads();  // every wave is done with the operand stages (no loads in flight)
+      char* stg = lds + wave * 8192;
+      const int ml = lane & 31, h = lane >> 5;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * r + ii, row = 32 * ii + ml;
+          const float sc = g127 * am[i];
+#pragma unroll
+          for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = 4 * j + q;
+              *(uint2*)(stg + row * 128 + 16 * (c ^ (row & 7)) + 8 * h) =
+                  make_uint2(cvt_pk_bf16((float)acc[i][j][4 * q] * sc, (float)acc[i][j][4 * q + 1] * sc),
+                             cvt_pk_bf16((float)acc[i][j][4 * q + 2] * sc, (float)acc[i][j][4 * q + 3] * sc));
+            }
+        }
+        const int c = lane & 7;
+        const int n = n0 + wn0 + 8 * c;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int row = 8 * u + (lane >> 3);
+          const uint4 v = *(const uint4*)(stg + row * 128 + 16 * (c ^ (row & 7)));
+          const int m = m0 + wm0 + 64 * r + row;
+          if (m < T && n < d_out) *(uint4*)((__bf16*)y + (int64_t)m * d_out + n) = v;
+        }
+      }
+      return;
+    }
+  }
+
   // Epilogue: each lane stores runs of 4 consecutive outputs of its token
   // (8 or 16 bytes); element stores only where a run leaves the matrix or
   // rows are not 4-aligned.
-  const float g127 = *gamma_p * (1.0f / 127.0f);
   const bool vec_out = (d_out & 3) == 0;
 #pragma unroll
   for (int i = 0; i < kMI; ++i) {
     const int m = m0 + wm0 + 32 * i + (lane & 31);
     if (m >= T) continue;
-    const float s = g127 * absmax[m];
+    const float s = g127 * am[i];
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) {
 #pragma unroll

@@ -5,8 +5,9 @@
 //
 // This is the plain-GEMM engine behind both products of the Dual-STE backward
 // ([SUM] 方法步骤详情 step (7)):
-//   dX = gamma * dY W_eff      A = dY [T, d_out], B = W_eff^T [d_in, d_out]
-//                              (expanded once per call into bf16 {-1, 0, +1}, exact)
+//   dX = gamma * dY W_eff      A = dY [T, d_out]; B = W_eff^T [d_in, d_out] as
+//                              2-bit codes (transposed once per call, see
+//                              BC below), widened to bf16 in registers
 //   dW = dY^T x~               A = dY^T [d_out, T], B = x~^T [d_in, T]
 //                              (both transposed once per call, token-contiguous)
 //
@@ -45,6 +46,23 @@ constexpr int kDmaA = kBM * 8 / kNT;      // 4
 constexpr int kDmaB = kBNn * 8 / kNT;     // 4
 constexpr int kDmaStep = kDmaA + kDmaB;
 constexpr int kKStep = kRowK / 2;         // 64 bf16 per K step
+constexpr int kStageBC = kBNn * 16;       // 4 KB: B as codes, 16 bytes per row and K step
+
+// B as codes (BC): row n of B holds, per K step of 64, 16 bytes = 4 words;
+// word 2 h + w serves lane half h (k groups 2 ks + h of the four 16-wide
+// slices ks) for slices 2 w and 2 w + 1.  In it, pair p = 4 (ks % 2) + q
+// (k = 16 ks + 8 h + 2 q and + 1) has the 2-bit code of its first k at bits
+// 14 - 2p, 15 - 2p and of its second at 30 - 2p, 31 - 2p, so that
+// (word << 2p) & 0xC000C000 is the bf16 pair of 2 W_eff: the high byte of
+// bf16 +2 is 0x40, of -2 is 0xC0 and of 0 is 0x00, i.e. code << 6 for the
+// codes 01 (+1), 11 (-1) and 00 (0), with a zero low byte in all three.
+// The product is therefore 2 A W_eff^T, exact, and alpha is halved.
+__device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
+  v4i r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r[q] = (int)((u << (2 * (p0 + q))) & 0xC000C000u);
+  return __builtin_bit_cast(v8bf, r);
+}
 
 // Requires K % 8 == 0 (16-byte rows, K chunks never straddle a row end).
 // blockIdx.y selects a K range [kps * y, kps * (y + 1)) (split-K); block y writes
@@ -56,13 +74,18 @@ constexpr int kKStep = kRowK / 2;         // 64 bf16 per K step
 // the dX product leaves dY^T behind for dW: every (m tile, K step) is written
 // once, by the block whose column tile index equals the step modulo the number
 // of column tiles, from the stage as soon as it has landed.
-template <int OUT, bool WTA>
+//
+// BC: B is the code layout above with rows of K64 / 4 bytes (K64 = K rounded
+// up to 64, codes past K are 00); no split-K.
+template <int OUT, bool WTA, bool BC>
 __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B, int M, int N, int K,
                                                               int kps, const float* __restrict__ alpha_p,
                                                               void* __restrict__ C, uint16_t* __restrict__ AT,
                                                               int at_ld) {
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStage];
+  constexpr int kSt = kStageA + (BC ? kStageBC : kStageB);
+  constexpr int kDmaBw = BC ? 1 : kDmaB;    // B loads per wave and step (BC: waves 0-3 only)
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kSt];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -79,13 +102,14 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   const int rows_a = min(kBM, M - m0);
   const int rows_b = min(kBNn, N - n0);
   const uint16_t* a_base = A + (int64_t)m0 * K;
-  const uint16_t* b_base = B + (int64_t)n0 * K;
+  const int64_t b_row = BC ? (int64_t)((K + 63) & ~63) / 4 : (int64_t)K * 2;  // bytes per B row
+  const char* b_base = (const char*)B + n0 * b_row;
 
   // Direct-load lanes: LDS chunk position p (16 bytes) of a stage holds row
   // p / 8, logical chunk (p % 8) ^ ((row / 2) % 8), i.e. swz8(row, c) = 16 p.
   // Wave w fills positions [64 (kDma w + i), +64) with its i-th load.
-  uint32_t a_off[kDmaA], b_off[kDmaB];
-  int a_k[kDmaA], b_k[kDmaB];
+  uint32_t a_off[kDmaA], b_off[kDmaBw];
+  int a_k[kDmaA], b_k[kDmaBw];
 #pragma unroll
   for (int i = 0; i < kDmaA; ++i) {
     const int p = 64 * (kDmaA * wave + i) + lane;
@@ -93,31 +117,40 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     a_off[i] = (uint32_t)(r * K * 2 + 16 * c);
     a_k[i] = 8 * c;
   }
+  if constexpr (BC) {
+    b_off[0] = (uint32_t)((64 * (wave & 3) + lane) * b_row);  // row 64 w + lane, one 16-byte piece
+    b_k[0] = 0;
+  } else {
 #pragma unroll
-  for (int i = 0; i < kDmaB; ++i) {
-    const int p = 64 * (kDmaB * wave + i) + lane;
-    const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-    b_off[i] = (uint32_t)(r * K * 2 + 16 * c);
-    b_k[i] = 8 * c;
+    for (int i = 0; i < kDmaB; ++i) {
+      const int p = 64 * (kDmaB * wave + i) + lane;
+      const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+      b_off[i] = (uint32_t)(r * K * 2 + 16 * c);
+      b_k[i] = 8 * c;
+    }
   }
 
   // Loads of K step kt into stage st.  The resources span the valid rows of the
   // block (rows past M or N read as zero) and the K offset rides in soffset;
   // chunks past K (last step only) are sent out of range explicitly.
   const auto ar = make_rsrc(a_base, clamp_bytes((int64_t)rows_a * K * 2));
-  const auto br = make_rsrc(b_base, clamp_bytes((int64_t)rows_b * K * 2));
+  const auto br = make_rsrc(b_base, clamp_bytes((int64_t)rows_b * b_row));
   const bool ktail = ((kend - kbeg) % kKStep) != 0;
   auto issue = [&](int kt, int st) {
     const int k0 = kbeg + kt * kKStep;
     const uint32_t soff = (uint32_t)k0 * 2;
-    char* sa = lds + st * kStage;
+    char* sa = lds + st * kSt;
     char* sb = sa + kStageA;
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i)
       dma16(ar, sa + 1024 * (kDmaA * wave + i), ktail && k0 + a_k[i] >= kend ? kOOB : a_off[i], soff);
+    if constexpr (BC) {
+      if (wave < 4) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
+    } else {
 #pragma unroll
-    for (int i = 0; i < kDmaB; ++i)
-      dma16(br, sb + 1024 * (kDmaB * wave + i), ktail && k0 + b_k[i] >= kend ? kOOB : b_off[i], soff);
+      for (int i = 0; i < kDmaB; ++i)
+        dma16(br, sb + 1024 * (kDmaB * wave + i), ktail && k0 + b_k[i] >= kend ? kOOB : b_off[i], soff);
+    }
   };
 
   v16f acc[kMI][kNJ];
@@ -128,16 +161,32 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // Fragments of K slice ks (16 of the 64 k of a step) of a stage.
+  // Fragments of K slice ks (16 of the 64 k of a step) of a stage.  BC: the
+  // code words of the whole step are read by rdc beforehand (at a point where
+  // no direct loads are in flight: the compiler makes a read of them wait for
+  // all outstanding loads) and widened per slice.
+  uint2 wb[kNJ];
+  auto rdc = [&](int st) {
+    if constexpr (BC) {
+      const char* b = lds + st * kSt + kStageA;
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j) wb[j] = *(const uint2*)(b + 16 * (wn0 + 32 * j + (lane & 31)) + 8 * (lane >> 5));
+    }
+  };
   auto rd = [&](int st, int ks, v8bf (&fa)[kMI], v8bf (&fb)[kNJ]) {
-    const char* a = lds + st * kStage;
+    const char* a = lds + st * kSt;
     const char* b = a + kStageA;
 #pragma unroll
     for (int i = 0; i < kMI; ++i)
       fa[i] = __builtin_bit_cast(v8bf, *(const v4i*)(a + swz8(wm0 + 32 * i + (lane & 31), 2 * ks + (lane >> 5))));
+    if constexpr (BC) {
 #pragma unroll
-    for (int j = 0; j < kNJ; ++j)
-      fb[j] = __builtin_bit_cast(v8bf, *(const v4i*)(b + swz8(wn0 + 32 * j + (lane & 31), 2 * ks + (lane >> 5))));
+      for (int j = 0; j < kNJ; ++j) fb[j] = widen_codes(ks < 2 ? wb[j].x : wb[j].y, 4 * (ks & 1));
+    } else {
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j)
+        fb[j] = __builtin_bit_cast(v8bf, *(const v4i*)(b + swz8(wn0 + 32 * j + (lane & 31), 2 * ks + (lane >> 5))));
+    }
   };
   // Transposed copy of the A tile of stage st (K step k0): wave w takes 16
   // K-columns (16 (w % 4) ..) and 128 rows (128 (w / 4) ..) in 4 rounds of 32;
@@ -146,7 +195,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // one 16-byte run of AT row k0 + column.
   const int gn = (N + kBNn - 1) / kBNn;
   auto write_at = [&](int st, int k0) {
-    const char* a = lds + st * kStage;
+    const char* a = lds + st * kSt;
     const int kb = 16 * (wave & 3), tb0 = 128 * (wave >> 2);
     const int g = lane >> 4, q = lane & 15;
     const auto atr = make_rsrc(AT + (int64_t)k0 * at_ld + m0, clamp_bytes((int64_t)(K - k0) * at_ld * 2 - m0 * 2));
@@ -176,9 +225,10 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       for (int j = 0; j < kNJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
+  constexpr int kRdN = BC ? kMI : kMI + kNJ;  // LDS reads of a slice
 #define ORDER_SLICE(id)                                            \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, id);              \
-  __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, id);      \
+  __builtin_amdgcn_sched_group_barrier(0x100, kRdN, id);           \
   __builtin_amdgcn_sched_group_barrier(0x008, kMI * kNJ - 1, id);
 
   // Step k (stage k % 2 has landed; slice 0 is already in fa0/fb0): each of
@@ -192,11 +242,17 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   const int last = nk - 1;
   issue(0, 0);
   issue(min(1, last), 1);
-  wait_vmcnt<kDmaStep>();
+  if constexpr (BC) {
+    if (wave < 4) wait_vmcnt<kDmaA + 1>();
+    else wait_vmcnt<kDmaA>();
+  } else {
+    wait_vmcnt<kDmaStep>();
+  }
   barrier_only();
   if constexpr (WTA) {
     if (nt == 0) write_at(0, kbeg);
   }
+  rdc(0);
   rd(0, 0, fa0, fb0);
   int sc = 0;
   for (int k = 0; k < nk; ++k) {
@@ -222,10 +278,14 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       if (k + 1 < nk && (k + 1) % gn == nt) write_at(sc ^ 1, kbeg + (k + 1) * kKStep);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (BC) {
+      rdc(sc ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     issue(min(k + 2, last), sc);
     rd(sc ^ 1, 0, fa0, fb0);
     mm(fa1, fb1);
-    __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, 3);
+    __builtin_amdgcn_sched_group_barrier(0x100, kRdN, 3);
 #pragma unroll
     for (int i = 0; i < kMI * kNJ; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
@@ -241,6 +301,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]: each lane stores runs
   // of 4 consecutive outputs of one row (16 bytes in float32, 8 in bf16).
   const float alpha = alpha_p ? *alpha_p : 1.0f;
+  constexpr float pre = BC ? 0.5f : 1.0f;  // BC: the sums are of 2 W_eff (halving is exact)
   C = (char*)C + (size_t)blockIdx.y * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
   const bool vec_out = (N & 3) == 0;
 #pragma unroll
@@ -254,8 +315,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
         const int n = n0 + wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
         if (n >= N) continue;
         const int64_t off = (int64_t)m * N + n;
-        const float v0 = acc[i][j][4 * q] * alpha, v1 = acc[i][j][4 * q + 1] * alpha;
-        const float v2 = acc[i][j][4 * q + 2] * alpha, v3 = acc[i][j][4 * q + 3] * alpha;
+        const float v0 = acc[i][j][4 * q] * pre * alpha, v1 = acc[i][j][4 * q + 1] * pre * alpha;
+        const float v2 = acc[i][j][4 * q + 2] * pre * alpha, v3 = acc[i][j][4 * q + 3] * pre * alpha;
         if (vec_out && n + 4 <= N) {
           if constexpr (OUT == SBL_F32) *(float4*)((float*)C + off) = make_float4(v0, v1, v2, v3);
           else *(uint2*)((__bf16*)C + off) = make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
@@ -289,23 +350,25 @@ hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, 
                                int64_t k_per_split, uint16_t* AT, int64_t at_ld) {
   if (splits < 1) splits = 1;
   if (splits == 1) k_per_split = K;
+  if (AT && splits != 1) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
-  if (AT) {
-    if (splits != 1) return hipErrorInvalidValue;
-    if (out_dtype == SBL_F32)
-      hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32, true>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
-                         (int)k_per_split, alpha, C, AT, (int)at_ld);
-    else
-      hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_BF16, true>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
-                         (int)k_per_split, alpha, C, AT, (int)at_ld);
-  } else {
-    if (out_dtype == SBL_F32)
-      hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32, false>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
-                         (int)k_per_split, alpha, C, nullptr, 0);
-    else
-      hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_BF16, false>), grid, block, 0, s, A, B, (int)M, (int)N, (int)K,
-                         (int)k_per_split, alpha, C, nullptr, 0);
-  }
+  const bool f32 = out_dtype == SBL_F32;
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, false> : k_gemm_nt_bf16<SBL_BF16, true, false>)
+                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, false> : k_gemm_nt_bf16<SBL_BF16, false, false>);
+  hipLaunchKernelGGL(kern, grid, block, 0, s, A, B, (int)M, (int)N, (int)K, (int)k_per_split, alpha, C, AT,
+                     (int)at_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt_codes(const uint16_t* A, const uint32_t* Bc, int64_t M, int64_t N, int64_t K,
+                                const float* alpha, void* C, int out_dtype, hipStream_t s, uint16_t* AT,
+                                int64_t at_ld) {
+  const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N)), block(kNT);
+  const bool f32 = out_dtype == SBL_F32;
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, true> : k_gemm_nt_bf16<SBL_BF16, true, true>)
+                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, true> : k_gemm_nt_bf16<SBL_BF16, false, true>);
+  hipLaunchKernelGGL(kern, grid, block, 0, s, A, (const uint16_t*)Bc, (int)M, (int)N, (int)K, (int)K, alpha, C, AT,
+                     (int)at_ld);
   return hipGetLastError();
 }
 

@@ -82,6 +82,12 @@ int64_t gemm_nt_bf16_tiles(int64_t M, int64_t N);
 hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
                                const float* alpha, void* C, int out_dtype, hipStream_t s, int splits = 1,
                                int64_t k_per_split = 0, uint16_t* AT = nullptr, int64_t at_ld = 0);
+// The same product with B = W_eff^T given as the transposed 2-bit code plane of
+// k_codes_t (gemm_bwd.hip): Bc [N, K64 / 16] words, K64 = K rounded up to 64.
+// No split-K; AT as above.
+hipError_t launch_gemm_nt_codes(const uint16_t* A, const uint32_t* Bc, int64_t M, int64_t N, int64_t K,
+                                const float* alpha, void* C, int out_dtype, hipStream_t s, uint16_t* AT = nullptr,
+                                int64_t at_ld = 0);
 
 size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flags);
 hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,

@@ -83,8 +83,10 @@ def test_forward_validation():
 
 def test_backward_validation():
     f = lib.sbl_backward
-    # dX: the bf16 transpose of W_eff (d_out % 8 == 0), else no workspace
-    assert lib.sbl_backward_workspace_size(64, 256, 256, 1) == 2 * 256 * 256
+    # dX: the transposed 2-bit code plane (d_in rows of d_out rounded up to 64,
+    # 2 bits each) when d_out % 8 == 0, else no workspace
+    assert lib.sbl_backward_workspace_size(64, 256, 256, 1) == 256 * 256 // 4
+    assert lib.sbl_backward_workspace_size(64, 256, 264, 1) == 256 * 320 // 4
     assert lib.sbl_backward_workspace_size(64, 256, 252, 1) == 0
     assert lib.sbl_backward_workspace_size(0, 256, 256, 1) == 0
     assert f(P, P, P, P, P, 4, 256, 256, P, 1, P, 1, NULL, 0, NULL) == WORKSPACE
