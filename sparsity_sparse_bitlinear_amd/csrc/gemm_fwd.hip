@@ -263,6 +263,12 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
     for (int i = 0; i < kFDmaA; ++i) dma16(ar, sa + 1024 * (kFDmaA * wave + i), a_off[i], (uint32_t)kt * kFK);
     dma16(br, sa + kFStageA + 1024 * wave, b_off, (uint32_t)kt * (kFK / 4));
   };
+  // Load idx (0 .. kFDmaA) of the wave's loads of step kt into stage st.
+  auto issue_one = [&](int kt, int st, int idx) {
+    char* sa = lds + st * kFStage;
+    if (idx < kFDmaA) dma16(ar, sa + 1024 * (kFDmaA * wave + idx), a_off[idx], (uint32_t)kt * kFK);
+    else dma16(br, sa + kFStageA + 1024 * wave, b_off, (uint32_t)kt * (kFK / 4));
+  };
 
   // Output scales of this lane's rows, fetched before the K loop so the
   // epilogue does not wait on them.
@@ -302,6 +308,9 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
 #pragma unroll
       for (int j = 0; j < kNJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[j], fa[i], acc[i][j], 0, 0, 0);
+  };
+  auto mm_one = [&](int t, const v4i (&fa)[kMI], const v4i (&fb)[kNJ]) {
+    acc[t / kNJ][t % kNJ] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[t % kNJ], fa[t / kNJ], acc[t / kNJ][t % kNJ], 0, 0, 0);
   };
   auto expand = [&](const uint32_t (&wb)[kNJ], v4i (&fb)[kNJ]) {
 #pragma unroll
@@ -353,49 +362,72 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
     wait_vmcnt_lgkm0<0>();
     barrier_only();
     __builtin_amdgcn_sched_barrier(0);
-    issue(min(k + 2, last), sc);
+    // Slice 3 (its fragments are in registers) restarts the matrix pipe right
+    // after the barrier; the reads of slice 0 of step k + 1, the loads of step
+    // k + 2 (one after each instruction) and the widening of the new code
+    // words go between its instructions.
+    const int kn = min(k + 2, last);
+    mm_one(0, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
     rd(sc ^ 1, 0, fa0, wb0);
-    mm(fa1, fb1);
-    expand(wb0, fb0);
-    SBL_FWD_SLICE_ORDER(3)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 1; t < kMI * kNJ; ++t) {
+      mm_one(t, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t - 1 <= kFDmaA) issue_one(kn, sc, t - 1);
+      if (t >= kMI * kNJ - kNJ) fb0[t - (kMI * kNJ - kNJ)] = __builtin_bit_cast(v4i, expand16(wb0[t - (kMI * kNJ - kNJ)]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
     sc ^= 1;
   }
 #undef SBL_FWD_SLICE_ORDER
   wait_vmcnt<0>();
 
-  // bf16 output with 16-byte aligned rows: the wave's 128 x 64 result goes
-  // through LDS in two rounds of 64 rows (8 KB per wave, rows of 128 bytes,
-  // 16-byte chunks swizzled by row) so that each store instruction writes 8
-  // whole 128-byte row segments.
-  if constexpr (OUT == SBL_BF16) {
-    if ((d_out & 7) == 0) {
+  // bf16 or float32 output with 16-byte aligned rows: the wave's 128 x 64
+  // result goes through LDS, 8 KB per wave and round (64 rows of 128 bytes in
+  // bf16, 32 rows of 256 bytes in float32; 16-byte chunks swizzled by row), so
+  // that each store instruction writes whole row segments of the wave's 64
+  // columns.
+  if constexpr (OUT == SBL_BF16 || OUT == SBL_F32) {
+    if ((d_out & (OUT == SBL_F32 ? 3 : 7)) == 0) {
       __syncthreads();  // every wave is done with the operand stages (no loads in flight)
       char* stg = lds + wave * 8192;
       const int ml = lane & 31, h = lane >> 5;
+      constexpr int kRB = OUT == SBL_F32 ? 256 : 128;   // bytes per staged row
+      constexpr int kCh = kRB / 16;                     // 16-byte chunks per row
+      constexpr int kIR = 8192 / kRB / 32;              // 32-row blocks per round
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < kMI / kIR; ++r) {
 #pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int i = 2 * r + ii, row = 32 * ii + ml;
+        for (int ii = 0; ii < kIR; ++ii) {
+          const int i = kIR * r + ii, row = 32 * ii + ml;
           const float sc = g127 * am[i];
 #pragma unroll
           for (int j = 0; j < kNJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const int c = 4 * j + q;
-              *(uint2*)(stg + row * 128 + 16 * (c ^ (row & 7)) + 8 * h) =
-                  make_uint2(cvt_pk_bf16((float)acc[i][j][4 * q] * sc, (float)acc[i][j][4 * q + 1] * sc),
-                             cvt_pk_bf16((float)acc[i][j][4 * q + 2] * sc, (float)acc[i][j][4 * q + 3] * sc));
+              const float v0 = (float)acc[i][j][4 * q] * sc, v1 = (float)acc[i][j][4 * q + 1] * sc;
+              const float v2 = (float)acc[i][j][4 * q + 2] * sc, v3 = (float)acc[i][j][4 * q + 3] * sc;
+              if constexpr (OUT == SBL_F32) {
+                const int c = 8 * j + 2 * q + h;
+                *(float4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1)))) = make_float4(v0, v1, v2, v3);
+              } else {
+                const int c = 4 * j + q;
+                *(uint2*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))) + 8 * h) =
+                    make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
+              }
             }
         }
-        const int c = lane & 7;
-        const int n = n0 + wn0 + 8 * c;
+        const int c = lane & (kCh - 1);
+        const int n = n0 + wn0 + c * (OUT == SBL_F32 ? 4 : 8);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int row = 8 * u + (lane >> 3);
-          const uint4 v = *(const uint4*)(stg + row * 128 + 16 * (c ^ (row & 7)));
-          const int m = m0 + wm0 + 64 * r + row;
-          if (m < T && n < d_out) *(uint4*)((__bf16*)y + (int64_t)m * d_out + n) = v;
+        for (int u = 0; u < 32 * kIR * kCh / 64; ++u) {
+          const int row = (64 / kCh) * u + lane / kCh;
+          const uint4 v = *(const uint4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))));
+          const int m = m0 + wm0 + 32 * kIR * r + row;
+          if (m < T && n < d_out)
+            *(uint4*)((char*)y + ((int64_t)m * d_out + n) * (OUT == SBL_F32 ? 4 : 2)) = v;
         }
       }
       return;

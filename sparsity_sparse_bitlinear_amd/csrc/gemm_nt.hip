@@ -153,6 +153,25 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     }
   };
 
+  const float alpha = alpha_p ? *alpha_p : 1.0f;  // fetched before the K loop
+
+  // One load (index idx of the wave's loads of a step) of K step kt into stage st.
+  constexpr int kNDma = BC ? kDmaA + 1 : kDmaStep;
+  auto issue_one = [&](int kt, int st, int idx) {
+    const int k0 = kbeg + kt * kKStep;
+    const uint32_t soff = (uint32_t)k0 * 2;
+    char* sa = lds + st * kSt;
+    char* sb = sa + kStageA;
+    if (idx < kDmaA) {
+      dma16(ar, sa + 1024 * (kDmaA * wave + idx), ktail && k0 + a_k[idx] >= kend ? kOOB : a_off[idx], soff);
+    } else if constexpr (BC) {
+      if (wave < 4) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
+    } else {
+      const int i = idx - kDmaA;
+      dma16(br, sb + 1024 * (kDmaB * wave + i), ktail && k0 + b_k[i] >= kend ? kOOB : b_off[i], soff);
+    }
+  };
+
   v16f acc[kMI][kNJ];
 #pragma unroll
   for (int i = 0; i < kMI; ++i)
@@ -218,6 +237,10 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     }
   };
 
+  auto mm_one = [&](int t, const v8bf (&fa)[kMI], const v8bf (&fb)[kNJ]) {
+    acc[t / kNJ][t % kNJ] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[t % kNJ], fa[t / kNJ], acc[t / kNJ][t % kNJ],
+                                                                    0, 0, 0);
+  };
   auto mm = [&](const v8bf (&fa)[kMI], const v8bf (&fb)[kNJ]) {
 #pragma unroll
     for (int i = 0; i < kMI; ++i)
@@ -282,15 +305,23 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       rdc(sc ^ 1);
       __builtin_amdgcn_sched_barrier(0);
     }
-    issue(min(k + 2, last), sc);
+    // Slice 3 (its fragments are in registers) restarts the matrix pipe right
+    // after the barrier; the reads of slice 0 of step k + 1 and the loads of
+    // step k + 2 go between its instructions, one load after each.
+    const int kn = min(k + 2, last);
+    mm_one(0, fa1, fb1);
+    __builtin_amdgcn_sched_barrier(0);
     rd(sc ^ 1, 0, fa0, fb0);
-    mm(fa1, fb1);
-    __builtin_amdgcn_sched_group_barrier(0x100, kRdN, 3);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < kMI * kNJ; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 3);
+    for (int t = 0; t < kMI * kNJ; ++t) {
+      if (t > 0) mm_one(t, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t < kNDma) issue_one(kn, sc, t);
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int t = kMI * kNJ; t < kNDma; ++t) issue_one(kn, sc, t);
     __builtin_amdgcn_sched_barrier(0);
     sc ^= 1;
   }
@@ -300,9 +331,54 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // B is the MFMA's first operand, so accumulator register r of lane l holds
   // C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]: each lane stores runs
   // of 4 consecutive outputs of one row (16 bytes in float32, 8 in bf16).
-  const float alpha = alpha_p ? *alpha_p : 1.0f;
   constexpr float pre = BC ? 0.5f : 1.0f;  // BC: the sums are of 2 W_eff (halving is exact)
   C = (char*)C + (size_t)blockIdx.y * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
+
+  // With 16-byte aligned output rows the wave's 128 x 64 result goes through
+  // LDS, 8 KB per wave and round (64 rows of 128 bytes in bf16, 32 rows of 256
+  // bytes in float32; 16-byte chunks swizzled by row), so that every store
+  // instruction writes whole row segments of the wave's 64 columns.
+  if ((N & (OUT == SBL_F32 ? 3 : 7)) == 0) {
+    __syncthreads();  // every wave is done with the operand stages (no loads in flight)
+    char* stg = lds + wave * 8192;
+    const int ml = lane & 31, h = lane >> 5;
+    constexpr int kRB = OUT == SBL_F32 ? 256 : 128;   // bytes per staged row
+    constexpr int kCh = kRB / 16;                     // 16-byte chunks per row
+    constexpr int kIR = 8192 / kRB / 32;              // 32-row blocks per round
+#pragma unroll
+    for (int r = 0; r < kMI / kIR; ++r) {
+#pragma unroll
+      for (int ii = 0; ii < kIR; ++ii) {
+        const int i = kIR * r + ii, row = 32 * ii + ml;
+#pragma unroll
+        for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float v0 = acc[i][j][4 * q] * pre * alpha, v1 = acc[i][j][4 * q + 1] * pre * alpha;
+            const float v2 = acc[i][j][4 * q + 2] * pre * alpha, v3 = acc[i][j][4 * q + 3] * pre * alpha;
+            if constexpr (OUT == SBL_F32) {
+              const int c = 8 * j + 2 * q + h;
+              *(float4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1)))) = make_float4(v0, v1, v2, v3);
+            } else {
+              const int c = 4 * j + q;
+              *(uint2*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))) + 8 * h) =
+                  make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
+            }
+          }
+      }
+      const int c = lane & (kCh - 1);
+      const int n = n0 + wn0 + c * (OUT == SBL_F32 ? 4 : 8);
+#pragma unroll
+      for (int u = 0; u < 32 * kIR * kCh / 64; ++u) {
+        const int row = (64 / kCh) * u + lane / kCh;
+        const uint4 v = *(const uint4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))));
+        const int m = m0 + wm0 + 32 * kIR * r + row;
+        if (m < M && n < N)
+          *(uint4*)((char*)C + ((int64_t)m * N + n) * (OUT == SBL_F32 ? 4 : 2)) = v;
+      }
+    }
+    return;
+  }
   const bool vec_out = (N & 3) == 0;
 #pragma unroll
   for (int i = 0; i < kMI; ++i) {
