@@ -14,6 +14,9 @@
 // Block tile 256 tokens x 128 outputs, K step 64 bytes.  Global loads are
 // buffer loads through a per-tile resource, so rows past the matrix end read
 // as zero; they run two K steps ahead of the matrix work.
+#include <atomic>
+#include <algorithm>
+
 #include "gemm_common.h"
 
 namespace sbl {
@@ -224,22 +227,38 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
                                                          const float* __restrict__ gamma_p,
                                                          const float* __restrict__ absmax, int T, int d_in,
                                                          int d_out, void* __restrict__ y) {
-  __shared__ __attribute__((aligned(1024))) char lds[kFS * kFStage];
+  // Operand stages, then a separate staging area for the output tile (8 KB per
+  // wave), so that a tile's epilogue runs while the next tile's first two K
+  // steps land in the stages.
+  __shared__ __attribute__((aligned(1024))) char lds[kFS * kFStage + kFT / 64 * 8192];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave >> 2) * kWM;
   const int wn0 = (wave & 3) * kWN;
-  int mt, nt;
-  xcd_tile_grouped(blockIdx.x, (T + kBM - 1) / kBM, (d_out + kFBN - 1) / kFBN, 4, mt, nt);
-  const int m0 = mt * kBM;
-  const int n0 = nt * kFBN;
+  const int mtn = (T + kBM - 1) / kBM, ntn = (d_out + kFBN - 1) / kFBN;
+  const int ntiles = mtn * ntn;
   const int G = d_in >> 3;
   const int nk = d_in / kFK;
-  const int rows_a = min(kBM, T - m0);
-  const int rows_b = min(kFBN, d_out - n0);
-  const auto ar = make_rsrc(xq + (int64_t)m0 * d_in, clamp_bytes((int64_t)rows_a * d_in));
-  const auto br = make_rsrc(codes + (int64_t)n0 * G, clamp_bytes((int64_t)rows_b * G * 2));
+
+  // Tiles blockIdx.x, + gridDim.x, ... in turn (the host launches one block per
+  // tile, or, with nk >= 2, at most one per CU).  XCD-aware order as for a
+  // grid of one block per tile, since gridDim.x is a multiple of the XCD count
+  // whenever a block takes more than one tile.
+  struct Tile {
+    int m0, n0;
+    __amdgpu_buffer_rsrc_t ar, br;
+  };
+  auto tile_at = [&](int t) {
+    Tile r;
+    int mt, nt;
+    xcd_tile_grouped(t, mtn, ntn, 4, mt, nt);
+    r.m0 = mt * kBM;
+    r.n0 = nt * kFBN;
+    r.ar = make_rsrc(xq + (int64_t)r.m0 * d_in, clamp_bytes((int64_t)min(kBM, T - r.m0) * d_in));
+    r.br = make_rsrc(codes + (int64_t)r.n0 * G, clamp_bytes((int64_t)min(kFBN, d_out - r.n0) * G * 2));
+    return r;
+  };
 
   // x_q tile: LDS chunk position p holds row p / 8, logical chunk (p % 8) ^ ((row / 2) % 8)
   uint32_t a_off[kFDmaA];
@@ -257,36 +276,29 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
     b_off = (uint32_t)(r * G * 2 + 16 * h);
   }
 
-  auto issue = [&](int kt, int st) {
+  // Load idx (0 .. kFDmaA) of the wave's loads of K step kt of tile tl into stage st.
+  auto issue_one = [&](const Tile& tl, int kt, int st, int idx) {
     char* sa = lds + st * kFStage;
-#pragma unroll
-    for (int i = 0; i < kFDmaA; ++i) dma16(ar, sa + 1024 * (kFDmaA * wave + i), a_off[i], (uint32_t)kt * kFK);
-    dma16(br, sa + kFStageA + 1024 * wave, b_off, (uint32_t)kt * (kFK / 4));
+    if (idx < kFDmaA) dma16(tl.ar, sa + 1024 * (kFDmaA * wave + idx), a_off[idx], (uint32_t)kt * kFK);
+    else dma16(tl.br, sa + kFStageA + 1024 * wave, b_off, (uint32_t)kt * (kFK / 4));
   };
-  // Load idx (0 .. kFDmaA) of the wave's loads of step kt into stage st.
-  auto issue_one = [&](int kt, int st, int idx) {
-    char* sa = lds + st * kFStage;
-    if (idx < kFDmaA) dma16(ar, sa + 1024 * (kFDmaA * wave + idx), a_off[idx], (uint32_t)kt * kFK);
-    else dma16(br, sa + kFStageA + 1024 * wave, b_off, (uint32_t)kt * (kFK / 4));
+  auto issue = [&](const Tile& tl, int kt, int st) {
+#pragma unroll
+    for (int i = 0; i <= kFDmaA; ++i) issue_one(tl, kt, st, i);
   };
 
-  // Output scales of this lane's rows, fetched before the K loop so the
-  // epilogue does not wait on them.
-  float am[kMI];
-#pragma unroll
-  for (int i = 0; i < kMI; ++i) {
-    const int m = m0 + wm0 + 32 * i + (lane & 31);
-    am[i] = m < T ? absmax[m] : 0.0f;
-  }
   const float g127 = *gamma_p * (1.0f / 127.0f);
+  // Output scales of this lane's rows, fetched a K loop ahead of the epilogue.
+  float am[kMI];
+  auto load_scales = [&](int m0) {
+#pragma unroll
+    for (int i = 0; i < kMI; ++i) {
+      const int m = m0 + wm0 + 32 * i + (lane & 31);
+      am[i] = m < T ? absmax[m] : 0.0f;
+    }
+  };
 
   v16i acc[kMI][kNJ];
-#pragma unroll
-  for (int i = 0; i < kMI; ++i)
-#pragma unroll
-    for (int j = 0; j < kNJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
   // K slice ks (32 of the 128 k of a step): A fragments, and the code word
   // (groups 4 ks + 2 (l / 32), +1) of output row wn0 + 32 j + l % 32.
@@ -330,150 +342,187 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
   __builtin_amdgcn_sched_group_barrier(0x008, 1, id);           \
   __builtin_amdgcn_sched_barrier(0);
 
-  // Step k (stage k % 2 has landed; slice 0 is read and expanded): each of the
-  // 4 slices is read and its code words expanded while the previous slice is
-  // multiplied.  Before the last slice: wait for this wave's loads of step
-  // k + 1 and its reads of stage k, barrier, refill stage k % 2 with step
-  // k + 2, then read slice 0 of step k + 1 while multiplying slice 3.  Past the
-  // last step the load index is clamped (redundant loads, never read).
+  // The K steps of all tiles of the block form one sequence with stage parity
+  // running on across tiles.  Step k (its stage has landed): each of the 4
+  // slices is read and its code words expanded while the previous slice is
+  // multiplied.  Before the last slice: wait for this wave's loads of the
+  // next step (of this tile, or the next tile's first) and its reads of this
+  // stage, barrier, then refill this stage with the step after next (again
+  // possibly the next tile's), its loads placed between the last slice's
+  // matrix instructions.  A tile's epilogue follows its last step; the next
+  // tile starts by reading its slice 0.
   v4i fa0[kMI], fa1[kMI], fb0[kNJ], fb1[kNJ];
   uint32_t wb0[kNJ], wb1[kNJ];
-  const int last = nk - 1;
-  issue(0, 0);
-  issue(min(1, last), 1);
-  wait_vmcnt<kFDmaStep>();
-  barrier_only();
-  rd(0, 0, fa0, wb0);
-  expand(wb0, fb0);
-  int sc = 0;
-  for (int k = 0; k < nk; ++k) {
-    rd(sc, 1, fa1, wb1);
-    mm(fa0, fb0);
-    expand(wb1, fb1);
-    SBL_FWD_SLICE_ORDER(0)
-    rd(sc, 2, fa0, wb0);
-    mm(fa1, fb1);
-    expand(wb0, fb0);
-    SBL_FWD_SLICE_ORDER(1)
-    rd(sc, 3, fa1, wb1);
-    mm(fa0, fb0);
-    expand(wb1, fb1);
-    SBL_FWD_SLICE_ORDER(2)
-    wait_vmcnt_lgkm0<0>();
-    barrier_only();
-    __builtin_amdgcn_sched_barrier(0);
-    // Slice 3 (its fragments are in registers) restarts the matrix pipe right
-    // after the barrier; the reads of slice 0 of step k + 1, the loads of step
-    // k + 2 (one after each instruction) and the widening of the new code
-    // words go between its instructions.
-    const int kn = min(k + 2, last);
-    mm_one(0, fa1, fb1);
-    __builtin_amdgcn_sched_barrier(0);
-    rd(sc ^ 1, 0, fa0, wb0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 1; t < kMI * kNJ; ++t) {
-      mm_one(t, fa1, fb1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (t - 1 <= kFDmaA) issue_one(kn, sc, t - 1);
-      if (t >= kMI * kNJ - kNJ) fb0[t - (kMI * kNJ - kNJ)] = __builtin_bit_cast(v4i, expand16(wb0[t - (kMI * kNJ - kNJ)]));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    sc ^= 1;
+  int t = blockIdx.x;
+  Tile cur = tile_at(t);
+  load_scales(cur.m0);
+  Tile nxt = cur;
+  bool has_next = t + (int)gridDim.x < ntiles;
+  if (has_next) nxt = tile_at(t + gridDim.x);
+  issue(cur, 0, 0);
+  if (nk > 1) {
+    issue(cur, 1, 1);
+    wait_vmcnt<kFDmaStep>();
+  } else {
+    if (has_next) issue(nxt, 0, 1);
+    wait_vmcnt<0>();
   }
-#undef SBL_FWD_SLICE_ORDER
-  wait_vmcnt<0>();
+  barrier_only();
+  int sc = 0;
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < kMI; ++i)
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    rd(sc, 0, fa0, wb0);
+    expand(wb0, fb0);
+    for (int k = 0; k < nk; ++k) {
+      rd(sc, 1, fa1, wb1);
+      mm(fa0, fb0);
+      expand(wb1, fb1);
+      SBL_FWD_SLICE_ORDER(0)
+      rd(sc, 2, fa0, wb0);
+      mm(fa1, fb1);
+      expand(wb0, fb0);
+      SBL_FWD_SLICE_ORDER(1)
+      rd(sc, 3, fa1, wb1);
+      mm(fa0, fb0);
+      expand(wb1, fb1);
+      SBL_FWD_SLICE_ORDER(2)
+      wait_vmcnt_lgkm0<0>();
+      barrier_only();
+      __builtin_amdgcn_sched_barrier(0);
+      // the step after next: of this tile, or the next tile's (nk >= 2 when a
+      // block takes more than one tile), or none
+      const bool in_tile = k + 2 < nk;
+      const bool load = in_tile || (has_next && k + 2 - nk < nk);
+      const Tile& lt = in_tile ? cur : nxt;
+      const int kn = in_tile ? k + 2 : k + 2 - nk;
+      mm_one(0, fa1, fb1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (k + 1 < nk) rd(sc ^ 1, 0, fa0, wb0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 1; u < kMI * kNJ; ++u) {
+        mm_one(u, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u - 1 <= kFDmaA && load) issue_one(lt, kn, sc, u - 1);
+        if (u >= kMI * kNJ - kNJ && k + 1 < nk)
+          fb0[u - (kMI * kNJ - kNJ)] = __builtin_bit_cast(v4i, expand16(wb0[u - (kMI * kNJ - kNJ)]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sc ^= 1;
+    }
 
-  // bf16 or float32 output with 16-byte aligned rows: the wave's 128 x 64
-  // result goes through LDS, 8 KB per wave and round (64 rows of 128 bytes in
-  // bf16, 32 rows of 256 bytes in float32; 16-byte chunks swizzled by row), so
-  // that each store instruction writes whole row segments of the wave's 64
-  // columns.
-  if constexpr (OUT == SBL_BF16 || OUT == SBL_F32) {
-    if ((d_out & (OUT == SBL_F32 ? 3 : 7)) == 0) {
-      __syncthreads();  // every wave is done with the operand stages (no loads in flight)
-      char* stg = lds + wave * 8192;
-      const int ml = lane & 31, h = lane >> 5;
-      constexpr int kRB = OUT == SBL_F32 ? 256 : 128;   // bytes per staged row
-      constexpr int kCh = kRB / 16;                     // 16-byte chunks per row
-      constexpr int kIR = 8192 / kRB / 32;              // 32-row blocks per round
+    // Epilogue of tile cur.
+    const int m0 = cur.m0, n0 = cur.n0;
+    float scl[kMI];
 #pragma unroll
-      for (int r = 0; r < kMI / kIR; ++r) {
+    for (int i = 0; i < kMI; ++i) scl[i] = g127 * am[i];
+    // bf16 or float32 output with 16-byte aligned rows: the wave's 128 x 64
+    // result goes through its staging area in rounds of 8 KB (64 rows of 128
+    // bytes in bf16, 32 rows of 256 bytes in float32; 16-byte chunks swizzled
+    // by row), so that each store instruction writes whole row segments of
+    // the wave's 64 columns.
+    bool staged = false;
+    if constexpr (OUT == SBL_BF16 || OUT == SBL_F32) {
+      if ((d_out & (OUT == SBL_F32 ? 3 : 7)) == 0) {
+        staged = true;
+        char* stg = lds + kFS * kFStage + wave * 8192;
+        const int ml = lane & 31, h = lane >> 5;
+        constexpr int kRB = OUT == SBL_F32 ? 256 : 128;   // bytes per staged row
+        constexpr int kCh = kRB / 16;                     // 16-byte chunks per row
+        constexpr int kIR = 8192 / kRB / 32;              // 32-row blocks per round
 #pragma unroll
-        for (int ii = 0; ii < kIR; ++ii) {
-          const int i = kIR * r + ii, row = 32 * ii + ml;
-          const float sc = g127 * am[i];
+        for (int r = 0; r < kMI / kIR; ++r) {
 #pragma unroll
-          for (int j = 0; j < kNJ; ++j)
+          for (int ii = 0; ii < kIR; ++ii) {
+            const int i = kIR * r + ii, row = 32 * ii + ml;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float v0 = (float)acc[i][j][4 * q] * sc, v1 = (float)acc[i][j][4 * q + 1] * sc;
-              const float v2 = (float)acc[i][j][4 * q + 2] * sc, v3 = (float)acc[i][j][4 * q + 3] * sc;
-              if constexpr (OUT == SBL_F32) {
-                const int c = 8 * j + 2 * q + h;
-                *(float4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1)))) = make_float4(v0, v1, v2, v3);
+            for (int j = 0; j < kNJ; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float v0 = (float)acc[i][j][4 * q] * scl[i], v1 = (float)acc[i][j][4 * q + 1] * scl[i];
+                const float v2 = (float)acc[i][j][4 * q + 2] * scl[i], v3 = (float)acc[i][j][4 * q + 3] * scl[i];
+                if constexpr (OUT == SBL_F32) {
+                  const int c = 8 * j + 2 * q + h;
+                  *(float4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1)))) = make_float4(v0, v1, v2, v3);
+                } else {
+                  const int c = 4 * j + q;
+                  *(uint2*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))) + 8 * h) =
+                      make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
+                }
+              }
+          }
+          const int c = lane & (kCh - 1);
+          const int n = n0 + wn0 + c * (OUT == SBL_F32 ? 4 : 8);
+#pragma unroll
+          for (int u = 0; u < 32 * kIR * kCh / 64; ++u) {
+            const int row = (64 / kCh) * u + lane / kCh;
+            const uint4 v = *(const uint4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))));
+            const int m = m0 + wm0 + 32 * kIR * r + row;
+            if (m < T && n < d_out)
+              *(uint4*)((char*)y + ((int64_t)m * d_out + n) * (OUT == SBL_F32 ? 4 : 2)) = v;
+          }
+        }
+      }
+    }
+    if (!staged) {
+      // each lane stores runs of 4 consecutive outputs of its token (8 or 16
+      // bytes); element stores only where a run leaves the matrix or rows are
+      // not 4-aligned
+      const bool vec_out = (d_out & 3) == 0;
+#pragma unroll
+      for (int i = 0; i < kMI; ++i) {
+        const int m = m0 + wm0 + 32 * i + (lane & 31);
+        if (m >= T) continue;
+        const float sv = scl[i];
+#pragma unroll
+        for (int j = 0; j < kNJ; ++j) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = n0 + wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
+            if (n >= d_out) continue;
+            const int64_t off = (int64_t)m * d_out + n;
+            const int a0 = acc[i][j][4 * q], a1 = acc[i][j][4 * q + 1], a2 = acc[i][j][4 * q + 2],
+                      a3 = acc[i][j][4 * q + 3];
+            if (vec_out && n + 4 <= d_out) {
+              if constexpr (OUT == SBL_I32) {
+                *(int4*)((int*)y + off) = make_int4(a0, a1, a2, a3);
+              } else if constexpr (OUT == SBL_F32) {
+                *(float4*)((float*)y + off) =
+                    make_float4((float)a0 * sv, (float)a1 * sv, (float)a2 * sv, (float)a3 * sv);
               } else {
-                const int c = 4 * j + q;
-                *(uint2*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))) + 8 * h) =
-                    make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
+                *(uint2*)((__bf16*)y + off) = make_uint2(cvt_pk_bf16((float)a0 * sv, (float)a1 * sv),
+                                                         cvt_pk_bf16((float)a2 * sv, (float)a3 * sv));
+              }
+            } else {
+              const int av[4] = {a0, a1, a2, a3};
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                if (n + u >= d_out) break;
+                if constexpr (OUT == SBL_I32) ((int*)y)[off + u] = av[u];
+                else if constexpr (OUT == SBL_F32) ((float*)y)[off + u] = (float)av[u] * sv;
+                else ((__bf16*)y)[off + u] = (__bf16)((float)av[u] * sv);
               }
             }
-        }
-        const int c = lane & (kCh - 1);
-        const int n = n0 + wn0 + c * (OUT == SBL_F32 ? 4 : 8);
-#pragma unroll
-        for (int u = 0; u < 32 * kIR * kCh / 64; ++u) {
-          const int row = (64 / kCh) * u + lane / kCh;
-          const uint4 v = *(const uint4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))));
-          const int m = m0 + wm0 + 32 * kIR * r + row;
-          if (m < T && n < d_out)
-            *(uint4*)((char*)y + ((int64_t)m * d_out + n) * (OUT == SBL_F32 ? 4 : 2)) = v;
+          }
         }
       }
-      return;
     }
-  }
 
-  // Epilogue: each lane stores runs of 4 consecutive outputs of its token
-  // (8 or 16 bytes); element stores only where a run leaves the matrix or
-  // rows are not 4-aligned.
-  const bool vec_out = (d_out & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < kMI; ++i) {
-    const int m = m0 + wm0 + 32 * i + (lane & 31);
-    if (m >= T) continue;
-    const float s = g127 * am[i];
-#pragma unroll
-    for (int j = 0; j < kNJ; ++j) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn0 + 32 * j + 8 * q + 4 * (lane >> 5);
-        if (n >= d_out) continue;
-        const int64_t off = (int64_t)m * d_out + n;
-        const int a0 = acc[i][j][4 * q], a1 = acc[i][j][4 * q + 1], a2 = acc[i][j][4 * q + 2],
-                  a3 = acc[i][j][4 * q + 3];
-        if (vec_out && n + 4 <= d_out) {
-          if constexpr (OUT == SBL_I32) {
-            *(int4*)((int*)y + off) = make_int4(a0, a1, a2, a3);
-          } else if constexpr (OUT == SBL_F32) {
-            *(float4*)((float*)y + off) = make_float4((float)a0 * s, (float)a1 * s, (float)a2 * s, (float)a3 * s);
-          } else {
-            *(uint2*)((__bf16*)y + off) =
-                make_uint2(cvt_pk_bf16((float)a0 * s, (float)a1 * s), cvt_pk_bf16((float)a2 * s, (float)a3 * s));
-          }
-        } else {
-          const int av[4] = {a0, a1, a2, a3};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            if (n + u >= d_out) break;
-            if constexpr (OUT == SBL_I32) ((int*)y)[off + u] = av[u];
-            else if constexpr (OUT == SBL_F32) ((float*)y)[off + u] = (float)av[u] * s;
-            else ((__bf16*)y)[off + u] = (__bf16)((float)av[u] * s);
-          }
-        }
-      }
-    }
+    if (!has_next) break;
+    t += gridDim.x;
+    cur = nxt;
+    load_scales(cur.m0);
+    has_next = t + (int)gridDim.x < ntiles;
+    if (has_next) nxt = tile_at(t + gridDim.x);
   }
+#undef SBL_FWD_SLICE_ORDER
+  // No direct loads may still target LDS when the block retires.
+  wait_vmcnt<0>();
 }
 
 // ---------------------------------------------------------------------------
@@ -628,6 +677,18 @@ hipError_t launch_fwd_v(const uint16_t* codes, const float* gamma, const int8_t*
 
 }  // namespace
 
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
@@ -636,8 +697,12 @@ hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_
     return launch_decode<4>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
   }
   if (d_in % kFK == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes) {
+    // One block per tile, or with two or more K steps per tile at most one
+    // block per CU (a multiple of 8, the XCD count), each walking its tiles.
     const int64_t nb = ((d_out + kFBN - 1) / kFBN) * ((T + kBM - 1) / kBM);
-    const dim3 grid((unsigned)nb), block(kFT);
+    const int64_t cus = std::max(8, device_cus() / 8 * 8);
+    const int64_t nblocks = d_in / kFK >= 2 && nb > cus ? cus : nb;
+    const dim3 grid((unsigned)nblocks), block(kFT);
     switch (y_dtype) {
       case SBL_F32:
         hipLaunchKernelGGL((k_fwd_i8_direct<SBL_F32>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T, (int)d_in,

@@ -67,6 +67,9 @@ __host__ __device__ float round_mean_words(const uint32_t* w, int nwords, unsign
 // ---------------------------------------------------------------------------
 hipError_t launch_act_quant(const uint16_t* x, int64_t T, int64_t d_in, int8_t* xq, float* absmax, hipStream_t s);
 
+// Compute units of the current device (cached per device).
+int device_cus();
+
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s);
 

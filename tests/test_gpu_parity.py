@@ -169,6 +169,27 @@ def test_forward_large_tiles_sampled():
     assert_y_close(y, y_ref, acc_ref)
 
 
+@pytest.mark.parametrize("d_in", [256, 384])
+def test_forward_several_tiles_per_block(d_in):
+    # 17 x 17 = 289 tiles of 256 x 256 (more than one per CU, ragged in both
+    # directions) with 2 or 3 K steps each: blocks walk several tiles and load
+    # the next tile's first steps during the current one.  Rows from every row
+    # tile (its first, last and a middle one), all outputs, exact int32, and
+    # the bf16 output within one rounding.
+    T, d_out = 4100, 4100
+    W = weight(43, d_in, d_out, d_in)
+    x = activation(43, d_out, T, d_in, dist="student_t4")
+    rows = np.unique(np.concatenate([np.arange(0, T, 256), np.arange(255, T, 256), np.arange(100, T, 256), [T - 1]]))
+    idx = torch.from_numpy(rows).cuda()
+    acc_ref, y_ref = ref_forward(W, x, 6, rows)
+    acc = gpu_forward(W, x, 6, sbl.I32)[idx].cpu().numpy()
+    np.testing.assert_array_equal(acc, acc_ref)
+    yb = gpu_forward(W, x, 6, sbl.BF16)[idx].float().cpu().numpy()
+    assert np.all(np.abs(yb - y_ref) <= 2.0 ** -8 * np.abs(y_ref) + 1e-30)
+    y = gpu_forward(W, x, 6, sbl.F32)[idx].cpu().numpy()
+    assert_y_close(y, y_ref, acc_ref)
+
+
 # Decode (T <= 64): the streaming kernel, every mask, ragged row counts.
 DECODE_T = [1, 5, 8, 16, 17, 33, 64]
 
