@@ -226,9 +226,23 @@ __global__ __launch_bounds__(256) void k_codes_t(const uint16_t* __restrict__ co
   const int i0 = blockIdx.x * kCtI, o0 = blockIdx.y * kCtO;
   const int g0 = i0 >> 3;
   const int tid = threadIdx.x;
-  for (int e = tid; e < kCtO * (kCtI / 8); e += 256) {
-    const int r = e / (kCtI / 8), g = e % (kCtI / 8);
-    tile[g][r] = (o0 + r < d_out && g0 + g < G) ? codes[(int64_t)(o0 + r) * G + g0 + g] : (uint16_t)0;
+  // 16-byte pieces (8 groups of one row o) where rows are 16-byte aligned and
+  // the piece is inside the plane; single words elsewhere
+#pragma unroll
+  for (int u = 0; u < kCtO * (kCtI / 64) / 256; ++u) {
+    const int e = tid + 256 * u;
+    const int r = e / (kCtI / 64), gq = 8 * (e % (kCtI / 64));
+    const int o = o0 + r, g = g0 + gq;
+    uint16_t w[8];
+    if ((G & 7) == 0 && o < d_out && g + 8 <= G) {
+      const uint4 v = *(const uint4*)(codes + (int64_t)o * G + g);
+      __builtin_memcpy(w, &v, 16);
+    } else {
+#pragma unroll
+      for (int z = 0; z < 8; ++z) w[z] = (o < d_out && g + z < G) ? codes[(int64_t)o * G + g + z] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int z = 0; z < 8; ++z) tile[gq + z][r] = w[z];
   }
   __syncthreads();
   const int i = i0 + tid;
@@ -334,6 +348,81 @@ __global__ __launch_bounds__(256) void k_token_major(const void* __restrict__ sr
       v[u] = (cl & 1) ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
     }
     *(uint4*)(dst + (int64_t)c * T8 + t) = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+// x~ for dW on the plain GEMM engine, token-contiguous in runs of 8 (the
+// run-major B operand of launch_gemm_nt_runs): x~[t, i] = bf16(x_q[t, i] *
+// (a_t / 127)) (the same values as k_token_major with DEQ) at element
+// (t / 8 * C + i) * 8 + t % 8, t < T8; tokens t >= T are zero.  A block of 256
+// threads takes 64 tokens x 256 columns: each thread issues its four 16-byte
+// row pieces of x_q first, widens and scales them into an LDS tile [t][c] of
+// bf16, and the tile is read back transposed with ds_read_b64_tr_b16 (16
+// lanes exchange a 4 x 16 block: lane q addresses row q / 4, columns
+// 4 (q % 4) .. + 3; lane i receives column i of the 4 rows).  Lane i of a wave
+// then holds the run of 8 tokens of column 64 w + i, so a wave's store is
+// 1 KB of contiguous memory.
+constexpr int kXtT = 64, kXtC = 256;
+constexpr int kXtPitch = 2 * kXtC + 32;  // bytes per LDS row; the pad spreads a 4-row read over the banks
+
+__global__ __launch_bounds__(256) void k_xt_bf16(const int8_t* __restrict__ xq, const float* __restrict__ absmax, int T,
+                                                 int C, int T8, uint16_t* __restrict__ dst) {
+  __shared__ __attribute__((aligned(16))) char tile[kXtT * kXtPitch];
+  const int t0 = blockIdx.x * kXtT, c0 = blockIdx.y * kXtC;
+  const int tid = threadIdx.x;
+  constexpr int kU = kXtT * kXtC / 16 / 256;  // 16-byte pieces per thread (4)
+  uint4 raw[kU];
+  float sc[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int q = tid + 256 * u;
+    const int r = q >> 4, c = c0 + 16 * (q & 15);
+    const int t = t0 + r;
+    raw[u] = make_uint4(0u, 0u, 0u, 0u);
+    sc[u] = 0.0f;
+    if (t < T) {
+      const int8_t* row = xq + (int64_t)t * C;
+      sc[u] = absmax[t] * (1.0f / 127.0f);
+      if ((C & 15) == 0 && c + 16 <= C) {
+        raw[u] = *(const uint4*)(row + c);
+      } else {
+        int8_t b[16];
+#pragma unroll
+        for (int z = 0; z < 16; ++z) b[z] = c + z < C ? row[c + z] : (int8_t)0;
+        __builtin_memcpy(&raw[u], b, 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int q = tid + 256 * u;
+    const int r = q >> 4, cc = q & 15;
+    int8_t b[16];
+    __builtin_memcpy(b, &raw[u], 16);
+    uint32_t w[8];
+#pragma unroll
+    for (int z = 0; z < 8; ++z) w[z] = cvt_pk_bf16((float)b[2 * z] * sc[u], (float)b[2 * z + 1] * sc[u]);
+    char* p = tile + r * kXtPitch + 32 * cc;
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+    *(uint4*)(p + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+  __syncthreads();
+  const int grp = tid >> 4, ql = tid & 15;  // 16-lane group: 16 consecutive columns
+  const int cb = 16 * grp;                      // this group's first column in the tile
+  const int c = c0 + cb + ql;                   // this lane's output row
+  const int col_addr = cb + 4 * (ql & 3);       // first of the 4 columns lane ql addresses
+#pragma unroll
+  for (int tb = 0; tb < kXtT / 8; ++tb) {
+    v4s part[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * tb + 4 * h + (ql >> 2);
+      part[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SBL_LDS v4s*)(tile + row * kXtPitch + 2 * col_addr));
+    }
+    const int t = t0 + 8 * tb;
+    if (c < C && t < T8)
+      *(v8s*)(dst + ((int64_t)(t >> 3) * C + c) * 8) =
+          (v8s){part[0][0], part[0][1], part[0][2], part[0][3], part[1][0], part[1][1], part[1][2], part[1][3]};
   }
 }
 
@@ -622,12 +711,21 @@ hipError_t run_dw_direct(const int8_t* xq, const float* absmax, const uint16_t* 
     else
       hipLaunchKernelGGL((k_token_major<false, false>), g1, dim3(256), 0, s, dY, nullptr, (int)T, (int)d_out, (int)T8, dyt);
   }
-  const dim3 g2((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_in + kTT - 1) / kTT));
-  hipLaunchKernelGGL((k_token_major<true, true>), g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   float* target = L.S > 1 ? (float*)((char*)ws + L.part) : dW;
-  e = launch_gemm_nt_bf16(dyt, xt, d_out, d_in, T8, nullptr, target, SBL_F32, s, L.S, L.kps);
+  hipError_t e;
+  if (gemm_nt_runs_supported(d_out, d_in, T8)) {
+    const dim3 g2((unsigned)((T8 + kXtT - 1) / kXtT), (unsigned)((d_in + kXtC - 1) / kXtC));
+    hipLaunchKernelGGL(k_xt_bf16, g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_gemm_nt_runs(dyt, xt, d_out, d_in, T8, target, s, L.S, L.kps);
+  } else {
+    const dim3 g2((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_in + kTT - 1) / kTT));
+    hipLaunchKernelGGL((k_token_major<true, true>), g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_gemm_nt_bf16(dyt, xt, d_out, d_in, T8, nullptr, target, SBL_F32, s, L.S, L.kps);
+  }
   if (e != hipSuccess) return e;
   if (L.S > 1) {
     const int64_t n4 = n / 4;

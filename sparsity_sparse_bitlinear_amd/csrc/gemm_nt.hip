@@ -77,7 +77,16 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 //
 // BC: B is the code layout above with rows of K64 / 4 bytes (K64 = K rounded
 // up to 64, codes past K are 00); no split-K.
-template <int OUT, bool WTA, bool BC>
+//
+// BR: B (bf16, K % 8 == 0) is run-major: the 8 values k = 8 j .. 8 j + 7 of
+// row n sit in the 16 bytes at (j N + n) * 16, i.e. [K / 8][N][8], which its
+// producer writes in whole contiguous pieces.  The B stage in LDS is then
+// run-major too, [8 runs][256 rows][16 bytes]: a direct load fills 64
+// consecutive rows of one run from 1 KB of contiguous memory, and fragment
+// reads (32 consecutive rows of a run per half wave) need no swizzle.  B rows
+// past N read whatever follows (or zero past the buffer); they only feed
+// output columns that are not stored.
+template <int OUT, bool WTA, bool BC, bool BR>
 __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B, int M, int N, int K,
                                                               int kps, const float* __restrict__ alpha_p,
@@ -103,7 +112,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   const int rows_b = min(kBNn, N - n0);
   const uint16_t* a_base = A + (int64_t)m0 * K;
   const int64_t b_row = BC ? (int64_t)((K + 63) & ~63) / 4 : (int64_t)K * 2;  // bytes per B row
-  const char* b_base = (const char*)B + n0 * b_row;
+  const char* b_base = (const char*)B + (BR ? (int64_t)n0 * 16 : n0 * b_row);
 
   // Direct-load lanes: LDS chunk position p (16 bytes) of a stage holds row
   // p / 8, logical chunk (p % 8) ^ ((row / 2) % 8), i.e. swz8(row, c) = 16 p.
@@ -124,9 +133,15 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i) {
       const int p = 64 * (kDmaB * wave + i) + lane;
-      const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-      b_off[i] = (uint32_t)(r * K * 2 + 16 * c);
-      b_k[i] = 8 * c;
+      if constexpr (BR) {
+        const int c = p >> 8, r = p & 255;
+        b_off[i] = (uint32_t)((c * N + r) * 16);
+        b_k[i] = 8 * c;
+      } else {
+        const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+        b_off[i] = (uint32_t)(r * K * 2 + 16 * c);
+        b_k[i] = 8 * c;
+      }
     }
   }
 
@@ -134,7 +149,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // block (rows past M or N read as zero) and the K offset rides in soffset;
   // chunks past K (last step only) are sent out of range explicitly.
   const auto ar = make_rsrc(a_base, clamp_bytes((int64_t)rows_a * K * 2));
-  const auto br = make_rsrc(b_base, clamp_bytes((int64_t)rows_b * b_row));
+  const auto br = make_rsrc(b_base, clamp_bytes(BR ? ((int64_t)(K / 8) * N - n0) * 16 : (int64_t)rows_b * b_row));
   const bool ktail = ((kend - kbeg) % kKStep) != 0;
   auto issue = [&](int kt, int st) {
     const int k0 = kbeg + kt * kKStep;
@@ -149,7 +164,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     } else {
 #pragma unroll
       for (int i = 0; i < kDmaB; ++i)
-        dma16(br, sb + 1024 * (kDmaB * wave + i), ktail && k0 + b_k[i] >= kend ? kOOB : b_off[i], soff);
+        dma16(br, sb + 1024 * (kDmaB * wave + i), ktail && k0 + b_k[i] >= kend ? kOOB : b_off[i],
+              BR ? (uint32_t)k0 * (uint32_t)N * 2 : soff);
     }
   };
 
@@ -168,7 +184,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       if (wave < 4) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
     } else {
       const int i = idx - kDmaA;
-      dma16(br, sb + 1024 * (kDmaB * wave + i), ktail && k0 + b_k[i] >= kend ? kOOB : b_off[i], soff);
+      dma16(br, sb + 1024 * (kDmaB * wave + i), ktail && k0 + b_k[i] >= kend ? kOOB : b_off[i],
+            BR ? (uint32_t)k0 * (uint32_t)N * 2 : soff);
     }
   };
 
@@ -203,8 +220,10 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       for (int j = 0; j < kNJ; ++j) fb[j] = widen_codes(ks < 2 ? wb[j].x : wb[j].y, 4 * (ks & 1));
     } else {
 #pragma unroll
-      for (int j = 0; j < kNJ; ++j)
-        fb[j] = __builtin_bit_cast(v8bf, *(const v4i*)(b + swz8(wn0 + 32 * j + (lane & 31), 2 * ks + (lane >> 5))));
+      for (int j = 0; j < kNJ; ++j) {
+        const int n = wn0 + 32 * j + (lane & 31), c = 2 * ks + (lane >> 5);
+        fb[j] = __builtin_bit_cast(v8bf, *(const v4i*)(b + (BR ? 16 * (c * kBNn + n) : swz8(n, c))));
+      }
     }
   };
   // Transposed copy of the A tile of stage st (K step k0): wave w takes 16
@@ -419,6 +438,11 @@ bool gemm_nt_bf16_supported(int64_t M, int64_t N, int64_t K) {
          (int64_t)kBNn * K * 2 <= kMaxRsrcBytes;
 }
 
+bool gemm_nt_runs_supported(int64_t M, int64_t N, int64_t K) {
+  // the whole run-major B is one buffer resource, and soffset = k0 * N * 2
+  return gemm_nt_bf16_supported(M, N, K) && (K / 8) * N * 16 <= kMaxRsrcBytes;
+}
+
 int64_t gemm_nt_bf16_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + kBNn - 1) / kBNn); }
 
 hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
@@ -429,10 +453,20 @@ hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, 
   if (AT && splits != 1) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
   const bool f32 = out_dtype == SBL_F32;
-  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, false> : k_gemm_nt_bf16<SBL_BF16, true, false>)
-                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, false> : k_gemm_nt_bf16<SBL_BF16, false, false>);
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, false, false> : k_gemm_nt_bf16<SBL_BF16, true, false, false>)
+                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, false, false> : k_gemm_nt_bf16<SBL_BF16, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, B, (int)M, (int)N, (int)K, (int)k_per_split, alpha, C, AT,
                      (int)at_ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_nt_runs(const uint16_t* A, const uint16_t* Brun, int64_t M, int64_t N, int64_t K, void* C,
+                               hipStream_t s, int splits, int64_t k_per_split) {
+  if (splits < 1) splits = 1;
+  if (splits == 1) k_per_split = K;
+  const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
+  hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32, false, false, true>), grid, block, 0, s, A, Brun, (int)M, (int)N, (int)K,
+                     (int)k_per_split, nullptr, C, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -441,8 +475,8 @@ hipError_t launch_gemm_nt_codes(const uint16_t* A, const uint32_t* Bc, int64_t M
                                 int64_t at_ld) {
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N)), block(kNT);
   const bool f32 = out_dtype == SBL_F32;
-  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, true> : k_gemm_nt_bf16<SBL_BF16, true, true>)
-                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, true> : k_gemm_nt_bf16<SBL_BF16, false, true>);
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, true, false> : k_gemm_nt_bf16<SBL_BF16, true, true, false>)
+                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, true, false> : k_gemm_nt_bf16<SBL_BF16, false, true, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, (const uint16_t*)Bc, (int)M, (int)N, (int)K, (int)K, alpha, C, AT,
                      (int)at_ld);
   return hipGetLastError();
