@@ -693,7 +693,9 @@ DwLayout dw_layout(int64_t T, int64_t d_in, int64_t d_out, bool fused) {
 }
 
 bool fused_backward(int64_t T, int64_t d_in, int64_t d_out, int flags) {
-  return (flags & SBL_BWD_DX) && (flags & SBL_BWD_DW) && dx_direct(T, d_in, d_out) && dw_direct(T, d_in, d_out);
+  // dY^T leaves the dX product run-major, which the dW product reads as such
+  return (flags & SBL_BWD_DX) && (flags & SBL_BWD_DW) && dx_direct(T, d_in, d_out) && dw_direct(T, d_in, d_out) &&
+         gemm_nt_runs_supported(d_out, d_in, round8(T));
 }
 
 // dW on the plain GEMM engine from the layout L: dY^T (unless the dX product
@@ -718,7 +720,7 @@ hipError_t run_dw_direct(const int8_t* xq, const float* absmax, const uint16_t* 
     hipLaunchKernelGGL(k_xt_bf16, g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_gemm_nt_runs(dyt, xt, d_out, d_in, T8, target, s, L.S, L.kps);
+    e = launch_gemm_nt_runs(dyt, dyt_ready, xt, d_out, d_in, T8, target, s, L.S, L.kps);
   } else {
     const dim3 g2((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_in + kTT - 1) / kTT));
     hipLaunchKernelGGL((k_token_major<true, true>), g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);

@@ -68,9 +68,10 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 // blockIdx.y selects a K range [kps * y, kps * (y + 1)) (split-K); block y writes
 // its partial product to C + y * M * N.  alpha_p == nullptr means alpha = 1.
 //
-// WTA (no split-K): the A tiles staged in LDS are also written out transposed,
-// AT[k, m] = A[m, k] with row length at_ld (>= M, a multiple of 8; columns M
-// to at_ld read as zero from the tile and are written as zeros).  This is how
+// WTA (no split-K): the A tiles staged in LDS are also written out transposed
+// and run-major (see BR), AT[k, m] = A[m, k] at element (m / 8 * K + k) * 8 +
+// m % 8 for m < at_ld (at_ld >= M, a multiple of 8; m from M to at_ld read as
+// zero from the tile and are written as zeros).  This is how
 // the dX product leaves dY^T behind for dW: every (m tile, K step) is written
 // once, by the block whose column tile index equals the step modulo the number
 // of column tiles, from the stage as soon as it has landed.
@@ -86,7 +87,9 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 // reads (32 consecutive rows of a run per half wave) need no swizzle.  B rows
 // past N read whatever follows (or zero past the buffer); they only feed
 // output columns that are not stored.
-template <int OUT, bool WTA, bool BC, bool BR>
+//
+// AR: A is run-major in the same way ([K / 8][M][8]) and so is its LDS stage.
+template <int OUT, bool WTA, bool BC, bool AR, bool BR>
 __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B, int M, int N, int K,
                                                               int kps, const float* __restrict__ alpha_p,
@@ -110,7 +113,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   const int nk = (kend - kbeg + kKStep - 1) / kKStep;  // >= 1: the host never makes an empty split
   const int rows_a = min(kBM, M - m0);
   const int rows_b = min(kBNn, N - n0);
-  const uint16_t* a_base = A + (int64_t)m0 * K;
+  const uint16_t* a_base = A + (AR ? (int64_t)m0 * 8 : (int64_t)m0 * K);
   const int64_t b_row = BC ? (int64_t)((K + 63) & ~63) / 4 : (int64_t)K * 2;  // bytes per B row
   const char* b_base = (const char*)B + (BR ? (int64_t)n0 * 16 : n0 * b_row);
 
@@ -122,9 +125,15 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
 #pragma unroll
   for (int i = 0; i < kDmaA; ++i) {
     const int p = 64 * (kDmaA * wave + i) + lane;
-    const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
-    a_off[i] = (uint32_t)(r * K * 2 + 16 * c);
-    a_k[i] = 8 * c;
+    if constexpr (AR) {
+      const int c = p >> 8, r = p & 255;
+      a_off[i] = (uint32_t)((c * M + r) * 16);
+      a_k[i] = 8 * c;
+    } else {
+      const int r = p >> 3, c = (p & 7) ^ ((r >> 1) & 7);
+      a_off[i] = (uint32_t)(r * K * 2 + 16 * c);
+      a_k[i] = 8 * c;
+    }
   }
   if constexpr (BC) {
     b_off[0] = (uint32_t)((64 * (wave & 3) + lane) * b_row);  // row 64 w + lane, one 16-byte piece
@@ -148,7 +157,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // Loads of K step kt into stage st.  The resources span the valid rows of the
   // block (rows past M or N read as zero) and the K offset rides in soffset;
   // chunks past K (last step only) are sent out of range explicitly.
-  const auto ar = make_rsrc(a_base, clamp_bytes((int64_t)rows_a * K * 2));
+  const auto ar = make_rsrc(a_base, clamp_bytes(AR ? ((int64_t)(K / 8) * M - m0) * 16 : (int64_t)rows_a * K * 2));
+  const uint32_t a_soff_per_k = AR ? (uint32_t)M * 2 : 2u;  // soffset bytes per k
   const auto br = make_rsrc(b_base, clamp_bytes(BR ? ((int64_t)(K / 8) * N - n0) * 16 : (int64_t)rows_b * b_row));
   const bool ktail = ((kend - kbeg) % kKStep) != 0;
   auto issue = [&](int kt, int st) {
@@ -158,7 +168,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     char* sb = sa + kStageA;
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i)
-      dma16(ar, sa + 1024 * (kDmaA * wave + i), ktail && k0 + a_k[i] >= kend ? kOOB : a_off[i], soff);
+      dma16(ar, sa + 1024 * (kDmaA * wave + i), ktail && k0 + a_k[i] >= kend ? kOOB : a_off[i],
+            (uint32_t)k0 * a_soff_per_k);
     if constexpr (BC) {
       if (wave < 4) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
     } else {
@@ -179,7 +190,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     char* sa = lds + st * kSt;
     char* sb = sa + kStageA;
     if (idx < kDmaA) {
-      dma16(ar, sa + 1024 * (kDmaA * wave + idx), ktail && k0 + a_k[idx] >= kend ? kOOB : a_off[idx], soff);
+      dma16(ar, sa + 1024 * (kDmaA * wave + idx), ktail && k0 + a_k[idx] >= kend ? kOOB : a_off[idx],
+            (uint32_t)k0 * a_soff_per_k);
     } else if constexpr (BC) {
       if (wave < 4) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
     } else {
@@ -213,8 +225,10 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     const char* a = lds + st * kSt;
     const char* b = a + kStageA;
 #pragma unroll
-    for (int i = 0; i < kMI; ++i)
-      fa[i] = __builtin_bit_cast(v8bf, *(const v4i*)(a + swz8(wm0 + 32 * i + (lane & 31), 2 * ks + (lane >> 5))));
+    for (int i = 0; i < kMI; ++i) {
+      const int m = wm0 + 32 * i + (lane & 31), c = 2 * ks + (lane >> 5);
+      fa[i] = __builtin_bit_cast(v8bf, *(const v4i*)(a + (AR ? 16 * (c * kBM + m) : swz8(m, c))));
+    }
     if constexpr (BC) {
 #pragma unroll
       for (int j = 0; j < kNJ; ++j) fb[j] = widen_codes(ks < 2 ? wb[j].x : wb[j].y, 4 * (ks & 1));
@@ -236,7 +250,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     const char* a = lds + st * kSt;
     const int kb = 16 * (wave & 3), tb0 = 128 * (wave >> 2);
     const int g = lane >> 4, q = lane & 15;
-    const auto atr = make_rsrc(AT + (int64_t)k0 * at_ld + m0, clamp_bytes((int64_t)(K - k0) * at_ld * 2 - m0 * 2));
+    const auto atr = make_rsrc(AT, clamp_bytes((int64_t)at_ld * K * 2));
     const int kc = kb + 4 * (q & 3);                    // first of the 4 columns lane q addresses
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -252,7 +266,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       const bool ok = k0 + col < K && m0 + t0 < at_ld;
       const v4i v = __builtin_bit_cast(v4i, (v8s){part[0][0], part[0][1], part[0][2], part[0][3],
                                                    part[1][0], part[1][1], part[1][2], part[1][3]});
-      __builtin_amdgcn_raw_buffer_store_b128(v, atr, ok ? (uint32_t)((col * at_ld + t0) * 2) : kOOB, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(v, atr, ok ? (uint32_t)((((m0 + t0) >> 3) * K + k0 + col) * 16) : kOOB,
+                                             0, 0);
     }
   };
 
@@ -439,8 +454,9 @@ bool gemm_nt_bf16_supported(int64_t M, int64_t N, int64_t K) {
 }
 
 bool gemm_nt_runs_supported(int64_t M, int64_t N, int64_t K) {
-  // the whole run-major B is one buffer resource, and soffset = k0 * N * 2
-  return gemm_nt_bf16_supported(M, N, K) && (K / 8) * N * 16 <= kMaxRsrcBytes;
+  // a whole run-major operand is one buffer resource, and soffset = k0 * rows * 2
+  return gemm_nt_bf16_supported(M, N, K) && K % 8 == 0 && (K / 8) * N * 16 <= kMaxRsrcBytes &&
+         (K / 8) * M * 16 <= kMaxRsrcBytes;
 }
 
 int64_t gemm_nt_bf16_tiles(int64_t M, int64_t N) { return ((M + kBM - 1) / kBM) * ((N + kBNn - 1) / kBNn); }
@@ -453,20 +469,21 @@ hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, 
   if (AT && splits != 1) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
   const bool f32 = out_dtype == SBL_F32;
-  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, false, false> : k_gemm_nt_bf16<SBL_BF16, true, false, false>)
-                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, false, false> : k_gemm_nt_bf16<SBL_BF16, false, false, false>);
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, false, false, false> : k_gemm_nt_bf16<SBL_BF16, true, false, false, false>)
+                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, false, false, false> : k_gemm_nt_bf16<SBL_BF16, false, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, B, (int)M, (int)N, (int)K, (int)k_per_split, alpha, C, AT,
                      (int)at_ld);
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_nt_runs(const uint16_t* A, const uint16_t* Brun, int64_t M, int64_t N, int64_t K, void* C,
-                               hipStream_t s, int splits, int64_t k_per_split) {
+hipError_t launch_gemm_nt_runs(const uint16_t* A, bool a_runs, const uint16_t* Brun, int64_t M, int64_t N, int64_t K,
+                               void* C, hipStream_t s, int splits, int64_t k_per_split) {
   if (splits < 1) splits = 1;
   if (splits == 1) k_per_split = K;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
-  hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32, false, false, true>), grid, block, 0, s, A, Brun, (int)M, (int)N, (int)K,
-                     (int)k_per_split, nullptr, C, nullptr, 0);
+  auto kern = a_runs ? k_gemm_nt_bf16<SBL_F32, false, false, true, true> : k_gemm_nt_bf16<SBL_F32, false, false, false, true>;
+  hipLaunchKernelGGL(kern, grid, block, 0, s, A, Brun, (int)M, (int)N, (int)K, (int)k_per_split, nullptr, C, nullptr,
+                     0);
   return hipGetLastError();
 }
 
@@ -475,8 +492,8 @@ hipError_t launch_gemm_nt_codes(const uint16_t* A, const uint32_t* Bc, int64_t M
                                 int64_t at_ld) {
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N)), block(kNT);
   const bool f32 = out_dtype == SBL_F32;
-  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, true, false> : k_gemm_nt_bf16<SBL_BF16, true, true, false>)
-                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, true, false> : k_gemm_nt_bf16<SBL_BF16, false, true, false>);
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, true, false, false> : k_gemm_nt_bf16<SBL_BF16, true, true, false, false>)
+                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, true, false, false> : k_gemm_nt_bf16<SBL_BF16, false, true, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, (const uint16_t*)Bc, (int)M, (int)N, (int)K, (int)K, alpha, C, AT,
                      (int)at_ld);
   return hipGetLastError();

@@ -80,17 +80,19 @@ hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_
 // product to C + z * M * N.
 bool gemm_nt_bf16_supported(int64_t M, int64_t N, int64_t K);
 int64_t gemm_nt_bf16_tiles(int64_t M, int64_t N);
-// AT != nullptr (splits == 1): also write A^T [K, at_ld] (at_ld >= M, a multiple
-// of 8; columns from M to at_ld become zero).
+// AT != nullptr (splits == 1): also write A^T run-major, element (m, k) at
+// (m / 8 * K + k) * 8 + m % 8 for m < at_ld (at_ld >= M, a multiple of 8; m
+// from M to at_ld become zero); at_ld * K * 2 bytes must stay below 2 GiB.
 hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, int64_t N, int64_t K,
                                const float* alpha, void* C, int out_dtype, hipStream_t s, int splits = 1,
                                int64_t k_per_split = 0, uint16_t* AT = nullptr, int64_t at_ld = 0);
 // The same product (float32 C, alpha = 1) with B given run-major: B[n, k] at
 // element (k / 8 * N + n) * 8 + k % 8 (K % 8 == 0), as written by k_xt_bf16
-// (gemm_bwd.hip).  Only where gemm_nt_runs_supported() holds.
+// (gemm_bwd.hip); with a_runs, A is run-major in the same way (as written by
+// the AT side output below).  Only where gemm_nt_runs_supported() holds.
 bool gemm_nt_runs_supported(int64_t M, int64_t N, int64_t K);
-hipError_t launch_gemm_nt_runs(const uint16_t* A, const uint16_t* Brun, int64_t M, int64_t N, int64_t K, void* C,
-                               hipStream_t s, int splits = 1, int64_t k_per_split = 0);
+hipError_t launch_gemm_nt_runs(const uint16_t* A, bool a_runs, const uint16_t* Brun, int64_t M, int64_t N, int64_t K,
+                               void* C, hipStream_t s, int splits = 1, int64_t k_per_split = 0);
 // The same product with B = W_eff^T given as the transposed 2-bit code plane of
 // k_codes_t (gemm_bwd.hip): Bc [N, K64 / 16] words, K64 = K rounded up to 64.
 // No split-K; AT as above.
