@@ -34,9 +34,9 @@ HBM_PEAK_GBS = 8000.0
 # HBM bytes per sbl_backward(dX + dW) call on the default workload (FETCH_SIZE x 2.000 +
 # WRITE_SIZE, scale factors from a plain 1 GiB copy), averaged over the 7 linears; measured with
 # rocprofv3 --pmc for the backward kernel sources whose hash is given
-# (profiles/traffic_backward_3b_32768tok.md).  None until measured for these sources.
-BWD_TRAFFIC_BYTES = None
-BWD_TRAFFIC_SRC_SHA = ""
+# (profiles/traffic_backward_3b_32768tok.md).
+BWD_TRAFFIC_BYTES = 3.24e9
+BWD_TRAFFIC_SRC_SHA = "dfe4e848e2f90971"
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -194,8 +194,8 @@ def main():
     gemm_parts = {
         "fwd": ("forward_int8", "TOP/s", INT8_PEAK_TOPS, ["k_fwd_i8_direct<bf16>"]),
         "bwd": ("backward_bf16 (dX + dW)", "TFLOP/s", BF16_PEAK_TFLOPS,
-                ["k_weff_t_bf16", "k_gemm_nt_bf16<bf16, writes dY^T>", "k_token_major<x~>", "k_gemm_nt_bf16<f32>",
-                 "k_splitk_reduce (split-K shapes)"]),
+                ["k_codes_t", "k_gemm_nt_bf16<bf16, codes B, writes dY^T>", "k_xt_bf16",
+                 "k_gemm_nt_bf16<f32, run-major A and B>", "k_splitk_reduce (split-K shapes)"]),
     }
     dom = max(gemm_parts, key=lambda p: tot_ms[parts.index(p)])
     dname, dunit, dpeak, dkernels = gemm_parts[dom]
