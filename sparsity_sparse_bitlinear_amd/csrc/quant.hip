@@ -139,23 +139,20 @@ __global__ __launch_bounds__(kAbsumThreads) void k_absum(const uint4* __restrict
   __syncthreads();
 
   U128 acc = {0, 0};
-  double fsum = 0.0;  // exact: at most 256 window values since the last flush
+  // kU independent float64 window sums, each exact while it holds at most 256
+  // window values (flushed every 32 rounds of 8); kU loads in flight per round.
+  constexpr int kU = 4;
+  double fsum[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) fsum[u] = 0.0;
   int fcount = 0;
   bool any_hist = false;
-  const int64_t stride = (int64_t)gridDim.x * kAbsumThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kAbsumThreads + tid; i < n_vec8; i += stride) {
-    const uint4 v = W[i];
+  auto one = [&](const uint4 v, double& fs) {
     if (__builtin_expect(in_fast_window(v), 1)) {
-      fsum += (double)__uint_as_float((v.x & 0x7FFFu) << 16) + (double)__uint_as_float(v.x & 0x7FFF0000u);
-      fsum += (double)__uint_as_float((v.y & 0x7FFFu) << 16) + (double)__uint_as_float(v.y & 0x7FFF0000u);
-      fsum += (double)__uint_as_float((v.z & 0x7FFFu) << 16) + (double)__uint_as_float(v.z & 0x7FFF0000u);
-      fsum += (double)__uint_as_float((v.w & 0x7FFFu) << 16) + (double)__uint_as_float(v.w & 0x7FFF0000u);
-      if (++fcount == 32) {  // 256 values: move the exact integer fsum * 2^(134 - kWinLo) < 2^53 out
-        const U128 f = {(unsigned long long)ldexp(fsum, 134 - kWinLo), 0ull};
-        add128(acc, f);
-        fsum = 0.0;
-        fcount = 0;
-      }
+      fs += (double)__uint_as_float((v.x & 0x7FFFu) << 16) + (double)__uint_as_float(v.x & 0x7FFF0000u);
+      fs += (double)__uint_as_float((v.y & 0x7FFFu) << 16) + (double)__uint_as_float(v.y & 0x7FFF0000u);
+      fs += (double)__uint_as_float((v.z & 0x7FFFu) << 16) + (double)__uint_as_float(v.z & 0x7FFF0000u);
+      fs += (double)__uint_as_float((v.w & 0x7FFFu) << 16) + (double)__uint_as_float(v.w & 0x7FFF0000u);
     } else {
       absum_half(v.x & 0xFFFFu, acc, hist, any_hist);
       absum_half(v.x >> 16, acc, hist, any_hist);
@@ -166,11 +163,32 @@ __global__ __launch_bounds__(kAbsumThreads) void k_absum(const uint4* __restrict
       absum_half(v.w & 0xFFFFu, acc, hist, any_hist);
       absum_half(v.w >> 16, acc, hist, any_hist);
     }
+  };
+  // move the exact integers fsum * 2^(134 - kWinLo) < 2^53 into the 128-bit sum
+  auto flush = [&]() {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const U128 f = {(unsigned long long)ldexp(fsum[u], 134 - kWinLo), 0ull};
+      add128(acc, f);
+      fsum[u] = 0.0;
+    }
+  };
+  const int64_t stride = (int64_t)gridDim.x * kAbsumThreads;
+  int64_t i = (int64_t)blockIdx.x * kAbsumThreads + tid;
+  for (; i + (kU - 1) * stride < n_vec8; i += kU * stride) {
+    uint4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = W[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) one(v[u], fsum[u]);
+    if (++fcount == 32) {
+      flush();
+      fcount = 0;
+    }
   }
-  {
-    const U128 f = {(unsigned long long)ldexp(fsum, 134 - kWinLo), 0ull};
-    add128(acc, f);
-  }
+  flush();
+  for (; i < n_vec8; i += stride) one(W[i], fsum[0]);  // fewer than kU more: at most 24 values
+  flush();
   if (any_hist) block_any = 1;  // benign race: every writer stores 1
   red[tid] = acc;
   __syncthreads();
@@ -332,18 +350,30 @@ __device__ __forceinline__ void pack_group(const uint4 v, uint32_t gamma_bits, u
   mask_out = (uint8_t)mask;
 }
 
+// A block takes 4 x 256 consecutive groups per round (each thread 4 groups,
+// 256 apart, so every load and store instruction is contiguous); the four
+// loads are issued before any group is packed.
 template <int N>
 __global__ __launch_bounds__(256) void k_mask_quant_pack(const uint4* __restrict__ W, int64_t n_groups,
                                                          const float* __restrict__ gamma_p,
                                                          uint16_t* __restrict__ codes, uint8_t* __restrict__ mask) {
+  constexpr int kU = 4;
   const uint32_t gamma_bits = __float_as_uint(*gamma_p);
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < n_groups; g += stride) {
-    uint16_t c;
-    uint8_t m;
-    pack_group<N>(W[g], gamma_bits, c, m);
-    codes[g] = c;
-    if (mask) mask[g] = m;
+  const int64_t stride = (int64_t)gridDim.x * 256 * kU;
+  for (int64_t g0 = (int64_t)blockIdx.x * 256 * kU + threadIdx.x; g0 < n_groups; g0 += stride) {
+    uint4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = g0 + 256 * u < n_groups ? W[g0 + 256 * u] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t g = g0 + 256 * u;
+      if (g >= n_groups) break;
+      uint16_t c;
+      uint8_t m;
+      pack_group<N>(v[u], gamma_bits, c, m);
+      codes[g] = c;
+      if (mask) mask[g] = m;
+    }
   }
 }
 
@@ -372,7 +402,7 @@ hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in
   hipLaunchKernelGGL(k_absum, dim3(nb), dim3(kAbsumThreads), 0, s, (const uint4*)W, n_groups, part, hist);
   hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(256), 0, s, (const AbsumPartial*)part,
                      (const unsigned long long*)hist, nb, (unsigned long long)(d_out * d_in), gamma);
-  int64_t pb = (n_groups + 255) / 256;
+  int64_t pb = (n_groups + 1023) / 1024;
   if (pb > 65536) pb = 65536;
   const dim3 grid((unsigned)pb), block(256);
   switch (n_keep) {
