@@ -365,46 +365,64 @@ __global__ __launch_bounds__(256) void k_token_major(const void* __restrict__ sr
 constexpr int kXtT = 64, kXtC = 256;
 constexpr int kXtPitch = 2 * kXtC + 32;  // bytes per LDS row; the pad spreads a 4-row read over the banks
 
-__global__ __launch_bounds__(256) void k_xt_bf16(const int8_t* __restrict__ xq, const float* __restrict__ absmax, int T,
+// Y: the same for a bf16 source row-scaled, dst = bf16(y[t, c] * (a_t / 127))
+// (the scaled dY that the int8 form of the dW product takes; C % 8 == 0).
+template <bool Y>
+__global__ __launch_bounds__(256) void k_xt_bf16(const void* __restrict__ src, const float* __restrict__ absmax, int T,
                                                  int C, int T8, uint16_t* __restrict__ dst) {
   __shared__ __attribute__((aligned(16))) char tile[kXtT * kXtPitch];
   const int t0 = blockIdx.x * kXtT, c0 = blockIdx.y * kXtC;
   const int tid = threadIdx.x;
-  constexpr int kU = kXtT * kXtC / 16 / 256;  // 16-byte pieces per thread (4)
+  constexpr int kPc = Y ? 8 : 16;                   // columns per 16-byte source piece
+  constexpr int kU = kXtT * kXtC / kPc / 256;       // pieces per thread (4 or 8)
   uint4 raw[kU];
   float sc[kU];
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int q = tid + 256 * u;
-    const int r = q >> 4, c = c0 + 16 * (q & 15);
+    const int r = q / (kXtC / kPc), c = c0 + kPc * (q % (kXtC / kPc));
     const int t = t0 + r;
     raw[u] = make_uint4(0u, 0u, 0u, 0u);
     sc[u] = 0.0f;
     if (t < T) {
-      const int8_t* row = xq + (int64_t)t * C;
       sc[u] = absmax[t] * (1.0f / 127.0f);
-      if ((C & 15) == 0 && c + 16 <= C) {
-        raw[u] = *(const uint4*)(row + c);
+      if constexpr (Y) {
+        const uint16_t* row = (const uint16_t*)src + (int64_t)t * C;
+        if (c + 8 <= C) raw[u] = *(const uint4*)(row + c);
       } else {
-        int8_t b[16];
+        const int8_t* row = (const int8_t*)src + (int64_t)t * C;
+        if ((C & 15) == 0 && c + 16 <= C) {
+          raw[u] = *(const uint4*)(row + c);
+        } else {
+          int8_t b[16];
 #pragma unroll
-        for (int z = 0; z < 16; ++z) b[z] = c + z < C ? row[c + z] : (int8_t)0;
-        __builtin_memcpy(&raw[u], b, 16);
+          for (int z = 0; z < 16; ++z) b[z] = c + z < C ? row[c + z] : (int8_t)0;
+          __builtin_memcpy(&raw[u], b, 16);
+        }
       }
     }
   }
 #pragma unroll
   for (int u = 0; u < kU; ++u) {
     const int q = tid + 256 * u;
-    const int r = q >> 4, cc = q & 15;
-    int8_t b[16];
-    __builtin_memcpy(b, &raw[u], 16);
-    uint32_t w[8];
+    const int r = q / (kXtC / kPc), cc = q % (kXtC / kPc);
+    char* p = tile + r * kXtPitch + 2 * kPc * cc;
+    if constexpr (Y) {
+      const uint32_t w4[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+      uint32_t w[4];
 #pragma unroll
-    for (int z = 0; z < 8; ++z) w[z] = cvt_pk_bf16((float)b[2 * z] * sc[u], (float)b[2 * z + 1] * sc[u]);
-    char* p = tile + r * kXtPitch + 32 * cc;
-    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
-    *(uint4*)(p + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+      for (int z = 0; z < 4; ++z)
+        w[z] = cvt_pk_bf16(__uint_as_float(w4[z] << 16) * sc[u], __uint_as_float(w4[z] & 0xFFFF0000u) * sc[u]);
+      *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      int8_t b[16];
+      __builtin_memcpy(b, &raw[u], 16);
+      uint32_t w[8];
+#pragma unroll
+      for (int z = 0; z < 8; ++z) w[z] = cvt_pk_bf16((float)b[2 * z] * sc[u], (float)b[2 * z + 1] * sc[u]);
+      *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+      *(uint4*)(p + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+    }
   }
   __syncthreads();
   const int grp = tid >> 4, ql = tid & 15;  // 16-lane group: 16 consecutive columns
@@ -436,6 +454,17 @@ int64_t round8(int64_t t) { return (t + 7) & ~(int64_t)7; }
 
 bool dw_direct(int64_t T, int64_t d_in, int64_t d_out) {
   return T > 0 && gemm_nt_bf16_supported(d_out, d_in, round8(T));
+}
+
+// dW on the int8 form: dW = (dY diag(a / 127))^T x_q, the scaled dY run-major
+// (written by the dX product, or by k_xt_bf16<true>), x_q read as it is.  It
+// saves the x~ pass (3 bytes per element of x) but its product, which widens
+// B in registers, runs about 12% longer than the bf16 one (measured on the 3B
+// shapes at 32768 tokens), so it is used only while the saved pass outweighs
+// that, i.e. for d_out up to about 2.7K (2560 here).
+bool dw_q(int64_t T, int64_t d_in, int64_t d_out) {
+  return dw_direct(T, d_in, d_out) && d_out % 8 == 0 && d_out <= 2560 &&
+         gemm_nt_q_supported(d_out, d_in, round8(T), T);
 }
 
 // K splits for the plain GEMM engine (one 256 x 256 block per CU): pick S to
@@ -677,15 +706,20 @@ struct DwLayout {
   size_t dyt, xt, part, wt, total;
   int S;
   int64_t kps;
+  bool q;  // int8 form: scaled dY^T and x_q as they are (no x~ copy)
 };
 
+// Workspace of dW (and, fused, of the dX code plane, which is dead before dW
+// starts): dY^T [T8 x d_out] bf16, x~ [T8 x d_in] bf16 unless the int8 form is
+// used, split-K partial sums.
 DwLayout dw_layout(int64_t T, int64_t d_in, int64_t d_out, bool fused) {
   DwLayout L{};
   const int64_t T8 = round8(T);
   nt_splits(d_out, d_in, T8, L.S, L.kps);
+  L.q = dw_q(T, d_in, d_out);
   L.dyt = 0;
   L.xt = align256((size_t)d_out * (size_t)T8 * 2);
-  L.part = L.xt + align256((size_t)d_in * (size_t)T8 * 2);
+  L.part = L.xt + (L.q ? 0 : align256((size_t)d_in * (size_t)T8 * 2));
   L.total = L.part + (L.S > 1 ? (size_t)L.S * (size_t)d_out * (size_t)d_in * sizeof(float) : 0);
   L.wt = L.xt;
   if (fused) L.total = std::max(L.total, L.wt + align256(codes_t_bytes(d_in, d_out)));
@@ -706,6 +740,25 @@ hipError_t run_dw_direct(const int8_t* xq, const float* absmax, const uint16_t* 
   const int64_t n = d_out * d_in;
   uint16_t* dyt = (uint16_t*)((char*)ws + L.dyt);
   uint16_t* xt = (uint16_t*)((char*)ws + L.xt);
+  float* target = L.S > 1 ? (float*)((char*)ws + L.part) : dW;
+  hipError_t e;
+  if (L.q) {
+    if (!dyt_ready) {  // the dX product did not write the scaled dY^T
+      const dim3 g((unsigned)((T8 + kXtT - 1) / kXtT), (unsigned)((d_out + kXtC - 1) / kXtC));
+      hipLaunchKernelGGL(k_xt_bf16<true>, g, dim3(256), 0, s, dY, absmax, (int)T, (int)d_out, (int)T8, dyt);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    e = launch_gemm_nt_q(dyt, xq, d_out, d_in, T8, T, target, s, L.S, L.kps);
+    if (e != hipSuccess) return e;
+    if (L.S > 1) {
+      const int64_t n4 = n / 4;
+      hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)std::min<int64_t>((n4 + 255) / 256, 65536)), dim3(256), 0,
+                         s, (const float4*)target, n4, L.S, (float4*)dW);
+      e = hipGetLastError();
+    }
+    return e;
+  }
   if (!dyt_ready) {
     const dim3 g1((unsigned)((T8 + kTT - 1) / kTT), (unsigned)((d_out + kTT - 1) / kTT));
     if (d_out % 8 == 0)
@@ -713,11 +766,9 @@ hipError_t run_dw_direct(const int8_t* xq, const float* absmax, const uint16_t* 
     else
       hipLaunchKernelGGL((k_token_major<false, false>), g1, dim3(256), 0, s, dY, nullptr, (int)T, (int)d_out, (int)T8, dyt);
   }
-  float* target = L.S > 1 ? (float*)((char*)ws + L.part) : dW;
-  hipError_t e;
   if (gemm_nt_runs_supported(d_out, d_in, T8)) {
     const dim3 g2((unsigned)((T8 + kXtT - 1) / kXtT), (unsigned)((d_in + kXtC - 1) / kXtC));
-    hipLaunchKernelGGL(k_xt_bf16, g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);
+    hipLaunchKernelGGL(k_xt_bf16<false>, g2, dim3(256), 0, s, xq, absmax, (int)T, (int)d_in, (int)T8, xt);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_gemm_nt_runs(dyt, dyt_ready, xt, d_out, d_in, T8, target, s, L.S, L.kps);
@@ -764,8 +815,9 @@ hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8
     uint32_t* WT = (uint32_t*)((char*)ws + L.wt);
     hipError_t e = launch_codes_t(codes, d_out, d_in, WT, s);
     if (e != hipSuccess) return e;
+    // with the int8 form of dW the side output is dY scaled by a_t / 127
     e = launch_gemm_nt_codes(dY, WT, T, d_in, d_out, gamma, dX, dx_dtype, s, (uint16_t*)((char*)ws + L.dyt),
-                             round8(T));
+                             round8(T), L.q ? absmax : nullptr);
     if (e != hipSuccess) return e;
     return run_dw_direct(xq, absmax, dY, T, d_in, d_out, dW, ws, L, true, s);
   }

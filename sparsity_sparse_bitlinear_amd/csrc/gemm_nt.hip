@@ -47,6 +47,7 @@ constexpr int kDmaB = kBNn * 8 / kNT;     // 4
 constexpr int kDmaStep = kDmaA + kDmaB;
 constexpr int kKStep = kRowK / 2;         // 64 bf16 per K step
 constexpr int kStageBC = kBNn * 16;       // 4 KB: B as codes, 16 bytes per row and K step
+constexpr int kStageBQ = kKStep * kBNn;   // 16 KB: B as int8, 64 rows k x 256 columns n
 
 // B as codes (BC): row n of B holds, per K step of 64, 16 bytes = 4 words;
 // word 2 h + w serves lane half h (k groups 2 ks + h of the four 16-wide
@@ -71,7 +72,9 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 // WTA (no split-K): the A tiles staged in LDS are also written out transposed
 // and run-major (see BR), AT[k, m] = A[m, k] at element (m / 8 * K + k) * 8 +
 // m % 8 for m < at_ld (at_ld >= M, a multiple of 8; m from M to at_ld read as
-// zero from the tile and are written as zeros).  This is how
+// zero from the tile and are written as zeros).  With wscale != nullptr each
+// row m is scaled on the way: AT[k, m] = bf16(A[m, k] * (wscale[m] / 127))
+// (float32 product, the scale taken as wscale[m] * fl(1/127)).  This is how
 // the dX product leaves dY^T behind for dW: every (m tile, K step) is written
 // once, by the block whose column tile index equals the step modulo the number
 // of column tiles, from the stage as soon as it has landed.
@@ -89,14 +92,24 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 // output columns that are not stored.
 //
 // AR: A is run-major in the same way ([K / 8][M][8]) and so is its LDS stage.
-template <int OUT, bool WTA, bool BC, bool AR, bool BR>
+//
+// BQ: B is given as int8 rows along K, Bq[k, n] = B[n, k] row-major [K][N]
+// (N % 16 == 0; rows k >= kb_rows read as zero), and widened to bf16 in
+// registers (exact).  Its LDS stage holds the 64 K rows of a step x 256
+// columns, 16-byte chunks of row k at chunk position c ^ (k % 8); a B fragment
+// (8 consecutive k of one n) is one ds_read_b64_tr_b8: in each 16-lane group,
+// lane q addresses the 8 bytes of row q / 2 at columns 8 (q % 2) .. + 7 of a
+// block of 8 rows x 16 columns, and lane i receives column i of the 8 rows;
+// the swizzle puts those 8 rows in 8 different bank groups.
+template <int OUT, bool WTA, bool BC, bool AR, bool BR, bool BQ>
 __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B, int M, int N, int K,
                                                               int kps, const float* __restrict__ alpha_p,
                                                               void* __restrict__ C, uint16_t* __restrict__ AT,
-                                                              int at_ld) {
-  constexpr int kSt = kStageA + (BC ? kStageBC : kStageB);
-  constexpr int kDmaBw = BC ? 1 : kDmaB;    // B loads per wave and step (BC: waves 0-3 only)
+                                                              int at_ld, const float* __restrict__ wscale,
+                                                              int kb_rows) {
+  constexpr int kSt = kStageA + (BC ? kStageBC : BQ ? kStageBQ : kStageB);
+  constexpr int kDmaBw = BC ? 1 : BQ ? 2 : kDmaB;  // B loads per wave and step (BC: waves 0-3 only)
   __shared__ __attribute__((aligned(1024))) char lds[kStages * kSt];
 
   const int tid = threadIdx.x;
@@ -115,7 +128,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   const int rows_b = min(kBNn, N - n0);
   const uint16_t* a_base = A + (AR ? (int64_t)m0 * 8 : (int64_t)m0 * K);
   const int64_t b_row = BC ? (int64_t)((K + 63) & ~63) / 4 : (int64_t)K * 2;  // bytes per B row
-  const char* b_base = (const char*)B + (BR ? (int64_t)n0 * 16 : n0 * b_row);
+  const char* b_base = (const char*)B + (BQ ? (int64_t)n0 : BR ? (int64_t)n0 * 16 : n0 * b_row);
 
   // Direct-load lanes: LDS chunk position p (16 bytes) of a stage holds row
   // p / 8, logical chunk (p % 8) ^ ((row / 2) % 8), i.e. swz8(row, c) = 16 p.
@@ -138,6 +151,14 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   if constexpr (BC) {
     b_off[0] = (uint32_t)((64 * (wave & 3) + lane) * b_row);  // row 64 w + lane, one 16-byte piece
     b_k[0] = 0;
+  } else if constexpr (BQ) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = 64 * (2 * wave + i) + lane;
+      const int r = p >> 4, c = (p & 15) ^ (r & 7);  // K row r, logical 16-column chunk c
+      b_off[i] = (uint32_t)(r * N + 16 * c);
+      b_k[i] = r;
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < kDmaB; ++i) {
@@ -159,7 +180,9 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // chunks past K (last step only) are sent out of range explicitly.
   const auto ar = make_rsrc(a_base, clamp_bytes(AR ? ((int64_t)(K / 8) * M - m0) * 16 : (int64_t)rows_a * K * 2));
   const uint32_t a_soff_per_k = AR ? (uint32_t)M * 2 : 2u;  // soffset bytes per k
-  const auto br = make_rsrc(b_base, clamp_bytes(BR ? ((int64_t)(K / 8) * N - n0) * 16 : (int64_t)rows_b * b_row));
+  const auto br = make_rsrc(b_base, clamp_bytes(BQ   ? (int64_t)kb_rows * N - n0
+                                                : BR ? ((int64_t)(K / 8) * N - n0) * 16
+                                                     : (int64_t)rows_b * b_row));
   const bool ktail = ((kend - kbeg) % kKStep) != 0;
   auto issue = [&](int kt, int st) {
     const int k0 = kbeg + kt * kKStep;
@@ -172,6 +195,10 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
             (uint32_t)k0 * a_soff_per_k);
     if constexpr (BC) {
       if (wave < 4) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
+    } else if constexpr (BQ) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        dma16(br, sb + 1024 * (2 * wave + i), k0 + b_k[i] >= kb_rows ? kOOB : b_off[i], (uint32_t)k0 * (uint32_t)N);
     } else {
 #pragma unroll
       for (int i = 0; i < kDmaB; ++i)
@@ -183,7 +210,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   const float alpha = alpha_p ? *alpha_p : 1.0f;  // fetched before the K loop
 
   // One load (index idx of the wave's loads of a step) of K step kt into stage st.
-  constexpr int kNDma = BC ? kDmaA + 1 : kDmaStep;
+  constexpr int kNDma = BC ? kDmaA + 1 : BQ ? kDmaA + 2 : kDmaStep;
   auto issue_one = [&](int kt, int st, int idx) {
     const int k0 = kbeg + kt * kKStep;
     const uint32_t soff = (uint32_t)k0 * 2;
@@ -194,6 +221,9 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
             (uint32_t)k0 * a_soff_per_k);
     } else if constexpr (BC) {
       if (wave < 4) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
+    } else if constexpr (BQ) {
+      const int i = idx - kDmaA;
+      dma16(br, sb + 1024 * (2 * wave + i), k0 + b_k[i] >= kb_rows ? kOOB : b_off[i], (uint32_t)k0 * (uint32_t)N);
     } else {
       const int i = idx - kDmaA;
       dma16(br, sb + 1024 * (kDmaB * wave + i), ktail && k0 + b_k[i] >= kend ? kOOB : b_off[i],
@@ -221,6 +251,32 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       for (int j = 0; j < kNJ; ++j) wb[j] = *(const uint2*)(b + 16 * (wn0 + 32 * j + (lane & 31)) + 8 * (lane >> 5));
     }
   };
+  // BQ: the int8 B fragments of a whole step (8 transposed reads), read by rdq
+  // where rdc reads code words (the compiler would make these reads wait for
+  // every load in flight) and widened per slice.
+  v2i wq[BQ ? 4 : 1][kNJ];
+  auto rdq = [&](int st) {
+    if constexpr (BQ) {
+      const char* b = lds + st * kSt + kStageA;
+      const int g = lane >> 4, q = lane & 15;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int r = 16 * ks + 8 * (g >> 1) + (q >> 1);  // the K row this lane addresses
+#pragma unroll
+        for (int j = 0; j < kNJ; ++j) {
+          const int c = (wn0 + 32 * j + 16 * (g & 1)) >> 4;
+          const SBL_LDS char* pa = (const SBL_LDS char*)(b + r * kBNn + 16 * (c ^ (r & 7)) + 8 * (q & 1));
+          wq[ks][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SBL_LDS v2i*)pa);
+        }
+      }
+    }
+  };
+  auto cvtq = [&](int ks, int j, v8bf (&fb)[kNJ]) {
+    if constexpr (BQ) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fb[j][e] = (__bf16)(float)(signed char)(wq[ks][j][e >> 2] >> (8 * (e & 3)));
+    }
+  };
   auto rd = [&](int st, int ks, v8bf (&fa)[kMI], v8bf (&fb)[kNJ]) {
     const char* a = lds + st * kSt;
     const char* b = a + kStageA;
@@ -232,6 +288,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     if constexpr (BC) {
 #pragma unroll
       for (int j = 0; j < kNJ; ++j) fb[j] = widen_codes(ks < 2 ? wb[j].x : wb[j].y, 4 * (ks & 1));
+    } else if constexpr (BQ) {
+      // widened by cvtq, spread between the matrix instructions
     } else {
 #pragma unroll
       for (int j = 0; j < kNJ; ++j) {
@@ -246,6 +304,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // ds_read_b64_tr_b16 (lane i: 4 rows of column i each) and stores them as
   // one 16-byte run of AT row k0 + column.
   const int gn = (N + kBNn - 1) / kBNn;
+  __shared__ __attribute__((aligned(16))) float wsc[WTA ? kBM : 4];
   auto write_at = [&](int st, int k0) {
     const char* a = lds + st * kSt;
     const int kb = 16 * (wave & 3), tb0 = 128 * (wave >> 2);
@@ -264,8 +323,18 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       }
       const int col = kb + q;                           // this lane's K column
       const bool ok = k0 + col < K && m0 + t0 < at_ld;
-      const v4i v = __builtin_bit_cast(v4i, (v8s){part[0][0], part[0][1], part[0][2], part[0][3],
-                                                   part[1][0], part[1][1], part[1][2], part[1][3]});
+      v4i v = __builtin_bit_cast(v4i, (v8s){part[0][0], part[0][1], part[0][2], part[0][3],
+                                             part[1][0], part[1][1], part[1][2], part[1][3]});
+      if (wscale) {
+        const float4 s0 = *(const float4*)(wsc + t0), s1 = *(const float4*)(wsc + t0 + 4);
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float lo = __uint_as_float((uint32_t)v[u] << 16) * sv[2 * u];
+          const float hi = __uint_as_float((uint32_t)v[u] & 0xFFFF0000u) * sv[2 * u + 1];
+          v[u] = (int)cvt_pk_bf16(lo, hi);
+        }
+      }
       __builtin_amdgcn_raw_buffer_store_b128(v, atr, ok ? (uint32_t)((((m0 + t0) >> 3) * K + k0 + col) * 16) : kOOB,
                                              0, 0);
     }
@@ -282,11 +351,22 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       for (int j = 0; j < kNJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
   };
-  constexpr int kRdN = BC ? kMI : kMI + kNJ;  // LDS reads of a slice
-#define ORDER_SLICE(id)                                            \
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, id);              \
-  __builtin_amdgcn_sched_group_barrier(0x100, kRdN, id);           \
-  __builtin_amdgcn_sched_group_barrier(0x008, kMI * kNJ - 1, id);
+  constexpr int kRdN = BC || BQ ? kMI : kMI + kNJ;  // LDS reads of a slice
+// BQ: the widening of the next slice's B fragments (vector ALU) is spread
+// over the slice's matrix instructions, 5 instructions after each.
+#define ORDER_SLICE(id)                                              \
+  if constexpr (BQ) {                                                \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, id);              \
+    __builtin_amdgcn_sched_group_barrier(0x100, kRdN, id);           \
+    for (int z_ = 0; z_ < kMI * kNJ - 1; ++z_) {                     \
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, id);            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, id);            \
+    }                                                                \
+  } else {                                                           \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, id);              \
+    __builtin_amdgcn_sched_group_barrier(0x100, kRdN, id);           \
+    __builtin_amdgcn_sched_group_barrier(0x008, kMI * kNJ - 1, id);  \
+  }
 
   // Step k (stage k % 2 has landed; slice 0 is already in fa0/fb0): each of
   // the 4 slices is read while the previous one is multiplied.  Before the
@@ -297,31 +377,44 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // the redundant loads go to a stage nobody reads again.
   v8bf fa0[kMI], fb0[kNJ], fa1[kMI], fb1[kNJ];
   const int last = nk - 1;
+  if constexpr (WTA) {
+    // row scales of the side output (visible to all waves after the first barrier)
+    if (wscale && tid < kBM) wsc[tid] = m0 + tid < M ? wscale[m0 + tid] * (1.0f / 127.0f) : 0.0f;
+  }
   issue(0, 0);
   issue(min(1, last), 1);
-  if constexpr (BC) {
-    if (wave < 4) wait_vmcnt<kDmaA + 1>();
-    else wait_vmcnt<kDmaA>();
+  if constexpr (BC) {  // (lgkmcnt too: the scale table above is read after the barrier)
+    if (wave < 4) wait_vmcnt_lgkm0<kDmaA + 1>();
+    else wait_vmcnt_lgkm0<kDmaA>();
   } else {
-    wait_vmcnt<kDmaStep>();
+    wait_vmcnt<kNDma>();  // this wave's loads of step 0 (those of step 1 may be in flight)
   }
   barrier_only();
   if constexpr (WTA) {
     if (nt == 0) write_at(0, kbeg);
   }
   rdc(0);
+  rdq(0);
   rd(0, 0, fa0, fb0);
+#pragma unroll
+  for (int j = 0; j < kNJ; ++j) cvtq(0, j, fb0);
   int sc = 0;
   for (int k = 0; k < nk; ++k) {
     rd(sc, 1, fa1, fb1);
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) cvtq(1, j, fb1);
     mm(fa0, fb0);
     ORDER_SLICE(0)
     __builtin_amdgcn_sched_barrier(0);
     rd(sc, 2, fa0, fb0);
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) cvtq(2, j, fb0);
     mm(fa1, fb1);
     ORDER_SLICE(1)
     __builtin_amdgcn_sched_barrier(0);
     rd(sc, 3, fa1, fb1);
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) cvtq(3, j, fb1);
     mm(fa0, fb0);
     ORDER_SLICE(2)
     __builtin_amdgcn_sched_barrier(0);
@@ -339,6 +432,10 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       rdc(sc ^ 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (BQ) {
+      rdq(sc ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // Slice 3 (its fragments are in registers) restarts the matrix pipe right
     // after the barrier; the reads of slice 0 of step k + 1 and the loads of
     // step k + 2 go between its instructions, one load after each.
@@ -352,6 +449,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       if (t > 0) mm_one(t, fa1, fb1);
       __builtin_amdgcn_sched_barrier(0);
       if (t < kNDma) issue_one(kn, sc, t);
+      // BQ: slice 0's B widening in the last slots, when its reads have landed
+      if (t >= kMI * kNJ - kNJ) cvtq(0, t - (kMI * kNJ - kNJ), fb0);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -469,10 +568,10 @@ hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, 
   if (AT && splits != 1) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
   const bool f32 = out_dtype == SBL_F32;
-  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, false, false, false> : k_gemm_nt_bf16<SBL_BF16, true, false, false, false>)
-                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, false, false, false> : k_gemm_nt_bf16<SBL_BF16, false, false, false, false>);
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, false, false, false, false> : k_gemm_nt_bf16<SBL_BF16, true, false, false, false, false>)
+                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, false, false, false, false> : k_gemm_nt_bf16<SBL_BF16, false, false, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, B, (int)M, (int)N, (int)K, (int)k_per_split, alpha, C, AT,
-                     (int)at_ld);
+                     (int)at_ld, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -481,21 +580,38 @@ hipError_t launch_gemm_nt_runs(const uint16_t* A, bool a_runs, const uint16_t* B
   if (splits < 1) splits = 1;
   if (splits == 1) k_per_split = K;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
-  auto kern = a_runs ? k_gemm_nt_bf16<SBL_F32, false, false, true, true> : k_gemm_nt_bf16<SBL_F32, false, false, false, true>;
+  auto kern = a_runs ? k_gemm_nt_bf16<SBL_F32, false, false, true, true, false> : k_gemm_nt_bf16<SBL_F32, false, false, false, true, false>;
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, Brun, (int)M, (int)N, (int)K, (int)k_per_split, nullptr, C, nullptr,
-                     0);
+                     0, nullptr, 0);
+  return hipGetLastError();
+}
+
+bool gemm_nt_q_supported(int64_t M, int64_t N, int64_t K, int64_t kb_rows) {
+  // run-major A and int8 B are each one buffer resource (soffset = k0 * rows * 2, k0 * N)
+  return gemm_nt_bf16_supported(M, N, K) && K % 8 == 0 && N % 16 == 0 && (K / 8) * M * 16 <= kMaxRsrcBytes &&
+         kb_rows * N <= kMaxRsrcBytes && K * N <= kMaxRsrcBytes;
+}
+
+hipError_t launch_gemm_nt_q(const uint16_t* Arun, const int8_t* Bq, int64_t M, int64_t N, int64_t K, int64_t kb_rows,
+                            float* C, hipStream_t s, int splits, int64_t k_per_split) {
+  if (splits < 1) splits = 1;
+  if (splits == 1) k_per_split = K;
+  const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
+  hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32, false, false, true, false, true>), grid, block, 0, s, Arun,
+                     (const uint16_t*)Bq, (int)M, (int)N, (int)K, (int)k_per_split, nullptr, (void*)C, nullptr, 0,
+                     nullptr, (int)kb_rows);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_nt_codes(const uint16_t* A, const uint32_t* Bc, int64_t M, int64_t N, int64_t K,
                                 const float* alpha, void* C, int out_dtype, hipStream_t s, uint16_t* AT,
-                                int64_t at_ld) {
+                                int64_t at_ld, const float* wscale) {
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N)), block(kNT);
   const bool f32 = out_dtype == SBL_F32;
-  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, true, false, false> : k_gemm_nt_bf16<SBL_BF16, true, true, false, false>)
-                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, true, false, false> : k_gemm_nt_bf16<SBL_BF16, false, true, false, false>);
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, true, false, false, false> : k_gemm_nt_bf16<SBL_BF16, true, true, false, false, false>)
+                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, true, false, false, false> : k_gemm_nt_bf16<SBL_BF16, false, true, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, (const uint16_t*)Bc, (int)M, (int)N, (int)K, (int)K, alpha, C, AT,
-                     (int)at_ld);
+                     (int)at_ld, wscale, 0);
   return hipGetLastError();
 }
 

@@ -96,9 +96,18 @@ hipError_t launch_gemm_nt_runs(const uint16_t* A, bool a_runs, const uint16_t* B
 // The same product with B = W_eff^T given as the transposed 2-bit code plane of
 // k_codes_t (gemm_bwd.hip): Bc [N, K64 / 16] words, K64 = K rounded up to 64.
 // No split-K; AT as above.
+// wscale != nullptr (with AT): the side output is scaled per row m, AT[k, m] =
+// bf16(A[m, k] * wscale[m] * fl(1/127)).
 hipError_t launch_gemm_nt_codes(const uint16_t* A, const uint32_t* Bc, int64_t M, int64_t N, int64_t K,
                                 const float* alpha, void* C, int out_dtype, hipStream_t s, uint16_t* AT = nullptr,
-                                int64_t at_ld = 0);
+                                int64_t at_ld = 0, const float* wscale = nullptr);
+// The same product (float32 C, alpha = 1) with A run-major (as the scaled AT
+// side output above writes it) and B given as int8 rows along K: Bq[k, n] =
+// B[n, k], [kb_rows][N] row-major (rows kb_rows .. K read as zero), widened to
+// bf16 exactly in registers.  Only where gemm_nt_q_supported() holds.
+bool gemm_nt_q_supported(int64_t M, int64_t N, int64_t K, int64_t kb_rows);
+hipError_t launch_gemm_nt_q(const uint16_t* Arun, const int8_t* Bq, int64_t M, int64_t N, int64_t K, int64_t kb_rows,
+                            float* C, hipStream_t s, int splits = 1, int64_t k_per_split = 0);
 
 size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flags);
 hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
