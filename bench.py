@@ -194,9 +194,8 @@ def main():
     gemm_parts = {
         "fwd": ("forward_int8", "TOP/s", INT8_PEAK_TOPS, ["k_fwd_i8_direct<bf16>"]),
         "bwd": ("backward_bf16 (dX + dW)", "TFLOP/s", BF16_PEAK_TFLOPS,
-                ["k_codes_t", "k_gemm_nt_bf16<bf16, codes B, writes dY^T (scaled for the int8 form)>",
-                 "k_xt_bf16 (d_out > 2560)", "k_gemm_nt_bf16<f32, run-major A and B> (d_out > 2560)",
-                 "k_gemm_nt_bf16<f32, run-major A, int8 B> (d_out <= 2560)", "k_splitk_reduce (split-K shapes)"]),
+                ["k_codes_t", "k_gemm_nt_bf16<bf16, codes B, writes dY a/127 run-major>",
+                 "k_gemm_nt_bf16<f32, run-major A, int8 B>", "k_splitk_reduce (split-K shapes)"]),
     }
     dom = max(gemm_parts, key=lambda p: tot_ms[parts.index(p)])
     dname, dunit, dpeak, dkernels = gemm_parts[dom]

@@ -457,14 +457,11 @@ bool dw_direct(int64_t T, int64_t d_in, int64_t d_out) {
 }
 
 // dW on the int8 form: dW = (dY diag(a / 127))^T x_q, the scaled dY run-major
-// (written by the dX product, or by k_xt_bf16<true>), x_q read as it is.  It
-// saves the x~ pass (3 bytes per element of x) but its product, which widens
-// B in registers, runs about 12% longer than the bf16 one (measured on the 3B
-// shapes at 32768 tokens), so it is used only while the saved pass outweighs
-// that, i.e. for d_out up to about 2.7K (2560 here).
+// (written by the dX product, or by k_xt_bf16<true>), x_q read as it is: no x~
+// pass, and half the B bytes of the bf16 form.  Needs d_in % 16 == 0 (16-byte
+// rows of x_q); otherwise x~ is made run-major and the bf16 form runs.
 bool dw_q(int64_t T, int64_t d_in, int64_t d_out) {
-  return dw_direct(T, d_in, d_out) && d_out % 8 == 0 && d_out <= 2560 &&
-         gemm_nt_q_supported(d_out, d_in, round8(T), T);
+  return dw_direct(T, d_in, d_out) && d_out % 8 == 0 && gemm_nt_q_supported(d_out, d_in, round8(T), T);
 }
 
 // K splits for the plain GEMM engine (one 256 x 256 block per CU): pick S to

@@ -96,11 +96,13 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 // BQ: B is given as int8 rows along K, Bq[k, n] = B[n, k] row-major [K][N]
 // (N % 16 == 0; rows k >= kb_rows read as zero), and widened to bf16 in
 // registers (exact).  Its LDS stage holds the 64 K rows of a step x 256
-// columns, 16-byte chunks of row k at chunk position c ^ (k % 8); a B fragment
-// (8 consecutive k of one n) is one ds_read_b64_tr_b8: in each 16-lane group,
-// lane q addresses the 8 bytes of row q / 2 at columns 8 (q % 2) .. + 7 of a
-// block of 8 rows x 16 columns, and lane i receives column i of the 8 rows;
-// the swizzle puts those 8 rows in 8 different bank groups.
+// columns, 16-byte chunks of row k at chunk position c ^ (2 (k % 8)); a B
+// fragment (8 consecutive k of one n) is one ds_read_b64_tr_b8: in each
+// 16-lane group, lane q addresses the 8 bytes of row q / 2 at columns
+// 8 (q % 2) .. + 7 of a block of 8 rows x 16 columns, and lane i receives
+// column i of the 8 rows.  The swizzle spreads those 8 rows over 8 even (or,
+// for the odd chunk the neighbouring group reads, 8 odd) chunk positions, so
+// two groups never share a bank.
 template <int OUT, bool WTA, bool BC, bool AR, bool BR, bool BQ>
 __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B, int M, int N, int K,
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int p = 64 * (2 * wave + i) + lane;
-      const int r = p >> 4, c = (p & 15) ^ (r & 7);  // K row r, logical 16-column chunk c
+      const int r = p >> 4, c = (p & 15) ^ ((r & 7) << 1);  // K row r, logical 16-column chunk c
       b_off[i] = (uint32_t)(r * N + 16 * c);
       b_k[i] = r;
     }
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
 #pragma unroll
         for (int j = 0; j < kNJ; ++j) {
           const int c = (wn0 + 32 * j + 16 * (g & 1)) >> 4;
-          const SBL_LDS char* pa = (const SBL_LDS char*)(b + r * kBNn + 16 * (c ^ (r & 7)) + 8 * (q & 1));
+          const SBL_LDS char* pa = (const SBL_LDS char*)(b + r * kBNn + 16 * (c ^ ((r & 7) << 1)) + 8 * (q & 1));
           wq[ks][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SBL_LDS v2i*)pa);
         }
       }
@@ -273,8 +275,10 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   };
   auto cvtq = [&](int ks, int j, v8bf (&fb)[kNJ]) {
     if constexpr (BQ) {
+      const unsigned long long w = ((unsigned long long)(uint32_t)wq[ks][j][1] << 32) | (uint32_t)wq[ks][j][0];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) fb[j][e] = (__bf16)(float)(signed char)(wq[ks][j][e >> 2] >> (8 * (e & 3)));
+      for (int e = 0; e < 8; ++e)  // byte e: one sign-extending byte-select convert each
+        fb[j][e] = (__bf16)(float)(signed char)(w >> (8 * e));
     }
   };
   auto rd = [&](int st, int ks, v8bf (&fa)[kMI], v8bf (&fb)[kNJ]) {
