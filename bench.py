@@ -35,8 +35,8 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE, scale factors from a plain 1 GiB copy), averaged over the 7 linears; measured with
 # rocprofv3 --pmc for the backward kernel sources whose hash is given
 # (profiles/traffic_backward_3b_32768tok.md).
-BWD_TRAFFIC_BYTES = 3.24e9
-BWD_TRAFFIC_SRC_SHA = "dfe4e848e2f90971"
+BWD_TRAFFIC_BYTES = 2.49e9
+BWD_TRAFFIC_SRC_SHA = "e9fa6919ba0ca201"
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
