@@ -254,6 +254,9 @@ def _bwd_sources_sha() -> str:
     return h.hexdigest()[:16]
 
 
+DECODE_FUSE_MAX = 4_000_000  # element-quantizations per launch up to which sbl_decode beats two calls
+
+
 def run_decode(args, wl, copies: int = 16):
     """Decode workload: act quant + forward of every linear of a layer on pre-packed codes, for
     each token count and mask.  `copies` distinct packed copies of the layer (more bytes than
@@ -287,10 +290,18 @@ def run_decode(args, wl, copies: int = 16):
                                  a=torch.empty((T,), dtype=torch.float32, device=dev),
                                  y=torch.empty((T, L.d_out), dtype=torch.bfloat16, device=dev)))
 
+            # one fused launch (sbl_decode) where it applies and its per-block re-quantization
+            # of the T rows stays small (T * d_in * blocks of 16 rows), else act quant + forward
+            fused = [sbl.decode_supported(T, L.d_in) and T * L.d_in * -(-L.d_out // 16) <= DECODE_FUSE_MAX
+                     for L in wl.linears]
+
             def layer(mats):
-                for (L, codes, gamma), b in zip(mats, bufs):
-                    sbl.act_quant(b["x"], x_q=b["x_q"], absmax=b["a"])
-                    sbl.forward(codes, gamma, b["x_q"], b["a"], out_dtype=sbl.BF16, y=b["y"])
+                for (L, codes, gamma), b, fu in zip(mats, bufs, fused):
+                    if fu:
+                        sbl.decode(codes, gamma, b["x"], out_dtype=sbl.BF16, y=b["y"])
+                    else:
+                        sbl.act_quant(b["x"], x_q=b["x_q"], absmax=b["a"])
+                        sbl.forward(codes, gamma, b["x_q"], b["a"], out_dtype=sbl.BF16, y=b["y"])
 
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
@@ -315,7 +326,7 @@ def run_decode(args, wl, copies: int = 16):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / args.steps / copies
             io_bytes = sum(2 * T * L.d_in + 2 * T * L.d_out for L in wl.linears)
-            results.append({"T": T, "n_keep": n_keep, "us_per_layer": round(us, 3),
+            results.append({"T": T, "n_keep": n_keep, "us_per_layer": round(us, 3), "fused_linears": sum(fused),
                             "tokens_per_s": round(T / (us * 1e-6), 1),
                             "GBps": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9, 1),
                             "frac_hbm": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})

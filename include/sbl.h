@@ -157,20 +157,52 @@ SBL_API int sbl_act_quant(const uint16_t* x_bf16, int64_t T, int64_t d_in, int8_
 SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t* x_q, const float* absmax,
                         int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, void* hip_stream);
 
+/* Decode step: sbl_act_quant followed by sbl_forward in one launch, for
+ * decode-sized token counts ([SUM] Table 3, decode rows: the activation
+ * quantization and the product of one generated token batch).
+ *
+ *   absmax[t] = max_i |x[t, i]|,  x_q = round-half-even(127 x / absmax[t]),
+ *   y[t, o]   = (sum_i x_q[t, i] W_eff[o, i]) * gamma * absmax[t] / 127,
+ *
+ * with x_q, absmax and the int32 sums bit-identical to the two-call path
+ * (the quantization runs the same arithmetic), so y is too.  x_q and absmax
+ * are not written.
+ *
+ * codes, gamma : from sbl_quant_mask_pack for W [d_out, d_in].
+ * x_bf16       : [T, d_in] bf16 bits.
+ * y            : [T, d_out] of y_dtype: SBL_F32, SBL_BF16 or SBL_I32.
+ * Supported (sbl_decode_supported): 1 <= T <= 16, d_in % 64 == 0,
+ * d_in <= 8192 and T * (d_in + 16) <= 49152 (the int8 tile each block keeps
+ * in LDS); other shapes return SBL_ERR_UNSUPPORTED and enqueue nothing (use
+ * sbl_act_quant + sbl_forward).  T = 0 is a no-op.
+ * Cost: every block of 16 output rows quantizes all T rows itself (there is
+ * no cross-block step), so the saving of one launch (a few us) is worth it
+ * while T * d_in * ceil(d_out / 16) stays below a few million; past that the
+ * two-call path is faster (measured: 11008 x 2048 at T = 8, 12.8 against
+ * 10.7 us).
+ */
+SBL_API int sbl_decode(const uint16_t* codes, const float* gamma, const uint16_t* x_bf16, int64_t T, int64_t d_in,
+                       int64_t d_out, void* y, int y_dtype, void* hip_stream);
+
+/* 1 if sbl_decode takes this (T, d_in), else 0. */
+SBL_API int sbl_decode_supported(int64_t T, int64_t d_in);
+
 /* ------------------------------------------------------------------------ */
 /* Backward (Dual STE)                                                        */
 /* ------------------------------------------------------------------------ */
 
 /* Bytes of workspace sbl_backward needs for these flags.  It holds the
- * per-call operand copies of the matrix-core path -- W_eff^T as bf16
- * ([d_in, d_out], for dX), dY^T and x~^T as bf16 ([d_out, T8] and
- * [d_in, T8] with T8 = T rounded up to 8, for dW) -- and split-K partial sums
- * of dW.  With SBL_BWD_DX | SBL_BWD_DW on shapes that take the matrix-core
- * path for both, the dX product also writes dY^T into the workspace, which
- * the dW product then reads, so that region is kept from one to the other and
- * W_eff^T shares space with x~^T only; otherwise the dX and dW parts are used
- * one after the other and share the space.  0 when nothing is needed (e.g.
- * T = 0). */
+ * per-call operands of the matrix-core path, in private layouts: the code
+ * plane transposed for the dX product (2 bits per weight, d_in rows of d_out
+ * rounded up to 64); dY^T in bf16, run-major ([T8 / 8][d_out][8] with T8 = T
+ * rounded up to 8), for the dW product: scaled to bf16(dY[t, o] absmax[t] /
+ * 127) when that product reads x_q as it is (d_in % 16 == 0), else unscaled
+ * next to x~ = bf16(x_q absmax / 127) in the same run-major form; and split-K
+ * partial sums of dW (float32, one [d_out, d_in] slice per split).  With
+ * SBL_BWD_DX | SBL_BWD_DW on shapes that take the matrix-core path for both,
+ * the dX product writes dY^T while it runs and the dW product reads it;
+ * otherwise dW makes it itself.  Shapes off the matrix-core path need at most
+ * the split-K partials.  0 when nothing is needed (e.g. T = 0). */
 SBL_API size_t sbl_backward_workspace_size(int64_t T, int64_t d_in, int64_t d_out, int flags);
 
 /* Dual-STE backward ([SUM] 前置知识 > Straight-Through Estimator (STE);

@@ -44,6 +44,8 @@ _SIGNATURES = {
     "sbl_quant_mask_pack": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "sbl_act_quant": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "sbl_forward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
+    "sbl_decode": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
+    "sbl_decode_supported": (_c_int, [_c_i64, _c_i64]),
     "sbl_backward_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int]),
     "sbl_backward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int,
                               _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr]),
@@ -67,7 +69,7 @@ class SblError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m sparsity_sparse_bitlinear_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python sparsity_sparse_bitlinear_amd/build.py` "
             "(hipcc for gfx950).  There is no fallback implementation.")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
@@ -192,6 +194,32 @@ def forward(codes: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax:
     _out(y, (T, d_out), (_OUT_TORCH[out_dtype],), x_q.device, "y")
     _check(lib.sbl_forward(_ptr(codes), _ptr(gamma), _ptr(x_q), _ptr(absmax), T, d_in, d_out, _ptr(y),
                            int(out_dtype), _stream(stream)), "sbl_forward")
+    return y
+
+
+def decode_supported(T: int, d_in: int) -> bool:
+    """True if ``decode`` takes this token count and input width."""
+    return bool(lib.sbl_decode_supported(int(T), int(d_in)))
+
+
+def decode(codes: torch.Tensor, gamma: torch.Tensor, x: torch.Tensor, *, out_dtype: int = F32,
+           y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """act_quant + forward in one launch for decode-sized T (see ``decode_supported``): same bits as the two calls."""
+    for t, n in ((codes, "codes"), (gamma, "gamma"), (x, "x")):
+        _dev(t, n)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    d_out, G = codes.shape
+    T, d_in = x.shape
+    if G * 8 != d_in:
+        raise ValueError(f"codes [{d_out}, {G}] do not match x [{T}, {d_in}]")
+    if out_dtype not in _OUT_TORCH:
+        raise ValueError(f"unknown out_dtype {out_dtype}")
+    if y is None:
+        y = torch.empty((T, d_out), dtype=_OUT_TORCH[out_dtype], device=x.device)
+    _out(y, (T, d_out), (_OUT_TORCH[out_dtype],), x.device, "y")
+    _check(lib.sbl_decode(_ptr(codes), _ptr(gamma), _ptr(x), T, d_in, d_out, _ptr(y), int(out_dtype),
+                          _stream(stream)), "sbl_decode")
     return y
 
 

@@ -1,54 +1,15 @@
-// Per-token absmax int8 activation quantization on gfx950.
-//
-// [SUM] 前置知识 > 1.58-bit BitNet 量化 (activations absmax-quantized to
-// 8-bit integers) and 方法步骤详情 step (3):
-//   a_t = max_i |x[t,i]|,  x_q[t,i] = round-half-even(127 x[t,i] / a_t).
+// Per-token absmax int8 activation quantization on gfx950 ([SUM] 前置知识 >
+// 1.58-bit BitNet 量化; 方法步骤详情 step (3)); the per-element arithmetic is in
+// act_common.h.
 //
 // One wavefront per token row: the row is held in registers (up to NC 16-byte
 // chunks per lane), the maximum is a wave reduction on the 15-bit magnitude
 // bits (integer order equals magnitude order for finite bf16), then every
 // element is quantized from registers.  Rows longer than 64*NC chunks re-read
 // the remainder.
-//
-// Binary32 evaluation: x and a are first scaled by the same exact power of two
-// so that a lands in [1, 2) (this keeps 127*x finite and a normal), then
-// q = rint(fl(fl(127 x') / a')).  For bf16 inputs the exact quotient is either a
-// half-integer or at least 2^-17 (relative) away from one, so the single
-// binary32 rounding of the division cannot change the rounded integer: the
-// result equals the exact round-half-even of 127 x / a.
-#include "sbl_internal.h"
+#include "act_common.h"
 
 namespace sbl {
-
-__device__ __forceinline__ uint32_t max_mag2(uint32_t w) {
-  return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
-}
-
-// Fast path: qf = fl(x' * fl(127 / a')) differs from the exact quotient
-// q = 127 x' / a' by less than |q| 2^-23 <= 2^-16 (|q| <= 127).  When qf is
-// more than 2^-14 away from a half-integer, rint(qf) is therefore the integer
-// nearest to q; otherwise (ties included) the element takes the division path,
-// which is exact as stated above.
-__device__ __forceinline__ int quant_one(uint32_t h16, int k, float as, float c) {
-  const float xs = ldexpf(__uint_as_float(h16 << 16), k);
-  const float qf = xs * c;
-  float r = rintf(qf);
-  if (__builtin_expect(fabsf(qf - r) > 0.5f - 0x1p-14f, 0)) r = rintf((127.0f * xs) / as);
-  return (int)r;
-}
-
-__device__ __forceinline__ uint32_t quant_word_pair(uint32_t w0, uint32_t w1, int k, float as, float c) {
-  const int q0 = quant_one(w0 & 0xFFFFu, k, as, c);
-  const int q1 = quant_one(w0 >> 16, k, as, c);
-  const int q2 = quant_one(w1 & 0xFFFFu, k, as, c);
-  const int q3 = quant_one(w1 >> 16, k, as, c);
-  return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
-         ((uint32_t)(q3 & 0xFF) << 24);
-}
-
-__device__ __forceinline__ uint2 quant_chunk(uint4 v, int k, float as, float c) {
-  return make_uint2(quant_word_pair(v.x, v.y, k, as, c), quant_word_pair(v.z, v.w, k, as, c));
-}
 
 // WPR waves per row (1: four rows per block of 256 threads; 4: one row per
 // block, for long rows); each lane keeps NC 16-byte chunks of its row in
@@ -97,11 +58,9 @@ __global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ 
     for (int idx = lane; idx < nch; idx += kR) out[idx] = make_uint2(0, 0);
     return;
   }
-  int e;
-  (void)frexpf(a, &e);  // a = f * 2^e, f in [0.5, 1)
-  const int k = 1 - e;  // a * 2^k in [1, 2)
-  const float as = ldexpf(a, k);
-  const float c127 = 127.0f / as;
+  const ActScale sc = act_scale(a);
+  const int k = sc.k;
+  const float as = sc.as, c127 = sc.c;
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int idx = lane + kR * c;

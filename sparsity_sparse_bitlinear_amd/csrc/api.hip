@@ -130,6 +130,30 @@ SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t*
   return SBL_OK;
 }
 
+SBL_API int sbl_decode_supported(int64_t T, int64_t d_in) { return decode_fused_supported(T, d_in) ? 1 : 0; }
+
+SBL_API int sbl_decode(const uint16_t* codes, const float* gamma, const uint16_t* x_bf16, int64_t T, int64_t d_in,
+                       int64_t d_out, void* y, int y_dtype, void* hip_stream) {
+  int rc = check_tokens(T);
+  if (rc != SBL_OK) return rc;
+  rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(y_dtype == SBL_F32 || y_dtype == SBL_BF16 || y_dtype == SBL_I32, SBL_ERR_INVALID_ARG,
+              "y_dtype=%d is not SBL_F32, SBL_BF16 or SBL_I32", y_dtype);
+  if (T == 0) return SBL_OK;
+  SBL_REQUIRE(decode_fused_supported(T, d_in), SBL_ERR_UNSUPPORTED,
+              "sbl_decode takes 1 <= T <= 16, d_in %% 64 == 0, d_in <= 8192, T * (d_in + 16) <= 49152 "
+              "(got T=%lld, d_in=%lld); "
+              "use sbl_act_quant + sbl_forward",
+              (long long)T, (long long)d_in);
+  SBL_REQUIRE(codes && gamma && x_bf16 && y, SBL_ERR_INVALID_ARG, "NULL pointer argument");
+  SBL_REQUIRE(aligned(codes, 16) && aligned(x_bf16, 16) && aligned(y, 16) && aligned(gamma, 4), SBL_ERR_INVALID_ARG,
+              "codes, x, y must be 16-byte aligned; gamma 4-byte aligned");
+  hipError_t e = launch_decode_fused(codes, gamma, x_bf16, T, d_in, d_out, y, y_dtype, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_decode launch");
+  return SBL_OK;
+}
+
 SBL_API size_t sbl_backward_workspace_size(int64_t T, int64_t d_in, int64_t d_out, int flags) {
   if (check_tokens(T) != SBL_OK || check_dims(d_out, d_in) != SBL_OK) return 0;
   return backward_workspace_bytes(T, d_in, d_out, flags);

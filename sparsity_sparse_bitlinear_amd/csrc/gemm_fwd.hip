@@ -18,6 +18,7 @@
 #include <algorithm>
 
 #include "gemm_common.h"
+#include "act_common.h"
 
 namespace sbl {
 
@@ -528,32 +529,100 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
 // ---------------------------------------------------------------------------
 // Decode forward (T <= 64, d_in % 64 == 0): the code plane is streamed once and
 // every weight meets at most 64 tokens, so the kernel is bound by the code
-// bytes, not by the matrix cores.  A block owns 16 output rows; its 4 waves
-// split the K range and each runs v_mfma_i32_16x16x64_i8 with the expanded
-// code words as the first operand (lane l: row l % 16, k 16 (l / 16) + 0..15,
-// one 32-bit word of 16 codes) and up to 4 tiles of 16 tokens as the second
-// (x_q rows past T read as zero).  Accumulator register r of lane l then holds
-// C[t = l % 16][o = 4 (l / 16) + r].  The 4 partial sums are added in LDS in a
-// fixed order (integers: exact) and scaled as in the large-T kernels.
+// bytes and, at these sizes, by the latency of one round of loads, not by the
+// matrix cores.  A block owns 16 output rows; its W waves split the K range
+// (all of a wave's loads are issued before its first product) and each runs
+// v_mfma_i32_16x16x64_i8 with the expanded code words as the first operand
+// (lane l: row l % 16, k 16 (l / 16) + 0..15, one 32-bit word of 16 codes) and
+// up to 4 tiles of 16 tokens as the second (rows past T read as zero).
+// Accumulator register r of lane l then holds C[t = l % 16][o = 4 (l / 16) + r].
+// The W partial sums are added in LDS in a fixed order (integers: exact) and
+// scaled as in the large-T kernels.
 // ---------------------------------------------------------------------------
 constexpr int kDecRows = 16;
-constexpr int kDecWaves = 4;
+constexpr int kDecSteps = 8;  // 64-wide K steps per wave whose loads are all in flight at once (one token tile)
 
-template <int NTT, int OUT>
-__global__ __launch_bounds__(64 * kDecWaves) void k_fwd_decode(const int8_t* __restrict__ xq,
-                                                              const uint16_t* __restrict__ codes,
-                                                              const float* __restrict__ gamma_p,
-                                                              const float* __restrict__ absmax, int T, int d_in,
-                                                              int d_out, void* __restrict__ y) {
-  constexpr int kDecUnroll = 4;  // k steps in flight per wave
-  __shared__ int red[kDecWaves - 1][NTT][4][64];
+// K steps in flight per wave for NTT token tiles (register budget of 16-wave blocks).
+template <int NTT>
+constexpr int dec_steps() { return NTT == 1 ? kDecSteps : kDecSteps / 2; }
+
+// Waves per block: 8 while the grid stays within about 4096 waves, else 4,
+// and at least min_w.  Measured on the decode shapes (16 packed copies per
+// graph): 16-wave blocks were slower everywhere (q at 64 tokens 13.1 us
+// against 11.4 with 8), 8 beat 4 on the 128-block grids (down at one token
+// 13.6 against 14.4 us), 4 and 8 tie on the 688-block grids.
+inline int decode_waves(int64_t nblocks, int min_w) {
+  const int w = nblocks * 8 <= 4096 ? 8 : 4;
+  return w < min_w ? min_w : w;
+}
+
+// Sum of the W waves' accumulators (wave 0 keeps the total) and the scaled
+// store of rows o0 .. o0 + 15; sc[tt] is the scale of this lane's token
+// 16 tt + l % 16.
+template <int NTT, int OUT, int W>
+__device__ __forceinline__ void decode_store(v4i (&acc)[NTT], int (*red)[NTT][4][64], int wave, int lane, int o0,
+                                             int T, int d_out, const float (&sc)[NTT], void* __restrict__ y) {
+  if (wave > 0) {
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave - 1][tt][r][lane] = acc[tt][r];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll 1
+  for (int w = 0; w < W - 1; ++w)
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[tt][r] += red[w][tt][r][lane];
+
+  const int q = lane >> 4, r16 = lane & 15;
+  const bool vec_out = (d_out & 3) == 0;
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    const int t = 16 * tt + r16;
+    const int o = o0 + 4 * q;
+    if (t >= T || o >= d_out) continue;
+    const float s = sc[tt];
+    const int64_t off = (int64_t)t * d_out + o;
+    const int a0 = acc[tt][0], a1 = acc[tt][1], a2 = acc[tt][2], a3 = acc[tt][3];
+    if (vec_out && o + 4 <= d_out) {
+      if constexpr (OUT == SBL_I32) {
+        *(int4*)((int*)y + off) = make_int4(a0, a1, a2, a3);
+      } else if constexpr (OUT == SBL_F32) {
+        *(float4*)((float*)y + off) = make_float4((float)a0 * s, (float)a1 * s, (float)a2 * s, (float)a3 * s);
+      } else {
+        *(uint2*)((__bf16*)y + off) =
+            make_uint2(cvt_pk_bf16((float)a0 * s, (float)a1 * s), cvt_pk_bf16((float)a2 * s, (float)a3 * s));
+      }
+    } else {
+      const int av[4] = {a0, a1, a2, a3};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (o + u >= d_out) break;
+        if constexpr (OUT == SBL_I32) ((int*)y)[off + u] = av[u];
+        else if constexpr (OUT == SBL_F32) ((float*)y)[off + u] = (float)av[u] * s;
+        else ((__bf16*)y)[off + u] = (__bf16)((float)av[u] * s);
+      }
+    }
+  }
+}
+
+template <int NTT, int OUT, int W>
+__global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict__ xq,
+                                                       const uint16_t* __restrict__ codes,
+                                                       const float* __restrict__ gamma_p,
+                                                       const float* __restrict__ absmax, int T, int d_in,
+                                                       int d_out, void* __restrict__ y) {
+  __shared__ int red[W - 1][NTT][4][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int o0 = blockIdx.x * kDecRows;
   const int G = d_in >> 3;
   const int nks = d_in >> 6;
-  const int per = (nks + kDecWaves - 1) / kDecWaves;
+  const int per = (nks + W - 1) / W;
   const int s_begin = wave * per, s_end = min(nks, s_begin + per);
   const int rows = min(kDecRows, d_out - o0);
   const auto br = make_rsrc(codes + (int64_t)o0 * G, clamp_bytes((int64_t)rows * G * 2));
@@ -567,90 +636,166 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_fwd_decode(const int8_t* __r
   v4i acc[NTT];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) acc[tt] = (v4i){0, 0, 0, 0};
-  for (int s0 = s_begin; s0 < s_end; s0 += kDecUnroll) {
-    uint32_t wb[kDecUnroll];
-    v4i fx[kDecUnroll][NTT];
+  constexpr int kS = dec_steps<NTT>();
+  for (int s0 = s_begin; s0 < s_end; s0 += kS) {
+    uint32_t wb[kS];
+    v4i fx[kS][NTT];
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
+    for (int u = 0; u < kS; ++u) {
       const bool ok = s0 + u < s_end;
       wb[u] = bload4(br, ok ? b_off + (uint32_t)(s0 + u) * 16 : kOOB);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
         fx[u][tt] = __builtin_bit_cast(v4i, bload16(xr, ok ? x_off[tt] + (uint32_t)(s0 + u) * 64 : kOOB));
     }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the round is issued before the first product
+    // Steps past the wave's range multiply zeros (their loads were out of
+    // range); no early exit, which would let the compiler sink each load to
+    // its use and serialize the round trips.
 #pragma unroll
-    for (int u = 0; u < kDecUnroll; ++u) {
+    for (int u = 0; u < kS; ++u) {
       const v4i fb = __builtin_bit_cast(v4i, expand16(wb[u]));
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt) acc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb, fx[u][tt], acc[tt], 0, 0, 0);
     }
   }
-  if (wave > 0) {
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave - 1][tt][r][lane] = acc[tt][r];
-  }
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll 1
-  for (int w = 0; w < kDecWaves - 1; ++w)
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[tt][r] += red[w][tt][r][lane];
-
   const float g127 = *gamma_p * (1.0f / 127.0f);
-  const bool vec_out = (d_out & 3) == 0;
+  float sc[NTT];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) {
     const int t = 16 * tt + r16;
-    const int o = o0 + 4 * q;
-    if (t >= T || o >= d_out) continue;
-    const float sc = g127 * absmax[t];
-    const int64_t off = (int64_t)t * d_out + o;
-    const int a0 = acc[tt][0], a1 = acc[tt][1], a2 = acc[tt][2], a3 = acc[tt][3];
-    if (vec_out && o + 4 <= d_out) {
-      if constexpr (OUT == SBL_I32) {
-        *(int4*)((int*)y + off) = make_int4(a0, a1, a2, a3);
-      } else if constexpr (OUT == SBL_F32) {
-        *(float4*)((float*)y + off) = make_float4((float)a0 * sc, (float)a1 * sc, (float)a2 * sc, (float)a3 * sc);
-      } else {
-        *(uint2*)((__bf16*)y + off) =
-            make_uint2(cvt_pk_bf16((float)a0 * sc, (float)a1 * sc), cvt_pk_bf16((float)a2 * sc, (float)a3 * sc));
-      }
-    } else {
-      const int av[4] = {a0, a1, a2, a3};
+    sc[tt] = t < T ? g127 * absmax[t] : 0.0f;
+  }
+  decode_store<NTT, OUT, W>(acc, red, wave, lane, o0, T, d_out, sc, y);
+}
+
+// Decode with the activation quantization fused in.  Each block quantizes the
+// T bf16 rows of x once into an int8 tile in LDS (every block covers all of K,
+// so it sees whole rows): wave w (W >= T) owns token w, reads its row with all
+// 64 lanes (16-byte chunks kept in registers), takes the row maximum by a wave
+// reduction, quantizes the chunks with the same arithmetic as k_act_quant and
+// stores them; after one barrier the product reads its x_q operands from the
+// tile.  x_q and a_t are therefore bit-identical to the
+// two-call path, and so are the int32 sums and y.  The first round of code
+// loads is issued before the quantization, so it overlaps it.
+constexpr int kFuseWaves = 16;        // most waves per block
+constexpr int kFuseChunks = 16;       // 16-byte x chunks per lane in registers
+constexpr int kFuseLdsBytes = 49152;  // int8 tile T x (d_in + 16)
+
+// Smallest wave count (4, 8, 16) with a wave per token, or 0 if T or the row
+// length does not fit.
+inline int decode_fused_min_waves(int64_t T, int64_t d_in) {
+  if ((d_in / 8 + 63) / 64 > kFuseChunks) return 0;
+  for (int w = 4; w <= kFuseWaves; w *= 2)
+    if (T <= w) return w;
+  return 0;
+}
+
+template <int OUT, int W>
+__global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ codes,
+                                                         const float* __restrict__ gamma_p, int T, int d_in,
+                                                         int d_out, void* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) char xs[];  // [T][d_in + 16] int8
+  __shared__ int red[W - 1][1][4][64];
+  __shared__ float amax[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int o0 = blockIdx.x * kDecRows;
+  const int G = d_in >> 3;
+  const int nks = d_in >> 6;
+  const int ld = d_in + 16;  // tile row stride: rows 16 bytes apart shift the banks
+  const int per = (nks + W - 1) / W;
+  const int s_begin = wave * per, s_end = min(nks, s_begin + per);
+  const int rows = min(kDecRows, d_out - o0);
+  const auto br = make_rsrc(codes + (int64_t)o0 * G, clamp_bytes((int64_t)rows * G * 2));
+  const int q = lane >> 4, r16 = lane & 15;
+  const uint32_t b_off = (uint32_t)(r16 * G * 2 + 4 * q);
+
+  // first round of code words
+  uint32_t wb[kDecSteps];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (o + u >= d_out) break;
-        if constexpr (OUT == SBL_I32) ((int*)y)[off + u] = av[u];
-        else if constexpr (OUT == SBL_F32) ((float*)y)[off + u] = (float)av[u] * sc;
-        else ((__bf16*)y)[off + u] = (__bf16)((float)av[u] * sc);
-      }
+  for (int u = 0; u < kDecSteps; ++u)
+    wb[u] = bload4(br, s_begin + u < s_end ? b_off + (uint32_t)(s_begin + u) * 16 : kOOB);
+
+  // this wave's row of x, whole, in registers (chunk j: lane j % 64, slot j / 64)
+  const int nch = d_in >> 3;
+  const int t = wave;
+  const auto xr = make_rsrc(x, clamp_bytes((int64_t)T * d_in * 2));
+  uint4 xv[kFuseChunks];
+#pragma unroll
+  for (int i = 0; i < kFuseChunks; ++i) {
+    const int j = lane + 64 * i;
+    xv[i] = bload16(xr, t < T && j < nch ? (uint32_t)((t * d_in + 8 * j) * 2) : kOOB);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
+  if (t < T) {  // wave-uniform
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < kFuseChunks; ++i)
+      m = max(m, max(max(max_mag2(xv[i].x), max_mag2(xv[i].y)), max(max_mag2(xv[i].z), max_mag2(xv[i].w))));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    if (lane == 0) amax[t] = __uint_as_float(m << 16);
+    const ActScale qs = act_scale(m ? __uint_as_float(m << 16) : 1.0f);
+#pragma unroll
+    for (int i = 0; i < kFuseChunks; ++i) {
+      const int j = lane + 64 * i;
+      if (j < nch) *(uint2*)(xs + t * ld + 8 * j) = m ? quant_chunk(xv[i], qs.k, qs.as, qs.c) : make_uint2(0u, 0u);
     }
   }
+  __syncthreads();  // tile and row maxima complete
+
+  const bool tok = r16 < T;
+  const char* xrow = xs + (tok ? r16 : 0) * ld + 16 * q;
+  v4i acc[1] = {(v4i){0, 0, 0, 0}};
+  for (int s0 = s_begin; s0 < s_end; s0 += kDecSteps) {
+    if (s0 != s_begin) {
+#pragma unroll
+      for (int u = 0; u < kDecSteps; ++u) wb[u] = bload4(br, s0 + u < s_end ? b_off + (uint32_t)(s0 + u) * 16 : kOOB);
+    }
+#pragma unroll
+    for (int u = 0; u < kDecSteps; ++u) {
+      if (s0 + u >= s_end) break;  // wave-uniform; the code words are already in registers
+      const v4i fb = __builtin_bit_cast(v4i, expand16(wb[u]));
+      const v4i fx = tok ? *(const v4i*)(xrow + 64 * (s0 + u)) : (v4i){0, 0, 0, 0};
+      acc[0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb, fx, acc[0], 0, 0, 0);
+    }
+  }
+  const float sc[1] = {tok ? *gamma_p * (1.0f / 127.0f) * amax[r16] : 0.0f};
+  decode_store<1, OUT, W>(acc, red, wave, lane, o0, T, d_out, sc, y);
+}
+
+template <int NTT, int W>
+hipError_t launch_decode_w(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax, int64_t T,
+                           int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
+  const dim3 grid((unsigned)((d_out + kDecRows - 1) / kDecRows)), block(64 * W);
+  switch (y_dtype) {
+    case SBL_F32:
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_F32, W>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+                         (int)d_in, (int)d_out, y);
+      break;
+    case SBL_BF16:
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_BF16, W>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+                         (int)d_in, (int)d_out, y);
+      break;
+    default:
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_I32, W>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+                         (int)d_in, (int)d_out, y);
+      break;
+  }
+  return hipGetLastError();
 }
 
 template <int NTT>
 hipError_t launch_decode(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax, int64_t T,
                          int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
-  const dim3 grid((unsigned)((d_out + kDecRows - 1) / kDecRows)), block(64 * kDecWaves);
-  switch (y_dtype) {
-    case SBL_F32:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_F32>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T, (int)d_in,
-                         (int)d_out, y);
-      break;
-    case SBL_BF16:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_BF16>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
-                         (int)d_in, (int)d_out, y);
-      break;
-    default:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_I32>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T, (int)d_in,
-                         (int)d_out, y);
-      break;
+  switch (decode_waves((d_out + kDecRows - 1) / kDecRows, 4)) {
+    case 16: return launch_decode_w<NTT, 16>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
+    case 8: return launch_decode_w<NTT, 8>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
+    default: return launch_decode_w<NTT, 4>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
   }
-  return hipGetLastError();
 }
 
 template <bool VEC>
@@ -721,6 +866,42 @@ hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_
   }
   if (d_in % 64 == 0) return launch_fwd_v<true>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
   return launch_fwd_v<false>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
+}
+
+bool decode_fused_supported(int64_t T, int64_t d_in) {
+  return T >= 1 && T <= 16 && d_in % 64 == 0 && d_in <= 8192 && T * (d_in + 16) <= kFuseLdsBytes &&
+         decode_fused_min_waves(T, d_in) > 0;
+}
+
+template <int W>
+hipError_t launch_decode_fused_w(const uint16_t* codes, const float* gamma, const uint16_t* x, int64_t T,
+                                 int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
+  const dim3 grid((unsigned)((d_out + kDecRows - 1) / kDecRows)), block(64 * W);
+  const size_t lds = (size_t)T * (size_t)(d_in + 16);
+  switch (y_dtype) {
+    case SBL_F32:
+      hipLaunchKernelGGL((k_decode_fused<SBL_F32, W>), grid, block, lds, s, x, codes, gamma, (int)T, (int)d_in,
+                         (int)d_out, y);
+      break;
+    case SBL_BF16:
+      hipLaunchKernelGGL((k_decode_fused<SBL_BF16, W>), grid, block, lds, s, x, codes, gamma, (int)T, (int)d_in,
+                         (int)d_out, y);
+      break;
+    default:
+      hipLaunchKernelGGL((k_decode_fused<SBL_I32, W>), grid, block, lds, s, x, codes, gamma, (int)T, (int)d_in,
+                         (int)d_out, y);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_fused(const uint16_t* codes, const float* gamma, const uint16_t* x, int64_t T, int64_t d_in,
+                               int64_t d_out, void* y, int y_dtype, hipStream_t s) {
+  switch (decode_waves((d_out + kDecRows - 1) / kDecRows, decode_fused_min_waves(T, d_in))) {
+    case 16: return launch_decode_fused_w<16>(codes, gamma, x, T, d_in, d_out, y, y_dtype, s);
+    case 8: return launch_decode_fused_w<8>(codes, gamma, x, T, d_in, d_out, y, y_dtype, s);
+    default: return launch_decode_fused_w<4>(codes, gamma, x, T, d_in, d_out, y, y_dtype, s);
+  }
 }
 
 }  // namespace sbl

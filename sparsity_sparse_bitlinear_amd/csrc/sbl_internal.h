@@ -72,6 +72,10 @@ int device_cus();
 
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s);
+// Decode with the activation quantization fused in (x given as bf16).
+bool decode_fused_supported(int64_t T, int64_t d_in);
+hipError_t launch_decode_fused(const uint16_t* codes, const float* gamma, const uint16_t* x, int64_t T, int64_t d_in,
+                               int64_t d_out, void* y, int y_dtype, hipStream_t s);
 
 // C[M, N] = alpha * A[M, K] B[N, K]^T, bf16 operands, float32 or bf16 output
 // (gemm_nt.hip).  Only for shapes where gemm_nt_bf16_supported() holds.

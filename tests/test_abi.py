@@ -81,6 +81,23 @@ def test_forward_validation():
     assert f(P, P, P, P, 4, 256, 256, P_MIS, 0, NULL) == INVALID
 
 
+def test_decode_validation():
+    f = lib.sbl_decode
+    assert f(NULL, NULL, NULL, 0, 256, 256, NULL, 0, NULL) == OK                 # T = 0: no-op
+    assert f(P, P, P, 4, 256, 256, P, 7, NULL) == INVALID                       # bad dtype
+    assert f(P, P, P, 4, 250, 256, P, 0, NULL) == SHAPE                         # d_in % 8
+    assert f(P, P, P, 17, 256, 256, P, 0, NULL) == UNSUPPORTED                  # T > 16
+    assert f(P, P, P, 4, 264, 256, P, 0, NULL) == UNSUPPORTED                   # d_in % 64
+    assert f(P, P, P, 4, 8256, 256, P, 0, NULL) == UNSUPPORTED                  # d_in > 8192
+    assert f(P, P, NULL, 4, 256, 256, P, 0, NULL) == INVALID
+    assert f(P, P, P_MIS, 4, 256, 256, P, 0, NULL) == INVALID
+    assert f(P, P, P, 8, 8192, 256, P, 0, NULL) == UNSUPPORTED                  # tile over 48 KB
+    s = lib.sbl_decode_supported
+    assert s(1, 64) == 1 and s(1, 8192) == 1 and s(5, 8192) == 1 and s(16, 3008) == 1
+    assert s(0, 64) == 0 and s(17, 64) == 0 and s(8, 96) == 0 and s(1, 8256) == 0
+    assert s(6, 8192) == 0 and s(16, 3072) == 0
+
+
 def test_backward_validation():
     f = lib.sbl_backward
     # dX: the transposed 2-bit code plane (d_in rows of d_out rounded up to 64,

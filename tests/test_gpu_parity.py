@@ -220,6 +220,76 @@ def test_decode_full_size(T, name, d_out, d_in):
     np.testing.assert_array_equal(acc, acc_ref)
 
 
+# Fused decode (sbl_decode: act quant + forward in one launch, T <= 16): the
+# same x_q and int32 sums as the two-call path, so every output is identical
+# to it, and it matches the oracle.
+@pytest.mark.parametrize("n", [6, 2])
+@pytest.mark.parametrize("d_out,d_in", [(256, 2048), (130, 448), (2050, 640), (7, 64), (40, 2944)])
+@pytest.mark.parametrize("T", [1, 3, 8, 16])
+def test_decode_fused_parity(T, d_out, d_in, n):
+    W = weight(63, d_out + d_in, d_out, d_in)
+    x = activation(63, d_out + d_in + T, T, d_in, dist="student_t4")
+    assert sbl.decode_supported(T, d_in)
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), n)
+    xd = to_dev_bf16(x)
+    acc_ref, y_ref = ref_forward(W, x, n)
+    xq, a = sbl.act_quant(xd)
+    for dt in (sbl.I32, sbl.F32, sbl.BF16):
+        y_two = sbl.forward(codes, gamma, xq, a, out_dtype=dt)
+        y_one = sbl.decode(codes, gamma, xd, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert torch.equal(y_one.view(torch.int32 if dt != sbl.BF16 else torch.int16),
+                           y_two.view(torch.int32 if dt != sbl.BF16 else torch.int16)), dt
+    np.testing.assert_array_equal(sbl.decode(codes, gamma, xd, out_dtype=sbl.I32).cpu().numpy(), acc_ref)
+    assert_y_close(sbl.decode(codes, gamma, xd, out_dtype=sbl.F32).cpu().numpy(), y_ref, acc_ref)
+
+
+@pytest.mark.parametrize("T,d_in", [(1, 8192), (5, 8192), (16, 3008)])
+def test_decode_fused_largest_rows(T, d_in):
+    # the longest rows the fused path takes (16 register chunks per lane, the 48 KB tile)
+    d_out = 48
+    W = weight(65, T, d_out, d_in)
+    x = activation(65, d_in + T, T, d_in, dist="student_t4")
+    assert sbl.decode_supported(T, d_in)
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+    acc_ref, _ = ref_forward(W, x, 6)
+    acc = sbl.decode(codes, gamma, to_dev_bf16(x), out_dtype=sbl.I32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+
+
+def test_decode_fused_zero_and_tiny_rows():
+    # a zero row (a_t = 0, x_q = 0, y = 0), a row of one non-zero, a row at the
+    # bf16 extremes: the fused quantization handles each as the act quant does
+    d_out, d_in, T = 64, 256, 4
+    W = weight(64, 0, d_out, d_in)
+    x = activation(64, 1, T, d_in)
+    x[0] = 0
+    x[1] = 0
+    x[1, 17] = f32_to_bf16_bits(np.float32(-3.0e-30))
+    x[2] = f32_to_bf16_bits(np.linspace(-3.0e38, 3.0e38, d_in).astype(np.float32))
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+    acc_ref, y_ref = ref_forward(W, x, 6)
+    acc = sbl.decode(codes, gamma, to_dev_bf16(x), out_dtype=sbl.I32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    y = sbl.decode(codes, gamma, to_dev_bf16(x), out_dtype=sbl.F32).cpu().numpy()
+    assert_y_close(y, y_ref, acc_ref)
+
+
+@pytest.mark.parametrize("T", [1, 8, 16])
+@pytest.mark.parametrize("name,d_out,d_in", [("gate", 11008, 2048), ("q", 2048, 2048), ("k", 256, 2048)])
+def test_decode_fused_full_size(T, name, d_out, d_in):
+    # decode workload shapes that take the fused path: exact int32 sums
+    W = weight(73, d_in, d_out, d_in)
+    x = activation(73, d_out + T, T, d_in, dist="student_t4")
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+    acc_ref, _ = ref_forward(W, x, 6)
+    acc = sbl.decode(codes, gamma, to_dev_bf16(x), out_dtype=sbl.I32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+
+
 def test_decode_graph_replay_matches_eager():
     # act quant + forward captured in a HIP graph (as the decode measurement runs them):
     # every replay, with eager work between replays, equals the eager result
@@ -229,14 +299,17 @@ def test_decode_graph_replay_matches_eager():
     xq = torch.empty((8, 1024), dtype=torch.int8, device="cuda")
     a = torch.empty((8,), dtype=torch.float32, device="cuda")
     y = torch.empty((8, 512), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((8, 512), dtype=torch.bfloat16, device="cuda")
 
     def run():
         sbl.act_quant(x, x_q=xq, absmax=a)
         sbl.forward(codes, gamma, xq, a, out_dtype=sbl.BF16, y=y)
+        sbl.decode(codes, gamma, x, out_dtype=sbl.BF16, y=y2)   # the fused form of the same step
 
     run()
     torch.cuda.synchronize()
     want = y.clone()
+    assert torch.equal(y2.view(torch.int16), want.view(torch.int16))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -248,12 +321,14 @@ def test_decode_graph_replay_matches_eager():
         run()
     for i in range(4):
         y.zero_()
+        y2.zero_()
         xq.zero_()
         other = sbl.forward(codes, gamma, xq, a)        # eager work between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), want.view(torch.int16)), f"replay {i}"
+        assert torch.equal(y2.view(torch.int16), want.view(torch.int16)), f"replay {i} (fused)"
         assert other.shape == (8, 512)
 
 
