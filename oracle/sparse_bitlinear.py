@@ -39,6 +39,10 @@ Readings of points the pages leave open (each is repeated where it is used):
 * Backward (Dual STE, identity through quantizers and the mask):
   dX = gamma * dY @ W_eff; dW = dY^T @ x~ with x~ = x_q * a_t / 127, dense over
   every master weight, masked ones included.
+* Ablations (4.3 消融实验): "mask from quantized weight" ranks |W_q| in {0, 1}
+  with the main mask's tie rule (lower index first); "mask without grad" sets
+  the gradient of masked slots to +0.
+* N:4 patterns (2:4) use groups of 4 inside the same 8-slot packed words.
 
 Parity pins live in ``tests/test_oracle_*.py``; none of them re-types these
 formulas.
@@ -241,10 +245,49 @@ def unpack_codes(codes: np.ndarray) -> np.ndarray:
     return out.reshape(d_out, G * 8)
 
 
-def quant_mask_pack(W_bits: np.ndarray, n_keep: int):
-    """The packing step as the library exposes it: (codes, mask plane, gamma)."""
-    w_eff, mask, g = effective_weight(W_bits, n_keep, 8)
+def quant_mask_pack(W_bits: np.ndarray, n_keep: int, m: int = 8, from_quantized: bool = False):
+    """The packing step as the library exposes it: (codes, mask plane, gamma).
+
+    m is the group size of the mask (8, or 4 for N:4 such as 2:4: two mask
+    groups per 8-slot word of the planes).  from_quantized selects the
+    ablation mask of ``mask_from_quantized`` instead of Pi_{N:M}(|W|).
+    """
+    if from_quantized:
+        g = gamma_f32(W_bits)
+        wq = ternary(W_bits, g)
+        mask = mask_from_quantized(wq, n_keep, m)
+        w_eff = (wq * mask.astype(np.int8)).astype(np.int8)
+    else:
+        w_eff, mask, g = effective_weight(W_bits, n_keep, m)
     return pack_codes(w_eff), pack_mask(mask), g
+
+
+# ----------------------------------------------------------------------------
+# Ablations  [SUM] 核心方法 (the two design points the variants remove) and
+#            4.3 消融实验: "mask from quantized weight" and "mask without grad"
+# ----------------------------------------------------------------------------
+
+
+def mask_from_quantized(w_q: np.ndarray, n_keep: int, m: int = 8) -> np.ndarray:
+    """Ablation mask Pi_{N:M}(|W_q|): top-n_keep of |W_q| in {0, 1} per group of m.
+
+    The pages give no tie rule for this variant, whose keys are nearly all tied
+    (they name the ties as the reason it fails); the main mask's rule is used:
+    equal keys keep the lower index.  So a group keeps its non-zero slots in
+    index order, then zero slots in index order, n_keep in all.
+    """
+    d_out, d_in = w_q.shape
+    assert d_in % m == 0 and 1 <= n_keep <= m
+    key = np.abs(w_q.astype(np.int64)).reshape(d_out, d_in // m, m)
+    order = np.argsort(-key, axis=-1, kind="stable")
+    keep = np.zeros(key.shape, dtype=bool)
+    np.put_along_axis(keep, order[..., :n_keep], True, axis=-1)
+    return keep.reshape(d_out, d_in)
+
+
+def mask_grad(dW: np.ndarray, mask: np.ndarray) -> np.ndarray:
+    """Ablation "mask without grad": the masked slots get no gradient (dW * M)."""
+    return np.where(mask, dW, 0.0)
 
 
 # ----------------------------------------------------------------------------
@@ -334,7 +377,7 @@ def backward(dY_bits: np.ndarray, w_eff: np.ndarray, gamma: float,
 def backward_stop_gradient(dY_bits, w_eff, gamma, x_q, absmax, mask):
     """Ablation from [SUM] 前置知识 > STE ("mask without grad"): dW multiplied by the mask."""
     dX, dW = backward(dY_bits, w_eff, gamma, x_q, absmax)
-    return dX, dW * mask
+    return dX, mask_grad(dW, mask)
 
 
 # ----------------------------------------------------------------------------

@@ -13,6 +13,7 @@ import test_oracle_gamma as t_gamma
 import test_oracle_gemm as t_gemm
 import test_oracle_mask as t_mask
 import test_oracle_ternary as t_tern
+import test_oracle_variants as t_var
 
 
 def _ties_to_higher_index(W_bits, n_keep, m=8):
@@ -76,6 +77,26 @@ def _forward_y_no_127(acc, gamma, absmax):
     return acc.astype(np.float64) * (float(gamma) * absmax.astype(np.float64)[:, None])
 
 
+def _qmask_ties_to_higher_index(w_q, n_keep, m=8):
+    d_out, d_in = w_q.shape
+    key = np.abs(w_q.astype(np.int64)).reshape(d_out, d_in // m, m)[..., ::-1]
+    order = np.argsort(-key, axis=-1, kind="stable")
+    keep = np.zeros(key.shape, dtype=bool)
+    np.put_along_axis(keep, order[..., :n_keep], True, axis=-1)
+    return keep[..., ::-1].reshape(d_out, d_in)
+
+
+def _mask_grad_multiply(dW, mask):
+    return dW * mask
+
+
+_ORIG_EFF = sb.effective_weight
+
+
+def _effective_weight_ignores_m(W_bits, n_keep, m=8):
+    return _ORIG_EFF(W_bits, n_keep, 8)
+
+
 _ORIG_PACK = sb.pack_codes
 
 
@@ -118,6 +139,12 @@ MUTANTS = [
     ("-1 packed as 10", "pack_codes", _pack_minus_as_10, [t_tern.test_pack_codes_bit_layout]),
     ("rational rounding ties up", "round_rational_to_f32", _round_ties_up,
      [t_gamma.test_round_rational_matches_numpy_on_exact_doubles]),
+    ("quantized-weight mask ties to higher index", "mask_from_quantized", _qmask_ties_to_higher_index,
+     [t_var.test_mask_from_quantized_worked_groups]),
+    ("masked gradient as dW * M (signed zeros)", "mask_grad", _mask_grad_multiply,
+     [t_var.test_mask_grad_zeroes_masked_slots_only]),
+    ("N:4 packed as N:8 groups", "effective_weight", _effective_weight_ignores_m,
+     [lambda: t_var.test_pack_n_of_4_planes(2)]),
 ]
 
 
