@@ -16,6 +16,7 @@ Metric: tokens per second of whole steps.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
        python bench.py --workload 4     (decode: per-layer latency at 1/8/64 tokens, 6/4/2:8)
+       python bench.py --variants       (every N of N:8, 2:4 and the two ablations, on the 3B-like matrices)
 """
 from __future__ import annotations
 
@@ -51,6 +52,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print the per-linear breakdown to stderr")
+    ap.add_argument("--variants", action="store_true",
+                    help="N:M patterns and ablations: quant/mask/pack per pattern and mask-without-grad on the "
+                         "3B-like matrices (one JSON line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -84,6 +88,9 @@ def main():
         print("copy calibration done", flush=True)
         return
     wl = WORKLOADS[args.workload]
+    if args.variants:
+        run_variants(args, wl)
+        return
     if not wl.backward and len(wl.T) > 1:
         run_decode(args, wl)
         return
@@ -252,6 +259,69 @@ def _bwd_sources_sha() -> str:
         with open(os.path.join(ROOT, "sparsity_sparse_bitlinear_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def run_variants(args, wl):
+    """The variant rows on the workload's matrices: quant/mask/pack for every N of N:8, 2:4 and the
+    mask-from-quantized-weight ablation (algorithmic 2.375 B per weight), and the mask-without-grad
+    ablation on float32 dW buffers of the same shapes (8.125 B per weight: dW read and written, mask)."""
+    import numpy as np
+    import torch
+
+    import sparsity_sparse_bitlinear_amd as sbl
+    from sbl_inputs import weight
+
+    dev = torch.device("cuda:0")
+    Ws = [torch.from_numpy(weight(wl.cfg, mi, L.d_out, L.d_in).view(np.int16)).view(torch.bfloat16).to(dev)
+          for mi, L in enumerate(wl.linears)]
+    outs = [(torch.empty((L.d_out, L.d_in // 8), dtype=torch.int16, device=dev),
+             torch.empty((L.d_out, L.d_in // 8), dtype=torch.uint8, device=dev),
+             torch.empty((1,), dtype=torch.float32, device=dev),
+             torch.empty((max(16, sbl.quant_workspace_size(L.d_out, L.d_in)),), dtype=torch.uint8, device=dev))
+            for L in wl.linears]
+    n_w = sum(L.d_out * L.d_in for L in wl.linears)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    patterns = [(n, 8, False) for n in (8, 7, 6, 5, 4, 3, 2)] + [(2, 4, False), (6, 8, True), (2, 4, True)]
+    rows = []
+    for n, m, fq in patterns:
+        def pack():
+            for W, (c, mk, g, ws) in zip(Ws, outs):
+                sbl.quant_mask_pack(W, n, m=m, from_quantized=fq, codes=c, mask=mk, gamma=g, workspace=ws)
+        ms = timed(pack)
+        gbs = 2.375 * n_w / (ms * 1e-3) / 1e9
+        rows.append({"pattern": f"{n}:{m}" + (" from W_q" if fq else ""), "ms": round(ms, 4),
+                     "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+    dWs = [torch.randn((L.d_out, L.d_in), device=dev) for L in wl.linears]
+    for W, (c, mk, g, ws) in zip(Ws, outs):
+        sbl.quant_mask_pack(W, 6, codes=c, mask=mk, gamma=g, workspace=ws)
+
+    def mg():
+        for dW, (_, mk, _, _) in zip(dWs, outs):
+            sbl.mask_grad(dW, mk)
+    ms = timed(mg)
+    gbs = 8.125 * n_w / (ms * 1e-3) / 1e9
+    line = {"metric": "Sparse-BitLinear variants: quant/mask/pack per N:M pattern and mask-without-grad, "
+                      "7 linears of a 3B-like layer",
+            "value": rows[2]["ms"], "unit": "ms per layer (6:8 quant/mask/pack)", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None,
+            "dtype": "bf16 in, 2-bit codes + mask plane out", "data": "synthetic",
+            "config": {"workload": wl.name, "weights": n_w},
+            "quant_mask_pack": rows,
+            "mask_grad": {"ms": round(ms, 4), "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}}
+    print(json.dumps(line), flush=True)
 
 
 DECODE_FUSE_MAX = 4_000_000  # element-quantizations per launch up to which sbl_decode beats two calls

@@ -104,7 +104,7 @@ SBL_API size_t sbl_quant_mask_pack_workspace_size(int64_t d_out, int64_t d_in);
  *   W_eff  = W_q * mask.
  *
  * W_bf16 : [d_out, d_in] bf16 bits.           d_in % 8 == 0, d_in >= 8.
- * n_keep : N of N:8, one of 2, 4, 6, 8.       d_out >= 1.
+ * n_keep : N of N:8, 1 <= N <= 8.             d_out >= 1.
  * codes  : [d_out, d_in/8] uint16 code plane.  Slot j (d_in position 8g+j)
  *          of group g sits at bits 2j..2j+1: 00 = 0, 01 = +1, 11 = -1 (10 is
  *          never written).  Masked slots hold 00.
@@ -117,6 +117,42 @@ SBL_API size_t sbl_quant_mask_pack_workspace_size(int64_t d_out, int64_t d_in);
 SBL_API int sbl_quant_mask_pack(const uint16_t* W_bf16, int64_t d_out, int64_t d_in, int n_keep,
                                 uint16_t* codes, uint8_t* mask, float* gamma, void* workspace,
                                 size_t workspace_bytes, void* hip_stream);
+
+/* sbl_quant_mask_pack_nm flags. */
+enum { SBL_MASK_FROM_QUANTIZED = 1 };
+
+/* sbl_quant_mask_pack with the mask pattern and the mask source chosen:
+ *
+ *   m_group : M of N:M, 8 or 4 ([SUM] 前置知识 > 半结构化 N:M 稀疏 names 2:4 as
+ *             the hardware pattern and 6:8 as the one studied; 方法步骤详情
+ *             compares the two).  M = 4 keeps n_keep of every 4 consecutive
+ *             d_in positions; the planes keep their 8-slot words (two mask
+ *             groups per word), so every other entry point takes them as is.
+ *   n_keep  : 1 <= n_keep <= m_group (the N:8 sweep of [GIST] 4.1 runs 8:8 to 2:8).
+ *   flags   : 0, or SBL_MASK_FROM_QUANTIZED for the ablation of [GIST] 4.3 消融实验
+ *             ("mask from quantized weight", which the pages report as
+ *             unstable): the mask ranks |W_q| in {0, 1} instead of |W|, ties
+ *             to the lower index as in the main rule, so a group keeps its
+ *             non-zero ternary slots in index order, then zero slots.
+ *
+ * Everything else (gamma, codes, planes, workspace, errors) as for
+ * sbl_quant_mask_pack, which is this call with m_group = 8 and flags = 0.
+ * Unsupported (n_keep, m_group) return SBL_ERR_UNSUPPORTED; unknown flag bits
+ * SBL_ERR_INVALID_ARG.
+ */
+SBL_API int sbl_quant_mask_pack_nm(const uint16_t* W_bf16, int64_t d_out, int64_t d_in, int n_keep, int m_group,
+                                   int flags, uint16_t* codes, uint8_t* mask, float* gamma, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream);
+
+/* "Mask without grad" ablation ([SUM] 核心方法, second design point; 4.3
+ * 消融实验 of [GIST]): the gradient of masked master weights is dropped, i.e. applied
+ * after sbl_backward, dW[o, i] = +0 wherever bit (i % 8) of mask[o, i / 8] is
+ * clear; kept entries are unchanged.  In place.
+ *
+ * dW   : [d_out, d_in] float32, 16-byte aligned.  d_in % 8 == 0.
+ * mask : [d_out, d_in/8] mask plane from sbl_quant_mask_pack(_nm).
+ */
+SBL_API int sbl_mask_grad(float* dW, const uint8_t* mask, int64_t d_out, int64_t d_in, void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
 /* Activation side                                                            */

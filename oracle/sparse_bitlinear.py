@@ -39,7 +39,7 @@ Readings of points the pages leave open (each is repeated where it is used):
 * Backward (Dual STE, identity through quantizers and the mask):
   dX = gamma * dY @ W_eff; dW = dY^T @ x~ with x~ = x_q * a_t / 127, dense over
   every master weight, masked ones included.
-* Ablations (4.3 消融实验): "mask from quantized weight" ranks |W_q| in {0, 1}
+* Ablations ([GIST] 4.3 消融实验): "mask from quantized weight" ranks |W_q| in {0, 1}
   with the main mask's tie rule (lower index first); "mask without grad" sets
   the gradient of masked slots to +0.
 * N:4 patterns (2:4) use groups of 4 inside the same 8-slot packed words.
@@ -264,7 +264,7 @@ def quant_mask_pack(W_bits: np.ndarray, n_keep: int, m: int = 8, from_quantized:
 
 # ----------------------------------------------------------------------------
 # Ablations  [SUM] 核心方法 (the two design points the variants remove) and
-#            4.3 消融实验: "mask from quantized weight" and "mask without grad"
+#            [GIST] 4.3 消融实验: "mask from quantized weight" and "mask without grad"
 # ----------------------------------------------------------------------------
 
 

@@ -33,6 +33,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsbl.so")
 
 F32, BF16, I32 = 0, 1, 2
 BWD_DX, BWD_DW = 1, 2
+MASK_FROM_QUANTIZED = 1
 
 _c_i64 = ctypes.c_int64
 _c_ptr = ctypes.c_void_p
@@ -42,6 +43,9 @@ _c_size = ctypes.c_size_t
 _SIGNATURES = {
     "sbl_quant_mask_pack_workspace_size": (_c_size, [_c_i64, _c_i64]),
     "sbl_quant_mask_pack": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
+    "sbl_quant_mask_pack_nm": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                        _c_size, _c_ptr]),
+    "sbl_mask_grad": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr]),
     "sbl_act_quant": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "sbl_forward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
@@ -130,13 +134,15 @@ def backward_workspace_size(T: int, d_in: int, d_out: int, flags: int = BWD_DX |
     return int(lib.sbl_backward_workspace_size(T, d_in, d_out, flags))
 
 
-def quant_mask_pack(W: torch.Tensor, n_keep: int = 6, *, codes: Optional[torch.Tensor] = None,
-                    mask: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, want_mask: bool = True, stream=None):
-    """gamma, N:8 mask and 2-bit ternary code plane of the bf16 master weight ``W`` [d_out, d_in].
+def quant_mask_pack(W: torch.Tensor, n_keep: int = 6, *, m: int = 8, from_quantized: bool = False,
+                    codes: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+                    gamma: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    want_mask: bool = True, stream=None):
+    """gamma, N:M mask and 2-bit ternary code plane of the bf16 master weight ``W`` [d_out, d_in].
 
-    Returns ``(codes int16 [d_out, d_in/8] (uint16 bit patterns), mask uint8 [d_out, d_in/8] or None,
-    gamma float32 [1])``; all on W's device.
+    ``m`` is 8 (N:8) or 4 (N:4, e.g. 2:4); ``from_quantized`` selects the mask-from-quantized-weight
+    ablation.  Returns ``(codes int16 [d_out, d_in/8] (uint16 bit patterns), mask uint8
+    [d_out, d_in/8] or None, gamma float32 [1])``; all on W's device.
     """
     _as_bits16(W, "W")
     d_out, d_in = W.shape
@@ -155,9 +161,20 @@ def quant_mask_pack(W: torch.Tensor, n_keep: int = 6, *, codes: Optional[torch.T
     if workspace is None:
         workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
     _out(workspace, (workspace.numel(),), (torch.uint8,), dev, "workspace")
-    _check(lib.sbl_quant_mask_pack(_ptr(W), d_out, d_in, int(n_keep), _ptr(codes), _ptr(mask), _ptr(gamma),
-                                   _ptr(workspace), workspace.numel(), _stream(stream)), "sbl_quant_mask_pack")
+    flags = MASK_FROM_QUANTIZED if from_quantized else 0
+    _check(lib.sbl_quant_mask_pack_nm(_ptr(W), d_out, d_in, int(n_keep), int(m), flags, _ptr(codes), _ptr(mask),
+                                      _ptr(gamma), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "sbl_quant_mask_pack_nm")
     return codes, mask, gamma
+
+
+def mask_grad(dW: torch.Tensor, mask: torch.Tensor, *, stream=None) -> torch.Tensor:
+    """Mask-without-grad ablation, in place: dW = +0 where the mask plane's bit is clear."""
+    _out(dW, tuple(dW.shape), (torch.float32,), dW.device, "dW")
+    d_out, d_in = dW.shape
+    _out(mask, (d_out, d_in // 8), (torch.uint8,), dW.device, "mask")
+    _check(lib.sbl_mask_grad(_ptr(dW), _ptr(mask), d_out, d_in, _stream(stream)), "sbl_mask_grad")
+    return dW
 
 
 def act_quant(x: torch.Tensor, *, x_q: Optional[torch.Tensor] = None, absmax: Optional[torch.Tensor] = None,

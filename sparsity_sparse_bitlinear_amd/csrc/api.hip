@@ -77,13 +77,15 @@ SBL_API size_t sbl_quant_mask_pack_workspace_size(int64_t d_out, int64_t d_in) {
   return quant_workspace_bytes(d_out, d_in);
 }
 
-SBL_API int sbl_quant_mask_pack(const uint16_t* W_bf16, int64_t d_out, int64_t d_in, int n_keep, uint16_t* codes,
-                                uint8_t* mask, float* gamma, void* workspace, size_t workspace_bytes,
-                                void* hip_stream) {
+SBL_API int sbl_quant_mask_pack_nm(const uint16_t* W_bf16, int64_t d_out, int64_t d_in, int n_keep, int m_group,
+                                   int flags, uint16_t* codes, uint8_t* mask, float* gamma, void* workspace,
+                                   size_t workspace_bytes, void* hip_stream) {
   int rc = check_dims(d_out, d_in);
   if (rc != SBL_OK) return rc;
-  SBL_REQUIRE(n_keep == 2 || n_keep == 4 || n_keep == 6 || n_keep == 8, SBL_ERR_UNSUPPORTED,
-              "n_keep=%d: supported N:8 patterns are 2, 4, 6, 8", n_keep);
+  SBL_REQUIRE(flags == 0 || flags == SBL_MASK_FROM_QUANTIZED, SBL_ERR_INVALID_ARG, "flags=%d: unknown flag bits",
+              flags);
+  SBL_REQUIRE(mask_pattern_supported(n_keep, m_group), SBL_ERR_UNSUPPORTED,
+              "n_keep=%d, m_group=%d: supported patterns are N:8 and N:4 with 1 <= N <= M", n_keep, m_group);
   SBL_REQUIRE(W_bf16 && codes && gamma, SBL_ERR_INVALID_ARG, "W, codes and gamma must be non-NULL");
   SBL_REQUIRE(aligned(W_bf16, 16) && aligned(codes, 16) && aligned(gamma, 4), SBL_ERR_INVALID_ARG,
               "W and codes must be 16-byte aligned, gamma 4-byte aligned");
@@ -91,9 +93,26 @@ SBL_API int sbl_quant_mask_pack(const uint16_t* W_bf16, int64_t d_out, int64_t d
   SBL_REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 16), SBL_ERR_WORKSPACE,
               "workspace of %zu bytes (16-byte aligned) required, got %zu", need,
               workspace ? workspace_bytes : (size_t)0);
-  hipError_t e = launch_quant_mask_pack(W_bf16, d_out, d_in, n_keep, codes, mask, gamma, workspace,
-                                        (hipStream_t)hip_stream);
+  hipError_t e = launch_quant_mask_pack(W_bf16, d_out, d_in, n_keep, m_group, flags == SBL_MASK_FROM_QUANTIZED,
+                                        codes, mask, gamma, workspace, (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "sbl_quant_mask_pack launch");
+  return SBL_OK;
+}
+
+SBL_API int sbl_quant_mask_pack(const uint16_t* W_bf16, int64_t d_out, int64_t d_in, int n_keep, uint16_t* codes,
+                                uint8_t* mask, float* gamma, void* workspace, size_t workspace_bytes,
+                                void* hip_stream) {
+  return sbl_quant_mask_pack_nm(W_bf16, d_out, d_in, n_keep, 8, 0, codes, mask, gamma, workspace, workspace_bytes,
+                                hip_stream);
+}
+
+SBL_API int sbl_mask_grad(float* dW, const uint8_t* mask, int64_t d_out, int64_t d_in, void* hip_stream) {
+  int rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(dW && mask, SBL_ERR_INVALID_ARG, "dW and mask must be non-NULL");
+  SBL_REQUIRE(aligned(dW, 16), SBL_ERR_INVALID_ARG, "dW must be 16-byte aligned");
+  hipError_t e = launch_mask_grad(dW, mask, d_out, d_in, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_mask_grad launch");
   return SBL_OK;
 }
 

@@ -12,6 +12,9 @@
 //   k_gamma_finalize one block: exact total, one correctly rounded division
 //   k_mask_quant_pack pass 2 over W: per 8-group sorting network -> keep bits,
 //                     threshold |w| > gamma/2 -> 2-bit codes, write both planes
+//                     (N:8 for any N, N:4 such as 2:4 as two groups per word,
+//                     and the mask-from-quantized-weight ablation)
+// plus k_mask_grad, the mask-without-grad ablation on a dW buffer.
 #include "sbl_internal.h"
 
 namespace sbl {
@@ -300,10 +303,13 @@ __device__ __forceinline__ void cswap_desc(uint32_t& a, uint32_t& b) {
   b = lo;
 }
 
-// One group of 8 bf16 values (4 words).  Rank keys u_j = (|w_j| bits << 3) | (7 - j)
-// are distinct and order slots by magnitude, lower index first on ties; an
-// optimal 19-comparator network sorts them and the N-th largest is the
-// keep threshold.
+// One word of 8 bf16 values (4 words of the row).  Rank keys
+// u_j = (key_j << 3) | (7 - j) are distinct and order slots by key, lower index
+// first on ties; the key is the 15-bit |w| bit pattern (the mask
+// Pi_{N:M}(|W|) of the master weight) or, for the "mask from quantized weight"
+// ablation (FQ), |W_q| in {0, 1}.  M = 8: one group, an optimal 19-comparator
+// network sorts the keys and the N-th largest is the keep threshold.  M = 4:
+// two groups (slots 0-3 and 4-7), each sorted by a 5-comparator network.
 // |w| > gamma/2  <=>  2|w| > gamma.  Both sides are non-negative binary32
 // values, compared through their bit patterns (monotone for non-negative
 // floats), so no floating-point mode (denormal flushing) can change the
@@ -316,16 +322,28 @@ __device__ __forceinline__ bool above_half_gamma(uint32_t mag16, uint32_t gamma_
   return twice > gamma_bits;
 }
 
+// N-th largest of 4 keys (descending network: (0,1) (2,3) (0,2) (1,3) (1,2)).
 template <int N>
+__device__ __forceinline__ uint32_t nth_of4(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  cswap_desc(a, b); cswap_desc(c, d); cswap_desc(a, c); cswap_desc(b, d); cswap_desc(b, c);
+  return N == 1 ? a : N == 2 ? b : N == 3 ? c : d;
+}
+
+template <int N, int M, bool FQ>
 __device__ __forceinline__ void pack_group(const uint4 v, uint32_t gamma_bits, uint16_t& code_out,
                                            uint8_t& mask_out) {
   uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
                    v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+  bool nz[8];
   uint32_t u[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) u[j] = ((h[j] & 0x7FFFu) << 3) | (uint32_t)(7 - j);
-  uint32_t thr = 0;
-  if constexpr (N < 8) {
+  for (int j = 0; j < 8; ++j) {
+    nz[j] = above_half_gamma(h[j] & 0x7FFFu, gamma_bits);
+    const uint32_t key = FQ ? (nz[j] ? 1u : 0u) : (h[j] & 0x7FFFu);
+    u[j] = (key << 3) | (uint32_t)(7 - j);
+  }
+  uint32_t thr_lo = 0, thr_hi = 0;
+  if constexpr (M == 8 && N < 8) {
     uint32_t s[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) s[j] = u[j];
@@ -335,14 +353,16 @@ __device__ __forceinline__ void pack_group(const uint4 v, uint32_t gamma_bits, u
     cswap_desc(s[2], s[4]); cswap_desc(s[3], s[5]);
     cswap_desc(s[1], s[4]); cswap_desc(s[3], s[6]);
     cswap_desc(s[1], s[2]); cswap_desc(s[3], s[4]); cswap_desc(s[5], s[6]);
-    thr = s[N - 1];
+    thr_lo = thr_hi = s[N - 1];
+  } else if constexpr (M == 4 && N < 4) {
+    thr_lo = nth_of4<N>(u[0], u[1], u[2], u[3]);
+    thr_hi = nth_of4<N>(u[4], u[5], u[6], u[7]);
   }
   uint32_t code = 0, mask = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const bool keep = (N == 8) || (u[j] >= thr);
-    const bool nz = above_half_gamma(h[j] & 0x7FFFu, gamma_bits);
-    const uint32_t c = (keep && nz) ? ((h[j] & 0x8000u) ? 3u : 1u) : 0u;
+    const bool keep = (N == M) || (u[j] >= (j < 4 ? thr_lo : thr_hi));
+    const uint32_t c = (keep && nz[j]) ? ((h[j] & 0x8000u) ? 3u : 1u) : 0u;
     code |= c << (2 * j);
     mask |= (keep ? 1u : 0u) << j;
   }
@@ -353,7 +373,7 @@ __device__ __forceinline__ void pack_group(const uint4 v, uint32_t gamma_bits, u
 // A block takes 4 x 256 consecutive groups per round (each thread 4 groups,
 // 256 apart, so every load and store instruction is contiguous); the four
 // loads are issued before any group is packed.
-template <int N>
+template <int N, int M, bool FQ>
 __global__ __launch_bounds__(256) void k_mask_quant_pack(const uint4* __restrict__ W, int64_t n_groups,
                                                          const float* __restrict__ gamma_p,
                                                          uint16_t* __restrict__ codes, uint8_t* __restrict__ mask) {
@@ -370,10 +390,32 @@ __global__ __launch_bounds__(256) void k_mask_quant_pack(const uint4* __restrict
       if (g >= n_groups) break;
       uint16_t c;
       uint8_t m;
-      pack_group<N>(v[u], gamma_bits, c, m);
+      pack_group<N, M, FQ>(v[u], gamma_bits, c, m);
       codes[g] = c;
       if (mask) mask[g] = m;
     }
+  }
+}
+
+// "Mask without grad" ablation: dW[o, i] = +0 where slot i of the mask plane
+// is clear.  One thread per 8-slot group: two 16-byte loads and stores of dW,
+// one mask byte.
+__global__ __launch_bounds__(256) void k_mask_grad(float4* __restrict__ dW, const uint8_t* __restrict__ mask,
+                                                   int64_t n_groups) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < n_groups; g += stride) {
+    const uint32_t m = mask[g];
+    float4 a = dW[2 * g], b = dW[2 * g + 1];
+    a.x = (m & 1u) ? a.x : 0.0f;
+    a.y = (m & 2u) ? a.y : 0.0f;
+    a.z = (m & 4u) ? a.z : 0.0f;
+    a.w = (m & 8u) ? a.w : 0.0f;
+    b.x = (m & 16u) ? b.x : 0.0f;
+    b.y = (m & 32u) ? b.y : 0.0f;
+    b.z = (m & 64u) ? b.z : 0.0f;
+    b.w = (m & 128u) ? b.w : 0.0f;
+    dW[2 * g] = a;
+    dW[2 * g + 1] = b;
   }
 }
 
@@ -393,8 +435,41 @@ size_t quant_workspace_bytes(int64_t d_out, int64_t d_in) {
   return (size_t)nb * sizeof(AbsumPartial) + (size_t)nb * 256 * sizeof(unsigned long long);
 }
 
-hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int n_keep, uint16_t* codes,
-                                  uint8_t* mask, float* gamma, void* ws, hipStream_t s) {
+using MqpKernel = void (*)(const uint4*, int64_t, const float*, uint16_t*, uint8_t*);
+
+// k_mask_quant_pack instance for (N, M, FQ); nullptr outside 1 <= N <= M, M in {4, 8}.
+static MqpKernel mqp_kernel(int n, int m, bool fq) {
+#define SBL_MQP(NN, MM) (fq ? (MqpKernel)k_mask_quant_pack<NN, MM, true> : (MqpKernel)k_mask_quant_pack<NN, MM, false>)
+  if (m == 8) {
+    switch (n) {
+      case 1: return SBL_MQP(1, 8);
+      case 2: return SBL_MQP(2, 8);
+      case 3: return SBL_MQP(3, 8);
+      case 4: return SBL_MQP(4, 8);
+      case 5: return SBL_MQP(5, 8);
+      case 6: return SBL_MQP(6, 8);
+      case 7: return SBL_MQP(7, 8);
+      case 8: return SBL_MQP(8, 8);
+    }
+  } else if (m == 4) {
+    switch (n) {
+      case 1: return SBL_MQP(1, 4);
+      case 2: return SBL_MQP(2, 4);
+      case 3: return SBL_MQP(3, 4);
+      case 4: return SBL_MQP(4, 4);
+    }
+  }
+#undef SBL_MQP
+  return nullptr;
+}
+
+bool mask_pattern_supported(int n_keep, int m_group) { return mqp_kernel(n_keep, m_group, false) != nullptr; }
+
+hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int n_keep, int m_group,
+                                  bool from_quantized, uint16_t* codes, uint8_t* mask, float* gamma, void* ws,
+                                  hipStream_t s) {
+  const MqpKernel pack = mqp_kernel(n_keep, m_group, from_quantized);
+  if (!pack) return hipErrorInvalidValue;
   const int64_t n_groups = d_out * d_in / 8;
   const int nb = absum_blocks(n_groups);
   AbsumPartial* part = (AbsumPartial*)ws;
@@ -404,13 +479,17 @@ hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in
                      (const unsigned long long*)hist, nb, (unsigned long long)(d_out * d_in), gamma);
   int64_t pb = (n_groups + 1023) / 1024;
   if (pb > 65536) pb = 65536;
-  const dim3 grid((unsigned)pb), block(256);
-  switch (n_keep) {
-    case 2: hipLaunchKernelGGL(k_mask_quant_pack<2>, grid, block, 0, s, (const uint4*)W, n_groups, gamma, codes, mask); break;
-    case 4: hipLaunchKernelGGL(k_mask_quant_pack<4>, grid, block, 0, s, (const uint4*)W, n_groups, gamma, codes, mask); break;
-    case 6: hipLaunchKernelGGL(k_mask_quant_pack<6>, grid, block, 0, s, (const uint4*)W, n_groups, gamma, codes, mask); break;
-    default: hipLaunchKernelGGL(k_mask_quant_pack<8>, grid, block, 0, s, (const uint4*)W, n_groups, gamma, codes, mask); break;
-  }
+  hipLaunchKernelGGL(pack, dim3((unsigned)pb), dim3(256), 0, s, (const uint4*)W, n_groups, (const float*)gamma, codes,
+                     mask);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_grad(float* dW, const uint8_t* mask, int64_t d_out, int64_t d_in, hipStream_t s) {
+  const int64_t n_groups = d_out * d_in / 8;
+  if (n_groups == 0) return hipSuccess;
+  int64_t nb = (n_groups + 255) / 256;
+  if (nb > 8192) nb = 8192;
+  hipLaunchKernelGGL(k_mask_grad, dim3((unsigned)nb), dim3(256), 0, s, (float4*)dW, mask, n_groups);
   return hipGetLastError();
 }
 

@@ -56,8 +56,12 @@ constexpr int kAbsumMaxBlocks = 1024;
 size_t quant_workspace_bytes(int64_t d_out, int64_t d_in);
 int absum_blocks(int64_t n_vec8);
 
-hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int n_keep, uint16_t* codes,
-                                  uint8_t* mask, float* gamma, void* ws, hipStream_t s);
+// N:M patterns with a packing kernel: M in {4, 8}, 1 <= N <= M.
+bool mask_pattern_supported(int n_keep, int m_group);
+hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in, int n_keep, int m_group,
+                                  bool from_quantized, uint16_t* codes, uint8_t* mask, float* gamma, void* ws,
+                                  hipStream_t s);
+hipError_t launch_mask_grad(float* dW, const uint8_t* mask, int64_t d_out, int64_t d_in, hipStream_t s);
 
 // Host/device: RN_float32(S * 2^-133 / count) for S given as 32-bit words.
 __host__ __device__ float round_mean_words(const uint32_t* w, int nwords, unsigned long long count);

@@ -52,7 +52,8 @@ def test_quant_mask_pack_validation():
     assert f(P, 256, 12, 6, P, P, P, P, ws, NULL) == SHAPE          # d_in not a multiple of 8
     assert f(P, 256, 0, 6, P, P, P, P, ws, NULL) == SHAPE
     assert f(P, 0, 256, 6, P, P, P, P, ws, NULL) == SHAPE
-    assert f(P, 256, 256, 5, P, P, P, P, ws, NULL) == UNSUPPORTED   # 5:8 not built
+    assert f(P, 256, 256, 9, P, P, P, P, ws, NULL) == UNSUPPORTED   # N > 8
+    assert f(P, 256, 256, 0, P, P, P, P, ws, NULL) == UNSUPPORTED
     assert f(NULL, 256, 256, 6, P, P, P, P, ws, NULL) == INVALID
     assert f(P, 256, 256, 6, NULL, P, P, P, ws, NULL) == INVALID
     assert f(P, 256, 256, 6, P, P, NULL, P, ws, NULL) == INVALID
@@ -61,6 +62,25 @@ def test_quant_mask_pack_validation():
     assert f(P, 256, 256, 6, P, P, P, NULL, ws, NULL) == WORKSPACE
     assert b"workspace" in lib.sbl_last_error()
     assert f(P, 1 << 20, 1 << 20, 6, P, P, P, P, ws, NULL) == SHAPE  # above the weight limit
+
+
+def test_quant_mask_pack_nm_validation():
+    ws = lib.sbl_quant_mask_pack_workspace_size(256, 256)
+    f = lib.sbl_quant_mask_pack_nm
+    assert f(P, 256, 256, 5, 4, 0, P, P, P, P, ws, NULL) == UNSUPPORTED     # 5:4
+    assert f(P, 256, 256, 2, 16, 0, P, P, P, P, ws, NULL) == UNSUPPORTED    # M = 16
+    assert f(P, 256, 256, 2, 4, 2, P, P, P, P, ws, NULL) == INVALID         # unknown flag bit
+    assert f(P, 256, 12, 2, 4, 0, P, P, P, P, ws, NULL) == SHAPE
+    assert f(NULL, 256, 256, 2, 4, 1, P, P, P, P, ws, NULL) == INVALID
+    assert f(P, 256, 256, 2, 4, 1, P, P, P, P, ws - 1, NULL) == WORKSPACE
+
+
+def test_mask_grad_validation():
+    f = lib.sbl_mask_grad
+    assert f(NULL, P, 256, 256, NULL) == INVALID
+    assert f(P, NULL, 256, 256, NULL) == INVALID
+    assert f(P_MIS, P, 256, 256, NULL) == INVALID
+    assert f(P, P, 256, 12, NULL) == SHAPE
 
 
 def test_act_quant_validation():

@@ -49,6 +49,69 @@ def test_pack_parity_tie_heavy(n):
     check_pack(tie_heavy_weight(2, 64, 64, alphabet=(-1, 1), scale=0.5), n)
 
 
+# N:M variants and the mask-from-quantized-weight ablation: every N of N:8,
+# N:4 (2:4) inside the 8-slot planes, bit-exact planes and gamma.
+def check_pack_nm(W_bits, n, m, fq):
+    codes, mask, gamma = sbl.quant_mask_pack(to_dev_bf16(W_bits), n, m=m, from_quantized=fq)
+    torch.cuda.synchronize()
+    rc, rm, rg = oracle.quant_mask_pack(W_bits, n, m, from_quantized=fq)
+    assert f32_bits(gamma.cpu().numpy()[0]) == f32_bits(rg)
+    np.testing.assert_array_equal(mask.cpu().numpy(), rm)
+    np.testing.assert_array_equal(bits16(codes), rc)
+
+
+@pytest.mark.parametrize("fq", [False, True])
+@pytest.mark.parametrize("n,m", [(n, 8) for n in range(1, 9)] + [(n, 4) for n in range(1, 5)])
+def test_pack_parity_nm_patterns(n, m, fq):
+    check_pack_nm(weight(13, 10 * n + m, 333, 1032), n, m, fq)
+    check_pack_nm(tie_heavy_weight(3, 64, 128), n, m, fq)
+    check_pack_nm(boundary_row_weight(24, 64), n, m, fq)
+
+
+@pytest.mark.parametrize("n,m", [(3, 8), (5, 8), (7, 8), (2, 4), (1, 4)])
+def test_step_parity_nm_patterns(n, m):
+    # the forward and backward kernels take the planes of any pattern as they are
+    T, d_out, d_in = 77, 200, 328
+    W = weight(53, n + m, d_out, d_in)
+    x = activation(53, n + m + 1, T, d_in, dist="student_t4")
+    dY = grad_out(53, n + m + 2, T, d_out)
+    w_eff, mask, g = oracle.effective_weight(W, n, m)
+    xq_r, a_r = oracle.act_quant(x)
+    acc_ref = oracle.forward_acc(w_eff, xq_r)
+    dX_r, dW_r = oracle.backward(dY, w_eff, g, xq_r, a_r)
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), n, m=m)
+    xq, a = sbl.act_quant(to_dev_bf16(x))
+    acc = sbl.forward(codes, gamma, xq, a, out_dtype=sbl.I32)
+    dX, dW = sbl.backward(codes, gamma, xq, a, to_dev_bf16(dY))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(acc.cpu().numpy(), acc_ref)
+    assert_grad_close(bf16_to_f64(dX), dX_r)
+    assert_grad_close(dW.cpu().numpy(), dW_r)
+
+
+@pytest.mark.parametrize("d_out,d_in", [(200, 328), (11008, 2048)])
+def test_mask_grad_parity(d_out, d_in):
+    # mask-without-grad ablation: masked slots +0, kept slots bit for bit, and the
+    # result against the oracle's stop-gradient backward
+    T = 64
+    W = weight(57, d_out, d_out, d_in)
+    x = activation(57, d_in, T, d_in, dist="student_t4")
+    dY = grad_out(57, T, T, d_out)
+    codes, mask, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+    xq, a = sbl.act_quant(to_dev_bf16(x))
+    _, dW = sbl.backward(codes, gamma, xq, a, to_dev_bf16(dY))
+    full = dW.clone()
+    sbl.mask_grad(dW, mask)
+    torch.cuda.synchronize()
+    keep = oracle.nm_mask(W, 6)
+    got = dW.cpu().numpy()
+    np.testing.assert_array_equal(got.view(np.int32), oracle.mask_grad(full.cpu().numpy(), keep).view(np.int32))
+    if d_out <= 256:
+        r = oracle.sparse_bitlinear_step(W, x, dY, 6)
+        _, dW_sg = oracle.backward_stop_gradient(dY, r["w_eff"], r["gamma"], r["x_q"], r["absmax"], r["mask"])
+        assert_grad_close(got, dW_sg)
+
+
 def test_pack_boundary_rows():
     W = boundary_row_weight(24, 64)     # gamma = 1 exactly; |w| = 0.5 sits on the threshold
     check_pack(W, 8)
