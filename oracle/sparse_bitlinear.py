@@ -381,6 +381,117 @@ def backward_stop_gradient(dY_bits, w_eff, gamma, x_q, absmax, mask):
 
 
 # ----------------------------------------------------------------------------
+# Optimizer step + repack  [SUM] 方法步骤详情 step (8) (AdamW updates W; its
+#                          hyper-parameters beta = (0.9, 0.95), eps = 1e-5,
+#                          weight decay 0.1, grad clip 1.0) and step (2) of the
+#                          next step (the mask is recomputed from the new W)
+# ----------------------------------------------------------------------------
+
+
+def adamw_update(W_bits: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, step: int, lr: float,
+                 beta1: float = 0.9, beta2: float = 0.95, eps: float = 1e-5, weight_decay: float = 0.1,
+                 grad_scale: float = 1.0):
+    """One AdamW step on the bf16 master weight, in float64.
+
+    AdamW with decoupled weight decay: the gradient is first multiplied by
+    grad_scale (the caller's global-norm clipping factor, min(1, clip / ||g||),
+    which spans every parameter of the model and so lies outside the
+    operator), then
+        m' = beta1 m + (1 - beta1) g,   v' = beta2 v + (1 - beta2) g^2,
+        W' = W (1 - lr wd) - lr (m' / (1 - beta1^t)) / (sqrt(v' / (1 - beta2^t)) + eps).
+    Returns (W' float64, W' rounded to bf16 bits, m' float64, v' float64).
+    The pages fix the hyper-parameters but not the state precision; float32
+    states are the reading (the library stores m', v' as float32).
+    """
+    assert step >= 1
+    W = bf16_to_f64(W_bits)
+    gs = np.asarray(g, np.float64) * float(grad_scale)
+    m1 = beta1 * np.asarray(m, np.float64) + (1.0 - beta1) * gs
+    v1 = beta2 * np.asarray(v, np.float64) + (1.0 - beta2) * gs * gs
+    mhat = m1 / (1.0 - beta1 ** step)
+    vhat = v1 / (1.0 - beta2 ** step)
+    W1 = W * (1.0 - lr * weight_decay) - lr * mhat / (np.sqrt(vhat) + eps)
+    return W1, f64_to_bf16_bits(W1), m1, v1
+
+
+def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to even), as bit patterns.
+
+    Exact: the value is split into its binary64 fields and rounded on the
+    integer significand (no intermediate float32 rounding).  Values beyond the
+    bf16 range become +-inf; subnormal results round on the subnormal grid.
+    """
+    x = np.asarray(x, np.float64)
+    bits = x.view(np.uint64)
+    sign = (bits >> np.uint64(63)).astype(np.uint64)
+    e = ((bits >> np.uint64(52)) & np.uint64(0x7FF)).astype(np.int64)
+    frac = (bits & np.uint64((1 << 52) - 1)).astype(np.uint64)
+    out = np.zeros(x.shape, np.uint64)
+    for idx in np.ndindex(x.shape):
+        ei, fi = int(e[idx]), int(frac[idx])
+        if ei == 0 and fi == 0:
+            out[idx] = 0
+            continue
+        assert ei != 0x7FF, "non-finite value"
+        # value = sig * 2^(exp2) with sig an integer of 53 bits (normal binary64)
+        sig = (fi | (1 << 52)) if ei else fi
+        exp2 = (ei if ei else 1) - 1075
+        # bf16 normal: 8-bit significand, exponent field 1..254; grid 2^(E - 7)
+        top = sig.bit_length() - 1 + exp2           # floor(log2 |x|)
+        q = max(top, -126) - 7                       # grid exponent (subnormals: 2^-133)
+        shift = q - exp2
+        if shift <= 0:
+            r = sig << (-shift)
+        else:
+            r, rem = sig >> shift, sig & ((1 << shift) - 1)
+            half = 1 << (shift - 1)
+            if rem > half or (rem == half and (r & 1)):
+                r += 1
+        # r * 2^q with r <= 256; a carry to 256 moves to the next binade
+        if r == 256:
+            r, q = 128, q + 1
+        if r == 0:
+            b = 0
+        else:
+            top_r = r.bit_length() - 1 + q
+            if top_r > 127:
+                b = 0x7F80                           # overflow to infinity
+            elif top_r < -126:
+                b = r << (q + 133)                   # subnormal: 2^-133 units
+            else:                                    # r has 8 bits: hidden one + 7-bit mantissa
+                b = ((top_r + 127) << 7) | (r & 0x7F)
+        out[idx] = b
+    return (out | (sign << np.uint64(15))).astype(np.uint16)
+
+
+def mask_flips(mask_prev: np.ndarray, mask_new: np.ndarray) -> int:
+    """Mask flip count: slots whose keep bit changed between two steps (the
+    training diagnostic of [SUM] 核心方法, masks recomputed every step)."""
+    return int(np.count_nonzero(np.asarray(mask_prev, bool) != np.asarray(mask_new, bool)))
+
+
+def adamw_repack(W_bits, g, m, v, step, lr, n_keep, m_group=8, mask_prev=None, **hp):
+    """Optimizer step followed by the next step's packing: (W' bf16 bits, m', v', codes, mask plane,
+    gamma, flips or None)."""
+    _, W1_bits, m1, v1 = adamw_update(W_bits, g, m, v, step, lr, **hp)
+    codes, mplane, gam = quant_mask_pack(W1_bits, n_keep, m_group)
+    flips = None
+    if mask_prev is not None:
+        flips = mask_flips(unpack_mask(mask_prev), unpack_mask(mplane))
+    return W1_bits, m1, v1, codes, mplane, gam, flips
+
+
+def unpack_mask(mplane: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_mask``: bool [d_out, 8 * groups]."""
+    mplane = np.asarray(mplane, np.uint8)
+    d_out, G = mplane.shape
+    out = np.zeros((d_out, G, 8), bool)
+    for j in range(8):
+        out[..., j] = (mplane >> j) & 1
+    return out.reshape(d_out, G * 8)
+
+
+# ----------------------------------------------------------------------------
 # Whole step
 # ----------------------------------------------------------------------------
 

@@ -13,6 +13,7 @@ import test_oracle_gamma as t_gamma
 import test_oracle_gemm as t_gemm
 import test_oracle_mask as t_mask
 import test_oracle_ternary as t_tern
+import test_oracle_optimizer as t_opt
 import test_oracle_variants as t_var
 
 
@@ -97,6 +98,31 @@ def _effective_weight_ignores_m(W_bits, n_keep, m=8):
     return _ORIG_EFF(W_bits, n_keep, 8)
 
 
+def _adamw_coupled_decay(W_bits, g, m, v, step, lr, beta1=0.9, beta2=0.95, eps=1e-5, weight_decay=0.1,
+                         grad_scale=1.0):
+    W = sb.bf16_to_f64(W_bits)
+    gs = np.asarray(g, np.float64) * grad_scale + weight_decay * W     # L2 in the gradient, not decoupled
+    m1 = beta1 * np.asarray(m, np.float64) + (1 - beta1) * gs
+    v1 = beta2 * np.asarray(v, np.float64) + (1 - beta2) * gs * gs
+    W1 = W - lr * (m1 / (1 - beta1 ** step)) / (np.sqrt(v1 / (1 - beta2 ** step)) + eps)
+    return W1, sb.f64_to_bf16_bits(W1), m1, v1
+
+
+def _adamw_no_bias_correction(W_bits, g, m, v, step, lr, beta1=0.9, beta2=0.95, eps=1e-5, weight_decay=0.1,
+                              grad_scale=1.0):
+    W = sb.bf16_to_f64(W_bits)
+    gs = np.asarray(g, np.float64) * grad_scale
+    m1 = beta1 * np.asarray(m, np.float64) + (1 - beta1) * gs
+    v1 = beta2 * np.asarray(v, np.float64) + (1 - beta2) * gs * gs
+    W1 = W * (1 - lr * weight_decay) - lr * m1 / (np.sqrt(v1) + eps)
+    return W1, sb.f64_to_bf16_bits(W1), m1, v1
+
+
+def _bf16_via_float32(x):
+    from sbl_inputs import f32_to_bf16_bits
+    return f32_to_bf16_bits(np.asarray(x, np.float64).astype(np.float32))
+
+
 _ORIG_PACK = sb.pack_codes
 
 
@@ -145,6 +171,12 @@ MUTANTS = [
      [t_var.test_mask_grad_zeroes_masked_slots_only]),
     ("N:4 packed as N:8 groups", "effective_weight", _effective_weight_ignores_m,
      [lambda: t_var.test_pack_n_of_4_planes(2)]),
+    ("AdamW with coupled weight decay", "adamw_update", _adamw_coupled_decay,
+     [lambda: t_opt.test_adamw_matches_torch(2)]),
+    ("AdamW without bias correction", "adamw_update", _adamw_no_bias_correction,
+     [t_opt.test_adamw_first_step_closed_form]),
+    ("bf16 rounding through float32 (double rounding)", "f64_to_bf16_bits", _bf16_via_float32,
+     [t_opt.test_bf16_rounding_no_double_rounding]),
 ]
 
 
