@@ -16,7 +16,7 @@ Metric: tokens per second of whole steps.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
        python bench.py --workload 4     (decode: per-layer latency at 1/8/64 tokens, 6/4/2:8)
-       python bench.py --variants       (every N of N:8, 2:4 and the two ablations, on the 3B-like matrices)
+       python bench.py --variants       (every N of N:8, 2:4, the two ablations and the AdamW step + repack)
 """
 from __future__ import annotations
 
@@ -263,8 +263,10 @@ def _bwd_sources_sha() -> str:
 
 def run_variants(args, wl):
     """The variant rows on the workload's matrices: quant/mask/pack for every N of N:8, 2:4 and the
-    mask-from-quantized-weight ablation (algorithmic 2.375 B per weight), and the mask-without-grad
-    ablation on float32 dW buffers of the same shapes (8.125 B per weight: dW read and written, mask)."""
+    mask-from-quantized-weight ablation (algorithmic 2.375 B per weight), the mask-without-grad
+    ablation on float32 dW buffers of the same shapes (8.125 B per weight: dW read and written, mask),
+    and the AdamW step + repack (24.5 B per weight: W, dW, m, v and the previous mask read; W, m, v,
+    the new mask and the codes written)."""
     import numpy as np
     import torch
 
@@ -313,6 +315,17 @@ def run_variants(args, wl):
             sbl.mask_grad(dW, mk)
     ms = timed(mg)
     gbs = 8.125 * n_w / (ms * 1e-3) / 1e9
+    # optimizer step + repack: reads W, dW, m, v, the previous mask; writes W, m, v, mask, codes
+    ms_moments = [(torch.zeros_like(dW), torch.zeros_like(dW)) for dW in dWs]
+    new_masks = [torch.empty_like(mk) for (_, mk, _, _) in outs]
+    flips = [torch.zeros((1,), dtype=torch.int64, device=dev) for _ in outs]
+
+    def opt():
+        for W, dW, (mm, vv), (c, mk, g, ws), mk2, fl in zip(Ws, dWs, ms_moments, outs, new_masks, flips):
+            sbl.adamw_repack(W, dW, mm, vv, step=2, lr=1e-5, n_keep=6, mask_prev=mk, mask=mk2, codes=c, gamma=g,
+                             flips=fl, workspace=ws)
+    ms_opt = timed(opt)
+    gbs_opt = 24.5 * n_w / (ms_opt * 1e-3) / 1e9
     line = {"metric": "Sparse-BitLinear variants: quant/mask/pack per N:M pattern and mask-without-grad, "
                       "7 linears of a 3B-like layer",
             "value": rows[2]["ms"], "unit": "ms per layer (6:8 quant/mask/pack)", "n_gpus": 1,
@@ -320,7 +333,9 @@ def run_variants(args, wl):
             "dtype": "bf16 in, 2-bit codes + mask plane out", "data": "synthetic",
             "config": {"workload": wl.name, "weights": n_w},
             "quant_mask_pack": rows,
-            "mask_grad": {"ms": round(ms, 4), "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}}
+            "mask_grad": {"ms": round(ms, 4), "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)},
+            "adamw_repack": {"ms": round(ms_opt, 4), "GBps": round(gbs_opt, 1),
+                             "frac_hbm": round(gbs_opt / HBM_PEAK_GBS, 4), "bytes_per_weight": 24.5}}
     print(json.dumps(line), flush=True)
 
 

@@ -154,6 +154,48 @@ SBL_API int sbl_quant_mask_pack_nm(const uint16_t* W_bf16, int64_t d_out, int64_
  */
 SBL_API int sbl_mask_grad(float* dW, const uint8_t* mask, int64_t d_out, int64_t d_in, void* hip_stream);
 
+/* Optimizer step followed by the next step's packing ([SUM] 方法步骤详情 step
+ * (8): AdamW updates the master weight, with beta = (0.9, 0.95), eps = 1e-5,
+ * weight decay 0.1 and gradient clipping at 1.0; step (2) of the next step
+ * recomputes the mask from the new W; the mask flip count is the training
+ * diagnostic behind the masks-recomputed-every-step design of 核心方法).
+ *
+ * In place on W, m, v, one read of each:
+ *   g      = dW * grad_scale        (grad_scale: the caller's global-norm clip
+ *                                    factor, min(1, clip / ||g||) over every
+ *                                    parameter, which no single layer sees)
+ *   m'     = beta1 m + (1 - beta1) g,   v' = beta2 v + (1 - beta2) g^2
+ *   W'     = W (1 - lr wd) - (lr / (1 - beta1^t)) m' / (sqrt(v') / sqrt(1 - beta2^t) + eps)
+ *            in float32 (the form of torch.optim.AdamW), rounded once to bf16;
+ * then, from W', what sbl_quant_mask_pack_nm(W', n_keep, m_group, 0) returns
+ * (gamma, codes, mask plane; bit-identical to calling it on W'), and the
+ * number of slots whose mask bit differs from mask_prev.
+ *
+ * W_bf16      : [d_out, d_in] bf16, updated.        d_in % 8 == 0.
+ * dW          : [d_out, d_in] float32 gradient (sbl_backward's dW).
+ * m, v        : [d_out, d_in] float32 AdamW moments, updated (zeros at t = 1).
+ * hp          : HOST pointer; step t >= 1, 0 <= beta < 1, eps > 0, lr >= 0,
+ *               weight_decay >= 0, grad_scale >= 0, all finite.
+ * mask_prev   : the previous mask plane, or NULL (then no flip count).  May
+ *               equal mask (each byte is read before it is overwritten).
+ * mask        : [d_out, d_in/8] new mask plane (required).
+ * codes, gamma: as sbl_quant_mask_pack.
+ * flips       : one uint64 in device memory, written when mask_prev is given;
+ *               may be NULL.
+ * workspace   : sbl_adamw_repack_workspace_size(d_out, d_in) bytes.
+ * All 16-byte aligned except gamma, flips (4 / 8) and the mask planes.
+ */
+typedef struct {
+  float lr, beta1, beta2, eps, weight_decay, grad_scale;
+  int64_t step;
+} sbl_adamw_params;
+
+SBL_API size_t sbl_adamw_repack_workspace_size(int64_t d_out, int64_t d_in);
+SBL_API int sbl_adamw_repack(uint16_t* W_bf16, const float* dW, float* m, float* v, int64_t d_out, int64_t d_in,
+                             const sbl_adamw_params* hp, int n_keep, int m_group, const uint8_t* mask_prev,
+                             uint8_t* mask, uint16_t* codes, float* gamma, uint64_t* flips, void* workspace,
+                             size_t workspace_bytes, void* hip_stream);
+
 /* ------------------------------------------------------------------------ */
 /* Activation side                                                            */
 /* ------------------------------------------------------------------------ */

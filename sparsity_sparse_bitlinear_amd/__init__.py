@@ -46,6 +46,9 @@ _SIGNATURES = {
     "sbl_quant_mask_pack_nm": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                         _c_size, _c_ptr]),
     "sbl_mask_grad": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr]),
+    "sbl_adamw_repack_workspace_size": (_c_size, [_c_i64, _c_i64]),
+    "sbl_adamw_repack": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, ctypes.c_void_p, _c_int, _c_int,
+                                  _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "sbl_act_quant": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "sbl_forward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
@@ -58,6 +61,13 @@ _SIGNATURES = {
     "sbl_version": (ctypes.c_char_p, []),
     "sbl_test_round_mean": (_c_int, [ctypes.POINTER(ctypes.c_uint32), _c_int, _c_i64, ctypes.POINTER(ctypes.c_float)]),
 }
+
+
+class AdamwParams(ctypes.Structure):
+    """sbl_adamw_params (host struct)."""
+    _fields_ = [("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+                ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("grad_scale", ctypes.c_float),
+                ("step", ctypes.c_int64)]
 
 
 class SblError(RuntimeError):
@@ -166,6 +176,47 @@ def quant_mask_pack(W: torch.Tensor, n_keep: int = 6, *, m: int = 8, from_quanti
                                       _ptr(gamma), _ptr(workspace), workspace.numel(), _stream(stream)),
            "sbl_quant_mask_pack_nm")
     return codes, mask, gamma
+
+
+def adamw_repack(W: torch.Tensor, dW: torch.Tensor, m: torch.Tensor, v: torch.Tensor, *, step: int, lr: float,
+                 beta1: float = 0.9, beta2: float = 0.95, eps: float = 1e-5, weight_decay: float = 0.1,
+                 grad_scale: float = 1.0, n_keep: int = 6, m_group: int = 8,
+                 mask_prev: Optional[torch.Tensor] = None, mask: Optional[torch.Tensor] = None,
+                 codes: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
+                 flips: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """AdamW step on the bf16 master ``W`` (in place, with ``m``, ``v``) and the next step's packing.
+
+    Returns ``(codes, mask, gamma, flips)``; ``flips`` (int64 [1]) is None without ``mask_prev``.
+    """
+    _as_bits16(W, "W")
+    d_out, d_in = W.shape
+    dev = W.device
+    for t, n in ((dW, "dW"), (m, "m"), (v, "v")):
+        _out(t, (d_out, d_in), (torch.float32,), dev, n)
+    if codes is None:
+        codes = torch.empty((d_out, d_in // 8), dtype=torch.int16, device=dev)
+    _out(codes, (d_out, d_in // 8), (torch.int16, torch.uint16), dev, "codes")
+    if mask is None:
+        mask = torch.empty((d_out, d_in // 8), dtype=torch.uint8, device=dev)
+    _out(mask, (d_out, d_in // 8), (torch.uint8,), dev, "mask")
+    if mask_prev is not None:
+        _out(mask_prev, (d_out, d_in // 8), (torch.uint8,), dev, "mask_prev")
+        if flips is None:
+            flips = torch.zeros((1,), dtype=torch.int64, device=dev)
+        _out(flips, (1,), (torch.int64,), dev, "flips")
+    if gamma is None:
+        gamma = torch.empty((1,), dtype=torch.float32, device=dev)
+    _out(gamma, (1,), (torch.float32,), dev, "gamma")
+    need = lib.sbl_adamw_repack_workspace_size(d_out, d_in)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    _out(workspace, (workspace.numel(),), (torch.uint8,), dev, "workspace")
+    hp = AdamwParams(lr, beta1, beta2, eps, weight_decay, grad_scale, int(step))
+    _check(lib.sbl_adamw_repack(_ptr(W), _ptr(dW), _ptr(m), _ptr(v), d_out, d_in,
+                                ctypes.c_void_p(ctypes.addressof(hp)), int(n_keep), int(m_group), _ptr(mask_prev), _ptr(mask),
+                                _ptr(codes), _ptr(gamma), _ptr(flips if mask_prev is not None else None),
+                                _ptr(workspace), workspace.numel(), _stream(stream)), "sbl_adamw_repack")
+    return codes, mask, gamma, (flips if mask_prev is not None else None)
 
 
 def mask_grad(dW: torch.Tensor, mask: torch.Tensor, *, stream=None) -> torch.Tensor:

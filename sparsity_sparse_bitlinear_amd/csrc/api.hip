@@ -6,6 +6,8 @@
 
 #include <algorithm>
 
+#include <cmath>
+
 #include "sbl_internal.h"
 
 namespace sbl {
@@ -113,6 +115,43 @@ SBL_API int sbl_mask_grad(float* dW, const uint8_t* mask, int64_t d_out, int64_t
   SBL_REQUIRE(aligned(dW, 16), SBL_ERR_INVALID_ARG, "dW must be 16-byte aligned");
   hipError_t e = launch_mask_grad(dW, mask, d_out, d_in, (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "sbl_mask_grad launch");
+  return SBL_OK;
+}
+
+SBL_API size_t sbl_adamw_repack_workspace_size(int64_t d_out, int64_t d_in) {
+  if (check_dims(d_out, d_in) != SBL_OK) return 0;
+  return quant_workspace_bytes(d_out, d_in);
+}
+
+SBL_API int sbl_adamw_repack(uint16_t* W_bf16, const float* dW, float* m, float* v, int64_t d_out, int64_t d_in,
+                             const sbl_adamw_params* hp, int n_keep, int m_group, const uint8_t* mask_prev,
+                             uint8_t* mask, uint16_t* codes, float* gamma, uint64_t* flips, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+  int rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(hp, SBL_ERR_INVALID_ARG, "hp (host pointer) must be non-NULL");
+  const bool fin = std::isfinite(hp->lr) && std::isfinite(hp->beta1) && std::isfinite(hp->beta2) &&
+                   std::isfinite(hp->eps) && std::isfinite(hp->weight_decay) && std::isfinite(hp->grad_scale);
+  SBL_REQUIRE(fin && hp->step >= 1 && hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f &&
+                  hp->beta2 < 1.0f && hp->eps > 0.0f && hp->lr >= 0.0f && hp->weight_decay >= 0.0f &&
+                  hp->grad_scale >= 0.0f,
+              SBL_ERR_INVALID_ARG, "AdamW parameters out of range (step >= 1, 0 <= beta < 1, eps > 0, lr, wd, "
+              "grad_scale >= 0, all finite)");
+  SBL_REQUIRE(mask_pattern_supported(n_keep, m_group), SBL_ERR_UNSUPPORTED,
+              "n_keep=%d, m_group=%d: supported patterns are N:8 and N:4 with 1 <= N <= M", n_keep, m_group);
+  SBL_REQUIRE(W_bf16 && dW && m && v && mask && codes && gamma, SBL_ERR_INVALID_ARG,
+              "W, dW, m, v, mask, codes and gamma must be non-NULL");
+  SBL_REQUIRE(aligned(W_bf16, 16) && aligned(dW, 16) && aligned(m, 16) && aligned(v, 16) && aligned(codes, 16) &&
+                  aligned(gamma, 4) && (!flips || aligned(flips, 8)),
+              SBL_ERR_INVALID_ARG, "W, dW, m, v, codes must be 16-byte aligned; gamma 4-byte, flips 8-byte");
+  const size_t need = quant_workspace_bytes(d_out, d_in);
+  SBL_REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 16), SBL_ERR_WORKSPACE,
+              "workspace of %zu bytes (16-byte aligned) required, got %zu", need,
+              workspace ? workspace_bytes : (size_t)0);
+  AdamwArgs a{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->grad_scale, hp->step};
+  hipError_t e = launch_adamw_repack(W_bf16, dW, m, v, d_out, d_in, a, n_keep, m_group, mask_prev, mask, codes,
+                                     gamma, (unsigned long long*)flips, workspace, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_adamw_repack launch");
   return SBL_OK;
 }
 

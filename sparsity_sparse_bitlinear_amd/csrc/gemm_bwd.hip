@@ -35,11 +35,6 @@ using namespace gemm;
 
 constexpr int kBK = 32;  // k elements (bf16) per LDS row
 
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  typedef float v2f __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
-}
 
 // Two 2-bit codes in bits 0-1 and 16-17 -> two bf16 values {0, +1 = 0x3F80, -1 = 0xBF80}.
 __device__ __forceinline__ uint32_t code_pair_to_bf16x2(uint32_t s) {

@@ -26,11 +26,6 @@ namespace {
 
 using namespace gemm;
 
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  typedef float v2f __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
-}
 
 // 4 two-bit codes (one byte) -> 4 int8 values.
 __device__ __forceinline__ uint32_t expand4(uint32_t byte4codes) {

@@ -30,11 +30,6 @@ using namespace gemm;
 // each): one block per CU.  Loading 64 KB per K step for 4M multiply-adds
 // halves the bytes each CU pulls through its L1 per matrix instruction
 // compared with a 256 x 128 tile, which is what the L2-to-CU path can feed.
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-  typedef float v2f __attribute__((ext_vector_type(2)));
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
-}
 
 constexpr int kNT = 512;                  // threads per block
 constexpr int kBNn = 256;                 // block cols (N)

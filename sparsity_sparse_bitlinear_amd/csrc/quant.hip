@@ -15,6 +15,8 @@
 //                     (N:8 for any N, N:4 such as 2:4 as two groups per word,
 //                     and the mask-from-quantized-weight ablation)
 // plus k_mask_grad, the mask-without-grad ablation on a dW buffer.
+#include <cmath>
+
 #include "sbl_internal.h"
 
 namespace sbl {
@@ -238,8 +240,10 @@ constexpr int kSumWords = 10;  // 320 bits: enough for any finite bf16 matrix be
 __global__ __launch_bounds__(256) void k_gamma_finalize(const AbsumPartial* __restrict__ part,
                                                         const unsigned long long* __restrict__ hist_in,
                                                         int nblocks, unsigned long long count,
-                                                        float* __restrict__ gamma) {
+                                                        float* __restrict__ gamma,
+                                                        unsigned long long* __restrict__ flips) {
   __shared__ U128 red[256];
+  __shared__ unsigned long long fl[256];
   __shared__ unsigned long long bins[256];
   __shared__ int flags[256];
   __shared__ int any_flag;
@@ -247,24 +251,29 @@ __global__ __launch_bounds__(256) void k_gamma_finalize(const AbsumPartial* __re
   if (tid == 0) any_flag = 0;
   __syncthreads();
   U128 acc = {0, 0};
+  unsigned long long nflip = 0;
   int any = 0;
   for (int b = tid; b < nblocks; b += 256) {
     const AbsumPartial p = part[b];
     U128 v = {p.lo, p.hi};
     add128(acc, v);
+    nflip += p.pad;
     any |= (p.flag != 0);
   }
   if (any) any_flag = 1;
   red[tid] = acc;
+  fl[tid] = nflip;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
     if (tid < s) {
       U128 a = red[tid];
       add128(a, red[tid + s]);
       red[tid] = a;
+      fl[tid] += fl[tid + s];
     }
     __syncthreads();
   }
+  if (flips && tid == 0) *flips = fl[0];
   // Histogram bins of the blocks that have one: the flags are staged in LDS so
   // that the serial walk over blocks reads global memory only for flagged ones.
   unsigned long long bin = 0;
@@ -329,19 +338,9 @@ __device__ __forceinline__ uint32_t nth_of4(uint32_t a, uint32_t b, uint32_t c, 
   return N == 1 ? a : N == 2 ? b : N == 3 ? c : d;
 }
 
-template <int N, int M, bool FQ>
-__device__ __forceinline__ void pack_group(const uint4 v, uint32_t gamma_bits, uint16_t& code_out,
-                                           uint8_t& mask_out) {
-  uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                   v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
-  bool nz[8];
-  uint32_t u[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    nz[j] = above_half_gamma(h[j] & 0x7FFFu, gamma_bits);
-    const uint32_t key = FQ ? (nz[j] ? 1u : 0u) : (h[j] & 0x7FFFu);
-    u[j] = (key << 3) | (uint32_t)(7 - j);
-  }
+// Keep bits (bit j = slot j) of N:M on the 8 rank keys u[j] (distinct).
+template <int N, int M>
+__device__ __forceinline__ uint32_t keep_bits(const uint32_t (&u)[8]) {
   uint32_t thr_lo = 0, thr_hi = 0;
   if constexpr (M == 8 && N < 8) {
     uint32_t s[8];
@@ -358,15 +357,43 @@ __device__ __forceinline__ void pack_group(const uint4 v, uint32_t gamma_bits, u
     thr_lo = nth_of4<N>(u[0], u[1], u[2], u[3]);
     thr_hi = nth_of4<N>(u[4], u[5], u[6], u[7]);
   }
-  uint32_t code = 0, mask = 0;
+  uint32_t mask = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) mask |= ((N == M) || (u[j] >= (j < 4 ? thr_lo : thr_hi)) ? 1u : 0u) << j;
+  return mask;
+}
+
+// Rank keys of the magnitude mask: (15-bit |w| bits << 3) | (7 - j).
+__device__ __forceinline__ void mag_keys(const uint32_t (&h)[8], uint32_t (&u)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) u[j] = ((h[j] & 0x7FFFu) << 3) | (uint32_t)(7 - j);
+}
+
+// 2-bit codes of the 8 slots: kept and |w| > gamma/2 -> sign code.
+__device__ __forceinline__ uint16_t codes_of(const uint32_t (&h)[8], uint32_t mask, uint32_t gamma_bits) {
+  uint32_t code = 0;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const bool keep = (N == M) || (u[j] >= (j < 4 ? thr_lo : thr_hi));
-    const uint32_t c = (keep && nz[j]) ? ((h[j] & 0x8000u) ? 3u : 1u) : 0u;
-    code |= c << (2 * j);
-    mask |= (keep ? 1u : 0u) << j;
+    const bool nz = ((mask >> j) & 1u) && above_half_gamma(h[j] & 0x7FFFu, gamma_bits);
+    code |= (nz ? ((h[j] & 0x8000u) ? 3u : 1u) : 0u) << (2 * j);
   }
-  code_out = (uint16_t)code;
+  return (uint16_t)code;
+}
+
+template <int N, int M, bool FQ>
+__device__ __forceinline__ void pack_group(const uint4 v, uint32_t gamma_bits, uint16_t& code_out,
+                                           uint8_t& mask_out) {
+  const uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                         v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+  uint32_t u[8];
+  if constexpr (FQ) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = ((above_half_gamma(h[j] & 0x7FFFu, gamma_bits) ? 1u : 0u) << 3) | (uint32_t)(7 - j);
+  } else {
+    mag_keys(h, u);
+  }
+  const uint32_t mask = keep_bits<N, M>(u);
+  code_out = codes_of(h, mask, gamma_bits);
   mask_out = (uint8_t)mask;
 }
 
@@ -416,6 +443,136 @@ __global__ __launch_bounds__(256) void k_mask_grad(float4* __restrict__ dW, cons
     b.w = (m & 128u) ? b.w : 0.0f;
     dW[2 * g] = a;
     dW[2 * g + 1] = b;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Optimizer step + repack ([SUM] 方法步骤详情 step (8), then step (2) of the next
+// step): AdamW on the bf16 master weight, and in the same pass over W the new
+// mask, its flips against the previous one and the exact |W'| partial sums;
+// gamma and the codes follow in the two launches after it.
+// ---------------------------------------------------------------------------
+
+// Host-folded hyper-parameters: m' = b1 m + c1 g, v' = b2 v + c2 g^2 (g scaled
+// by gs), W' = W decay - step_size m' / (sqrt(v') / sqrt_bc2 + eps), the
+// arithmetic of torch.optim.AdamW in float32 with one rounding of W' to bf16.
+struct AdamHp {
+  float b1, c1, b2, c2, gs, step_size, sqrt_bc2, eps, decay;
+};
+
+template <int N, int M>
+__global__ __launch_bounds__(kAbsumThreads) void k_adamw_mask(uint4* __restrict__ W, const float4* __restrict__ g,
+                                                              float4* __restrict__ mo, float4* __restrict__ vo,
+                                                              int64_t n_groups, AdamHp hp,
+                                                              const uint8_t* __restrict__ mask_prev,
+                                                              uint8_t* __restrict__ mask,
+                                                              AbsumPartial* __restrict__ part,
+                                                              unsigned long long* __restrict__ hist_out) {
+  __shared__ unsigned long long hist[256];
+  __shared__ U128 red[kAbsumThreads];
+  __shared__ unsigned long long fred[kAbsumThreads];
+  __shared__ int block_any;
+  const int tid = threadIdx.x;
+  hist[tid] = 0;
+  if (tid == 0) block_any = 0;
+  __syncthreads();
+
+  U128 acc = {0, 0};
+  double fsum = 0.0;  // exact while it holds at most 256 window values
+  int fcount = 0;
+  bool any_hist = false;
+  unsigned long long nflip = 0;
+  const int64_t stride = (int64_t)gridDim.x * kAbsumThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kAbsumThreads + tid; i < n_groups; i += stride) {
+    const uint4 w = W[i];
+    const float4 g0 = g[2 * i], g1 = g[2 * i + 1];
+    float4 m0 = mo[2 * i], m1 = mo[2 * i + 1], v0 = vo[2 * i], v1 = vo[2 * i + 1];
+    const uint32_t prev = mask_prev ? mask_prev[i] : 0u;
+    float wv[8] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u),
+                   __uint_as_float(w.z << 16), __uint_as_float(w.z & 0xFFFF0000u),
+                   __uint_as_float(w.w << 16), __uint_as_float(w.w & 0xFFFF0000u)};
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    float mv[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float gj = gv[j] * hp.gs;
+      mv[j] = hp.b1 * mv[j] + hp.c1 * gj;
+      vv[j] = hp.b2 * vv[j] + hp.c2 * (gj * gj);
+      const float denom = sqrtf(vv[j]) / hp.sqrt_bc2 + hp.eps;
+      wv[j] = wv[j] * hp.decay - hp.step_size * (mv[j] / denom);
+    }
+    const uint4 wn = make_uint4(cvt_pk_bf16(wv[0], wv[1]), cvt_pk_bf16(wv[2], wv[3]), cvt_pk_bf16(wv[4], wv[5]),
+                                cvt_pk_bf16(wv[6], wv[7]));
+    W[i] = wn;
+    mo[2 * i] = make_float4(mv[0], mv[1], mv[2], mv[3]);
+    mo[2 * i + 1] = make_float4(mv[4], mv[5], mv[6], mv[7]);
+    vo[2 * i] = make_float4(vv[0], vv[1], vv[2], vv[3]);
+    vo[2 * i + 1] = make_float4(vv[4], vv[5], vv[6], vv[7]);
+    // the next step's mask, from |W'|
+    const uint32_t h[8] = {wn.x & 0xFFFFu, wn.x >> 16, wn.y & 0xFFFFu, wn.y >> 16,
+                           wn.z & 0xFFFFu, wn.z >> 16, wn.w & 0xFFFFu, wn.w >> 16};
+    uint32_t u[8];
+    mag_keys(h, u);
+    const uint32_t keep = keep_bits<N, M>(u);
+    mask[i] = (uint8_t)keep;
+    nflip += (unsigned long long)__popc((prev ^ keep) & 0xFFu);
+    // exact partial sum of |W'| (as k_absum)
+    if (__builtin_expect(in_fast_window(wn), 1)) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fsum += (double)__uint_as_float((h[j] & 0x7FFFu) << 16);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) absum_half(h[j], acc, hist, any_hist);
+    }
+    if (++fcount == 32) {
+      const U128 f = {(unsigned long long)ldexp(fsum, 134 - kWinLo), 0ull};
+      add128(acc, f);
+      fsum = 0.0;
+      fcount = 0;
+    }
+  }
+  {
+    const U128 f = {(unsigned long long)ldexp(fsum, 134 - kWinLo), 0ull};
+    add128(acc, f);
+  }
+  if (any_hist) block_any = 1;  // benign race: every writer stores 1
+  red[tid] = acc;
+  fred[tid] = nflip;
+  __syncthreads();
+  for (int st = kAbsumThreads / 2; st > 0; st >>= 1) {
+    if (tid < st) {
+      U128 a = red[tid];
+      add128(a, red[tid + st]);
+      red[tid] = a;
+      fred[tid] += fred[tid + st];
+    }
+    __syncthreads();
+  }
+  const int any = block_any;
+  if (tid == 0) {
+    AbsumPartial p;
+    p.lo = red[0].lo;
+    p.hi = red[0].hi;
+    p.flag = (unsigned long long)any;
+    p.pad = fred[0];
+    part[blockIdx.x] = p;
+  }
+  if (any) hist_out[(size_t)blockIdx.x * 256 + tid] = hist[tid];
+}
+
+// Codes of the updated W from its mask plane and gamma (pass 2).
+__global__ __launch_bounds__(256) void k_codes_from_mask(const uint4* __restrict__ W, const uint8_t* __restrict__ mask,
+                                                         int64_t n_groups, const float* __restrict__ gamma_p,
+                                                         uint16_t* __restrict__ codes) {
+  const uint32_t gamma_bits = __float_as_uint(*gamma_p);
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_groups; i += stride) {
+    const uint4 w = W[i];
+    const uint32_t h[8] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16,
+                           w.z & 0xFFFFu, w.z >> 16, w.w & 0xFFFFu, w.w >> 16};
+    codes[i] = codes_of(h, mask[i], gamma_bits);
   }
 }
 
@@ -476,11 +633,72 @@ hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in
   unsigned long long* hist = (unsigned long long*)((char*)ws + (size_t)nb * sizeof(AbsumPartial));
   hipLaunchKernelGGL(k_absum, dim3(nb), dim3(kAbsumThreads), 0, s, (const uint4*)W, n_groups, part, hist);
   hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(256), 0, s, (const AbsumPartial*)part,
-                     (const unsigned long long*)hist, nb, (unsigned long long)(d_out * d_in), gamma);
+                     (const unsigned long long*)hist, nb, (unsigned long long)(d_out * d_in), gamma,
+                     (unsigned long long*)nullptr);
   int64_t pb = (n_groups + 1023) / 1024;
   if (pb > 65536) pb = 65536;
   hipLaunchKernelGGL(pack, dim3((unsigned)pb), dim3(256), 0, s, (const uint4*)W, n_groups, (const float*)gamma, codes,
                      mask);
+  return hipGetLastError();
+}
+
+using AdamKernel = void (*)(uint4*, const float4*, float4*, float4*, int64_t, AdamHp, const uint8_t*, uint8_t*,
+                           AbsumPartial*, unsigned long long*);
+
+static AdamKernel adam_kernel(int n, int m) {
+  if (m == 8) {
+    switch (n) {
+      case 1: return k_adamw_mask<1, 8>;
+      case 2: return k_adamw_mask<2, 8>;
+      case 3: return k_adamw_mask<3, 8>;
+      case 4: return k_adamw_mask<4, 8>;
+      case 5: return k_adamw_mask<5, 8>;
+      case 6: return k_adamw_mask<6, 8>;
+      case 7: return k_adamw_mask<7, 8>;
+      case 8: return k_adamw_mask<8, 8>;
+    }
+  } else if (m == 4) {
+    switch (n) {
+      case 1: return k_adamw_mask<1, 4>;
+      case 2: return k_adamw_mask<2, 4>;
+      case 3: return k_adamw_mask<3, 4>;
+      case 4: return k_adamw_mask<4, 4>;
+    }
+  }
+  return nullptr;
+}
+
+hipError_t launch_adamw_repack(uint16_t* W, const float* g, float* m, float* v, int64_t d_out, int64_t d_in,
+                               const AdamwArgs& a, int n_keep, int m_group, const uint8_t* mask_prev, uint8_t* mask,
+                               uint16_t* codes, float* gamma, unsigned long long* flips, void* ws, hipStream_t s) {
+  const AdamKernel k1 = adam_kernel(n_keep, m_group);
+  if (!k1) return hipErrorInvalidValue;
+  // hyper-parameters folded in double, then float32 (as torch's scalars)
+  const double bc1 = 1.0 - std::pow((double)a.beta1, (double)a.step);
+  const double bc2 = 1.0 - std::pow((double)a.beta2, (double)a.step);
+  AdamHp hp;
+  hp.b1 = a.beta1;
+  hp.c1 = (float)(1.0 - (double)a.beta1);
+  hp.b2 = a.beta2;
+  hp.c2 = (float)(1.0 - (double)a.beta2);
+  hp.gs = a.grad_scale;
+  hp.step_size = (float)((double)a.lr / bc1);
+  hp.sqrt_bc2 = (float)std::sqrt(bc2);
+  hp.eps = a.eps;
+  hp.decay = (float)(1.0 - (double)a.lr * (double)a.weight_decay);
+  const int64_t n_groups = d_out * d_in / 8;
+  const int nb = absum_blocks(n_groups);
+  AbsumPartial* part = (AbsumPartial*)ws;
+  unsigned long long* hist = (unsigned long long*)((char*)ws + (size_t)nb * sizeof(AbsumPartial));
+  hipLaunchKernelGGL(k1, dim3(nb), dim3(kAbsumThreads), 0, s, (uint4*)W, (const float4*)g, (float4*)m, (float4*)v,
+                     n_groups, hp, mask_prev, mask, part, hist);
+  hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(256), 0, s, (const AbsumPartial*)part,
+                     (const unsigned long long*)hist, nb, (unsigned long long)(d_out * d_in), gamma,
+                     mask_prev ? flips : (unsigned long long*)nullptr);
+  int64_t pb = (n_groups + 255) / 256;
+  if (pb > 65536) pb = 65536;
+  hipLaunchKernelGGL(k_codes_from_mask, dim3((unsigned)pb), dim3(256), 0, s, (const uint4*)W, (const uint8_t*)mask,
+                     n_groups, (const float*)gamma, codes);
   return hipGetLastError();
 }
 

@@ -43,6 +43,13 @@ constexpr int kWinHi = kWinLo + 56;
 constexpr int kFastHi = kWinLo + 37;
 
 // Partial results of one absum block (written to the workspace).
+// Two float32 -> two bf16 (round to nearest even) in one word, lo in bits 0-15.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){lo, hi}, v2bf));
+}
+
 struct AbsumPartial {
   unsigned long long lo;    // 128-bit fast-window sum, low word
   unsigned long long hi;    // high word
@@ -62,6 +69,15 @@ hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in
                                   bool from_quantized, uint16_t* codes, uint8_t* mask, float* gamma, void* ws,
                                   hipStream_t s);
 hipError_t launch_mask_grad(float* dW, const uint8_t* mask, int64_t d_out, int64_t d_in, hipStream_t s);
+
+// AdamW step + repack (quant.hip).  W, m, v updated in place.
+struct AdamwArgs {
+  float lr, beta1, beta2, eps, weight_decay, grad_scale;
+  int64_t step;
+};
+hipError_t launch_adamw_repack(uint16_t* W, const float* g, float* m, float* v, int64_t d_out, int64_t d_in,
+                               const AdamwArgs& a, int n_keep, int m_group, const uint8_t* mask_prev, uint8_t* mask,
+                               uint16_t* codes, float* gamma, unsigned long long* flips, void* ws, hipStream_t s);
 
 // Host/device: RN_float32(S * 2^-133 / count) for S given as 32-bit words.
 __host__ __device__ float round_mean_words(const uint32_t* w, int nwords, unsigned long long count);

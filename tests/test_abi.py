@@ -83,6 +83,38 @@ def test_mask_grad_validation():
     assert f(P, P, 256, 12, NULL) == SHAPE
 
 
+def test_adamw_repack_validation():
+    import sparsity_sparse_bitlinear_amd as sbl
+    ws = lib.sbl_adamw_repack_workspace_size(256, 256)
+    assert ws > 0 and lib.sbl_adamw_repack_workspace_size(256, 12) == 0
+    f = lib.sbl_adamw_repack
+
+    keep = []
+
+    def hp(**kw):
+        d = dict(lr=1e-3, beta1=0.9, beta2=0.95, eps=1e-5, weight_decay=0.1, grad_scale=1.0, step=1)
+        d.update(kw)
+        keep.append(sbl.AdamwParams(**d))      # alive until the call returns
+        return ctypes.c_void_p(ctypes.addressof(keep[-1]))
+
+    def call(h, n=6, m=8, W=P, mask=P, w=ws, flips=NULL):
+        return f(W, P, P, P, 256, 256, h, n, m, NULL, mask, P, P, flips, P, w, NULL)
+
+    assert call(NULL) == INVALID                                    # no parameters
+    assert call(hp(step=0)) == INVALID
+    assert call(hp(beta1=1.0)) == INVALID
+    assert call(hp(eps=0.0)) == INVALID
+    assert call(hp(lr=float("nan"))) == INVALID
+    assert call(hp(grad_scale=-1.0)) == INVALID
+    assert call(hp(), n=5, m=4) == UNSUPPORTED
+    assert call(hp(), W=NULL) == INVALID
+    assert call(hp(), mask=NULL) == INVALID
+    assert call(hp(), W=P_MIS) == INVALID
+    assert call(hp(), flips=ctypes.c_void_p(0x10004)) == INVALID  # flips not 8-byte aligned
+    assert call(hp(), w=ws - 1) == WORKSPACE
+    assert f(P, P, P, P, 256, 12, hp(), 6, 8, NULL, P, P, P, NULL, P, ws, NULL) == SHAPE
+
+
 def test_act_quant_validation():
     f = lib.sbl_act_quant
     assert f(NULL, 0, 256, NULL, NULL, NULL) == OK                   # T = 0 is a no-op

@@ -112,6 +112,70 @@ def test_mask_grad_parity(d_out, d_in):
         assert_grad_close(got, dW_sg)
 
 
+# Optimizer step + repack (AdamW on the bf16 master weight, then the next
+# step's gamma, mask, codes and the mask flip count).  W' within one bf16 step
+# of the float64 oracle (the kernel computes in float32), m' and v' to float32
+# accuracy; the packing of the W' the kernel wrote is bit-exact.
+@pytest.mark.parametrize("step", [1, 7])
+@pytest.mark.parametrize("n,m_group,d_out,d_in", [(6, 8, 200, 328), (2, 4, 333, 1032), (6, 8, 2048, 2048)])
+def test_adamw_repack_parity(step, n, m_group, d_out, d_in):
+    W = weight(81, step + d_in, d_out, d_in)
+    g_ = np.random.default_rng(step + d_out)
+    grad = (g_.standard_normal(W.shape) * 1e-3).astype(np.float32)
+    m0 = (g_.standard_normal(W.shape) * 1e-4).astype(np.float32) if step > 1 else np.zeros(W.shape, np.float32)
+    v0 = (g_.random(W.shape) * 1e-6).astype(np.float32) if step > 1 else np.zeros(W.shape, np.float32)
+    hp = dict(beta1=0.9, beta2=0.95, eps=1e-5, weight_decay=0.1, grad_scale=0.5)
+    lr = 2e-3
+    Wd = to_dev_bf16(W)
+    _, mprev, _ = sbl.quant_mask_pack(Wd, n, m=m_group)
+    md, vd = torch.from_numpy(m0).cuda(), torch.from_numpy(v0).cuda()
+    codes, mask, gamma, flips = sbl.adamw_repack(Wd, torch.from_numpy(grad).cuda(), md, vd, step=step, lr=lr,
+                                                 n_keep=n, m_group=m_group, mask_prev=mprev, **hp)
+    torch.cuda.synchronize()
+    W1_ref, _, m1_ref, v1_ref = oracle.adamw_update(W, grad, m0, v0, step, lr, **hp)
+    W1 = oracle.bf16_to_f64(bits16(Wd))
+    # within one bf16 step of the exact value, plus the float32 error of the two terms
+    # (where they cancel near zero the float32 error exceeds a bf16 step), and nearly
+    # always the nearest bf16 value
+    ulp = np.ldexp(1.0, np.floor(np.log2(np.maximum(np.abs(W1_ref), 2.0 ** -126))).astype(int) - 7)
+    W0 = oracle.bf16_to_f64(W)
+    decayed = W0 * (1 - lr * hp["weight_decay"])
+    terms = np.abs(decayed) + np.abs(W1_ref - decayed)
+    assert np.all(np.abs(W1 - W1_ref) < ulp + 2.0 ** -21 * terms)
+    exact = bits16(Wd) == oracle.f64_to_bf16_bits(W1_ref)
+    assert exact.mean() > 0.999, exact.mean()
+    # float32 error bound of a two-term update, relative to its terms (they may cancel)
+    gs = grad.astype(np.float64) * hp["grad_scale"]
+    m_terms = 0.9 * np.abs(m0) + 0.1 * np.abs(gs)
+    v_terms = 0.95 * np.abs(v0) + 0.05 * gs * gs
+    assert np.all(np.abs(md.cpu().numpy() - m1_ref) <= 2.0 ** -21 * m_terms + 1e-30)
+    assert np.all(np.abs(vd.cpu().numpy() - v1_ref) <= 2.0 ** -21 * v_terms + 1e-30)
+    rc, rm, rg = oracle.quant_mask_pack(bits16(Wd), n, m_group)
+    assert f32_bits(gamma.cpu().numpy()[0]) == f32_bits(rg)
+    np.testing.assert_array_equal(mask.cpu().numpy(), rm)
+    np.testing.assert_array_equal(bits16(codes), rc)
+    want_flips = oracle.mask_flips(oracle.unpack_mask(mprev.cpu().numpy()), oracle.unpack_mask(rm))
+    assert int(flips.item()) == want_flips
+
+
+def test_adamw_repack_in_place_mask_and_no_flips():
+    # mask_prev == mask (in place), and without mask_prev no flip count
+    W = weight(82, 0, 64, 256)
+    grad = torch.from_numpy((np.random.default_rng(1).standard_normal(W.shape) * 1e-2).astype(np.float32)).cuda()
+    Wa, Wb = to_dev_bf16(W), to_dev_bf16(W)
+    _, mk, _ = sbl.quant_mask_pack(Wa, 6)
+    prev = mk.clone()
+    ma, va = torch.zeros(W.shape, device="cuda"), torch.zeros(W.shape, device="cuda")
+    mb, vb = torch.zeros(W.shape, device="cuda"), torch.zeros(W.shape, device="cuda")
+    ca, _, ga, fa = sbl.adamw_repack(Wa, grad, ma, va, step=1, lr=1e-2, mask_prev=mk, mask=mk)
+    cb, mkb, gb, fb = sbl.adamw_repack(Wb, grad, mb, vb, step=1, lr=1e-2)
+    torch.cuda.synchronize()
+    assert fb is None
+    assert torch.equal(ca, cb) and torch.equal(mk, mkb) and torch.equal(ga, gb)
+    assert int(fa.item()) == oracle.mask_flips(oracle.unpack_mask(prev.cpu().numpy()),
+                                               oracle.unpack_mask(mkb.cpu().numpy()))
+
+
 def test_pack_boundary_rows():
     W = boundary_row_weight(24, 64)     # gamma = 1 exactly; |w| = 0.5 sits on the threshold
     check_pack(W, 8)
