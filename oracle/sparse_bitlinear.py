@@ -381,6 +381,59 @@ def backward_stop_gradient(dY_bits, w_eff, gamma, x_q, absmax, mask):
 
 
 # ----------------------------------------------------------------------------
+# Norm + activation quantization  [SUM] 方法步骤详情 step (3): x~ = Q_a(Norm(x))
+# ----------------------------------------------------------------------------
+
+RMS_THREADS = 256  # the reduction shape that fixes the float32 summation order
+
+
+def rmsnorm_bf16(x_bits: np.ndarray, g_bits, eps: float) -> np.ndarray:
+    """RMSNorm of each row in binary32, rounded to bf16: y = bf16((x * r) * g),
+    r = 1 / sqrt(fl(fl(ss / d) + eps)).
+
+    The pages name Norm(x) but not its kind; RMSNorm with a bf16 weight g (None:
+    ones) is the reading (the Qwen2.5 models they train use it), evaluated in
+    binary32 with the output in bf16, the activation dtype of the model.  Since
+    the result feeds an integer decision (x_q), the float32 summation order is
+    fixed and written out here: squares of bf16 values are exact in float32;
+    thread t of 256 adds the squares of 16-byte chunks t, t + 256, ... (8
+    elements each, in order) one at a time; the 64 partial sums of each wave are
+    combined pairwise across lane distances 32, 16, 8, 4, 2, 1 (the two lanes of
+    a pair add the same two values), and the four wave sums as
+    (w0 + w1) + (w2 + w3).
+    """
+    x = bf16_to_f64(x_bits).astype(np.float32)
+    T, d = x.shape
+    assert d % 8 == 0
+    f = np.float32
+    gv = np.ones(d, np.float32) if g_bits is None else bf16_to_f64(np.asarray(g_bits)).astype(np.float32)
+    nch = d // 8
+    out = np.zeros((T, d), np.uint16)
+    for t in range(T):
+        sq = (x[t] * x[t]).reshape(nch, 8)  # exact products
+        part = np.zeros(RMS_THREADS, np.float32)
+        for c0 in range(0, nch, RMS_THREADS):
+            cs = sq[c0:c0 + RMS_THREADS]
+            n = cs.shape[0]
+            for e in range(8):
+                part[:n] = part[:n] + cs[:, e]
+        for off in (32, 16, 8, 4, 2, 1):
+            idx = np.arange(RMS_THREADS)
+            part = part + part[idx ^ off]
+        w = part[::64]
+        ss = (w[0] + w[1]) + (w[2] + w[3])
+        r = f(1.0) / np.sqrt(f(ss / f(d)) + f(eps))
+        y = (x[t] * r) * gv
+        out[t] = f64_to_bf16_bits(y.astype(np.float64))
+    return out
+
+
+def rmsnorm_act_quant(x_bits: np.ndarray, g_bits, eps: float):
+    """Q_a(Norm(x)): (x_q int8, absmax float32) of the bf16 RMSNorm output."""
+    return act_quant(rmsnorm_bf16(x_bits, g_bits, eps))
+
+
+# ----------------------------------------------------------------------------
 # Optimizer step + repack  [SUM] 方法步骤详情 step (8) (AdamW updates W; its
 #                          hyper-parameters beta = (0.9, 0.95), eps = 1e-5,
 #                          weight decay 0.1, grad clip 1.0) and step (2) of the

@@ -13,6 +13,7 @@ import test_oracle_gamma as t_gamma
 import test_oracle_gemm as t_gemm
 import test_oracle_mask as t_mask
 import test_oracle_ternary as t_tern
+import test_oracle_norm as t_norm
 import test_oracle_optimizer as t_opt
 import test_oracle_variants as t_var
 
@@ -123,6 +124,17 @@ def _bf16_via_float32(x):
     return f32_to_bf16_bits(np.asarray(x, np.float64).astype(np.float32))
 
 
+_ORIG_RMS = sb.rmsnorm_bf16
+
+
+def _rmsnorm_sum_not_mean(x_bits, g_bits, eps):
+    x = sb.bf16_to_f64(x_bits)
+    d = x.shape[1]
+    return _ORIG_RMS(x_bits, g_bits, eps * d) if d == 1 else sb.f64_to_bf16_bits(
+        x / np.sqrt((x ** 2).sum(axis=1, keepdims=True) + eps) *
+        (1.0 if g_bits is None else sb.bf16_to_f64(np.asarray(g_bits))))
+
+
 _ORIG_PACK = sb.pack_codes
 
 
@@ -177,6 +189,8 @@ MUTANTS = [
      [t_opt.test_adamw_first_step_closed_form]),
     ("bf16 rounding through float32 (double rounding)", "f64_to_bf16_bits", _bf16_via_float32,
      [t_opt.test_bf16_rounding_no_double_rounding]),
+    ("RMSNorm with the sum of squares instead of the mean", "rmsnorm_bf16", _rmsnorm_sum_not_mean,
+     [lambda: t_norm.test_rmsnorm_within_bf16_rounding_of_float64(64)]),
 ]
 
 
