@@ -16,7 +16,7 @@ Metric: tokens per second of whole steps.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
        python bench.py --workload 4     (decode: per-layer latency at 1/8/64 tokens, 6/4/2:8)
-       python bench.py --variants       (every N of N:8, 2:4, the two ablations and the AdamW step + repack)
+       python bench.py --variants       (every N of N:8, 2:4, the two ablations, AdamW + repack, norm + act quant)
 """
 from __future__ import annotations
 
@@ -265,8 +265,9 @@ def run_variants(args, wl):
     """The variant rows on the workload's matrices: quant/mask/pack for every N of N:8, 2:4 and the
     mask-from-quantized-weight ablation (algorithmic 2.375 B per weight), the mask-without-grad
     ablation on float32 dW buffers of the same shapes (8.125 B per weight: dW read and written, mask),
-    and the AdamW step + repack (24.5 B per weight: W, dW, m, v and the previous mask read; W, m, v,
-    the new mask and the codes written)."""
+    the AdamW step + repack (24.5 B per weight: W, dW, m, v and the previous mask read; W, m, v,
+    the new mask and the codes written), and Q_a(Norm(x)) fused against the act quant alone on the
+    workload's activations (3 B per element + 4 B per token: the norm adds arithmetic, no bytes)."""
     import numpy as np
     import torch
 
@@ -326,6 +327,26 @@ def run_variants(args, wl):
                              flips=fl, workspace=ws)
     ms_opt = timed(opt)
     gbs_opt = 24.5 * n_w / (ms_opt * 1e-3) / 1e9
+    # Q_a(Norm(x)) fused against the act quant alone, on the workload's activations
+    from sbl_inputs import activation
+    T = max(wl.T)
+    xs = [torch.from_numpy(activation(wl.cfg, mi, T, L.d_in, dist=wl.act_dist).view(np.int16)).view(torch.bfloat16)
+          .to(dev) for mi, L in enumerate(wl.linears)]
+    gs = [torch.ones((L.d_in,), dtype=torch.bfloat16, device=dev) for L in wl.linears]
+    qs = [(torch.empty((T, L.d_in), dtype=torch.int8, device=dev), torch.empty((T,), device=dev))
+          for L in wl.linears]
+    n_x = sum(T * L.d_in for L in wl.linears)
+
+    def norm_q():
+        for x, g, (q, a) in zip(xs, gs, qs):
+            sbl.rmsnorm_act_quant(x, g, 1e-6, x_q=q, absmax=a)
+
+    def plain_q():
+        for x, (q, a) in zip(xs, qs):
+            sbl.act_quant(x, x_q=q, absmax=a)
+    ms_norm, ms_act = timed(norm_q), timed(plain_q)
+    bytes_x = 3 * n_x + 4 * T * len(xs)
+    del xs, qs
     line = {"metric": "Sparse-BitLinear variants: quant/mask/pack per N:M pattern and mask-without-grad, "
                       "7 linears of a 3B-like layer",
             "value": rows[2]["ms"], "unit": "ms per layer (6:8 quant/mask/pack)", "n_gpus": 1,
@@ -335,7 +356,11 @@ def run_variants(args, wl):
             "quant_mask_pack": rows,
             "mask_grad": {"ms": round(ms, 4), "GBps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)},
             "adamw_repack": {"ms": round(ms_opt, 4), "GBps": round(gbs_opt, 1),
-                             "frac_hbm": round(gbs_opt / HBM_PEAK_GBS, 4), "bytes_per_weight": 24.5}}
+                             "frac_hbm": round(gbs_opt / HBM_PEAK_GBS, 4), "bytes_per_weight": 24.5},
+            "rmsnorm_act_quant": {"tokens": T, "ms": round(ms_norm, 4),
+                                  "GBps": round(bytes_x / (ms_norm * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(bytes_x / (ms_norm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "act_quant_alone_ms": round(ms_act, 4)}}
     print(json.dumps(line), flush=True)
 
 

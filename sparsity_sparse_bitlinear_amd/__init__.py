@@ -51,6 +51,7 @@ _SIGNATURES = {
                                   _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "sbl_act_quant": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "sbl_forward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
+    "sbl_rmsnorm_act_quant": (_c_int, [_c_ptr, _c_ptr, ctypes.c_float, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "sbl_decode": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode_supported": (_c_int, [_c_i64, _c_i64]),
     "sbl_backward_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int]),
@@ -240,6 +241,26 @@ def act_quant(x: torch.Tensor, *, x_q: Optional[torch.Tensor] = None, absmax: Op
     _out(x_q, (T, d_in), (torch.int8,), x.device, "x_q")
     _out(absmax, (T,), (torch.float32,), x.device, "absmax")
     _check(lib.sbl_act_quant(_ptr(x), T, d_in, _ptr(x_q), _ptr(absmax), _stream(stream)), "sbl_act_quant")
+    return x_q, absmax
+
+
+def rmsnorm_act_quant(x: torch.Tensor, g: Optional[torch.Tensor] = None, eps: float = 1e-6, *,
+                      x_q: Optional[torch.Tensor] = None, absmax: Optional[torch.Tensor] = None, stream=None):
+    """Q_a(RMSNorm(x)) in one pass: ``(x_q int8 [T, d_in], absmax float32 [T])``; ``g`` bf16 [d_in] or None."""
+    _as_bits16(x, "x")
+    T, d_in = x.shape
+    if g is not None:
+        _as_bits16(g, "g")
+        if tuple(g.shape) != (d_in,):
+            raise ValueError(f"g has shape {tuple(g.shape)}, expected ({d_in},)")
+    if x_q is None:
+        x_q = torch.empty((T, d_in), dtype=torch.int8, device=x.device)
+    if absmax is None:
+        absmax = torch.empty((T,), dtype=torch.float32, device=x.device)
+    _out(x_q, (T, d_in), (torch.int8,), x.device, "x_q")
+    _out(absmax, (T,), (torch.float32,), x.device, "absmax")
+    _check(lib.sbl_rmsnorm_act_quant(_ptr(x), _ptr(g), float(eps), T, d_in, _ptr(x_q), _ptr(absmax),
+                                     _stream(stream)), "sbl_rmsnorm_act_quant")
     return x_q, absmax
 
 

@@ -171,6 +171,24 @@ SBL_API int sbl_act_quant(const uint16_t* x_bf16, int64_t T, int64_t d_in, int8_
   return SBL_OK;
 }
 
+SBL_API int sbl_rmsnorm_act_quant(const uint16_t* x_bf16, const uint16_t* g_bf16, float eps, int64_t T, int64_t d_in,
+                                  int8_t* x_q, float* absmax, void* hip_stream) {
+  int rc = check_tokens(T);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(d_in >= 8 && d_in % 8 == 0, SBL_ERR_SHAPE, "d_in=%lld must be a positive multiple of 8",
+              (long long)d_in);
+  SBL_REQUIRE(rmsnorm_supported(d_in), SBL_ERR_UNSUPPORTED, "d_in=%lld: rows up to 16384 are supported",
+              (long long)d_in);
+  SBL_REQUIRE(std::isfinite(eps) && eps >= 0.0f, SBL_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (T == 0) return SBL_OK;
+  SBL_REQUIRE(x_bf16 && x_q && absmax, SBL_ERR_INVALID_ARG, "x, x_q and absmax must be non-NULL");
+  SBL_REQUIRE(aligned(x_bf16, 16) && aligned(x_q, 16) && aligned(absmax, 4) && (!g_bf16 || aligned(g_bf16, 16)),
+              SBL_ERR_INVALID_ARG, "x, g, x_q must be 16-byte aligned; absmax 4-byte aligned");
+  hipError_t e = launch_rmsnorm_act_quant(x_bf16, g_bf16, eps, T, d_in, x_q, absmax, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_rmsnorm_act_quant launch");
+  return SBL_OK;
+}
+
 SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t* x_q, const float* absmax, int64_t T,
                         int64_t d_in, int64_t d_out, void* y, int y_dtype, void* hip_stream) {
   int rc = check_tokens(T);

@@ -86,6 +86,10 @@ __host__ __device__ float round_mean_words(const uint32_t* w, int nwords, unsign
 // activations, forward, backward launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_act_quant(const uint16_t* x, int64_t T, int64_t d_in, int8_t* xq, float* absmax, hipStream_t s);
+// RMSNorm + act quant (act.hip), d_in <= 16384.
+bool rmsnorm_supported(int64_t d_in);
+hipError_t launch_rmsnorm_act_quant(const uint16_t* x, const uint16_t* g, float eps, int64_t T, int64_t d_in,
+                                    int8_t* xq, float* absmax, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cus();

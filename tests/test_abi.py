@@ -115,6 +115,17 @@ def test_adamw_repack_validation():
     assert f(P, P, P, P, 256, 12, hp(), 6, 8, NULL, P, P, P, NULL, P, ws, NULL) == SHAPE
 
 
+def test_rmsnorm_act_quant_validation():
+    f = lib.sbl_rmsnorm_act_quant
+    assert f(NULL, NULL, 1e-6, 0, 256, NULL, NULL, NULL) == OK              # T = 0
+    assert f(P, NULL, 1e-6, 4, 100, P, P, NULL) == SHAPE
+    assert f(P, NULL, 1e-6, 4, 16392, P, P, NULL) == UNSUPPORTED
+    assert f(P, NULL, -1.0, 4, 256, P, P, NULL) == INVALID
+    assert f(P, NULL, float("inf"), 4, 256, P, P, NULL) == INVALID
+    assert f(NULL, NULL, 1e-6, 4, 256, P, P, NULL) == INVALID
+    assert f(P, P_MIS, 1e-6, 4, 256, P, P, NULL) == INVALID
+
+
 def test_act_quant_validation():
     f = lib.sbl_act_quant
     assert f(NULL, 0, 256, NULL, NULL, NULL) == OK                   # T = 0 is a no-op

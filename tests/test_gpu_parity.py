@@ -231,6 +231,21 @@ def test_act_parity(shape, dist, outl):
     check_act(activation(21, shape[1], *shape, dist=dist, outlier_frac=outl))
 
 
+# Q_a(Norm(x)) fused: bit-exact x_q and absmax against the oracle's binary32
+# RMSNorm (fixed order) followed by the exact act quant.
+@pytest.mark.parametrize("with_g", [False, True])
+@pytest.mark.parametrize("T,d_in", [(64, 2048), (33, 11008), (7, 64), (5, 4104), (2, 16384), (300, 896)])
+def test_rmsnorm_act_quant_parity(T, d_in, with_g):
+    x = activation(91, d_in + T, T, d_in, dist="student_t4", outlier_frac=0.001)
+    g = f32_to_bf16_bits(np.random.default_rng(d_in).uniform(0.25, 2.0, d_in).astype(np.float32)) if with_g else None
+    x[0] = 0  # a zero row
+    xq, a = sbl.rmsnorm_act_quant(to_dev_bf16(x), to_dev_bf16(g) if with_g else None, 1e-6)
+    torch.cuda.synchronize()
+    rq, ra = oracle.rmsnorm_act_quant(x, g, 1e-6)
+    np.testing.assert_array_equal(a.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+    np.testing.assert_array_equal(xq.cpu().numpy(), rq)
+
+
 def test_act_edge_rows():
     g = np.random.default_rng(9)
     x = f32_to_bf16_bits(g.standard_normal((8, 136)).astype(np.float32))
