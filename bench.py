@@ -6,8 +6,8 @@ Workload (default): the 3B-like decoder-layer linears q/o 2048->2048, k/v
 bf16 master weights ~ N(0, 0.02), Student-t(4) activations, dY ~ N(0, 1),
 all seeded synthetic data already resident in HBM.
 
-One step = for each of the 7 linears, in order:
-  sbl_quant_mask_pack (gamma, 6:8 mask, codes; recomputed every step)
+One step = sbl_quant_mask_pack_batch (gamma, 6:8 mask and codes of all 7 linears in one call,
+recomputed every step), then for each of the 7 linears, in order:
   sbl_act_quant       (per-token absmax int8)
   sbl_forward         (int8 MFMA, y bf16)
   sbl_backward        (dX and dW in one call: bf16 MFMA, dX bf16, dW float32 dense;
@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="index into sbl_inputs.WORKLOADS (2, 3, or 4 = decode)")
     ap.add_argument("--n-keep", type=int, default=6)
+    ap.add_argument("--pack", choices=("batch", "single"), default="batch",
+                    help="pack all linears in one batched call (default) or one call per linear")
     ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="print the per-linear breakdown to stderr")
@@ -116,7 +118,6 @@ def main():
             codes=torch.empty((d_out, d_in // 8), dtype=torch.int16, device=dev),
             mask=torch.empty((d_out, d_in // 8), dtype=torch.uint8, device=dev),
             gamma=torch.empty((1,), dtype=torch.float32, device=dev),
-            qws=torch.empty((max(16, sbl.quant_workspace_size(d_out, d_in)),), dtype=torch.uint8, device=dev),
             x_q=torch.empty((T, d_in), dtype=torch.int8, device=dev),
             absmax=torch.empty((T,), dtype=torch.float32, device=dev),
             y=torch.empty((T, d_out), dtype=torch.bfloat16, device=dev),
@@ -125,19 +126,31 @@ def main():
             bws=torch.empty((max(16, sbl.backward_workspace_size(T, d_in, d_out, sbl.BWD_DX | sbl.BWD_DW)),),
                             dtype=torch.uint8, device=dev),
         ))
+    qws = torch.empty((max(16, sbl.quant_batch_workspace_size([(L["d_out"], L["d_in"]) for L in layers])),),
+                      dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     t_gen = time.time() - t_gen
 
     parts = ("quant", "act", "fwd", "bwd")
 
     def step(events=None):
+        # the packing of every linear in one batched call (three launches), then each linear
+        if args.pack == "batch":
+            if events is not None:
+                events[0][0].record()
+            sbl.quant_mask_pack_batch([Lr["W"] for Lr in layers], n_keep, codes=[Lr["codes"] for Lr in layers],
+                                      masks=[Lr["mask"] for Lr in layers], gammas=[Lr["gamma"] for Lr in layers],
+                                      workspace=qws)
         for li, Lr in enumerate(layers):
             def mark(k):
                 if events is not None:
                     events[li][k].record()
-            mark(0)
-            sbl.quant_mask_pack(Lr["W"], n_keep, codes=Lr["codes"], mask=Lr["mask"], gamma=Lr["gamma"],
-                                workspace=Lr["qws"])
+            if args.pack == "single":
+                mark(0)
+                sbl.quant_mask_pack(Lr["W"], n_keep, codes=Lr["codes"], mask=Lr["mask"], gamma=Lr["gamma"],
+                                    workspace=qws)
+            elif li > 0:
+                mark(0)                 # the batch's time is counted once, on the first linear
             mark(1)
             sbl.act_quant(Lr["x"], x_q=Lr["x_q"], absmax=Lr["absmax"])
             mark(2)

@@ -144,6 +144,29 @@ SBL_API int sbl_quant_mask_pack_nm(const uint16_t* W_bf16, int64_t d_out, int64_
                                    int flags, uint16_t* codes, uint8_t* mask, float* gamma, void* workspace,
                                    size_t workspace_bytes, void* hip_stream);
 
+/* sbl_quant_mask_pack_nm for several matrices at once (a layer's linears):
+ * the same results, bit for bit, as one call per matrix, in three launches in
+ * all instead of three per matrix.
+ *
+ * items : HOST array of `count` descriptors, 1 <= count <= SBL_PACK_BATCH_MAX;
+ *         each as the arguments of the single call (W, d_out, d_in, codes,
+ *         mask or NULL, gamma).  Matrices must not overlap.
+ * n_keep, m_group, flags : as sbl_quant_mask_pack_nm, for every matrix.
+ * workspace : sbl_quant_mask_pack_batch_workspace_size(count, items) bytes.
+ */
+#define SBL_PACK_BATCH_MAX 16
+typedef struct {
+  const uint16_t* W_bf16;
+  int64_t d_out, d_in;
+  uint16_t* codes;
+  uint8_t* mask;
+  float* gamma;
+} sbl_pack_item;
+
+SBL_API size_t sbl_quant_mask_pack_batch_workspace_size(int count, const sbl_pack_item* items);
+SBL_API int sbl_quant_mask_pack_batch(int count, const sbl_pack_item* items, int n_keep, int m_group, int flags,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* "Mask without grad" ablation ([SUM] 核心方法, second design point; 4.3
  * 消融实验 of [GIST]): the gradient of masked master weights is dropped, i.e. applied
  * after sbl_backward, dW[o, i] = +0 wherever bit (i % 8) of mask[o, i / 8] is

@@ -46,6 +46,8 @@ _SIGNATURES = {
     "sbl_quant_mask_pack_nm": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                         _c_size, _c_ptr]),
     "sbl_mask_grad": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr]),
+    "sbl_quant_mask_pack_batch_workspace_size": (_c_size, [_c_int, ctypes.c_void_p]),
+    "sbl_quant_mask_pack_batch": (_c_int, [_c_int, ctypes.c_void_p, _c_int, _c_int, _c_int, _c_ptr, _c_size, _c_ptr]),
     "sbl_adamw_repack_workspace_size": (_c_size, [_c_i64, _c_i64]),
     "sbl_adamw_repack": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, ctypes.c_void_p, _c_int, _c_int,
                                   _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
@@ -62,6 +64,15 @@ _SIGNATURES = {
     "sbl_version": (ctypes.c_char_p, []),
     "sbl_test_round_mean": (_c_int, [ctypes.POINTER(ctypes.c_uint32), _c_int, _c_i64, ctypes.POINTER(ctypes.c_float)]),
 }
+
+
+class PackItem(ctypes.Structure):
+    """sbl_pack_item (host struct)."""
+    _fields_ = [("W", ctypes.c_void_p), ("d_out", ctypes.c_int64), ("d_in", ctypes.c_int64),
+                ("codes", ctypes.c_void_p), ("mask", ctypes.c_void_p), ("gamma", ctypes.c_void_p)]
+
+
+PACK_BATCH_MAX = 16
 
 
 class AdamwParams(ctypes.Structure):
@@ -218,6 +229,55 @@ def adamw_repack(W: torch.Tensor, dW: torch.Tensor, m: torch.Tensor, v: torch.Te
                                 _ptr(codes), _ptr(gamma), _ptr(flips if mask_prev is not None else None),
                                 _ptr(workspace), workspace.numel(), _stream(stream)), "sbl_adamw_repack")
     return codes, mask, gamma, (flips if mask_prev is not None else None)
+
+
+def quant_mask_pack_batch(Ws, n_keep: int = 6, *, m: int = 8, from_quantized: bool = False, codes=None,
+                          masks=None, gammas=None, workspace: Optional[torch.Tensor] = None, want_mask: bool = True,
+                          stream=None):
+    """``quant_mask_pack`` for up to 16 matrices in three launches in all.  Returns lists
+    ``(codes, masks, gammas)`` in the order of ``Ws``; the results equal one call per matrix."""
+    Ws = list(Ws)
+    n = len(Ws)
+    if not 1 <= n <= PACK_BATCH_MAX:
+        raise ValueError(f"1..{PACK_BATCH_MAX} matrices per batch, got {n}")
+    codes = list(codes) if codes is not None else [None] * n
+    masks = list(masks) if masks is not None else [None] * n
+    gammas = list(gammas) if gammas is not None else [None] * n
+    items = (PackItem * n)()
+    for i, W in enumerate(Ws):
+        _as_bits16(W, f"W[{i}]")
+        d_out, d_in = W.shape
+        dev = W.device
+        if codes[i] is None:
+            codes[i] = torch.empty((d_out, d_in // 8), dtype=torch.int16, device=dev)
+        _out(codes[i], (d_out, d_in // 8), (torch.int16, torch.uint16), dev, f"codes[{i}]")
+        if masks[i] is None and want_mask:
+            masks[i] = torch.empty((d_out, d_in // 8), dtype=torch.uint8, device=dev)
+        if masks[i] is not None:
+            _out(masks[i], (d_out, d_in // 8), (torch.uint8,), dev, f"mask[{i}]")
+        if gammas[i] is None:
+            gammas[i] = torch.empty((1,), dtype=torch.float32, device=dev)
+        _out(gammas[i], (1,), (torch.float32,), dev, f"gamma[{i}]")
+        items[i] = PackItem(W.data_ptr(), d_out, d_in, codes[i].data_ptr(),
+                            masks[i].data_ptr() if masks[i] is not None else None, gammas[i].data_ptr())
+    need = lib.sbl_quant_mask_pack_batch_workspace_size(n, ctypes.c_void_p(ctypes.addressof(items)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=Ws[0].device)
+    _out(workspace, (workspace.numel(),), (torch.uint8,), Ws[0].device, "workspace")
+    flags = MASK_FROM_QUANTIZED if from_quantized else 0
+    _check(lib.sbl_quant_mask_pack_batch(n, ctypes.c_void_p(ctypes.addressof(items)), int(n_keep), int(m), flags,
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+           "sbl_quant_mask_pack_batch")
+    return codes, masks, gammas
+
+
+def quant_batch_workspace_size(shapes) -> int:
+    """Workspace bytes of ``quant_mask_pack_batch`` for [(d_out, d_in), ...]."""
+    shapes = list(shapes)
+    items = (PackItem * len(shapes))()
+    for i, (d_out, d_in) in enumerate(shapes):
+        items[i] = PackItem(None, d_out, d_in, None, None, None)
+    return int(lib.sbl_quant_mask_pack_batch_workspace_size(len(shapes), ctypes.c_void_p(ctypes.addressof(items))))
 
 
 def mask_grad(dW: torch.Tensor, mask: torch.Tensor, *, stream=None) -> torch.Tensor:

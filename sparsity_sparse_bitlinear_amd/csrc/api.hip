@@ -108,6 +108,49 @@ SBL_API int sbl_quant_mask_pack(const uint16_t* W_bf16, int64_t d_out, int64_t d
                                 hip_stream);
 }
 
+static_assert(SBL_PACK_BATCH_MAX == kPackBatchMax, "batch limit");
+
+SBL_API size_t sbl_quant_mask_pack_batch_workspace_size(int count, const sbl_pack_item* items) {
+  if (count < 1 || count > SBL_PACK_BATCH_MAX || !items) return 0;
+  int64_t nw[SBL_PACK_BATCH_MAX];
+  for (int i = 0; i < count; ++i) {
+    if (check_dims(items[i].d_out, items[i].d_in) != SBL_OK) return 0;
+    nw[i] = items[i].d_out * items[i].d_in;
+  }
+  return quant_batch_workspace_bytes(count, nw);
+}
+
+SBL_API int sbl_quant_mask_pack_batch(int count, const sbl_pack_item* items, int n_keep, int m_group, int flags,
+                                      void* workspace, size_t workspace_bytes, void* hip_stream) {
+  SBL_REQUIRE(items && count >= 1 && count <= SBL_PACK_BATCH_MAX, SBL_ERR_INVALID_ARG,
+              "count=%d: 1..%d items (host array) required", count, SBL_PACK_BATCH_MAX);
+  SBL_REQUIRE(flags == 0 || flags == SBL_MASK_FROM_QUANTIZED, SBL_ERR_INVALID_ARG, "flags=%d: unknown flag bits",
+              flags);
+  SBL_REQUIRE(mask_pattern_supported(n_keep, m_group), SBL_ERR_UNSUPPORTED,
+              "n_keep=%d, m_group=%d: supported patterns are N:8 and N:4 with 1 <= N <= M", n_keep, m_group);
+  PackItem it[SBL_PACK_BATCH_MAX];
+  int64_t nw[SBL_PACK_BATCH_MAX];
+  for (int i = 0; i < count; ++i) {
+    const sbl_pack_item& q = items[i];
+    const int rc = check_dims(q.d_out, q.d_in);
+    if (rc != SBL_OK) return rc;
+    SBL_REQUIRE(q.W_bf16 && q.codes && q.gamma, SBL_ERR_INVALID_ARG, "item %d: W, codes and gamma must be non-NULL",
+                i);
+    SBL_REQUIRE(aligned(q.W_bf16, 16) && aligned(q.codes, 16) && aligned(q.gamma, 4), SBL_ERR_INVALID_ARG,
+                "item %d: W and codes must be 16-byte aligned, gamma 4-byte aligned", i);
+    it[i] = PackItem{q.W_bf16, q.d_out, q.d_in, q.codes, q.mask, q.gamma};
+    nw[i] = q.d_out * q.d_in;
+  }
+  const size_t need = quant_batch_workspace_bytes(count, nw);
+  SBL_REQUIRE(workspace && workspace_bytes >= need && aligned(workspace, 16), SBL_ERR_WORKSPACE,
+              "workspace of %zu bytes (16-byte aligned) required, got %zu", need,
+              workspace ? workspace_bytes : (size_t)0);
+  hipError_t e = launch_quant_mask_pack_batch(count, it, n_keep, m_group, flags == SBL_MASK_FROM_QUANTIZED,
+                                              workspace, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_quant_mask_pack_batch launch");
+  return SBL_OK;
+}
+
 SBL_API int sbl_mask_grad(float* dW, const uint8_t* mask, int64_t d_out, int64_t d_in, void* hip_stream) {
   int rc = check_dims(d_out, d_in);
   if (rc != SBL_OK) return rc;

@@ -132,9 +132,11 @@ __device__ __forceinline__ bool in_fast_window(const uint4 v) {
   return ok;
 }
 
-__global__ __launch_bounds__(kAbsumThreads) void k_absum(const uint4* __restrict__ W, int64_t n_vec8,
-                                                         AbsumPartial* __restrict__ part,
-                                                         unsigned long long* __restrict__ hist_out) {
+// Block blk of nblk over one matrix: its exact partial sum into *part, its
+// histogram (if any value fell outside the float64 window) into hist_out[0..256).
+__device__ __forceinline__ void absum_body(const uint4* __restrict__ W, int64_t n_vec8, int nblk, int blk,
+                                           AbsumPartial* __restrict__ part,
+                                           unsigned long long* __restrict__ hist_out) {
   __shared__ unsigned long long hist[256];
   __shared__ U128 red[kAbsumThreads];
   __shared__ int block_any;
@@ -178,8 +180,8 @@ __global__ __launch_bounds__(kAbsumThreads) void k_absum(const uint4* __restrict
       fsum[u] = 0.0;
     }
   };
-  const int64_t stride = (int64_t)gridDim.x * kAbsumThreads;
-  int64_t i = (int64_t)blockIdx.x * kAbsumThreads + tid;
+  const int64_t stride = (int64_t)nblk * kAbsumThreads;
+  int64_t i = (int64_t)blk * kAbsumThreads + tid;
   for (; i + (kU - 1) * stride < n_vec8; i += kU * stride) {
     uint4 v[kU];
 #pragma unroll
@@ -212,9 +214,15 @@ __global__ __launch_bounds__(kAbsumThreads) void k_absum(const uint4* __restrict
     p.hi = red[0].hi;
     p.flag = (unsigned long long)any;
     p.pad = 0;
-    part[blockIdx.x] = p;
+    *part = p;
   }
-  if (any) hist_out[(size_t)blockIdx.x * 256 + tid] = hist[tid];
+  if (any) hist_out[tid] = hist[tid];
+}
+
+__global__ __launch_bounds__(kAbsumThreads) void k_absum(const uint4* __restrict__ W, int64_t n_vec8,
+                                                         AbsumPartial* __restrict__ part,
+                                                         unsigned long long* __restrict__ hist_out) {
+  absum_body(W, n_vec8, gridDim.x, blockIdx.x, part + blockIdx.x, hist_out + (size_t)blockIdx.x * 256);
 }
 
 // Adds v * 2^shift into the little-endian word array w[0..nw).
@@ -237,11 +245,10 @@ __device__ void add_shifted(uint32_t* w, int nw, unsigned long long v, int shift
 
 constexpr int kSumWords = 10;  // 320 bits: enough for any finite bf16 matrix below 2^40 weights
 
-__global__ __launch_bounds__(256) void k_gamma_finalize(const AbsumPartial* __restrict__ part,
-                                                        const unsigned long long* __restrict__ hist_in,
-                                                        int nblocks, unsigned long long count,
-                                                        float* __restrict__ gamma,
-                                                        unsigned long long* __restrict__ flips) {
+__device__ __forceinline__ void finalize_body(const AbsumPartial* __restrict__ part,
+                                              const unsigned long long* __restrict__ hist_in, int nblocks,
+                                              unsigned long long count, float* __restrict__ gamma,
+                                              unsigned long long* __restrict__ flips) {
   __shared__ U128 red[256];
   __shared__ unsigned long long fl[256];
   __shared__ unsigned long long bins[256];
@@ -300,6 +307,14 @@ __global__ __launch_bounds__(256) void k_gamma_finalize(const AbsumPartial* __re
       for (int e = 1; e < 255; ++e) add_shifted(w, kSumWords, bins[e], e - 1);
     *gamma = round_mean_words(w, kSumWords, count);
   }
+}
+
+__global__ __launch_bounds__(256) void k_gamma_finalize(const AbsumPartial* __restrict__ part,
+                                                        const unsigned long long* __restrict__ hist_in,
+                                                        int nblocks, unsigned long long count,
+                                                        float* __restrict__ gamma,
+                                                        unsigned long long* __restrict__ flips) {
+  finalize_body(part, hist_in, nblocks, count, gamma, flips);
 }
 
 // ---------------------------------------------------------------------------
@@ -401,13 +416,13 @@ __device__ __forceinline__ void pack_group(const uint4 v, uint32_t gamma_bits, u
 // 256 apart, so every load and store instruction is contiguous); the four
 // loads are issued before any group is packed.
 template <int N, int M, bool FQ>
-__global__ __launch_bounds__(256) void k_mask_quant_pack(const uint4* __restrict__ W, int64_t n_groups,
-                                                         const float* __restrict__ gamma_p,
-                                                         uint16_t* __restrict__ codes, uint8_t* __restrict__ mask) {
+__device__ __forceinline__ void mqp_body(const uint4* __restrict__ W, int64_t n_groups,
+                                         const float* __restrict__ gamma_p, uint16_t* __restrict__ codes,
+                                         uint8_t* __restrict__ mask, int nblk, int blk) {
   constexpr int kU = 4;
   const uint32_t gamma_bits = __float_as_uint(*gamma_p);
-  const int64_t stride = (int64_t)gridDim.x * 256 * kU;
-  for (int64_t g0 = (int64_t)blockIdx.x * 256 * kU + threadIdx.x; g0 < n_groups; g0 += stride) {
+  const int64_t stride = (int64_t)nblk * 256 * kU;
+  for (int64_t g0 = (int64_t)blk * 256 * kU + threadIdx.x; g0 < n_groups; g0 += stride) {
     uint4 v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) v[u] = g0 + 256 * u < n_groups ? W[g0 + 256 * u] : make_uint4(0u, 0u, 0u, 0u);
@@ -422,6 +437,58 @@ __global__ __launch_bounds__(256) void k_mask_quant_pack(const uint4* __restrict
       if (mask) mask[g] = m;
     }
   }
+}
+
+template <int N, int M, bool FQ>
+__global__ __launch_bounds__(256) void k_mask_quant_pack(const uint4* __restrict__ W, int64_t n_groups,
+                                                         const float* __restrict__ gamma_p,
+                                                         uint16_t* __restrict__ codes, uint8_t* __restrict__ mask) {
+  mqp_body<N, M, FQ>(W, n_groups, gamma_p, codes, mask, gridDim.x, blockIdx.x);
+}
+
+// ---------------------------------------------------------------------------
+// Several matrices in one launch per pass (a layer's linears): the blocks of
+// the grid are dealt to the matrices by the prefix sums in the descriptor, so
+// the three launches cover every matrix and the small ones stop costing a
+// launch each.
+// ---------------------------------------------------------------------------
+struct PackBatch {
+  int count;
+  const uint4* W[kPackBatchMax];
+  int64_t n_groups[kPackBatchMax];
+  uint16_t* codes[kPackBatchMax];
+  uint8_t* mask[kPackBatchMax];
+  float* gamma[kPackBatchMax];
+  int absum_begin[kPackBatchMax + 1];  // absum blocks of matrix i: [absum_begin[i], absum_begin[i + 1])
+  int pack_begin[kPackBatchMax + 1];   // packing blocks, likewise
+};
+
+__device__ __forceinline__ int batch_item(const int* begin, int count, int b) {
+  int i = 0;
+  while (i + 1 < count && b >= begin[i + 1]) ++i;
+  return i;
+}
+
+__global__ __launch_bounds__(kAbsumThreads) void k_absum_batch(PackBatch pb, AbsumPartial* __restrict__ part,
+                                                               unsigned long long* __restrict__ hist_out) {
+  const int i = batch_item(pb.absum_begin, pb.count, blockIdx.x);
+  absum_body(pb.W[i], pb.n_groups[i], pb.absum_begin[i + 1] - pb.absum_begin[i], blockIdx.x - pb.absum_begin[i],
+             part + blockIdx.x, hist_out + (size_t)blockIdx.x * 256);
+}
+
+__global__ __launch_bounds__(256) void k_gamma_finalize_batch(PackBatch pb, const AbsumPartial* __restrict__ part,
+                                                              const unsigned long long* __restrict__ hist_in) {
+  const int i = blockIdx.x;
+  const int b0 = pb.absum_begin[i];
+  finalize_body(part + b0, hist_in + (size_t)b0 * 256, pb.absum_begin[i + 1] - b0,
+                (unsigned long long)pb.n_groups[i] * 8ull, pb.gamma[i], nullptr);
+}
+
+template <int N, int M, bool FQ>
+__global__ __launch_bounds__(256) void k_mask_quant_pack_batch(PackBatch pb) {
+  const int i = batch_item(pb.pack_begin, pb.count, blockIdx.x);
+  mqp_body<N, M, FQ>(pb.W[i], pb.n_groups[i], pb.gamma[i], pb.codes[i], pb.mask[i],
+                     pb.pack_begin[i + 1] - pb.pack_begin[i], blockIdx.x - pb.pack_begin[i]);
 }
 
 // "Mask without grad" ablation: dW[o, i] = +0 where slot i of the mask plane
@@ -699,6 +766,79 @@ hipError_t launch_adamw_repack(uint16_t* W, const float* g, float* m, float* v, 
   if (pb > 65536) pb = 65536;
   hipLaunchKernelGGL(k_codes_from_mask, dim3((unsigned)pb), dim3(256), 0, s, (const uint4*)W, (const uint8_t*)mask,
                      n_groups, (const float*)gamma, codes);
+  return hipGetLastError();
+}
+
+using MqpBatchKernel = void (*)(PackBatch);
+
+static MqpBatchKernel mqp_batch_kernel(int n, int m, bool fq) {
+#define SBL_MQPB(NN, MM) \
+  (fq ? (MqpBatchKernel)k_mask_quant_pack_batch<NN, MM, true> : (MqpBatchKernel)k_mask_quant_pack_batch<NN, MM, false>)
+  if (m == 8) {
+    switch (n) {
+      case 1: return SBL_MQPB(1, 8);
+      case 2: return SBL_MQPB(2, 8);
+      case 3: return SBL_MQPB(3, 8);
+      case 4: return SBL_MQPB(4, 8);
+      case 5: return SBL_MQPB(5, 8);
+      case 6: return SBL_MQPB(6, 8);
+      case 7: return SBL_MQPB(7, 8);
+      case 8: return SBL_MQPB(8, 8);
+    }
+  } else if (m == 4) {
+    switch (n) {
+      case 1: return SBL_MQPB(1, 4);
+      case 2: return SBL_MQPB(2, 4);
+      case 3: return SBL_MQPB(3, 4);
+      case 4: return SBL_MQPB(4, 4);
+    }
+  }
+#undef SBL_MQPB
+  return nullptr;
+}
+
+static int64_t pack_blocks(int64_t n_groups) {
+  int64_t pb = (n_groups + 1023) / 1024;
+  return pb > 65536 ? 65536 : (pb < 1 ? 1 : pb);
+}
+
+size_t quant_batch_workspace_bytes(int count, const int64_t* n_weights) {
+  size_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    const int nb = absum_blocks(n_weights[i] / 8);
+    total += (size_t)nb * sizeof(AbsumPartial) + (size_t)nb * 256 * sizeof(unsigned long long);
+  }
+  return total;
+}
+
+hipError_t launch_quant_mask_pack_batch(int count, const PackItem* items, int n_keep, int m_group,
+                                        bool from_quantized, void* ws, hipStream_t s) {
+  const MqpBatchKernel pack = mqp_batch_kernel(n_keep, m_group, from_quantized);
+  if (!pack || count < 1 || count > kPackBatchMax) return hipErrorInvalidValue;
+  PackBatch pb{};
+  pb.count = count;
+  int64_t na = 0, np = 0;
+  for (int i = 0; i < count; ++i) {
+    const int64_t ng = items[i].d_out * items[i].d_in / 8;
+    pb.W[i] = (const uint4*)items[i].W;
+    pb.n_groups[i] = ng;
+    pb.codes[i] = items[i].codes;
+    pb.mask[i] = items[i].mask;
+    pb.gamma[i] = items[i].gamma;
+    pb.absum_begin[i] = (int)na;
+    pb.pack_begin[i] = (int)np;
+    na += absum_blocks(ng);
+    np += pack_blocks(ng);
+  }
+  pb.absum_begin[count] = (int)na;
+  pb.pack_begin[count] = (int)np;
+  if (np > 0x7FFFFFFF) return hipErrorInvalidValue;
+  AbsumPartial* part = (AbsumPartial*)ws;
+  unsigned long long* hist = (unsigned long long*)((char*)ws + (size_t)na * sizeof(AbsumPartial));
+  hipLaunchKernelGGL(k_absum_batch, dim3((unsigned)na), dim3(kAbsumThreads), 0, s, pb, part, hist);
+  hipLaunchKernelGGL(k_gamma_finalize_batch, dim3((unsigned)count), dim3(256), 0, s, pb,
+                     (const AbsumPartial*)part, (const unsigned long long*)hist);
+  hipLaunchKernelGGL(pack, dim3((unsigned)np), dim3(256), 0, s, pb);
   return hipGetLastError();
 }
 

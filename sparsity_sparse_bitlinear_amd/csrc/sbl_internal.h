@@ -59,6 +59,7 @@ struct AbsumPartial {
 
 constexpr int kAbsumThreads = 256;
 constexpr int kAbsumMaxBlocks = 1024;
+constexpr int kPackBatchMax = 16;  // matrices per batched packing call
 
 size_t quant_workspace_bytes(int64_t d_out, int64_t d_in);
 int absum_blocks(int64_t n_vec8);
@@ -69,6 +70,18 @@ hipError_t launch_quant_mask_pack(const uint16_t* W, int64_t d_out, int64_t d_in
                                   bool from_quantized, uint16_t* codes, uint8_t* mask, float* gamma, void* ws,
                                   hipStream_t s);
 hipError_t launch_mask_grad(float* dW, const uint8_t* mask, int64_t d_out, int64_t d_in, hipStream_t s);
+
+// Several matrices packed with three launches in all (quant.hip).
+struct PackItem {
+  const uint16_t* W;
+  int64_t d_out, d_in;
+  uint16_t* codes;
+  uint8_t* mask;
+  float* gamma;
+};
+size_t quant_batch_workspace_bytes(int count, const int64_t* n_weights);
+hipError_t launch_quant_mask_pack_batch(int count, const PackItem* items, int n_keep, int m_group,
+                                        bool from_quantized, void* ws, hipStream_t s);
 
 // AdamW step + repack (quant.hip).  W, m, v updated in place.
 struct AdamwArgs {

@@ -75,6 +75,29 @@ def test_quant_mask_pack_nm_validation():
     assert f(P, 256, 256, 2, 4, 1, P, P, P, P, ws - 1, NULL) == WORKSPACE
 
 
+def test_quant_mask_pack_batch_validation():
+    import sparsity_sparse_bitlinear_amd as sbl
+    items = (sbl.PackItem * 3)(sbl.PackItem(0x10000, 256, 256, 0x20000, 0x30000, 0x40000),
+                               sbl.PackItem(0x50000, 8, 64, 0x60000, None, 0x70000),
+                               sbl.PackItem(0x80000, 11008, 2048, 0x90000, None, 0xA0000))
+    ip = ctypes.c_void_p(ctypes.addressof(items))
+    ws = lib.sbl_quant_mask_pack_batch_workspace_size(3, ip)
+    single = sum(lib.sbl_quant_mask_pack_workspace_size(d_o, d_i) for d_o, d_i in ((256, 256), (8, 64), (11008, 2048)))
+    assert ws == single
+    f = lib.sbl_quant_mask_pack_batch
+    assert f(0, ip, 6, 8, 0, P, ws, NULL) == INVALID
+    assert f(17, ip, 6, 8, 0, P, ws, NULL) == INVALID
+    assert f(3, NULL, 6, 8, 0, P, ws, NULL) == INVALID
+    assert f(3, ip, 5, 4, 0, P, ws, NULL) == UNSUPPORTED
+    assert f(3, ip, 6, 8, 4, P, ws, NULL) == INVALID
+    assert f(3, ip, 6, 8, 0, P, ws - 1, NULL) == WORKSPACE
+    items[1].d_in = 60
+    assert f(3, ip, 6, 8, 0, P, ws, NULL) == SHAPE
+    items[1].d_in = 64
+    items[2].codes = 0x90002                                                  # misaligned
+    assert f(3, ip, 6, 8, 0, P, ws, NULL) == INVALID
+
+
 def test_mask_grad_validation():
     f = lib.sbl_mask_grad
     assert f(NULL, P, 256, 256, NULL) == INVALID

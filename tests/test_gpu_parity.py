@@ -68,6 +68,26 @@ def test_pack_parity_nm_patterns(n, m, fq):
     check_pack_nm(boundary_row_weight(24, 64), n, m, fq)
 
 
+@pytest.mark.parametrize("n,m,fq", [(6, 8, False), (2, 4, False), (6, 8, True), (8, 8, False)])
+def test_pack_batch_matches_single_calls(n, m, fq):
+    # one batched call over a layer's worth of shapes (tiny, ragged, large) equals the single calls
+    shapes = [(256, 2048), (1, 8), (333, 1032), (11008, 2048), (3, 24), (2048, 11008), (40, 64)]
+    Ws = [to_dev_bf16(weight(17, i, d_o, d_i)) for i, (d_o, d_i) in enumerate(shapes)]
+    Ws[4] = to_dev_bf16(tie_heavy_weight(5, 3, 24))
+    cb, mb, gb = sbl.quant_mask_pack_batch(Ws, n, m=m, from_quantized=fq)
+    for i, W in enumerate(Ws):
+        c1, m1, g1 = sbl.quant_mask_pack(W, n, m=m, from_quantized=fq)
+        torch.cuda.synchronize()
+        assert torch.equal(cb[i], c1) and torch.equal(mb[i], m1), i
+        assert f32_bits(gb[i].cpu().numpy()[0]) == f32_bits(g1.cpu().numpy()[0]), i
+    # and the small ones against the oracle
+    for i in (0, 1, 2, 4, 6):
+        rc, rm, rg = oracle.quant_mask_pack(bits16(Ws[i]), n, m, from_quantized=fq)
+        np.testing.assert_array_equal(bits16(cb[i]), rc)
+        np.testing.assert_array_equal(mb[i].cpu().numpy(), rm)
+        assert f32_bits(gb[i].cpu().numpy()[0]) == f32_bits(rg)
+
+
 @pytest.mark.parametrize("n,m", [(3, 8), (5, 8), (7, 8), (2, 4), (1, 4)])
 def test_step_parity_nm_patterns(n, m):
     # the forward and backward kernels take the planes of any pattern as they are
