@@ -36,8 +36,8 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE, scale factors from a plain 1 GiB copy), averaged over the 7 linears; measured with
 # rocprofv3 --pmc for the backward kernel sources whose hash is given
 # (profiles/traffic_backward_3b_32768tok.md).
-BWD_TRAFFIC_BYTES = 2.49e9
-BWD_TRAFFIC_SRC_SHA = "e9fa6919ba0ca201"
+BWD_TRAFFIC_BYTES = 2.48e9
+BWD_TRAFFIC_SRC_SHA = "b6811c550191b403"
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -176,11 +176,15 @@ def main():
 
     # Timed region 2: the same steps with HIP events between the calls (same stream), for the
     # per-kernel durations behind the roofline figures.
+    # All steps are enqueued before the one synchronization, so no step starts on an idle GPU
+    # waiting for the host (which would count the host's enqueue time in the first call).
     sums = np.zeros((len(layers), len(parts)))
-    for _ in range(args.steps):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in layers]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)] for _ in layers]
+           for _ in range(args.steps)]
+    for ev in evs:
         step(ev)
-        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    for ev in evs:
         for li in range(len(layers)):
             for k in range(len(parts)):
                 sums[li, k] += ev[li][k].elapsed_time(ev[li][k + 1])
