@@ -5,7 +5,7 @@ cpu_baseline leg of bench.py, never by the product path.
 """
 from .sparse_bitlinear import (CODE_MINUS, CODE_PLUS, CODE_ZERO, abs_sum_exact, act_quant,  # noqa: F401
                                adamw_repack, adamw_update, f64_to_bf16_bits, mask_flips, unpack_mask,
-                               rmsnorm_act_quant, rmsnorm_bf16,
+                               rmsnorm_act_quant, rmsnorm_bf16, pack_sparse24, unpack_sparse24,
                                backward, backward_stop_gradient, bf16_to_f64, dequant_act,
                                effective_weight, forward_acc, forward_y, gamma_f32, mask_from_quantized,
                                mask_grad, nm_mask,

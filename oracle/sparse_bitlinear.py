@@ -381,6 +381,77 @@ def backward_stop_gradient(dY_bits, w_eff, gamma, x_q, absmax, mask):
 
 
 # ----------------------------------------------------------------------------
+# Kept-only 2:4 operand plane (2:8 and 2:4 patterns)  [SUM] 前置知识 > 半结构化
+# N:M 稀疏 (2:4 as the hardware pattern; at most N non-zeros per group)
+# ----------------------------------------------------------------------------
+
+
+def pack_sparse24(w_eff: np.ndarray) -> np.ndarray:
+    """Kept-only plane uint8 [d_out, d_in / 64, 16] of a ternary W_eff whose every
+    group of 4 consecutive d_in positions holds at most 2 non-zeros (always true
+    for 2:8 and 2:4 masks).
+
+    Per row and 64-wide step s, for each half h (positions 64 s + 32 h .. + 31,
+    8 groups of 4): a 32-bit word of 16 two-bit codes (00 = 0, 01 = +1, 11 = -1),
+    slot 2 g + i being the i-th stored value of group g, and a 32-bit word of
+    positions, bits 4 g .. 4 g + 1 and 4 g + 2 .. 4 g + 3 holding the positions
+    (0..3, first < second) of those two values in their group.  Stored values:
+    the group's non-zeros in position order, padded with zeros at the next free
+    positions (one non-zero at a: (a, a + 1), or (2, 3) for a = 3; none: (0, 1)).
+    Bytes 0-3: codes of h = 0, 4-7: codes of h = 1, 8-11: positions of h = 0,
+    12-15: positions of h = 1 (little endian).  Same size as the code plane.
+    """
+    w = np.asarray(w_eff, np.int8)
+    d_out, d_in = w.shape
+    assert d_in % 64 == 0
+    out = np.zeros((d_out, d_in // 64, 16), np.uint8)
+    code_of = {0: 0, 1: CODE_PLUS, -1: CODE_MINUS}
+    for o in range(d_out):
+        for st in range(d_in // 64):
+            for h in range(2):
+                cw = 0
+                iw = 0
+                for g in range(8):
+                    k0 = 64 * st + 32 * h + 4 * g
+                    grp = [int(v) for v in w[o, k0:k0 + 4]]
+                    nz = [i for i in range(4) if grp[i] != 0]
+                    assert len(nz) <= 2, "more than 2 non-zeros in a group of 4"
+                    if len(nz) == 2:
+                        i0, i1 = nz
+                    elif len(nz) == 1:
+                        i0, i1 = (nz[0], nz[0] + 1) if nz[0] < 3 else (2, 3)
+                    else:
+                        i0, i1 = 0, 1
+                    cw |= code_of[grp[i0]] << (2 * (2 * g)) | code_of[grp[i1]] << (2 * (2 * g + 1))
+                    iw |= (i0 | (i1 << 2)) << (4 * g)
+                out[o, st, 4 * h:4 * h + 4] = np.frombuffer(np.uint32(cw).tobytes(), np.uint8)
+                out[o, st, 8 + 4 * h:12 + 4 * h] = np.frombuffer(np.uint32(iw).tobytes(), np.uint8)
+    return out
+
+
+def unpack_sparse24(plane: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_sparse24``: int8 W_eff [d_out, 64 * steps]."""
+    plane = np.asarray(plane, np.uint8)
+    d_out, steps, _ = plane.shape
+    w = np.zeros((d_out, steps * 64), np.int8)
+    val = {0: 0, CODE_PLUS: 1, CODE_MINUS: -1}
+    for o in range(d_out):
+        for st in range(steps):
+            for h in range(2):
+                cw = int(np.frombuffer(plane[o, st, 4 * h:4 * h + 4].tobytes(), np.uint32)[0])
+                iw = int(np.frombuffer(plane[o, st, 8 + 4 * h:12 + 4 * h].tobytes(), np.uint32)[0])
+                for g in range(8):
+                    i0, i1 = (iw >> (4 * g)) & 3, (iw >> (4 * g + 2)) & 3
+                    assert i0 < i1, "positions out of order"
+                    c0, c1 = (cw >> (4 * g)) & 3, (cw >> (4 * g + 2)) & 3
+                    assert c0 != 0b10 and c1 != 0b10, "invalid code 10"
+                    k0 = 64 * st + 32 * h + 4 * g
+                    w[o, k0 + i0] = val[c0]
+                    w[o, k0 + i1] = val[c1]
+    return w
+
+
+# ----------------------------------------------------------------------------
 # Norm + activation quantization  [SUM] 方法步骤详情 step (3): x~ = Q_a(Norm(x))
 # ----------------------------------------------------------------------------
 

@@ -15,6 +15,7 @@ import test_oracle_mask as t_mask
 import test_oracle_ternary as t_tern
 import test_oracle_norm as t_norm
 import test_oracle_optimizer as t_opt
+import test_oracle_sparse24 as t_sp
 import test_oracle_variants as t_var
 
 
@@ -135,6 +136,15 @@ def _rmsnorm_sum_not_mean(x_bits, g_bits, eps):
         (1.0 if g_bits is None else sb.bf16_to_f64(np.asarray(g_bits))))
 
 
+_ORIG_SP = sb.pack_sparse24
+
+
+def _sparse24_halves_swapped(w_eff):
+    p = _ORIG_SP(w_eff).copy()
+    p[..., 0:4], p[..., 4:8] = p[..., 4:8].copy(), p[..., 0:4].copy()
+    return p
+
+
 _ORIG_PACK = sb.pack_codes
 
 
@@ -191,6 +201,8 @@ MUTANTS = [
      [t_opt.test_bf16_rounding_no_double_rounding]),
     ("RMSNorm with the sum of squares instead of the mean", "rmsnorm_bf16", _rmsnorm_sum_not_mean,
      [lambda: t_norm.test_rmsnorm_within_bf16_rounding_of_float64(64)]),
+    ("kept-only plane with the two halves' codes swapped", "pack_sparse24", _sparse24_halves_swapped,
+     [t_sp.test_worked_groups]),
 ]
 
 
