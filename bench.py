@@ -16,7 +16,8 @@ Metric: tokens per second of whole steps.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
        python bench.py --workload 4     (decode: per-layer latency at 1/8/64 tokens, 6/4/2:8)
-       python bench.py --variants       (every N of N:8, 2:4, the two ablations, AdamW + repack, norm + act quant)
+       python bench.py --variants       (every N of N:8, 2:4, the ablations, AdamW + repack, norm + act quant,
+                                         2:8 forward dense vs sparse matrix instruction)
 """
 from __future__ import annotations
 
@@ -363,7 +364,25 @@ def run_variants(args, wl):
             sbl.act_quant(x, x_q=q, absmax=a)
     ms_norm, ms_act = timed(norm_q), timed(plain_q)
     bytes_x = 3 * n_x + 4 * T * len(xs)
-    del xs, qs
+    # 2:8 forward: the dense path (codes expanded to int8, dense matrix instruction) against the
+    # kept-only 2:4 plane on the sparse matrix instruction; the same int32 sums
+    sp = []
+    for W, (x, (q, a)) in zip(Ws, zip(xs, qs)):
+        c28, _, g28 = sbl.quant_mask_pack(W, 2, want_mask=False)
+        plane, _ = sbl.pack_sparse24(c28)
+        sbl.act_quant(x, x_q=q, absmax=a)
+        sp.append((c28, g28, plane, q, a, torch.empty((T, W.shape[0]), dtype=torch.bfloat16, device=dev)))
+
+    def fwd_dense():
+        for c28, g28, _, q, a, y in sp:
+            sbl.forward(c28, g28, q, a, out_dtype=sbl.BF16, y=y)
+
+    def fwd_sparse():
+        for _, g28, plane, q, a, y in sp:
+            sbl.forward_sparse24(plane, g28, q, a, out_dtype=sbl.BF16, y=y)
+    ms_fd, ms_fs = timed(fwd_dense), timed(fwd_sparse)
+    ops_28 = sum(2.0 * T * L.d_out * L.d_in * 2 / 8 for L in wl.linears)
+    del xs, qs, sp
     line = {"metric": "Sparse-BitLinear variants: quant/mask/pack per N:M pattern and mask-without-grad, "
                       "7 linears of a 3B-like layer",
             "value": rows[2]["ms"], "unit": "ms per layer (6:8 quant/mask/pack)", "n_gpus": 1,
@@ -377,7 +396,10 @@ def run_variants(args, wl):
             "rmsnorm_act_quant": {"tokens": T, "ms": round(ms_norm, 4),
                                   "GBps": round(bytes_x / (ms_norm * 1e-3) / 1e9, 1),
                                   "frac_hbm": round(bytes_x / (ms_norm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                  "act_quant_alone_ms": round(ms_act, 4)}}
+                                  "act_quant_alone_ms": round(ms_act, 4)},
+            "forward_2of8": {"tokens": T, "dense_ms": round(ms_fd, 4), "sparse24_ms": round(ms_fs, 4),
+                             "sparse24_TOPs_algorithmic": round(ops_28 / (ms_fs * 1e-3) / 1e12, 1),
+                             "speedup": round(ms_fd / ms_fs, 3)}}
     print(json.dumps(line), flush=True)
 
 

@@ -308,6 +308,32 @@ SBL_API int sbl_decode(const uint16_t* codes, const float* gamma, const uint16_t
 /* 1 if sbl_decode takes this (T, d_in), else 0. */
 SBL_API int sbl_decode_supported(int64_t T, int64_t d_in);
 
+/* Kept-only 2:4 operand plane for 2:8 and 2:4 masks, and the forward on it,
+ * which runs on gfx950's sparse int8 matrix instruction (2 stored values of
+ * every 4 k): half the matrix work of sbl_forward for the same result ([SUM]
+ * 前置知识 > 半结构化 N:M 稀疏 names 2:4 the hardware pattern; [SUM] Table 3,
+ * the sparse kernels' speed-ups).
+ *
+ * sbl_pack_sparse24: codes [d_out, d_in/8] (from sbl_quant_mask_pack(_nm) with
+ * a 2:8, 2:4 or 1:4 pattern) -> plane uint8 [d_out, d_in/64, 16], the same size.
+ * Per row and 64-wide step, for each half h (32 positions, 8 groups of 4): a
+ * 32-bit word of 16 two-bit codes (slot 2 g + i = the i-th stored value of
+ * group g) at bytes 4 h, and a 32-bit word of their positions (bits 4 g ..
+ * 4 g + 3: first | second << 2, first < second) at bytes 8 + 4 h.  A group's
+ * non-zeros are stored in position order, padded with zeros at the next free
+ * positions.  Groups with more than 2 non-zeros (other patterns) cannot be
+ * represented: their count is added to *bad (device uint64, may be NULL; the
+ * caller zeroes it) and the plane is then not valid for sbl_forward_sparse24.
+ * d_in % 64 == 0.
+ *
+ * sbl_forward_sparse24: as sbl_forward with the plane in place of the codes
+ * (the same int32 sums, so the same y bit for bit).  d_in % 128 == 0.
+ */
+SBL_API int sbl_pack_sparse24(const uint16_t* codes, int64_t d_out, int64_t d_in, uint8_t* plane, uint64_t* bad,
+                              void* hip_stream);
+SBL_API int sbl_forward_sparse24(const uint8_t* plane, const float* gamma, const int8_t* x_q, const float* absmax,
+                                 int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, void* hip_stream);
+
 /* ------------------------------------------------------------------------ */
 /* Backward (Dual STE)                                                        */
 /* ------------------------------------------------------------------------ */

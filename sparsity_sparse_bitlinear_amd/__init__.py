@@ -54,6 +54,8 @@ _SIGNATURES = {
     "sbl_act_quant": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "sbl_forward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_rmsnorm_act_quant": (_c_int, [_c_ptr, _c_ptr, ctypes.c_float, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "sbl_pack_sparse24": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "sbl_forward_sparse24": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode_supported": (_c_int, [_c_i64, _c_i64]),
     "sbl_backward_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int]),
@@ -325,6 +327,40 @@ def rmsnorm_act_quant(x: torch.Tensor, g: Optional[torch.Tensor] = None, eps: fl
 
 
 _OUT_TORCH = {F32: torch.float32, BF16: torch.bfloat16, I32: torch.int32}
+
+
+def pack_sparse24(codes: torch.Tensor, *, plane: Optional[torch.Tensor] = None, stream=None):
+    """Kept-only 2:4 plane of a 2:8 / 2:4 code plane: ``(plane uint8 [d_out, d_in/64, 16], bad int64 [1])``;
+    ``bad`` counts groups of 4 with more than 2 non-zeros (0 for 2:8 and 2:4 masks)."""
+    _dev(codes, "codes")
+    d_out, G = codes.shape
+    d_in = 8 * G
+    if plane is None:
+        plane = torch.empty((d_out, d_in // 64, 16), dtype=torch.uint8, device=codes.device)
+    _out(plane, (d_out, d_in // 64, 16), (torch.uint8,), codes.device, "plane")
+    bad = torch.zeros((1,), dtype=torch.int64, device=codes.device)
+    _check(lib.sbl_pack_sparse24(_ptr(codes), d_out, d_in, _ptr(plane), _ptr(bad), _stream(stream)),
+           "sbl_pack_sparse24")
+    return plane, bad
+
+
+def forward_sparse24(plane: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax: torch.Tensor, *,
+                     out_dtype: int = F32, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """``forward`` on the kept-only 2:4 plane (sparse matrix instruction); same result as ``forward``."""
+    for t, n in ((plane, "plane"), (gamma, "gamma"), (x_q, "x_q"), (absmax, "absmax")):
+        _dev(t, n)
+    d_out, steps, _ = plane.shape
+    T, d_in = x_q.shape
+    if steps * 64 != d_in:
+        raise ValueError(f"plane {tuple(plane.shape)} does not match x_q [{T}, {d_in}]")
+    if out_dtype not in _OUT_TORCH:
+        raise ValueError(f"unknown out_dtype {out_dtype}")
+    if y is None:
+        y = torch.empty((T, d_out), dtype=_OUT_TORCH[out_dtype], device=x_q.device)
+    _out(y, (T, d_out), (_OUT_TORCH[out_dtype],), x_q.device, "y")
+    _check(lib.sbl_forward_sparse24(_ptr(plane), _ptr(gamma), _ptr(x_q), _ptr(absmax), T, d_in, d_out, _ptr(y),
+                                    int(out_dtype), _stream(stream)), "sbl_forward_sparse24")
+    return y
 
 
 def forward(codes: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax: torch.Tensor, *,

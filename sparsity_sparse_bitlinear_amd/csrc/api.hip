@@ -273,6 +273,39 @@ SBL_API int sbl_decode(const uint16_t* codes, const float* gamma, const uint16_t
   return SBL_OK;
 }
 
+SBL_API int sbl_pack_sparse24(const uint16_t* codes, int64_t d_out, int64_t d_in, uint8_t* plane, uint64_t* bad,
+                              void* hip_stream) {
+  int rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(d_in % 64 == 0, SBL_ERR_SHAPE, "d_in=%lld must be a multiple of 64", (long long)d_in);
+  SBL_REQUIRE(codes && plane, SBL_ERR_INVALID_ARG, "codes and plane must be non-NULL");
+  SBL_REQUIRE(aligned(codes, 16) && aligned(plane, 16) && (!bad || aligned(bad, 8)), SBL_ERR_INVALID_ARG,
+              "codes and plane must be 16-byte aligned, bad 8-byte aligned");
+  hipError_t e = launch_pack_sparse24(codes, d_out, d_in, plane, (unsigned long long*)bad, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_pack_sparse24 launch");
+  return SBL_OK;
+}
+
+SBL_API int sbl_forward_sparse24(const uint8_t* plane, const float* gamma, const int8_t* x_q, const float* absmax,
+                                 int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, void* hip_stream) {
+  int rc = check_tokens(T);
+  if (rc != SBL_OK) return rc;
+  rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(y_dtype == SBL_F32 || y_dtype == SBL_BF16 || y_dtype == SBL_I32, SBL_ERR_INVALID_ARG,
+              "y_dtype=%d is not SBL_F32, SBL_BF16 or SBL_I32", y_dtype);
+  SBL_REQUIRE(forward_sparse24_supported(d_in), SBL_ERR_UNSUPPORTED, "d_in=%lld: a multiple of 128 is required",
+              (long long)d_in);
+  if (T == 0) return SBL_OK;
+  SBL_REQUIRE(plane && gamma && x_q && absmax && y, SBL_ERR_INVALID_ARG, "NULL pointer argument");
+  SBL_REQUIRE(aligned(plane, 16) && aligned(x_q, 16) && aligned(y, 16) && aligned(gamma, 4) && aligned(absmax, 4),
+              SBL_ERR_INVALID_ARG, "plane, x_q, y must be 16-byte aligned; gamma, absmax 4-byte aligned");
+  hipError_t e = launch_forward_sparse24(plane, gamma, x_q, absmax, T, d_in, d_out, y, y_dtype,
+                                         (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_forward_sparse24 launch");
+  return SBL_OK;
+}
+
 SBL_API size_t sbl_backward_workspace_size(int64_t T, int64_t d_in, int64_t d_out, int flags) {
   if (check_tokens(T) != SBL_OK || check_dims(d_out, d_in) != SBL_OK) return 0;
   return backward_workspace_bytes(T, d_in, d_out, flags);

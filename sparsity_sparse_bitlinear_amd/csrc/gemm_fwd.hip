@@ -217,7 +217,17 @@ constexpr int kFDmaStep = kFDmaA + 1;
 // which halves the bank conflicts of the 32 rows a fragment read touches.
 __device__ __forceinline__ int code_word_at(int n, int w) { return 32 * n + 16 * ((w >> 2) ^ ((n >> 3) & 1)) + 4 * (w & 3); }
 
-template <int OUT>
+// SP: the weight operand is the kept-only 2:4 plane (2:8 and 2:4 masks) and the
+// product runs on v_smfmac_i32_32x32x64_i8, whose first operand holds 2 of
+// every 4 k: per lane 16 stored codes (a 32-bit word, expanded to 16 int8 as
+// the dense code words are) and a 32-bit word of their positions.  Lane l
+// holds output row l % 32 and the 8 groups of 4 at k 32 (l / 32) .. + 31 of a
+// 64-wide slice; the x_q operand holds, for token l % 32, k 16 (l / 32) .. + 15
+// and 32 + 16 (l / 32) .. + 15 (two 16-byte chunks), which is the pairing the
+// instruction uses (established on the hardware with random operands).  A K
+// step of 128 is then 2 slices instead of 4; loads, stages and the epilogue
+// are those of the dense path (the plane has the code plane's size).
+template <int OUT, bool SP>
 __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restrict__ xq,
                                                          const uint16_t* __restrict__ codes,
                                                          const float* __restrict__ gamma_p,
@@ -324,6 +334,37 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) fb[j] = __builtin_bit_cast(v4i, expand16(wb[j]));
   };
+  // SP: a K step is 2 slices of 64 k, each done as 2 units of 2 x_q fragments
+  // (units 0-3 of a step: slice u / 2, fragments i = 2 (u % 2), + 1), so the
+  // operand registers match the dense path's.  Unit u: the x_q chunks
+  // 4 (u / 2) + h and 4 (u / 2) + 2 + h of rows wm0 + 32 i + l % 32.
+  auto rd_fh = [&](int st, int u, v8i (&fh)[2]) {
+    const char* a = lds + st * kFStage;
+    const int h = lane >> 5, s2 = u >> 1;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = wm0 + 32 * (2 * (u & 1) + q) + (lane & 31);
+      const v4i lo = *(const v4i*)(a + swz8(row, 4 * s2 + h));
+      const v4i hi = *(const v4i*)(a + swz8(row, 4 * s2 + 2 + h));
+      fh[q] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+  };
+  // SP: the stored-code word 4 s2 + h and the position word 4 s2 + 2 + h of slice s2.
+  auto rd_cc = [&](int st, int s2, uint32_t (&cc)[kNJ], uint32_t (&ix)[kNJ]) {
+    const char* b = lds + st * kFStage + kFStageA;
+    const int h = lane >> 5;
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) {
+      const int n = wn0 + 32 * j + (lane & 31);
+      cc[j] = *(const uint32_t*)(b + code_word_at(n, 4 * s2 + h));
+      ix[j] = *(const uint32_t*)(b + code_word_at(n, 4 * s2 + 2 + h));
+    }
+  };
+  // SP: instruction q * kNJ + j of unit u.
+  auto mm_sp_one = [&](int u, int t, const v8i (&fh)[2], const v4i (&fb)[kNJ], const uint32_t (&ix)[kNJ]) {
+    const int i = 2 * (u & 1) + t / kNJ, j = t % kNJ;
+    acc[i][j] = __builtin_amdgcn_smfmac_i32_32x32x64_i8(fb[j], fh[t / kNJ], acc[i][j], (int)ix[j], 0, 0);
+  };
 #define SBL_FWD_SLICE_ORDER(id)                                 \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, id);           \
   __builtin_amdgcn_sched_group_barrier(0x100, kMI + kNJ, id);   \
@@ -337,6 +378,15 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
   __builtin_amdgcn_sched_group_barrier(0x002, 12, id);          \
   __builtin_amdgcn_sched_group_barrier(0x008, 1, id);           \
   __builtin_amdgcn_sched_barrier(0);
+// SP: one unit = 2 kNJ sparse instructions with `nrd` LDS reads and `nva`
+// vector instructions (the next slice's code expansion) placed between them.
+#define SBL_FWD_SP_ORDER(id, nrd, nva)                       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, id);        \
+  __builtin_amdgcn_sched_group_barrier(0x100, nrd, id);      \
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, id);        \
+  __builtin_amdgcn_sched_group_barrier(0x002, nva, id);      \
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * kNJ - 2, id); \
+  __builtin_amdgcn_sched_barrier(0);
 
   // The K steps of all tiles of the block form one sequence with stage parity
   // running on across tiles.  Step k (its stage has landed): each of the 4
@@ -349,6 +399,9 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
   // tile starts by reading its slice 0.
   v4i fa0[kMI], fa1[kMI], fb0[kNJ], fb1[kNJ];
   uint32_t wb0[kNJ], wb1[kNJ];
+  v8i fh0[2], fh1[2];                               // SP: x_q operands of a unit
+  uint32_t cc0[kNJ], cc1[kNJ], ix0[kNJ], ix1[kNJ];  // SP: stored-code and position words
+  v4i fbs0[kNJ], fbs1[kNJ];                         // SP: expanded stored codes of a slice
   int t = blockIdx.x;
   Tile cur = tile_at(t);
   load_scales(cur.m0);
@@ -372,6 +425,60 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
       for (int j = 0; j < kNJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    if constexpr (SP) {
+      rd_cc(sc, 0, cc0, ix0);
+      rd_fh(sc, 0, fh0);
+      expand(cc0, fbs0);
+      for (int k = 0; k < nk; ++k) {
+        rd_fh(sc, 1, fh1);
+        rd_cc(sc, 1, cc1, ix1);
+#pragma unroll
+        for (int t2 = 0; t2 < 2 * kNJ; ++t2) mm_sp_one(0, t2, fh0, fbs0, ix0);
+        expand(cc1, fbs1);
+        SBL_FWD_SP_ORDER(0, 4 + 2 * kNJ, 8)
+        rd_fh(sc, 2, fh0);
+#pragma unroll
+        for (int t2 = 0; t2 < 2 * kNJ; ++t2) mm_sp_one(1, t2, fh1, fbs0, ix0);
+        SBL_FWD_SP_ORDER(1, 4, 0)
+        rd_fh(sc, 3, fh1);
+#pragma unroll
+        for (int t2 = 0; t2 < 2 * kNJ; ++t2) mm_sp_one(2, t2, fh0, fbs1, ix1);
+        SBL_FWD_SP_ORDER(2, 4, 0)
+        wait_vmcnt_lgkm0<0>();
+        barrier_only();
+        __builtin_amdgcn_sched_barrier(0);
+        const bool in_tile = k + 2 < nk;
+        const bool load = in_tile || (has_next && k + 2 - nk < nk);
+        const Tile& lt = in_tile ? cur : nxt;
+        const int kn = in_tile ? k + 2 : k + 2 - nk;
+        // unit 3 restarts the pipe; the next step's slice-0 words and unit-0
+        // fragments and this step's refill loads go between its instructions
+        mm_sp_one(3, 0, fh1, fbs1, ix1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < nk) {
+          rd_cc(sc ^ 1, 0, cc0, ix0);
+          rd_fh(sc ^ 1, 0, fh0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 1; u < 2 * kNJ; ++u) {
+          mm_sp_one(3, u, fh1, fbs1, ix1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {  // kFDmaA + 1 = 5 loads over the 3 remaining slots
+            const int li = 2 * (u - 1) + d;
+            if (li <= kFDmaA && load) issue_one(lt, kn, sc, li);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int li = 2 * (2 * kNJ - 1); li <= kFDmaA; ++li)
+          if (load) issue_one(lt, kn, sc, li);
+        if (k + 1 < nk) expand(cc0, fbs0);
+        __builtin_amdgcn_sched_barrier(0);
+        sc ^= 1;
+      }
+    } else {
     rd(sc, 0, fa0, wb0);
     expand(wb0, fb0);
     for (int k = 0; k < nk; ++k) {
@@ -410,6 +517,7 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
         __builtin_amdgcn_sched_barrier(0);
       }
       sc ^= 1;
+    }
     }
 
     // Epilogue of tile cur.
@@ -517,6 +625,7 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
     if (has_next) nxt = tile_at(t + gridDim.x);
   }
 #undef SBL_FWD_SLICE_ORDER
+#undef SBL_FWD_SP_ORDER
   // No direct loads may still target LDS when the block retires.
   wait_vmcnt<0>();
 }
@@ -829,6 +938,32 @@ int device_cus() {
   return n;
 }
 
+// One block per tile, or with two or more K steps per tile at most one block
+// per CU (a multiple of 8, the XCD count), each walking its tiles.
+template <bool SP>
+static hipError_t launch_fwd_direct(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
+                                    int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
+  const int64_t nb = ((d_out + kFBN - 1) / kFBN) * ((T + kBM - 1) / kBM);
+  const int64_t cus = std::max(8, device_cus() / 8 * 8);
+  const int64_t nblocks = d_in / kFK >= 2 && nb > cus ? cus : nb;
+  const dim3 grid((unsigned)nblocks), block(kFT);
+  switch (y_dtype) {
+    case SBL_F32:
+      hipLaunchKernelGGL((k_fwd_i8_direct<SBL_F32, SP>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+                         (int)d_in, (int)d_out, y);
+      break;
+    case SBL_BF16:
+      hipLaunchKernelGGL((k_fwd_i8_direct<SBL_BF16, SP>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+                         (int)d_in, (int)d_out, y);
+      break;
+    default:
+      hipLaunchKernelGGL((k_fwd_i8_direct<SBL_I32, SP>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+                         (int)d_in, (int)d_out, y);
+      break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
@@ -836,31 +971,19 @@ hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_
     if (T <= 16) return launch_decode<1>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
     return launch_decode<4>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
   }
-  if (d_in % kFK == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes) {
-    // One block per tile, or with two or more K steps per tile at most one
-    // block per CU (a multiple of 8, the XCD count), each walking its tiles.
-    const int64_t nb = ((d_out + kFBN - 1) / kFBN) * ((T + kBM - 1) / kBM);
-    const int64_t cus = std::max(8, device_cus() / 8 * 8);
-    const int64_t nblocks = d_in / kFK >= 2 && nb > cus ? cus : nb;
-    const dim3 grid((unsigned)nblocks), block(kFT);
-    switch (y_dtype) {
-      case SBL_F32:
-        hipLaunchKernelGGL((k_fwd_i8_direct<SBL_F32>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T, (int)d_in,
-                           (int)d_out, y);
-        break;
-      case SBL_BF16:
-        hipLaunchKernelGGL((k_fwd_i8_direct<SBL_BF16>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
-                           (int)d_in, (int)d_out, y);
-        break;
-      default:
-        hipLaunchKernelGGL((k_fwd_i8_direct<SBL_I32>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T, (int)d_in,
-                           (int)d_out, y);
-        break;
-    }
-    return hipGetLastError();
-  }
+  if (d_in % kFK == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes)
+    return launch_fwd_direct<false>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
   if (d_in % 64 == 0) return launch_fwd_v<true>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
   return launch_fwd_v<false>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
+}
+
+bool forward_sparse24_supported(int64_t d_in) { return d_in % kFK == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes; }
+
+hipError_t launch_forward_sparse24(const uint8_t* plane, const float* gamma, const int8_t* xq, const float* absmax,
+                                   int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (!forward_sparse24_supported(d_in)) return hipErrorInvalidValue;
+  return launch_fwd_direct<true>((const uint16_t*)plane, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
 }
 
 bool decode_fused_supported(int64_t T, int64_t d_in) {

@@ -644,6 +644,69 @@ __global__ __launch_bounds__(256) void k_codes_from_mask(const uint4* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Kept-only 2:4 plane from the code plane (2:8 and 2:4 masks leave at most 2
+// non-zeros in every group of 4 positions).  Per row and 64-wide step, for each
+// half h (32 positions = 8 groups of 4): a word of 16 two-bit codes, slot 2 g + i
+// holding the i-th stored value of group g, and a word of their positions
+// (bits 4 g .. 4 g + 3: first | second << 2, first < second).  The group's
+// non-zeros are stored in position order, padded with zeros at the next free
+// positions (one non-zero at a: (a, a + 1), or (2, 3) for a = 3; none: (0, 1)).
+// Bytes 0-3 codes of h = 0, 4-7 codes of h = 1, 8-11 and 12-15 positions.
+// ---------------------------------------------------------------------------
+// One group of 4 codes (8 bits) -> (2 stored codes, 4 position bits); *bad set
+// for more than 2 non-zeros (the first two are kept).
+__device__ __forceinline__ void sparse24_group(uint32_t c4, uint32_t& codes2, uint32_t& pos4, bool& bad) {
+  int i0 = -1, i1 = -1, cnt = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if ((c4 >> (2 * i)) & 3u) {
+      if (i0 < 0) i0 = i;
+      else if (i1 < 0) i1 = i;
+      ++cnt;
+    }
+  }
+  bad = cnt > 2;
+  if (i0 < 0) {
+    i0 = 0;
+    i1 = 1;
+  } else if (i1 < 0) {
+    if (i0 < 3) i1 = i0 + 1;
+    else { i0 = 2; i1 = 3; }
+  }
+  codes2 = ((c4 >> (2 * i0)) & 3u) | (((c4 >> (2 * i1)) & 3u) << 2);
+  pos4 = (uint32_t)i0 | ((uint32_t)i1 << 2);
+}
+
+// One thread per (row, 64-wide step): the step's 16 bytes of codes (8 code
+// words of 8 positions; 32-bit word q = positions 16 q .. 16 q + 15).
+__global__ __launch_bounds__(256) void k_pack_sparse24(const uint16_t* __restrict__ codes, int64_t items,
+                                                       uint4* __restrict__ plane, unsigned long long* __restrict__ bad) {
+  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= items) return;
+  const uint4 cw = *(const uint4*)(codes + id * 8);
+  const uint32_t w[4] = {cw.x, cw.y, cw.z, cw.w};
+  uint32_t out[4];
+  unsigned long long nbad = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t cc = 0, ix = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      uint32_t c2, p4;
+      bool b;
+      sparse24_group((w[2 * h + (g >> 2)] >> (8 * (g & 3))) & 0xFFu, c2, p4, b);
+      cc |= c2 << (4 * g);
+      ix |= p4 << (4 * g);
+      nbad += b ? 1u : 0u;
+    }
+    out[h] = cc;
+    out[2 + h] = ix;
+  }
+  plane[id] = make_uint4(out[0], out[1], out[2], out[3]);
+  if (bad && nbad) atomicAdd(bad, nbad);
+}
+
+// ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 
@@ -839,6 +902,15 @@ hipError_t launch_quant_mask_pack_batch(int count, const PackItem* items, int n_
   hipLaunchKernelGGL(k_gamma_finalize_batch, dim3((unsigned)count), dim3(256), 0, s, pb,
                      (const AbsumPartial*)part, (const unsigned long long*)hist);
   hipLaunchKernelGGL(pack, dim3((unsigned)np), dim3(256), 0, s, pb);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_sparse24(const uint16_t* codes, int64_t d_out, int64_t d_in, uint8_t* plane,
+                                unsigned long long* bad, hipStream_t s) {
+  const int64_t items = d_out * (d_in / 64);
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_pack_sparse24, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, codes, items,
+                     (uint4*)plane, bad);
   return hipGetLastError();
 }
 

@@ -13,6 +13,7 @@ namespace sbl {
 // ---------------------------------------------------------------------------
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -109,6 +110,15 @@ int device_cus();
 
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s);
+// Forward on the kept-only 2:4 plane (2:8 and 2:4 masks; d_in % 128 == 0).
+bool forward_sparse24_supported(int64_t d_in);
+hipError_t launch_forward_sparse24(const uint8_t* plane, const float* gamma, const int8_t* xq, const float* absmax,
+                                   int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s);
+// Code plane -> kept-only 2:4 plane (quant.hip); groups of 4 with more than 2
+// non-zeros are counted into *bad (may be null).
+hipError_t launch_pack_sparse24(const uint16_t* codes, int64_t d_out, int64_t d_in, uint8_t* plane,
+                                unsigned long long* bad, hipStream_t s);
+
 // Decode with the activation quantization fused in (x given as bf16).
 bool decode_fused_supported(int64_t T, int64_t d_in);
 hipError_t launch_decode_fused(const uint16_t* codes, const float* gamma, const uint16_t* x, int64_t T, int64_t d_in,

@@ -184,6 +184,18 @@ def test_decode_validation():
     assert s(6, 8192) == 0 and s(16, 3072) == 0
 
 
+def test_sparse24_validation():
+    f = lib.sbl_pack_sparse24
+    assert f(P, 256, 96, P, NULL, NULL) == SHAPE                               # d_in % 64
+    assert f(NULL, 256, 256, P, NULL, NULL) == INVALID
+    assert f(P, 256, 256, P_MIS, NULL, NULL) == INVALID
+    g = lib.sbl_forward_sparse24
+    assert g(NULL, NULL, NULL, NULL, 0, 256, 256, NULL, 0, NULL) == OK           # T = 0
+    assert g(P, P, P, P, 4, 192, 256, P, 0, NULL) == UNSUPPORTED                # d_in % 128
+    assert g(P, P, P, P, 4, 256, 256, P, 9, NULL) == INVALID
+    assert g(P, P, NULL, P, 4, 256, 256, P, 0, NULL) == INVALID
+
+
 def test_backward_validation():
     f = lib.sbl_backward
     # dX: the transposed 2-bit code plane (d_in rows of d_out rounded up to 64,

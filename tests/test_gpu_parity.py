@@ -88,6 +88,43 @@ def test_pack_batch_matches_single_calls(n, m, fq):
         assert f32_bits(gb[i].cpu().numpy()[0]) == f32_bits(rg)
 
 
+# Kept-only 2:4 plane and the forward on the sparse matrix instruction: the
+# plane bit-exact against the oracle, and the int32 sums (so every output)
+# identical to the dense path's.
+@pytest.mark.parametrize("n,m", [(2, 8), (2, 4), (1, 4)])
+@pytest.mark.parametrize("T,d_out,d_in", [(300, 200, 256), (77, 1000, 1152), (513, 256, 2048), (33, 40, 11008)])
+def test_sparse24_parity(T, d_out, d_in, n, m):
+    W = weight(67, n + m + d_in, d_out, d_in)
+    x = activation(67, d_out + T, T, d_in, dist="student_t4")
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), n, m=m)
+    plane, bad = sbl.pack_sparse24(codes)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    w_eff, _, _ = oracle.effective_weight(W, n, m)
+    if d_out * d_in <= 300_000:
+        np.testing.assert_array_equal(plane.cpu().numpy(), oracle.pack_sparse24(w_eff))
+    xq, a = sbl.act_quant(to_dev_bf16(x))
+    for dt in (sbl.I32, sbl.F32, sbl.BF16):
+        y_d = sbl.forward(codes, gamma, xq, a, out_dtype=dt)
+        y_s = sbl.forward_sparse24(plane, gamma, xq, a, out_dtype=dt)
+        torch.cuda.synchronize()
+        view = torch.int16 if dt == sbl.BF16 else torch.int32
+        assert torch.equal(y_s.view(view), y_d.view(view)), dt
+    acc_ref = oracle.forward_acc(w_eff, oracle.act_quant(x)[0])
+    np.testing.assert_array_equal(sbl.forward_sparse24(plane, gamma, xq, a, out_dtype=sbl.I32).cpu().numpy(), acc_ref)
+
+
+def test_sparse24_counts_unrepresentable_groups():
+    # a 6:8 code plane has groups of 4 with 3 or 4 non-zeros; their count is reported
+    W = weight(68, 0, 64, 256)
+    codes, _, _ = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+    _, bad = sbl.pack_sparse24(codes)
+    torch.cuda.synchronize()
+    w_eff = oracle.unpack_codes(bits16(codes))
+    want = int(np.count_nonzero(np.count_nonzero(w_eff.reshape(64, -1, 4), axis=-1) > 2))
+    assert want > 0 and int(bad.item()) == want
+
+
 @pytest.mark.parametrize("n,m", [(3, 8), (5, 8), (7, 8), (2, 4), (1, 4)])
 def test_step_parity_nm_patterns(n, m):
     # the forward and backward kernels take the planes of any pattern as they are
