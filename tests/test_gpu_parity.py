@@ -88,6 +88,45 @@ def test_pack_batch_matches_single_calls(n, m, fq):
         assert f32_bits(gb[i].cpu().numpy()[0]) == f32_bits(rg)
 
 
+def test_pack_graph_capture_matches_eager():
+    # the packing (three kernels, no memset) captured in a HIP graph: every replay, with
+    # eager work between the replays, equals the eager result bit for bit, single and batched
+    shapes = [(1000, 1032), (11008, 2048), (3, 24)]
+    Ws = [to_dev_bf16(weight(19, i, d_o, d_i)) for i, (d_o, d_i) in enumerate(shapes)]
+    want = [sbl.quant_mask_pack(W, 6) for W in Ws]
+    torch.cuda.synchronize()
+    one = [torch.empty_like(t) for t in want[0]]
+    bat = [[torch.empty_like(t) for t in w] for w in want]
+    ws1 = torch.empty((sbl.quant_workspace_size(*shapes[0]),), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty((sbl.quant_batch_workspace_size(shapes),), dtype=torch.uint8, device="cuda")
+
+    def run():
+        sbl.quant_mask_pack(Ws[0], 6, codes=one[0], mask=one[1], gamma=one[2], workspace=ws1)
+        sbl.quant_mask_pack_batch(Ws, 6, codes=[b[0] for b in bat], masks=[b[1] for b in bat],
+                                  gammas=[b[2] for b in bat], workspace=wsb)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(3):
+        for t in one + [t for b in bat for t in b]:
+            t.zero_()
+        other = sbl.quant_mask_pack(Ws[2], 2)           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, ref in [(one, want[0])] + list(zip(bat, want)):
+            assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]), f"replay {i}"
+            assert torch.equal(got[2].view(torch.int32), ref[2].view(torch.int32)), f"replay {i}"
+        assert other[0].shape == (3, 3)
+
+
 # Kept-only 2:4 plane and the forward on the sparse matrix instruction: the
 # plane bit-exact against the oracle, and the int32 sums (so every output)
 # identical to the dense path's.
@@ -531,10 +570,15 @@ def test_decode_graph_replay_matches_eager():
         assert other.shape == (8, 512)
 
 
-@pytest.mark.parametrize("name,d_out,d_in", [("gate", 11008, 2048), ("down", 2048, 11008)])
-def test_forward_full_size_sampled(name, d_out, d_in):
-    # the 3B-like training shapes at 32768 tokens, as timed: 64 sampled tokens, all outputs, exact int32
-    T = 32768
+# training shapes as timed: the 3B-like layer at 32768 tokens and the 1.5B-like one at 8192
+FULL_SHAPES = [("gate", 32768, 11008, 2048), ("down", 32768, 2048, 11008), ("q", 32768, 2048, 2048),
+               ("k", 32768, 256, 2048), ("gate_1.5b", 8192, 8960, 1536), ("down_1.5b", 8192, 1536, 8960),
+               ("q_1.5b", 8192, 1536, 1536)]
+
+
+@pytest.mark.parametrize("name,T,d_out,d_in", FULL_SHAPES)
+def test_forward_full_size_sampled(name, T, d_out, d_in):
+    # 64 sampled tokens, all outputs, exact int32
     W = weight(81, d_in, d_out, d_in)
     x = activation(81, d_out, T, d_in, dist="student_t4")
     rows = sample_rows(81, 2, T, 64)
@@ -595,11 +639,10 @@ def test_backward_dx_large_tiles_sampled():
     assert_grad_close(dW.cpu().numpy()[cols], dW_ref)
 
 
-@pytest.mark.parametrize("name,d_out,d_in", [("gate", 11008, 2048), ("down", 2048, 11008)])
-def test_backward_full_size_sampled(name, d_out, d_in):
-    # the 3B-like training shapes at 32768 tokens, as timed: dX on 64 sampled tokens,
-    # dW on 32 sampled output rows over all tokens (split-K and transposes included)
-    T = 32768
+@pytest.mark.parametrize("name,T,d_out,d_in", FULL_SHAPES)
+def test_backward_full_size_sampled(name, T, d_out, d_in):
+    # dX on 64 sampled tokens, dW on 32 sampled output rows over all tokens (split-K
+    # and transposes included)
     W = weight(91, d_in, d_out, d_in)
     x = activation(91, d_out, T, d_in, dist="student_t4")
     dY = grad_out(91, d_out + 1, T, d_out)
