@@ -406,11 +406,31 @@ def run_variants(args, wl):
 DECODE_FUSE_MAX = 4_000_000  # element-quantizations per launch up to which sbl_decode beats two calls
 
 
+# Linears of a decoder layer that read the same activations: q, k, v the normed hidden
+# state, gate and up the normed residual; o and down read their own inputs.
+DECODE_GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+
+def decode_groups(wl):
+    """Index groups of wl.linears that share one input (DECODE_GROUPS; anything else alone)."""
+    names = [L.name for L in wl.linears]
+    groups, seen = [], set()
+    for g in DECODE_GROUPS:
+        idx = [names.index(n) for n in g if n in names]
+        if idx:
+            groups.append(idx)
+            seen.update(idx)
+    groups += [[i] for i in range(len(names)) if i not in seen]
+    return groups
+
+
 def run_decode(args, wl, copies: int = 16):
     """Decode workload: act quant + forward of every linear of a layer on pre-packed codes, for
-    each token count and mask.  `copies` distinct packed copies of the layer (more bytes than
-    the 256 MB last-level cache) are walked in turn inside one captured HIP graph, so the code
-    planes stream from HBM; the figure is graph time / copies per layer."""
+    each token count and mask.  The linears that read the same activations (q, k, v; gate, up)
+    share one input and one call (sbl_decode_multi, or sbl_act_quant + sbl_forward_decode_multi).
+    `copies` distinct packed copies of the layer (more bytes than the 256 MB last-level cache)
+    are walked in turn inside one captured HIP graph, so the code planes stream from HBM; the
+    figure is graph time / copies per layer."""
     import numpy as np
     import torch
 
@@ -423,34 +443,37 @@ def run_decode(args, wl, copies: int = 16):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
     Ws = [up(weight(wl.cfg, mi, L.d_out, L.d_in)) for mi, L in enumerate(wl.linears)]
+    groups = decode_groups(wl)
     results = []
     for n_keep in wl.n_keep:
         packed = [sbl.quant_mask_pack(W, n_keep, want_mask=False) for W in Ws]
         # distinct buffers holding the same packed layer: the graph walks all of them
-        layers = [[(L, codes.clone(), gamma.clone()) for L, (codes, _, gamma) in zip(wl.linears, packed)]
-                  for _ in range(copies)]
+        layers = [[(codes.clone(), gamma.clone()) for (codes, _, gamma) in packed] for _ in range(copies)]
         torch.cuda.synchronize()
         code_bytes = sum(L.d_out * L.d_in // 4 for L in wl.linears)
         for T in wl.T:
-            bufs = []
-            for mi, L in enumerate(wl.linears):
-                x = up(activation(wl.cfg, mi, T, L.d_in, dist=wl.act_dist))
-                bufs.append(dict(x=x, x_q=torch.empty((T, L.d_in), dtype=torch.int8, device=dev),
-                                 a=torch.empty((T,), dtype=torch.float32, device=dev),
-                                 y=torch.empty((T, L.d_out), dtype=torch.bfloat16, device=dev)))
-
-            # one fused launch (sbl_decode) where it applies and its per-block re-quantization
-            # of the T rows stays small (T * d_in * blocks of 16 rows), else act quant + forward
-            fused = [sbl.decode_supported(T, L.d_in) and T * L.d_in * -(-L.d_out // 16) <= DECODE_FUSE_MAX
-                     for L in wl.linears]
+            gbufs = []
+            for g in groups:
+                L0 = wl.linears[g[0]]
+                x = up(activation(wl.cfg, g[0], T, L0.d_in, dist=wl.act_dist))
+                # one fused launch (sbl_decode_multi) where it applies and its per-block
+                # re-quantization of the T rows stays small (T * d_in * blocks of 16 rows),
+                # else act quant + one sbl_forward_decode_multi
+                blocks = sum(-(-wl.linears[i].d_out // 16) for i in g)
+                gbufs.append(dict(x=x, fused=sbl.decode_supported(T, L0.d_in) and T * L0.d_in * blocks <= DECODE_FUSE_MAX,
+                                  x_q=torch.empty((T, L0.d_in), dtype=torch.int8, device=dev),
+                                  a=torch.empty((T,), dtype=torch.float32, device=dev),
+                                  ys=[torch.empty((T, wl.linears[i].d_out), dtype=torch.bfloat16, device=dev)
+                                      for i in g]))
 
             def layer(mats):
-                for (L, codes, gamma), b, fu in zip(mats, bufs, fused):
-                    if fu:
-                        sbl.decode(codes, gamma, b["x"], out_dtype=sbl.BF16, y=b["y"])
+                for g, b in zip(groups, gbufs):
+                    gm = [mats[i] for i in g]
+                    if b["fused"]:
+                        sbl.decode_multi(gm, b["x"], out_dtype=sbl.BF16, ys=b["ys"])
                     else:
                         sbl.act_quant(b["x"], x_q=b["x_q"], absmax=b["a"])
-                        sbl.forward(codes, gamma, b["x_q"], b["a"], out_dtype=sbl.BF16, y=b["y"])
+                        sbl.forward_decode_multi(gm, b["x_q"], b["a"], out_dtype=sbl.BF16, ys=b["ys"])
 
             side = torch.cuda.Stream()
             side.wait_stream(torch.cuda.current_stream())
@@ -474,8 +497,10 @@ def run_decode(args, wl, copies: int = 16):
             e1.record()
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) * 1e3 / args.steps / copies
-            io_bytes = sum(2 * T * L.d_in + 2 * T * L.d_out for L in wl.linears)
-            results.append({"T": T, "n_keep": n_keep, "us_per_layer": round(us, 3), "fused_linears": sum(fused),
+            io_bytes = (sum(2 * T * wl.linears[grp[0]].d_in for grp in groups)
+                        + sum(2 * T * L.d_out for L in wl.linears))
+            launches = sum(1 if b["fused"] else 2 for b in gbufs)
+            results.append({"T": T, "n_keep": n_keep, "us_per_layer": round(us, 3), "launches_per_layer": launches,
                             "tokens_per_s": round(T / (us * 1e-6), 1),
                             "GBps": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9, 1),
                             "frac_hbm": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
@@ -485,6 +510,7 @@ def run_decode(args, wl, copies: int = 16):
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
             "vs_baseline": None, "dtype": "int8 x ternary (int32 accumulate), y bf16", "data": "synthetic",
             "config": {"workload": wl.name, "layer_copies_per_graph": copies,
+                       "input_groups": ["+".join(wl.linears[i].name for i in grp) for grp in groups],
                        "code_bytes_per_layer": code_bytes}, "results": results}
     print(json.dumps(line), flush=True)
 

@@ -308,6 +308,41 @@ SBL_API int sbl_decode(const uint16_t* codes, const float* gamma, const uint16_t
 /* 1 if sbl_decode takes this (T, d_in), else 0. */
 SBL_API int sbl_decode_supported(int64_t T, int64_t d_in);
 
+/* Decode of several matrices that read the same activations, in one launch:
+ * a layer's q, k and v projections (one normed hidden state), or gate and up
+ * ([SUM] Table 3, decode rows: every linear of the decoder layer runs per
+ * generated token batch).  Each item is one matrix of the same d_in:
+ *
+ *   y_i[t, o] = (sum_k x_q[t, k] W_eff,i[o, k]) * gamma_i * absmax[t] / 127
+ *
+ * bit-identical to one sbl_decode (sbl_decode_multi, x as bf16, the
+ * activation quantization fused in; sbl_decode_supported(T, d_in) must hold)
+ * or one sbl_forward (sbl_forward_decode_multi, x_q and absmax from
+ * sbl_act_quant; 0 <= T <= 64 and d_in % 64 == 0) per item.  Blocks of 16
+ * output rows of every item share the launch, so the fixed cost of a launch
+ * (several us at these sizes) is paid once per group instead of per matrix.
+ *
+ * items : HOST array of `count` descriptors, 1 <= count <= SBL_DECODE_MULTI_MAX;
+ *         codes and gamma as from sbl_quant_mask_pack for W_i [d_out, d_in];
+ *         y [T, d_out] of y_dtype (SBL_F32, SBL_BF16 or SBL_I32); codes and y
+ *         16-byte aligned, gamma 4-byte aligned.
+ * Errors: SBL_ERR_INVALID_ARG (count, NULL or misaligned pointers, y_dtype),
+ * SBL_ERR_SHAPE, SBL_ERR_UNSUPPORTED (T or d_in outside the range above);
+ * nothing is enqueued then.  T = 0 is a no-op.
+ */
+#define SBL_DECODE_MULTI_MAX 4
+typedef struct sbl_decode_item {
+  const uint16_t* codes;
+  const float* gamma;
+  int64_t d_out;
+  void* y;
+} sbl_decode_item;
+
+SBL_API int sbl_decode_multi(int count, const sbl_decode_item* items, const uint16_t* x_bf16, int64_t T,
+                             int64_t d_in, int y_dtype, void* hip_stream);
+SBL_API int sbl_forward_decode_multi(int count, const sbl_decode_item* items, const int8_t* x_q, const float* absmax,
+                                     int64_t T, int64_t d_in, int y_dtype, void* hip_stream);
+
 /* Kept-only 2:4 operand plane for 2:8 and 2:4 masks, and the forward on it,
  * which runs on gfx950's sparse int8 matrix instruction (2 stored values of
  * every 4 k): half the matrix work of sbl_forward for the same result ([SUM]

@@ -58,6 +58,8 @@ _SIGNATURES = {
     "sbl_forward_sparse24": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode_supported": (_c_int, [_c_i64, _c_i64]),
+    "sbl_decode_multi": (_c_int, [_c_int, ctypes.c_void_p, _c_ptr, _c_i64, _c_i64, _c_int, _c_ptr]),
+    "sbl_forward_decode_multi": (_c_int, [_c_int, ctypes.c_void_p, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_int, _c_ptr]),
     "sbl_backward_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int]),
     "sbl_backward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int,
                               _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr]),
@@ -75,6 +77,15 @@ class PackItem(ctypes.Structure):
 
 
 PACK_BATCH_MAX = 16
+
+
+class DecodeItem(ctypes.Structure):
+    """sbl_decode_item (host struct)."""
+    _fields_ = [("codes", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("d_out", ctypes.c_int64),
+                ("y", ctypes.c_void_p)]
+
+
+DECODE_MULTI_MAX = 4
 
 
 class AdamwParams(ctypes.Structure):
@@ -406,6 +417,56 @@ def decode(codes: torch.Tensor, gamma: torch.Tensor, x: torch.Tensor, *, out_dty
     _check(lib.sbl_decode(_ptr(codes), _ptr(gamma), _ptr(x), T, d_in, d_out, _ptr(y), int(out_dtype),
                           _stream(stream)), "sbl_decode")
     return y
+
+
+def _decode_items(mats, T: int, d_in: int, out_dtype: int, ys, dev):
+    mats = list(mats)
+    n = len(mats)
+    if not 1 <= n <= DECODE_MULTI_MAX:
+        raise ValueError(f"1..{DECODE_MULTI_MAX} matrices per call, got {n}")
+    if out_dtype not in _OUT_TORCH:
+        raise ValueError(f"unknown out_dtype {out_dtype}")
+    ys = list(ys) if ys is not None else [None] * n
+    items = (DecodeItem * n)()
+    for i, (codes, gamma) in enumerate(mats):
+        _dev(codes, f"codes[{i}]")
+        _dev(gamma, f"gamma[{i}]")
+        d_out, G = codes.shape
+        if G * 8 != d_in:
+            raise ValueError(f"codes[{i}] [{d_out}, {G}] do not match d_in = {d_in}")
+        if ys[i] is None:
+            ys[i] = torch.empty((T, d_out), dtype=_OUT_TORCH[out_dtype], device=dev)
+        _out(ys[i], (T, d_out), (_OUT_TORCH[out_dtype],), dev, f"y[{i}]")
+        items[i] = DecodeItem(codes.data_ptr(), gamma.data_ptr(), d_out, ys[i].data_ptr())
+    return items, ys
+
+
+def decode_multi(mats, x: torch.Tensor, *, out_dtype: int = F32, ys=None, stream=None):
+    """``decode`` of up to 4 matrices that read the same ``x`` (a layer's q, k, v or gate, up), in one
+    launch.  ``mats`` is a list of ``(codes, gamma)``; returns the list of outputs, each bit-identical to
+    ``decode`` of that matrix alone."""
+    _dev(x, "x")
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be a 2-D bfloat16 tensor")
+    T, d_in = x.shape
+    items, ys = _decode_items(mats, T, d_in, out_dtype, ys, x.device)
+    _check(lib.sbl_decode_multi(len(ys), ctypes.c_void_p(ctypes.addressof(items)), _ptr(x), T, d_in,
+                                int(out_dtype), _stream(stream)), "sbl_decode_multi")
+    return ys
+
+
+def forward_decode_multi(mats, x_q: torch.Tensor, absmax: torch.Tensor, *, out_dtype: int = F32, ys=None,
+                         stream=None):
+    """``forward`` of up to 4 matrices that read the same ``x_q`` at decode sizes (T <= 64), in one launch;
+    each output bit-identical to ``forward`` of that matrix alone."""
+    _dev(x_q, "x_q")
+    _dev(absmax, "absmax")
+    T, d_in = x_q.shape
+    items, ys = _decode_items(mats, T, d_in, out_dtype, ys, x_q.device)
+    _check(lib.sbl_forward_decode_multi(len(ys), ctypes.c_void_p(ctypes.addressof(items)), _ptr(x_q),
+                                        _ptr(absmax), T, d_in, int(out_dtype), _stream(stream)),
+           "sbl_forward_decode_multi")
+    return ys
 
 
 def backward(codes: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax: torch.Tensor,

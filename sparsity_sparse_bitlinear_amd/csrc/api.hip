@@ -273,6 +273,62 @@ SBL_API int sbl_decode(const uint16_t* codes, const float* gamma, const uint16_t
   return SBL_OK;
 }
 
+static_assert(SBL_DECODE_MULTI_MAX == kDecodeMultiMax, "decode group limit");
+
+// Shared checks of the multi-matrix decode entry points; fills it[].
+static int check_decode_items(int count, const sbl_decode_item* items, int64_t d_in, int y_dtype, DecodeItem* it) {
+  SBL_REQUIRE(items && count >= 1 && count <= SBL_DECODE_MULTI_MAX, SBL_ERR_INVALID_ARG,
+              "count=%d: 1..%d items (host array) required", count, SBL_DECODE_MULTI_MAX);
+  SBL_REQUIRE(y_dtype == SBL_F32 || y_dtype == SBL_BF16 || y_dtype == SBL_I32, SBL_ERR_INVALID_ARG,
+              "y_dtype=%d is not SBL_F32, SBL_BF16 or SBL_I32", y_dtype);
+  for (int i = 0; i < count; ++i) {
+    const sbl_decode_item& q = items[i];
+    const int rc = check_dims(q.d_out, d_in);
+    if (rc != SBL_OK) return rc;
+    SBL_REQUIRE(q.codes && q.gamma && q.y, SBL_ERR_INVALID_ARG, "item %d: codes, gamma and y must be non-NULL", i);
+    SBL_REQUIRE(aligned(q.codes, 16) && aligned(q.y, 16) && aligned(q.gamma, 4), SBL_ERR_INVALID_ARG,
+                "item %d: codes and y must be 16-byte aligned, gamma 4-byte aligned", i);
+    it[i] = DecodeItem{q.codes, q.gamma, q.d_out, q.y};
+  }
+  return SBL_OK;
+}
+
+SBL_API int sbl_decode_multi(int count, const sbl_decode_item* items, const uint16_t* x_bf16, int64_t T,
+                             int64_t d_in, int y_dtype, void* hip_stream) {
+  DecodeItem it[SBL_DECODE_MULTI_MAX];
+  int rc = check_tokens(T);
+  if (rc != SBL_OK) return rc;
+  rc = check_decode_items(count, items, d_in, y_dtype, it);
+  if (rc != SBL_OK) return rc;
+  if (T == 0) return SBL_OK;
+  SBL_REQUIRE(decode_fused_supported(T, d_in), SBL_ERR_UNSUPPORTED,
+              "sbl_decode_multi takes what sbl_decode takes (got T=%lld, d_in=%lld); "
+              "use sbl_act_quant + sbl_forward_decode_multi",
+              (long long)T, (long long)d_in);
+  SBL_REQUIRE(x_bf16 && aligned(x_bf16, 16), SBL_ERR_INVALID_ARG, "x must be non-NULL and 16-byte aligned");
+  hipError_t e = launch_decode_fused_multi(count, it, x_bf16, T, d_in, y_dtype, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_decode_multi launch");
+  return SBL_OK;
+}
+
+SBL_API int sbl_forward_decode_multi(int count, const sbl_decode_item* items, const int8_t* x_q, const float* absmax,
+                                     int64_t T, int64_t d_in, int y_dtype, void* hip_stream) {
+  DecodeItem it[SBL_DECODE_MULTI_MAX];
+  int rc = check_tokens(T);
+  if (rc != SBL_OK) return rc;
+  rc = check_decode_items(count, items, d_in, y_dtype, it);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(T <= 64 && d_in % 64 == 0, SBL_ERR_UNSUPPORTED,
+              "sbl_forward_decode_multi takes T <= 64 and d_in %% 64 == 0 (got T=%lld, d_in=%lld); use sbl_forward",
+              (long long)T, (long long)d_in);
+  if (T == 0) return SBL_OK;
+  SBL_REQUIRE(x_q && absmax && aligned(x_q, 16) && aligned(absmax, 4), SBL_ERR_INVALID_ARG,
+              "x_q (16-byte aligned) and absmax (4-byte aligned) must be non-NULL");
+  hipError_t e = launch_forward_decode_multi(count, it, x_q, absmax, T, d_in, y_dtype, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_forward_decode_multi launch");
+  return SBL_OK;
+}
+
 SBL_API int sbl_pack_sparse24(const uint16_t* codes, int64_t d_out, int64_t d_in, uint8_t* plane, uint64_t* bad,
                               void* hip_stream) {
   int rc = check_dims(d_out, d_in);

@@ -713,17 +713,39 @@ __device__ __forceinline__ void decode_store(v4i (&acc)[NTT], int (*red)[NTT][4]
   }
 }
 
+// Up to kDecodeMultiMax matrices that share one activation input (a layer's
+// q, k and v, or gate and up) in one launch: the blocks are dealt to the
+// matrices by the prefix sums of their 16-row blocks, so each block still
+// owns 16 output rows of one matrix and computes exactly what a launch for
+// that matrix alone computes.
+struct DecBatch {
+  int count;
+  int begin[kDecodeMultiMax + 1];  // row blocks of matrix i: [begin[i], begin[i + 1])
+  int d_out[kDecodeMultiMax];
+  const uint16_t* codes[kDecodeMultiMax];
+  const float* gamma[kDecodeMultiMax];
+  void* y[kDecodeMultiMax];
+};
+
+__device__ __forceinline__ int dec_item(const DecBatch& db, int b) {
+  int i = 0;
+  while (i + 1 < db.count && b >= db.begin[i + 1]) ++i;
+  return i;
+}
+
 template <int NTT, int OUT, int W>
-__global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict__ xq,
-                                                       const uint16_t* __restrict__ codes,
-                                                       const float* __restrict__ gamma_p,
-                                                       const float* __restrict__ absmax, int T, int d_in,
-                                                       int d_out, void* __restrict__ y) {
+__global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict__ xq, const DecBatch db,
+                                                       const float* __restrict__ absmax, int T, int d_in) {
   __shared__ int red[W - 1][NTT][4][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int o0 = blockIdx.x * kDecRows;
+  const int item = dec_item(db, blockIdx.x);
+  const uint16_t* __restrict__ codes = db.codes[item];
+  const float* __restrict__ gamma_p = db.gamma[item];
+  const int d_out = db.d_out[item];
+  void* __restrict__ y = db.y[item];
+  const int o0 = (blockIdx.x - db.begin[item]) * kDecRows;
   const int G = d_in >> 3;
   const int nks = d_in >> 6;
   const int per = (nks + W - 1) / W;
@@ -796,17 +818,20 @@ inline int decode_fused_min_waves(int64_t T, int64_t d_in) {
 }
 
 template <int OUT, int W>
-__global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restrict__ x,
-                                                         const uint16_t* __restrict__ codes,
-                                                         const float* __restrict__ gamma_p, int T, int d_in,
-                                                         int d_out, void* __restrict__ y) {
+__global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restrict__ x, const DecBatch db, int T,
+                                                         int d_in) {
   extern __shared__ __attribute__((aligned(16))) char xs[];  // [T][d_in + 16] int8
   __shared__ int red[W - 1][1][4][64];
   __shared__ float amax[16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int o0 = blockIdx.x * kDecRows;
+  const int item = dec_item(db, blockIdx.x);
+  const uint16_t* __restrict__ codes = db.codes[item];
+  const float* __restrict__ gamma_p = db.gamma[item];
+  const int d_out = db.d_out[item];
+  void* __restrict__ y = db.y[item];
+  const int o0 = (blockIdx.x - db.begin[item]) * kDecRows;
   const int G = d_in >> 3;
   const int nks = d_in >> 6;
   const int ld = d_in + 16;  // tile row stride: rows 16 bytes apart shift the banks
@@ -872,34 +897,50 @@ __global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restr
 }
 
 template <int NTT, int W>
-hipError_t launch_decode_w(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax, int64_t T,
-                           int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
-  const dim3 grid((unsigned)((d_out + kDecRows - 1) / kDecRows)), block(64 * W);
+hipError_t launch_decode_w(const DecBatch& db, const int8_t* xq, const float* absmax, int64_t T, int64_t d_in,
+                           int y_dtype, hipStream_t s) {
+  const dim3 grid((unsigned)db.begin[db.count]), block(64 * W);
   switch (y_dtype) {
     case SBL_F32:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_F32, W>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
-                         (int)d_in, (int)d_out, y);
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_F32, W>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
       break;
     case SBL_BF16:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_BF16, W>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
-                         (int)d_in, (int)d_out, y);
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_BF16, W>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
       break;
     default:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_I32, W>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
-                         (int)d_in, (int)d_out, y);
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_I32, W>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
       break;
   }
   return hipGetLastError();
 }
 
 template <int NTT>
-hipError_t launch_decode(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax, int64_t T,
-                         int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
-  switch (decode_waves((d_out + kDecRows - 1) / kDecRows, 4)) {
-    case 16: return launch_decode_w<NTT, 16>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
-    case 8: return launch_decode_w<NTT, 8>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
-    default: return launch_decode_w<NTT, 4>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
+hipError_t launch_decode(const DecBatch& db, const int8_t* xq, const float* absmax, int64_t T, int64_t d_in,
+                         int y_dtype, hipStream_t s) {
+  switch (decode_waves(db.begin[db.count], 4)) {
+    case 16: return launch_decode_w<NTT, 16>(db, xq, absmax, T, d_in, y_dtype, s);
+    case 8: return launch_decode_w<NTT, 8>(db, xq, absmax, T, d_in, y_dtype, s);
+    default: return launch_decode_w<NTT, 4>(db, xq, absmax, T, d_in, y_dtype, s);
   }
+}
+
+// Descriptor of count matrices; false if the row blocks overflow an int.
+bool make_dec_batch(int count, const DecodeItem* items, DecBatch& db) {
+  if (count < 1 || count > kDecodeMultiMax) return false;
+  db = DecBatch{};
+  db.count = count;
+  int64_t nb = 0;
+  for (int i = 0; i < count; ++i) {
+    db.begin[i] = (int)nb;
+    db.d_out[i] = (int)items[i].d_out;
+    db.codes[i] = items[i].codes;
+    db.gamma[i] = items[i].gamma;
+    db.y[i] = items[i].y;
+    nb += (items[i].d_out + kDecRows - 1) / kDecRows;
+    if (nb > 0x7FFFFFFF) return false;
+  }
+  db.begin[count] = (int)nb;
+  return true;
 }
 
 template <bool VEC>
@@ -968,8 +1009,8 @@ hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (T <= 64 && d_in % 64 == 0) {
-    if (T <= 16) return launch_decode<1>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
-    return launch_decode<4>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
+    const DecodeItem it{codes, gamma, d_out, y};
+    return launch_forward_decode_multi(1, &it, xq, absmax, T, d_in, y_dtype, s);
   }
   if (d_in % kFK == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes)
     return launch_fwd_direct<false>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
@@ -992,34 +1033,49 @@ bool decode_fused_supported(int64_t T, int64_t d_in) {
 }
 
 template <int W>
-hipError_t launch_decode_fused_w(const uint16_t* codes, const float* gamma, const uint16_t* x, int64_t T,
-                                 int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
-  const dim3 grid((unsigned)((d_out + kDecRows - 1) / kDecRows)), block(64 * W);
+hipError_t launch_decode_fused_w(const DecBatch& db, const uint16_t* x, int64_t T, int64_t d_in, int y_dtype,
+                                 hipStream_t s) {
+  const dim3 grid((unsigned)db.begin[db.count]), block(64 * W);
   const size_t lds = (size_t)T * (size_t)(d_in + 16);
   switch (y_dtype) {
     case SBL_F32:
-      hipLaunchKernelGGL((k_decode_fused<SBL_F32, W>), grid, block, lds, s, x, codes, gamma, (int)T, (int)d_in,
-                         (int)d_out, y);
+      hipLaunchKernelGGL((k_decode_fused<SBL_F32, W>), grid, block, lds, s, x, db, (int)T, (int)d_in);
       break;
     case SBL_BF16:
-      hipLaunchKernelGGL((k_decode_fused<SBL_BF16, W>), grid, block, lds, s, x, codes, gamma, (int)T, (int)d_in,
-                         (int)d_out, y);
+      hipLaunchKernelGGL((k_decode_fused<SBL_BF16, W>), grid, block, lds, s, x, db, (int)T, (int)d_in);
       break;
     default:
-      hipLaunchKernelGGL((k_decode_fused<SBL_I32, W>), grid, block, lds, s, x, codes, gamma, (int)T, (int)d_in,
-                         (int)d_out, y);
+      hipLaunchKernelGGL((k_decode_fused<SBL_I32, W>), grid, block, lds, s, x, db, (int)T, (int)d_in);
       break;
   }
   return hipGetLastError();
 }
 
+hipError_t launch_decode_fused_multi(int count, const DecodeItem* items, const uint16_t* x, int64_t T, int64_t d_in,
+                                     int y_dtype, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  DecBatch db;
+  if (!decode_fused_supported(T, d_in) || !make_dec_batch(count, items, db)) return hipErrorInvalidValue;
+  switch (decode_waves(db.begin[count], decode_fused_min_waves(T, d_in))) {
+    case 16: return launch_decode_fused_w<16>(db, x, T, d_in, y_dtype, s);
+    case 8: return launch_decode_fused_w<8>(db, x, T, d_in, y_dtype, s);
+    default: return launch_decode_fused_w<4>(db, x, T, d_in, y_dtype, s);
+  }
+}
+
 hipError_t launch_decode_fused(const uint16_t* codes, const float* gamma, const uint16_t* x, int64_t T, int64_t d_in,
                                int64_t d_out, void* y, int y_dtype, hipStream_t s) {
-  switch (decode_waves((d_out + kDecRows - 1) / kDecRows, decode_fused_min_waves(T, d_in))) {
-    case 16: return launch_decode_fused_w<16>(codes, gamma, x, T, d_in, d_out, y, y_dtype, s);
-    case 8: return launch_decode_fused_w<8>(codes, gamma, x, T, d_in, d_out, y, y_dtype, s);
-    default: return launch_decode_fused_w<4>(codes, gamma, x, T, d_in, d_out, y, y_dtype, s);
-  }
+  const DecodeItem it{codes, gamma, d_out, y};
+  return launch_decode_fused_multi(1, &it, x, T, d_in, y_dtype, s);
+}
+
+hipError_t launch_forward_decode_multi(int count, const DecodeItem* items, const int8_t* xq, const float* absmax,
+                                       int64_t T, int64_t d_in, int y_dtype, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  DecBatch db;
+  if (T > 64 || d_in % 64 != 0 || !make_dec_batch(count, items, db)) return hipErrorInvalidValue;
+  if (T <= 16) return launch_decode<1>(db, xq, absmax, T, d_in, y_dtype, s);
+  return launch_decode<4>(db, xq, absmax, T, d_in, y_dtype, s);
 }
 
 }  // namespace sbl

@@ -123,6 +123,19 @@ hipError_t launch_pack_sparse24(const uint16_t* codes, int64_t d_out, int64_t d_
 bool decode_fused_supported(int64_t T, int64_t d_in);
 hipError_t launch_decode_fused(const uint16_t* codes, const float* gamma, const uint16_t* x, int64_t T, int64_t d_in,
                                int64_t d_out, void* y, int y_dtype, hipStream_t s);
+// Several matrices sharing one input in one launch (gemm_fwd.hip): the fused
+// decode above, and the decode-size product of x_q (T <= 64, d_in % 64 == 0).
+constexpr int kDecodeMultiMax = 4;
+struct DecodeItem {
+  const uint16_t* codes;
+  const float* gamma;
+  int64_t d_out;
+  void* y;
+};
+hipError_t launch_decode_fused_multi(int count, const DecodeItem* items, const uint16_t* x, int64_t T, int64_t d_in,
+                                     int y_dtype, hipStream_t s);
+hipError_t launch_forward_decode_multi(int count, const DecodeItem* items, const int8_t* xq, const float* absmax,
+                                       int64_t T, int64_t d_in, int y_dtype, hipStream_t s);
 
 // C[M, N] = alpha * A[M, K] B[N, K]^T, bf16 operands, float32 or bf16 output
 // (gemm_nt.hip).  Only for shapes where gemm_nt_bf16_supported() holds.

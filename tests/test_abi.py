@@ -184,6 +184,32 @@ def test_decode_validation():
     assert s(6, 8192) == 0 and s(16, 3072) == 0
 
 
+def test_decode_multi_validation():
+    import sparsity_sparse_bitlinear_amd as sbl
+    items = (sbl.DecodeItem * 3)(sbl.DecodeItem(0x10000, 0x20000, 2048, 0x30000),
+                                 sbl.DecodeItem(0x40000, 0x50000, 256, 0x60000),
+                                 sbl.DecodeItem(0x70000, 0x80000, 40, 0x90000))
+    ip = ctypes.c_void_p(ctypes.addressof(items))
+    for f, extra in ((lib.sbl_decode_multi, (P,)), (lib.sbl_forward_decode_multi, (P, P))):
+        assert f(3, ip, *extra, 0, 256, 0, NULL) == OK                            # T = 0: no-op
+        assert f(0, ip, *extra, 4, 256, 0, NULL) == INVALID
+        assert f(5, ip, *extra, 4, 256, 0, NULL) == INVALID
+        assert f(3, NULL, *extra, 4, 256, 0, NULL) == INVALID
+        assert f(3, ip, *extra, 4, 256, 7, NULL) == INVALID                       # bad dtype
+        assert f(3, ip, *extra, 4, 250, 0, NULL) == SHAPE                         # d_in % 8
+        assert f(3, ip, *extra, 4, 264, 0, NULL) == UNSUPPORTED                   # d_in % 64
+        assert f(3, ip, *extra, 65, 256, 0, NULL) == UNSUPPORTED                  # T > 64
+        items[1].y = 0x60008                                                      # misaligned y
+        assert f(3, ip, *extra, 4, 256, 0, NULL) == INVALID
+        items[1].y = 0x60000
+        items[2].gamma = None
+        assert f(3, ip, *extra, 4, 256, 0, NULL) == INVALID
+        items[2].gamma = 0x80000
+    assert lib.sbl_decode_multi(3, ip, P, 17, 256, 0, NULL) == UNSUPPORTED        # T > 16 (fused form)
+    assert lib.sbl_decode_multi(3, ip, NULL, 4, 256, 0, NULL) == INVALID
+    assert lib.sbl_forward_decode_multi(3, ip, P, NULL, 4, 256, 0, NULL) == INVALID
+
+
 def test_sparse24_validation():
     f = lib.sbl_pack_sparse24
     assert f(P, 256, 96, P, NULL, NULL) == SHAPE                               # d_in % 64

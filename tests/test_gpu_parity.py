@@ -482,6 +482,65 @@ def test_decode_fused_parity(T, d_out, d_in, n):
     assert_y_close(sbl.decode(codes, gamma, xd, out_dtype=sbl.F32).cpu().numpy(), y_ref, acc_ref)
 
 
+DECODE_GROUPS = {"qkv": [(2048, 2048), (256, 2048), (256, 2048)], "gate_up": [(11008, 2048), (11008, 2048)],
+                 "ragged": [(40, 1024), (8, 1024), (1000, 1024), (17, 1024)]}
+
+
+def decode_group(group, T, n=6):
+    shapes = DECODE_GROUPS[group]
+    d_in = shapes[0][1]
+    Ws = [weight(77, 10 * i + len(group), d_o, d_i) for i, (d_o, d_i) in enumerate(shapes)]
+    mats = []
+    for W in Ws:
+        codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), n, want_mask=False)
+        mats.append((codes, gamma))
+    x = activation(77, 99 + T, T, d_in, dist="student_t4")
+    return Ws, mats, x
+
+
+def same_bits(a, b, dt):
+    v = torch.int16 if dt == sbl.BF16 else torch.int32
+    return torch.equal(a.view(v), b.view(v))
+
+
+@pytest.mark.parametrize("group", sorted(DECODE_GROUPS))
+@pytest.mark.parametrize("T", [1, 5, 16])
+def test_decode_multi_matches_single(T, group):
+    # several matrices sharing x in one launch: every output equals decode of that matrix alone
+    Ws, mats, x = decode_group(group, T)
+    xd = to_dev_bf16(x)
+    for dt in (sbl.I32, sbl.BF16, sbl.F32):
+        ys = sbl.decode_multi(mats, xd, out_dtype=dt)
+        for (codes, gamma), y in zip(mats, ys):
+            want = sbl.decode(codes, gamma, xd, out_dtype=dt)
+            torch.cuda.synchronize()
+            assert same_bits(y, want, dt), (group, T, dt)
+    if group == "ragged":  # and, directly, against the oracle
+        ys = sbl.decode_multi(mats, xd, out_dtype=sbl.I32)
+        for W, y in zip(Ws, ys):
+            acc_ref, _ = ref_forward(W, x, 6)
+            np.testing.assert_array_equal(y.cpu().numpy(), acc_ref)
+
+
+@pytest.mark.parametrize("group", sorted(DECODE_GROUPS))
+@pytest.mark.parametrize("T", [1, 16, 33, 64])
+def test_forward_decode_multi_matches_single(T, group):
+    # the same with x_q given (every decode token count, one and four token tiles)
+    Ws, mats, x = decode_group(group, T)
+    xq, a = sbl.act_quant(to_dev_bf16(x))
+    for dt in (sbl.I32, sbl.BF16, sbl.F32):
+        ys = sbl.forward_decode_multi(mats, xq, a, out_dtype=dt)
+        for (codes, gamma), y in zip(mats, ys):
+            want = sbl.forward(codes, gamma, xq, a, out_dtype=dt)
+            torch.cuda.synchronize()
+            assert same_bits(y, want, dt), (group, T, dt)
+    if group == "ragged":
+        ys = sbl.forward_decode_multi(mats, xq, a, out_dtype=sbl.I32)
+        for W, y in zip(Ws, ys):
+            acc_ref, _ = ref_forward(W, x, 6)
+            np.testing.assert_array_equal(y.cpu().numpy(), acc_ref)
+
+
 @pytest.mark.parametrize("T,d_in", [(1, 8192), (5, 8192), (16, 3008)])
 def test_decode_fused_largest_rows(T, d_in):
     # the longest rows the fused path takes (16 register chunks per lane, the 48 KB tile)
