@@ -817,7 +817,9 @@ inline int decode_fused_min_waves(int64_t T, int64_t d_in) {
   return 0;
 }
 
-template <int OUT, int W>
+// NCH: 16-byte x chunks per lane (d_in <= 512 NCH), sized to the row so that
+// short rows do not hold registers for long ones (occupancy).
+template <int OUT, int W, int NCH>
 __global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restrict__ x, const DecBatch db, int T,
                                                          int d_in) {
   extern __shared__ __attribute__((aligned(16))) char xs[];  // [T][d_in + 16] int8
@@ -852,9 +854,9 @@ __global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restr
   const int nch = d_in >> 3;
   const int t = wave;
   const auto xr = make_rsrc(x, clamp_bytes((int64_t)T * d_in * 2));
-  uint4 xv[kFuseChunks];
+  uint4 xv[NCH];
 #pragma unroll
-  for (int i = 0; i < kFuseChunks; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int j = lane + 64 * i;
     xv[i] = bload16(xr, t < T && j < nch ? (uint32_t)((t * d_in + 8 * j) * 2) : kOOB);
   }
@@ -862,14 +864,14 @@ __global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restr
   if (t < T) {  // wave-uniform
     uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < kFuseChunks; ++i)
+    for (int i = 0; i < NCH; ++i)
       m = max(m, max(max(max_mag2(xv[i].x), max_mag2(xv[i].y)), max(max_mag2(xv[i].z), max_mag2(xv[i].w))));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
     if (lane == 0) amax[t] = __uint_as_float(m << 16);
     const ActScale qs = act_scale(m ? __uint_as_float(m << 16) : 1.0f);
 #pragma unroll
-    for (int i = 0; i < kFuseChunks; ++i) {
+    for (int i = 0; i < NCH; ++i) {
       const int j = lane + 64 * i;
       if (j < nch) *(uint2*)(xs + t * ld + 8 * j) = m ? quant_chunk(xv[i], qs.k, qs.as, qs.c) : make_uint2(0u, 0u);
     }
@@ -1032,23 +1034,33 @@ bool decode_fused_supported(int64_t T, int64_t d_in) {
          decode_fused_min_waves(T, d_in) > 0;
 }
 
-template <int W>
-hipError_t launch_decode_fused_w(const DecBatch& db, const uint16_t* x, int64_t T, int64_t d_in, int y_dtype,
-                                 hipStream_t s) {
+template <int W, int NCH>
+hipError_t launch_decode_fused_wc(const DecBatch& db, const uint16_t* x, int64_t T, int64_t d_in, int y_dtype,
+                                  hipStream_t s) {
   const dim3 grid((unsigned)db.begin[db.count]), block(64 * W);
   const size_t lds = (size_t)T * (size_t)(d_in + 16);
   switch (y_dtype) {
     case SBL_F32:
-      hipLaunchKernelGGL((k_decode_fused<SBL_F32, W>), grid, block, lds, s, x, db, (int)T, (int)d_in);
+      hipLaunchKernelGGL((k_decode_fused<SBL_F32, W, NCH>), grid, block, lds, s, x, db, (int)T, (int)d_in);
       break;
     case SBL_BF16:
-      hipLaunchKernelGGL((k_decode_fused<SBL_BF16, W>), grid, block, lds, s, x, db, (int)T, (int)d_in);
+      hipLaunchKernelGGL((k_decode_fused<SBL_BF16, W, NCH>), grid, block, lds, s, x, db, (int)T, (int)d_in);
       break;
     default:
-      hipLaunchKernelGGL((k_decode_fused<SBL_I32, W>), grid, block, lds, s, x, db, (int)T, (int)d_in);
+      hipLaunchKernelGGL((k_decode_fused<SBL_I32, W, NCH>), grid, block, lds, s, x, db, (int)T, (int)d_in);
       break;
   }
   return hipGetLastError();
+}
+
+template <int W>
+hipError_t launch_decode_fused_w(const DecBatch& db, const uint16_t* x, int64_t T, int64_t d_in, int y_dtype,
+                                 hipStream_t s) {
+  static_assert(kFuseChunks == 16, "chunk variants");
+  const int64_t per_lane = (d_in / 8 + 63) / 64;  // 16-byte chunks per lane
+  if (per_lane <= 4) return launch_decode_fused_wc<W, 4>(db, x, T, d_in, y_dtype, s);
+  if (per_lane <= 8) return launch_decode_fused_wc<W, 8>(db, x, T, d_in, y_dtype, s);
+  return launch_decode_fused_wc<W, 16>(db, x, T, d_in, y_dtype, s);
 }
 
 hipError_t launch_decode_fused_multi(int count, const DecodeItem* items, const uint16_t* x, int64_t T, int64_t d_in,
