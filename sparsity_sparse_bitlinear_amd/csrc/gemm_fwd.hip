@@ -634,7 +634,8 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
 // Decode forward (T <= 64, d_in % 64 == 0): the code plane is streamed once and
 // every weight meets at most 64 tokens, so the kernel is bound by the code
 // bytes and, at these sizes, by the latency of one round of loads, not by the
-// matrix cores.  A block owns 16 output rows; its W waves split the K range
+// matrix cores.  A block owns 16 output rows (8 on grids too small to fill
+// the CUs, see DecBatch); its W waves split the K range
 // (all of a wave's loads are issued before its first product) and each runs
 // v_mfma_i32_16x16x64_i8 with the expanded code words as the first operand
 // (lane l: row l % 16, k 16 (l / 16) + 0..15, one 32-bit word of 16 codes) and
@@ -661,11 +662,12 @@ inline int decode_waves(int64_t nblocks, int min_w) {
 }
 
 // Sum of the W waves' accumulators (wave 0 keeps the total) and the scaled
-// store of rows o0 .. o0 + 15; sc[tt] is the scale of this lane's token
-// 16 tt + l % 16.
+// store of rows o0 .. o_end - 1 (at most 16); sc[tt] is the scale of this
+// lane's token 16 tt + l % 16.
 template <int NTT, int OUT, int W>
 __device__ __forceinline__ void decode_store(v4i (&acc)[NTT], int (*red)[NTT][4][64], int wave, int lane, int o0,
-                                             int T, int d_out, const float (&sc)[NTT], void* __restrict__ y) {
+                                             int T, int d_out, int o_end, const float (&sc)[NTT],
+                                             void* __restrict__ y) {
   if (wave > 0) {
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt)
@@ -687,11 +689,11 @@ __device__ __forceinline__ void decode_store(v4i (&acc)[NTT], int (*red)[NTT][4]
   for (int tt = 0; tt < NTT; ++tt) {
     const int t = 16 * tt + r16;
     const int o = o0 + 4 * q;
-    if (t >= T || o >= d_out) continue;
+    if (t >= T || o >= o_end) continue;
     const float s = sc[tt];
     const int64_t off = (int64_t)t * d_out + o;
     const int a0 = acc[tt][0], a1 = acc[tt][1], a2 = acc[tt][2], a3 = acc[tt][3];
-    if (vec_out && o + 4 <= d_out) {
+    if (vec_out && o + 4 <= o_end) {
       if constexpr (OUT == SBL_I32) {
         *(int4*)((int*)y + off) = make_int4(a0, a1, a2, a3);
       } else if constexpr (OUT == SBL_F32) {
@@ -704,7 +706,7 @@ __device__ __forceinline__ void decode_store(v4i (&acc)[NTT], int (*red)[NTT][4]
       const int av[4] = {a0, a1, a2, a3};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (o + u >= d_out) break;
+        if (o + u >= o_end) break;
         if constexpr (OUT == SBL_I32) ((int*)y)[off + u] = av[u];
         else if constexpr (OUT == SBL_F32) ((float*)y)[off + u] = (float)av[u] * s;
         else ((__bf16*)y)[off + u] = (__bf16)((float)av[u] * s);
@@ -715,11 +717,15 @@ __device__ __forceinline__ void decode_store(v4i (&acc)[NTT], int (*red)[NTT][4]
 
 // Up to kDecodeMultiMax matrices that share one activation input (a layer's
 // q, k and v, or gate and up) in one launch: the blocks are dealt to the
-// matrices by the prefix sums of their 16-row blocks, so each block still
-// owns 16 output rows of one matrix and computes exactly what a launch for
-// that matrix alone computes.
+// matrices by the prefix sums of their row blocks, so each block owns rows of
+// one matrix and computes exactly what a launch for that matrix alone
+// computes.  A block owns 16 rows (one matrix-instruction tile), or 8 when
+// the 16-row grid would leave half of the CUs idle (its other 8 tile rows
+// read zero codes and are not stored): 128-block grids such as o and down of
+// a 3B layer at one token gain (down 10.5 -> 8.5 us), 160-block ones lose.
 struct DecBatch {
   int count;
+  int rows;                        // output rows per block: 16, or 8 on grids too small to fill the CUs
   int begin[kDecodeMultiMax + 1];  // row blocks of matrix i: [begin[i], begin[i + 1])
   int d_out[kDecodeMultiMax];
   const uint16_t* codes[kDecodeMultiMax];
@@ -745,12 +751,12 @@ __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict_
   const float* __restrict__ gamma_p = db.gamma[item];
   const int d_out = db.d_out[item];
   void* __restrict__ y = db.y[item];
-  const int o0 = (blockIdx.x - db.begin[item]) * kDecRows;
+  const int o0 = (blockIdx.x - db.begin[item]) * db.rows;
   const int G = d_in >> 3;
   const int nks = d_in >> 6;
   const int per = (nks + W - 1) / W;
   const int s_begin = wave * per, s_end = min(nks, s_begin + per);
-  const int rows = min(kDecRows, d_out - o0);
+  const int rows = min(db.rows, d_out - o0);
   const auto br = make_rsrc(codes + (int64_t)o0 * G, clamp_bytes((int64_t)rows * G * 2));
   const auto xr = make_rsrc(xq, clamp_bytes((int64_t)T * d_in));
   const int q = lane >> 4, r16 = lane & 15;
@@ -792,7 +798,7 @@ __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict_
     const int t = 16 * tt + r16;
     sc[tt] = t < T ? g127 * absmax[t] : 0.0f;
   }
-  decode_store<NTT, OUT, W>(acc, red, wave, lane, o0, T, d_out, sc, y);
+  decode_store<NTT, OUT, W>(acc, red, wave, lane, o0, T, d_out, o0 + rows, sc, y);
 }
 
 // Decode with the activation quantization fused in.  Each block quantizes the
@@ -833,13 +839,13 @@ __global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restr
   const float* __restrict__ gamma_p = db.gamma[item];
   const int d_out = db.d_out[item];
   void* __restrict__ y = db.y[item];
-  const int o0 = (blockIdx.x - db.begin[item]) * kDecRows;
+  const int o0 = (blockIdx.x - db.begin[item]) * db.rows;
   const int G = d_in >> 3;
   const int nks = d_in >> 6;
   const int ld = d_in + 16;  // tile row stride: rows 16 bytes apart shift the banks
   const int per = (nks + W - 1) / W;
   const int s_begin = wave * per, s_end = min(nks, s_begin + per);
-  const int rows = min(kDecRows, d_out - o0);
+  const int rows = min(db.rows, d_out - o0);
   const auto br = make_rsrc(codes + (int64_t)o0 * G, clamp_bytes((int64_t)rows * G * 2));
   const int q = lane >> 4, r16 = lane & 15;
   const uint32_t b_off = (uint32_t)(r16 * G * 2 + 4 * q);
@@ -895,7 +901,7 @@ __global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restr
     }
   }
   const float sc[1] = {tok ? *gamma_p * (1.0f / 127.0f) * amax[r16] : 0.0f};
-  decode_store<1, OUT, W>(acc, red, wave, lane, o0, T, d_out, sc, y);
+  decode_store<1, OUT, W>(acc, red, wave, lane, o0, T, d_out, o0 + rows, sc, y);
 }
 
 template <int NTT, int W>
@@ -927,10 +933,15 @@ hipError_t launch_decode(const DecBatch& db, const int8_t* xq, const float* absm
 }
 
 // Descriptor of count matrices; false if the row blocks overflow an int.
-bool make_dec_batch(int count, const DecodeItem* items, DecBatch& db) {
+// half: 8-row blocks allowed (one token tile; with four tiles of 64 tokens
+// the doubled re-reads of x_q cost more than the extra blocks give).
+bool make_dec_batch(int count, const DecodeItem* items, bool half, DecBatch& db) {
   if (count < 1 || count > kDecodeMultiMax) return false;
   db = DecBatch{};
   db.count = count;
+  int64_t full = 0;
+  for (int i = 0; i < count; ++i) full += (items[i].d_out + kDecRows - 1) / kDecRows;
+  db.rows = half && 2 * full <= device_cus() ? kDecRows / 2 : kDecRows;
   int64_t nb = 0;
   for (int i = 0; i < count; ++i) {
     db.begin[i] = (int)nb;
@@ -938,7 +949,7 @@ bool make_dec_batch(int count, const DecodeItem* items, DecBatch& db) {
     db.codes[i] = items[i].codes;
     db.gamma[i] = items[i].gamma;
     db.y[i] = items[i].y;
-    nb += (items[i].d_out + kDecRows - 1) / kDecRows;
+    nb += (items[i].d_out + db.rows - 1) / db.rows;
     if (nb > 0x7FFFFFFF) return false;
   }
   db.begin[count] = (int)nb;
@@ -1067,7 +1078,7 @@ hipError_t launch_decode_fused_multi(int count, const DecodeItem* items, const u
                                      int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   DecBatch db;
-  if (!decode_fused_supported(T, d_in) || !make_dec_batch(count, items, db)) return hipErrorInvalidValue;
+  if (!decode_fused_supported(T, d_in) || !make_dec_batch(count, items, true, db)) return hipErrorInvalidValue;
   switch (decode_waves(db.begin[count], decode_fused_min_waves(T, d_in))) {
     case 16: return launch_decode_fused_w<16>(db, x, T, d_in, y_dtype, s);
     case 8: return launch_decode_fused_w<8>(db, x, T, d_in, y_dtype, s);
@@ -1085,7 +1096,7 @@ hipError_t launch_forward_decode_multi(int count, const DecodeItem* items, const
                                        int64_t T, int64_t d_in, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   DecBatch db;
-  if (T > 64 || d_in % 64 != 0 || !make_dec_batch(count, items, db)) return hipErrorInvalidValue;
+  if (T > 64 || d_in % 64 != 0 || !make_dec_batch(count, items, T <= 16, db)) return hipErrorInvalidValue;
   if (T <= 16) return launch_decode<1>(db, xq, absmax, T, d_in, y_dtype, s);
   return launch_decode<4>(db, xq, absmax, T, d_in, y_dtype, s);
 }
