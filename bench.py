@@ -54,6 +54,8 @@ def parse():
                     help="pack all linears in one batched call (default) or one call per linear")
     ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-fuse-max", type=int, default=None,
+                    help="decode: largest T * d_in * (16-row blocks of a group) that takes the fused launch")
     ap.add_argument("--breakdown", action="store_true", help="print the per-linear breakdown to stderr")
     ap.add_argument("--variants", action="store_true",
                     help="N:M patterns and ablations: quant/mask/pack per pattern and mask-without-grad on the "
@@ -403,7 +405,8 @@ def run_variants(args, wl):
     print(json.dumps(line), flush=True)
 
 
-DECODE_FUSE_MAX = 4_000_000  # element-quantizations per launch up to which sbl_decode beats two calls
+DECODE_FUSE_MAX = 32_000_000  # T * d_in * (16-row blocks) per launch up to which the fused decode beats
+                              # two calls (2048-wide rows: gate+up of a 3B layer at 8 tokens, 22.5e6, wins)
 
 
 # Linears of a decoder layer that read the same activations: q, k, v the normed hidden
@@ -444,6 +447,7 @@ def run_decode(args, wl, copies: int = 16):
 
     Ws = [up(weight(wl.cfg, mi, L.d_out, L.d_in)) for mi, L in enumerate(wl.linears)]
     groups = decode_groups(wl)
+    fuse_max = DECODE_FUSE_MAX if args.decode_fuse_max is None else args.decode_fuse_max
     results = []
     for n_keep in wl.n_keep:
         packed = [sbl.quant_mask_pack(W, n_keep, want_mask=False) for W in Ws]
@@ -460,7 +464,7 @@ def run_decode(args, wl, copies: int = 16):
                 # re-quantization of the T rows stays small (T * d_in * blocks of 16 rows),
                 # else act quant + one sbl_forward_decode_multi
                 blocks = sum(-(-wl.linears[i].d_out // 16) for i in g)
-                gbufs.append(dict(x=x, fused=sbl.decode_supported(T, L0.d_in) and T * L0.d_in * blocks <= DECODE_FUSE_MAX,
+                gbufs.append(dict(x=x, fused=sbl.decode_supported(T, L0.d_in) and T * L0.d_in * blocks <= fuse_max,
                                   x_q=torch.empty((T, L0.d_in), dtype=torch.int8, device=dev),
                                   a=torch.empty((T,), dtype=torch.float32, device=dev),
                                   ys=[torch.empty((T, wl.linears[i].d_out), dtype=torch.bfloat16, device=dev)

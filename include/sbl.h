@@ -296,11 +296,11 @@ SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t*
  * d_in <= 8192 and T * (d_in + 16) <= 49152 (the int8 tile each block keeps
  * in LDS); other shapes return SBL_ERR_UNSUPPORTED and enqueue nothing (use
  * sbl_act_quant + sbl_forward).  T = 0 is a no-op.
- * Cost: every block of 16 output rows quantizes all T rows itself (there is
- * no cross-block step), so the saving of one launch (a few us) is worth it
- * while T * d_in * ceil(d_out / 16) stays below a few million; past that the
- * two-call path is faster (measured: 11008 x 2048 at T = 8, 12.8 against
- * 10.7 us).
+ * Cost: every block of output rows quantizes all T rows itself (there is no
+ * cross-block step), so the saving of one launch (a few us) is worth it while
+ * T * d_in * ceil(d_out / 16) stays moderate: with 2048-wide rows the fused
+ * launch still won at about 2e7 (gate and up of a 3B layer, 2 x 11008 rows,
+ * at T = 8, through sbl_decode_multi: 40.7 against 41.4 us per layer).
  */
 SBL_API int sbl_decode(const uint16_t* codes, const float* gamma, const uint16_t* x_bf16, int64_t T, int64_t d_in,
                        int64_t d_out, void* y, int y_dtype, void* hip_stream);
