@@ -662,37 +662,40 @@ inline int decode_waves(int64_t nblocks, int min_w) {
 }
 
 // Sum of the W waves' accumulators (wave 0 keeps the total) and the scaled
-// store of rows o0 .. o_end - 1 (at most 16); sc[tt] is the scale of this
-// lane's token 16 tt + l % 16.
-template <int NTT, int OUT, int W>
-__device__ __forceinline__ void decode_store(v4i (&acc)[NTT], int (*red)[NTT][4][64], int wave, int lane, int o0,
-                                             int T, int d_out, int o_end, const float (&sc)[NTT],
+// store of rows o0 .. o_end - 1 (RT tiles of 16 rows at most); accumulator
+// i = NTT rt + tt holds row tile rt and token tile tt, and sc[tt] is the
+// scale of this lane's token 16 tt + l % 16.
+template <int NTT, int OUT, int W, int RT = 1>
+__device__ __forceinline__ void decode_store(v4i (&acc)[RT * NTT], int (*red)[RT * NTT][4][64], int wave, int lane,
+                                             int o0, int T, int d_out, int o_end, const float (&sc)[NTT],
                                              void* __restrict__ y) {
+  constexpr int NA = RT * NTT;
   if (wave > 0) {
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave - 1][tt][r][lane] = acc[tt][r];
+      for (int r = 0; r < 4; ++r) red[wave - 1][i][r][lane] = acc[i][r];
   }
   __syncthreads();
   if (wave != 0) return;
 #pragma unroll 1
   for (int w = 0; w < W - 1; ++w)
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[tt][r] += red[w][tt][r][lane];
+      for (int r = 0; r < 4; ++r) acc[i][r] += red[w][i][r][lane];
 
   const int q = lane >> 4, r16 = lane & 15;
   const bool vec_out = (d_out & 3) == 0;
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) {
+  for (int i = 0; i < NA; ++i) {
+    const int tt = i % NTT;
     const int t = 16 * tt + r16;
-    const int o = o0 + 4 * q;
+    const int o = o0 + 16 * (i / NTT) + 4 * q;
     if (t >= T || o >= o_end) continue;
     const float s = sc[tt];
     const int64_t off = (int64_t)t * d_out + o;
-    const int a0 = acc[tt][0], a1 = acc[tt][1], a2 = acc[tt][2], a3 = acc[tt][3];
+    const int a0 = acc[i][0], a1 = acc[i][1], a2 = acc[i][2], a3 = acc[i][3];
     if (vec_out && o + 4 <= o_end) {
       if constexpr (OUT == SBL_I32) {
         *(int4*)((int*)y + off) = make_int4(a0, a1, a2, a3);
@@ -725,7 +728,7 @@ __device__ __forceinline__ void decode_store(v4i (&acc)[NTT], int (*red)[NTT][4]
 // a 3B layer at one token gain (down 10.5 -> 8.5 us), 160-block ones lose.
 struct DecBatch {
   int count;
-  int rows;                        // output rows per block: 16, or 8 on grids too small to fill the CUs
+  int rows;                        // output rows per block: 8, 16 or 32 (16 per row tile of k_fwd_decode<.., RT>)
   int begin[kDecodeMultiMax + 1];  // row blocks of matrix i: [begin[i], begin[i + 1])
   int d_out[kDecodeMultiMax];
   const uint16_t* codes[kDecodeMultiMax];
@@ -739,10 +742,12 @@ __device__ __forceinline__ int dec_item(const DecBatch& db, int b) {
   return i;
 }
 
-template <int NTT, int OUT, int W>
+// RT row tiles of 16 per block (RT = 2 on large grids with 4 token tiles:
+// every block reads all of x_q, so 32-row blocks halve those re-reads).
+template <int NTT, int OUT, int W, int RT>
 __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict__ xq, const DecBatch db,
                                                        const float* __restrict__ absmax, int T, int d_in) {
-  __shared__ int red[W - 1][NTT][4][64];
+  __shared__ int red[W - 1][RT * NTT][4][64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -765,17 +770,19 @@ __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict_
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) x_off[tt] = (uint32_t)((16 * tt + r16) * d_in + 16 * q);
 
-  v4i acc[NTT];
+  v4i acc[RT * NTT];
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) acc[tt] = (v4i){0, 0, 0, 0};
+  for (int i = 0; i < RT * NTT; ++i) acc[i] = (v4i){0, 0, 0, 0};
   constexpr int kS = dec_steps<NTT>();
   for (int s0 = s_begin; s0 < s_end; s0 += kS) {
-    uint32_t wb[kS];
+    uint32_t wb[kS][RT];
     v4i fx[kS][NTT];
 #pragma unroll
     for (int u = 0; u < kS; ++u) {
       const bool ok = s0 + u < s_end;
-      wb[u] = bload4(br, ok ? b_off + (uint32_t)(s0 + u) * 16 : kOOB);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        wb[u][rt] = bload4(br, ok ? b_off + (uint32_t)(rt * 32 * G + (s0 + u) * 16) : kOOB);
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
         fx[u][tt] = __builtin_bit_cast(v4i, bload16(xr, ok ? x_off[tt] + (uint32_t)(s0 + u) * 64 : kOOB));
@@ -785,11 +792,14 @@ __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict_
     // range); no early exit, which would let the compiler sink each load to
     // its use and serialize the round trips.
 #pragma unroll
-    for (int u = 0; u < kS; ++u) {
-      const v4i fb = __builtin_bit_cast(v4i, expand16(wb[u]));
+    for (int u = 0; u < kS; ++u)
 #pragma unroll
-      for (int tt = 0; tt < NTT; ++tt) acc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb, fx[u][tt], acc[tt], 0, 0, 0);
-    }
+      for (int rt = 0; rt < RT; ++rt) {
+        const v4i fb = __builtin_bit_cast(v4i, expand16(wb[u][rt]));
+#pragma unroll
+        for (int tt = 0; tt < NTT; ++tt)
+          acc[NTT * rt + tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb, fx[u][tt], acc[NTT * rt + tt], 0, 0, 0);
+      }
   }
   const float g127 = *gamma_p * (1.0f / 127.0f);
   float sc[NTT];
@@ -798,7 +808,7 @@ __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict_
     const int t = 16 * tt + r16;
     sc[tt] = t < T ? g127 * absmax[t] : 0.0f;
   }
-  decode_store<NTT, OUT, W>(acc, red, wave, lane, o0, T, d_out, o0 + rows, sc, y);
+  decode_store<NTT, OUT, W, RT>(acc, red, wave, lane, o0, T, d_out, o0 + rows, sc, y);
 }
 
 // Decode with the activation quantization fused in.  Each block quantizes the
@@ -904,19 +914,19 @@ __global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restr
   decode_store<1, OUT, W>(acc, red, wave, lane, o0, T, d_out, o0 + rows, sc, y);
 }
 
-template <int NTT, int W>
+template <int NTT, int W, int RT>
 hipError_t launch_decode_w(const DecBatch& db, const int8_t* xq, const float* absmax, int64_t T, int64_t d_in,
                            int y_dtype, hipStream_t s) {
   const dim3 grid((unsigned)db.begin[db.count]), block(64 * W);
   switch (y_dtype) {
     case SBL_F32:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_F32, W>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_F32, W, RT>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
       break;
     case SBL_BF16:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_BF16, W>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_BF16, W, RT>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
       break;
     default:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_I32, W>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_I32, W, RT>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
       break;
   }
   return hipGetLastError();
@@ -925,23 +935,32 @@ hipError_t launch_decode_w(const DecBatch& db, const int8_t* xq, const float* ab
 template <int NTT>
 hipError_t launch_decode(const DecBatch& db, const int8_t* xq, const float* absmax, int64_t T, int64_t d_in,
                          int y_dtype, hipStream_t s) {
-  switch (decode_waves(db.begin[db.count], 4)) {
-    case 16: return launch_decode_w<NTT, 16>(db, xq, absmax, T, d_in, y_dtype, s);
-    case 8: return launch_decode_w<NTT, 8>(db, xq, absmax, T, d_in, y_dtype, s);
-    default: return launch_decode_w<NTT, 4>(db, xq, absmax, T, d_in, y_dtype, s);
+  const int w = decode_waves(db.begin[db.count], 4);
+  if constexpr (NTT == 4) {
+    if (db.rows == 2 * kDecRows) {  // two row tiles: at most 8 waves (LDS of the partial sums)
+      if (w >= 8) return launch_decode_w<NTT, 8, 2>(db, xq, absmax, T, d_in, y_dtype, s);
+      return launch_decode_w<NTT, 4, 2>(db, xq, absmax, T, d_in, y_dtype, s);
+    }
+  }
+  switch (w) {
+    case 16: return launch_decode_w<NTT, 16, 1>(db, xq, absmax, T, d_in, y_dtype, s);
+    case 8: return launch_decode_w<NTT, 8, 1>(db, xq, absmax, T, d_in, y_dtype, s);
+    default: return launch_decode_w<NTT, 4, 1>(db, xq, absmax, T, d_in, y_dtype, s);
   }
 }
 
 // Descriptor of count matrices; false if the row blocks overflow an int.
-// half: 8-row blocks allowed (one token tile; with four tiles of 64 tokens
-// the doubled re-reads of x_q cost more than the extra blocks give).
-bool make_dec_batch(int count, const DecodeItem* items, bool half, DecBatch& db) {
+// half: 8-row blocks allowed on small grids (one token tile; with four tiles
+// of up to 64 tokens the doubled re-reads of x_q cost more than the extra
+// blocks give); twin: 32-row blocks on grids of at least 4 blocks of 16 rows
+// per CU (four token tiles: halves the re-reads of x_q).
+bool make_dec_batch(int count, const DecodeItem* items, bool half, bool twin, DecBatch& db) {
   if (count < 1 || count > kDecodeMultiMax) return false;
   db = DecBatch{};
   db.count = count;
   int64_t full = 0;
   for (int i = 0; i < count; ++i) full += (items[i].d_out + kDecRows - 1) / kDecRows;
-  db.rows = half && 2 * full <= device_cus() ? kDecRows / 2 : kDecRows;
+  db.rows = half && 2 * full <= device_cus() ? kDecRows / 2 : twin && full >= 4 * device_cus() ? 2 * kDecRows : kDecRows;
   int64_t nb = 0;
   for (int i = 0; i < count; ++i) {
     db.begin[i] = (int)nb;
@@ -1078,7 +1097,7 @@ hipError_t launch_decode_fused_multi(int count, const DecodeItem* items, const u
                                      int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   DecBatch db;
-  if (!decode_fused_supported(T, d_in) || !make_dec_batch(count, items, true, db)) return hipErrorInvalidValue;
+  if (!decode_fused_supported(T, d_in) || !make_dec_batch(count, items, true, false, db)) return hipErrorInvalidValue;
   switch (decode_waves(db.begin[count], decode_fused_min_waves(T, d_in))) {
     case 16: return launch_decode_fused_w<16>(db, x, T, d_in, y_dtype, s);
     case 8: return launch_decode_fused_w<8>(db, x, T, d_in, y_dtype, s);
@@ -1096,7 +1115,7 @@ hipError_t launch_forward_decode_multi(int count, const DecodeItem* items, const
                                        int64_t T, int64_t d_in, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   DecBatch db;
-  if (T > 64 || d_in % 64 != 0 || !make_dec_batch(count, items, T <= 16, db)) return hipErrorInvalidValue;
+  if (T > 64 || d_in % 64 != 0 || !make_dec_batch(count, items, T <= 16, T > 16, db)) return hipErrorInvalidValue;
   if (T <= 16) return launch_decode<1>(db, xq, absmax, T, d_in, y_dtype, s);
   return launch_decode<4>(db, xq, absmax, T, d_in, y_dtype, s);
 }
