@@ -1,5 +1,5 @@
-"""Pins for the oracle's optimizer step + repack (SURVEY NEXT-1 reading of
-[SUM] 方法步骤详情 step (8)): AdamW against torch.optim.AdamW in float64 (a library
+"""Pins for the oracle's optimizer step + repack (the reading of [SUM]
+方法步骤详情 step (8) with the optimizer's hyper-parameters): AdamW against torch.optim.AdamW in float64 (a library
 routine), its closed form at the first step, the exact float64 -> bf16 rounding
 against the float32 route and hand-derived double-rounding cases, and the flip
 count against a loop."""
