@@ -629,6 +629,48 @@ def test_decode_graph_replay_matches_eager():
         assert other.shape == (8, 512)
 
 
+@pytest.mark.parametrize("T", [8, 48])
+def test_decode_multi_graph_replay_matches_eager(T):
+    # the grouped launches captured in a HIP graph, as the decode measurement runs them
+    # (the fused form up to 16 tokens, act quant + the grouped product past that, on the
+    # 32-row blocks of a large grid): every replay equals the eager result
+    Ws, mats, xb = decode_group("gate_up", T)
+    x = to_dev_bf16(xb)
+    xq = torch.empty((T, 2048), dtype=torch.int8, device="cuda")
+    a = torch.empty((T,), dtype=torch.float32, device="cuda")
+    ys = [torch.empty((T, 11008), dtype=torch.bfloat16, device="cuda") for _ in mats]
+
+    def run():
+        if sbl.decode_supported(T, 2048):
+            sbl.decode_multi(mats, x, out_dtype=sbl.BF16, ys=ys)
+        else:
+            sbl.act_quant(x, x_q=xq, absmax=a)
+            sbl.forward_decode_multi(mats, xq, a, out_dtype=sbl.BF16, ys=ys)
+
+    run()
+    torch.cuda.synchronize()
+    want = [y.clone() for y in ys]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(3):
+        for y in ys:
+            y.zero_()
+        other = sbl.decode_multi(mats[:1], x[:1], out_dtype=sbl.F32)     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, w in zip(ys, want):
+            assert torch.equal(y.view(torch.int16), w.view(torch.int16)), f"replay {i}"
+        assert other[0].shape == (1, 11008)
+
+
 # training shapes as timed: the 3B-like layer at 32768 tokens and the 1.5B-like one at 8192
 FULL_SHAPES = [("gate", 32768, 11008, 2048), ("down", 32768, 2048, 11008), ("q", 32768, 2048, 2048),
                ("k", 32768, 256, 2048), ("gate_1.5b", 8192, 8960, 1536), ("down_1.5b", 8192, 1536, 8960),
