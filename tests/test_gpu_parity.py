@@ -563,7 +563,7 @@ def test_decode_fused_zero_and_tiny_rows():
     x = activation(64, 1, T, d_in)
     x[0] = 0
     x[1] = 0
-    x[1, 17] = f32_to_bf16_bits(np.float32(-3.0e-30))
+    x[1, 17] = f32_to_bf16_bits(np.array([-3.0e-30], np.float32))[0]
     x[2] = f32_to_bf16_bits(np.linspace(-3.0e38, 3.0e38, d_in).astype(np.float32))
     codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
     acc_ref, y_ref = ref_forward(W, x, 6)
