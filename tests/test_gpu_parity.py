@@ -629,6 +629,28 @@ def test_decode_graph_replay_matches_eager():
         assert other.shape == (8, 512)
 
 
+@pytest.mark.parametrize("T", [17, 64])
+def test_forward_decode_multi_ragged_twin_rows(T):
+    # a grid of 1026 blocks of 16 rows past 16 tokens takes 32-row blocks; d_out = 8200 leaves
+    # each matrix a last block of 8 rows (and one of 40 a short last tile): outputs equal one
+    # call per matrix (16-row blocks) and the oracle, bit for bit
+    shapes = [(8200, 128), (8200, 128), (40, 128)]
+    Ws = [weight(79, i, d_o, d_i) for i, (d_o, d_i) in enumerate(shapes)]
+    mats = []
+    for W in Ws:
+        codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6, want_mask=False)
+        mats.append((codes, gamma))
+    x = activation(79, 9, T, 128, dist="student_t4")
+    xq, a = sbl.act_quant(to_dev_bf16(x))
+    ys = sbl.forward_decode_multi(mats, xq, a, out_dtype=sbl.I32)
+    for W, (codes, gamma), y in zip(Ws, mats, ys):
+        want = sbl.forward(codes, gamma, xq, a, out_dtype=sbl.I32)
+        torch.cuda.synchronize()
+        assert torch.equal(y, want)
+        acc_ref, _ = ref_forward(W, x, 6)
+        np.testing.assert_array_equal(y.cpu().numpy(), acc_ref)
+
+
 @pytest.mark.parametrize("T", [8, 48])
 def test_decode_multi_graph_replay_matches_eager(T):
     # the grouped launches captured in a HIP graph, as the decode measurement runs them
