@@ -950,10 +950,11 @@ hipError_t launch_decode(const DecBatch& db, const int8_t* xq, const float* absm
 }
 
 // Descriptor of count matrices; false if the row blocks overflow an int.
-// half: 8-row blocks allowed on small grids (one token tile; with four tiles
-// of up to 64 tokens the doubled re-reads of x_q cost more than the extra
-// blocks give); twin: 32-row blocks on grids of at least 4 blocks of 16 rows
-// per CU (four token tiles: halves the re-reads of x_q).
+// half: 8-row blocks allowed on small grids (one token tile, or rows of 8192
+// and more: with four tiles of up to 64 tokens and shorter rows the doubled
+// re-reads of x_q cost more than the extra blocks give; down of a 3B layer at
+// 64 tokens gains); twin: 32-row blocks on grids of at least 4 blocks of 16
+// rows per CU (four token tiles: halves the re-reads of x_q).
 bool make_dec_batch(int count, const DecodeItem* items, bool half, bool twin, DecBatch& db) {
   if (count < 1 || count > kDecodeMultiMax) return false;
   db = DecBatch{};
@@ -1115,7 +1116,7 @@ hipError_t launch_forward_decode_multi(int count, const DecodeItem* items, const
                                        int64_t T, int64_t d_in, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   DecBatch db;
-  if (T > 64 || d_in % 64 != 0 || !make_dec_batch(count, items, T <= 16, T > 16, db)) return hipErrorInvalidValue;
+  if (T > 64 || d_in % 64 != 0 || !make_dec_batch(count, items, T <= 16 || d_in >= 8192, T > 16, db)) return hipErrorInvalidValue;
   if (T <= 16) return launch_decode<1>(db, xq, absmax, T, d_in, y_dtype, s);
   return launch_decode<4>(db, xq, absmax, T, d_in, y_dtype, s);
 }
