@@ -455,48 +455,108 @@ def unpack_sparse24(plane: np.ndarray) -> np.ndarray:
 # Norm + activation quantization  [SUM] 方法步骤详情 step (3): x~ = Q_a(Norm(x))
 # ----------------------------------------------------------------------------
 
-RMS_THREADS = 256  # the reduction shape that fixes the float32 summation order
+BF16_SQUARE_QUANTUM_LOG2 = -266  # (2^-133)^2: every square of a bf16 is a multiple of it
+
+
+def square_sum_exact(x_bits: np.ndarray) -> list:
+    """Exact sum of x^2 over each row, as Python integers in units of 2^-266.
+
+    A bf16 magnitude is sig * 2^(s - 133) with s = max(e, 1) - 1 (see
+    ``abs_sum_exact``), so its square is sig^2 * 2^(2 s) units of 2^-266.
+    Squared significands are summed per exponent (exact: below 2^53) and then
+    combined as big integers.
+    """
+    b = np.asarray(x_bits, dtype=np.uint16)
+    assert b.ndim == 2
+    T, d = b.shape
+    m = b.astype(np.int64) & 0x7FFF
+    e = m >> 7
+    assert not np.any(e == 0xFF), "non-finite bf16 input"
+    frac = m & 0x7F
+    sig = np.where(e > 0, frac | 0x80, frac)
+    shift = np.maximum(e, 1) - 1
+    assert d * 255 * 255 < 2 ** 53
+    rows = np.repeat(np.arange(T, dtype=np.int64), d)
+    bins = np.bincount(rows * 254 + shift.ravel(), weights=(sig * sig).ravel().astype(np.float64),
+                       minlength=T * 254).reshape(T, 254)
+    out = []
+    for t in range(T):
+        total = 0
+        for s_, v in zip(np.flatnonzero(bins[t]), bins[t][bins[t] != 0]):
+            total += int(v) << (2 * int(s_))
+        out.append(total)
+    return out
+
+
+def mean_square_f32(x_bits: np.ndarray) -> np.ndarray:
+    """Per row, the correctly rounded binary32 value of the exact mean of x^2.
+
+    Rounding the exact mean once makes the value independent of any summation
+    order, as for gamma; it overflows to +inf only beyond the binary32 range.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, d = x_bits.shape
+    assert d > 0
+    sums = square_sum_exact(x_bits)
+    return np.array([round_rational_to_f32(S, d << -BF16_SQUARE_QUANTUM_LOG2) for S in sums],
+                    dtype=np.float32)
+
+
+def rsqrt_rn32(v) -> np.float32:
+    """The binary32 value nearest to 1 / sqrt(v), for a binary32 v > 0 (+inf gives 0).
+
+    Exact integer arithmetic: with 2^E <= 1/sqrt(v) < 2^(E+1), the result is
+    round(z) 2^(E - 23) for z = 2^(23 - E) / sqrt(v) in [2^23, 2^24), and
+    floor(z) = isqrt(floor(z^2)).  1/sqrt(v) is never a midpoint of the
+    binary32 grid (a midpoint's square is not the reciprocal of a dyadic
+    rational), so there is no tie; for binary32 v the result is always normal.
+    """
+    v = float(np.float32(v))
+    if math.isinf(v):
+        return np.float32(0.0)
+    assert v > 0.0
+    B, A = v.as_integer_ratio()          # v = B / A, so 1/v = A / B
+    E = (A.bit_length() - B.bit_length()) // 2 + 1
+    while (A << max(0, -2 * E)) < (B << max(0, 2 * E)):      # 1/v < 4^E
+        E -= 1
+    while (A << max(0, -2 * (E + 1))) >= (B << max(0, 2 * (E + 1))):  # 1/v >= 4^(E+1)
+        E += 1
+    k = 46 - 2 * E                        # z^2 = (A / B) 2^k
+    num, den = (A << k, B) if k >= 0 else (A, B << -k)
+    z = math.isqrt(num // den)
+    if 4 * num >= (2 * z + 1) ** 2 * den:
+        z += 1
+    return np.float32(math.ldexp(z, E - 23))
+
+
+def rmsnorm_rstd(x_bits: np.ndarray, eps: float) -> np.ndarray:
+    """r = RN32(1 / sqrt(RN32(ms + eps))) per row, ms = ``mean_square_f32``; eps a
+    binary32 value > 0 (the addition is one binary32 operation)."""
+    eps32 = np.float32(eps)
+    assert np.isfinite(eps32) and eps32 > 0
+    ms = mean_square_f32(x_bits)
+    return np.array([rsqrt_rn32(np.float32(m) + eps32) for m in ms], dtype=np.float32)
 
 
 def rmsnorm_bf16(x_bits: np.ndarray, g_bits, eps: float) -> np.ndarray:
-    """RMSNorm of each row in binary32, rounded to bf16: y = bf16((x * r) * g),
-    r = 1 / sqrt(fl(fl(ss / d) + eps)).
+    """RMSNorm of each row, rounded to bf16: y = bf16(RN32(RN32(x r) g)) with
+    r = ``rmsnorm_rstd`` (the correctly rounded reciprocal square root of the
+    binary32 sum of the exact mean square and eps).
 
     The pages name Norm(x) but not its kind; RMSNorm with a bf16 weight g (None:
-    ones) is the reading (the Qwen2.5 models they train use it), evaluated in
-    binary32 with the output in bf16, the activation dtype of the model.  Since
-    the result feeds an integer decision (x_q), the float32 summation order is
-    fixed and written out here: squares of bf16 values are exact in float32;
-    thread t of 256 adds the squares of 16-byte chunks t, t + 256, ... (8
-    elements each, in order) one at a time; the 64 partial sums of each wave are
-    combined pairwise across lane distances 32, 16, 8, 4, 2, 1 (the two lanes of
-    a pair add the same two values), and the four wave sums as
-    (w0 + w1) + (w2 + w3).
+    ones) is the reading (the Qwen2.5 models they train use it), in binary32
+    with the output in bf16, the activation dtype of the model.  Since the
+    result feeds an integer decision (x_q), every step is one correctly rounded
+    operation on exact inputs: the mean square of the row is rounded once from
+    its exact value, the same for any order of the sum.
     """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    T, d = x_bits.shape
     x = bf16_to_f64(x_bits).astype(np.float32)
-    T, d = x.shape
-    assert d % 8 == 0
-    f = np.float32
     gv = np.ones(d, np.float32) if g_bits is None else bf16_to_f64(np.asarray(g_bits)).astype(np.float32)
-    nch = d // 8
-    out = np.zeros((T, d), np.uint16)
-    for t in range(T):
-        sq = (x[t] * x[t]).reshape(nch, 8)  # exact products
-        part = np.zeros(RMS_THREADS, np.float32)
-        for c0 in range(0, nch, RMS_THREADS):
-            cs = sq[c0:c0 + RMS_THREADS]
-            n = cs.shape[0]
-            for e in range(8):
-                part[:n] = part[:n] + cs[:, e]
-        for off in (32, 16, 8, 4, 2, 1):
-            idx = np.arange(RMS_THREADS)
-            part = part + part[idx ^ off]
-        w = part[::64]
-        ss = (w[0] + w[1]) + (w[2] + w[3])
-        r = f(1.0) / np.sqrt(f(ss / f(d)) + f(eps))
-        y = (x[t] * r) * gv
-        out[t] = f64_to_bf16_bits(y.astype(np.float64))
-    return out
+    r = rmsnorm_rstd(x_bits, eps)
+    y = (x * r[:, None]) * gv[None, :]       # two binary32 products per element
+    return f64_to_bf16_bits(y.astype(np.float64))
 
 
 def rmsnorm_act_quant(x_bits: np.ndarray, g_bits, eps: float):

@@ -136,6 +136,21 @@ def _rmsnorm_sum_not_mean(x_bits, g_bits, eps):
         (1.0 if g_bits is None else sb.bf16_to_f64(np.asarray(g_bits))))
 
 
+def _mean_square_float32_sum(x_bits):
+    x = sb.bf16_to_f64(x_bits).astype(np.float32)
+    s = np.zeros(x.shape[0], np.float32)
+    for j in range(x.shape[1]):
+        s = s + x[:, j] * x[:, j]
+    return (s / np.float32(x.shape[1])).astype(np.float32)
+
+
+def _rsqrt_double_rounded(v):
+    v32 = np.float32(v)
+    if np.isinf(v32):
+        return np.float32(0.0)
+    return np.float32(np.float32(1.0) / np.sqrt(v32))
+
+
 _ORIG_SP = sb.pack_sparse24
 
 
@@ -201,6 +216,10 @@ MUTANTS = [
      [t_opt.test_bf16_rounding_no_double_rounding]),
     ("RMSNorm with the sum of squares instead of the mean", "rmsnorm_bf16", _rmsnorm_sum_not_mean,
      [lambda: t_norm.test_rmsnorm_within_bf16_rounding_of_float64(64)]),
+    ("RMSNorm mean square from a float32 running sum", "mean_square_f32", _mean_square_float32_sum,
+     [t_norm.test_mean_square_midpoint_rows]),
+    ("RMSNorm reciprocal square root rounded twice", "rsqrt_rn32", _rsqrt_double_rounded,
+     [t_norm.test_rsqrt_nearest_by_fractions]),
     ("kept-only plane with the two halves' codes swapped", "pack_sparse24", _sparse24_halves_swapped,
      [t_sp.test_worked_groups]),
 ]
