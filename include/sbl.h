@@ -240,22 +240,28 @@ SBL_API int sbl_act_quant(const uint16_t* x_bf16, int64_t T, int64_t d_in, int8_
 /* Q_a(Norm(x)) in one pass ([SUM] 方法步骤详情 step (3)): RMSNorm of each row,
  * rounded to bf16, then the activation quantization of sbl_act_quant on it.
  *
- *   r      = 1 / sqrt(sum_i x[t, i]^2 / d_in + eps),  y = bf16((x * r) * g)
+ *   ms     = RN32(sum_i x[t, i]^2 / d_in)      (the exact mean, rounded once)
+ *   r      = RN32(1 / sqrt(RN32(ms + eps)))   (correctly rounded)
+ *   y      = bf16(RN32(RN32(x * r) * g))
  *   absmax, x_q as sbl_act_quant(y).
  *
  * The pages name Norm(x) without its kind; RMSNorm with a bf16 weight g is
- * the reading.  y is evaluated in binary32 in a fixed order (squares of bf16
- * values are exact; per-thread sums over 16-byte chunks t, t + 256, ... of the
- * row, a pairwise lane combination, wave sums (w0 + w1) + (w2 + w3); correctly
- * rounded division and square root), so x_q is reproducible bit for bit.
+ * the reading.  Each step is one correctly rounded binary32 operation on an
+ * exact value (RN32: nearest, ties to even), so the result does not depend on
+ * any summation order and x_q is reproducible bit for bit.  A row whose mean
+ * square overflows binary32 gives r = 0 and y = 0.
  *
- * x_bf16 : [T, d_in] bf16 bits.   d_in % 8 == 0, d_in <= 16384.
+ * x_bf16 : [T, d_in] bf16 bits.   d_in % 8 == 0, d_in <= 16384 (else
+ *          SBL_ERR_UNSUPPORTED).
  * g_bf16 : [d_in] bf16 weight, or NULL for ones.
- * eps    : >= 0, finite.
- * x_q, absmax : as sbl_act_quant.  T = 0 is a no-op.
+ * eps    : > 0, finite (else SBL_ERR_INVALID_ARG).
+ * x_q, absmax : as sbl_act_quant.
+ * rstd   : [T] float32, r of each row (what the norm's backward needs), or
+ *          NULL.
+ * T = 0 is a no-op.  Outputs are defined while y stays finite.
  */
 SBL_API int sbl_rmsnorm_act_quant(const uint16_t* x_bf16, const uint16_t* g_bf16, float eps, int64_t T, int64_t d_in,
-                                  int8_t* x_q, float* absmax, void* hip_stream);
+                                  int8_t* x_q, float* absmax, float* rstd, void* hip_stream);
 
 /* ------------------------------------------------------------------------ */
 /* Forward                                                                    */

@@ -53,7 +53,8 @@ _SIGNATURES = {
                                   _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "sbl_act_quant": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "sbl_forward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
-    "sbl_rmsnorm_act_quant": (_c_int, [_c_ptr, _c_ptr, ctypes.c_float, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "sbl_rmsnorm_act_quant": (_c_int, [_c_ptr, _c_ptr, ctypes.c_float, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr,
+                                       _c_ptr]),
     "sbl_pack_sparse24": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
     "sbl_forward_sparse24": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
@@ -318,23 +319,33 @@ def act_quant(x: torch.Tensor, *, x_q: Optional[torch.Tensor] = None, absmax: Op
 
 
 def rmsnorm_act_quant(x: torch.Tensor, g: Optional[torch.Tensor] = None, eps: float = 1e-6, *,
-                      x_q: Optional[torch.Tensor] = None, absmax: Optional[torch.Tensor] = None, stream=None):
-    """Q_a(RMSNorm(x)) in one pass: ``(x_q int8 [T, d_in], absmax float32 [T])``; ``g`` bf16 [d_in] or None."""
+                      x_q: Optional[torch.Tensor] = None, absmax: Optional[torch.Tensor] = None,
+                      rstd: Optional[torch.Tensor] = None, with_rstd: bool = False, stream=None):
+    """Q_a(RMSNorm(x)) in one pass: ``(x_q int8 [T, d_in], absmax float32 [T])``, plus ``rstd`` float32 [T]
+    (the per-row 1/sqrt(mean square + eps)) as a third item when ``with_rstd`` or ``rstd`` is given;
+    ``g`` bf16 [d_in] or None."""
     _as_bits16(x, "x")
     T, d_in = x.shape
     if g is not None:
         _as_bits16(g, "g")
         if tuple(g.shape) != (d_in,):
             raise ValueError(f"g has shape {tuple(g.shape)}, expected ({d_in},)")
+        if g.device != x.device:
+            raise ValueError("g must be on the device of x")
     if x_q is None:
         x_q = torch.empty((T, d_in), dtype=torch.int8, device=x.device)
     if absmax is None:
         absmax = torch.empty((T,), dtype=torch.float32, device=x.device)
+    want_rstd = with_rstd or rstd is not None
+    if want_rstd and rstd is None:
+        rstd = torch.empty((T,), dtype=torch.float32, device=x.device)
     _out(x_q, (T, d_in), (torch.int8,), x.device, "x_q")
     _out(absmax, (T,), (torch.float32,), x.device, "absmax")
+    if want_rstd:
+        _out(rstd, (T,), (torch.float32,), x.device, "rstd")
     _check(lib.sbl_rmsnorm_act_quant(_ptr(x), _ptr(g), float(eps), T, d_in, _ptr(x_q), _ptr(absmax),
-                                     _stream(stream)), "sbl_rmsnorm_act_quant")
-    return x_q, absmax
+                                     _ptr(rstd), _stream(stream)), "sbl_rmsnorm_act_quant")
+    return (x_q, absmax, rstd) if want_rstd else (x_q, absmax)
 
 
 _OUT_TORCH = {F32: torch.float32, BF16: torch.bfloat16, I32: torch.int32}

@@ -103,7 +103,7 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t T, int64_t d_in, int8_t* 
 // RMSNorm + act quant (act.hip), d_in <= 16384.
 bool rmsnorm_supported(int64_t d_in);
 hipError_t launch_rmsnorm_act_quant(const uint16_t* x, const uint16_t* g, float eps, int64_t T, int64_t d_in,
-                                    int8_t* xq, float* absmax, hipStream_t s);
+                                    int8_t* xq, float* absmax, float* rstd, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cus();

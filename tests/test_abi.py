@@ -140,13 +140,15 @@ def test_adamw_repack_validation():
 
 def test_rmsnorm_act_quant_validation():
     f = lib.sbl_rmsnorm_act_quant
-    assert f(NULL, NULL, 1e-6, 0, 256, NULL, NULL, NULL) == OK              # T = 0
-    assert f(P, NULL, 1e-6, 4, 100, P, P, NULL) == SHAPE
-    assert f(P, NULL, 1e-6, 4, 16392, P, P, NULL) == UNSUPPORTED
-    assert f(P, NULL, -1.0, 4, 256, P, P, NULL) == INVALID
-    assert f(P, NULL, float("inf"), 4, 256, P, P, NULL) == INVALID
-    assert f(NULL, NULL, 1e-6, 4, 256, P, P, NULL) == INVALID
-    assert f(P, P_MIS, 1e-6, 4, 256, P, P, NULL) == INVALID
+    assert f(NULL, NULL, 1e-6, 0, 256, NULL, NULL, NULL, NULL) == OK              # T = 0
+    assert f(P, NULL, 1e-6, 4, 100, P, P, NULL, NULL) == SHAPE
+    assert f(P, NULL, 1e-6, 4, 16392, P, P, NULL, NULL) == UNSUPPORTED
+    assert f(P, NULL, -1.0, 4, 256, P, P, NULL, NULL) == INVALID
+    assert f(P, NULL, 0.0, 4, 256, P, P, NULL, NULL) == INVALID                  # eps must be > 0
+    assert f(P, NULL, float("inf"), 4, 256, P, P, NULL, NULL) == INVALID
+    assert f(NULL, NULL, 1e-6, 4, 256, P, P, NULL, NULL) == INVALID
+    assert f(P, P_MIS, 1e-6, 4, 256, P, P, NULL, NULL) == INVALID
+    assert f(P, NULL, 1e-6, 4, 256, P, P, ctypes.c_void_p(0x10002), NULL) == INVALID  # rstd misaligned
 
 
 def test_act_quant_validation():

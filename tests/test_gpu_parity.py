@@ -327,19 +327,60 @@ def test_act_parity(shape, dist, outl):
     check_act(activation(21, shape[1], *shape, dist=dist, outlier_frac=outl))
 
 
-# Q_a(Norm(x)) fused: bit-exact x_q and absmax against the oracle's binary32
-# RMSNorm (fixed order) followed by the exact act quant.
+# Q_a(Norm(x)) fused: bit-exact x_q, absmax and rstd against the oracle's
+# RMSNorm (the exact mean square rounded once, a correctly rounded reciprocal
+# square root) followed by the exact act quant.
+def check_rmsnorm(x, g, eps):
+    xq, a, r = sbl.rmsnorm_act_quant(to_dev_bf16(x), to_dev_bf16(g) if g is not None else None, eps,
+                                     with_rstd=True)
+    torch.cuda.synchronize()
+    rq, ra = oracle.rmsnorm_act_quant(x, g, eps)
+    np.testing.assert_array_equal(r.cpu().numpy().view(np.uint32), oracle.rmsnorm_rstd(x, eps).view(np.uint32))
+    np.testing.assert_array_equal(a.cpu().numpy().view(np.uint32), ra.view(np.uint32))
+    np.testing.assert_array_equal(xq.cpu().numpy(), rq)
+
+
 @pytest.mark.parametrize("with_g", [False, True])
-@pytest.mark.parametrize("T,d_in", [(64, 2048), (33, 11008), (7, 64), (5, 4104), (2, 16384), (300, 896)])
+@pytest.mark.parametrize("T,d_in", [(64, 2048), (33, 11008), (7, 64), (5, 4104), (2, 16384), (300, 896),
+                                    (6, 4096), (3, 8)])
 def test_rmsnorm_act_quant_parity(T, d_in, with_g):
     x = activation(91, d_in + T, T, d_in, dist="student_t4", outlier_frac=0.001)
     g = f32_to_bf16_bits(np.random.default_rng(d_in).uniform(0.25, 2.0, d_in).astype(np.float32)) if with_g else None
     x[0] = 0  # a zero row
-    xq, a = sbl.rmsnorm_act_quant(to_dev_bf16(x), to_dev_bf16(g) if with_g else None, 1e-6)
-    torch.cuda.synchronize()
-    rq, ra = oracle.rmsnorm_act_quant(x, g, 1e-6)
-    np.testing.assert_array_equal(a.cpu().numpy().view(np.uint32), ra.view(np.uint32))
-    np.testing.assert_array_equal(xq.cpu().numpy(), rq)
+    check_rmsnorm(x, g, 1e-6)
+
+
+def _midpoint_rows(d, n, seed):
+    """Rows whose mean square is exactly the binary32 midpoint 3/4 + 2^-25 (the
+    8-element pattern 1 x 6, 2^-11, 0 tiled over the row, in a shuffled order,
+    scaled by 4^k), and the same rows with a 2^-100 in one zero slot (just above
+    the midpoint)."""
+    rng = np.random.default_rng(seed)
+    base = np.tile(np.array([1.0] * 6 + [2.0 ** -11, 0.0], np.float64), d // 8)
+    rows = []
+    for i in range(n):
+        r = base.copy()
+        if i % 2:
+            r[7] = 2.0 ** -100
+        r = r[rng.permutation(d)] * 4.0 ** int(rng.integers(-20, 20))
+        rows.append(r * rng.choice([-1.0, 1.0], size=d))
+    return f32_to_bf16_bits(np.array(rows, np.float32))
+
+
+@pytest.mark.parametrize("d_in", [8, 64, 2048, 4096, 8192, 11008])
+def test_rmsnorm_exact_path_rows(d_in):
+    """Rows at (and just past) a rounding tie of the mean square, which the
+    float64 estimate cannot decide; subnormal, mixed-range and overflowing rows."""
+    x = _midpoint_rows(d_in, 8, d_in)
+    g = np.random.default_rng(5)
+    extra = np.zeros((4, d_in), np.uint16)
+    extra[0] = 0x0001                                      # all smallest subnormals
+    extra[1, ::3] = 0x0075                                 # subnormals and zeros
+    extra[2] = f32_to_bf16_bits((np.exp2(g.uniform(-130, 60, d_in)) *
+                                 g.choice([-1, 1], d_in)).astype(np.float32))
+    extra[3] = 0x7F7F                                      # largest bf16: the mean square overflows
+    check_rmsnorm(np.concatenate([x, extra]), None, 2.0 ** -149)
+    check_rmsnorm(x, None, 1e-6)
 
 
 def test_act_edge_rows():
