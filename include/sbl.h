@@ -118,6 +118,25 @@ SBL_API int sbl_quant_mask_pack(const uint16_t* W_bf16, int64_t d_out, int64_t d
                                 uint16_t* codes, uint8_t* mask, float* gamma, void* workspace,
                                 size_t workspace_bytes, void* hip_stream);
 
+/* sbl_quant_mask_pack without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors as
+ * sbl_quant_mask_pack with n_keep 1..8 (N:8); it calls no allocator.
+ *
+ * Its scratch (the partial sums of the gamma reduction) is a static device
+ * array of sbl_quant_mask_pack_noalloc_scratch_bytes() bytes (2,129,920: the
+ * reduction never launches more than 1024 blocks, so every shape accepted by
+ * sbl_quant_mask_pack fits; a larger need returns SBL_ERR_WORKSPACE).  Each
+ * GPU holds one copy until the process ends, located on that GPU's first
+ * call.  All calls on one GPU share it and it keeps the last call's contents
+ * (no clearing is needed: each call writes what it reads), so calls that
+ * overlap on one GPU (concurrent streams or host threads) race: serialize
+ * them.
+ */
+SBL_API int sbl_quant_mask_pack_noalloc(const uint16_t* W_bf16, int64_t d_out, int64_t d_in, int n_keep,
+                                        uint16_t* codes, uint8_t* mask, float* gamma, void* hip_stream);
+SBL_API size_t sbl_quant_mask_pack_noalloc_scratch_bytes(void);
+
 /* sbl_quant_mask_pack_nm flags. */
 enum { SBL_MASK_FROM_QUANTIZED = 1 };
 

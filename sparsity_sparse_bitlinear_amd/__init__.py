@@ -45,6 +45,8 @@ _SIGNATURES = {
     "sbl_quant_mask_pack": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_size, _c_ptr]),
     "sbl_quant_mask_pack_nm": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_int, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
                                         _c_size, _c_ptr]),
+    "sbl_quant_mask_pack_noalloc": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_int, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
+    "sbl_quant_mask_pack_noalloc_scratch_bytes": (_c_size, []),
     "sbl_mask_grad": (_c_int, [_c_ptr, _c_ptr, _c_i64, _c_i64, _c_ptr]),
     "sbl_quant_mask_pack_batch_workspace_size": (_c_size, [_c_int, ctypes.c_void_p]),
     "sbl_quant_mask_pack_batch": (_c_int, [_c_int, ctypes.c_void_p, _c_int, _c_int, _c_int, _c_ptr, _c_size, _c_ptr]),

@@ -7,6 +7,7 @@
 #include <algorithm>
 
 #include <cmath>
+#include <mutex>
 
 #include "sbl_internal.h"
 
@@ -49,6 +50,39 @@ static int check_dims(int64_t d_out, int64_t d_in) {
 static int check_tokens(int64_t T) {
   SBL_REQUIRE(T >= 0 && T <= SBL_MAX_DIM, SBL_ERR_SHAPE, "T=%lld outside [0, %lld]", (long long)T,
               (long long)SBL_MAX_DIM);
+  return SBL_OK;
+}
+
+// Scratch of sbl_quant_mask_pack_noalloc: the per-block partial sums of the
+// gamma reduction for the largest grid that reduction launches
+// (kAbsumMaxBlocks blocks, whatever the matrix size).  Each GPU holds its own
+// copy until the process ends.  Every block writes its partial (and its
+// histogram when it has one) before the finalize reads it, so nothing needs
+// clearing between calls.
+constexpr size_t kPackScratchBytes =
+    (size_t)kAbsumMaxBlocks * (sizeof(AbsumPartial) + 256 * sizeof(unsigned long long));
+static __device__ __align__(256) unsigned char scratch[kPackScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the host-side name is only a handle for the runtime).
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int pack_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  SBL_REQUIRE(dev >= 0 && dev < kMaxDevices, SBL_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    SBL_REQUIRE(p != nullptr, SBL_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return SBL_OK;
 }
 
@@ -107,6 +141,30 @@ SBL_API int sbl_quant_mask_pack(const uint16_t* W_bf16, int64_t d_out, int64_t d
   return sbl_quant_mask_pack_nm(W_bf16, d_out, d_in, n_keep, 8, 0, codes, mask, gamma, workspace, workspace_bytes,
                                 hip_stream);
 }
+
+SBL_API int sbl_quant_mask_pack_noalloc(const uint16_t* W_bf16, int64_t d_out, int64_t d_in, int n_keep,
+                                        uint16_t* codes, uint8_t* mask, float* gamma, void* hip_stream) {
+  int rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(mask_pattern_supported(n_keep, 8), SBL_ERR_UNSUPPORTED, "n_keep=%d: supported are 1 <= N <= 8",
+              n_keep);
+  SBL_REQUIRE(W_bf16 && codes && gamma, SBL_ERR_INVALID_ARG, "W, codes and gamma must be non-NULL");
+  SBL_REQUIRE(aligned(W_bf16, 16) && aligned(codes, 16) && aligned(gamma, 4), SBL_ERR_INVALID_ARG,
+              "W and codes must be 16-byte aligned, gamma 4-byte aligned");
+  const size_t need = quant_workspace_bytes(d_out, d_in);
+  SBL_REQUIRE(need <= kPackScratchBytes, SBL_ERR_WORKSPACE,
+              "d_out=%lld, d_in=%lld needs %zu bytes of scratch; the static scratch holds %zu",
+              (long long)d_out, (long long)d_in, need, kPackScratchBytes);
+  void* ws = nullptr;
+  rc = pack_scratch(&ws);
+  if (rc != SBL_OK) return rc;
+  hipError_t e = launch_quant_mask_pack(W_bf16, d_out, d_in, n_keep, 8, false, codes, mask, gamma, ws,
+                                        (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_quant_mask_pack_noalloc launch");
+  return SBL_OK;
+}
+
+SBL_API size_t sbl_quant_mask_pack_noalloc_scratch_bytes(void) { return kPackScratchBytes; }
 
 static_assert(SBL_PACK_BATCH_MAX == kPackBatchMax, "batch limit");
 
