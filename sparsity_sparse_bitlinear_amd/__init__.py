@@ -145,6 +145,47 @@ def _dev(t: torch.Tensor, name: str) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def _typed(t: torch.Tensor, name: str, dtypes, ndim: int) -> None:
+    """A contiguous GPU tensor of one of ``dtypes`` with ``ndim`` dimensions."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    _dev(t, name)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {[str(d) for d in dtypes]}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+
+
+def _gamma_ok(gamma: torch.Tensor, name: str = "gamma") -> None:
+    _typed(gamma, name, (torch.float32,), 1)
+    if gamma.numel() < 1:
+        raise ValueError(f"{name} must hold one float32")
+
+
+def _act_operands(x_q: torch.Tensor, absmax: torch.Tensor):
+    """x_q int8 [T, d_in] and absmax float32 [T] on one device; returns (T, d_in)."""
+    _typed(x_q, "x_q", (torch.int8,), 2)
+    _typed(absmax, "absmax", (torch.float32,), 1)
+    T, d_in = x_q.shape
+    if absmax.numel() != T:
+        raise ValueError(f"absmax has {absmax.numel()} entries, expected T = {T}")
+    if absmax.device != x_q.device:
+        raise ValueError("x_q and absmax must be on one device")
+    return T, d_in
+
+
+def _code_operands(codes: torch.Tensor, gamma: torch.Tensor, d_in: int, dev, name: str = "codes"):
+    """codes int16 [d_out, d_in/8] and gamma float32 [>= 1] on ``dev``; returns d_out."""
+    _typed(codes, name, (torch.int16, torch.uint16), 2)
+    _gamma_ok(gamma)
+    d_out, G = codes.shape
+    if G * 8 != d_in:
+        raise ValueError(f"{name} [{d_out}, {G}] do not match d_in = {d_in}")
+    if codes.device != dev or gamma.device != dev:
+        raise ValueError(f"{name} and gamma must be on the device of the activations")
+    return d_out
+
+
 def _out(t: torch.Tensor, shape, dtypes, device, name: str) -> torch.Tensor:
     """Check a caller-provided output buffer: the kernels write exactly ``shape`` elements of one of ``dtypes``."""
     _dev(t, name)
@@ -371,12 +412,14 @@ def pack_sparse24(codes: torch.Tensor, *, plane: Optional[torch.Tensor] = None, 
 def forward_sparse24(plane: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax: torch.Tensor, *,
                      out_dtype: int = F32, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """``forward`` on the kept-only 2:4 plane (sparse matrix instruction); same result as ``forward``."""
-    for t, n in ((plane, "plane"), (gamma, "gamma"), (x_q, "x_q"), (absmax, "absmax")):
-        _dev(t, n)
-    d_out, steps, _ = plane.shape
-    T, d_in = x_q.shape
-    if steps * 64 != d_in:
+    T, d_in = _act_operands(x_q, absmax)
+    _typed(plane, "plane", (torch.uint8,), 3)
+    _gamma_ok(gamma)
+    d_out, steps, sixteen = plane.shape
+    if steps * 64 != d_in or sixteen != 16:
         raise ValueError(f"plane {tuple(plane.shape)} does not match x_q [{T}, {d_in}]")
+    if plane.device != x_q.device or gamma.device != x_q.device:
+        raise ValueError("plane and gamma must be on the device of x_q")
     if out_dtype not in _OUT_TORCH:
         raise ValueError(f"unknown out_dtype {out_dtype}")
     if y is None:
@@ -390,12 +433,8 @@ def forward_sparse24(plane: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor
 def forward(codes: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax: torch.Tensor, *,
             out_dtype: int = F32, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """y[t, o] = (sum_i x_q[t, i] W_eff[o, i]) * gamma * absmax[t] / 127  (or the raw int32 sums)."""
-    for t, n in ((codes, "codes"), (gamma, "gamma"), (x_q, "x_q"), (absmax, "absmax")):
-        _dev(t, n)
-    d_out, G = codes.shape
-    T, d_in = x_q.shape
-    if G * 8 != d_in:
-        raise ValueError(f"codes [{d_out}, {G}] do not match x_q [{T}, {d_in}]")
+    T, d_in = _act_operands(x_q, absmax)
+    d_out = _code_operands(codes, gamma, d_in, x_q.device)
     if out_dtype not in _OUT_TORCH:
         raise ValueError(f"unknown out_dtype {out_dtype}")
     if y is None:
@@ -414,14 +453,9 @@ def decode_supported(T: int, d_in: int) -> bool:
 def decode(codes: torch.Tensor, gamma: torch.Tensor, x: torch.Tensor, *, out_dtype: int = F32,
            y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """act_quant + forward in one launch for decode-sized T (see ``decode_supported``): same bits as the two calls."""
-    for t, n in ((codes, "codes"), (gamma, "gamma"), (x, "x")):
-        _dev(t, n)
-    if x.dtype != torch.bfloat16 or x.dim() != 2:
-        raise ValueError("x must be a 2-D bfloat16 tensor")
-    d_out, G = codes.shape
+    _typed(x, "x", (torch.bfloat16,), 2)
     T, d_in = x.shape
-    if G * 8 != d_in:
-        raise ValueError(f"codes [{d_out}, {G}] do not match x [{T}, {d_in}]")
+    d_out = _code_operands(codes, gamma, d_in, x.device)
     if out_dtype not in _OUT_TORCH:
         raise ValueError(f"unknown out_dtype {out_dtype}")
     if y is None:
@@ -442,11 +476,7 @@ def _decode_items(mats, T: int, d_in: int, out_dtype: int, ys, dev):
     ys = list(ys) if ys is not None else [None] * n
     items = (DecodeItem * n)()
     for i, (codes, gamma) in enumerate(mats):
-        _dev(codes, f"codes[{i}]")
-        _dev(gamma, f"gamma[{i}]")
-        d_out, G = codes.shape
-        if G * 8 != d_in:
-            raise ValueError(f"codes[{i}] [{d_out}, {G}] do not match d_in = {d_in}")
+        d_out = _code_operands(codes, gamma, d_in, dev, name=f"codes[{i}]")
         if ys[i] is None:
             ys[i] = torch.empty((T, d_out), dtype=_OUT_TORCH[out_dtype], device=dev)
         _out(ys[i], (T, d_out), (_OUT_TORCH[out_dtype],), dev, f"y[{i}]")
@@ -458,9 +488,7 @@ def decode_multi(mats, x: torch.Tensor, *, out_dtype: int = F32, ys=None, stream
     """``decode`` of up to 4 matrices that read the same ``x`` (a layer's q, k, v or gate, up), in one
     launch.  ``mats`` is a list of ``(codes, gamma)``; returns the list of outputs, each bit-identical to
     ``decode`` of that matrix alone."""
-    _dev(x, "x")
-    if x.dtype != torch.bfloat16 or x.dim() != 2:
-        raise ValueError("x must be a 2-D bfloat16 tensor")
+    _typed(x, "x", (torch.bfloat16,), 2)
     T, d_in = x.shape
     items, ys = _decode_items(mats, T, d_in, out_dtype, ys, x.device)
     _check(lib.sbl_decode_multi(len(ys), ctypes.c_void_p(ctypes.addressof(items)), _ptr(x), T, d_in,
@@ -472,9 +500,7 @@ def forward_decode_multi(mats, x_q: torch.Tensor, absmax: torch.Tensor, *, out_d
                          stream=None):
     """``forward`` of up to 4 matrices that read the same ``x_q`` at decode sizes (T <= 64), in one launch;
     each output bit-identical to ``forward`` of that matrix alone."""
-    _dev(x_q, "x_q")
-    _dev(absmax, "absmax")
-    T, d_in = x_q.shape
+    T, d_in = _act_operands(x_q, absmax)
     items, ys = _decode_items(mats, T, d_in, out_dtype, ys, x_q.device)
     _check(lib.sbl_forward_decode_multi(len(ys), ctypes.c_void_p(ctypes.addressof(items)), _ptr(x_q),
                                         _ptr(absmax), T, d_in, int(out_dtype), _stream(stream)),
@@ -488,9 +514,11 @@ def backward(codes: torch.Tensor, gamma: torch.Tensor, x_q: torch.Tensor, absmax
              workspace: Optional[torch.Tensor] = None, stream=None):
     """Dual-STE gradients: dX = gamma dY W_eff [T, d_in], dW = dY^T x~ [d_out, d_in] (float32)."""
     _as_bits16(dY, "dY")
-    d_out, G = codes.shape
-    T, d_in = x_q.shape
+    T, d_in = _act_operands(x_q, absmax)
+    d_out = _code_operands(codes, gamma, d_in, x_q.device)
     flags = (BWD_DX if need_dx else 0) | (BWD_DW if need_dw else 0)
+    if dY.device != x_q.device:
+        raise ValueError("dY must be on the device of x_q")
     if tuple(dY.shape) != (T, d_out):
         raise ValueError(f"dY has shape {tuple(dY.shape)}, expected {(T, d_out)}")
     if dx_dtype not in (F32, BF16):
