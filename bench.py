@@ -15,7 +15,11 @@ recomputed every step), then for each of the 7 linears, in order:
 Metric: tokens per second of whole steps.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+       python bench.py --workload 0     (one 256x256 linear, 64 tokens, fwd+bwd: launch-bound)
+       python bench.py --workload 1     (0.5B-like up-projection 896->4864, 512 tokens, forward, 8/6/4/2:8)
+       python bench.py --workload 2     (1.5B-like linears, 8192 tokens, fwd+bwd)
        python bench.py --workload 4     (decode: per-layer latency at 1/8/64 tokens, 6/4/2:8)
+       python bench.py --peaks          (measured ceilings only: matrix instructions on registers, HBM read)
        python bench.py --variants       (every N of N:8, 2:4, the ablations, AdamW + repack, norm + act quant,
                                          2:8 forward dense vs sparse matrix instruction)
 """
@@ -60,6 +64,10 @@ def parse():
     ap.add_argument("--variants", action="store_true",
                     help="N:M patterns and ablations: quant/mask/pack per pattern and mask-without-grad on the "
                          "3B-like matrices (one JSON line)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only measure the ceilings (int8 and bf16 matrix instructions on register operands, "
+                         "HBM read and copy) and print them as one JSON line")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured ceilings in the other modes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -92,12 +100,18 @@ def main():
         torch.cuda.synchronize()
         print("copy calibration done", flush=True)
         return
+    if args.peaks:
+        print(json.dumps({"metric": "measured ceilings", "n_gpus": 1, **measured_peaks()}), flush=True)
+        return
     wl = WORKLOADS[args.workload]
     if args.variants:
         run_variants(args, wl)
         return
     if not wl.backward and len(wl.T) > 1:
         run_decode(args, wl)
+        return
+    if not wl.backward:
+        run_forward_sweep(args, wl)
         return
     if not wl.backward or len(wl.T) != 1:
         print(f"workload {args.workload} is not a single-T fwd+bwd training workload", file=sys.stderr)
@@ -238,13 +252,26 @@ def main():
                 "launches_per_step": n_launch, "hip_kernels": dkernels,
                 "avg_launch_ms": round(tot_ms[parts.index(dom)] / n_launch, 4)}
 
+    # Measured ceilings of this GPU (matrix instructions on register operands, HBM read), beside the
+    # datasheet peaks.
+    peaks = None if args.no_peaks else measured_peaks()
+    if peaks:
+        mp = peaks["bf16_TFLOPs"] if dom == "bwd" else peaks["int8_TOPs"]
+        roofline["peak_measured"] = mp
+        roofline["frac_measured"] = round(achieved / mp, 4)
+        kernels["forward_int8"]["frac_int8_measured"] = rate("fwd") / 1e12 / peaks["int8_TOPs"]
+        kernels["backward_bf16"]["frac_bf16_measured"] = rate("bwd") / 1e12 / peaks["bf16_TFLOPs"]
+        for k, part in (("quant_mask_pack", "quant"), ("act_quant", "act")):
+            kernels[k]["frac_hbm_measured"] = rate(part) / 1e9 / peaks["read_GBps"]
+
     # CPU baseline: the oracle on a bounded sample, on this host's cores.
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, T, n_keep, args.cpu_tokens)
 
     line = {
-        "metric": "Sparse-BitLinear 6:8 fwd+bwd tokens/s at 3B shapes; % int8 MFMA / HBM peak",
+        "metric": ("Sparse-BitLinear 6:8 fwd+bwd tokens/s at 3B shapes; % int8 MFMA / HBM peak" if args.workload == 3
+                   else f"Sparse-BitLinear {n_keep}:8 fwd+bwd tokens/s ({wl.name})"),
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -263,6 +290,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kernels.items()},
         "cpu_baseline": cpu,
+        "measured_peaks": peaks,
         "input_gen_s": round(t_gen, 1),
     }
     if args.breakdown:
@@ -447,6 +475,7 @@ def run_decode(args, wl, copies: int = 16):
 
     Ws = [up(weight(wl.cfg, mi, L.d_out, L.d_in)) for mi, L in enumerate(wl.linears)]
     groups = decode_groups(wl)
+    peaks = None if args.no_peaks else measured_peaks()
     fuse_max = DECODE_FUSE_MAX if args.decode_fuse_max is None else args.decode_fuse_max
     results = []
     for n_keep in wl.n_keep:
@@ -508,6 +537,9 @@ def run_decode(args, wl, copies: int = 16):
                             "tokens_per_s": round(T / (us * 1e-6), 1),
                             "GBps": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9, 1),
                             "frac_hbm": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
+            if peaks:
+                results[-1]["frac_hbm_measured"] = round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 /
+                                                         peaks["read_GBps"], 4)
             del g
     line = {"metric": "Sparse-BitLinear decode: act quant + forward of a 3B-like layer (7 linears) on packed codes",
             "value": results[0]["us_per_layer"], "unit": "us per layer (T=%d, %d:8)" % (results[0]["T"], results[0]["n_keep"]),
@@ -515,8 +547,161 @@ def run_decode(args, wl, copies: int = 16):
             "vs_baseline": None, "dtype": "int8 x ternary (int32 accumulate), y bf16", "data": "synthetic",
             "config": {"workload": wl.name, "layer_copies_per_graph": copies,
                        "input_groups": ["+".join(wl.linears[i].name for i in grp) for grp in groups],
-                       "code_bytes_per_layer": code_bytes}, "results": results}
+                       "code_bytes_per_layer": code_bytes}, "results": results, "measured_peaks": peaks}
     print(json.dumps(line), flush=True)
+
+
+def measured_peaks():
+    """Ceilings measured on this GPU: the int8 (32x32x32) and bf16 (32x32x16) matrix instructions
+    on register operands (1024 blocks of 4 waves, 4 independent chains each), a streaming read of
+    2 GiB with the library's read kernel, and a torch copy of 1 GiB (read + write)."""
+    import torch
+
+    import sparsity_sparse_bitlinear_amd as sbl
+
+    dev = torch.device("cuda:0")
+    blocks, iters = 1024, 20000
+    sink = torch.zeros((blocks,), dtype=torch.float32, device=dev)
+    out = {}
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    for kind, key, ops in ((0, "int8_TOPs", 65536), (1, "bf16_TFLOPs", 32768)):
+        sec = timed(lambda: sbl._check(sbl.lib.sbl_peak_mfma(kind, iters, blocks, sbl._ptr(sink), None),
+                                       "sbl_peak_mfma"), 3)
+        out[key] = round(blocks * 4 * 4 * iters * ops / sec / 1e12, 1)
+    nbytes = 2 << 30
+    buf = torch.ones((nbytes // 4,), dtype=torch.float32, device=dev)
+    word = torch.zeros((1,), dtype=torch.int32, device=dev)
+    sec = timed(lambda: sbl._check(sbl.lib.sbl_peak_read(sbl._ptr(buf), nbytes, sbl._ptr(word), None),
+                                   "sbl_peak_read"), 10)
+    out["read_GBps"] = round(nbytes / sec / 1e9, 1)
+    a = buf[: (1 << 28)]
+    b = torch.empty_like(a)
+    sec = timed(lambda: b.copy_(a), 10)
+    out["copy_GBps"] = round(2 * a.numel() * 4 / sec / 1e9, 1)
+    out["datasheet"] = {"int8_TOPs": INT8_PEAK_TOPS, "bf16_TFLOPs": BF16_PEAK_TFLOPS, "hbm_GBps": HBM_PEAK_GBS}
+    del buf, a, b
+    torch.cuda.synchronize()
+    return out
+
+
+def run_forward_sweep(args, wl):
+    """Forward-only workload swept over masks (the 0.5B-like up-projection): per mask, one step is
+    the packing of W (quant/mask/pack), the act quant of x and the forward (y bf16), each timed
+    with HIP events on the stream; tokens/s = T / step time.  Inputs resident in HBM."""
+    import numpy as np
+    import torch
+
+    import sparsity_sparse_bitlinear_amd as sbl
+    from sbl_inputs import activation, weight
+
+    dev = torch.device("cuda:0")
+    T = wl.T[0]
+    (L,) = wl.linears
+    d_out, d_in = L.d_out, L.d_in
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    W = up(weight(wl.cfg, 0, d_out, d_in))
+    x = up(activation(wl.cfg, 0, T, d_in, dist=wl.act_dist, outlier_frac=wl.outlier_frac))
+    codes = torch.empty((d_out, d_in // 8), dtype=torch.int16, device=dev)
+    mask = torch.empty((d_out, d_in // 8), dtype=torch.uint8, device=dev)
+    gamma = torch.empty((1,), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(16, sbl.quant_workspace_size(d_out, d_in)),), dtype=torch.uint8, device=dev)
+    x_q = torch.empty((T, d_in), dtype=torch.int8, device=dev)
+    absmax = torch.empty((T,), dtype=torch.float32, device=dev)
+    y = torch.empty((T, d_out), dtype=torch.bfloat16, device=dev)
+    peaks = None if args.no_peaks else measured_peaks()
+    results = []
+    for n_keep in wl.n_keep:
+        calls = (lambda: sbl.quant_mask_pack(W, n_keep, codes=codes, mask=mask, gamma=gamma, workspace=ws),
+                 lambda: sbl.act_quant(x, x_q=x_q, absmax=absmax),
+                 lambda: sbl.forward(codes, gamma, x_q, absmax, out_dtype=sbl.BF16, y=y))
+        for _ in range(args.warmup):
+            for c in calls:
+                c()
+        torch.cuda.synchronize()
+        reps = max(args.steps, 20)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+        t0 = time.perf_counter()
+        for ev in evs:
+            for k, c in enumerate(calls):
+                ev[k].record()
+                c()
+            ev[3].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / reps
+        ms = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(3)] for ev in evs]).mean(axis=0)
+        step_ms = float(ms.sum())
+        ops = 2.0 * T * d_out * d_in * n_keep / 8
+        q_bytes = 2.375 * d_out * d_in
+        a_bytes = 3.0 * T * d_in + 4.0 * T
+        f_bytes = T * d_in + d_out * d_in / 4 + 2.0 * T * d_out
+        r = {"n_keep": n_keep, "tokens_per_s": round(T / (step_ms * 1e-3), 1), "step_ms": round(step_ms, 5),
+             "wall_ms_per_step": round(wall * 1e3, 5),
+             "quant_mask_pack": {"ms": round(ms[0], 5), "frac_hbm": round(q_bytes / (ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+             "act_quant": {"ms": round(ms[1], 5), "frac_hbm": round(a_bytes / (ms[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+             "forward_int8": {"ms": round(ms[2], 5), "TOPs": round(ops / (ms[2] * 1e-3) / 1e12, 2),
+                              "frac_int8": round(ops / (ms[2] * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                              "frac_hbm": round(f_bytes / (ms[2] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+        results.append(r)
+    main6 = next((r for r in results if r["n_keep"] == 6), results[0])
+    # The dominant kernel of the 6:8 step (all three are far below a microsecond of work at roofline:
+    # these launches are bound by launch and memory latency, not by a peak).
+    parts = {"quant_mask_pack": ("hbm", 2.375 * d_out * d_in, "GB/s", HBM_PEAK_GBS, 1e9),
+             "act_quant": ("hbm", 3.0 * T * d_in + 4.0 * T, "GB/s", HBM_PEAK_GBS, 1e9),
+             "forward_int8": ("mfma", 2.0 * T * d_out * d_in * 6 / 8, "TOP/s", INT8_PEAK_TOPS, 1e12)}
+    dom = max(parts, key=lambda k: main6[k]["ms"])
+    bound, work, unit, peak, scale = parts[dom]
+    achieved = work / (main6[dom]["ms"] * 1e-3) / scale
+    roofline = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": None, "avg_launch_ms": main6[dom]["ms"]}
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_forward_sweep(wl)
+    line = {"metric": "Sparse-BitLinear forward tokens/s, 0.5B-like up-projection (quant/mask/pack + act quant + "
+                      "forward per step), swept over N:8",
+            "value": main6["tokens_per_s"], "unit": "tokens/s (6:8)", "n_gpus": 1, "steps": reps,
+            "warmup": args.warmup, "ms_per_step": main6["step_ms"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "int8 x ternary (int32 accumulate), y bf16", "data": "synthetic",
+            "config": {"workload": wl.name, "tokens": T, "d_out": d_out, "d_in": d_in, "masks": list(wl.n_keep)},
+            "roofline": roofline, "results": results, "cpu_baseline": cpu, "measured_peaks": peaks}
+    print(json.dumps(line), flush=True)
+
+
+def cpu_forward_sweep(wl):
+    """The oracle's forward step (packing, act quant, int64 forward, y) at full shape, 6:8."""
+    import oracle
+    from sbl_inputs import activation, weight
+
+    (L,) = wl.linears
+    T = wl.T[0]
+    W = weight(wl.cfg, 0, L.d_out, L.d_in)
+    x = activation(wl.cfg, 0, T, L.d_in, dist=wl.act_dist, outlier_frac=wl.outlier_frac)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    w_eff, mask, g = oracle.effective_weight(W, 6)
+    oracle.pack_codes(w_eff)
+    xq, a = oracle.act_quant(x)
+    oracle.forward_y(oracle.forward_acc(w_eff, xq), g, a)
+    sec = time.perf_counter() - t0
+    return {"value": round(T / sec, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"the whole 6:8 step at full shape ({T} tokens), {sec:.2f} s"}
 
 
 def cpu_baseline(wl, T, n_keep, T_s):
@@ -533,6 +718,7 @@ def cpu_baseline(wl, T, n_keep, T_s):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
+    T_s = min(T_s, T)
     t_fixed = 0.0
     t_tok = 0.0
     for mi, L in enumerate(wl.linears):
@@ -556,7 +742,7 @@ def cpu_baseline(wl, T, n_keep, T_s):
     return {"value": round(T / est, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"all {len(wl.linears)} linears: quant/mask/pack at full size ({t_fixed:.1f} s) + "
                       f"act quant, forward, backward on {T_s} of {T} sampled tokens ({t_tok:.1f} s), "
-                      f"token part scaled by {T // T_s}; estimated {est:.1f} s per step"}
+                      f"token part scaled by {T / T_s:g}; estimated {est:.1f} s per step"}
 
 
 if __name__ == "__main__":

@@ -461,6 +461,24 @@ SBL_API const char* sbl_version(void);
  * pointer).  n_words <= 10. */
 SBL_API int sbl_test_round_mean(const uint32_t* S_words, int n_words, int64_t count, float* out);
 
+/* ------------------------------------------------------------------------ */
+/* Measurement helpers (not part of the operator)                            */
+/* ------------------------------------------------------------------------ */
+
+/* The matrix instruction the operator uses, on register operands only, so
+ * that its rate can be read against a measured ceiling beside the datasheet
+ * one: kind 0 = int8 32x32x32 (forward), 1 = bf16 32x32x16 (backward).
+ * blocks x 4 waves each issue 4 independent chains of iters instructions:
+ * blocks * 4 * 4 * iters instructions of 65,536 (int8) or 32,768 (bf16)
+ * operations.  sink: [blocks] float32, device memory, never read back.
+ */
+SBL_API int sbl_peak_mfma(int kind, int64_t iters, int blocks, float* sink, void* hip_stream);
+
+/* A streaming read of `bytes` bytes at `src` (device, 16-byte aligned, a
+ * multiple of 16), four 16-byte loads in flight per lane; sink: one uint32.
+ */
+SBL_API int sbl_peak_read(const void* src, int64_t bytes, uint32_t* sink, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -66,6 +66,8 @@ _SIGNATURES = {
     "sbl_backward_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int]),
     "sbl_backward": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int,
                               _c_ptr, _c_int, _c_ptr, _c_size, _c_ptr]),
+    "sbl_peak_mfma": (_c_int, [_c_int, _c_i64, _c_int, _c_ptr, _c_ptr]),
+    "sbl_peak_read": (_c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr]),
     "sbl_status_string": (ctypes.c_char_p, [_c_int]),
     "sbl_last_error": (ctypes.c_char_p, []),
     "sbl_version": (ctypes.c_char_p, []),

@@ -475,4 +475,24 @@ SBL_API int sbl_test_round_mean(const uint32_t* S_words, int n_words, int64_t co
   return SBL_OK;
 }
 
+SBL_API int sbl_peak_mfma(int kind, int64_t iters, int blocks, float* sink, void* hip_stream) {
+  SBL_REQUIRE(kind == 0 || kind == 1, SBL_ERR_INVALID_ARG, "kind=%d: 0 (int8) or 1 (bf16)", kind);
+  SBL_REQUIRE(iters >= 1 && iters <= ((int64_t)1 << 40), SBL_ERR_INVALID_ARG, "iters=%lld out of range",
+              (long long)iters);
+  SBL_REQUIRE(blocks >= 1 && blocks <= 65536, SBL_ERR_INVALID_ARG, "blocks=%d out of [1, 65536]", blocks);
+  SBL_REQUIRE(sink && aligned(sink, 4), SBL_ERR_INVALID_ARG, "sink must be a non-NULL float buffer of blocks");
+  hipError_t e = launch_mfma_peak(kind, iters, blocks, sink, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_peak_mfma launch");
+  return SBL_OK;
+}
+
+SBL_API int sbl_peak_read(const void* src, int64_t bytes, uint32_t* sink, void* hip_stream) {
+  SBL_REQUIRE(src && aligned(src, 16) && bytes >= 16 && bytes % 16 == 0, SBL_ERR_INVALID_ARG,
+              "src must be 16-byte aligned and bytes a positive multiple of 16");
+  SBL_REQUIRE(sink && aligned(sink, 4), SBL_ERR_INVALID_ARG, "sink must be a non-NULL uint32");
+  hipError_t e = launch_read_peak(src, bytes, sink, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_peak_read launch");
+  return SBL_OK;
+}
+
 }  // extern "C"

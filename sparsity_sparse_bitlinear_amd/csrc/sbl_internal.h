@@ -173,6 +173,12 @@ bool gemm_nt_q_supported(int64_t M, int64_t N, int64_t K, int64_t kb_rows);
 hipError_t launch_gemm_nt_q(const uint16_t* Arun, const int8_t* Bq, int64_t M, int64_t N, int64_t K, int64_t kb_rows,
                             float* C, hipStream_t s, int splits = 1, int64_t k_per_split = 0);
 
+// Measurement helpers (peak.hip): the matrix instruction on register operands
+// (kind 0: int8 32x32x32, 1: bf16 32x32x16; 4 chains per wave, iters each) and
+// a streaming read of `bytes` bytes.
+hipError_t launch_mfma_peak(int kind, int64_t iters, int blocks, float* sink, hipStream_t s);
+hipError_t launch_read_peak(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
+
 size_t backward_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int flags);
 hipError_t launch_backward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                            const uint16_t* dY, int64_t T, int64_t d_in, int64_t d_out, void* dX, int dx_dtype,
