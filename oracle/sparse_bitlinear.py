@@ -452,6 +452,71 @@ def unpack_sparse24(plane: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Pair plane: one byte per group of 8 for masks keeping at most 2 of 8 (2:8,
+# 1:8)  [SUM] 前置知识 > 半结构化 N:M 稀疏 (at most N non-zeros per group of M);
+# the packed weight format of inference decoding is precomputed once
+# ----------------------------------------------------------------------------
+
+PAIR_CODES = 252  # 28 position pairs x 3 x 3 ternary values
+
+
+def pair_index(p0: int, p1: int) -> int:
+    """Rank of the position pair (p0, p1), 0 <= p0 < p1 <= 7, in lexicographic order (0 .. 27)."""
+    assert 0 <= p0 < p1 <= 7
+    return sum(7 - a for a in range(p0)) + (p1 - p0 - 1)
+
+
+def pack_pairs(w_eff: np.ndarray) -> np.ndarray:
+    """Pair plane uint8 [d_out, d_in / 8] of a ternary W_eff whose every group of 8
+    consecutive d_in positions holds at most 2 non-zeros.
+
+    Each group is two stored slots at positions p0 < p1 with ternary values
+    v0, v1 (digits 0, 1, 2 for 0, +1, -1), and its byte is
+    9 * pair_index(p0, p1) + 3 * digit(v0) + digit(v1), always below 252.
+    The stored slots are the group's non-zeros; a group with fewer than two
+    pads with zero values at the lowest free positions (one non-zero at a:
+    (0, a), or (0, 1) when a = 0; none: (0, 1)), so each group has one byte.
+    1 bit per weight: the information content of a 2:8 group (28 x 9 cases
+    need log2(252) bits).
+    """
+    w = np.asarray(w_eff, np.int8)
+    d_out, d_in = w.shape
+    assert d_in % 8 == 0
+    digit = {0: 0, 1: 1, -1: 2}
+    out = np.zeros((d_out, d_in // 8), np.uint8)
+    for o in range(d_out):
+        for g in range(d_in // 8):
+            grp = [int(v) for v in w[o, 8 * g:8 * g + 8]]
+            nz = [j for j in range(8) if grp[j] != 0]
+            assert len(nz) <= 2, "more than 2 non-zeros in a group of 8"
+            if len(nz) == 2:
+                p0, p1 = nz
+            elif len(nz) == 1:
+                p0, p1 = (0, 1) if nz[0] == 0 else (0, nz[0])
+            else:
+                p0, p1 = 0, 1
+            out[o, g] = 9 * pair_index(p0, p1) + 3 * digit[grp[p0]] + digit[grp[p1]]
+    return out
+
+
+def unpack_pairs(plane: np.ndarray) -> np.ndarray:
+    """Inverse of ``pack_pairs``: int8 W_eff [d_out, 8 * groups]."""
+    plane = np.asarray(plane, np.uint8)
+    d_out, G = plane.shape
+    pairs = [(a, b) for a in range(8) for b in range(a + 1, 8)]
+    value = (0, 1, -1)
+    w = np.zeros((d_out, 8 * G), np.int8)
+    for o in range(d_out):
+        for g in range(G):
+            b = int(plane[o, g])
+            assert b < PAIR_CODES, "pair byte out of range"
+            p0, p1 = pairs[b // 9]
+            w[o, 8 * g + p0] = value[(b % 9) // 3]
+            w[o, 8 * g + p1] = value[b % 3]
+    return w
+
+
+# ----------------------------------------------------------------------------
 # Norm + activation quantization  [SUM] 方法步骤详情 step (3): x~ = Q_a(Norm(x))
 # ----------------------------------------------------------------------------
 

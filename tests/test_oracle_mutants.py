@@ -15,6 +15,7 @@ import test_oracle_mask as t_mask
 import test_oracle_ternary as t_tern
 import test_oracle_norm as t_norm
 import test_oracle_optimizer as t_opt
+import test_oracle_pairs as t_pairs
 import test_oracle_sparse24 as t_sp
 import test_oracle_variants as t_var
 
@@ -151,6 +152,21 @@ def _rsqrt_double_rounded(v):
     return np.float32(np.float32(1.0) / np.sqrt(v32))
 
 
+def _pack_pairs_digits_swapped(w_eff):
+    p = sb.unpack_pairs  # noqa: F841  (the inverse is left as it is)
+    w = np.asarray(w_eff, np.int8)
+    out = np.zeros((w.shape[0], w.shape[1] // 8), np.uint8)
+    digit = {0: 0, 1: 1, -1: 2}
+    for o in range(w.shape[0]):
+        for g in range(w.shape[1] // 8):
+            grp = [int(v) for v in w[o, 8 * g:8 * g + 8]]
+            nz = [j for j in range(8) if grp[j]]
+            p0, p1 = (nz + [j for j in range(8) if j not in nz])[:2] if len(nz) < 2 else nz
+            p0, p1 = min(p0, p1), max(p0, p1)
+            out[o, g] = 9 * sb.pair_index(p0, p1) + 3 * digit[grp[p1]] + digit[grp[p0]]
+    return out
+
+
 _ORIG_SP = sb.pack_sparse24
 
 
@@ -222,6 +238,8 @@ MUTANTS = [
      [t_norm.test_rsqrt_nearest_by_fractions]),
     ("kept-only plane with the two halves' codes swapped", "pack_sparse24", _sparse24_halves_swapped,
      [t_sp.test_worked_groups]),
+    ("pair byte with the two digits swapped", "pack_pairs", _pack_pairs_digits_swapped,
+     [t_pairs.test_worked_groups]),
 ]
 
 
