@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-fuse-max", type=int, default=None,
-                    help="decode: largest T * d_in * (16-row blocks of a group) that takes the fused launch")
+                    help="decode: largest T * d_in of a group that takes the fused launch (default: wherever supported)")
     ap.add_argument("--breakdown", action="store_true", help="print the per-linear breakdown to stderr")
     ap.add_argument("--variants", action="store_true",
                     help="N:M patterns and ablations: quant/mask/pack per pattern and mask-without-grad on the "
@@ -433,8 +433,7 @@ def run_variants(args, wl):
     print(json.dumps(line), flush=True)
 
 
-DECODE_FUSE_MAX = 32_000_000  # T * d_in * (16-row blocks) per launch up to which the fused decode beats
-                              # two calls (2048-wide rows: gate+up of a 3B layer at 8 tokens, 22.5e6, wins)
+DECODE_FUSE_MAX = 1 << 62  # T * d_in up to which a group takes the fused launch (where it is supported)
 
 
 # Linears of a decoder layer that read the same activations: q, k, v the normed hidden
@@ -455,10 +454,70 @@ def decode_groups(wl):
     return groups
 
 
+def _decode_case(args, wl, sbl, torch, up, activation, groups, layers, plane_name, plane_fmt, code_bytes, n_keep, T,
+                 copies, fuse_max, peaks):
+    """One (plane, mask, T) case of the decode workload: the layer's input groups in one captured graph
+    over `copies` packed copies; returns the result record."""
+    dev = torch.device("cuda:0")
+    gbufs = []
+    for g in groups:
+        L0 = wl.linears[g[0]]
+        x = up(activation(wl.cfg, g[0], T, L0.d_in, dist=wl.act_dist))
+        # the activation quantization inside the product's launch wherever it is supported
+        fused = sbl.decode_plane_supported(plane_fmt, T, L0.d_in) and T * L0.d_in <= fuse_max
+        gbufs.append(dict(x=x, fused=fused,
+                          x_q=torch.empty((T, L0.d_in), dtype=torch.int8, device=dev),
+                          a=torch.empty((T,), dtype=torch.float32, device=dev),
+                          ys=[torch.empty((T, wl.linears[i].d_out), dtype=torch.bfloat16, device=dev) for i in g]))
+
+    def layer(mats):
+        for g, b in zip(groups, gbufs):
+            gm = [mats[i] for i in g]
+            if b["fused"]:
+                sbl.forward_plane_multi(plane_fmt, gm, x=b["x"], out_dtype=sbl.BF16, ys=b["ys"])
+            else:
+                sbl.act_quant(b["x"], x_q=b["x_q"], absmax=b["a"])
+                sbl.forward_plane_multi(plane_fmt, gm, x_q=b["x_q"], absmax=b["a"], out_dtype=sbl.BF16, ys=b["ys"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for mats in layers:         # warm up outside the capture
+            layer(mats)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for mats in layers:
+            layer(mats)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps / copies
+    io_bytes = (sum(2 * T * wl.linears[grp[0]].d_in for grp in groups) + sum(2 * T * L.d_out for L in wl.linears))
+    launches = sum(1 if b["fused"] else 2 for b in gbufs)
+    r = {"T": T, "n_keep": n_keep, "plane": plane_name, "us_per_layer": round(us, 3), "launches_per_layer": launches,
+         "tokens_per_s": round(T / (us * 1e-6), 1), "code_bytes_per_layer": code_bytes,
+         "GBps": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9, 1),
+         "frac_hbm": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    if peaks:
+        r["frac_hbm_measured"] = round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 / peaks["read_GBps"], 4)
+    del graph
+    return r
+
+
 def run_decode(args, wl, copies: int = 16):
     """Decode workload: act quant + forward of every linear of a layer on pre-packed codes, for
     each token count and mask.  The linears that read the same activations (q, k, v; gate, up)
-    share one input and one call (sbl_decode_multi, or sbl_act_quant + sbl_forward_decode_multi).
+    share one input and one call (the activation quantization fused in where supported, else
+    sbl_act_quant + the product); masks keeping at most 2 of 8 are also run on the pair plane.
     `copies` distinct packed copies of the layer (more bytes than the 256 MB last-level cache)
     are walked in turn inside one captured HIP graph, so the code planes stream from HBM; the
     figure is graph time / copies per layer."""
@@ -480,74 +539,25 @@ def run_decode(args, wl, copies: int = 16):
     results = []
     for n_keep in wl.n_keep:
         packed = [sbl.quant_mask_pack(W, n_keep, want_mask=False) for W in Ws]
-        # distinct buffers holding the same packed layer: the graph walks all of them
-        layers = [[(codes.clone(), gamma.clone()) for (codes, _, gamma) in packed] for _ in range(copies)]
-        torch.cuda.synchronize()
-        code_bytes = sum(L.d_out * L.d_in // 4 for L in wl.linears)
-        for T in wl.T:
-            gbufs = []
-            for g in groups:
-                L0 = wl.linears[g[0]]
-                x = up(activation(wl.cfg, g[0], T, L0.d_in, dist=wl.act_dist))
-                # one fused launch (sbl_decode_multi) where it applies and its per-block
-                # re-quantization of the T rows stays small (T * d_in * blocks of 16 rows),
-                # else act quant + one sbl_forward_decode_multi
-                blocks = sum(-(-wl.linears[i].d_out // 16) for i in g)
-                gbufs.append(dict(x=x, fused=sbl.decode_supported(T, L0.d_in) and T * L0.d_in * blocks <= fuse_max,
-                                  x_q=torch.empty((T, L0.d_in), dtype=torch.int8, device=dev),
-                                  a=torch.empty((T,), dtype=torch.float32, device=dev),
-                                  ys=[torch.empty((T, wl.linears[i].d_out), dtype=torch.bfloat16, device=dev)
-                                      for i in g]))
-
-            def layer(mats):
-                for g, b in zip(groups, gbufs):
-                    gm = [mats[i] for i in g]
-                    if b["fused"]:
-                        sbl.decode_multi(gm, b["x"], out_dtype=sbl.BF16, ys=b["ys"])
-                    else:
-                        sbl.act_quant(b["x"], x_q=b["x_q"], absmax=b["a"])
-                        sbl.forward_decode_multi(gm, b["x_q"], b["a"], out_dtype=sbl.BF16, ys=b["ys"])
-
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                for mats in layers:         # warm up outside the capture
-                    layer(mats)
-            torch.cuda.current_stream().wait_stream(side)
+        planes = [("codes", sbl.PLANE_CODES, [(c, g) for (c, _, g) in packed])]
+        if n_keep <= 2:  # the pair plane: one byte per group of 8
+            planes.append(("pairs", sbl.PLANE_PAIRS, [(sbl.pack_pairs(c)[0], g) for (c, _, g) in packed]))
+        for plane_name, plane_fmt, mats0 in planes:
+            # distinct buffers holding the same packed layer: the graph walks all of them
+            layers = [[(pl.clone(), g.clone()) for (pl, g) in mats0] for _ in range(copies)]
             torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for mats in layers:
-                    layer(mats)
-            for _ in range(args.warmup):
-                g.replay()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _ in range(args.steps):
-                g.replay()
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / args.steps / copies
-            io_bytes = (sum(2 * T * wl.linears[grp[0]].d_in for grp in groups)
-                        + sum(2 * T * L.d_out for L in wl.linears))
-            launches = sum(1 if b["fused"] else 2 for b in gbufs)
-            results.append({"T": T, "n_keep": n_keep, "us_per_layer": round(us, 3), "launches_per_layer": launches,
-                            "tokens_per_s": round(T / (us * 1e-6), 1),
-                            "GBps": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9, 1),
-                            "frac_hbm": round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)})
-            if peaks:
-                results[-1]["frac_hbm_measured"] = round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 /
-                                                         peaks["read_GBps"], 4)
-            del g
+            code_bytes = sum(L.d_out * L.d_in // (4 if plane_fmt == sbl.PLANE_CODES else 8) for L in wl.linears)
+            for T in wl.T:
+                results.append(_decode_case(args, wl, sbl, torch, up, activation, groups, layers, plane_name, plane_fmt,
+                                            code_bytes, n_keep, T, copies, fuse_max, peaks))
     line = {"metric": "Sparse-BitLinear decode: act quant + forward of a 3B-like layer (7 linears) on packed codes",
             "value": results[0]["us_per_layer"], "unit": "us per layer (T=%d, %d:8)" % (results[0]["T"], results[0]["n_keep"]),
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
             "vs_baseline": None, "dtype": "int8 x ternary (int32 accumulate), y bf16", "data": "synthetic",
             "config": {"workload": wl.name, "layer_copies_per_graph": copies,
                        "input_groups": ["+".join(wl.linears[i].name for i in grp) for grp in groups],
-                       "code_bytes_per_layer": code_bytes}, "results": results, "measured_peaks": peaks}
+                       "code_bytes_per_layer": sum(L.d_out * L.d_in // 4 for L in wl.linears)},
+            "results": results, "measured_peaks": peaks}
     print(json.dumps(line), flush=True)
 
 

@@ -77,6 +77,9 @@ typedef enum {
 /* sbl_backward flags: which gradients to compute. */
 enum { SBL_BWD_DX = 1, SBL_BWD_DW = 2 };
 
+/* Weight planes the decode-size forward reads (sbl_forward_plane_multi). */
+enum { SBL_PLANE_CODES = 0, SBL_PLANE_PAIRS = 1 };
+
 /* Size limits checked by every entry point. */
 #define SBL_MAX_DIM ((int64_t)1 << 21)      /* d_in, d_out, T each <= 2,097,152 */
 #define SBL_MAX_WEIGHTS ((int64_t)1 << 36)  /* d_out * d_in                       */
@@ -318,14 +321,12 @@ SBL_API int sbl_forward(const uint16_t* codes, const float* gamma, const int8_t*
  * x_bf16       : [T, d_in] bf16 bits.
  * y            : [T, d_out] of y_dtype: SBL_F32, SBL_BF16 or SBL_I32.
  * Supported (sbl_decode_supported): 1 <= T <= 16, d_in % 64 == 0,
- * d_in <= 8192 and T * (d_in + 16) <= 49152 (the int8 tile each block keeps
- * in LDS); other shapes return SBL_ERR_UNSUPPORTED and enqueue nothing (use
- * sbl_act_quant + sbl_forward).  T = 0 is a no-op.
- * Cost: every block of output rows quantizes all T rows itself (there is no
- * cross-block step), so the saving of one launch (a few us) is worth it while
- * T * d_in * ceil(d_out / 16) stays moderate: with 2048-wide rows the fused
- * launch still won at about 2e7 (gate and up of a 3B layer, 2 x 11008 rows,
- * at T = 8, through sbl_decode_multi: 40.7 against 41.4 us per layer).
+ * T * d_in <= 65536 and T * (d_in + 16) <= 56832 (the int8 tile each block
+ * keeps in LDS); other shapes return SBL_ERR_UNSUPPORTED and enqueue nothing
+ * (use sbl_act_quant + sbl_forward).  T = 0 is a no-op.
+ * Cost: each resident block quantizes the T rows once for all the output
+ * rows it walks, a few blocks per compute unit, which is cheaper than the
+ * launch and the memory round trip of a separate quantization.
  */
 SBL_API int sbl_decode(const uint16_t* codes, const float* gamma, const uint16_t* x_bf16, int64_t T, int64_t d_in,
                        int64_t d_out, void* y, int y_dtype, void* hip_stream);
@@ -367,6 +368,45 @@ SBL_API int sbl_decode_multi(int count, const sbl_decode_item* items, const uint
                              int64_t d_in, int y_dtype, void* hip_stream);
 SBL_API int sbl_forward_decode_multi(int count, const sbl_decode_item* items, const int8_t* x_q, const float* absmax,
                                      int64_t T, int64_t d_in, int y_dtype, void* hip_stream);
+
+/* Pair plane of a weight whose mask keeps at most 2 of every 8 (2:8, 1:8):
+ * one byte per group of 8 instead of two, for decoding, which streams the
+ * weights once per generated token batch ([SUM] Table 3 decode rows; the
+ * packed format is precomputed once for inference).  Group g of row o gets
+ *
+ *   plane[o, g] = 9 * rank(p0, p1) + 3 * digit(v0) + digit(v1)   (< 252)
+ *
+ * where p0 < p1 are the positions (0..7) of its stored slots, rank their
+ * index among the 28 pairs in lexicographic order, v0, v1 the ternary values
+ * there and digit(0, +1, -1) = 0, 1, 2.  The stored slots are the group's
+ * non-zeros, padded with zeros at the lowest free positions (one non-zero at
+ * a: (0, a), or (0, 1) when a = 0; none: (0, 1)), so every group has one byte.
+ *
+ * codes : [d_out, d_in/8] code plane (sbl_quant_mask_pack with N <= 2).
+ * plane : [d_out, d_in/8] uint8.
+ * bad   : one uint64 in device memory or NULL; the number of groups with more
+ *         than 2 non-zeros (their byte is written as 0 and the plane is then
+ *         not valid) is ADDED to it, so the caller zeroes it first.
+ * Pointers 16-byte aligned (bad: 8).  d_in % 8 == 0.
+ */
+SBL_API int sbl_pack_pairs(const uint16_t* codes, int64_t d_out, int64_t d_in, uint8_t* plane, uint64_t* bad,
+                           void* hip_stream);
+
+/* sbl_forward_decode_multi (x_q and absmax given) and sbl_decode_multi (x as
+ * bf16, the activation quantization fused in: x_q = NULL, x_bf16 given,
+ * absmax = NULL) on either weight plane: format SBL_PLANE_CODES (items[i].codes
+ * is the code plane) or SBL_PLANE_PAIRS (items[i].codes points at the pair
+ * plane of sbl_pack_pairs, uint8 [d_out, d_in/8]).  The int32 sums, hence y,
+ * are identical for the two planes of one weight.
+ * T <= 64 and d_in % 64 == 0 (codes) or % 128 == 0 (pairs); the fused form
+ * takes what sbl_decode_supported accepts (pairs: d_in % 128 == 0 and
+ * T * (d_in + 16) <= 54784; sbl_decode_plane_supported).  Otherwise
+ * SBL_ERR_UNSUPPORTED.
+ */
+SBL_API int sbl_decode_plane_supported(int format, int64_t T, int64_t d_in); /* the fused form: 1 or 0 */
+SBL_API int sbl_forward_plane_multi(int format, int count, const sbl_decode_item* items, const int8_t* x_q,
+                                    const float* absmax, const uint16_t* x_bf16, int64_t T, int64_t d_in,
+                                    int y_dtype, void* hip_stream);
 
 /* Kept-only 2:4 operand plane for 2:8 and 2:4 masks, and the forward on it,
  * which runs on gfx950's sparse int8 matrix instruction (2 stored values of

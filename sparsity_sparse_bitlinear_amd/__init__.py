@@ -58,6 +58,10 @@ _SIGNATURES = {
     "sbl_rmsnorm_act_quant": (_c_int, [_c_ptr, _c_ptr, ctypes.c_float, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr,
                                        _c_ptr]),
     "sbl_pack_sparse24": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "sbl_pack_pairs": (_c_int, [_c_ptr, _c_i64, _c_i64, _c_ptr, _c_ptr, _c_ptr]),
+    "sbl_decode_plane_supported": (_c_int, [_c_int, _c_i64, _c_i64]),
+    "sbl_forward_plane_multi": (_c_int, [_c_int, _c_int, ctypes.c_void_p, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64,
+                                         _c_int, _c_ptr]),
     "sbl_forward_sparse24": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i64, _c_i64, _c_i64, _c_ptr, _c_int, _c_ptr]),
     "sbl_decode_supported": (_c_int, [_c_i64, _c_i64]),
@@ -176,9 +180,11 @@ def _act_operands(x_q: torch.Tensor, absmax: torch.Tensor):
     return T, d_in
 
 
-def _code_operands(codes: torch.Tensor, gamma: torch.Tensor, d_in: int, dev, name: str = "codes"):
-    """codes int16 [d_out, d_in/8] and gamma float32 [>= 1] on ``dev``; returns d_out."""
-    _typed(codes, name, (torch.int16, torch.uint16), 2)
+def _code_operands(codes: torch.Tensor, gamma: torch.Tensor, d_in: int, dev, name: str = "codes",
+                   plane: int = 0):
+    """codes int16 [d_out, d_in/8] (or, for the pair plane, uint8 [d_out, d_in/8]) and gamma float32 [>= 1]
+    on ``dev``; returns d_out."""
+    _typed(codes, name, (torch.uint8,) if plane == PLANE_PAIRS else (torch.int16, torch.uint16), 2)
     _gamma_ok(gamma)
     d_out, G = codes.shape
     if G * 8 != d_in:
@@ -395,6 +401,50 @@ def rmsnorm_act_quant(x: torch.Tensor, g: Optional[torch.Tensor] = None, eps: fl
 
 _OUT_TORCH = {F32: torch.float32, BF16: torch.bfloat16, I32: torch.int32}
 
+PLANE_CODES, PLANE_PAIRS = 0, 1
+
+
+def pack_pairs(codes: torch.Tensor, *, plane: Optional[torch.Tensor] = None, stream=None):
+    """Pair plane (one byte per group of 8) of a code plane whose mask keeps at most 2 of 8:
+    ``(plane uint8 [d_out, d_in/8], bad int64 [1])``; ``bad`` counts groups with more than 2 non-zeros."""
+    _typed(codes, "codes", (torch.int16, torch.uint16), 2)
+    d_out, G = codes.shape
+    if plane is None:
+        plane = torch.empty((d_out, G), dtype=torch.uint8, device=codes.device)
+    _out(plane, (d_out, G), (torch.uint8,), codes.device, "plane")
+    bad = torch.zeros((1,), dtype=torch.int64, device=codes.device)
+    _check(lib.sbl_pack_pairs(_ptr(codes), d_out, 8 * G, _ptr(plane), _ptr(bad), _stream(stream)), "sbl_pack_pairs")
+    return plane, bad
+
+
+def decode_plane_supported(plane_format: int, T: int, d_in: int) -> bool:
+    """True if ``forward_plane_multi`` takes ``x`` (the quantization fused in) at this (T, d_in)."""
+    return bool(lib.sbl_decode_plane_supported(int(plane_format), int(T), int(d_in)))
+
+
+def forward_plane_multi(plane_format: int, mats, *, x_q: Optional[torch.Tensor] = None,
+                        absmax: Optional[torch.Tensor] = None, x: Optional[torch.Tensor] = None,
+                        out_dtype: int = F32, ys=None, stream=None):
+    """Decode-size forward (T <= 64) of up to 4 matrices sharing one input, on the code plane
+    (``PLANE_CODES``) or the pair plane (``PLANE_PAIRS``, ``mats`` holding ``(plane, gamma)``); with ``x``
+    (bf16) the activation quantization runs in the same launch, else ``x_q`` and ``absmax`` are given."""
+    if plane_format not in (PLANE_CODES, PLANE_PAIRS):
+        raise ValueError(f"unknown plane format {plane_format}")
+    if (x is None) == (x_q is None):
+        raise ValueError("give either x (bf16) or x_q with absmax")
+    if x is not None:
+        _typed(x, "x", (torch.bfloat16,), 2)
+        T, d_in = x.shape
+        dev = x.device
+    else:
+        T, d_in = _act_operands(x_q, absmax)
+        dev = x_q.device
+    items, ys = _decode_items(mats, T, d_in, out_dtype, ys, dev, plane=plane_format)
+    _check(lib.sbl_forward_plane_multi(int(plane_format), len(ys), ctypes.c_void_p(ctypes.addressof(items)),
+                                       _ptr(x_q), _ptr(absmax), _ptr(x), T, d_in, int(out_dtype), _stream(stream)),
+           "sbl_forward_plane_multi")
+    return ys
+
 
 def pack_sparse24(codes: torch.Tensor, *, plane: Optional[torch.Tensor] = None, stream=None):
     """Kept-only 2:4 plane of a 2:8 / 2:4 code plane: ``(plane uint8 [d_out, d_in/64, 16], bad int64 [1])``;
@@ -468,7 +518,7 @@ def decode(codes: torch.Tensor, gamma: torch.Tensor, x: torch.Tensor, *, out_dty
     return y
 
 
-def _decode_items(mats, T: int, d_in: int, out_dtype: int, ys, dev):
+def _decode_items(mats, T: int, d_in: int, out_dtype: int, ys, dev, plane: int = 0):
     mats = list(mats)
     n = len(mats)
     if not 1 <= n <= DECODE_MULTI_MAX:
@@ -478,7 +528,7 @@ def _decode_items(mats, T: int, d_in: int, out_dtype: int, ys, dev):
     ys = list(ys) if ys is not None else [None] * n
     items = (DecodeItem * n)()
     for i, (codes, gamma) in enumerate(mats):
-        d_out = _code_operands(codes, gamma, d_in, dev, name=f"codes[{i}]")
+        d_out = _code_operands(codes, gamma, d_in, dev, name=f"codes[{i}]", plane=plane)
         if ys[i] is None:
             ys[i] = torch.empty((T, d_out), dtype=_OUT_TORCH[out_dtype], device=dev)
         _out(ys[i], (T, d_out), (_OUT_TORCH[out_dtype],), dev, f"y[{i}]")

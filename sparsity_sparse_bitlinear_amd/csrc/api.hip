@@ -321,14 +321,16 @@ SBL_API int sbl_decode(const uint16_t* codes, const float* gamma, const uint16_t
               "y_dtype=%d is not SBL_F32, SBL_BF16 or SBL_I32", y_dtype);
   if (T == 0) return SBL_OK;
   SBL_REQUIRE(decode_fused_supported(T, d_in), SBL_ERR_UNSUPPORTED,
-              "sbl_decode takes 1 <= T <= 16, d_in %% 64 == 0, d_in <= 8192, T * (d_in + 16) <= 49152 "
+              "sbl_decode takes 1 <= T <= 16, d_in %% 64 == 0, T * d_in <= 65536, T * (d_in + 16) <= 56832 "
               "(got T=%lld, d_in=%lld); "
               "use sbl_act_quant + sbl_forward",
               (long long)T, (long long)d_in);
   SBL_REQUIRE(codes && gamma && x_bf16 && y, SBL_ERR_INVALID_ARG, "NULL pointer argument");
   SBL_REQUIRE(aligned(codes, 16) && aligned(x_bf16, 16) && aligned(y, 16) && aligned(gamma, 4), SBL_ERR_INVALID_ARG,
               "codes, x, y must be 16-byte aligned; gamma 4-byte aligned");
-  hipError_t e = launch_decode_fused(codes, gamma, x_bf16, T, d_in, d_out, y, y_dtype, (hipStream_t)hip_stream);
+  const DecodeItem it{codes, gamma, d_out, y};
+  hipError_t e = launch_decode_plane(SBL_PLANE_CODES, 1, &it, true, x_bf16, nullptr, T, d_in, y_dtype,
+                                     (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "sbl_decode launch");
   return SBL_OK;
 }
@@ -366,7 +368,8 @@ SBL_API int sbl_decode_multi(int count, const sbl_decode_item* items, const uint
               "use sbl_act_quant + sbl_forward_decode_multi",
               (long long)T, (long long)d_in);
   SBL_REQUIRE(x_bf16 && aligned(x_bf16, 16), SBL_ERR_INVALID_ARG, "x must be non-NULL and 16-byte aligned");
-  hipError_t e = launch_decode_fused_multi(count, it, x_bf16, T, d_in, y_dtype, (hipStream_t)hip_stream);
+  hipError_t e = launch_decode_plane(SBL_PLANE_CODES, count, it, true, x_bf16, nullptr, T, d_in, y_dtype,
+                                     (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "sbl_decode_multi launch");
   return SBL_OK;
 }
@@ -384,8 +387,52 @@ SBL_API int sbl_forward_decode_multi(int count, const sbl_decode_item* items, co
   if (T == 0) return SBL_OK;
   SBL_REQUIRE(x_q && absmax && aligned(x_q, 16) && aligned(absmax, 4), SBL_ERR_INVALID_ARG,
               "x_q (16-byte aligned) and absmax (4-byte aligned) must be non-NULL");
-  hipError_t e = launch_forward_decode_multi(count, it, x_q, absmax, T, d_in, y_dtype, (hipStream_t)hip_stream);
+  hipError_t e = launch_decode_plane(SBL_PLANE_CODES, count, it, false, x_q, absmax, T, d_in, y_dtype,
+                                     (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "sbl_forward_decode_multi launch");
+  return SBL_OK;
+}
+
+SBL_API int sbl_pack_pairs(const uint16_t* codes, int64_t d_out, int64_t d_in, uint8_t* plane, uint64_t* bad,
+                           void* hip_stream) {
+  int rc = check_dims(d_out, d_in);
+  if (rc != SBL_OK) return rc;
+  SBL_REQUIRE(codes && plane, SBL_ERR_INVALID_ARG, "codes and plane must be non-NULL");
+  SBL_REQUIRE(aligned(codes, 16) && aligned(plane, 16) && (!bad || aligned(bad, 8)), SBL_ERR_INVALID_ARG,
+              "codes and plane must be 16-byte aligned, bad 8-byte aligned");
+  hipError_t e = launch_pack_pairs(codes, d_out, d_in, plane, (unsigned long long*)bad, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_pack_pairs launch");
+  return SBL_OK;
+}
+
+SBL_API int sbl_decode_plane_supported(int format, int64_t T, int64_t d_in) {
+  return (format == SBL_PLANE_CODES || format == SBL_PLANE_PAIRS) && decode_fused_plane_supported(format, T, d_in);
+}
+
+SBL_API int sbl_forward_plane_multi(int format, int count, const sbl_decode_item* items, const int8_t* x_q,
+                                    const float* absmax, const uint16_t* x_bf16, int64_t T, int64_t d_in,
+                                    int y_dtype, void* hip_stream) {
+  DecodeItem it[SBL_DECODE_MULTI_MAX];
+  SBL_REQUIRE(format == SBL_PLANE_CODES || format == SBL_PLANE_PAIRS, SBL_ERR_INVALID_ARG,
+              "format=%d is not SBL_PLANE_CODES or SBL_PLANE_PAIRS", format);
+  int rc = check_tokens(T);
+  if (rc != SBL_OK) return rc;
+  rc = check_decode_items(count, items, d_in, y_dtype, it);
+  if (rc != SBL_OK) return rc;
+  const bool fused = x_bf16 != nullptr;
+  SBL_REQUIRE(fused != (x_q != nullptr) && (fused || absmax), SBL_ERR_INVALID_ARG,
+              "give either x_bf16 (quantization fused in) or x_q and absmax");
+  SBL_REQUIRE(decode_plane_supported(format, T, d_in), SBL_ERR_UNSUPPORTED,
+              "T=%lld, d_in=%lld: T <= 64 and d_in a multiple of %d are required", (long long)T, (long long)d_in,
+              format == SBL_PLANE_PAIRS ? 128 : 64);
+  SBL_REQUIRE(!fused || T == 0 || decode_fused_plane_supported(format, T, d_in), SBL_ERR_UNSUPPORTED,
+              "T=%lld, d_in=%lld: outside the fused form's range", (long long)T, (long long)d_in);
+  if (T == 0) return SBL_OK;
+  SBL_REQUIRE(fused ? aligned(x_bf16, 16) : (aligned(x_q, 16) && aligned(absmax, 4)), SBL_ERR_INVALID_ARG,
+              "x_bf16 and x_q must be 16-byte aligned, absmax 4-byte aligned");
+  hipError_t e = launch_decode_plane(format, count, it, fused, fused ? (const void*)x_bf16 : (const void*)x_q,
+                                     absmax, T, d_in, y_dtype, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "sbl_forward_plane_multi launch");
   return SBL_OK;
 }
 

@@ -631,6 +631,9 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Decode-size forward for 17 to 64 tokens on the code plane (up to 16 tokens,
+// and the pair plane, go through decode.hip).
+// ---------------------------------------------------------------------------
 // Decode forward (T <= 64, d_in % 64 == 0): the code plane is streamed once and
 // every weight meets at most 64 tokens, so the kernel is bound by the code
 // bytes and, at these sizes, by the latency of one round of loads, not by the
@@ -744,10 +747,17 @@ __device__ __forceinline__ int dec_item(const DecBatch& db, int b) {
 
 // RT row tiles of 16 per block (RT = 2 on large grids with 4 token tiles:
 // every block reads all of x_q, so 32-row blocks halve those re-reads).
-template <int NTT, int OUT, int W, int RT>
+// PAIRS: the weights as the pair plane (one byte per group of 8; a lane's 16 k
+// of a step are 2 bytes, expanded through a table of the 252 bytes in LDS).
+template <int NTT, int OUT, int W, int RT, bool PAIRS>
 __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict__ xq, const DecBatch db,
                                                        const float* __restrict__ absmax, int T, int d_in) {
   __shared__ int red[W - 1][RT * NTT][4][64];
+  __shared__ uint2 table[PAIRS ? 256 : 1];
+  if constexpr (PAIRS) {
+    if (threadIdx.x < 256) table[threadIdx.x] = pair_expand(threadIdx.x);
+    __syncthreads();
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -762,10 +772,12 @@ __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict_
   const int per = (nks + W - 1) / W;
   const int s_begin = wave * per, s_end = min(nks, s_begin + per);
   const int rows = min(db.rows, d_out - o0);
-  const auto br = make_rsrc(codes + (int64_t)o0 * G, clamp_bytes((int64_t)rows * G * 2));
+  const int row_bytes = PAIRS ? G : 2 * G;
+  constexpr int kStepBytes = PAIRS ? 8 : 16;  // bytes of a row per 64-wide K step
+  const auto br = make_rsrc((const uint8_t*)codes + (int64_t)o0 * row_bytes, clamp_bytes((int64_t)rows * row_bytes));
   const auto xr = make_rsrc(xq, clamp_bytes((int64_t)T * d_in));
   const int q = lane >> 4, r16 = lane & 15;
-  const uint32_t b_off = (uint32_t)(r16 * G * 2 + 4 * q);
+  const uint32_t b_off = (uint32_t)(r16 * row_bytes + (PAIRS ? 2 : 4) * q);
   uint32_t x_off[NTT];
 #pragma unroll
   for (int tt = 0; tt < NTT; ++tt) x_off[tt] = (uint32_t)((16 * tt + r16) * d_in + 16 * q);
@@ -781,8 +793,10 @@ __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict_
     for (int u = 0; u < kS; ++u) {
       const bool ok = s0 + u < s_end;
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        wb[u][rt] = bload4(br, ok ? b_off + (uint32_t)(rt * 32 * G + (s0 + u) * 16) : kOOB);
+      for (int rt = 0; rt < RT; ++rt) {
+        const uint32_t off = ok ? b_off + (uint32_t)(rt * 16 * row_bytes + (s0 + u) * kStepBytes) : kOOB;
+        wb[u][rt] = PAIRS ? bload2(br, off) : bload4(br, off);
+      }
 #pragma unroll
       for (int tt = 0; tt < NTT; ++tt)
         fx[u][tt] = __builtin_bit_cast(v4i, bload16(xr, ok ? x_off[tt] + (uint32_t)(s0 + u) * 64 : kOOB));
@@ -795,7 +809,13 @@ __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict_
     for (int u = 0; u < kS; ++u)
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        const v4i fb = __builtin_bit_cast(v4i, expand16(wb[u][rt]));
+        v4i fb;
+        if constexpr (PAIRS) {
+          const uint2 e0 = table[wb[u][rt] & 0xFFu], e1 = table[(wb[u][rt] >> 8) & 0xFFu];
+          fb = (v4i){(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
+        } else {
+          fb = __builtin_bit_cast(v4i, expand16(wb[u][rt]));
+        }
 #pragma unroll
         for (int tt = 0; tt < NTT; ++tt)
           acc[NTT * rt + tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb, fx[u][tt], acc[NTT * rt + tt], 0, 0, 0);
@@ -811,152 +831,42 @@ __global__ __launch_bounds__(64 * W) void k_fwd_decode(const int8_t* __restrict_
   decode_store<NTT, OUT, W, RT>(acc, red, wave, lane, o0, T, d_out, o0 + rows, sc, y);
 }
 
-// Decode with the activation quantization fused in.  Each block quantizes the
-// T bf16 rows of x once into an int8 tile in LDS (every block covers all of K,
-// so it sees whole rows): wave w (W >= T) owns token w, reads its row with all
-// 64 lanes (16-byte chunks kept in registers), takes the row maximum by a wave
-// reduction, quantizes the chunks with the same arithmetic as k_act_quant and
-// stores them; after one barrier the product reads its x_q operands from the
-// tile.  x_q and a_t are therefore bit-identical to the
-// two-call path, and so are the int32 sums and y.  The first round of code
-// loads is issued before the quantization, so it overlaps it.
-constexpr int kFuseWaves = 16;        // most waves per block
-constexpr int kFuseChunks = 16;       // 16-byte x chunks per lane in registers
-constexpr int kFuseLdsBytes = 49152;  // int8 tile T x (d_in + 16)
 
-// Smallest wave count (4, 8, 16) with a wave per token, or 0 if T or the row
-// length does not fit.
-inline int decode_fused_min_waves(int64_t T, int64_t d_in) {
-  if ((d_in / 8 + 63) / 64 > kFuseChunks) return 0;
-  for (int w = 4; w <= kFuseWaves; w *= 2)
-    if (T <= w) return w;
-  return 0;
-}
-
-// NCH: 16-byte x chunks per lane (d_in <= 512 NCH), sized to the row so that
-// short rows do not hold registers for long ones (occupancy).
-// RT: row tiles of 16 per block (2 on large grids: each block then quantizes
-// the T rows for 32 output rows).
-template <int OUT, int W, int NCH, int RT>
-__global__ __launch_bounds__(64 * W) void k_decode_fused(const uint16_t* __restrict__ x, const DecBatch db, int T,
-                                                         int d_in) {
-  extern __shared__ __attribute__((aligned(16))) char xs[];  // [T][d_in + 16] int8
-  __shared__ int red[W - 1][RT][4][64];
-  __shared__ float amax[16];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int item = dec_item(db, blockIdx.x);
-  const uint16_t* __restrict__ codes = db.codes[item];
-  const float* __restrict__ gamma_p = db.gamma[item];
-  const int d_out = db.d_out[item];
-  void* __restrict__ y = db.y[item];
-  const int o0 = (blockIdx.x - db.begin[item]) * db.rows;
-  const int G = d_in >> 3;
-  const int nks = d_in >> 6;
-  const int ld = d_in + 16;  // tile row stride: rows 16 bytes apart shift the banks
-  const int per = (nks + W - 1) / W;
-  const int s_begin = wave * per, s_end = min(nks, s_begin + per);
-  const int rows = min(db.rows, d_out - o0);
-  const auto br = make_rsrc(codes + (int64_t)o0 * G, clamp_bytes((int64_t)rows * G * 2));
-  const int q = lane >> 4, r16 = lane & 15;
-  const uint32_t b_off = (uint32_t)(r16 * G * 2 + 4 * q);
-
-  // first round of code words
-  uint32_t wb[kDecSteps][RT];
-#pragma unroll
-  for (int u = 0; u < kDecSteps; ++u)
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-      wb[u][rt] = bload4(br, s_begin + u < s_end ? b_off + (uint32_t)(rt * 32 * G + (s_begin + u) * 16) : kOOB);
-
-  // this wave's row of x, whole, in registers (chunk j: lane j % 64, slot j / 64)
-  const int nch = d_in >> 3;
-  const int t = wave;
-  const auto xr = make_rsrc(x, clamp_bytes((int64_t)T * d_in * 2));
-  uint4 xv[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int j = lane + 64 * i;
-    xv[i] = bload16(xr, t < T && j < nch ? (uint32_t)((t * d_in + 8 * j) * 2) : kOOB);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
-  if (t < T) {  // wave-uniform
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i)
-      m = max(m, max(max(max_mag2(xv[i].x), max_mag2(xv[i].y)), max(max_mag2(xv[i].z), max_mag2(xv[i].w))));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-    if (lane == 0) amax[t] = __uint_as_float(m << 16);
-    const ActScale qs = act_scale(m ? __uint_as_float(m << 16) : 1.0f);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int j = lane + 64 * i;
-      if (j < nch) *(uint2*)(xs + t * ld + 8 * j) = m ? quant_chunk(xv[i], qs.k, qs.as, qs.c) : make_uint2(0u, 0u);
-    }
-  }
-  __syncthreads();  // tile and row maxima complete
-
-  const bool tok = r16 < T;
-  const char* xrow = xs + (tok ? r16 : 0) * ld + 16 * q;
-  v4i acc[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) acc[rt] = (v4i){0, 0, 0, 0};
-  for (int s0 = s_begin; s0 < s_end; s0 += kDecSteps) {
-    if (s0 != s_begin) {
-#pragma unroll
-      for (int u = 0; u < kDecSteps; ++u)
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-          wb[u][rt] = bload4(br, s0 + u < s_end ? b_off + (uint32_t)(rt * 32 * G + (s0 + u) * 16) : kOOB);
-    }
-#pragma unroll
-    for (int u = 0; u < kDecSteps; ++u) {
-      if (s0 + u >= s_end) break;  // wave-uniform; the code words are already in registers
-      const v4i fx = tok ? *(const v4i*)(xrow + 64 * (s0 + u)) : (v4i){0, 0, 0, 0};
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-        acc[rt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(v4i, expand16(wb[u][rt])), fx, acc[rt], 0,
-                                                        0, 0);
-    }
-  }
-  const float sc[1] = {tok ? *gamma_p * (1.0f / 127.0f) * amax[r16] : 0.0f};
-  decode_store<1, OUT, W, RT>(acc, red, wave, lane, o0, T, d_out, o0 + rows, sc, y);
-}
-
-template <int NTT, int W, int RT>
+template <int NTT, int W, int RT, bool PAIRS>
 hipError_t launch_decode_w(const DecBatch& db, const int8_t* xq, const float* absmax, int64_t T, int64_t d_in,
                            int y_dtype, hipStream_t s) {
   const dim3 grid((unsigned)db.begin[db.count]), block(64 * W);
   switch (y_dtype) {
     case SBL_F32:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_F32, W, RT>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_F32, W, RT, PAIRS>), grid, block, 0, s, xq, db, absmax, (int)T,
+                         (int)d_in);
       break;
     case SBL_BF16:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_BF16, W, RT>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_BF16, W, RT, PAIRS>), grid, block, 0, s, xq, db, absmax, (int)T,
+                         (int)d_in);
       break;
     default:
-      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_I32, W, RT>), grid, block, 0, s, xq, db, absmax, (int)T, (int)d_in);
+      hipLaunchKernelGGL((k_fwd_decode<NTT, SBL_I32, W, RT, PAIRS>), grid, block, 0, s, xq, db, absmax, (int)T,
+                         (int)d_in);
       break;
   }
   return hipGetLastError();
 }
 
-template <int NTT>
+template <int NTT, bool PAIRS>
 hipError_t launch_decode(const DecBatch& db, const int8_t* xq, const float* absmax, int64_t T, int64_t d_in,
                          int y_dtype, hipStream_t s) {
   const int w = decode_waves(db.begin[db.count], 4);
   if constexpr (NTT == 4) {
     if (db.rows == 2 * kDecRows) {  // two row tiles: at most 8 waves (LDS of the partial sums)
-      if (w >= 8) return launch_decode_w<NTT, 8, 2>(db, xq, absmax, T, d_in, y_dtype, s);
-      return launch_decode_w<NTT, 4, 2>(db, xq, absmax, T, d_in, y_dtype, s);
+      if (w >= 8) return launch_decode_w<NTT, 8, 2, PAIRS>(db, xq, absmax, T, d_in, y_dtype, s);
+      return launch_decode_w<NTT, 4, 2, PAIRS>(db, xq, absmax, T, d_in, y_dtype, s);
     }
   }
   switch (w) {
-    case 16: return launch_decode_w<NTT, 16, 1>(db, xq, absmax, T, d_in, y_dtype, s);
-    case 8: return launch_decode_w<NTT, 8, 1>(db, xq, absmax, T, d_in, y_dtype, s);
-    default: return launch_decode_w<NTT, 4, 1>(db, xq, absmax, T, d_in, y_dtype, s);
+    case 16: return launch_decode_w<NTT, 16, 1, PAIRS>(db, xq, absmax, T, d_in, y_dtype, s);
+    case 8: return launch_decode_w<NTT, 8, 1, PAIRS>(db, xq, absmax, T, d_in, y_dtype, s);
+    default: return launch_decode_w<NTT, 4, 1, PAIRS>(db, xq, absmax, T, d_in, y_dtype, s);
   }
 }
 
@@ -1052,9 +962,9 @@ static hipError_t launch_fwd_direct(const uint16_t* codes, const float* gamma, c
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
                           int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  if (T <= 64 && d_in % 64 == 0) {
+  if (T <= 64 && decode_plane_supported(SBL_PLANE_CODES, T, d_in)) {
     const DecodeItem it{codes, gamma, d_out, y};
-    return launch_forward_decode_multi(1, &it, xq, absmax, T, d_in, y_dtype, s);
+    return launch_decode_plane(SBL_PLANE_CODES, 1, &it, false, xq, absmax, T, d_in, y_dtype, s);
   }
   if (d_in % kFK == 0 && (int64_t)kBM * d_in <= kMaxRsrcBytes)
     return launch_fwd_direct<false>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
@@ -1071,74 +981,16 @@ hipError_t launch_forward_sparse24(const uint8_t* plane, const float* gamma, con
   return launch_fwd_direct<true>((const uint16_t*)plane, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, s);
 }
 
-bool decode_fused_supported(int64_t T, int64_t d_in) {
-  return T >= 1 && T <= 16 && d_in % 64 == 0 && d_in <= 8192 && T * (d_in + 16) <= kFuseLdsBytes &&
-         decode_fused_min_waves(T, d_in) > 0;
-}
-
-template <int W, int NCH, int RT>
-hipError_t launch_decode_fused_wcr(const DecBatch& db, const uint16_t* x, int64_t T, int64_t d_in, int y_dtype,
-                                   hipStream_t s) {
-  const dim3 grid((unsigned)db.begin[db.count]), block(64 * W);
-  const size_t lds = (size_t)T * (size_t)(d_in + 16);
-  switch (y_dtype) {
-    case SBL_F32:
-      hipLaunchKernelGGL((k_decode_fused<SBL_F32, W, NCH, RT>), grid, block, lds, s, x, db, (int)T, (int)d_in);
-      break;
-    case SBL_BF16:
-      hipLaunchKernelGGL((k_decode_fused<SBL_BF16, W, NCH, RT>), grid, block, lds, s, x, db, (int)T, (int)d_in);
-      break;
-    default:
-      hipLaunchKernelGGL((k_decode_fused<SBL_I32, W, NCH, RT>), grid, block, lds, s, x, db, (int)T, (int)d_in);
-      break;
-  }
-  return hipGetLastError();
-}
-
-template <int W, int NCH>
-hipError_t launch_decode_fused_wc(const DecBatch& db, const uint16_t* x, int64_t T, int64_t d_in, int y_dtype,
-                                  hipStream_t s) {
-  if (db.rows == 2 * kDecRows) return launch_decode_fused_wcr<W, NCH, 2>(db, x, T, d_in, y_dtype, s);
-  return launch_decode_fused_wcr<W, NCH, 1>(db, x, T, d_in, y_dtype, s);
-}
-
-template <int W>
-hipError_t launch_decode_fused_w(const DecBatch& db, const uint16_t* x, int64_t T, int64_t d_in, int y_dtype,
-                                 hipStream_t s) {
-  static_assert(kFuseChunks == 16, "chunk variants");
-  const int64_t per_lane = (d_in / 8 + 63) / 64;  // 16-byte chunks per lane
-  if (per_lane <= 4) return launch_decode_fused_wc<W, 4>(db, x, T, d_in, y_dtype, s);
-  if (per_lane <= 8) return launch_decode_fused_wc<W, 8>(db, x, T, d_in, y_dtype, s);
-  return launch_decode_fused_wc<W, 16>(db, x, T, d_in, y_dtype, s);
-}
-
-hipError_t launch_decode_fused_multi(int count, const DecodeItem* items, const uint16_t* x, int64_t T, int64_t d_in,
-                                     int y_dtype, hipStream_t s) {
-  if (T == 0) return hipSuccess;
-  DecBatch db;
-  // 32-row blocks from 8 tokens on (gate + up of a 3B layer at 8 tokens: 41.0 -> 39.2 us per
-  // layer; at one token they lost, 34.4 -> 35.0)
-  if (!decode_fused_supported(T, d_in) || !make_dec_batch(count, items, true, T >= 8, db)) return hipErrorInvalidValue;
-  switch (decode_waves(db.begin[count], decode_fused_min_waves(T, d_in))) {
-    case 16: return launch_decode_fused_w<16>(db, x, T, d_in, y_dtype, s);
-    case 8: return launch_decode_fused_w<8>(db, x, T, d_in, y_dtype, s);
-    default: return launch_decode_fused_w<4>(db, x, T, d_in, y_dtype, s);
-  }
-}
-
-hipError_t launch_decode_fused(const uint16_t* codes, const float* gamma, const uint16_t* x, int64_t T, int64_t d_in,
-                               int64_t d_out, void* y, int y_dtype, hipStream_t s) {
-  const DecodeItem it{codes, gamma, d_out, y};
-  return launch_decode_fused_multi(1, &it, x, T, d_in, y_dtype, s);
-}
-
-hipError_t launch_forward_decode_multi(int count, const DecodeItem* items, const int8_t* xq, const float* absmax,
-                                       int64_t T, int64_t d_in, int y_dtype, hipStream_t s) {
+hipError_t launch_decode_codes_many(int count, const DecodeItem* items, bool pairs, const int8_t* xq,
+                                    const float* absmax, int64_t T, int64_t d_in, int y_dtype, hipStream_t s) {
   if (T == 0) return hipSuccess;
   DecBatch db;
   if (T > 64 || d_in % 64 != 0 || !make_dec_batch(count, items, T <= 16 || d_in >= 8192, T > 16, db)) return hipErrorInvalidValue;
-  if (T <= 16) return launch_decode<1>(db, xq, absmax, T, d_in, y_dtype, s);
-  return launch_decode<4>(db, xq, absmax, T, d_in, y_dtype, s);
+  if (T <= 16) return pairs ? launch_decode<1, true>(db, xq, absmax, T, d_in, y_dtype, s)
+                            : launch_decode<1, false>(db, xq, absmax, T, d_in, y_dtype, s);
+  return pairs ? launch_decode<4, true>(db, xq, absmax, T, d_in, y_dtype, s)
+               : launch_decode<4, false>(db, xq, absmax, T, d_in, y_dtype, s);
 }
+
 
 }  // namespace sbl

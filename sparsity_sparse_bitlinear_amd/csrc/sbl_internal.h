@@ -119,12 +119,12 @@ hipError_t launch_forward_sparse24(const uint8_t* plane, const float* gamma, con
 hipError_t launch_pack_sparse24(const uint16_t* codes, int64_t d_out, int64_t d_in, uint8_t* plane,
                                 unsigned long long* bad, hipStream_t s);
 
-// Decode with the activation quantization fused in (x given as bf16).
-bool decode_fused_supported(int64_t T, int64_t d_in);
-hipError_t launch_decode_fused(const uint16_t* codes, const float* gamma, const uint16_t* x, int64_t T, int64_t d_in,
-                               int64_t d_out, void* y, int y_dtype, hipStream_t s);
-// Several matrices sharing one input in one launch (gemm_fwd.hip): the fused
-// decode above, and the decode-size product of x_q (T <= 64, d_in % 64 == 0).
+// Decode-size forward (decode.hip), T <= 64: the weights as the 2-bit code
+// plane (SBL_PLANE_CODES, d_in % 64 == 0) or the pair plane (SBL_PLANE_PAIRS,
+// d_in % 128 == 0; items[i].codes then points at bytes), up to
+// kDecodeMultiMax matrices sharing one input.  fused: x is bf16 and the
+// activation quantization runs in the launch (decode_fused_supported);
+// otherwise x is x_q with absmax.
 constexpr int kDecodeMultiMax = 4;
 struct DecodeItem {
   const uint16_t* codes;
@@ -132,10 +132,32 @@ struct DecodeItem {
   int64_t d_out;
   void* y;
 };
-hipError_t launch_decode_fused_multi(int count, const DecodeItem* items, const uint16_t* x, int64_t T, int64_t d_in,
-                                     int y_dtype, hipStream_t s);
-hipError_t launch_forward_decode_multi(int count, const DecodeItem* items, const int8_t* xq, const float* absmax,
-                                       int64_t T, int64_t d_in, int y_dtype, hipStream_t s);
+bool decode_plane_supported(int format, int64_t T, int64_t d_in);
+bool decode_fused_supported(int64_t T, int64_t d_in);
+bool decode_fused_plane_supported(int format, int64_t T, int64_t d_in);
+hipError_t launch_decode_plane(int format, int count, const DecodeItem* items, bool fused, const void* x,
+                               const float* absmax, int64_t T, int64_t d_in, int y_dtype, hipStream_t s);
+// Pair byte -> its 8 int8 values (bytes 252..255 are not produced: zeros).
+__device__ inline uint2 pair_expand(uint32_t b) {
+  if (b >= 252u) return make_uint2(0u, 0u);
+  const uint32_t pr = b / 9u, cc = b - 9u * pr, d0 = cc / 3u, d1 = cc - 3u * d0;
+  // pairs starting at a come after a (15 - a) / 2 others
+  uint32_t p0 = 0;
+  while (p0 < 6u && (p0 + 1u) * (14u - p0) / 2u <= pr) ++p0;
+  const uint32_t p1 = pr - p0 * (15u - p0) / 2u + p0 + 1u;
+  const unsigned long long v = ((unsigned long long)(d0 == 2u ? 0xFFu : d0) << (8u * p0)) |
+                               ((unsigned long long)(d1 == 2u ? 0xFFu : d1) << (8u * p1));
+  return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+
+// The product of x_q for 17 to 64 tokens on the code plane or the pair plane
+// (gemm_fwd.hip).
+hipError_t launch_decode_codes_many(int count, const DecodeItem* items, bool pairs, const int8_t* xq,
+                                    const float* absmax, int64_t T, int64_t d_in, int y_dtype, hipStream_t s);
+// Code plane -> pair plane (masks keeping at most 2 of 8); groups with more
+// than 2 non-zeros are written as 0 and counted into *bad (may be null).
+hipError_t launch_pack_pairs(const uint16_t* codes, int64_t d_out, int64_t d_in, uint8_t* plane,
+                             unsigned long long* bad, hipStream_t s);
 
 // C[M, N] = alpha * A[M, K] B[N, K]^T, bf16 operands, float32 or bf16 output
 // (gemm_nt.hip).  Only for shapes where gemm_nt_bf16_supported() holds.

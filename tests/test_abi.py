@@ -176,14 +176,18 @@ def test_decode_validation():
     assert f(P, P, P, 4, 250, 256, P, 0, NULL) == SHAPE                         # d_in % 8
     assert f(P, P, P, 17, 256, 256, P, 0, NULL) == UNSUPPORTED                  # T > 16
     assert f(P, P, P, 4, 264, 256, P, 0, NULL) == UNSUPPORTED                   # d_in % 64
-    assert f(P, P, P, 4, 8256, 256, P, 0, NULL) == UNSUPPORTED                  # d_in > 8192
+    assert f(P, P, P, 4, 16448, 256, P, 0, NULL) == UNSUPPORTED                 # T * d_in > 65536
     assert f(P, P, NULL, 4, 256, 256, P, 0, NULL) == INVALID
     assert f(P, P, P_MIS, 4, 256, 256, P, 0, NULL) == INVALID
-    assert f(P, P, P, 8, 8192, 256, P, 0, NULL) == UNSUPPORTED                  # tile over 48 KB
+    assert f(P, P, P, 8, 8192, 256, P, 0, NULL) == UNSUPPORTED                  # tile over 56832 bytes
     s = lib.sbl_decode_supported
     assert s(1, 64) == 1 and s(1, 8192) == 1 and s(5, 8192) == 1 and s(16, 3008) == 1
-    assert s(0, 64) == 0 and s(17, 64) == 0 and s(8, 96) == 0 and s(1, 8256) == 0
-    assert s(6, 8192) == 0 and s(16, 3072) == 0
+    assert s(1, 11008) == 1 and s(4, 11008) == 1 and s(6, 8192) == 1 and s(16, 3072) == 1
+    assert s(0, 64) == 0 and s(17, 64) == 0 and s(8, 96) == 0 and s(1, 65600) == 0
+    assert s(8, 8192) == 0 and s(16, 4096) == 0
+    sp = lib.sbl_decode_plane_supported
+    assert sp(0, 5, 11008) == 1 and sp(1, 5, 11008) == 0 and sp(1, 4, 11008) == 1 and sp(1, 1, 64) == 0
+    assert sp(2, 1, 2048) == 0
 
 
 def test_decode_multi_validation():
@@ -210,6 +214,27 @@ def test_decode_multi_validation():
     assert lib.sbl_decode_multi(3, ip, P, 17, 256, 0, NULL) == UNSUPPORTED        # T > 16 (fused form)
     assert lib.sbl_decode_multi(3, ip, NULL, 4, 256, 0, NULL) == INVALID
     assert lib.sbl_forward_decode_multi(3, ip, P, NULL, 4, 256, 0, NULL) == INVALID
+
+
+def test_pairs_validation():
+    import sparsity_sparse_bitlinear_amd as sbl
+    f = lib.sbl_pack_pairs
+    assert f(P, 256, 12, P, NULL, NULL) == SHAPE                                # d_in % 8
+    assert f(NULL, 256, 256, P, NULL, NULL) == INVALID
+    assert f(P, 256, 256, P_MIS, NULL, NULL) == INVALID
+    assert f(P, 256, 256, P, ctypes.c_void_p(0x10004), NULL) == INVALID        # bad not 8-byte aligned
+    items = (sbl.DecodeItem * 2)(sbl.DecodeItem(0x10000, 0x20000, 2048, 0x30000),
+                                 sbl.DecodeItem(0x40000, 0x50000, 256, 0x60000))
+    ip = ctypes.c_void_p(ctypes.addressof(items))
+    g = lib.sbl_forward_plane_multi
+    assert g(1, 2, ip, P, P, NULL, 0, 256, 0, NULL) == OK                      # T = 0
+    assert g(2, 2, ip, P, P, NULL, 4, 256, 0, NULL) == INVALID                 # unknown format
+    assert g(1, 2, ip, P, P, NULL, 4, 192, 0, NULL) == UNSUPPORTED             # pairs: d_in % 128
+    assert g(1, 2, ip, P, P, NULL, 65, 256, 0, NULL) == UNSUPPORTED            # T > 64
+    assert g(1, 2, ip, NULL, NULL, P, 17, 256, 0, NULL) == UNSUPPORTED         # fused form: T > 16
+    assert g(1, 2, ip, P, P, P, 4, 256, 0, NULL) == INVALID                    # both x_q and x
+    assert g(1, 2, ip, P, NULL, NULL, 4, 256, 0, NULL) == INVALID              # x_q without absmax
+    assert g(1, 2, ip, NULL, NULL, P_MIS, 4, 256, 0, NULL) == INVALID
 
 
 def test_sparse24_validation():

@@ -952,3 +952,94 @@ def test_binding_rejects_mismatched_operands():
     for exc, call in bad:
         with pytest.raises(exc):
             call()
+
+
+# ---------------------------------------------------------------------------
+# pair plane (one byte per group of 8, masks keeping at most 2 of 8): packing
+# against the oracle, and the decode-size forward on it against the code plane
+# and the oracle (exact int32)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [2, 1])
+@pytest.mark.parametrize("d_out,d_in", [(256, 2048), (37, 1024), (11008, 2048), (5, 8)])
+def test_pack_pairs_parity(d_out, d_in, n):
+    W = weight(93, d_out + d_in + n, d_out, d_in)
+    codes, _, _ = sbl.quant_mask_pack(to_dev_bf16(W), n, want_mask=False)
+    plane, bad = sbl.pack_pairs(codes)
+    torch.cuda.synchronize()
+    w_eff, _, _ = oracle.effective_weight(W, n) if d_out * d_in <= 4 << 20 else (None, None, None)
+    if w_eff is not None:
+        np.testing.assert_array_equal(plane.cpu().numpy(), oracle.pack_pairs(w_eff))
+    else:  # large: the plane unpacks to the GPU's own code plane
+        np.testing.assert_array_equal(oracle.unpack_pairs(plane.cpu().numpy()), oracle.unpack_codes(bits16(codes)))
+    assert int(bad.item()) == 0
+
+
+def test_pack_pairs_counts_unrepresentable_groups():
+    # a 6:8 code plane has groups with more than 2 non-zeros: each is counted and written as 0
+    W = weight(94, 0, 64, 256)
+    codes, _, _ = sbl.quant_mask_pack(to_dev_bf16(W), 6, want_mask=False)
+    plane, bad = sbl.pack_pairs(codes)
+    torch.cuda.synchronize()
+    nz = (oracle.unpack_codes(bits16(codes)) != 0).reshape(64, 32, 8).sum(axis=2)
+    assert int(bad.item()) == int((nz > 2).sum()) > 0
+    assert np.all(plane.cpu().numpy()[nz > 2] == 0)
+
+
+def _pairs_mats(shapes, n, seed):
+    Ws, codes_mats, pair_mats = [], [], []
+    for i, (d_o, d_i) in enumerate(shapes):
+        W = weight(seed, 10 * i + n, d_o, d_i)
+        codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), n, want_mask=False)
+        plane, bad = sbl.pack_pairs(codes)
+        Ws.append(W)
+        codes_mats.append((codes, gamma))
+        pair_mats.append((plane, gamma))
+    torch.cuda.synchronize()
+    return Ws, codes_mats, pair_mats
+
+
+PAIR_SHAPES = {"qkv": [(2048, 2048), (256, 2048), (256, 2048)], "down": [(2048, 11008)],
+               "ragged": [(40, 1024), (8200, 1024), (17, 1024)], "small": [(7, 128)]}
+
+
+@pytest.mark.parametrize("n", [2, 1])
+@pytest.mark.parametrize("group", sorted(PAIR_SHAPES))
+@pytest.mark.parametrize("T", [1, 5, 8, 16, 17, 33, 64])
+def test_decode_pairs_parity(T, group, n):
+    shapes = PAIR_SHAPES[group]
+    d_in = shapes[0][1]
+    Ws, cm, pm = _pairs_mats(shapes, n, 95)
+    x = activation(95, T + d_in, T, d_in, dist="student_t4")
+    xd = to_dev_bf16(x)
+    xq, a = sbl.act_quant(xd)
+    for dt in (sbl.I32, sbl.F32, sbl.BF16):
+        yc = sbl.forward_plane_multi(sbl.PLANE_CODES, cm, x_q=xq, absmax=a, out_dtype=dt)
+        yp = sbl.forward_plane_multi(sbl.PLANE_PAIRS, pm, x_q=xq, absmax=a, out_dtype=dt)
+        fused = sbl.decode_plane_supported(sbl.PLANE_PAIRS, T, d_in)
+        yf = sbl.forward_plane_multi(sbl.PLANE_PAIRS, pm, x=xd, out_dtype=dt) if fused else yp
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            assert same_bits(yp[i], yc[i], dt), (i, dt)
+            assert same_bits(yf[i], yc[i], dt), (i, dt)
+    # exact sums against the oracle (the largest matrix on sampled rows)
+    rq, _ = oracle.act_quant(x)
+    yp = sbl.forward_plane_multi(sbl.PLANE_PAIRS, pm, x_q=xq, absmax=a, out_dtype=sbl.I32)
+    torch.cuda.synchronize()
+    for i, W in enumerate(Ws):
+        rows = sample_rows(95, i, W.shape[0], 512)
+        w_eff = oracle.unpack_codes(bits16(cm[i][0]))[rows]
+        # the GPU's code plane equals the oracle's (pinned elsewhere); check it on these rows too
+        w_ref, _, _ = oracle.effective_weight(W, n) if W.size <= 4 << 20 else (None, None, None)
+        if w_ref is not None:
+            np.testing.assert_array_equal(w_eff, w_ref[rows])
+        acc_ref = oracle.forward_acc(w_eff, rq)
+        np.testing.assert_array_equal(yp[i].cpu().numpy()[:, rows], acc_ref)
+
+
+def test_decode_pairs_moves_half_the_code_bytes():
+    # the plane a 2:8 decode streams: d_in / 8 bytes per row against d_in / 4
+    W = weight(96, 0, 2048, 11008)
+    codes, _, _ = sbl.quant_mask_pack(to_dev_bf16(W), 2, want_mask=False)
+    plane, bad = sbl.pack_pairs(codes)
+    assert plane.numel() * plane.element_size() * 2 == codes.numel() * codes.element_size()
