@@ -39,32 +39,35 @@ __device__ __forceinline__ ActScale act_scale(float a) {
   return s;
 }
 
+// Eight bf16 (one 16-byte chunk) -> eight int8, element order kept.
 // Fast path: qf = fl(x' * fl(127 / a')) differs from the exact quotient
 // q = 127 x' / a' by less than |q| 2^-23 <= 2^-16 (|q| <= 127).  When qf is
 // more than 2^-14 away from a half-integer, rint(qf) is therefore the integer
-// nearest to q; otherwise (ties included) the element takes the division path,
-// which is exact as stated above.
-__device__ __forceinline__ int quant_one(uint32_t h16, int k, float as, float c) {
-  const float xs = ldexpf(__uint_as_float(h16 << 16), k);
-  const float qf = xs * c;
-  float r = rintf(qf);
-  if (__builtin_expect(fabsf(qf - r) > 0.5f - 0x1p-14f, 0)) r = rintf((127.0f * xs) / as);
-  return (int)r;
-}
-
-// Four bf16 (two words) -> four int8 in one word, element order kept.
-__device__ __forceinline__ uint32_t quant_word_pair(uint32_t w0, uint32_t w1, int k, float as, float c) {
-  const int q0 = quant_one(w0 & 0xFFFFu, k, as, c);
-  const int q1 = quant_one(w0 >> 16, k, as, c);
-  const int q2 = quant_one(w1 & 0xFFFFu, k, as, c);
-  const int q3 = quant_one(w1 >> 16, k, as, c);
-  return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
-         ((uint32_t)(q3 & 0xFF) << 24);
-}
-
-// Eight bf16 (one 16-byte chunk) -> eight int8.
+// nearest to q.  One test per chunk: if any of the eight is that close (ties
+// included), all eight take the division path, which is exact for every
+// element as stated above, so the others keep the value the fast path gives.
 __device__ __forceinline__ uint2 quant_chunk(uint4 v, int k, float as, float c) {
-  return make_uint2(quant_word_pair(v.x, v.y, k, as, c), quant_word_pair(v.z, v.w, k, as, c));
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float xs[8], r[8];
+  bool near = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t h16 = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+    xs[e] = ldexpf(__uint_as_float(h16 << 16), k);
+    const float qf = xs[e] * c;
+    r[e] = rintf(qf);
+    near = near || fabsf(qf - r[e]) > 0.5f - 0x1p-14f;
+  }
+  if (__builtin_expect(near, 0)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = rintf((127.0f * xs[e]) / as);
+  }
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    out[h] = ((uint32_t)((int)r[4 * h] & 0xFF)) | ((uint32_t)((int)r[4 * h + 1] & 0xFF) << 8) |
+             ((uint32_t)((int)r[4 * h + 2] & 0xFF) << 16) | ((uint32_t)((int)r[4 * h + 3] & 0xFF) << 24);
+  return make_uint2(out[0], out[1]);
 }
 
 }  // namespace sbl

@@ -142,9 +142,38 @@ __global__ __launch_bounds__(64 * W) void k_decode(const void* __restrict__ xin,
     }
   };
 
-  // The first group's weight loads go out before the activations are staged.
+  // XS == 2: this thread's activation chunks (kc consecutive 16-byte chunks, so that a
+  // thread's chunks mostly lie in one row) are loaded first, then the first group's weights;
+  // vector memory returns in issue order, so the quantization below waits for the
+  // activations only and runs while the weight bytes are in flight.
+  uint4 xv[XS == 2 ? kFuseRegs : 1];
+  int kc = 0;
+  if constexpr (XS == 2) {
+    const int total = T * (d_in >> 3);
+    kc = (total + 64 * W - 1) / (64 * W);  // <= kFuseRegs (checked by the launcher)
+    const auto xr0 = make_rsrc(xin, clamp_bytes((int64_t)total * 16));
+#pragma unroll
+    for (int i = 0; i < kFuseRegs; ++i) {
+      const int c = tid * kc + i;
+      xv[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < kc) xv[i] = bload16(xr0, c < total ? (uint32_t)c * 16u : kOOB);  // block-uniform test
+    }
+  }
   TileRef ti = tile_ref(blockIdx.x);
-  if (blockIdx.x < p.groups && qbeg < qend) issue(ti, qbeg);
+  if constexpr (XS == 2) {
+    // exactly kQ loads whatever the wave's share (slots past it read zero without touching
+    // memory), so that the compiler can wait for the activations with vmcnt(kQ)
+    const bool on = blockIdx.x < p.groups && qbeg < qend;
+    const int nq = on ? min(kQ, qend - qbeg) : 0;
+#pragma unroll
+    for (int j = 0; j < kQ; ++j) {
+      const int chunk = 4 * (qbeg + j) + q;
+      cw[j] = bload16(ti.br, j < nq && chunk < p.nchunk && r16 < ti.rows ? (uint32_t)(r16 * row_bytes + 16 * chunk)
+                                                                         : kOOB);
+    }
+  } else {
+    if (blockIdx.x < p.groups && qbeg < qend) issue(ti, qbeg);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- set-up: pair table, activation tile and token scales
@@ -152,34 +181,62 @@ __global__ __launch_bounds__(64 * W) void k_decode(const void* __restrict__ xin,
     if (tid < 256) ((uint2*)(smem + L.table))[tid] = pair_expand((uint32_t)tid);
   }
   if constexpr (XS == 2) {
-    // x bf16 [T][d_in]: T * d_in / 8 chunks over the block, kept in registers
+    // x bf16 [T][d_in]: T * d_in / 8 chunks over the block, kc consecutive ones per thread
     const int nch = d_in >> 3, total = T * nch;
     if (tid < T) rmax[tid] = 0u;
     __syncthreads();
-    uint4 xv[kFuseRegs];
-#pragma unroll
-    for (int i = 0; i < kFuseRegs; ++i) {
-      const int c = tid + 64 * W * i;
-      xv[i] = c < total ? ((const uint4*)xin)[c] : make_uint4(0u, 0u, 0u, 0u);
-    }
-#pragma unroll
-    for (int i = 0; i < kFuseRegs; ++i) {
-      const int c = tid + 64 * W * i;
-      if (c < total) {
-        const uint32_t m = max(max(max_mag2(xv[i].x), max_mag2(xv[i].y)), max(max_mag2(xv[i].z), max_mag2(xv[i].w)));
-        atomicMax(&rmax[c / nch], m);  // integer maximum: the order does not matter
-      }
-    }
-    __syncthreads();
-    if (tid < T) amax[tid] = __uint_as_float(rmax[tid] << 16);
-#pragma unroll
-    for (int i = 0; i < kFuseRegs; ++i) {
-      const int c = tid + 64 * W * i;
-      if (c < total) {
-        const int t = c / nch, j = c - t * nch;
+    const auto cmax = [&](const uint4& v) {
+      return max(max(max_mag2(v.x), max_mag2(v.y)), max(max_mag2(v.z), max_mag2(v.w)));
+    };
+    if (kc == 1) {  // (block-uniform) one chunk per thread: chunk tid
+      const bool in = tid < total;
+      const int t = in ? tid / nch : 0;
+      if (in) atomicMax(&rmax[t], cmax(xv[0]));  // integer maximum: the order does not matter
+      __syncthreads();
+      if (tid < T) amax[tid] = __uint_as_float(rmax[tid] << 16);
+      if (in) {
         const uint32_t m = rmax[t];
         const ActScale qs = act_scale(m ? __uint_as_float(m << 16) : 1.0f);
-        *(uint2*)(xs + t * ld + 8 * j) = m ? quant_chunk(xv[i], qs.k, qs.as, qs.c) : make_uint2(0u, 0u);
+        *(uint2*)(xs + t * ld + 8 * (tid - t * nch)) = m ? quant_chunk(xv[0], qs.k, qs.as, qs.c) : make_uint2(0u, 0u);
+      }
+    } else {
+      {  // row maxima: a running maximum per thread, one LDS atomic per row it touches
+        uint32_t m = 0;
+        int trow = -1;
+#pragma unroll
+        for (int i = 0; i < kFuseRegs; ++i) {
+          const int c = tid * kc + i;
+          if (i < kc && c < total) {
+            const int t = c / nch;
+            if (t != trow) {
+              if (trow >= 0) atomicMax(&rmax[trow], m);
+              trow = t;
+              m = 0;
+            }
+            m = max(m, cmax(xv[i]));
+          }
+        }
+        if (trow >= 0) atomicMax(&rmax[trow], m);
+      }
+      __syncthreads();
+      if (tid < T) amax[tid] = __uint_as_float(rmax[tid] << 16);
+      {  // the row scale set-up once per row a thread touches
+        int srow = -1;
+        uint32_t m = 0;
+        ActScale qs = {0, 1.0f, 1.0f};
+#pragma unroll
+        for (int i = 0; i < kFuseRegs; ++i) {
+          const int c = tid * kc + i;
+          if (i < kc && c < total) {
+            const int t = c / nch, j = c - t * nch;
+            if (t != srow) {
+              srow = t;
+              m = rmax[t];
+              qs = act_scale(m ? __uint_as_float(m << 16) : 1.0f);
+            }
+            *(uint2*)(xs + t * ld + 8 * j) = m ? quant_chunk(xv[i], qs.k, qs.as, qs.c) : make_uint2(0u, 0u);
+          }
+        }
       }
     }
   } else if constexpr (XS == 1) {

@@ -623,6 +623,35 @@ def test_decode_fused_zero_and_tiny_rows():
     assert_y_close(y, y_ref, acc_ref)
 
 
+@pytest.mark.parametrize("T,d_in", [(16, 448), (9, 2944), (3, 11008), (16, 64)])
+def test_decode_fused_row_maxima_positions(T, d_in):
+    # the in-launch row maxima are reduced per wave over runs of 64 consecutive 16-byte
+    # chunks that may cross row ends: each row's largest magnitude is placed at its first
+    # chunk, its last chunk, a chunk at a 64-chunk boundary or in between, and x_q (hence
+    # the int32 sums) must equal the two-call path and the oracle
+    d_out = 48
+    nch = d_in // 8
+    W = weight(66, T, d_out, d_in)
+    x = activation(66, d_in + T, T, d_in)
+    big = f32_to_bf16_bits(np.array([5.0e3, -7.5e3], np.float32))
+    for t in range(T):
+        c = t * nch
+        choice = [c, c + nch - 1, ((c // 64) + 1) * 64, c + nch // 2][t % 4]
+        if not c <= choice < c + nch:
+            choice = c + (t * 13) % nch
+        x[t, 8 * (choice - c) + t % 8] = big[t % 2]
+    assert sbl.decode_supported(T, d_in)
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+    acc_ref, _ = ref_forward(W, x, 6)
+    xd = to_dev_bf16(x)
+    xq, a = sbl.act_quant(xd)
+    two = sbl.forward(codes, gamma, xq, a, out_dtype=sbl.I32)
+    one = sbl.decode(codes, gamma, xd, out_dtype=sbl.I32)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+    np.testing.assert_array_equal(one.cpu().numpy(), acc_ref)
+
+
 @pytest.mark.parametrize("T", [1, 8, 16])
 @pytest.mark.parametrize("name,d_out,d_in", [("gate", 11008, 2048), ("q", 2048, 2048), ("k", 256, 2048)])
 def test_decode_fused_full_size(T, name, d_out, d_in):
