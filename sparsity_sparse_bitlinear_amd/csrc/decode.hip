@@ -257,9 +257,11 @@ __global__ __launch_bounds__(64 * W) void k_decode(const void* __restrict__ xin,
     const bool tile_ok = ti.rows > 0;
     const int item = ti.item, row0 = ti.row0, rows = ti.rows;
     const int d_out = p.d_out[item];
-    v4i acc[NTT];
+    // two accumulators per token tile, alternating over the instructions, so that
+    // consecutive matrix instructions do not wait on each other (integer sums: exact)
+    v4i acc[NTT], acc2[NTT];
 #pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[tt] = (v4i){0, 0, 0, 0};
+    for (int tt = 0; tt < NTT; ++tt) acc[tt] = acc2[tt] = (v4i){0, 0, 0, 0};
 
     // rounds of up to kQ chunk quads (the first one already in flight)
     for (int qb = qbeg; qb < qend; qb += kQ) {
@@ -274,41 +276,44 @@ __global__ __launch_bounds__(64 * W) void k_decode(const void* __restrict__ xin,
         const int chunk = min(4 * (qb + j) + q, p.nchunk - 1);  // past the row: zero weights, any x
 #pragma unroll
         for (int h = 0; h < U; h += UH) {
-          v4i bx[UH][NTT];
-          if constexpr (XS == 0) {  // this half's token operands from global memory, issued together
+          // this part's token operands (global memory or the LDS tile) and weight operands
+          // (expanded codes, or pair-table entries from LDS), all read before its first
+          // matrix instruction so that their latencies overlap
+          v4i bx[UH][NTT], av[UH];
 #pragma unroll
-            for (int u = 0; u < UH; ++u)
-#pragma unroll
-              for (int tt = 0; tt < NTT; ++tt) {
-                const int t = 16 * tt + r16;
-                bx[u][tt] = __builtin_bit_cast(
-                    v4i, bload16(xr, t < T ? (uint32_t)(t * d_in + chunk * KC + 16 * (h + u)) : kOOB));
-              }
-          }
-#pragma unroll
-          for (int u = 0; u < UH; ++u) {
-            v4i a;
-            if constexpr (PAIRS) {
-              const uint32_t w = word_of(cw[j], (h + u) >> 1) >> (16 * ((h + u) & 1));
-              const uint2 e0 = table[w & 0xFFu], e1 = table[(w >> 8) & 0xFFu];
-              a = (v4i){(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
-            } else {
-              const uint32_t w = word_of(cw[j], h + u);
-              a = (v4i){(int)codes4(w), (int)codes4(w >> 8), (int)codes4(w >> 16), (int)codes4(w >> 24)};
-            }
-            const int kb = chunk * KC + 16 * (h + u);
+          for (int u = 0; u < UH; ++u)
 #pragma unroll
             for (int tt = 0; tt < NTT; ++tt) {
               const int t = 16 * tt + r16;
-              v4i b;
-              if constexpr (XS > 0) b = t < T ? *(const v4i*)(xs + t * ld + kb) : (v4i){0, 0, 0, 0};
-              else b = bx[u][tt];
-              acc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[tt], 0, 0, 0);
+              const int kb = chunk * KC + 16 * (h + u);
+              if constexpr (XS == 0)
+                bx[u][tt] = __builtin_bit_cast(v4i, bload16(xr, t < T ? (uint32_t)(t * d_in + kb) : kOOB));
+              else
+                bx[u][tt] = t < T ? *(const v4i*)(xs + t * ld + kb) : (v4i){0, 0, 0, 0};
+            }
+#pragma unroll
+          for (int u = 0; u < UH; ++u) {
+            if constexpr (PAIRS) {
+              const uint32_t w = word_of(cw[j], (h + u) >> 1) >> (16 * ((h + u) & 1));
+              const uint2 e0 = table[w & 0xFFu], e1 = table[(w >> 8) & 0xFFu];
+              av[u] = (v4i){(int)e0.x, (int)e0.y, (int)e1.x, (int)e1.y};
+            } else {
+              const uint32_t w = word_of(cw[j], h + u);
+              av[u] = (v4i){(int)codes4(w), (int)codes4(w >> 8), (int)codes4(w >> 16), (int)codes4(w >> 24)};
             }
           }
+#pragma unroll
+          for (int u = 0; u < UH; ++u)
+#pragma unroll
+            for (int tt = 0; tt < NTT; ++tt) {
+              if (u & 1) acc2[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[u], bx[u][tt], acc2[tt], 0, 0, 0);
+              else acc[tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(av[u], bx[u][tt], acc[tt], 0, 0, 0);
+            }
         }
       }
     }
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[tt] += acc2[tt];
     // the next group's first loads go out before this one's sums are stored
     if (g + (int)gridDim.x < p.groups) {
       ti = tile_ref(g + gridDim.x);
@@ -436,11 +441,9 @@ hipError_t launch_xs(const DecPlan& p, int xs, const void* x, const float* absma
 template <int OUT, int W, bool PAIRS>
 hipError_t launch_ntt(const DecPlan& p, int xs, int ntt, const void* x, const float* absmax, int64_t T, int64_t d_in,
                       int grid, size_t lds, hipStream_t s) {
-  switch (ntt) {
-    case 1: return launch_xs<OUT, W, 1, PAIRS>(p, xs, x, absmax, T, d_in, grid, lds, s);
-    case 2: return launch_xs<OUT, W, 2, PAIRS>(p, xs, x, absmax, T, d_in, grid, lds, s);
-    default: return launch_xs<OUT, W, 4, PAIRS>(p, xs, x, absmax, T, d_in, grid, lds, s);
-  }
+  // one 16-token tile: more than 16 tokens take the row-tile kernel of the forward
+  if (ntt != 1) return hipErrorInvalidValue;
+  return launch_xs<OUT, W, 1, PAIRS>(p, xs, x, absmax, T, d_in, grid, lds, s);
 }
 
 template <int OUT, bool PAIRS>
@@ -514,7 +517,7 @@ hipError_t launch_decode_plane(int format, int count, const DecodeItem* items, b
   p.per = (nquad + wpt - 1) / wpt;
   const int tpg = W / wpt;
   p.groups = (int)((nt + tpg - 1) / tpg);
-  const int ntt = T <= 16 ? 1 : T <= 32 ? 2 : 4;
+  const int ntt = 1;  // T <= 16 from here on (fused: checked above; otherwise the kernel above took T > 16)
   int xs = fused ? 2 : 1;  // x_q staged in LDS when the tile fits, else read from global memory
   DecLds L = dec_lds((int)T, (int)d_in, W, ntt, pairs, true);
   if (!fused && L.total > kLdsMax) {
