@@ -68,6 +68,9 @@ def parse():
                     help="only measure the ceilings (int8 and bf16 matrix instructions on register operands, "
                          "HBM read and copy) and print them as one JSON line")
     ap.add_argument("--no-peaks", action="store_true", help="skip the measured ceilings in the other modes")
+    ap.add_argument("--launch-floor", action="store_true",
+                    help="only time one launch of the library's streaming-read kernel per size (1 KB to 128 MB, "
+                         "in a captured graph over distinct buffers) and print one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -102,6 +105,14 @@ def main():
         return
     if args.peaks:
         print(json.dumps({"metric": "measured ceilings", "n_gpus": 1, **measured_peaks()}), flush=True)
+        return
+    if args.launch_floor:
+        sizes = [1 << 14, 1 << 20, 2 << 20, 4 << 20, 8 << 20, 11272192, 16 << 20, 32 << 20, 64 << 20, 128 << 20]
+        rows = [{"bytes": n, "us_per_launch": round(read_floor_us(n), 3)} for n in sizes]
+        for r in rows:
+            r["GBps"] = round(r["bytes"] / r["us_per_launch"] / 1e3, 1)
+        print(json.dumps({"metric": "time of one dependent launch of the streaming-read kernel (captured graph)",
+                          "unit": "us", "n_gpus": 1, "results": rows}), flush=True)
         return
     wl = WORKLOADS[args.workload]
     if args.variants:
@@ -470,14 +481,17 @@ def _decode_case(args, wl, sbl, torch, up, activation, groups, layers, plane_nam
                           a=torch.empty((T,), dtype=torch.float32, device=dev),
                           ys=[torch.empty((T, wl.linears[i].d_out), dtype=torch.bfloat16, device=dev) for i in g]))
 
+    def run_group(g, b, mats):
+        gm = [mats[i] for i in g]
+        if b["fused"]:
+            sbl.forward_plane_multi(plane_fmt, gm, x=b["x"], out_dtype=sbl.BF16, ys=b["ys"])
+        else:
+            sbl.act_quant(b["x"], x_q=b["x_q"], absmax=b["a"])
+            sbl.forward_plane_multi(plane_fmt, gm, x_q=b["x_q"], absmax=b["a"], out_dtype=sbl.BF16, ys=b["ys"])
+
     def layer(mats):
         for g, b in zip(groups, gbufs):
-            gm = [mats[i] for i in g]
-            if b["fused"]:
-                sbl.forward_plane_multi(plane_fmt, gm, x=b["x"], out_dtype=sbl.BF16, ys=b["ys"])
-            else:
-                sbl.act_quant(b["x"], x_q=b["x_q"], absmax=b["a"])
-                sbl.forward_plane_multi(plane_fmt, gm, x_q=b["x_q"], absmax=b["a"], out_dtype=sbl.BF16, ys=b["ys"])
+            run_group(g, b, mats)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -510,7 +524,69 @@ def _decode_case(args, wl, sbl, torch, up, activation, groups, layers, plane_nam
     if peaks:
         r["frac_hbm_measured"] = round((code_bytes + io_bytes) / (us * 1e-6) / 1e9 / peaks["read_GBps"], 4)
     del graph
+    # each input group alone (same copies), beside one launch of the streaming-read kernel over
+    # the group's plane bytes: the floor of a dependent launch that moves those bytes
+    r["groups"] = []
+    for g, b in zip(groups, gbufs):
+        gus = graph_us(lambda: [run_group(g, b, mats) for mats in layers], reps=args.steps, warmup=args.warmup)
+        gbytes = sum(layers[0][i][0].numel() * layers[0][i][0].element_size() for i in g)
+        r["groups"].append({"group": "+".join(wl.linears[i].name for i in g), "launches": 1 if b["fused"] else 2,
+                            "us": round(gus / copies, 3), "plane_bytes": gbytes,
+                            "read_floor_us": round(read_floor_us(gbytes), 3)})
     return r
+
+
+def graph_us(fn, reps: int = 20, warmup: int = 3) -> float:
+    """Time of one replay of fn captured in a HIP graph (fn's launches go to the current stream)."""
+    import torch
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()  # warm up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def read_floor_us(nbytes: int) -> float:
+    """Time per launch of the library's streaming-read kernel (sbl_peak_read) over nbytes, each
+    launch of a captured graph reading its own slice of a buffer larger than the last-level cache:
+    the floor of one dependent launch that moves nbytes from HBM."""
+    import math
+
+    import torch
+
+    import sparsity_sparse_bitlinear_amd as sbl
+
+    nbytes = max(16, nbytes // 16 * 16)
+    copies = max(4, min(64, math.ceil(600e6 / nbytes)))
+    buf = torch.ones((copies * nbytes // 4 + 4,), dtype=torch.float32, device="cuda")
+    word = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    base = buf.data_ptr()
+
+    def run():
+        for c in range(copies):
+            sbl._check(sbl.lib.sbl_peak_read(base + c * nbytes, nbytes, sbl._ptr(word), sbl._stream()),
+                       "sbl_peak_read")
+
+    us = graph_us(run) / copies
+    del buf
+    torch.cuda.synchronize()
+    return us
 
 
 def run_decode(args, wl, copies: int = 16):
