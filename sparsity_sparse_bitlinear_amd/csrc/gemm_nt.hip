@@ -32,17 +32,11 @@ using namespace gemm;
 // compared with a 256 x 128 tile, which is what the L2-to-CU path can feed.
 
 constexpr int kNT = 512;                  // threads per block
-constexpr int kBNn = 256;                 // block cols (N)
-constexpr int kStages = 2;
-constexpr int kStageA = kBM * kRowK;      // 32 KB
-constexpr int kStageB = kBNn * kRowK;     // 32 KB
-constexpr int kStage = kStageA + kStageB; // 64 KB
-constexpr int kDmaA = kBM * 8 / kNT;      // 4
-constexpr int kDmaB = kBNn * 8 / kNT;     // 4
-constexpr int kDmaStep = kDmaA + kDmaB;
+constexpr int kBNn = 256;                 // block cols (N) of the square tile (host-side tile counts)
+constexpr int kStages = 2;                // LDS stages of one K step each
 constexpr int kKStep = kRowK / 2;         // 64 bf16 per K step
-constexpr int kStageBC = kBNn * 16;       // 4 KB: B as codes, 16 bytes per row and K step
-constexpr int kStageBQ = kKStep * kBNn;   // 16 KB: B as int8, 64 rows k x 256 columns n
+// Per K step a stage holds kBM rows of A (128 bytes each) and kBNn rows of B:
+// 128 bytes of bf16, 16 bytes of codes (BC) or, for BQ, 64 rows k x kBNn int8.
 
 // B as codes (BC): row n of B holds, per K step of 64, 16 bytes = 4 words;
 // word 2 h + w serves lane half h (k groups 2 ks + h of the four 16-wide
@@ -98,24 +92,42 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 // column i of the 8 rows.  The swizzle spreads those 8 rows over 8 even (or,
 // for the odd chunk the neighbouring group reads, 8 odd) chunk positions, so
 // two groups never share a bank.
-template <int OUT, bool WTA, bool BC, bool AR, bool BR, bool BQ>
+//
+// BN: block columns, 256 or 512 (codes B only); the block has BM = 65536 / BN
+// rows, so the accumulators stay 128 per lane with 8 waves of 128 x 64 (2 x 4
+// waves, or 1 x 8).  With the 2-bit B of dX a K step then loads 16 KB of A and
+// 8 KB of codes instead of 32 KB and 4 KB: a third fewer bytes per product.
+template <int BN, int OUT, bool WTA, bool BC, bool AR, bool BR, bool BQ>
 __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restrict__ A,
                                                               const uint16_t* __restrict__ B, int M, int N, int K,
                                                               int kps, const float* __restrict__ alpha_p,
                                                               void* __restrict__ C, uint16_t* __restrict__ AT,
                                                               int at_ld, const float* __restrict__ wscale,
                                                               int kb_rows) {
+  static_assert(BN == 256 || (BN == 512 && BC), "512-column blocks take the code-plane B only");
+  constexpr int kBM = 65536 / BN, kBNn = BN;  // (hide the square tile's constants)
+  constexpr int kWavesN = BN / 64;            // waves along N (each 64 columns)
+  constexpr int kStageA = kBM * kRowK;
+  constexpr int kStageB = kBNn * kRowK;
+  constexpr int kStageBC = kBNn * 16;
+  constexpr int kStageBQ = kKStep * kBNn;
+  constexpr int kDmaA = kBM * 8 / kNT;        // A loads (1 KB) per wave and K step
+  constexpr int kDmaB = kBNn * 8 / kNT;
+  constexpr int kDmaStep = kDmaA + kDmaB;
   constexpr int kSt = kStageA + (BC ? kStageBC : BQ ? kStageBQ : kStageB);
-  constexpr int kDmaBw = BC ? 1 : BQ ? 2 : kDmaB;  // B loads per wave and step (BC: waves 0-3 only)
-  __shared__ __attribute__((aligned(1024))) char lds[kStages * kSt];
+  constexpr int kDmaBw = BC ? 1 : BQ ? 2 : kDmaB;  // B loads per wave and step (BC: waves below kWavesN only)
+  // the operand stages, which the epilogue reuses as 8 KB of staging per wave
+  constexpr int kLdsBytes = kStages * kSt > 8 * 8192 ? kStages * kSt : 8 * 8192;
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS targets live in SGPRs
-  const int wm0 = (wave >> 2) * kWM;
-  const int wn0 = (wave & 3) * kWN;
+  const int wm0 = (wave / kWavesN) * kWM;
+  const int wn0 = (wave % kWavesN) * kWN;
   int mt, nt;
-  xcd_tile_grouped(blockIdx.x, (M + kBM - 1) / kBM, (N + kBNn - 1) / kBNn, 4, mt, nt);
+  // 32 tiles resident per XCD: 4 x 8 of 256 x 256 tiles, 8 x 4 of 128 x 512 ones
+  xcd_tile_grouped(blockIdx.x, (M + kBM - 1) / kBM, (N + kBNn - 1) / kBNn, BN == 256 ? 4 : 8, mt, nt);
   const int m0 = mt * kBM;
   const int n0 = nt * kBNn;
   const int kbeg = blockIdx.y * kps;
@@ -146,7 +158,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     }
   }
   if constexpr (BC) {
-    b_off[0] = (uint32_t)((64 * (wave & 3) + lane) * b_row);  // row 64 w + lane, one 16-byte piece
+    b_off[0] = (uint32_t)((64 * (wave % kWavesN) + lane) * b_row);  // row 64 w + lane, one 16-byte piece
     b_k[0] = 0;
   } else if constexpr (BQ) {
 #pragma unroll
@@ -191,7 +203,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       dma16(ar, sa + 1024 * (kDmaA * wave + i), ktail && k0 + a_k[i] >= kend ? kOOB : a_off[i],
             (uint32_t)k0 * a_soff_per_k);
     if constexpr (BC) {
-      if (wave < 4) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
+      if (wave < kWavesN) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
     } else if constexpr (BQ) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
       dma16(ar, sa + 1024 * (kDmaA * wave + idx), ktail && k0 + a_k[idx] >= kend ? kOOB : a_off[idx],
             (uint32_t)k0 * a_soff_per_k);
     } else if constexpr (BC) {
-      if (wave < 4) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
+      if (wave < kWavesN) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
     } else if constexpr (BQ) {
       const int i = idx - kDmaA;
       dma16(br, sb + 1024 * (2 * wave + i), k0 + b_k[i] >= kb_rows ? kOOB : b_off[i], (uint32_t)k0 * (uint32_t)N);
@@ -298,7 +310,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     }
   };
   // Transposed copy of the A tile of stage st (K step k0): wave w takes 16
-  // K-columns (16 (w % 4) ..) and 128 rows (128 (w / 4) ..) in 4 rounds of 32;
+  // K-columns (16 (w % 4) ..) and kBM / 2 rows (from kBM / 2 (w / 4)) in rounds of 32;
   // in each round its 16-lane group g reads rows 8 g .. 8 g + 7 with two
   // ds_read_b64_tr_b16 (lane i: 4 rows of column i each) and stores them as
   // one 16-byte run of AT row k0 + column.
@@ -306,12 +318,13 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   __shared__ __attribute__((aligned(16))) float wsc[WTA ? kBM : 4];
   auto write_at = [&](int st, int k0) {
     const char* a = lds + st * kSt;
-    const int kb = 16 * (wave & 3), tb0 = 128 * (wave >> 2);
+    constexpr int kRounds = kBM / 64;  // 32-row rounds of each wave
+    const int kb = 16 * (wave & 3), tb0 = 32 * kRounds * (wave >> 2);
     const int g = lane >> 4, q = lane & 15;
     const auto atr = make_rsrc(AT, clamp_bytes((int64_t)at_ld * K * 2));
     const int kc = kb + 4 * (q & 3);                    // first of the 4 columns lane q addresses
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < kRounds; ++r) {
       const int t0 = tb0 + 32 * r + 8 * g;              // first of this group's 8 rows
       v4s part[2];
 #pragma unroll
@@ -383,7 +396,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   issue(0, 0);
   issue(min(1, last), 1);
   if constexpr (BC) {  // (lgkmcnt too: the scale table above is read after the barrier)
-    if (wave < 4) wait_vmcnt_lgkm0<kDmaA + 1>();
+    if (wave < kWavesN) wait_vmcnt_lgkm0<kDmaA + 1>();
     else wait_vmcnt_lgkm0<kDmaA>();
   } else {
     wait_vmcnt<kNDma>();  // this wave's loads of step 0 (those of step 1 may be in flight)
@@ -567,8 +580,8 @@ hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, 
   if (AT && splits != 1) return hipErrorInvalidValue;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
   const bool f32 = out_dtype == SBL_F32;
-  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, false, false, false, false> : k_gemm_nt_bf16<SBL_BF16, true, false, false, false, false>)
-                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, false, false, false, false> : k_gemm_nt_bf16<SBL_BF16, false, false, false, false, false>);
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<256, SBL_F32, true, false, false, false, false> : k_gemm_nt_bf16<256, SBL_BF16, true, false, false, false, false>)
+                 : (f32 ? k_gemm_nt_bf16<256, SBL_F32, false, false, false, false, false> : k_gemm_nt_bf16<256, SBL_BF16, false, false, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, B, (int)M, (int)N, (int)K, (int)k_per_split, alpha, C, AT,
                      (int)at_ld, nullptr, 0);
   return hipGetLastError();
@@ -579,7 +592,7 @@ hipError_t launch_gemm_nt_runs(const uint16_t* A, bool a_runs, const uint16_t* B
   if (splits < 1) splits = 1;
   if (splits == 1) k_per_split = K;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
-  auto kern = a_runs ? k_gemm_nt_bf16<SBL_F32, false, false, true, true, false> : k_gemm_nt_bf16<SBL_F32, false, false, false, true, false>;
+  auto kern = a_runs ? k_gemm_nt_bf16<256, SBL_F32, false, false, true, true, false> : k_gemm_nt_bf16<256, SBL_F32, false, false, false, true, false>;
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, Brun, (int)M, (int)N, (int)K, (int)k_per_split, nullptr, C, nullptr,
                      0, nullptr, 0);
   return hipGetLastError();
@@ -596,7 +609,7 @@ hipError_t launch_gemm_nt_q(const uint16_t* Arun, const int8_t* Bq, int64_t M, i
   if (splits < 1) splits = 1;
   if (splits == 1) k_per_split = K;
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
-  hipLaunchKernelGGL((k_gemm_nt_bf16<SBL_F32, false, false, true, false, true>), grid, block, 0, s, Arun,
+  hipLaunchKernelGGL((k_gemm_nt_bf16<256, SBL_F32, false, false, true, false, true>), grid, block, 0, s, Arun,
                      (const uint16_t*)Bq, (int)M, (int)N, (int)K, (int)k_per_split, nullptr, (void*)C, nullptr, 0,
                      nullptr, (int)kb_rows);
   return hipGetLastError();
@@ -605,10 +618,11 @@ hipError_t launch_gemm_nt_q(const uint16_t* Arun, const int8_t* Bq, int64_t M, i
 hipError_t launch_gemm_nt_codes(const uint16_t* A, const uint32_t* Bc, int64_t M, int64_t N, int64_t K,
                                 const float* alpha, void* C, int out_dtype, hipStream_t s, uint16_t* AT,
                                 int64_t at_ld, const float* wscale) {
-  const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N)), block(kNT);
+  // 128 x 512 blocks: a third fewer operand bytes per product than 256 x 256 with a 2-bit B
+  const dim3 grid((unsigned)(((M + 127) / 128) * ((N + 511) / 512))), block(kNT);
   const bool f32 = out_dtype == SBL_F32;
-  auto kern = AT ? (f32 ? k_gemm_nt_bf16<SBL_F32, true, true, false, false, false> : k_gemm_nt_bf16<SBL_BF16, true, true, false, false, false>)
-                 : (f32 ? k_gemm_nt_bf16<SBL_F32, false, true, false, false, false> : k_gemm_nt_bf16<SBL_BF16, false, true, false, false, false>);
+  auto kern = AT ? (f32 ? k_gemm_nt_bf16<512, SBL_F32, true, true, false, false, false> : k_gemm_nt_bf16<512, SBL_BF16, true, true, false, false, false>)
+                 : (f32 ? k_gemm_nt_bf16<512, SBL_F32, false, true, false, false, false> : k_gemm_nt_bf16<512, SBL_BF16, false, true, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, (const uint16_t*)Bc, (int)M, (int)N, (int)K, (int)K, alpha, C, AT,
                      (int)at_ld, wscale, 0);
   return hipGetLastError();
