@@ -12,9 +12,9 @@
 //                              (both transposed once per call, token-contiguous)
 //
 // Operand tiles move from global memory to LDS with direct-to-LDS buffer loads
-// (no register staging and no LDS store instructions) through two LDS stages
-// of one K step (64 bf16) each: a step's loads are issued one step ahead, in
-// the middle of the previous step.  Each lane of a direct load picks the
+// (no register staging and no LDS store instructions) through two or three LDS
+// stages of one K step (64 bf16) each: a step's loads are issued one or two
+// steps ahead, in the middle of an earlier step.  Each lane of a direct load picks the
 // global chunk that belongs at its LDS position, which is how the swizzle
 // (see swz8) is applied without a store.  128-byte row pieces per K step let
 // every load cover whole cache lines.
@@ -25,6 +25,11 @@ namespace sbl {
 namespace {
 
 using namespace gemm;
+
+template <int S>
+struct StageIdx {
+  static constexpr int value = S;
+};
 
 // Block tile 256 x 256 computed by 8 waves (2 along M x 4 along N, 128 x 64
 // each): one block per CU.  Loading 64 KB per K step for 4M multiply-adds
@@ -116,9 +121,20 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   constexpr int kDmaStep = kDmaA + kDmaB;
   constexpr int kSt = kStageA + (BC ? kStageBC : BQ ? kStageBQ : kStageB);
   constexpr int kDmaBw = BC ? 1 : BQ ? 2 : kDmaB;  // B loads per wave and step (BC: waves below kWavesN only)
-  // the operand stages, which the epilogue reuses as 8 KB of staging per wave
-  constexpr int kLdsBytes = kStages * kSt > 8 * 8192 ? kStages * kSt : 8 * 8192;
-  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  // LDS stages of one K step each: three for the 128 x 512 code-plane form (3 x 24 KB,
+  // loads two steps ahead), two elsewhere (a third 48 KB stage of the int8 B form
+  // measured no faster).  Each stage is an LDS variable of its own and the K loop is
+  // unrolled by the number of stages, so that every stage access names its variable: the
+  // compiler then tells the direct loads into one stage from reads of another and makes a
+  // read wait only for the loads of its own stage (with one array it waits for all of them).
+  // The epilogue reuses the stages as 8 KB of staging per wave.
+  constexpr int kS = BC && BN == 512 ? 3 : kStages;
+  // (with two stages of less than 32 KB the third variable holds the rest of the staging)
+  constexpr int kWpS = kSt / 8192;  // 8 KB staging areas per stage
+  static_assert(kSt % 8192 == 0 && (kS == 3 ? 3 * kWpS >= 8 : true), "stages must hold the 8 staging areas");
+  __shared__ __attribute__((aligned(1024))) char lds0[kSt];
+  __shared__ __attribute__((aligned(1024))) char lds1[kSt];
+  __shared__ __attribute__((aligned(1024))) char lds2[kS == 3 ? kSt : 2 * kWpS >= 8 ? 16 : (8 - 2 * kWpS) * 8192];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,17 +209,18 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
                                                 : BR ? ((int64_t)(K / 8) * N - n0) * 16
                                                      : (int64_t)rows_b * b_row));
   const bool ktail = ((kend - kbeg) % kKStep) != 0;
-  auto issue = [&](int kt, int st) {
+  // BC: the waves that load the code rows of a step (one 1 KB piece each; all 8 with 512 columns)
+  const bool b_loader = kWavesN == 8 || wave < kWavesN;
+  auto issue = [&](int kt, char* sa) {
     const int k0 = kbeg + kt * kKStep;
     const uint32_t soff = (uint32_t)k0 * 2;
-    char* sa = lds + st * kSt;
     char* sb = sa + kStageA;
 #pragma unroll
     for (int i = 0; i < kDmaA; ++i)
       dma16(ar, sa + 1024 * (kDmaA * wave + i), ktail && k0 + a_k[i] >= kend ? kOOB : a_off[i],
             (uint32_t)k0 * a_soff_per_k);
     if constexpr (BC) {
-      if (wave < kWavesN) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
+      if (b_loader) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
     } else if constexpr (BQ) {
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -218,18 +235,17 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
 
   const float alpha = alpha_p ? *alpha_p : 1.0f;  // fetched before the K loop
 
-  // One load (index idx of the wave's loads of a step) of K step kt into stage st.
+  // One load (index idx of the wave's loads of a step) of K step kt into stage sa.
   constexpr int kNDma = BC ? kDmaA + 1 : BQ ? kDmaA + 2 : kDmaStep;
-  auto issue_one = [&](int kt, int st, int idx) {
+  auto issue_one = [&](int kt, char* sa, int idx) {
     const int k0 = kbeg + kt * kKStep;
     const uint32_t soff = (uint32_t)k0 * 2;
-    char* sa = lds + st * kSt;
     char* sb = sa + kStageA;
     if (idx < kDmaA) {
       dma16(ar, sa + 1024 * (kDmaA * wave + idx), ktail && k0 + a_k[idx] >= kend ? kOOB : a_off[idx],
             (uint32_t)k0 * a_soff_per_k);
     } else if constexpr (BC) {
-      if (wave < kWavesN) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
+      if (b_loader) dma16(br, sb + 1024 * wave, b_off[0], (uint32_t)k0 / 4);
     } else if constexpr (BQ) {
       const int i = idx - kDmaA;
       dma16(br, sb + 1024 * (2 * wave + i), k0 + b_k[i] >= kb_rows ? kOOB : b_off[i], (uint32_t)k0 * (uint32_t)N);
@@ -253,9 +269,9 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // no direct loads are in flight: the compiler makes a read of them wait for
   // all outstanding loads) and widened per slice.
   uint2 wb[kNJ];
-  auto rdc = [&](int st) {
+  auto rdc = [&](const char* st) {
     if constexpr (BC) {
-      const char* b = lds + st * kSt + kStageA;
+      const char* b = st + kStageA;
 #pragma unroll
       for (int j = 0; j < kNJ; ++j) wb[j] = *(const uint2*)(b + 16 * (wn0 + 32 * j + (lane & 31)) + 8 * (lane >> 5));
     }
@@ -264,17 +280,27 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // where rdc reads code words (the compiler would make these reads wait for
   // every load in flight) and widened per slice.
   v2i wq[BQ ? 4 : 1][kNJ];
-  auto rdq = [&](int st) {
+  auto rdq = [&](const char* st) {
     if constexpr (BQ) {
-      const char* b = lds + st * kSt + kStageA;
+      const char* b = st + kStageA;
       const int g = lane >> 4, q = lane & 15;
+      const int r0 = 8 * (g >> 1) + (q >> 1);  // the K row this lane addresses in slice 0 (+16 per slice)
+      // One opaque lane offset per column block, so that every read is the stage
+      // variable plus two offsets: the compiler tags only short address chains
+      // with their LDS variable, and an untagged read waits for every load in
+      // flight (which matters once loads are in flight here, with three stages).
+      int qo[kNJ];
+#pragma unroll
+      for (int j = 0; j < kNJ; ++j) {
+        const int c = (wn0 + 32 * j + 16 * (g & 1)) >> 4;
+        qo[j] = r0 * kBNn + 16 * (c ^ ((r0 & 7) << 1)) + 8 * (q & 1);
+        asm volatile("" : "+v"(qo[j]));
+      }
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int r = 16 * ks + 8 * (g >> 1) + (q >> 1);  // the K row this lane addresses
 #pragma unroll
         for (int j = 0; j < kNJ; ++j) {
-          const int c = (wn0 + 32 * j + 16 * (g & 1)) >> 4;
-          const SBL_LDS char* pa = (const SBL_LDS char*)(b + r * kBNn + 16 * (c ^ ((r & 7) << 1)) + 8 * (q & 1));
+          const SBL_LDS char* pa = (const SBL_LDS char*)(b + qo[j] + 16 * ks * kBNn);
           wq[ks][j] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((SBL_LDS v2i*)pa);
         }
       }
@@ -288,8 +314,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
         fb[j][e] = (__bf16)(float)(signed char)(w >> (8 * e));
     }
   };
-  auto rd = [&](int st, int ks, v8bf (&fa)[kMI], v8bf (&fb)[kNJ]) {
-    const char* a = lds + st * kSt;
+  auto rd = [&](const char* a, int ks, v8bf (&fa)[kMI], v8bf (&fb)[kNJ]) {
     const char* b = a + kStageA;
 #pragma unroll
     for (int i = 0; i < kMI; ++i) {
@@ -316,8 +341,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // one 16-byte run of AT row k0 + column.
   const int gn = (N + kBNn - 1) / kBNn;
   __shared__ __attribute__((aligned(16))) float wsc[WTA ? kBM : 4];
-  auto write_at = [&](int st, int k0) {
-    const char* a = lds + st * kSt;
+  auto write_at = [&](const char* a, int k0) {
     constexpr int kRounds = kBM / 64;  // 32-row rounds of each wave
     const int kb = 16 * (wave & 3), tb0 = 32 * kRounds * (wave >> 2);
     const int g = lane >> 4, q = lane & 15;
@@ -380,95 +404,117 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     __builtin_amdgcn_sched_group_barrier(0x008, kMI * kNJ - 1, id);  \
   }
 
-  // Step k (stage k % 2 has landed; slice 0 is already in fa0/fb0): each of
+  // Step k (stage k % kS has landed; slice 0 is already in fa0/fb0): each of
   // the 4 slices is read while the previous one is multiplied.  Before the
-  // last slice: wait for this wave's loads of step k + 1 and for its reads of
-  // stage k, barrier (every wave's loads landed, every wave done reading stage
-  // k), refill stage k % 2 with step k + 2, then read slice 0 of step k + 1
-  // while multiplying slice 3.  Past the last step the load index is clamped:
-  // the redundant loads go to a stage nobody reads again.
+  // last slice: wait for this wave's loads of step k + 1 (with three stages
+  // those of step k + 2 stay in flight) and for its reads of stage k, barrier
+  // (every wave's loads of step k + 1 landed, every wave done reading stage k),
+  // refill stage k % kS with step k + kS, then read slice 0 of step k + 1 while
+  // multiplying slice 3.  Past the last step the load index is clamped: the
+  // redundant loads go to a stage nobody reads again.
   v8bf fa0[kMI], fb0[kNJ], fa1[kMI], fb1[kNJ];
   const int last = nk - 1;
   if constexpr (WTA) {
     // row scales of the side output (visible to all waves after the first barrier)
     if (wscale && tid < kBM) wsc[tid] = m0 + tid < M ? wscale[m0 + tid] * (1.0f / 127.0f) : 0.0f;
   }
-  issue(0, 0);
-  issue(min(1, last), 1);
+  issue(0, lds0);
+  issue(min(1, last), lds1);
+  if constexpr (kS == 3) issue(min(2, last), lds2);
   if constexpr (BC) {  // (lgkmcnt too: the scale table above is read after the barrier)
-    if (wave < kWavesN) wait_vmcnt_lgkm0<kDmaA + 1>();
-    else wait_vmcnt_lgkm0<kDmaA>();
+    if (b_loader) wait_vmcnt_lgkm0<(kS - 1) * (kDmaA + 1)>();
+    else wait_vmcnt_lgkm0<(kS - 1) * kDmaA>();
   } else {
-    wait_vmcnt<kNDma>();  // this wave's loads of step 0 (those of step 1 may be in flight)
+    wait_vmcnt<(kS - 1) * kNDma>();  // this wave's loads of step 0 (those of the later steps may be in flight)
   }
   barrier_only();
   if constexpr (WTA) {
-    if (nt == 0) write_at(0, kbeg);
+    if (nt == 0) write_at(lds0, kbeg);
   }
-  rdc(0);
-  rdq(0);
-  rd(0, 0, fa0, fb0);
+  rdc(lds0);
+  rdq(lds0);
+  rd(lds0, 0, fa0, fb0);
 #pragma unroll
   for (int j = 0; j < kNJ; ++j) cvtq(0, j, fb0);
-  int sc = 0;
-  for (int k = 0; k < nk; ++k) {
-    rd(sc, 1, fa1, fb1);
+  // Step k out of stage S (a constant: see the LDS variables above).
+  auto step = [&](auto stage, int k) {
+    constexpr int S = decltype(stage)::value, X = (S + 1) % kS;  // stages of steps k and k + 1
+    char* const cur = S == 0 ? lds0 : S == 1 ? lds1 : lds2;
+    char* const nxt = X == 0 ? lds0 : X == 1 ? lds1 : lds2;
+    rd(cur, 1, fa1, fb1);
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) cvtq(1, j, fb1);
     mm(fa0, fb0);
     ORDER_SLICE(0)
     __builtin_amdgcn_sched_barrier(0);
-    rd(sc, 2, fa0, fb0);
+    rd(cur, 2, fa0, fb0);
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) cvtq(2, j, fb0);
     mm(fa1, fb1);
     ORDER_SLICE(1)
     __builtin_amdgcn_sched_barrier(0);
-    rd(sc, 3, fa1, fb1);
+    rd(cur, 3, fa1, fb1);
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) cvtq(3, j, fb1);
     mm(fa0, fb0);
     ORDER_SLICE(2)
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_lgkm0<0>();
+    if constexpr (kS == 3) {  // all but the newest step's loads (loads complete in order)
+      if (BC && !b_loader) wait_vmcnt_lgkm0<kDmaA>();
+      else wait_vmcnt_lgkm0<kNDma>();
+    } else {
+      wait_vmcnt_lgkm0<0>();
+    }
     barrier_only();
     __builtin_amdgcn_sched_barrier(0);
-    // Transposed copy of step k + 1's A tile: it has just landed and is not
-    // refilled before the next barrier; no loads are in flight yet, so the
-    // reads wait for nothing.
+    // Transposed copy of step k + 1's A tile: it has landed and is not
+    // refilled before the next barrier.
     if constexpr (WTA) {
-      if (k + 1 < nk && (k + 1) % gn == nt) write_at(sc ^ 1, kbeg + (k + 1) * kKStep);
+      if (k + 1 < nk && (k + 1) % gn == nt) write_at(nxt, kbeg + (k + 1) * kKStep);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (BC) {
-      rdc(sc ^ 1);
+      rdc(nxt);
       __builtin_amdgcn_sched_barrier(0);
     }
     if constexpr (BQ) {
-      rdq(sc ^ 1);
+      rdq(nxt);
       __builtin_amdgcn_sched_barrier(0);
     }
     // Slice 3 (its fragments are in registers) restarts the matrix pipe right
     // after the barrier; the reads of slice 0 of step k + 1 and the loads of
-    // step k + 2 go between its instructions, one load after each.
-    const int kn = min(k + 2, last);
+    // step k + kS go between its instructions, one load after each, into the
+    // stage of step k, which every wave has finished reading.
+    const int kn = min(k + kS, last);
     mm_one(0, fa1, fb1);
     __builtin_amdgcn_sched_barrier(0);
-    rd(sc ^ 1, 0, fa0, fb0);
+    rd(nxt, 0, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < kMI * kNJ; ++t) {
       if (t > 0) mm_one(t, fa1, fb1);
       __builtin_amdgcn_sched_barrier(0);
-      if (t < kNDma) issue_one(kn, sc, t);
+      if (t < kNDma) issue_one(kn, cur, t);
       // BQ: slice 0's B widening in the last slots, when its reads have landed
       if (t >= kMI * kNJ - kNJ) cvtq(0, t - (kMI * kNJ - kNJ), fb0);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int t = kMI * kNJ; t < kNDma; ++t) issue_one(kn, sc, t);
+    for (int t = kMI * kNJ; t < kNDma; ++t) issue_one(kn, cur, t);
     __builtin_amdgcn_sched_barrier(0);
-    sc ^= 1;
+  };
+  // Whole rounds of kS steps, then the remaining steps in straight code (an
+  // exit from the middle of a round makes the compiler keep more registers
+  // live across the loop).
+  int k = 0;
+  for (; k + kS <= nk; k += kS) {
+    step(StageIdx<0>{}, k);
+    step(StageIdx<1>{}, k + 1);
+    if constexpr (kS == 3) step(StageIdx<2>{}, k + 2);
+  }
+  if (k < nk) step(StageIdx<0>{}, k);
+  if constexpr (kS == 3) {
+    if (k + 1 < nk) step(StageIdx<1>{}, k + 1);
   }
   // No direct loads may still target LDS when the block retires.
   wait_vmcnt<0>();
@@ -485,7 +531,8 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // instruction writes whole row segments of the wave's 64 columns.
   if ((N & (OUT == SBL_F32 ? 3 : 7)) == 0) {
     __syncthreads();  // every wave is done with the operand stages (no loads in flight)
-    char* stg = lds + wave * 8192;
+    char* stg = wave < kWpS ? lds0 + wave * 8192
+                : wave < 2 * kWpS ? lds1 + (wave - kWpS) * 8192 : lds2 + (wave - 2 * kWpS) * 8192;
     const int ml = lane & 31, h = lane >> 5;
     constexpr int kRB = OUT == SBL_F32 ? 256 : 128;   // bytes per staged row
     constexpr int kCh = kRB / 16;                     // 16-byte chunks per row
