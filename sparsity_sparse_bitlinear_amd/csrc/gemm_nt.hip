@@ -308,10 +308,19 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   };
   auto cvtq = [&](int ks, int j, v8bf (&fb)[kNJ]) {
     if constexpr (BQ) {
-      const unsigned long long w = ((unsigned long long)(uint32_t)wq[ks][j][1] << 32) | (uint32_t)wq[ks][j][0];
+      // byte e: one sign-extending byte-select convert each; the bf16 of an integer
+      // of at most 8 significant bits is the high half of its float32 (the low half
+      // is zero), so one byte permute packs two of them
+      v4i r;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)  // byte e: one sign-extending byte-select convert each
-        fb[j][e] = (__bf16)(float)(signed char)(w >> (8 * e));
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t d = (uint32_t)wq[ks][j][h];
+        const float f0 = (float)(int)(signed char)d, f1 = (float)(int)(signed char)(d >> 8);
+        const float f2 = (float)(int)(signed char)(d >> 16), f3 = (float)((int)d >> 24);
+        r[2 * h] = (int)__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+        r[2 * h + 1] = (int)__builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+      }
+      fb[j] = __builtin_bit_cast(v8bf, r);
     }
   };
   auto rd = [&](const char* a, int ks, v8bf (&fa)[kMI], v8bf (&fb)[kNJ]) {
