@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 # rocprofv3 --pmc for the backward kernel sources whose hash is given
 # (profiles/traffic_backward_3b_32768tok.md).
 BWD_TRAFFIC_BYTES = 2.40e9
-BWD_TRAFFIC_SRC_SHA = "895deab4aba90b10"
+BWD_TRAFFIC_SRC_SHA = "6c90edac77e95db5"
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
