@@ -66,6 +66,13 @@ __device__ __forceinline__ void xcd_tile(int b, int gm, int gn, int& mt, int& nt
 // rows, column by column inside a group: the blocks resident on an XCD at one
 // time then cover about a GM x (resident / GM) patch of the output, so both
 // operands are shared in its L2 instead of one of them streaming through.
+__device__ __forceinline__ void grouped_tile(int tile, int gm, int gn, int GM, int& mt, int& nt) {
+  const int g = tile / (GM * gn);
+  const int rem = tile - g * GM * gn;
+  const int rows = min(GM, gm - g * GM);
+  mt = g * GM + rem % rows;
+  nt = rem / rows;
+}
 __device__ __forceinline__ void xcd_tile_grouped(int b, int gm, int gn, int GM, int& mt, int& nt) {
   const int nb = gm * gn;
   int tile = b;
@@ -74,11 +81,28 @@ __device__ __forceinline__ void xcd_tile_grouped(int b, int gm, int gn, int GM, 
     const int q = nb >> 3, r = nb & 7;
     tile = x * q + min(x, r) + local;
   }
-  const int g = tile / (GM * gn);
-  const int rem = tile - g * GM * gn;
-  const int rows = min(GM, gm - g * GM);
-  mt = g * GM + rem % rows;
-  nt = rem / rows;
+  grouped_tile(tile, gm, gn, GM, mt, nt);
+}
+
+// Split-K grids (S K ranges of T tiles, block L = x + T y in launch order):
+// with one block per CU an XCD holds 32 blocks at a time, so the blocks are
+// dealt in rounds of 256, and in each full round XCD x takes 32 consecutive
+// work items.  Work items run over chunks of 32 consecutive tiles of the
+// grouped order, each chunk once per K range (chunk-major), so that a full
+// round gives every XCD one chunk (a 4 x 8 patch of 256 x 256 tiles) at one K
+// range: its operand rows are shared by all 32 resident blocks.  The last,
+// partial round is dealt evenly.  Returns the K range s and the tile index t
+// in grouped order; every (s, t) is taken by exactly one block.
+__device__ __forceinline__ void xcd_split_order(int L, int T, int S, int& s, int& t) {
+  const int total = T * S;
+  const int x = L & 7, local = L >> 3;
+  const int base = 256 * (local >> 5), j = local & 31;
+  const int R = min(256, total - base);
+  const int item = R == 256 ? base + 32 * x + j : base + x * (R >> 3) + min(x, R & 7) + j;
+  const int c = item / (32 * S), rem = item - c * 32 * S;
+  const int cs = min(32, T - 32 * c);
+  s = rem / cs;
+  t = 32 * c + (rem - s * cs);
 }
 
 // Buffer resource for raw (unformatted) loads of `bytes` bytes at `base`.

@@ -60,8 +60,9 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 }
 
 // Requires K % 8 == 0 (16-byte rows, K chunks never straddle a row end).
-// blockIdx.y selects a K range [kps * y, kps * (y + 1)) (split-K); block y writes
-// its partial product to C + y * M * N.  alpha_p == nullptr means alpha = 1.
+// A split-K grid has gridDim.y K ranges [kps * s, kps * (s + 1)); the blocks are
+// dealt to (range, tile) pairs by xcd_split_order, and range s writes
+// its partial product to C + s * M * N.  alpha_p == nullptr means alpha = 1.
 //
 // WTA (no split-K): the A tiles staged in LDS are also written out transposed
 // and run-major (see BR), AT[k, m] = A[m, k] at element (m / 8 * K + k) * 8 +
@@ -141,12 +142,21 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS targets live in SGPRs
   const int wm0 = (wave / kWavesN) * kWM;
   const int wn0 = (wave % kWavesN) * kWN;
-  int mt, nt;
+  int mt, nt, split = 0;
   // 32 tiles resident per XCD: 4 x 8 of 256 x 256 tiles, 8 x 4 of 128 x 512 ones
-  xcd_tile_grouped(blockIdx.x, (M + kBM - 1) / kBM, (N + kBNn - 1) / kBNn, BN == 256 ? 4 : 8, mt, nt);
+  {
+    const int gm = (M + kBM - 1) / kBM, gn = (N + kBNn - 1) / kBNn;
+    if (gridDim.y > 1) {
+      int t;
+      xcd_split_order(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x, gridDim.y, split, t);
+      grouped_tile(t, gm, gn, BN == 256 ? 4 : 8, mt, nt);
+    } else {
+      xcd_tile_grouped(blockIdx.x, gm, gn, BN == 256 ? 4 : 8, mt, nt);
+    }
+  }
   const int m0 = mt * kBM;
   const int n0 = nt * kBNn;
-  const int kbeg = blockIdx.y * kps;
+  const int kbeg = split * kps;
   const int kend = min(K, kbeg + kps);
   const int nk = (kend - kbeg + kKStep - 1) / kKStep;  // >= 1: the host never makes an empty split
   const int rows_a = min(kBM, M - m0);
@@ -532,7 +542,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]: each lane stores runs
   // of 4 consecutive outputs of one row (16 bytes in float32, 8 in bf16).
   constexpr float pre = BC ? 0.5f : 1.0f;  // BC: the sums are of 2 W_eff (halving is exact)
-  C = (char*)C + (size_t)blockIdx.y * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
+  C = (char*)C + (size_t)split * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
 
   // With 16-byte aligned output rows the wave's 128 x 64 result goes through
   // LDS, 8 KB per wave and round (64 rows of 128 bytes in bf16, 32 rows of 256

@@ -826,6 +826,26 @@ def test_backward_parity(T, d_out, d_in):
         assert np.count_nonzero(dW.cpu().numpy()[masked]) > 0.99 * masked.sum()
 
 
+@pytest.mark.parametrize("d_out", [64, 128, 192, 256, 320, 448, 200])
+def test_backward_dx_k_step_counts(d_out):
+    # the dX product runs its K steps (64 wide, K = d_out) in rounds of three LDS stages
+    # and the remaining one or two in straight code: 1 to 7 steps, and a ragged tail
+    # (200 = 3 steps + 8); 600 tokens make 5 row tiles, the last ragged
+    T, d_in = 600, 1024
+    W = weight(57, d_out, d_out, d_in)
+    x = activation(57, d_out + 1, T, d_in)
+    dY = grad_out(57, d_out + 2, T, d_out)
+    rows = sample_rows(57, d_out, T, 64)
+    dX, _ = gpu_backward(W, x, dY, 6)
+    w_eff, _, g = oracle.effective_weight(W, 6)
+    xq, a = oracle.act_quant(x)
+    dX_ref, _ = oracle.backward(dY[rows], w_eff, g, xq[rows], a[rows])
+    assert_grad_close(bf16_to_f64(dX)[rows], dX_ref)
+    assert_grad_close(bf16_to_f64(dX)[rows], dX_ref, tol=ERR_MODEL_BF16)
+    dX32, _ = gpu_backward(W, x, dY, 6, dx_dtype=0)
+    assert_grad_close(dX32.cpu().numpy().astype(np.float64)[rows], dX_ref, tol=ERR_MODEL_F32)
+
+
 def test_backward_dx_large_tiles_sampled():
     T, d_out, d_in = 4096, 264, 8192
     W = weight(61, 0, d_out, d_in)
