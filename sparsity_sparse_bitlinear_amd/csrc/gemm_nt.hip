@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
                                                               int kps, const float* __restrict__ alpha_p,
                                                               void* __restrict__ C, uint16_t* __restrict__ AT,
                                                               int at_ld, const float* __restrict__ wscale,
-                                                              int kb_rows) {
+                                                              int kb_rows, SplitTail tail) {
   static_assert(BN == 256 || (BN == 512 && BC), "512-column blocks take the code-plane B only");
   constexpr int kBM = 65536 / BN, kBNn = BN;  // (hide the square tile's constants)
   constexpr int kWavesN = BN / 64;            // waves along N (each 64 columns)
@@ -146,7 +146,20 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // 32 tiles resident per XCD: 4 x 8 of 256 x 256 tiles, 8 x 4 of 128 x 512 ones
   {
     const int gm = (M + kBM - 1) / kBM, gn = (N + kBNn - 1) / kBNn;
-    if (gridDim.y > 1) {
+    if (tail.head > 0) {
+      // the head's blocks (whole rounds) take kps-long K ranges; the blocks after
+      // them serve the remaining tiles with the deeper split
+      const int nh = tail.head * tail.head_splits;
+      int t;
+      if ((int)blockIdx.x < nh) {
+        xcd_split_order(blockIdx.x, tail.head, tail.head_splits, split, t);
+      } else {
+        xcd_split_order(blockIdx.x - nh, gm * gn - tail.head, tail.tail_splits, split, t);
+        t += tail.head;
+        kps = tail.tail_kps;
+      }
+      grouped_tile(t, gm, gn, BN == 256 ? 4 : 8, mt, nt);
+    } else if (gridDim.y > 1) {
       int t;
       xcd_split_order(blockIdx.x + blockIdx.y * gridDim.x, gridDim.x, gridDim.y, split, t);
       grouped_tile(t, gm, gn, BN == 256 ? 4 : 8, mt, nt);
@@ -649,7 +662,7 @@ hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, 
   auto kern = AT ? (f32 ? k_gemm_nt_bf16<256, SBL_F32, true, false, false, false, false> : k_gemm_nt_bf16<256, SBL_BF16, true, false, false, false, false>)
                  : (f32 ? k_gemm_nt_bf16<256, SBL_F32, false, false, false, false, false> : k_gemm_nt_bf16<256, SBL_BF16, false, false, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, B, (int)M, (int)N, (int)K, (int)k_per_split, alpha, C, AT,
-                     (int)at_ld, nullptr, 0);
+                     (int)at_ld, nullptr, 0, SplitTail{0, 0, 0, 0});
   return hipGetLastError();
 }
 
@@ -660,7 +673,7 @@ hipError_t launch_gemm_nt_runs(const uint16_t* A, bool a_runs, const uint16_t* B
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
   auto kern = a_runs ? k_gemm_nt_bf16<256, SBL_F32, false, false, true, true, false> : k_gemm_nt_bf16<256, SBL_F32, false, false, false, true, false>;
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, Brun, (int)M, (int)N, (int)K, (int)k_per_split, nullptr, C, nullptr,
-                     0, nullptr, 0);
+                     0, nullptr, 0, SplitTail{0, 0, 0, 0});
   return hipGetLastError();
 }
 
@@ -671,13 +684,21 @@ bool gemm_nt_q_supported(int64_t M, int64_t N, int64_t K, int64_t kb_rows) {
 }
 
 hipError_t launch_gemm_nt_q(const uint16_t* Arun, const int8_t* Bq, int64_t M, int64_t N, int64_t K, int64_t kb_rows,
-                            float* C, hipStream_t s, int splits, int64_t k_per_split) {
+                            float* C, hipStream_t s, int splits, int64_t k_per_split, SplitTail tail) {
   if (splits < 1) splits = 1;
   if (splits == 1) k_per_split = K;
-  const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
-  hipLaunchKernelGGL((k_gemm_nt_bf16<256, SBL_F32, false, false, true, false, true>), grid, block, 0, s, Arun,
+  const int64_t tiles = gemm_nt_bf16_tiles(M, N);
+  dim3 grid((unsigned)tiles, (unsigned)splits);
+  if (tail.head > 0) {
+    // the head's blocks must fill whole rounds (the tail's order starts a round)
+    if (tail.head >= tiles || tail.head_splits != splits || (tail.head * splits) % 256 != 0 ||
+        tail.tail_splits < 1 || tail.tail_kps < 64 || tail.tail_kps % 64 != 0 || k_per_split % 64 != 0)
+      return hipErrorInvalidValue;
+    grid = dim3((unsigned)(tail.head * splits + (tiles - tail.head) * tail.tail_splits), 1);
+  }
+  hipLaunchKernelGGL((k_gemm_nt_bf16<256, SBL_F32, false, false, true, false, true>), grid, dim3(kNT), 0, s, Arun,
                      (const uint16_t*)Bq, (int)M, (int)N, (int)K, (int)k_per_split, nullptr, (void*)C, nullptr, 0,
-                     nullptr, (int)kb_rows);
+                     nullptr, (int)kb_rows, tail);
   return hipGetLastError();
 }
 
@@ -690,7 +711,7 @@ hipError_t launch_gemm_nt_codes(const uint16_t* A, const uint32_t* Bc, int64_t M
   auto kern = AT ? (f32 ? k_gemm_nt_bf16<512, SBL_F32, true, true, false, false, false> : k_gemm_nt_bf16<512, SBL_BF16, true, true, false, false, false>)
                  : (f32 ? k_gemm_nt_bf16<512, SBL_F32, false, true, false, false, false> : k_gemm_nt_bf16<512, SBL_BF16, false, true, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, (const uint16_t*)Bc, (int)M, (int)N, (int)K, (int)K, alpha, C, AT,
-                     (int)at_ld, wscale, 0);
+                     (int)at_ld, wscale, 0, SplitTail{0, 0, 0, 0});
   return hipGetLastError();
 }
 

@@ -884,6 +884,26 @@ def test_backward_full_size_sampled(name, T, d_out, d_in):
     assert_grad_close(dW.cpu().numpy()[cols], dW_ref, tol=ERR_MODEL_BF16)
 
 
+def test_backward_dw_split_tail_full():
+    # 288 tiles of 256 x 256: the first 256 take two K ranges (two whole rounds of
+    # blocks), the last 32 a deeper split; every dW entry against the oracle
+    T, d_out, d_in = 4096, 4608, 4096
+    assert sbl.backward_workspace_size(T, d_in, d_out) > 4 * d_out * d_in * 4  # more than two partial planes
+    W = weight(97, 0, d_out, d_in)
+    x = activation(97, 1, T, d_in, dist="student_t4")
+    dY = grad_out(97, 2, T, d_out)
+    codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6)
+    xq, a = sbl.act_quant(to_dev_bf16(x))
+    _, dW = sbl.backward(codes, gamma, xq, a, to_dev_bf16(dY), need_dx=False)
+    _, dW2 = sbl.backward(codes, gamma, xq, a, to_dev_bf16(dY))  # fused with dX: same bits
+    torch.cuda.synchronize()
+    assert torch.equal(dW, dW2)
+    xq_h, a_h = oracle.act_quant(x)
+    dW_ref = oracle.bf16_to_f64(dY).T @ oracle.dequant_act(xq_h, a_h)
+    assert_grad_close(dW.cpu().numpy(), dW_ref)
+    assert_grad_close(dW.cpu().numpy(), dW_ref, tol=ERR_MODEL_BF16)
+
+
 @pytest.mark.parametrize("T,d_out,d_in", [(1000, 520, 776), (77, 200, 328), (4096, 256, 2048), (300, 2048, 512)])
 def test_backward_fused_matches_separate(T, d_out, d_in):
     # dX and dW in one call (the dX product writes dY^T for dW) equal the two separate calls bit for bit
