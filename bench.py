@@ -39,10 +39,10 @@ HBM_PEAK_GBS = 8000.0
 
 # HBM bytes per sbl_backward(dX + dW) call on the default workload (FETCH_SIZE x 2.000 +
 # WRITE_SIZE, scale factors from a plain 1 GiB copy), averaged over the 7 linears; measured with
-# rocprofv3 --pmc for the backward kernel sources whose hash is given
+# rocprofv3 --pmc for the backward kernel sources whose hash (code without comments) is given
 # (profiles/traffic_backward_3b_32768tok.md).
 BWD_TRAFFIC_BYTES = 2.056e9
-BWD_TRAFFIC_SRC_SHA = "431e94fa0d831c2b"
+BWD_TRAFFIC_SRC_SHA = "5faf56aacf0f0bc9"
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
@@ -311,12 +311,20 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def _code_text(src: str) -> str:
+    """Source text without comments and blank runs (the code that the counters measured)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(" ".join(line.split()) for line in src.splitlines() if line.strip())
+
+
 def _bwd_sources_sha() -> str:
     import hashlib
     h = hashlib.sha256()
     for f in ("gemm_common.h", "gemm_nt.hip", "gemm_bwd.hip"):
-        with open(os.path.join(ROOT, "sparsity_sparse_bitlinear_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sparsity_sparse_bitlinear_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

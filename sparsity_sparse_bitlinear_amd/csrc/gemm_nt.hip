@@ -62,7 +62,10 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 // Requires K % 8 == 0 (16-byte rows, K chunks never straddle a row end).
 // A split-K grid has gridDim.y K ranges [kps * s, kps * (s + 1)); the blocks are
 // dealt to (range, tile) pairs by xcd_split_order, and range s writes
-// its partial product to C + s * M * N.  alpha_p == nullptr means alpha = 1.
+// its partial product to C + s * M * N.  With tail.head > 0 (a one-row grid)
+// the first tail.head tiles of the grouped order take tail.head_splits ranges
+// of kps and the others tail.tail_splits ranges of tail.tail_kps, each range s
+// again into plane s.  alpha_p == nullptr means alpha = 1.
 //
 // WTA (no split-K): the A tiles staged in LDS are also written out transposed
 // and run-major (see BR), AT[k, m] = A[m, k] at element (m / 8 * K + k) * 8 +
