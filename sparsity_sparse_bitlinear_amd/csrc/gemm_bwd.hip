@@ -479,32 +479,37 @@ void nt_splits(int64_t M, int64_t N, int64_t K, int& S, int64_t& kps) {
   S = (int)((K + kps - 1) / kps);
 }
 
-// A 2-way plan whose last round of blocks is partial (e.g. 344 tiles: 688
-// blocks, rounds of 256, 256 and 176) can give the tiles after the whole
-// rounds a deeper split instead: 256 tiles x 2 ranges, then 88 tiles x 5
-// ranges (440 blocks of 2/5 the length) finish in 2.8 instead of 3 half-tile
-// rounds, for (tail splits - 2) more partial planes on the tail tiles only.
-// Same cost model as nt_splits; head == 0 keeps the uniform plan.
+// A split whose last round of blocks is partial (e.g. 344 tiles: 2 ranges
+// make 688 blocks, rounds of 256, 256 and 176) can instead give the tiles that
+// fill whole rounds fewer ranges and the remaining tiles a deeper split.  The
+// plan with one range for the head writes the head tiles' sums into dW
+// directly: 256 full-K blocks, then 88 tiles x 5 ranges (440 blocks of 1/5 the
+// length) finish in 1.4 instead of 1.5 full-K rounds, and only the tail tiles
+// have partial planes (plane 0 in dW, planes 1-4 in the workspace).  Same cost
+// model as nt_splits; head == 0 keeps the uniform plan.
 void nt_split_tail(int64_t M, int64_t N, int64_t K, int S, int64_t kps, SplitTail& tail) {
-  tail = SplitTail{0, 0, 0, 0};
+  tail = SplitTail{0, 0, 0, 0, nullptr};
   const int64_t tiles = gemm_nt_bf16_tiles(M, N);
-  if (S != 2 || M > 65535 || kps * 2 < K) return;
-  const int64_t head = (tiles * S / 256) * 256 / S;  // tiles whose blocks fill whole rounds
-  const int64_t rest = tiles - head;
-  if (head <= 0 || rest <= 0) return;
+  if (tiles <= 256 || M > 65535) return;
   const double t_block = 2.0 * 256.0 * 256.0 * (double)K / 5.0e12, t_byte = 1.0 / 5.0e12;
   const double tile_bytes = 256.0 * 256.0 * 4.0;
-  const double base = std::ceil((double)tiles * S / 256.0) * t_block / S + (S + 1) * 4.0 * (double)M * (double)N * t_byte;
+  const double base = std::ceil((double)tiles * S / 256.0) * t_block / S +
+                      (S > 1 ? (S + 1) * 4.0 * (double)M * (double)N * t_byte : 0.0);
   double best = base * 0.97;
   const int max_s = (int)std::min<int64_t>(16, K / 512);
-  for (int sb = S + 1; sb <= max_s; ++sb) {
+  const int64_t head = tiles / 256 * 256;  // one full-K block each: whole rounds
+  const int64_t rest = tiles - head;
+  if (rest <= 0) return;
+  for (int sb = 2; sb <= max_s; ++sb) {
     const int64_t tkps = ((K + sb - 1) / sb + 63) / 64 * 64;
     const int sbe = (int)((K + tkps - 1) / tkps);  // ranges actually made (none empty)
-    const double cost = (double)(head * S / 256) * t_block / S + std::ceil((double)rest * sbe / 256.0) * t_block / sbe +
-                        ((S + 1) * 4.0 * (double)M * (double)N + (sbe - S) * 2.0 * (double)rest * tile_bytes) * t_byte;
+    if (sbe < 2) continue;
+    // head rounds, tail rounds; partial planes 1.. of the tail tiles written and read, plane 0 read
+    const double cost = (double)(head / 256) * t_block + std::ceil((double)rest * sbe / 256.0) * t_block / sbe +
+                        (2.0 * (sbe - 1) + 2.0) * (double)rest * tile_bytes * t_byte;
     if (cost < best) {
       best = cost;
-      tail = SplitTail{(int)head, S, sbe, (int)tkps};
+      tail = SplitTail{(int)head, 1, sbe, (int)tkps, nullptr};
     }
   }
 }
@@ -694,22 +699,23 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float4* __restrict_
   }
 }
 
-// The same sum for a plan with a deeper split of the tail tiles (SplitTail):
-// tile t (grouped order, 4 tile rows per group) has S ranges below `head`,
-// S_tail from there.  One block row per output row m, float4 columns (N % 4 == 0).
-__global__ __launch_bounds__(256) void k_splitk_reduce_tail(const float4* __restrict__ part, int M, int N, int S,
-                                                            int head, int S_tail, float4* __restrict__ dW) {
-  const int m = blockIdx.y, c4 = blockIdx.x * 256 + threadIdx.x, n4r = N >> 2;
-  if (c4 >= n4r) return;
+// The split-K sum of the tail tiles of a SplitTail plan with planes: plane 0
+// is already in dW, planes z = 1 .. S_tail - 1 at part + (z - 1) M N are added
+// to it in order (the head tiles' dW is final).  Block (t, y): tail tile t
+// (grouped order, 4 tile rows per group), rows 4 y .. 4 y + 3 of it, one float4
+// column per thread (N % 4 == 0).
+__global__ __launch_bounds__(256) void k_splitk_add_tail(const float4* __restrict__ part, int M, int N, int head,
+                                                         int S_tail, float4* __restrict__ dW) {
   const int gm = (M + 255) >> 8, gn = (N + 255) >> 8;
-  const int mt = m >> 8, nt = (c4 * 4) >> 8;
-  const int g = mt >> 2, rows = min(4, gm - 4 * g);
-  const int t = 4 * g * gn + nt * rows + (mt - 4 * g);
-  const int sz = t < head ? S : S_tail;
+  int mt, nt;
+  grouped_tile(head + (int)blockIdx.x, gm, gn, 4, mt, nt);
+  const int m = mt * 256 + 4 * (int)blockIdx.y + ((int)threadIdx.x >> 6);
+  const int c4 = nt * 64 + ((int)threadIdx.x & 63), n4r = N >> 2;
+  if (m >= M || c4 >= n4r) return;
   const int64_t plane = (int64_t)M * n4r, i = (int64_t)m * n4r + c4;
-  float4 s = part[i];
-  for (int z = 1; z < sz; ++z) {
-    const float4 v = part[(int64_t)z * plane + i];
+  float4 s = dW[i];
+  for (int z = 1; z < S_tail; ++z) {
+    const float4 v = part[(int64_t)(z - 1) * plane + i];
     s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
   }
   dW[i] = s;
@@ -761,13 +767,17 @@ DwLayout dw_layout(int64_t T, int64_t d_in, int64_t d_out, bool fused) {
   const int64_t T8 = round8(T);
   nt_splits(d_out, d_in, T8, L.S, L.kps);
   L.q = dw_q(T, d_in, d_out);
-  L.tail = SplitTail{0, 0, 0, 0};
+  L.tail = SplitTail{0, 0, 0, 0, nullptr};
   if (L.q) nt_split_tail(d_out, d_in, T8, L.S, L.kps, L.tail);
-  const int planes = L.tail.head > 0 ? std::max(L.S, L.tail.tail_splits) : L.S;
+  if (L.tail.head > 0) {  // one range for the head tiles; planes 1.. of the tail in the workspace
+    L.S = 1;
+    L.kps = T8;
+  }
+  const int planes = L.tail.head > 0 ? L.tail.tail_splits - 1 : L.S > 1 ? L.S : 0;
   L.dyt = 0;
   L.xt = align256((size_t)d_out * (size_t)T8 * 2);
   L.part = L.xt + (L.q ? 0 : align256((size_t)d_in * (size_t)T8 * 2));
-  L.total = L.part + (planes > 1 ? (size_t)planes * (size_t)d_out * (size_t)d_in * sizeof(float) : 0);
+  L.total = L.part + (size_t)planes * (size_t)d_out * (size_t)d_in * sizeof(float);
   L.wt = L.xt;
   if (fused) L.total = std::max(L.total, L.wt + align256(codes_t_bytes(d_in, d_out)));
   return L;
@@ -787,7 +797,7 @@ hipError_t run_dw_direct(const int8_t* xq, const float* absmax, const uint16_t* 
   const int64_t n = d_out * d_in;
   uint16_t* dyt = (uint16_t*)((char*)ws + L.dyt);
   uint16_t* xt = (uint16_t*)((char*)ws + L.xt);
-  float* target = L.S > 1 ? (float*)((char*)ws + L.part) : dW;
+  float* target = L.S > 1 ? (float*)((char*)ws + L.part) : dW;  // one range (also the tail plan): dW itself
   hipError_t e;
   if (L.q) {
     if (!dyt_ready) {  // the dX product did not write the scaled dY^T
@@ -796,12 +806,15 @@ hipError_t run_dw_direct(const int8_t* xq, const float* absmax, const uint16_t* 
       e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
-    e = launch_gemm_nt_q(dyt, xq, d_out, d_in, T8, T, target, s, L.S, L.kps, L.tail);
+    SplitTail tail = L.tail;
+    if (tail.head > 0) tail.planes = (float*)((char*)ws + L.part);
+    e = launch_gemm_nt_q(dyt, xq, d_out, d_in, T8, T, target, s, L.S, L.kps, tail);
     if (e != hipSuccess) return e;
-    if (L.tail.head > 0) {
-      const dim3 g((unsigned)((d_in / 4 + 255) / 256), (unsigned)d_out);
-      hipLaunchKernelGGL(k_splitk_reduce_tail, g, dim3(256), 0, s, (const float4*)target, (int)d_out, (int)d_in, L.S,
-                         L.tail.head, L.tail.tail_splits, (float4*)dW);
+    if (tail.head > 0) {
+      const int64_t tiles = gemm_nt_bf16_tiles(d_out, d_in);
+      const dim3 g((unsigned)(tiles - tail.head), 64);
+      hipLaunchKernelGGL(k_splitk_add_tail, g, dim3(256), 0, s, (const float4*)tail.planes, (int)d_out, (int)d_in,
+                         tail.head, tail.tail_splits, (float4*)dW);
       e = hipGetLastError();
     } else if (L.S > 1) {
       const int64_t n4 = n / 4;

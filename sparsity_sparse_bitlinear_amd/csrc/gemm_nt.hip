@@ -65,7 +65,8 @@ __device__ __forceinline__ v8bf widen_codes(uint32_t u, int p0) {
 // its partial product to C + s * M * N.  With tail.head > 0 (a one-row grid)
 // the first tail.head tiles of the grouped order take tail.head_splits ranges
 // of kps and the others tail.tail_splits ranges of tail.tail_kps, each range s
-// again into plane s.  alpha_p == nullptr means alpha = 1.
+// again into plane s (with tail.planes: plane 0 in C, plane s >= 1 at
+// tail.planes + (s - 1) M N).  alpha_p == nullptr means alpha = 1.
 //
 // WTA (no split-K): the A tiles staged in LDS are also written out transposed
 // and run-major (see BR), AT[k, m] = A[m, k] at element (m / 8 * K + k) * 8 +
@@ -558,7 +559,10 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]: each lane stores runs
   // of 4 consecutive outputs of one row (16 bytes in float32, 8 in bf16).
   constexpr float pre = BC ? 0.5f : 1.0f;  // BC: the sums are of 2 W_eff (halving is exact)
-  C = (char*)C + (size_t)split * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
+  if (tail.planes && split > 0)
+    C = (char*)tail.planes + (size_t)(split - 1) * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
+  else
+    C = (char*)C + (size_t)split * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
 
   // With 16-byte aligned output rows the wave's 128 x 64 result goes through
   // LDS, 8 KB per wave and round (64 rows of 128 bytes in bf16, 32 rows of 256
@@ -665,7 +669,7 @@ hipError_t launch_gemm_nt_bf16(const uint16_t* A, const uint16_t* B, int64_t M, 
   auto kern = AT ? (f32 ? k_gemm_nt_bf16<256, SBL_F32, true, false, false, false, false> : k_gemm_nt_bf16<256, SBL_BF16, true, false, false, false, false>)
                  : (f32 ? k_gemm_nt_bf16<256, SBL_F32, false, false, false, false, false> : k_gemm_nt_bf16<256, SBL_BF16, false, false, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, B, (int)M, (int)N, (int)K, (int)k_per_split, alpha, C, AT,
-                     (int)at_ld, nullptr, 0, SplitTail{0, 0, 0, 0});
+                     (int)at_ld, nullptr, 0, SplitTail{0, 0, 0, 0, nullptr});
   return hipGetLastError();
 }
 
@@ -676,7 +680,7 @@ hipError_t launch_gemm_nt_runs(const uint16_t* A, bool a_runs, const uint16_t* B
   const dim3 grid((unsigned)gemm_nt_bf16_tiles(M, N), (unsigned)splits), block(kNT);
   auto kern = a_runs ? k_gemm_nt_bf16<256, SBL_F32, false, false, true, true, false> : k_gemm_nt_bf16<256, SBL_F32, false, false, false, true, false>;
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, Brun, (int)M, (int)N, (int)K, (int)k_per_split, nullptr, C, nullptr,
-                     0, nullptr, 0, SplitTail{0, 0, 0, 0});
+                     0, nullptr, 0, SplitTail{0, 0, 0, 0, nullptr});
   return hipGetLastError();
 }
 
@@ -695,7 +699,7 @@ hipError_t launch_gemm_nt_q(const uint16_t* Arun, const int8_t* Bq, int64_t M, i
   if (tail.head > 0) {
     // the head's blocks must fill whole rounds (the tail's order starts a round)
     if (tail.head >= tiles || tail.head_splits != splits || (tail.head * splits) % 256 != 0 ||
-        tail.tail_splits < 1 || tail.tail_kps < 64 || tail.tail_kps % 64 != 0 || k_per_split % 64 != 0)
+        tail.tail_splits < 1 || tail.tail_kps < 64 || tail.tail_kps % 64 != 0 || (splits > 1 && k_per_split % 64 != 0))
       return hipErrorInvalidValue;
     grid = dim3((unsigned)(tail.head * splits + (tiles - tail.head) * tail.tail_splits), 1);
   }
@@ -714,7 +718,7 @@ hipError_t launch_gemm_nt_codes(const uint16_t* A, const uint32_t* Bc, int64_t M
   auto kern = AT ? (f32 ? k_gemm_nt_bf16<512, SBL_F32, true, true, false, false, false> : k_gemm_nt_bf16<512, SBL_BF16, true, true, false, false, false>)
                  : (f32 ? k_gemm_nt_bf16<512, SBL_F32, false, true, false, false, false> : k_gemm_nt_bf16<512, SBL_BF16, false, true, false, false, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, s, A, (const uint16_t*)Bc, (int)M, (int)N, (int)K, (int)K, alpha, C, AT,
-                     (int)at_ld, wscale, 0, SplitTail{0, 0, 0, 0});
+                     (int)at_ld, wscale, 0, SplitTail{0, 0, 0, 0, nullptr});
   return hipGetLastError();
 }
 

@@ -195,14 +195,16 @@ bool gemm_nt_q_supported(int64_t M, int64_t N, int64_t K, int64_t kb_rows);
 // Split-K with a deeper split for the last tiles: the first `head` tiles of the
 // grouped tile order take `splits` K ranges of k_per_split (a whole number of
 // 256-block rounds), the rest take `tail_splits` ranges of tail_kps, partial
-// product z of every tile in plane z of C (planes [max(splits, tail_splits)][M][N]).
+// product z of every tile in plane z of C (planes [max(splits, tail_splits)][M][N]),
+// or, with `planes` set, plane 0 in C and plane z >= 1 at planes + (z - 1) M N.
 // head == 0: every tile takes `splits` ranges.
 struct SplitTail {
   int head, head_splits, tail_splits, tail_kps;
+  float* planes;
 };
 hipError_t launch_gemm_nt_q(const uint16_t* Arun, const int8_t* Bq, int64_t M, int64_t N, int64_t K, int64_t kb_rows,
                             float* C, hipStream_t s, int splits = 1, int64_t k_per_split = 0,
-                            SplitTail tail = SplitTail{0, 0, 0, 0});
+                            SplitTail tail = SplitTail{0, 0, 0, 0, nullptr});
 
 // Measurement helpers (peak.hip): the matrix instruction on register operands
 // (kind 0: int8 32x32x32, 1: bf16 32x32x16; 4 chains per wave, iters each) and

@@ -884,11 +884,13 @@ def test_backward_full_size_sampled(name, T, d_out, d_in):
     assert_grad_close(dW.cpu().numpy()[cols], dW_ref, tol=ERR_MODEL_BF16)
 
 
-def test_backward_dw_split_tail_full():
-    # 288 tiles of 256 x 256: the first 256 take two K ranges (two whole rounds of
-    # blocks), the last 32 a deeper split; every dW entry against the oracle
-    T, d_out, d_in = 4096, 4608, 4096
-    assert sbl.backward_workspace_size(T, d_in, d_out) > 4 * d_out * d_in * 4  # more than two partial planes
+@pytest.mark.parametrize("T,d_out,d_in,planes", [(4096, 4608, 4096, 5), (2000, 4504, 4112, 2)])
+def test_backward_dw_split_tail_full(T, d_out, d_in, planes):
+    # 288 (306) tiles of 256 x 256: the first 256 take one full-K range (a whole
+    # round of blocks, summed straight into dW), the last 32 (50, ragged in both
+    # dimensions) a deeper split with a ragged last K range, planes 1.. of it in
+    # the workspace; every dW entry against the oracle
+    assert sbl.backward_workspace_size(T, d_in, d_out) >= planes * d_out * d_in * 4
     W = weight(97, 0, d_out, d_in)
     x = activation(97, 1, T, d_in, dist="student_t4")
     dY = grad_out(97, 2, T, d_out)
