@@ -195,22 +195,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_i8(const int8_t* __restrict
 
 // ---------------------------------------------------------------------------
 // Direct-load forward (d_in % 128 == 0): block tile 256 tokens x 256 outputs,
-// 8 waves (2 along M x 4 along N, 128 x 64 each), one block per CU.  Per K
-// step of 128: the x_q tile (256 rows x 128 bytes, swizzled as swz8) and the
+// 8 waves (2 along M x 4 along N, 128 x 64 each), one block per CU (NW = 8),
+// or 128 x 256 with 4 waves, two blocks per CU (NW = 4, for small grids).  Per K
+// step of 128: the x_q tile (256 or 128 rows x 128 bytes, swizzled as swz8) and the
 // code tile (256 rows x 16 code words = 32 bytes) move to LDS with direct-to-
 // LDS loads through two stages; each wave expands the code words of its own B
 // fragments in registers (one 32-bit word = 16 codes = one MFMA operand of 16
 // int8), one slice ahead of the matrix instructions that use them.
 // ---------------------------------------------------------------------------
-constexpr int kFT = 512;                   // threads
 constexpr int kFBN = 256;                  // block cols (outputs)
 constexpr int kFS = 2;                     // LDS stages
 constexpr int kFK = 128;                   // k per step
-constexpr int kFStageA = kBM * kRowK;      // 32 KB
 constexpr int kFStageB = kFBN * 32;        // 8 KB of code words
-constexpr int kFStage = kFStageA + kFStageB;
-constexpr int kFDmaA = kBM * 8 / kFT;      // 4 direct loads per thread per K step
-constexpr int kFDmaStep = kFDmaA + 1;
 
 // Byte offset of code word w (0..7, groups 2w and 2w + 1 of the step) of tile
 // row n: the two 16-byte halves of a row swap places on rows with bit 3 set,
@@ -227,8 +223,8 @@ __device__ __forceinline__ int code_word_at(int n, int w) { return 32 * n + 16 *
 // instruction uses (established on the hardware with random operands).  A K
 // step of 128 is then 2 slices instead of 4; loads, stages and the epilogue
 // are those of the dense path (the plane has the code plane's size).
-template <int OUT, bool SP>
-__global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restrict__ xq,
+template <int OUT, bool SP, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_fwd_i8_direct(const int8_t* __restrict__ xq,
                                                          const uint16_t* __restrict__ codes,
                                                          const float* __restrict__ gamma_p,
                                                          const float* __restrict__ absmax, int T, int d_in,
@@ -236,13 +232,20 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
   // Operand stages, then a separate staging area for the output tile (8 KB per
   // wave), so that a tile's epilogue runs while the next tile's first two K
   // steps land in the stages.
-  __shared__ __attribute__((aligned(1024))) char lds[kFS * kFStage + kFT / 64 * 8192];
+  constexpr int kFT = 64 * NW;                 // threads
+  constexpr int kFBM = NW == 8 ? 256 : 128;    // block rows (tokens)
+  constexpr int kFStageA = kFBM * kRowK;       // x_q tile of a K step
+  constexpr int kFStage = kFStageA + kFStageB;
+  constexpr int kFDmaA = kFBM * 8 / kFT;       // 4 direct loads of x_q per thread per K step
+  constexpr int kFDmaB = kFStageB / 16 / kFT;  // and 1 or 2 of code words
+  constexpr int kFDmaStep = kFDmaA + kFDmaB;
+  __shared__ __attribute__((aligned(1024))) char lds[kFS * kFStage + NW * 8192];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm0 = (wave >> 2) * kWM;
   const int wn0 = (wave & 3) * kWN;
-  const int mtn = (T + kBM - 1) / kBM, ntn = (d_out + kFBN - 1) / kFBN;
+  const int mtn = (T + kFBM - 1) / kFBM, ntn = (d_out + kFBN - 1) / kFBN;
   const int ntiles = mtn * ntn;
   const int G = d_in >> 3;
   const int nk = d_in / kFK;
@@ -259,9 +262,9 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
     Tile r;
     int mt, nt;
     xcd_tile_grouped(t, mtn, ntn, 4, mt, nt);
-    r.m0 = mt * kBM;
+    r.m0 = mt * kFBM;
     r.n0 = nt * kFBN;
-    r.ar = make_rsrc(xq + (int64_t)r.m0 * d_in, clamp_bytes((int64_t)min(kBM, T - r.m0) * d_in));
+    r.ar = make_rsrc(xq + (int64_t)r.m0 * d_in, clamp_bytes((int64_t)min(kFBM, T - r.m0) * d_in));
     r.br = make_rsrc(codes + (int64_t)r.n0 * G, clamp_bytes((int64_t)min(kFBN, d_out - r.n0) * G * 2));
     return r;
   };
@@ -275,22 +278,23 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
     a_off[i] = (uint32_t)(r * d_in + 16 * c);
   }
   // code tile: chunk position p holds row p / 2, half (p % 2) ^ ((row / 8) % 2)
-  uint32_t b_off;
-  {
-    const int p = 64 * wave + lane;
+  uint32_t b_off[kFDmaB];
+#pragma unroll
+  for (int i = 0; i < kFDmaB; ++i) {
+    const int p = 64 * (NW * i + wave) + lane;
     const int r = p >> 1, h = (p & 1) ^ ((r >> 3) & 1);
-    b_off = (uint32_t)(r * G * 2 + 16 * h);
+    b_off[i] = (uint32_t)(r * G * 2 + 16 * h);
   }
 
-  // Load idx (0 .. kFDmaA) of the wave's loads of K step kt of tile tl into stage st.
+  // Load idx (0 .. kFDmaStep - 1) of the wave's loads of K step kt of tile tl into stage st.
   auto issue_one = [&](const Tile& tl, int kt, int st, int idx) {
     char* sa = lds + st * kFStage;
     if (idx < kFDmaA) dma16(tl.ar, sa + 1024 * (kFDmaA * wave + idx), a_off[idx], (uint32_t)kt * kFK);
-    else dma16(tl.br, sa + kFStageA + 1024 * wave, b_off, (uint32_t)kt * (kFK / 4));
+    else dma16(tl.br, sa + kFStageA + 1024 * (NW * (idx - kFDmaA) + wave), b_off[idx - kFDmaA], (uint32_t)kt * (kFK / 4));
   };
   auto issue = [&](const Tile& tl, int kt, int st) {
 #pragma unroll
-    for (int i = 0; i <= kFDmaA; ++i) issue_one(tl, kt, st, i);
+    for (int i = 0; i < kFDmaStep; ++i) issue_one(tl, kt, st, i);
   };
 
   const float g127 = *gamma_p * (1.0f / 127.0f);
@@ -465,14 +469,14 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
           mm_sp_one(3, u, fh1, fbs1, ix1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int d = 0; d < 2; ++d) {  // kFDmaA + 1 = 5 loads over the 3 remaining slots
+          for (int d = 0; d < 2; ++d) {  // 5 or 6 loads over the 3 remaining slots
             const int li = 2 * (u - 1) + d;
-            if (li <= kFDmaA && load) issue_one(lt, kn, sc, li);
+            if (li < kFDmaStep && load) issue_one(lt, kn, sc, li);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int li = 2 * (2 * kNJ - 1); li <= kFDmaA; ++li)
+        for (int li = 2 * (2 * kNJ - 1); li < kFDmaStep; ++li)
           if (load) issue_one(lt, kn, sc, li);
         if (k + 1 < nk) expand(cc0, fbs0);
         __builtin_amdgcn_sched_barrier(0);
@@ -511,7 +515,7 @@ __global__ __launch_bounds__(kFT, 1) void k_fwd_i8_direct(const int8_t* __restri
       for (int u = 1; u < kMI * kNJ; ++u) {
         mm_one(u, fa1, fb1);
         __builtin_amdgcn_sched_barrier(0);
-        if (u - 1 <= kFDmaA && load) issue_one(lt, kn, sc, u - 1);
+        if (u - 1 < kFDmaStep && load) issue_one(lt, kn, sc, u - 1);
         if (u >= kMI * kNJ - kNJ && k + 1 < nk)
           fb0[u - (kMI * kNJ - kNJ)] = __builtin_bit_cast(v4i, expand16(wb0[u - (kMI * kNJ - kNJ)]));
         __builtin_amdgcn_sched_barrier(0);
@@ -934,29 +938,42 @@ int device_cus() {
 }
 
 // One block per tile, or with two or more K steps per tile at most one block
-// per CU (a multiple of 8, the XCD count), each walking its tiles.
-template <bool SP>
-static hipError_t launch_fwd_direct(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
-                                    int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
-  const int64_t nb = ((d_out + kFBN - 1) / kFBN) * ((T + kBM - 1) / kBM);
-  const int64_t cus = std::max(8, device_cus() / 8 * 8);
-  const int64_t nblocks = d_in / kFK >= 2 && nb > cus ? cus : nb;
-  const dim3 grid((unsigned)nblocks), block(kFT);
+// per CU (a multiple of 8, the XCD count), each walking its tiles.  Grids of
+// 256-token tiles that leave CUs idle take 128-token tiles of 4 waves, two
+// blocks per CU, instead (k and v of a 3B layer: 0.035 -> 0.029 ms); on full
+// grids the halved tiles measured 2-3% slower (more operand bytes per product).
+template <bool SP, int NW>
+static hipError_t launch_fwd_nw(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
+                                int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, int64_t slots,
+                                hipStream_t s) {
+  constexpr int bm = NW == 8 ? 256 : 128;
+  const int64_t nb = ((d_out + kFBN - 1) / kFBN) * ((T + bm - 1) / bm);
+  const int64_t nblocks = d_in / kFK >= 2 && nb > slots ? slots : nb;
+  const dim3 grid((unsigned)nblocks), block(64 * NW);
   switch (y_dtype) {
     case SBL_F32:
-      hipLaunchKernelGGL((k_fwd_i8_direct<SBL_F32, SP>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+      hipLaunchKernelGGL((k_fwd_i8_direct<SBL_F32, SP, NW>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
                          (int)d_in, (int)d_out, y);
       break;
     case SBL_BF16:
-      hipLaunchKernelGGL((k_fwd_i8_direct<SBL_BF16, SP>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+      hipLaunchKernelGGL((k_fwd_i8_direct<SBL_BF16, SP, NW>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
                          (int)d_in, (int)d_out, y);
       break;
     default:
-      hipLaunchKernelGGL((k_fwd_i8_direct<SBL_I32, SP>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
+      hipLaunchKernelGGL((k_fwd_i8_direct<SBL_I32, SP, NW>), grid, block, 0, s, xq, codes, gamma, absmax, (int)T,
                          (int)d_in, (int)d_out, y);
       break;
   }
   return hipGetLastError();
+}
+
+template <bool SP>
+static hipError_t launch_fwd_direct(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,
+                                    int64_t T, int64_t d_in, int64_t d_out, void* y, int y_dtype, hipStream_t s) {
+  const int64_t cus = std::max(8, device_cus() / 8 * 8);
+  const int64_t nb8 = ((d_out + kFBN - 1) / kFBN) * ((T + 255) / 256);
+  if (nb8 < cus) return launch_fwd_nw<SP, 4>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, 2 * cus, s);
+  return launch_fwd_nw<SP, 8>(codes, gamma, xq, absmax, T, d_in, d_out, y, y_dtype, cus, s);
 }
 
 hipError_t launch_forward(const uint16_t* codes, const float* gamma, const int8_t* xq, const float* absmax,

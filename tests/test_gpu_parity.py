@@ -135,9 +135,11 @@ def test_pack_graph_capture_matches_eager():
 
 # Kept-only 2:4 plane and the forward on the sparse matrix instruction: the
 # plane bit-exact against the oracle, and the int32 sums (so every output)
-# identical to the dense path's.
+# identical to the dense path's.  (4096, 4096, 128) is a grid of 256 blocks of
+# 256 x 256 (the 8-wave kernel); the smaller grids run the 4-wave one.
 @pytest.mark.parametrize("n,m", [(2, 8), (2, 4), (1, 4)])
-@pytest.mark.parametrize("T,d_out,d_in", [(300, 200, 256), (77, 1000, 1152), (513, 256, 2048), (33, 40, 11008)])
+@pytest.mark.parametrize("T,d_out,d_in", [(300, 200, 256), (77, 1000, 1152), (513, 256, 2048), (33, 40, 11008),
+                                          (4096, 4096, 128)])
 def test_sparse24_parity(T, d_out, d_in, n, m):
     W = weight(67, n + m + d_in, d_out, d_in)
     x = activation(67, d_out + T, T, d_in, dist="student_t4")
