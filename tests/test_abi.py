@@ -271,6 +271,24 @@ def test_backward_validation():
     assert f(NULL, NULL, NULL, NULL, NULL, 0, 256, 256, NULL, 1, NULL, 1, NULL, 0, NULL) == OK
 
 
+@pytest.mark.parametrize("T,d_in,d_out,planes", [
+    (32768, 2048, 11008, 4),  # 344 tiles: 256 over all of K into dW, 88 in 5 K ranges (planes 1-4)
+    (32768, 11008, 2048, 4),  # the same plan for the transposed shape
+    (4096, 4096, 4608, 5),    # 288 tiles: 32 tail tiles in 6 ranges
+    (2000, 4112, 4504, 2),    # 306 tiles, ragged in both dimensions: 50 tail tiles in 3 ranges
+    (32768, 2048, 2048, 4),   # 64 tiles: a uniform 4-way split fills the 256 CUs
+    (32768, 2048, 256, 32),   # 8 tiles: 32-way split
+    (8192, 1536, 8960, 0),    # 210 tiles: one round without a split
+    (8192, 8960, 1536, 0),
+])
+def test_backward_dw_workspace_plan(T, d_in, d_out, planes):
+    # dW alone on the int8 form: the scaled dY^T (run-major bf16, 256-byte aligned) and
+    # the split-K planes of float32 [d_out][d_in] that the plan needs
+    T8 = (T + 7) // 8 * 8
+    dyt = (d_out * T8 * 2 + 255) // 256 * 256
+    assert lib.sbl_backward_workspace_size(T, d_in, d_out, 2) == dyt + planes * d_out * d_in * 4
+
+
 def _round_mean_lib(S: int, count: int) -> float:
     words = (ctypes.c_uint32 * 10)(*[(S >> (32 * i)) & 0xFFFFFFFF for i in range(10)])
     out = ctypes.c_float()
