@@ -15,8 +15,10 @@ recomputed every step), then for each of the 7 linears, in order:
 Metric: tokens per second of whole steps.  Prints one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
-       python bench.py --workload 0     (one 256x256 linear, 64 tokens, fwd+bwd: launch-bound)
-       python bench.py --workload 1     (0.5B-like up-projection 896->4864, 512 tokens, forward, 8/6/4/2:8)
+       python bench.py --workload 0     (one 256x256 linear, 64 tokens, fwd+bwd: launch-bound, timed as
+                                         replays of the step captured in a HIP graph; --timing eager for launches)
+       python bench.py --workload 1     (0.5B-like up-projection 896->4864, 512 tokens, forward, 8/6/4/2:8;
+                                         graph replays as for workload 0)
        python bench.py --workload 2     (1.5B-like linears, 8192 tokens, fwd+bwd)
        python bench.py --workload 4     (decode: per-layer latency at 1/8/64 tokens, 6/4/2:8)
        python bench.py --peaks          (measured ceilings only: matrix instructions on registers, HBM read)
@@ -73,7 +75,24 @@ def parse():
                          "in a captured graph over distinct buffers) and print one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
+    ap.add_argument("--timing", choices=("auto", "eager", "graph"), default="auto",
+                    help="how steps are timed: eager launches, or replays of the step captured in one HIP graph "
+                         "(auto: graph for the launch-bound workloads 0 and 1, whose kernels run for a few "
+                         "microseconds each, eager otherwise)")
     return ap.parse_args()
+
+
+# Workloads whose step is a handful of launches of a few microseconds each: eager timing would
+# measure the host's enqueue rate, so their steps are timed as replays of a captured graph (how a
+# training or serving loop at these sizes would run them), the eager figure reported beside it.
+# GRAPH_COPIES steps (or calls, for the per-call figures) go into one graph, back to back, so that
+# the fixed cost of a graph launch is spread over them.
+LAUNCH_BOUND_WORKLOADS = (0, 1)
+GRAPH_COPIES = 10
+
+
+def use_graph(args) -> bool:
+    return args.timing == "graph" or (args.timing == "auto" and args.workload in LAUNCH_BOUND_WORKLOADS)
 
 
 def main():
@@ -201,6 +220,12 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T * args.steps / elapsed
+    eager_ms_per_step = ms_per_step
+    graph = use_graph(args)
+    if graph:
+        # the whole step captured once and replayed (every kernel of every call runs in each replay)
+        ms_per_step = graph_us(step, reps=max(args.steps, 20), warmup=args.warmup, copies=GRAPH_COPIES) / 1e3
+        tokens_per_s = T / (ms_per_step * 1e-3)
 
     # Timed region 2: the same steps with HIP events between the calls (same stream), for the
     # per-kernel durations behind the roofline figures.
@@ -217,6 +242,31 @@ def main():
             for k in range(len(parts)):
                 sums[li, k] += ev[li][k].elapsed_time(ev[li][k + 1])
     per_launch_ms = sums / args.steps          # [layer, part]
+    if graph:
+        # per call: each call alone captured in a graph and replayed (events between eager launches
+        # would time the host's enqueue gaps)
+        for li, Lr in enumerate(layers):
+            if args.pack == "single":
+                quant = lambda Lr=Lr: sbl.quant_mask_pack(Lr["W"], n_keep, codes=Lr["codes"], mask=Lr["mask"],
+                                                          gamma=Lr["gamma"], workspace=qws)
+            elif li == 0:
+                quant = lambda: sbl.quant_mask_pack_batch([Lq["W"] for Lq in layers], n_keep,
+                                                          codes=[Lq["codes"] for Lq in layers],
+                                                          masks=[Lq["mask"] for Lq in layers],
+                                                          gammas=[Lq["gamma"] for Lq in layers], workspace=qws)
+            else:
+                quant = None  # the batch's time is counted once, on the first linear
+            calls = [
+                quant,
+                lambda Lr=Lr: sbl.act_quant(Lr["x"], x_q=Lr["x_q"], absmax=Lr["absmax"]),
+                lambda Lr=Lr: sbl.forward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], out_dtype=sbl.BF16,
+                                          y=Lr["y"]),
+                lambda Lr=Lr: sbl.backward(Lr["codes"], Lr["gamma"], Lr["x_q"], Lr["absmax"], Lr["dY"],
+                                           dx_dtype=sbl.BF16, dX=Lr["dX"], dW=Lr["dW"], workspace=Lr["bws"]),
+            ]
+            for k, c in enumerate(calls):
+                per_launch_ms[li, k] = 0.0 if c is None else graph_us(c, reps=max(args.steps, 20), warmup=args.warmup,
+                                                                       copies=GRAPH_COPIES) / 1e3
 
     # Algorithmic work per launch (units x per-unit figure).
     work = []
@@ -304,6 +354,10 @@ def main():
         "measured_peaks": peaks,
         "input_gen_s": round(t_gen, 1),
     }
+    if graph:
+        line["timing"] = (f"graph replay: {GRAPH_COPIES} steps captured back to back in one HIP graph, replayed, "
+                          f"time / {GRAPH_COPIES}; per-call figures likewise from {GRAPH_COPIES} copies of each call")
+        line["eager_ms_per_step"] = round(eager_ms_per_step, 4)
     if args.breakdown:
         for li, Lr in enumerate(layers):
             print(Lr["name"], " ".join(f"{p}={per_launch_ms[li, k]:.4f}ms" for k, p in enumerate(parts)),
@@ -544,8 +598,10 @@ def _decode_case(args, wl, sbl, torch, up, activation, groups, layers, plane_nam
     return r
 
 
-def graph_us(fn, reps: int = 20, warmup: int = 3) -> float:
-    """Time of one replay of fn captured in a HIP graph (fn's launches go to the current stream)."""
+def graph_us(fn, reps: int = 20, warmup: int = 3, copies: int = 1) -> float:
+    """Time of one call of fn, from replays of a HIP graph that holds `copies` calls of fn back to
+    back (fn's launches go to the current stream); copies > 1 spreads the fixed cost of one graph
+    launch (about 20 us here, more than a small step's kernels) over that many calls."""
     import torch
 
     side = torch.cuda.Stream()
@@ -556,7 +612,8 @@ def graph_us(fn, reps: int = 20, warmup: int = 3) -> float:
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        fn()
+        for _ in range(copies):
+            fn()
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -567,7 +624,7 @@ def graph_us(fn, reps: int = 20, warmup: int = 3) -> float:
     e1.record()
     torch.cuda.synchronize()
     del graph
-    return e0.elapsed_time(e1) * 1e3 / reps
+    return e0.elapsed_time(e1) * 1e3 / reps / copies
 
 
 def read_floor_us(nbytes: int) -> float:
@@ -691,8 +748,10 @@ def measured_peaks():
 
 def run_forward_sweep(args, wl):
     """Forward-only workload swept over masks (the 0.5B-like up-projection): per mask, one step is
-    the packing of W (quant/mask/pack), the act quant of x and the forward (y bf16), each timed
-    with HIP events on the stream; tokens/s = T / step time.  Inputs resident in HBM."""
+    the packing of W (quant/mask/pack), the act quant of x and the forward (y bf16); tokens/s =
+    T / step time.  The step is timed as replays of one captured graph (and, as eager_step_ms,
+    with HIP events between eager launches; --timing eager makes that the figure).  Inputs
+    resident in HBM."""
     import numpy as np
     import torch
 
@@ -738,12 +797,17 @@ def run_forward_sweep(args, wl):
         wall = (time.perf_counter() - t0) / reps
         ms = np.array([[ev[k].elapsed_time(ev[k + 1]) for k in range(3)] for ev in evs]).mean(axis=0)
         step_ms = float(ms.sum())
+        eager_step_ms = step_ms
+        if use_graph(args):
+            # the three calls captured in one graph and replayed; per call, each captured alone
+            step_ms = graph_us(lambda: [c() for c in calls], reps=reps, warmup=args.warmup, copies=GRAPH_COPIES) / 1e3
+            ms = np.array([graph_us(c, reps=reps, warmup=args.warmup, copies=GRAPH_COPIES) / 1e3 for c in calls])
         ops = 2.0 * T * d_out * d_in * n_keep / 8
         q_bytes = 2.375 * d_out * d_in
         a_bytes = 3.0 * T * d_in + 4.0 * T
         f_bytes = T * d_in + d_out * d_in / 4 + 2.0 * T * d_out
         r = {"n_keep": n_keep, "tokens_per_s": round(T / (step_ms * 1e-3), 1), "step_ms": round(step_ms, 5),
-             "wall_ms_per_step": round(wall * 1e3, 5),
+             "eager_step_ms": round(eager_step_ms, 5), "wall_ms_per_step": round(wall * 1e3, 5),
              "quant_mask_pack": {"ms": round(ms[0], 5), "frac_hbm": round(q_bytes / (ms[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
              "act_quant": {"ms": round(ms[1], 5), "frac_hbm": round(a_bytes / (ms[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
              "forward_int8": {"ms": round(ms[2], 5), "TOPs": round(ops / (ms[2] * 1e-3) / 1e12, 2),
@@ -771,6 +835,10 @@ def run_forward_sweep(args, wl):
             "vs_baseline": None, "dtype": "int8 x ternary (int32 accumulate), y bf16", "data": "synthetic",
             "config": {"workload": wl.name, "tokens": T, "d_out": d_out, "d_in": d_in, "masks": list(wl.n_keep)},
             "roofline": roofline, "results": results, "cpu_baseline": cpu, "measured_peaks": peaks}
+    if use_graph(args):
+        line["timing"] = (f"graph replay: {GRAPH_COPIES} steps (the three calls each) captured back to back in one HIP "
+                          f"graph, replayed, time / {GRAPH_COPIES}; per-call figures likewise from {GRAPH_COPIES} copies "
+                          "of each call; eager_step_ms: events between eager launches")
     print(json.dumps(line), flush=True)
 
 

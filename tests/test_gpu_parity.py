@@ -958,6 +958,57 @@ def test_step_bitwise_deterministic():
         assert torch.equal(u, v)
 
 
+@pytest.mark.parametrize("d_out,d_in,T", [(256, 256, 64), (512, 1024, 1000), (4864, 896, 512)])
+def test_step_graph_replay_matches_eager(d_out, d_in, T):
+    # a whole step (packing, act quant, forward, backward with its split-K sums) captured in one
+    # HIP graph, as bench.py times the launch-bound workloads: every replay, with eager work and
+    # cleared outputs between the replays, equals the eager step bit for bit
+    W = to_dev_bf16(weight(83, d_out, d_out, d_in))
+    x = to_dev_bf16(activation(83, d_in, T, d_in, dist="student_t4"))
+    dY = to_dev_bf16(grad_out(83, T, T, d_out))
+    codes, mask, gamma = sbl.quant_mask_pack(W, 6)
+    xq, a = sbl.act_quant(x)
+    y = sbl.forward(codes, gamma, xq, a, out_dtype=sbl.BF16)
+    dX, dW = sbl.backward(codes, gamma, xq, a, dY, dx_dtype=sbl.BF16)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (codes, mask, gamma, xq, a, y, dX, dW)]
+    outs = [torch.empty_like(t) for t in want]
+    qws = torch.empty((max(16, sbl.quant_workspace_size(d_out, d_in)),), dtype=torch.uint8, device="cuda")
+    bws = torch.empty((max(16, sbl.backward_workspace_size(T, d_in, d_out, sbl.BWD_DX | sbl.BWD_DW)),),
+                      dtype=torch.uint8, device="cuda")
+
+    def run():
+        c, m, g, q, s, yy, dx, dw = outs
+        sbl.quant_mask_pack(W, 6, codes=c, mask=m, gamma=g, workspace=qws)
+        sbl.act_quant(x, x_q=q, absmax=s)
+        sbl.forward(c, g, q, s, out_dtype=sbl.BF16, y=yy)
+        sbl.backward(c, g, q, s, dY, dx_dtype=sbl.BF16, dX=dx, dW=dw, workspace=bws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for i in range(3):
+        for t in outs:
+            t.zero_()
+        other = sbl.act_quant(x[:7])                   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, (got, ref) in enumerate(zip(outs, want)):
+            if got.dtype.is_floating_point:
+                got, ref = got.view(torch.int16 if got.element_size() == 2 else torch.int32), \
+                    ref.view(torch.int16 if ref.element_size() == 2 else torch.int32)
+            assert torch.equal(got, ref), f"replay {i}, output {k}"
+        assert other[0].shape == (7, d_in)
+    del g
+
+
 def test_autograd_function_matches_oracle():
     W = weight(91, 0, 96, 128)
     x = activation(91, 1, 40, 128)
