@@ -43,8 +43,8 @@ HBM_PEAK_GBS = 8000.0
 # WRITE_SIZE, scale factors from a plain 1 GiB copy), averaged over the 7 linears; measured with
 # rocprofv3 --pmc for the backward kernel sources whose hash (code without comments) is given
 # (profiles/traffic_backward_3b_32768tok.md).
-BWD_TRAFFIC_BYTES = 1.942e9
-BWD_TRAFFIC_SRC_SHA = "aff1f9b4014f9405"
+BWD_TRAFFIC_BYTES = 1.937e9
+BWD_TRAFFIC_SRC_SHA = "cc9ce8ccca9351e6"
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 

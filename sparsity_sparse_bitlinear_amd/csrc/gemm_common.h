@@ -151,6 +151,14 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds_wave_b
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SBL_LDS void*)lds_wave_base, 16, voff, soff, 0, 0);
 }
 
+// 16-byte store that is not kept in the caches (the `nt` store): for the large outputs (y, dX,
+// the final dW) that nothing in the same call reads again; streaming them past the caches
+// leaves L2 and the last-level cache to the operands.
+__device__ __forceinline__ void store_nt16(void* p, uint4 v) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), (u32x4*)p);
+}
+
 // 4-byte variant: lane l lands at +4 l (256 bytes per wave).
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char* lds_wave_base, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (SBL_LDS void*)lds_wave_base, 4, voff, soff, 0, 0);

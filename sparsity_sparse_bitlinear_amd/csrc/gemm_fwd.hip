@@ -571,8 +571,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_fwd_i8_direct(const int8_t*
             const int row = (64 / kCh) * u + lane / kCh;
             const uint4 v = *(const uint4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))));
             const int m = m0 + wm0 + 32 * kIR * r + row;
-            if (m < T && n < d_out)
-              *(uint4*)((char*)y + ((int64_t)m * d_out + n) * (OUT == SBL_F32 ? 4 : 2)) = v;
+            if (m < T && n < d_out) store_nt16((char*)y + ((int64_t)m * d_out + n) * (OUT == SBL_F32 ? 4 : 2), v);
           }
         }
       }

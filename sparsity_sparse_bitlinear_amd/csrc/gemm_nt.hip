@@ -559,6 +559,9 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
   // C[m = l % 32][n = 8 (r / 4) + 4 (l / 32) + r % 4]: each lane stores runs
   // of 4 consecutive outputs of one row (16 bytes in float32, 8 in bf16).
   constexpr float pre = BC ? 0.5f : 1.0f;  // BC: the sums are of 2 W_eff (halving is exact)
+  // bf16 outputs (dX) stream past the caches: -0.5% on the backward; the float32 ones (dW, and
+  // split-K planes that the sum reads back) measured the same either way and stay cached stores
+  constexpr bool final_out = OUT == SBL_BF16;
   if (tail.planes && split > 0)
     C = (char*)tail.planes + (size_t)(split - 1) * (size_t)M * (size_t)N * (OUT == SBL_F32 ? 4 : 2);
   else
@@ -604,8 +607,11 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
         const int row = (64 / kCh) * u + lane / kCh;
         const uint4 v = *(const uint4*)(stg + row * kRB + 16 * (c ^ (row & (kCh - 1))));
         const int m = m0 + wm0 + 32 * kIR * r + row;
-        if (m < M && n < N)
-          *(uint4*)((char*)C + ((int64_t)m * N + n) * (OUT == SBL_F32 ? 4 : 2)) = v;
+        if (m < M && n < N) {
+          char* const p = (char*)C + ((int64_t)m * N + n) * (OUT == SBL_F32 ? 4 : 2);
+          if (final_out) store_nt16(p, v);
+          else *(uint4*)p = v;
+        }
       }
     }
     return;
