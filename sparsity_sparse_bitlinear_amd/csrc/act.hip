@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ 
   for (int c = 0; c < NC; ++c) {
     const int idx = lane + kR * c;
     if (idx < nch) {
-      v[c] = row[idx];
+      v[c] = load_nt16(row + idx);
       m = max(m, max(max_mag2(v[c].x), max_mag2(v[c].y)));
       m = max(m, max(max_mag2(v[c].z), max_mag2(v[c].w)));
     } else {
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void k_act_quant(const uint16_t* __restrict__ 
     }
   }
   for (int idx = lane + kR * NC; idx < nch; idx += kR) {  // rows longer than the register window
-    const uint4 w = row[idx];
+    const uint4 w = row[idx];  // (read again below: cached)
     m = max(m, max(max_mag2(w.x), max_mag2(w.y)));
     m = max(m, max(max_mag2(w.z), max_mag2(w.w)));
   }

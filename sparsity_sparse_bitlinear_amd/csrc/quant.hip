@@ -425,7 +425,7 @@ __device__ __forceinline__ void mqp_body(const uint4* __restrict__ W, int64_t n_
   for (int64_t g0 = (int64_t)blk * 256 * kU + threadIdx.x; g0 < n_groups; g0 += stride) {
     uint4 v[kU];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) v[u] = g0 + 256 * u < n_groups ? W[g0 + 256 * u] : make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < kU; ++u) v[u] = g0 + 256 * u < n_groups ? load_nt16(W + g0 + 256 * u) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int64_t g = g0 + 256 * u;

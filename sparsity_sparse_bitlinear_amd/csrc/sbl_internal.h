@@ -8,6 +8,15 @@
 
 namespace sbl {
 
+// 16-byte load that is not kept in the caches (`nt`): for inputs read exactly once (x in the
+// activation quantization, W in the packing's second pass), so that they do not push out of
+// L2 and the last-level cache what the next kernels read again (x_q, the code plane).
+__device__ __forceinline__ uint4 load_nt16(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4*)p));
+}
+
+
 // ---------------------------------------------------------------------------
 // Vector types used for MFMA operands and 16-byte memory traffic.
 // ---------------------------------------------------------------------------
