@@ -573,6 +573,35 @@ def test_decode_multi_matches_single(T, group):
             np.testing.assert_array_equal(y.cpu().numpy(), acc_ref)
 
 
+@pytest.mark.parametrize("T,shapes", [(8, [(8200, 128), (8200, 128), (40, 128)]),
+                                      (12, [(8200, 128), (8200, 128), (40, 128)]),
+                                      (16, [(8200, 128), (8200, 128), (40, 128)]),
+                                      (16, [(8192, 2944), (8200, 2944)])])
+def test_decode_multi_ragged_and_wide_rows(T, shapes):
+    # x quantized in the launch (bf16 x given): ragged last tiles of 8200 and 40 rows at 8-16
+    # tokens, and rows of 2944 whose 16-token activation tile fills most of a block's LDS over
+    # more than 16384 output rows; every output equals decode of that matrix alone, and the
+    # int32 sums equal the oracle's
+    d_in = shapes[0][1]
+    Ws = [weight(78, 10 * i + T, d_o, d_i) for i, (d_o, d_i) in enumerate(shapes)]
+    mats = []
+    for W in Ws:
+        codes, _, gamma = sbl.quant_mask_pack(to_dev_bf16(W), 6, want_mask=False)
+        mats.append((codes, gamma))
+    x = activation(78, 200 + T, T, d_in, dist="student_t4")
+    xd = to_dev_bf16(x)
+    for dt in (sbl.I32, sbl.BF16):
+        ys = sbl.decode_multi(mats, xd, out_dtype=dt)
+        for (codes, gamma), y in zip(mats, ys):
+            want = sbl.decode(codes, gamma, xd, out_dtype=dt)
+            torch.cuda.synchronize()
+            assert same_bits(y, want, dt), (shapes, T, dt)
+    ys = sbl.decode_multi(mats, xd, out_dtype=sbl.I32)
+    for W, y in zip(Ws, ys):
+        acc_ref, _ = ref_forward(W, x, 6)
+        np.testing.assert_array_equal(y.cpu().numpy(), acc_ref)
+
+
 @pytest.mark.parametrize("group", sorted(DECODE_GROUPS))
 @pytest.mark.parametrize("T", [1, 16, 33, 64])
 def test_forward_decode_multi_matches_single(T, group):
