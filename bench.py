@@ -44,7 +44,7 @@ HBM_PEAK_GBS = 8000.0
 # rocprofv3 --pmc for the backward kernel sources whose hash (code without comments) is given
 # (profiles/traffic_backward_3b_32768tok.md).
 BWD_TRAFFIC_BYTES = 1.937e9
-BWD_TRAFFIC_SRC_SHA = "cc9ce8ccca9351e6"
+BWD_TRAFFIC_SRC_SHA = "723f0d7b93da5309"
 INT8_PEAK_TOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
