@@ -506,8 +506,6 @@ __global__ __launch_bounds__(kNT, 1) void k_gemm_nt_bf16(const uint16_t* __restr
     }
     barrier_only();
     __builtin_amdgcn_sched_barrier(0);
-    // Transposed copy of step k + 1's A tile: it has landed and is not
-    // refilled before the next barrier.
     // this block writes the transposed copy of step k + 1's A tile (landed, and not refilled
     // before the next barrier), one round after each of the first matrix instructions below
     const bool wt = WTA && k + 1 < nk && (k + 1) % gn == nt;
