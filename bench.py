@@ -223,7 +223,8 @@ def main():
     eager_ms_per_step = ms_per_step
     graph = use_graph(args)
     if graph:
-        # the whole step captured once and replayed (every kernel of every call runs in each replay)
+        # GRAPH_COPIES whole steps captured back to back and replayed (every kernel of every call
+        # runs in each copy)
         ms_per_step = graph_us(step, reps=max(args.steps, 20), warmup=args.warmup, copies=GRAPH_COPIES) / 1e3
         tokens_per_s = T / (ms_per_step * 1e-3)
 
@@ -243,8 +244,8 @@ def main():
                 sums[li, k] += ev[li][k].elapsed_time(ev[li][k + 1])
     per_launch_ms = sums / args.steps          # [layer, part]
     if graph:
-        # per call: each call alone captured in a graph and replayed (events between eager launches
-        # would time the host's enqueue gaps)
+        # per call: GRAPH_COPIES copies of the call alone captured in a graph and replayed (events
+        # between eager launches would time the host's enqueue gaps)
         for li, Lr in enumerate(layers):
             if args.pack == "single":
                 quant = lambda Lr=Lr: sbl.quant_mask_pack(Lr["W"], n_keep, codes=Lr["codes"], mask=Lr["mask"],
@@ -799,7 +800,8 @@ def run_forward_sweep(args, wl):
         step_ms = float(ms.sum())
         eager_step_ms = step_ms
         if use_graph(args):
-            # the three calls captured in one graph and replayed; per call, each captured alone
+            # GRAPH_COPIES steps of the three calls captured in one graph and replayed; per call,
+            # GRAPH_COPIES copies of it alone
             step_ms = graph_us(lambda: [c() for c in calls], reps=reps, warmup=args.warmup, copies=GRAPH_COPIES) / 1e3
             ms = np.array([graph_us(c, reps=reps, warmup=args.warmup, copies=GRAPH_COPIES) / 1e3 for c in calls])
         ops = 2.0 * T * d_out * d_in * n_keep / 8
