@@ -12,7 +12,9 @@ recomputed every step), then for each of the 7 linears, in order:
   sbl_forward         (int8 MFMA, y bf16)
   sbl_backward        (dX and dW in one call: bf16 MFMA, dX bf16, dW float32 dense;
                        the dX product leaves dY^T behind for dW)
-Metric: tokens per second of whole steps.  Prints one JSON line.
+Metric: tokens per second of whole steps.  Prints one JSON line; after the timed steps the default
+workload also counts the backward call's HBM bytes with two rocprofv3 --pmc passes run as child
+processes (--no-live-traffic skips them).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
        python bench.py --workload 0     (one 256x256 linear, 64 tokens, fwd+bwd: launch-bound, timed as
@@ -75,6 +77,10 @@ def parse():
                          "in a captured graph over distinct buffers) and print one JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (scale reference for HBM byte counters)")
+    ap.add_argument("--no-live-traffic", action="store_true",
+                    help="default workload: skip the live HBM byte count of the backward call (two rocprofv3 "
+                         "--pmc passes and their copy calibration, run as child processes after the timed "
+                         "steps) and report the figure of the committed profile instead")
     ap.add_argument("--timing", choices=("auto", "eager", "graph"), default="auto",
                     help="how steps are timed: eager launches, or replays of the step captured in one HIP graph "
                          "(auto: graph for the launch-bound workloads 0 and 1, whose kernels run for a few "
@@ -304,13 +310,21 @@ def main():
     dname, dunit, dpeak, dkernels = gemm_parts[dom]
     n_launch = len(layers)
     achieved = sum(w[dom] for w in work) / n_launch / (tot_ms[parts.index(dom)] / n_launch * 1e-3) / 1e12
-    traffic = None
-    if (dom == "bwd" and args.workload == 3 and n_keep == 6 and BWD_TRAFFIC_BYTES is not None
+    traffic, traffic_src = None, None
+    if dom == "bwd" and args.workload == 3 and n_keep == 6 and not args.no_live_traffic:
+        live = live_traffic(2 * len(layers))  # the child runs one timed and one event-timed step
+        if live is not None:
+            traffic, traffic_src = live["bytes"], ("rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE over this "
+                                                   "workload in this run, copy-calibrated")
+    if (traffic is None and dom == "bwd" and args.workload == 3 and n_keep == 6 and BWD_TRAFFIC_BYTES is not None
             and _bwd_sources_sha() == BWD_TRAFFIC_SRC_SHA):
-        traffic = BWD_TRAFFIC_BYTES
+        traffic, traffic_src = BWD_TRAFFIC_BYTES, "committed counter profile of these backward sources"
+    if traffic is not None:
+        traffic = float(round(traffic, -6))
     roofline = {"bound": "mfma", "kernel": dname, "achieved": round(achieved, 1), "peak": dpeak,
                 "unit": dunit, "frac": round(achieved / dpeak, 4), "traffic": traffic,
                 "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                "traffic_source": traffic_src,
                 "launches_per_step": n_launch, "hip_kernels": dkernels,
                 "avg_launch_ms": round(tot_ms[parts.index(dom)] / n_launch, 4)}
 
@@ -364,6 +378,74 @@ def main():
             print(Lr["name"], " ".join(f"{p}={per_launch_ms[li, k]:.4f}ms" for k, p in enumerate(parts)),
                   file=sys.stderr)
     print(json.dumps(line), flush=True)
+
+
+def _counter_kib(csv_path: str, pick) -> tuple:
+    """Sum of Counter_Value (KiB) over the dispatches whose kernel name `pick` accepts, and their
+    count, from a rocprofv3 counter_collection.csv."""
+    import csv
+    total, n = 0.0, 0
+    with open(csv_path, newline="") as fh:
+        for row in csv.DictReader(fh):
+            if pick(row["Kernel_Name"]):
+                total += float(row["Counter_Value"])
+                n += 1
+    return total, n
+
+
+def live_traffic(n_calls: int, timeout_s: float = 180.0):
+    """HBM bytes per sbl_backward call of the default workload, counted in this run: rocprofv3
+    --pmc FETCH_SIZE, then WRITE_SIZE, each over a child `bench.py --steps 1 --warmup 0` (two steps:
+    n_calls backward calls) and over a plain 1 GiB copy whose known size scales the counter.  The
+    backward call's kernels are the code-plane transpose, the two bf16 products and the split-K
+    sums.  None if rocprofv3 is missing or any pass fails or runs out of time."""
+    import glob
+    import shutil
+    import subprocess
+    import tempfile
+
+    prof = shutil.which("rocprofv3")
+    if prof is None:
+        return None
+    me = os.path.abspath(__file__)
+    env = dict(os.environ, TMPDIR="/tmp")
+    bwd = ("k_codes_t", "k_gemm_nt_bf16", "k_splitk_reduce", "k_splitk_add_tail")
+    out = {}
+    try:
+        with tempfile.TemporaryDirectory(prefix="sbl_pmc_", dir="/tmp") as tmp:
+            for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+                got = {}
+                for kind, extra in (("copy", ["--copy-calibration"]),
+                                    ("train", ["--steps", "1", "--warmup", "0", "--no-cpu-baseline", "--no-peaks",
+                                               "--no-live-traffic"])):
+                    d = os.path.join(tmp, f"{kind}_{counter}")
+                    cmd = [prof, "--pmc", counter, "--output-format", "csv", "-d", d, "-o", "run", "--",
+                           sys.executable, me, *extra]
+                    # rocprofv3 may end with a fault of its own after the program has finished: the
+                    # result file decides, not the exit status.  The pass runs in a process group of its
+                    # own, so that a time-out ends the profiled program too, not only the profiler
+                    proc = subprocess.Popen(cmd, cwd="/tmp", env=env, stdout=subprocess.DEVNULL,
+                                            stderr=subprocess.DEVNULL, start_new_session=True)
+                    try:
+                        proc.wait(timeout=timeout_s)
+                    except subprocess.TimeoutExpired:
+                        import signal
+                        os.killpg(proc.pid, signal.SIGKILL)
+                        proc.wait()
+                        return None
+                    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+                    if not files:
+                        return None
+                    got[kind] = files[0]
+                copy_kib, n_copy = _counter_kib(got["copy"], lambda k: "copyBuffer" in k)
+                kib, n_k = _counter_kib(got["train"], lambda k: any(b in k for b in bwd))
+                if n_copy == 0 or copy_kib <= 0 or n_k == 0:
+                    return None
+                scale = (1 << 30) / 1024.0 / (copy_kib / n_copy)  # counter KiB -> true KiB (1 GiB per copy)
+                out[counter] = kib * scale * 1024.0 / n_calls
+    except (subprocess.SubprocessError, OSError, ValueError, KeyError):
+        return None
+    return {"bytes": out["FETCH_SIZE"] + out["WRITE_SIZE"], "fetch": out["FETCH_SIZE"], "write": out["WRITE_SIZE"]}
 
 
 def _code_text(src: str) -> str:
