@@ -60,7 +60,8 @@ def parse():
     ap.add_argument("--n-keep", type=int, default=6)
     ap.add_argument("--pack", choices=("batch", "single"), default="batch",
                     help="pack all linears in one batched call (default) or one call per linear")
-    ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=12288,
+                    help="token sample for the oracle baseline (about 10 s of host work on the default workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-fuse-max", type=int, default=None,
                     help="decode: largest T * d_in of a group that takes the fused launch (default: wherever supported)")
