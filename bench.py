@@ -394,12 +394,13 @@ def _counter_kib(csv_path: str, pick) -> tuple:
     return total, n
 
 
-def live_traffic(n_calls: int, timeout_s: float = 180.0):
+def live_traffic(n_calls: int, timeout_s: float = 90.0):
     """HBM bytes per sbl_backward call of the default workload, counted in this run: rocprofv3
     --pmc FETCH_SIZE, then WRITE_SIZE, each over a child `bench.py --steps 1 --warmup 0` (two steps:
     n_calls backward calls) and over a plain 1 GiB copy whose known size scales the counter.  The
     backward call's kernels are the code-plane transpose, the two bf16 products and the split-K
-    sums.  None if rocprofv3 is missing or any pass fails or runs out of time."""
+    sums.  None if rocprofv3 is missing or any pass fails or runs out of time (a pass takes 5-10 s;
+    the first failure ends the count, so a stuck profiler costs at most one time limit)."""
     import glob
     import shutil
     import subprocess
